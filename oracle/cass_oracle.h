@@ -1,0 +1,83 @@
+/*
+ * CPU oracle for the Cassandra bit-level weight format -- TEST INFRASTRUCTURE.
+ *
+ * A plain, slow, scalar C implementation of what the format and the draft /
+ * verify products compute.  Only tests, the smoke check and the CPU-baseline
+ * leg of the benchmark may call it; the HIP library never does, and the two
+ * share no code.  Every function follows the method's steps in the order the
+ * pages give them:
+ *   pruning -> mantissa truncation -> exponent coding, producing a
+ *   speculation stream and a verification stream
+ *   (Cassandra review, marsggbo.github.io, section 3.1 "从 bit 里抠 draft model";
+ *    exponent coding: section 3.2, Cassandra-1 unary code and Cassandra-2 MX).
+ *
+ * Byte layout of a stream (written out here independently of the library):
+ *   [0,256)  header: u32 magic, u32 version(=1), u32 format, u32 mant_bits,
+ *            i64 rows, i64 cols, i64 block, i64 keep, i64 total_bytes,
+ *            u32 n_sections, u32 reserved, then 12 x {i64 offset, i64 bytes}.
+ *   sections follow in a fixed order, each starting at a multiple of 256 B;
+ *   padding bytes and pad bits are zero.  Bit i of a bit section is bit (i&7)
+ *   of byte i>>3 (least significant bit first).
+ *
+ * Status codes match the library's public ones by value.
+ */
+#ifndef CASS_ORACLE_H
+#define CASS_ORACLE_H
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { ORC_OK = 0, ORC_ERR_INVALID = 1, ORC_ERR_UNSUPPORTED = 2, ORC_ERR_OVERFLOW = 3,
+       ORC_ERR_CORRUPT = 4, ORC_ERR_CAPACITY = 5 };
+enum { ORC_FMT_C1 = 1, ORC_FMT_C2 = 2 };
+
+#define ORC_MAGIC_SPEC  0x50535343u /* "CSSP" */
+#define ORC_MAGIC_VERIF 0x46565343u /* "CSVF" */
+
+/* --- individual steps, exposed so tests can pin them one by one --- */
+
+/* Step 1, pruning: per row of C values keep exactly k, ordered by |w| (the 15
+ * magnitude bits) descending, ties to the lower column.  keep[r*C+j] = 0/1. */
+int orc_select(const uint16_t* w, int64_t R, int64_t C, int64_t k, uint8_t* keep);
+
+/* Exponent histograms: hist_kept[e] over kept values, hist_pruned[e] over the rest. */
+int orc_histograms(const uint16_t* w, const uint8_t* keep, int64_t n,
+                   uint64_t hist_kept[256], uint64_t hist_pruned[256]);
+
+/* Frequency ranking: perm[r] = symbol of rank r, symbols ordered by count
+ * descending, ties (and absent symbols) by symbol ascending. */
+void orc_rank_table(const uint64_t hist[256], uint8_t perm[256]);
+
+/* --- Cassandra-1 (unary exponents, lossless) and Cassandra-2 (MX-32) --- */
+
+/* Encode w[R][C] (bf16 bit patterns).  With spec == NULL (or verif == NULL)
+ * only the sizes are returned.  Returns a status code. */
+int orc_encode(const uint16_t* w, int64_t R, int64_t C, int64_t k, int m, int64_t B,
+               int format, uint8_t* spec, int64_t spec_cap, uint8_t* verif,
+               int64_t verif_cap, int64_t* spec_bytes, int64_t* verif_bytes);
+
+/* Zero-filled draft weights from the speculation stream alone: out[R][C]. */
+int orc_draft_decode(const uint8_t* spec, int64_t spec_len, uint16_t* out);
+
+/* Exact original weights from both streams: out[R][C]. */
+int orc_reconstruct(const uint8_t* spec, int64_t spec_len, const uint8_t* verif,
+                    int64_t verif_len, uint16_t* out);
+
+/* y[t][n] = sum_j f64(W'[n][j]) * f64(x[t][j]), j ascending, where W' is the
+ * draft (verif == NULL) or the exact reconstruction.  absy[t][n] receives
+ * sum_j |W'[n][j]| * |x[t][j]| (the tolerance scale).  x is bf16 [ntok][C]. */
+int orc_product(const uint8_t* spec, int64_t spec_len, const uint8_t* verif,
+                int64_t verif_len, const uint16_t* x, int64_t ntok, double* y,
+                double* absy, int threads);
+
+/* Read header fields: out[0..7] = format, mant_bits, rows, cols, block, keep,
+ * total_bytes, n_sections; sec_off/sec_len receive the 12 section entries. */
+int orc_header(const uint8_t* buf, int64_t len, uint32_t expect_magic, int64_t out[8],
+               int64_t sec_off[12], int64_t sec_len[12]);
+
+#ifdef __cplusplus
+}
+#endif
+#endif
