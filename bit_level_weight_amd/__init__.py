@@ -1,0 +1,234 @@
+"""Python binding of libcassandra (the Cassandra bit-level weight format on
+MI355X).  Argument marshalling only: every step runs in the HIP library.
+
+The functions carry the C names (see include/cassandra.h) and take torch
+tensors for device buffers; PyTorch provides device memory and streams.
+``encode()`` is a convenience wrapper that sizes and allocates the buffers
+with torch and runs the two encoder passes.
+
+Importing this package does not touch the GPU.  Loading the library fails
+loudly when it has not been built (``python -m bit_level_weight_amd.build``).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libcassandra.so")
+
+CASS_OK, CASS_ERR_INVALID, CASS_ERR_UNSUPPORTED, CASS_ERR_OVERFLOW, CASS_ERR_CORRUPT, \
+    CASS_ERR_CAPACITY, CASS_ERR_HIP = range(7)
+CASS_FMT_C1_UNARY, CASS_FMT_C2_MX32 = 1, 2
+MAX_SECTIONS = 12
+
+# symbols include/cassandra.h declares
+EXPORTED = (
+    "cass_encode_ws_bytes", "cass_encode_plan", "cass_encode_tensor", "cass_tensor_describe",
+    "cass_draft_gemv", "cass_verify_gemm", "cass_reconstruct", "cass_draft_decode",
+    "cass_tensor_validate", "cass_status_string", "cass_last_error", "cass_version",
+)
+
+
+class CassParams(ctypes.Structure):
+    _fields_ = [("format", ctypes.c_int32), ("mant_bits", ctypes.c_int32),
+                ("block", ctypes.c_int64), ("keep", ctypes.c_int64)]
+
+
+class CassTensor(ctypes.Structure):
+    _fields_ = [("format", ctypes.c_int32), ("mant_bits", ctypes.c_int32),
+                ("rows", ctypes.c_int64), ("cols", ctypes.c_int64), ("block", ctypes.c_int64),
+                ("keep", ctypes.c_int64),
+                ("spec", ctypes.c_void_p), ("spec_bytes", ctypes.c_int64),
+                ("verif", ctypes.c_void_p), ("verif_bytes", ctypes.c_int64),
+                ("spec_sec", ctypes.c_int64 * MAX_SECTIONS),
+                ("verif_sec", ctypes.c_int64 * MAX_SECTIONS)]
+
+
+class CassPlan(ctypes.Structure):
+    _fields_ = [("rows", ctypes.c_int64), ("cols", ctypes.c_int64), ("p", CassParams),
+                ("spec_bytes", ctypes.c_int64), ("verif_bytes", ctypes.c_int64),
+                ("spec_sec", ctypes.c_int64 * MAX_SECTIONS),
+                ("spec_len", ctypes.c_int64 * MAX_SECTIONS),
+                ("verif_sec", ctypes.c_int64 * MAX_SECTIONS),
+                ("verif_len", ctypes.c_int64 * MAX_SECTIONS),
+                ("hist_kept", ctypes.c_uint64 * 256), ("hist_pruned", ctypes.c_uint64 * 256),
+                ("perm_spec", ctypes.c_uint8 * 256), ("perm_verif", ctypes.c_uint8 * 256),
+                ("spec_code_bits", ctypes.c_uint64), ("verif_code_bits", ctypes.c_uint64),
+                ("resid_bits", ctypes.c_uint64),
+                ("ws", ctypes.c_void_p), ("ws_bytes", ctypes.c_int64)]
+
+
+class CassError(RuntimeError):
+    def __init__(self, status, detail):
+        super().__init__(f"libcassandra status {status}: {detail}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib():
+    """Load libcassandra.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"HIP library missing: {LIB_PATH}; build it with "
+                               "`python -m bit_level_weight_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I64, I32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        L.cass_encode_ws_bytes.argtypes = [I64, I64, ctypes.POINTER(CassParams),
+                                           ctypes.POINTER(I64)]
+        L.cass_encode_plan.argtypes = [P, I64, I64, ctypes.POINTER(CassParams), P, I64, P,
+                                       ctypes.POINTER(CassPlan)]
+        L.cass_encode_tensor.argtypes = [P, ctypes.POINTER(CassPlan), P, I64, P, I64, P,
+                                         ctypes.POINTER(CassTensor)]
+        L.cass_tensor_describe.argtypes = [P, P, I64, P, P, I64, ctypes.POINTER(CassTensor)]
+        L.cass_draft_gemv.argtypes = [ctypes.POINTER(CassTensor), P, I32, I64, P, I64, P]
+        L.cass_verify_gemm.argtypes = [ctypes.POINTER(CassTensor), P, I32, I64, P, I64, P]
+        L.cass_reconstruct.argtypes = [ctypes.POINTER(CassTensor), P, P]
+        L.cass_draft_decode.argtypes = [ctypes.POINTER(CassTensor), P, P]
+        L.cass_tensor_validate.argtypes = [P, I64, P, I64]
+        L.cass_status_string.argtypes = [I32]
+        L.cass_status_string.restype = ctypes.c_char_p
+        L.cass_last_error.argtypes = []
+        L.cass_last_error.restype = ctypes.c_char_p
+        L.cass_version.argtypes = []
+        _lib = L
+    return _lib
+
+
+def _check(status):
+    if status != CASS_OK:
+        raise CassError(status, lib().cass_last_error().decode())
+
+
+def _stream(stream):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _params(fmt, mant_bits, block, keep):
+    return CassParams(int(fmt), int(mant_bits), int(block), int(keep))
+
+
+# ------------------------------------------------------------ C-named calls
+
+
+def cass_encode_ws_bytes(rows, cols, params: CassParams) -> int:
+    n = ctypes.c_int64(0)
+    _check(lib().cass_encode_ws_bytes(rows, cols, ctypes.byref(params), ctypes.byref(n)))
+    return n.value
+
+
+def cass_encode_plan(w, params: CassParams, ws, stream=None) -> CassPlan:
+    rows, cols = w.shape
+    plan = CassPlan()
+    _check(lib().cass_encode_plan(_ptr(w), rows, cols, ctypes.byref(params), _ptr(ws),
+                                  ws.numel() * ws.element_size(), _stream(stream),
+                                  ctypes.byref(plan)))
+    return plan
+
+
+def cass_encode_tensor(w, plan: CassPlan, spec, verif, stream=None) -> CassTensor:
+    t = CassTensor()
+    _check(lib().cass_encode_tensor(_ptr(w), ctypes.byref(plan), _ptr(spec), spec.numel(),
+                                    _ptr(verif), verif.numel(), _stream(stream),
+                                    ctypes.byref(t)))
+    return t
+
+
+def cass_tensor_describe(spec_header: bytes, spec, verif_header: bytes | None = None,
+                         verif=None) -> CassTensor:
+    t = CassTensor()
+    sh = ctypes.create_string_buffer(bytes(spec_header[:256]), 256)
+    vh = ctypes.create_string_buffer(bytes(verif_header[:256]), 256) if verif_header else None
+    _check(lib().cass_tensor_describe(sh, _ptr(spec), spec.numel(), vh, _ptr(verif),
+                                      0 if verif is None else verif.numel(), ctypes.byref(t)))
+    return t
+
+
+def cass_draft_gemv(W: CassTensor, x, y, stream=None):
+    """x: [batch, >=cols] bf16 patterns on the GPU; y: [batch, >=rows] float32."""
+    assert x.dim() == 2 and y.dim() == 2 and x.shape[0] == y.shape[0]
+    _check(lib().cass_draft_gemv(ctypes.byref(W), _ptr(x), x.shape[0], x.stride(0), _ptr(y),
+                                 y.stride(0), _stream(stream)))
+
+
+def cass_verify_gemm(W: CassTensor, X, Y, stream=None):
+    assert X.dim() == 2 and Y.dim() == 2 and X.shape[0] == Y.shape[0]
+    _check(lib().cass_verify_gemm(ctypes.byref(W), _ptr(X), X.shape[0], X.stride(0), _ptr(Y),
+                                  Y.stride(0), _stream(stream)))
+
+
+def cass_reconstruct(W: CassTensor, out, stream=None):
+    _check(lib().cass_reconstruct(ctypes.byref(W), _ptr(out), _stream(stream)))
+
+
+def cass_draft_decode(W: CassTensor, out, stream=None):
+    _check(lib().cass_draft_decode(ctypes.byref(W), _ptr(out), _stream(stream)))
+
+
+def cass_tensor_validate(spec: np.ndarray, verif: np.ndarray | None = None) -> int:
+    spec = np.ascontiguousarray(spec, dtype=np.uint8)
+    vp = None
+    if verif is not None:
+        verif = np.ascontiguousarray(verif, dtype=np.uint8)
+        vp = verif.ctypes.data_as(ctypes.c_void_p)
+    return lib().cass_tensor_validate(spec.ctypes.data_as(ctypes.c_void_p), spec.size, vp,
+                                      0 if verif is None else verif.size)
+
+
+def cass_version() -> int:
+    return lib().cass_version()
+
+
+# ------------------------------------------------------------ convenience
+
+
+class Encoded:
+    """Device buffers of one encoded tensor plus its descriptor."""
+
+    def __init__(self, desc: CassTensor, spec, verif, plan: CassPlan):
+        self.desc, self.spec, self.verif, self.plan = desc, spec, verif, plan
+
+    @property
+    def rows(self):
+        return self.desc.rows
+
+    @property
+    def cols(self):
+        return self.desc.cols
+
+    @property
+    def spec_bytes(self):
+        return self.desc.spec_bytes
+
+    @property
+    def verif_bytes(self):
+        return self.desc.verif_bytes
+
+
+def encode(w, keep: int, mant_bits: int, block: int = 256, fmt: int = CASS_FMT_C1_UNARY,
+           stream=None, ws=None) -> Encoded:
+    """Encode a [rows, cols] bf16-pattern tensor on the GPU (int16/uint16/bfloat16)."""
+    import torch
+    rows, cols = w.shape
+    p = _params(fmt, mant_bits, block, keep)
+    need = cass_encode_ws_bytes(rows, cols, p)
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(need, dtype=torch.uint8, device=w.device)
+    plan = cass_encode_plan(w, p, ws, stream)
+    spec = torch.empty(plan.spec_bytes, dtype=torch.uint8, device=w.device)
+    verif = torch.empty(plan.verif_bytes, dtype=torch.uint8, device=w.device)
+    desc = cass_encode_tensor(w, plan, spec, verif, stream)
+    enc = Encoded(desc, spec, verif, plan)
+    enc._ws = ws  # the workspace must outlive the packing pass
+    return enc

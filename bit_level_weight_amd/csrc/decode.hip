@@ -1,0 +1,107 @@
+// Whole-tensor decoders: exact reconstruction (both streams) and the
+// zero-filled draft (speculation stream only).
+//
+// Method: Cassandra review (marsggbo.github.io), section 3.1 -- the draft
+// loads only speculation data and zero-fills it back to standard floating
+// point; the target loads both streams and reassembles the original
+// losslessly.
+#include "decoders.hpp"
+
+namespace cass {
+
+namespace {
+
+// Decode one block into out[pos0 .. pos0+B): 32 positions per bitmap word,
+// written as four 16-byte stores.
+template <typename Dec>
+__device__ __forceinline__ void decode_block_to(Dec& d, const uint32_t* __restrict__ bitmap,
+                                                int64_t pos0, int64_t B, uint16_t* __restrict__ out) {
+  for (int64_t wi = 0; wi < B / 32; ++wi) {
+    const uint32_t bw = bitmap[pos0 / 32 + wi];
+    uint32_t v[16];
+#pragma unroll
+    for (int j = 0; j < 32; j += 2) {
+      const uint32_t lo = d.next((bw >> j) & 1u, (int)wi);
+      const uint32_t hi = d.next((bw >> (j + 1)) & 1u, (int)wi);
+      v[j / 2] = lo | (hi << 16);
+    }
+    uint4* o = reinterpret_cast<uint4*>(out + pos0 + wi * 32);
+    o[0] = make_uint4(v[0], v[1], v[2], v[3]);
+    o[1] = make_uint4(v[4], v[5], v[6], v[7]);
+    o[2] = make_uint4(v[8], v[9], v[10], v[11]);
+    o[3] = make_uint4(v[12], v[13], v[14], v[15]);
+  }
+}
+
+__global__ void __launch_bounds__(256) k_exact_c1(SpecViewC1 sv, VerifViewC1 vv, Shape sh,
+                                                  uint16_t* __restrict__ out) {
+  const int64_t nb = sh.cols / sh.block, nblk = sh.rows * nb;
+  for (int64_t bi = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; bi < nblk;
+       bi += (int64_t)gridDim.x * blockDim.x) {
+    ExactC1 d;
+    d.init(sv, vv, sh, bi / nb, bi % nb);
+    decode_block_to(d, sv.bitmap, bi * sh.block, sh.block, out);
+  }
+}
+
+__global__ void __launch_bounds__(256) k_draft_c1(SpecViewC1 sv, Shape sh,
+                                                  uint16_t* __restrict__ out) {
+  const int64_t nb = sh.cols / sh.block, nblk = sh.rows * nb;
+  for (int64_t bi = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; bi < nblk;
+       bi += (int64_t)gridDim.x * blockDim.x) {
+    DraftC1 d;
+    d.init(sv, sh, bi / nb, bi % nb);
+    decode_block_to(d, sv.bitmap, bi * sh.block, sh.block, out);
+  }
+}
+
+__global__ void __launch_bounds__(256) k_exact_c2(SpecViewC2 sv, VerifViewC2 vv, Shape sh,
+                                                  uint16_t* __restrict__ out) {
+  const int64_t nb = sh.cols / sh.block, nblk = sh.rows * nb;
+  for (int64_t bi = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; bi < nblk;
+       bi += (int64_t)gridDim.x * blockDim.x) {
+    ExactC2 d;
+    d.init(sv, vv, sh, bi / nb, bi % nb);
+    decode_block_to(d, sv.bitmap, bi * sh.block, sh.block, out);
+  }
+}
+
+__global__ void __launch_bounds__(256) k_draft_c2(SpecViewC2 sv, Shape sh,
+                                                  uint16_t* __restrict__ out) {
+  const int64_t nb = sh.cols / sh.block, nblk = sh.rows * nb;
+  for (int64_t bi = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; bi < nblk;
+       bi += (int64_t)gridDim.x * blockDim.x) {
+    DraftC2 d;
+    d.init(sv, sh, bi / nb, bi % nb);
+    decode_block_to(d, sv.bitmap, bi * sh.block, sh.block, out);
+  }
+}
+
+unsigned grid_blocks(int64_t nblk) {
+  int64_t g = (nblk + 255) / 256;
+  const int64_t cap = (int64_t)device_cu_count() * 8;
+  if (g > cap) g = cap;
+  return (unsigned)(g < 1 ? 1 : g);
+}
+
+}  // namespace
+
+hipError_t launch_decode_c1(const SpecViewC1& sv, const VerifViewC1* vv, const Shape& sh,
+                            uint16_t* out, hipStream_t s) {
+  const int64_t nblk = sh.rows * (sh.cols / sh.block);
+  if (nblk == 0) return hipSuccess;
+  if (vv) k_exact_c1<<<grid_blocks(nblk), 256, 0, s>>>(sv, *vv, sh, out);
+  else k_draft_c1<<<grid_blocks(nblk), 256, 0, s>>>(sv, sh, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_c2(const SpecViewC2& sv, const VerifViewC2* vv, const Shape& sh,
+                            uint16_t* out, hipStream_t s) {
+  const int64_t nblk = sh.rows * (sh.cols / sh.block);
+  if (nblk == 0) return hipSuccess;
+  if (vv) k_exact_c2<<<grid_blocks(nblk), 256, 0, s>>>(sv, *vv, sh, out);
+  else k_draft_c2<<<grid_blocks(nblk), 256, 0, s>>>(sv, sh, out);
+  return hipGetLastError();
+}
+
+}  // namespace cass

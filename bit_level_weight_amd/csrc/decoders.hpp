@@ -1,0 +1,153 @@
+// Per-lane block decoders shared by the reconstruction, draft-decode and
+// verification kernels.  A decoder walks one block of `block` positions of
+// one row, 32 positions (one bitmap word) at a time.
+//
+// Method: Cassandra review (marsggbo.github.io), section 3.1 -- the draft
+// zero-fills the speculation data back to bf16; the target reassembles both
+// streams losslessly.  Section 3.2 -- unary exponent codes are decoded by
+// counting zeros up to the one; Cassandra-2 values share one exponent per 32
+// positions (OCP MX specification).
+#pragma once
+
+#include "bits.hpp"
+#include "internal.hpp"
+
+namespace cass {
+
+// Cassandra-1, both streams -> exact original bf16 patterns.
+struct ExactC1 {
+  BitReader fr, er, lr, vr;
+  const uint8_t* perm_s;
+  const uint8_t* perm_v;
+  const uint8_t* pruned;
+  int64_t pidx;
+  int m;
+
+  __device__ __forceinline__ void init(const SpecViewC1& sv, const VerifViewC1& vv,
+                                       const Shape& sh, int64_t row, int64_t b) {
+    const int64_t nb = sh.cols / sh.block;
+    const int64_t bi = row * nb + b;
+    m = sh.mant;
+    const uint32_t kb = sv.keptb[bi];
+    const uint64_t kin0 = (uint64_t)row * sh.keep + kb;
+    fr.init(sv.fields, kin0 * (uint64_t)(1 + m));
+    er.init(sv.codes, sv.rowbase[row] + sv.blkoff[bi]);
+    lr.init(vv.lowmant, kin0 * (uint64_t)(7 - m));
+    vr.init(vv.codes, vv.rowbase[row] + vv.blkoff[bi]);
+    perm_s = sv.perm;
+    perm_v = vv.perm;
+    pruned = vv.pruned;
+    pidx = row * (sh.cols - sh.keep) + b * sh.block - kb;
+  }
+  // one position; kept = its bitmap bit
+  __device__ __forceinline__ uint32_t next(uint32_t kept, int /*word*/) {
+    if (kept) {
+      const uint32_t f = fr.take(1 + m);
+      const int r = er.unary();
+      const uint32_t low = lr.take(7 - m);
+      const uint32_t e = perm_s[r];
+      return ((f >> m) << 15) | (e << 7) | ((f & ((1u << m) - 1)) << (7 - m)) | low;
+    }
+    const uint32_t byte = pruned[pidx++];
+    const uint32_t e = perm_v[vr.unary()];
+    return ((byte >> 7) << 15) | (e << 7) | (byte & 0x7F);
+  }
+};
+
+// Cassandra-1 speculation stream -> zero-filled draft.
+struct DraftC1 {
+  BitReader fr, er;
+  const uint8_t* perm_s;
+  int m;
+  __device__ __forceinline__ void init(const SpecViewC1& sv, const Shape& sh, int64_t row,
+                                       int64_t b) {
+    const int64_t nb = sh.cols / sh.block;
+    const int64_t bi = row * nb + b;
+    m = sh.mant;
+    const uint32_t kb = sv.keptb[bi];
+    fr.init(sv.fields, ((uint64_t)row * sh.keep + kb) * (uint64_t)(1 + m));
+    er.init(sv.codes, sv.rowbase[row] + sv.blkoff[bi]);
+    perm_s = sv.perm;
+  }
+  __device__ __forceinline__ uint32_t next(uint32_t kept, int /*word*/) {
+    if (!kept) return 0u;
+    const uint32_t f = fr.take(1 + m);
+    const uint32_t e = perm_s[er.unary()];
+    return ((f >> m) << 15) | (e << 7) | ((f & ((1u << m) - 1)) << (7 - m));
+  }
+};
+
+// bf16 pattern of sign * a * 2^(E-127-m): normalise the (m+1)-bit significand.
+__device__ __forceinline__ uint32_t mx_value_bits(uint32_t s, uint32_t a, int E, int m) {
+  if (a == 0) return 0u;
+  const int p = 31 - __builtin_clz(a);
+  const int e = E - m + p;
+  if (e >= 1) return (s << 15) | ((uint32_t)e << 7) | ((a << (7 - p)) & 0x7F);
+  return (s << 15) | (a << (E - m + 6));
+}
+
+// Cassandra-2 speculation stream -> zero-filled (MX-truncated) draft.
+struct DraftC2 {
+  BitReader fr;
+  const uint8_t* shexp;
+  int64_t g0;
+  int m;
+  __device__ __forceinline__ void init(const SpecViewC2& sv, const Shape& sh, int64_t row,
+                                       int64_t b) {
+    const int64_t nb = sh.cols / sh.block;
+    const int64_t bi = row * nb + b;
+    m = sh.mant;
+    const uint32_t kb = sv.keptb[bi];
+    fr.init(sv.fields, ((uint64_t)row * sh.keep + kb) * (uint64_t)(2 + m));
+    shexp = sv.shexp;
+    g0 = bi * sh.block / 32;
+  }
+  __device__ __forceinline__ uint32_t next(uint32_t kept, int word) {
+    if (!kept) return 0u;
+    const uint32_t f = fr.take(2 + m);
+    return mx_value_bits(f >> (m + 1), f & ((2u << m) - 1), shexp[g0 + word], m);
+  }
+};
+
+// Cassandra-2, both streams -> exact original bf16 patterns.
+struct ExactC2 {
+  BitReader fr, kr, vr;
+  const uint8_t* shexp;
+  const uint8_t* perm_v;
+  const uint8_t* pruned;
+  int64_t g0, pidx;
+  int m;
+  __device__ __forceinline__ void init(const SpecViewC2& sv, const VerifViewC2& vv,
+                                       const Shape& sh, int64_t row, int64_t b) {
+    const int64_t nb = sh.cols / sh.block;
+    const int64_t bi = row * nb + b;
+    m = sh.mant;
+    const uint32_t kb = sv.keptb[bi];
+    fr.init(sv.fields, ((uint64_t)row * sh.keep + kb) * (uint64_t)(2 + m));
+    kr.init(vv.resid, vv.rowbase_k[row] + vv.blkoff_k[bi]);
+    vr.init(vv.codes, vv.rowbase_p[row] + vv.blkoff_p[bi]);
+    shexp = sv.shexp;
+    perm_v = vv.perm;
+    pruned = vv.pruned;
+    g0 = bi * sh.block / 32;
+    pidx = row * (sh.cols - sh.keep) + b * sh.block - kb;
+  }
+  __device__ __forceinline__ uint32_t next(uint32_t kept, int word) {
+    if (kept) {
+      const uint32_t f = fr.take(2 + m);
+      const uint32_t s = f >> (m + 1), a = f & ((2u << m) - 1);
+      const int d = kr.unary();
+      const int wd = (7 - m + d < 8) ? 7 - m + d : 8;
+      const uint32_t L = kr.take(wd);
+      const uint32_t M = (wd < 8) ? ((a << wd) | L) : L;
+      const int E = shexp[g0 + word];
+      const uint32_t e = (M >= 128u) ? (uint32_t)(E - d) : 0u;
+      return (s << 15) | ((e & 0xFF) << 7) | (M & 0x7F);
+    }
+    const uint32_t byte = pruned[pidx++];
+    const uint32_t e = perm_v[vr.unary()];
+    return ((byte >> 7) << 15) | (e << 7) | (byte & 0x7F);
+  }
+};
+
+}  // namespace cass

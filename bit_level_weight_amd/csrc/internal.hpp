@@ -1,0 +1,127 @@
+// Internal declarations shared by the library's translation units.
+// Stream layout: see include/cassandra.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/cassandra.h"
+
+namespace cass {
+
+constexpr int kHeaderBytes = 256;
+constexpr uint32_t kMagicSpec = 0x50535343u;   // "CSSP"
+constexpr uint32_t kMagicVerif = 0x46565343u;  // "CSVF"
+
+// Section indices of each stream.
+enum SpecC1 { S1_RANK = 0, S1_BITMAP, S1_ROWBASE, S1_BLKOFF, S1_KEPTB, S1_FIELDS, S1_CODES, S1_COUNT };
+enum VerifC1 { V1_RANK = 0, V1_ROWBASE, V1_BLKOFF, V1_LOWMANT, V1_PRUNED, V1_CODES, V1_COUNT };
+enum SpecC2 { S2_BITMAP = 0, S2_SHEXP, S2_KEPTB, S2_FIELDS, S2_COUNT };
+enum VerifC2 { V2_RANK = 0, V2_ROWBASE_K, V2_BLKOFF_K, V2_RESID, V2_PRUNED, V2_ROWBASE_P,
+               V2_BLKOFF_P, V2_CODES, V2_COUNT };
+
+// Tables passed to kernels by value.
+struct RankTables {
+  uint8_t rank_kept[256];    // exponent -> rank, speculation codes (C-1)
+  uint8_t rank_pruned[256];  // exponent -> rank, verification codes
+};
+
+struct HeaderBlob {
+  uint8_t spec_hdr[kHeaderBytes];
+  uint8_t verif_hdr[kHeaderBytes];
+  uint8_t perm_spec[256];
+  uint8_t perm_verif[256];
+};
+
+// Workspace carve-up of cass_encode_plan / cass_encode_tensor.
+struct Workspace {
+  uint32_t* bitmap;      // rows*cols/32 keep words
+  uint8_t* shexp;        // rows*cols/32 shared exponents (C-2)
+  unsigned long long* hist;  // [2][256]: kept, pruned
+  uint32_t* blk_a;       // per block: C-1 spec code bits / C-2 residue bits
+  uint32_t* blk_v;       // per block: pruned code bits
+  uint32_t* blk_kept;    // per block: kept count
+  uint32_t* off_a;       // per block: exclusive prefix of blk_a within the row
+  uint32_t* off_v;
+  uint16_t* keptb;       // per block: kept-before count
+  unsigned long long* row_a;  // per row: totals, then (after scan) bases
+  unsigned long long* row_v;
+  unsigned long long* totals; // [2]
+  int64_t bytes;
+};
+
+Workspace carve_workspace(void* base, int64_t rows, int64_t cols, int64_t block);
+
+// Device views of the sections a kernel reads.
+struct SpecViewC1 {
+  const uint8_t* perm;       // rank -> exponent
+  const uint32_t* bitmap;
+  const unsigned long long* rowbase;
+  const uint32_t* blkoff;
+  const uint16_t* keptb;
+  const uint32_t* fields;
+  const uint32_t* codes;
+};
+struct VerifViewC1 {
+  const uint8_t* perm;
+  const unsigned long long* rowbase;
+  const uint32_t* blkoff;
+  const uint32_t* lowmant;
+  const uint8_t* pruned;
+  const uint32_t* codes;
+};
+struct SpecViewC2 {
+  const uint32_t* bitmap;
+  const uint8_t* shexp;
+  const uint16_t* keptb;
+  const uint32_t* fields;
+};
+struct VerifViewC2 {
+  const uint8_t* perm;
+  const unsigned long long* rowbase_k;
+  const uint32_t* blkoff_k;
+  const uint32_t* resid;
+  const uint8_t* pruned;
+  const unsigned long long* rowbase_p;
+  const uint32_t* blkoff_p;
+  const uint32_t* codes;
+};
+
+struct Shape {
+  int64_t rows, cols, block, keep;
+  int mant;
+};
+
+// ---- launchers (return hipSuccess or the launch error) ----
+hipError_t launch_fill_zero(void* p, int64_t bytes, hipStream_t s);
+hipError_t launch_select(const uint16_t* w, const Shape& sh, uint32_t* bitmap, hipStream_t s);
+hipError_t launch_histograms(const uint16_t* w, const Shape& sh, int format, const Workspace& ws,
+                             hipStream_t s);
+hipError_t launch_block_bits(const uint16_t* w, const Shape& sh, int format, const Workspace& ws,
+                             const RankTables& rt, hipStream_t s);
+hipError_t launch_row_scan(const Shape& sh, const Workspace& ws, hipStream_t s);
+hipError_t launch_rows_scan(const Shape& sh, const Workspace& ws, hipStream_t s);
+hipError_t launch_write_headers(const HeaderBlob& hb, uint8_t* spec, int64_t spec_rank_off,
+                                uint8_t* verif, int64_t verif_rank_off, hipStream_t s);
+hipError_t launch_pack(const uint16_t* w, const Shape& sh, int format, const Workspace& ws,
+                       const RankTables& rt, uint8_t* spec, const int64_t* spec_sec,
+                       uint8_t* verif, const int64_t* verif_sec, hipStream_t s);
+
+hipError_t launch_draft_gemv_c1(const SpecViewC1& v, const Shape& sh, const uint16_t* x,
+                                int batch, int64_t ldx, float* y, int64_t ldy, hipStream_t s);
+hipError_t launch_draft_gemv_c2(const SpecViewC2& v, const Shape& sh, const uint16_t* x,
+                                int batch, int64_t ldx, float* y, int64_t ldy, hipStream_t s);
+hipError_t launch_decode_c1(const SpecViewC1& sv, const VerifViewC1* vv, const Shape& sh,
+                            uint16_t* out, hipStream_t s);
+hipError_t launch_decode_c2(const SpecViewC2& sv, const VerifViewC2* vv, const Shape& sh,
+                            uint16_t* out, hipStream_t s);
+hipError_t launch_verify_gemm_c1(const SpecViewC1& sv, const VerifViewC1& vv, const Shape& sh,
+                                 const uint16_t* X, int ntok, int64_t ldx, float* Y,
+                                 int64_t ldy, hipStream_t s);
+hipError_t launch_verify_gemm_c2(const SpecViewC2& sv, const VerifViewC2& vv, const Shape& sh,
+                                 const uint16_t* X, int ntok, int64_t ldx, float* Y,
+                                 int64_t ldy, hipStream_t s);
+
+int device_cu_count();
+
+}  // namespace cass

@@ -1,0 +1,188 @@
+/*
+ * libcassandra -- the Cassandra bit-level weight format on AMD Instinct MI355X
+ * (gfx950): encoder, draft GEMV, verification GEMM and exact reconstruction.
+ *
+ * The method (Cassandra review, marsggbo.github.io, section 3.1): each bf16
+ * tensor goes through unstructured value pruning (keep the most salient values
+ * of a group), mantissa truncation of the kept values and exponent
+ * compression, and is split into a speculation stream -- all the draft model
+ * loads, zero-filled back to bf16 -- and a verification stream, which together
+ * with the speculation stream rebuilds the original bits exactly.  Exponent
+ * coding (same page, section 3.2): Cassandra-1 gives frequent exponents short
+ * unary codes (decoding counts zeros up to the one), Cassandra-2 shares one
+ * MX exponent per 32 values (OCP Microscaling spec, cited by the paper).
+ *
+ * Conventions for every call:
+ *  - All tensor data lives in device memory owned by the caller; the library
+ *    never allocates device memory and keeps no state besides its code object
+ *    and a thread-local error string.
+ *  - bf16 data is passed as its 16-bit patterns (uint16_t).  Products are fp32.
+ *  - Matrices are row-major; a weight matrix W is [rows = out features][cols =
+ *    in features]; the pruning group is one row.
+ *  - Kernels run on the caller's stream; only cass_encode_plan synchronises it.
+ *  - Argument errors are returned before anything is launched; a launch
+ *    failure returns CASS_ERR_HIP.  cass_last_error() gives the detail.
+ *
+ * Stream layout (both streams): a 256-byte header (u32 magic, u32 version=1,
+ * u32 format, u32 mant_bits, i64 rows, cols, block, keep, total_bytes, u32
+ * n_sections, u32 0, then 12 x {i64 offset, i64 bytes}) followed by the
+ * sections, each starting on a multiple of 256 bytes and followed by at least
+ * 16 zero bytes.  Bit sections are little-endian: bit i is bit (i & 31) of
+ * 32-bit word i >> 5.
+ *
+ *  Cassandra-1 speculation sections: 0 rank table (256 B, exponent of rank r),
+ *   1 keep bitmap (rows*cols bits), 2 row bases (u64 per row: first code bit
+ *   of the row in section 6), 3 block offsets (u32 per block of `block`
+ *   positions, code bits relative to the row base), 4 kept-before counts
+ *   (u16 per block), 5 sign+top-m mantissa fields ((s<<m)|ft, 1+m bits per
+ *   kept value, value i of row r at bit (r*keep+i)*(1+m)), 6 exponent codes
+ *   (rank r -> r zero bits then a one bit; kept values in row-major order).
+ *  Cassandra-1 verification sections: 0 rank table of pruned exponents,
+ *   1 row bases, 2 block offsets (for section 5), 3 low mantissa bits of kept
+ *   values (7-m bits each), 4 pruned values' (s<<7)|mantissa bytes, 5 pruned
+ *   exponent codes.
+ *  Cassandra-2 speculation sections: 0 keep bitmap, 1 shared exponent (u8 per
+ *   32 positions: the largest max(e,1) over the kept values, 0 if none),
+ *   2 kept-before counts, 3 fields ((s<<(m+1))|a, m+2 bits, a = the value's
+ *   significand aligned to the shared exponent and cut to m+1 bits).
+ *  Cassandra-2 verification sections: 0 pruned rank table, 1 residue row
+ *   bases, 2 residue block offsets, 3 kept residues (unary(d) then the
+ *   min(8, 7-m+d) bits the draft dropped, d = shared - own exponent),
+ *   4 pruned bytes, 5 pruned-code row bases, 6 pruned-code block offsets,
+ *   7 pruned exponent codes.
+ */
+#ifndef CASSANDRA_H
+#define CASSANDRA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CASS_VERSION 1
+
+enum cass_status {
+  CASS_OK = 0,
+  CASS_ERR_INVALID = 1,     /* bad argument, shape or descriptor */
+  CASS_ERR_UNSUPPORTED = 2, /* valid but not implemented here (e.g. batch > 8) */
+  CASS_ERR_OVERFLOW = 3,    /* a size or offset does not fit its field */
+  CASS_ERR_CORRUPT = 4,     /* a stream fails validation */
+  CASS_ERR_CAPACITY = 5,    /* a caller buffer is too small */
+  CASS_ERR_HIP = 6          /* a HIP runtime call or launch failed */
+};
+
+enum cass_format { CASS_FMT_C1_UNARY = 1, CASS_FMT_C2_MX32 = 2 };
+
+#define CASS_MAX_SECTIONS 12
+
+/* Encoding parameters.  keep = values kept per row (the pages' keep ratio
+ * times cols, chosen by the caller); mant_bits = mantissa bits kept, 0..7;
+ * block = positions per offset block, a power of two >= 32 dividing cols. */
+typedef struct cass_params {
+  int32_t format;
+  int32_t mant_bits;
+  int64_t block;
+  int64_t keep;
+} cass_params;
+
+/* Descriptor of an encoded tensor: a plain host struct pointing at the
+ * caller's device buffers.  Filled by cass_encode_tensor or by
+ * cass_tensor_describe from the two stream headers. */
+typedef struct cass_tensor {
+  int32_t format;
+  int32_t mant_bits;
+  int64_t rows, cols, block, keep;
+  const void* spec;   /* device, spec_bytes long */
+  int64_t spec_bytes;
+  const void* verif;  /* device, or NULL when only the draft is needed */
+  int64_t verif_bytes;
+  int64_t spec_sec[CASS_MAX_SECTIONS];  /* byte offsets of the sections */
+  int64_t verif_sec[CASS_MAX_SECTIONS];
+} cass_tensor;
+
+/* Result of the planning pass of the encoder (host struct). */
+typedef struct cass_plan {
+  int64_t rows, cols;
+  cass_params p;
+  int64_t spec_bytes, verif_bytes;      /* buffer sizes cass_encode_tensor needs */
+  int64_t spec_sec[CASS_MAX_SECTIONS], spec_len[CASS_MAX_SECTIONS];
+  int64_t verif_sec[CASS_MAX_SECTIONS], verif_len[CASS_MAX_SECTIONS];
+  uint64_t hist_kept[256], hist_pruned[256]; /* exponent histograms */
+  uint8_t perm_spec[256], perm_verif[256];   /* rank -> exponent tables */
+  uint64_t spec_code_bits, verif_code_bits, resid_bits;
+  const void* ws;                       /* workspace the plan was made in */
+  int64_t ws_bytes;
+} cass_plan;
+
+/* Workspace bytes cass_encode_plan needs for a rows x cols tensor. */
+int cass_encode_ws_bytes(int64_t rows, int64_t cols, const cass_params* p, int64_t* ws_bytes);
+
+/* Planning pass of the encoder (section 3.1 steps one to three): per-row
+ * top-`keep` selection by |w| with ties to the lower column, exponent
+ * histograms of kept and pruned values, frequency-ranked tables (count
+ * descending, exponent ascending), code lengths and offsets.  w: device
+ * [rows][cols] bf16 patterns (row stride cols).  ws: device workspace of
+ * ws_bytes >= cass_encode_ws_bytes(); it holds intermediate results that
+ * cass_encode_tensor reads, so it must stay untouched in between.
+ * Synchronises `stream` twice (histograms, sizes).  rows may be 0. */
+int cass_encode_plan(const uint16_t* w, int64_t rows, int64_t cols, const cass_params* p,
+                     void* ws, int64_t ws_bytes, hipStream_t stream, cass_plan* plan);
+
+/* Packing pass: writes both streams, byte for byte the canonical encoding, to
+ * the device buffers spec (>= plan->spec_bytes) and verif (>= plan->
+ * verif_bytes), and fills *out.  w and ws must be those given to the plan.
+ * Asynchronous. */
+int cass_encode_tensor(const uint16_t* w, const cass_plan* plan, void* spec, int64_t spec_cap,
+                       void* verif, int64_t verif_cap, hipStream_t stream, cass_tensor* out);
+
+/* Build a descriptor from host copies of the two 256-byte stream headers and
+ * the device buffers holding the streams (verif may be NULL). */
+int cass_tensor_describe(const void* spec_header, const void* spec, int64_t spec_bytes,
+                         const void* verif_header, const void* verif, int64_t verif_bytes,
+                         cass_tensor* out);
+
+/* Draft GEMV (section 3.1: the draft runs the full-size product on the
+ * zero-filled speculation data): y[b][n] = sum_j Wdraft[n][j] * x[b][j] for
+ * b < batch, accumulated in fp32.  x: device bf16 [batch][ldx], ldx >= cols;
+ * y: device fp32 [batch][ldy], ldy >= rows.  batch 1..8.  Reads only the
+ * speculation stream.  Asynchronous. */
+int cass_draft_gemv(const cass_tensor* W, const uint16_t* x, int batch, int64_t ldx,
+                    float* y, int64_t ldy, hipStream_t stream);
+
+/* Verification GEMM for the k+1 drafted tokens (Cassandra review, section 1:
+ * the target verifies the drafted tokens in parallel; section 3.1: it loads
+ * both streams and reassembles the weights losslessly):
+ * Y[t][n] = sum_j W[n][j] * X[t][j], t < ntok, W the exact original weights,
+ * fp32 accumulation.  X: device bf16 [ntok][ldx]; Y: device fp32 [ntok][ldy].
+ * ntok 1..16.  Needs W->verif.  Asynchronous. */
+int cass_verify_gemm(const cass_tensor* W, const uint16_t* X, int ntok, int64_t ldx,
+                     float* Y, int64_t ldy, hipStream_t stream);
+
+/* Exact reconstruction of the original bf16 patterns from both streams:
+ * out: device [rows][cols].  Asynchronous. */
+int cass_reconstruct(const cass_tensor* W, uint16_t* out, hipStream_t stream);
+
+/* Zero-filled draft weights from the speculation stream alone: out: device
+ * [rows][cols] bf16 patterns.  Asynchronous. */
+int cass_draft_decode(const cass_tensor* W, uint16_t* out, hipStream_t stream);
+
+/* Host-only structural validation of a stream pair held in host memory
+ * (verif may be NULL): header fields, section bounds, bitmap counts, the
+ * kept-before counts and that every row base and block offset lands on a code
+ * boundary.  Returns CASS_OK or CASS_ERR_CORRUPT.  Touches no GPU. */
+int cass_tensor_validate(const void* spec, int64_t spec_bytes, const void* verif,
+                         int64_t verif_bytes);
+
+const char* cass_status_string(int status);
+/* Detail of the last error on the calling thread ("" if none). */
+const char* cass_last_error(void);
+int cass_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

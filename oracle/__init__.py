@@ -59,6 +59,7 @@ def lib():
         L.orc_draft_decode.argtypes = [P, I64, P]
         L.orc_reconstruct.argtypes = [P, I64, P, I64, P]
         L.orc_product.argtypes = [P, I64, P, I64, P, I64, P, P, ctypes.c_int]
+        L.orc_product_rows.argtypes = [P, I64, P, I64, P, I64, P, I64, P, P]
         L.orc_header.argtypes = [P, I64, ctypes.c_uint32, P, P, P]
         _lib = L
     return _lib
@@ -163,4 +164,20 @@ def product(spec, x, verif=None, threads: int = 1):
     _check(lib().orc_product(_p(spec), spec.size, _p(verif),
                              0 if verif is None else verif.size, _p(x), ntok, _p(y),
                              _p(absy), threads), "product")
+    return y, absy
+
+
+def product_rows(spec, x, rows, verif=None):
+    """orc_product for the listed rows only -> (y, absy), shape [ntok, len(rows)]."""
+    spec = np.ascontiguousarray(spec, dtype=np.uint8)
+    x = _u16(np.atleast_2d(x))
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    ntok = x.shape[0]
+    y = np.zeros((ntok, rows.size), dtype=np.float64)
+    absy = np.zeros_like(y)
+    if verif is not None:
+        verif = np.ascontiguousarray(verif, dtype=np.uint8)
+    _check(lib().orc_product_rows(_p(spec), spec.size, _p(verif),
+                                  0 if verif is None else verif.size, _p(x), ntok, _p(rows),
+                                  rows.size, _p(y), _p(absy)), "product_rows")
     return y, absy

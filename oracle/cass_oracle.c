@@ -213,7 +213,10 @@ int orc_header(const uint8_t* buf, int64_t len, uint32_t expect_magic, int64_t o
   return ORC_OK;
 }
 
-/* lay sections out back to back after the header, each 256-aligned */
+/* Lay sections out in order after the header.  Each starts on a multiple of
+ * 256 bytes and is followed by at least 16 zero bytes before the next one (or
+ * the end of the stream), so that a reader fetching whole words past the last
+ * bit of a section stays inside the stream. */
 static int64_t layout(hdr_t* h, int nsec, const int64_t* lens) {
   int64_t pos = HDR_BYTES;
   h->nsec = (uint32_t)nsec;
@@ -221,7 +224,7 @@ static int64_t layout(hdr_t* h, int nsec, const int64_t* lens) {
   for (int s = 0; s < nsec; s++) {
     h->off[s] = pos;
     h->len[s] = lens[s];
-    pos = align256(pos + lens[s]);
+    pos = align256(pos + lens[s] + 16);
   }
   h->total = pos;
   return pos;
@@ -617,4 +620,35 @@ int orc_product(const uint8_t* spec, int64_t spec_len, const uint8_t* verif,
     free(row);
   }
   return bad ? ORC_ERR_CORRUPT : ORC_OK;
+}
+
+/* The same product restricted to the listed rows: y[t][i] and absy[t][i] for
+ * row rows[i] (used to check single outputs of very large tensors). */
+int orc_product_rows(const uint8_t* spec, int64_t spec_len, const uint8_t* verif,
+                     int64_t verif_len, const uint16_t* x, int64_t ntok, const int64_t* rows,
+                     int64_t nrows, double* y, double* absy) {
+  hdr_t hs, hv;
+  int st = open_pair(spec, spec_len, verif, verif_len, &hs, &hv);
+  if (st) return st;
+  const int64_t C = hs.C;
+  uint16_t* row = (uint16_t*)malloc((size_t)C * sizeof(uint16_t));
+  if (!row) return ORC_ERR_CAPACITY;
+  for (int64_t i = 0; i < nrows; i++) {
+    if (rows[i] < 0 || rows[i] >= hs.R) { free(row); return ORC_ERR_INVALID; }
+    st = decode_row(spec, &hs, verif, verif ? &hv : NULL, rows[i], row);
+    if (st) { free(row); return st; }
+    for (int64_t t = 0; t < ntok; t++) {
+      double acc = 0.0, aacc = 0.0;
+      for (int64_t j = 0; j < C; j++) {
+        double wv = bf16_to_double(row[j]);
+        double xv = bf16_to_double(x[t * C + j]);
+        acc += wv * xv;
+        aacc += fabs(wv) * fabs(xv);
+      }
+      y[t * nrows + i] = acc;
+      absy[t * nrows + i] = aacc;
+    }
+  }
+  free(row);
+  return ORC_OK;
 }

@@ -72,6 +72,11 @@ int orc_product(const uint8_t* spec, int64_t spec_len, const uint8_t* verif,
                 int64_t verif_len, const uint16_t* x, int64_t ntok, double* y,
                 double* absy, int threads);
 
+/* orc_product for the listed rows only: y[t][i], absy[t][i] belong to rows[i]. */
+int orc_product_rows(const uint8_t* spec, int64_t spec_len, const uint8_t* verif,
+                     int64_t verif_len, const uint16_t* x, int64_t ntok, const int64_t* rows,
+                     int64_t nrows, double* y, double* absy);
+
 /* Read header fields: out[0..7] = format, mant_bits, rows, cols, block, keep,
  * total_bytes, n_sections; sec_off/sec_len receive the 12 section entries. */
 int orc_header(const uint8_t* buf, int64_t len, uint32_t expect_magic, int64_t out[8],

@@ -1,0 +1,120 @@
+"""Host-only checks of the C-ABI library: it loads, exports every symbol the
+public header declares, rejects bad arguments before launching anything, and
+its host-side stream validator accepts canonical streams and rejects corrupted
+ones.  No GPU is touched."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def cass():
+    import bit_level_weight_amd as b
+    if not os.path.exists(b.LIB_PATH):
+        pytest.fail("libcassandra.so is not built (python -m bit_level_weight_amd.build)")
+    b.lib()
+    return b
+
+
+def declared_symbols():
+    names = set()
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", fn)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names |= set(re.findall(r"\b(cass_\w+)\s*\(", text))
+    return names
+
+
+def test_exports_every_declared_symbol(cass):
+    names = declared_symbols()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(cass.lib(), n), n
+    assert set(cass.EXPORTED) == names
+
+
+def test_version_and_status_strings(cass):
+    L = cass.lib()
+    assert L.cass_version() == 1
+    assert L.cass_status_string(0) == b"ok"
+    assert L.cass_status_string(4) == b"corrupt stream"
+
+
+def test_ws_bytes_and_argument_errors(cass):
+    L = cass.lib()
+    p = cass.CassParams(1, 3, 256, 1229)
+    n = ctypes.c_int64(0)
+    assert L.cass_encode_ws_bytes(4096, 4096, ctypes.byref(p), ctypes.byref(n)) == 0
+    assert n.value >= 4096 * 4096 // 8
+    for bad in [cass.CassParams(3, 3, 256, 10), cass.CassParams(1, 8, 256, 10),
+                cass.CassParams(1, 3, 100, 10), cass.CassParams(1, 3, 256, 5000),
+                cass.CassParams(1, 3, 16, 10)]:
+        assert L.cass_encode_ws_bytes(16, 4096, ctypes.byref(bad), ctypes.byref(n)) == \
+            cass.CASS_ERR_INVALID
+    assert L.cass_encode_ws_bytes(16, 131072, ctypes.byref(p), ctypes.byref(n)) == \
+        cass.CASS_ERR_UNSUPPORTED
+    # descriptor checks happen before any launch
+    t = cass.CassTensor()
+    assert L.cass_draft_gemv(None, None, 1, 0, None, 0, None) == cass.CASS_ERR_INVALID
+    t.format, t.mant_bits, t.rows, t.cols, t.block, t.keep = 1, 3, 4, 256, 256, 77
+    assert L.cass_draft_gemv(ctypes.byref(t), None, 1, 256, None, 4, None) == cass.CASS_ERR_INVALID
+    assert L.cass_reconstruct(ctypes.byref(t), None, None) == cass.CASS_ERR_INVALID
+
+
+@pytest.mark.parametrize("fmt", [1, 2])
+def test_host_validator_on_oracle_streams(cass, orc, fmt):
+    w = synth.weight(24, 1024, 7, outlier_frac=0.01)
+    for k, m in [(307, 3), (0, 0), (1024, 7), (512, 2)]:
+        spec, verif = orc.encode(w, k, m, block=256, fmt=fmt)
+        assert cass.cass_tensor_validate(spec, verif) == cass.CASS_OK
+        assert cass.cass_tensor_validate(spec) == cass.CASS_OK
+    spec, verif = orc.encode(w, 307, 3, fmt=fmt)
+    rng = np.random.default_rng(0)
+    # flipping any header byte that matters, or an offset/count, is caught
+    for pos in [0, 4, 8, 16, 24, 40, 48, 64, 72]:
+        bad = spec.copy(); bad[pos] ^= 0x01
+        assert cass.cass_tensor_validate(bad, verif) == cass.CASS_ERR_CORRUPT, pos
+    h = orc.header(spec)
+    kb_sec = 4 if fmt == 1 else 2
+    off, n = h["sections"][kb_sec]
+    for _ in range(5):
+        bad = spec.copy()
+        bad[off + int(rng.integers(0, n))] ^= 0x04
+        assert cass.cass_tensor_validate(bad, verif) == cass.CASS_ERR_CORRUPT
+    if fmt == 1:
+        off, n = h["sections"][3]  # block offsets
+        bad = spec.copy(); bad[off + 8] ^= 0x02
+        assert cass.cass_tensor_validate(bad, verif) == cass.CASS_ERR_CORRUPT
+    hv = orc.header(verif, orc.MAGIC_VERIF)
+    off, n = hv["sections"][1]  # verification row bases
+    bad = verif.copy(); bad[off + 8] ^= 0x10
+    assert cass.cass_tensor_validate(spec, bad) == cass.CASS_ERR_CORRUPT
+    assert cass.cass_tensor_validate(spec[:200]) == cass.CASS_ERR_CORRUPT
+
+
+def test_describe_from_headers(cass, orc):
+    w = synth.weight(8, 512, 3)
+    spec, verif = orc.encode(w, 150, 3)
+
+    class FakeDev:  # describe only reads the host headers and records pointers
+        def __init__(self, n):
+            self.n = n
+        def numel(self):
+            return self.n
+        def data_ptr(self):
+            return 0x100000
+    t = cass.cass_tensor_describe(spec.tobytes(), FakeDev(spec.size), verif.tobytes(),
+                                  FakeDev(verif.size))
+    h = orc.header(spec)
+    assert (t.rows, t.cols, t.keep, t.mant_bits, t.block) == (8, 512, 150, 3, 256)
+    assert [t.spec_sec[i] for i in range(7)] == [o for o, _ in h["sections"]]
+    with pytest.raises(cass.CassError):
+        cass.cass_tensor_describe(verif.tobytes(), FakeDev(verif.size))

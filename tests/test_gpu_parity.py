@@ -1,0 +1,228 @@
+"""GPU parity: the HIP library against the CPU oracle, through the C ABI.
+
+  * encoded streams: byte for byte;
+  * draft decode and reconstruction: bit for bit;
+  * draft GEMV and verification GEMM (fp32 accumulation) against the oracle's
+    fp64 products: |y - y_ref| <= 1e-3 * sum_j |W'[n][j]| |x[j]| per element.
+Inputs are the seeded synthetic tensors of the workloads.
+"""
+import numpy as np
+import pytest
+
+import synth
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-3
+
+
+@pytest.fixture(scope="module")
+def gpu():
+    import torch
+    import bit_level_weight_amd as cass
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    cass.lib()
+    return torch, cass
+
+
+def dev(torch, a):
+    a = np.ascontiguousarray(a, dtype=np.uint16)
+    return torch.from_numpy(a.view(np.int16)).cuda()
+
+
+def host_u8(t):
+    return t.cpu().numpy().view(np.uint8)
+
+
+def host_u16(t):
+    return t.cpu().numpy().view(np.uint16)
+
+
+def check_product(y_gpu, y_ref, absy):
+    err = np.abs(y_gpu.astype(np.float64) - y_ref)
+    bound = TOL * absy
+    bad = err > bound
+    assert not bad.any(), (f"{bad.sum()} outputs outside tolerance; worst ratio "
+                           f"{(err / np.maximum(bound, 1e-300)).max():.3g}")
+
+
+CASES = [
+    # rows, cols, keep, mant, block, format
+    (1024, 1024, 512, 3, 256, 1),   # the small worked configuration
+    (37, 4096, 1229, 3, 256, 1),    # ragged row count, keep 0.3
+    (64, 14336, 4301, 2, 256, 1),   # long rows
+    (5, 1024, 0, 3, 256, 1),        # keep nothing
+    (5, 1024, 1024, 7, 256, 1),     # keep everything, full mantissa
+    (16, 512, 205, 0, 32, 1),       # sign only, smallest block
+    (16, 512, 205, 7, 64, 1),
+    (1, 32, 1, 4, 32, 1),           # single word
+    (1024, 2560, 768, 3, 256, 2),   # Cassandra-2
+    (33, 1024, 307, 0, 256, 2),
+    (8, 512, 512, 7, 256, 2),
+    (7, 1024, 0, 5, 128, 2),
+]
+
+
+def make_w(R, C, seed):
+    w = synth.weight(R, C, seed, outlier_frac=0.01)
+    if R > 2 and C >= 64:
+        w[:, C // 2: C // 2 + 16] = w[:, 0:16]  # ties at many thresholds
+    return w
+
+
+@pytest.mark.parametrize("case", CASES, ids=[str(c) for c in CASES])
+def test_encode_decode_bit_exact(gpu, orc, case):
+    torch, cass = gpu
+    R, C, k, m, B, fmt = case
+    print("case", case, flush=True)
+    w = make_w(R, C, 1000 + R + C + k)
+    spec_o, verif_o = orc.encode(w, k, m, block=B, fmt=fmt)
+    wd = dev(torch, w)
+    enc = cass.encode(wd, k, m, block=B, fmt=fmt)
+    torch.cuda.synchronize()
+    spec_g, verif_g = host_u8(enc.spec), host_u8(enc.verif)
+    assert spec_g.size == spec_o.size and verif_g.size == verif_o.size
+    assert np.array_equal(spec_g, spec_o), f"spec differs at {np.flatnonzero(spec_g != spec_o)[:8]}"
+    assert np.array_equal(verif_g, verif_o), f"verif differs at {np.flatnonzero(verif_g != verif_o)[:8]}"
+    out = torch.empty((R, C), dtype=torch.int16, device="cuda")
+    cass.cass_reconstruct(enc.desc, out)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_u16(out), w)
+    cass.cass_draft_decode(enc.desc, out)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_u16(out), orc.draft_decode(spec_o))
+
+
+def test_all_bf16_patterns_gpu(gpu, orc):
+    torch, cass = gpu
+    w = synth.all_bf16_patterns(seed=3)
+    for fmt in (1, 2):
+        for k, m in [(77, 3), (256, 7), (0, 0), (200, 5)]:
+            spec_o, verif_o = orc.encode(w, k, m, block=64, fmt=fmt)
+            enc = cass.encode(dev(torch, w), k, m, block=64, fmt=fmt)
+            out = torch.empty((256, 256), dtype=torch.int16, device="cuda")
+            cass.cass_reconstruct(enc.desc, out)
+            torch.cuda.synchronize()
+            assert np.array_equal(host_u8(enc.spec), spec_o), (fmt, k, m)
+            assert np.array_equal(host_u8(enc.verif), verif_o), (fmt, k, m)
+            assert np.array_equal(host_u16(out), w), (fmt, k, m)
+            cass.cass_draft_decode(enc.desc, out)
+            torch.cuda.synchronize()
+            assert np.array_equal(host_u16(out), orc.draft_decode(spec_o)), (fmt, k, m)
+
+
+def test_encode_is_deterministic(gpu):
+    torch, cass = gpu
+    w = dev(torch, make_w(300, 4096, 5))
+    a = cass.encode(w, 1229, 3)
+    b = cass.encode(w, 1229, 3)
+    torch.cuda.synchronize()
+    assert torch.equal(a.spec, b.spec) and torch.equal(a.verif, b.verif)
+
+
+PRODUCT_CASES = [
+    (1024, 1024, 512, 3, 256, 1),
+    (37, 4096, 1229, 3, 256, 1),
+    (64, 14336, 4301, 4, 256, 1),
+    (5, 1024, 0, 3, 256, 1),
+    (96, 2560, 768, 3, 256, 2),
+    (21, 9728, 2918, 3, 256, 2),
+    (40, 1024, 1024, 7, 256, 2),
+]
+
+
+@pytest.mark.parametrize("case", PRODUCT_CASES, ids=[str(c) for c in PRODUCT_CASES])
+def test_draft_gemv_and_verify_gemm(gpu, orc, case):
+    torch, cass = gpu
+    R, C, k, m, B, fmt = case
+    print("case", case, flush=True)
+    w = make_w(R, C, 77 + R + C)
+    spec_o, verif_o = orc.encode(w, k, m, block=B, fmt=fmt)
+    enc = cass.encode(dev(torch, w), k, m, block=B, fmt=fmt)
+    for batch in (1, 2, 3):
+        x = synth.activations(batch, C, 2, t0=batch)
+        y = torch.full((batch, R), float("nan"), dtype=torch.float32, device="cuda")
+        cass.cass_draft_gemv(enc.desc, dev(torch, x), y)
+        torch.cuda.synchronize()
+        y_ref, absy = orc.product(spec_o, x, threads=4)
+        check_product(y.cpu().numpy(), y_ref, absy)
+        if k == 0:
+            assert (y.cpu().numpy() == 0).all()
+    for ntok in (1, 5, 16):
+        X = synth.activations(ntok, C, 3, t0=ntok)
+        Y = torch.full((ntok, R), float("nan"), dtype=torch.float32, device="cuda")
+        cass.cass_verify_gemm(enc.desc, dev(torch, X), Y)
+        torch.cuda.synchronize()
+        Y_ref, absY = orc.product(spec_o, X, verif=verif_o, threads=4)
+        check_product(Y.cpu().numpy(), Y_ref, absY)
+
+
+def test_strided_operands(gpu, orc):
+    """ldx > cols and ldy > rows are honoured (padding untouched)."""
+    torch, cass = gpu
+    R, C = 100, 2048
+    w = make_w(R, C, 9)
+    spec_o, verif_o = orc.encode(w, 614, 3)
+    enc = cass.encode(dev(torch, w), 614, 3)
+    x = synth.activations(2, C, 4)
+    xpad = np.zeros((2, C + 64), dtype=np.uint16)
+    xpad[:, :C] = x
+    y = torch.full((2, R + 3), 7.0, dtype=torch.float32, device="cuda")
+    cass.cass_draft_gemv(enc.desc, dev(torch, xpad)[:, :C], y[:, :R])
+    torch.cuda.synchronize()
+    yh = y.cpu().numpy()
+    assert (yh[:, R:] == 7.0).all()
+    y_ref, absy = orc.product(spec_o, x)
+    check_product(yh[:, :R], y_ref, absy)
+
+
+def test_empty_tensor(gpu):
+    torch, cass = gpu
+    w = torch.empty((0, 1024), dtype=torch.int16, device="cuda")
+    enc = cass.encode(w, 300, 3)
+    torch.cuda.synchronize()
+    assert enc.rows == 0
+    y = torch.empty((1, 0), dtype=torch.float32, device="cuda")
+    cass.cass_draft_gemv(enc.desc, torch.zeros((1, 1024), dtype=torch.int16, device="cuda"), y)
+    torch.cuda.synchronize()
+
+
+def test_llama8b_layer_full_size(gpu, orc):
+    """The 8B-shaped layer (q|k|v, o, gate|up, down) at keep 0.3, 3 mantissa bits,
+    in the launch configuration the benchmark times: o's streams byte
+    for byte; every matrix reconstructs exactly and its host copy validates;
+    sampled draft-GEMV / verify-GEMM outputs match the oracle."""
+    torch, cass = gpu
+    layer = synth.fused_layer(synth.LLAMA3_8B, config=2, layer=0, outlier_frac=0.01)
+    rng = np.random.default_rng(0)
+    for name, w in layer.items():
+        R, C = w.shape
+        k = synth.keep_count(0.3, C)
+        print("matrix", name, w.shape, flush=True)
+        wd = dev(torch, w)
+        enc = cass.encode(wd, k, 3)
+        out = torch.empty_like(wd)
+        cass.cass_reconstruct(enc.desc, out)
+        torch.cuda.synchronize()
+        assert torch.equal(out, wd)
+        spec_g, verif_g = host_u8(enc.spec), host_u8(enc.verif)
+        assert cass.cass_tensor_validate(spec_g, verif_g) == cass.CASS_OK
+        if name == "o":
+            spec_o, verif_o = orc.encode(w, k, 3)
+            assert np.array_equal(spec_g, spec_o) and np.array_equal(verif_g, verif_o)
+        rows = np.unique(np.concatenate([[0, R - 1], rng.integers(0, R, 62)]))
+        x = synth.activations(1, C, 2)
+        y = torch.empty((1, R), dtype=torch.float32, device="cuda")
+        cass.cass_draft_gemv(enc.desc, dev(torch, x), y)
+        X = synth.activations(5, C, 2, t0=10)
+        Y = torch.empty((5, R), dtype=torch.float32, device="cuda")
+        cass.cass_verify_gemm(enc.desc, dev(torch, X), Y)
+        torch.cuda.synchronize()
+        # the draft of a row depends on that row alone, so the oracle encodes
+        # just the sampled rows to get their reference outputs
+        spec_r, verif_r = orc.encode(w[rows], k, 3)
+        y_ref, absy = orc.product(spec_r, x)
+        check_product(y.cpu().numpy()[:, rows], y_ref, absy)
+        Y_ref, absY = orc.product(spec_r, X, verif=verif_r)
+        check_product(Y.cpu().numpy()[:, rows], Y_ref, absY)
+        del enc, out, wd

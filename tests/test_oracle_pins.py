@@ -248,11 +248,11 @@ def test_stream_sizes_closed_form(orc, k, m):
                   -(-verif_code_bits // 8)]
     assert [n for _, n in h["secs"]] == want_spec
     assert [n for _, n in hv["secs"]] == want_verif
-    # sections are 256-aligned and back to back
+    # sections are 256-aligned, in order, each followed by >= 16 padding bytes
     pos = 256
     for off, n in h["secs"]:
         assert off == pos
-        pos = (off + n + 255) // 256 * 256
+        pos = (off + n + 16 + 255) // 256 * 256
     assert h["total"] == pos == spec.size
 
 
