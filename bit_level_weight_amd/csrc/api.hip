@@ -433,6 +433,7 @@ int cass_draft_gemv(const cass_tensor* W, const uint16_t* x, int batch, int64_t 
   int st = check_tensor(W, false);
   if (st) return st;
   if (batch < 1 || batch > 8) return fail(CASS_ERR_UNSUPPORTED, "batch %d outside 1..8", batch);
+  if (W->rows == 0) return CASS_OK;
   if (!x || !y) return fail(CASS_ERR_INVALID, "x or y is NULL");
   if (ldx < W->cols || ldy < W->rows) return fail(CASS_ERR_INVALID, "ldx < cols or ldy < rows");
   const Shape sh = shape_of(W);
@@ -451,6 +452,7 @@ int cass_verify_gemm(const cass_tensor* W, const uint16_t* X, int ntok, int64_t 
   int st = check_tensor(W, true);
   if (st) return st;
   if (ntok < 1 || ntok > 16) return fail(CASS_ERR_UNSUPPORTED, "ntok %d outside 1..16", ntok);
+  if (W->rows == 0) return CASS_OK;
   if (!X || !Y) return fail(CASS_ERR_INVALID, "X or Y is NULL");
   if (ldx < W->cols || ldy < W->rows) return fail(CASS_ERR_INVALID, "ldx < cols or ldy < rows");
   const Shape sh = shape_of(W);
@@ -464,6 +466,7 @@ int cass_reconstruct(const cass_tensor* W, uint16_t* out, hipStream_t stream) {
   g_last_error.clear();
   int st = check_tensor(W, true);
   if (st) return st;
+  if (W->rows == 0) return CASS_OK;
   if (!out || ((uintptr_t)out % 16)) return fail(CASS_ERR_INVALID, "out must be 16-byte aligned");
   const Shape sh = shape_of(W);
   hipError_t e;
@@ -481,6 +484,7 @@ int cass_draft_decode(const cass_tensor* W, uint16_t* out, hipStream_t stream) {
   g_last_error.clear();
   int st = check_tensor(W, false);
   if (st) return st;
+  if (W->rows == 0) return CASS_OK;
   if (!out || ((uintptr_t)out % 16)) return fail(CASS_ERR_INVALID, "out must be 16-byte aligned");
   const Shape sh = shape_of(W);
   hipError_t e = W->format == CASS_FMT_C1_UNARY
