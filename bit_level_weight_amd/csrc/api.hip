@@ -13,8 +13,6 @@
 
 namespace cass {
 
-int64_t draft_gemv_lds_bytes(const Shape& sh, int batch);
-
 namespace {
 
 thread_local std::string g_last_error;
@@ -141,13 +139,21 @@ Shape shape_of(const cass_tensor* W) {
   return Shape{W->rows, W->cols, W->block, W->keep, W->mant_bits};
 }
 
+// Whole 16-byte units between a section start and the end of the buffer, in
+// 32-bit words: the bulk copies of the staged kernels stay below this.
+int64_t word_limit(int64_t buffer_bytes, int64_t section_off) {
+  return (buffer_bytes - section_off) / 16 * 4;
+}
+
 SpecViewC1 spec_c1(const cass_tensor* W) {
   const uint8_t* b = (const uint8_t*)W->spec;
   const int64_t* o = W->spec_sec;
   return SpecViewC1{b + o[S1_RANK], (const uint32_t*)(b + o[S1_BITMAP]),
                     (const unsigned long long*)(b + o[S1_ROWBASE]),
                     (const uint32_t*)(b + o[S1_BLKOFF]), (const uint16_t*)(b + o[S1_KEPTB]),
-                    (const uint32_t*)(b + o[S1_FIELDS]), (const uint32_t*)(b + o[S1_CODES])};
+                    (const uint32_t*)(b + o[S1_FIELDS]), (const uint32_t*)(b + o[S1_CODES]),
+                    word_limit(W->spec_bytes, o[S1_BITMAP]), word_limit(W->spec_bytes, o[S1_FIELDS]),
+                    word_limit(W->spec_bytes, o[S1_CODES])};
 }
 VerifViewC1 verif_c1(const cass_tensor* W) {
   const uint8_t* b = (const uint8_t*)W->verif;
@@ -160,7 +166,9 @@ SpecViewC2 spec_c2(const cass_tensor* W) {
   const uint8_t* b = (const uint8_t*)W->spec;
   const int64_t* o = W->spec_sec;
   return SpecViewC2{(const uint32_t*)(b + o[S2_BITMAP]), b + o[S2_SHEXP],
-                    (const uint16_t*)(b + o[S2_KEPTB]), (const uint32_t*)(b + o[S2_FIELDS])};
+                    (const uint16_t*)(b + o[S2_KEPTB]), (const uint32_t*)(b + o[S2_FIELDS]),
+                    word_limit(W->spec_bytes, o[S2_BITMAP]), word_limit(W->spec_bytes, o[S2_SHEXP]),
+                    word_limit(W->spec_bytes, o[S2_FIELDS])};
 }
 VerifViewC2 verif_c2(const cass_tensor* W) {
   const uint8_t* b = (const uint8_t*)W->verif;
@@ -437,7 +445,9 @@ int cass_draft_gemv(const cass_tensor* W, const uint16_t* x, int batch, int64_t 
   if (!x || !y) return fail(CASS_ERR_INVALID, "x or y is NULL");
   if (ldx < W->cols || ldy < W->rows) return fail(CASS_ERR_INVALID, "ldx < cols or ldy < rows");
   const Shape sh = shape_of(W);
-  if (draft_gemv_lds_bytes(sh, batch) > 150 * 1024)
+  const int64_t code_limit = W->format == CASS_FMT_C1_UNARY ? spec_c1(W).codes_limit : 0;
+  if (!draft_gemv_staged_fits(sh, batch, W->format, code_limit) &&
+      draft_gemv_direct_lds_bytes(sh, batch) > 150 * 1024)
     return fail(CASS_ERR_UNSUPPORTED, "batch %d x cols %lld does not fit in LDS", batch,
                 (long long)W->cols);
   hipError_t e = W->format == CASS_FMT_C1_UNARY

@@ -1,3 +1,7 @@
+// Fused draft GEMV, direct variant: every stream word is read from global
+// memory by the lane that decodes it (no LDS staging of the compressed bytes).
+// Serves shapes whose tiles do not fit the staged kernels' LDS plan.
+//
 // Fused draft GEMV: decode the speculation stream and multiply in one pass,
 // y[b][n] = sum over kept j of Wdraft[n][j] * x[b][j], fp32 accumulation.
 //
@@ -162,9 +166,6 @@ __global__ void __launch_bounds__(kThreads) k_draft_gemv_c2(SpecViewC2 v, Shape 
   }
 }
 
-template <int BATCH>
-void pick_c1(const void** fn) { *fn = (const void*)&k_draft_gemv_c1<BATCH>; }
-
 int64_t lds_bytes(const GemvGeom& g, const Shape& sh, int batch) {
   return g.x_lds_elems * 2 + 1024 + (int64_t)g.rows_per_tile * (sh.cols / sh.block) * batch * 4;
 }
@@ -196,12 +197,13 @@ hipError_t launch_gemv(Kern kern, const View& v, const Shape& sh, const GemvGeom
 
 }  // namespace
 
-int64_t draft_gemv_lds_bytes(const Shape& sh, int batch) {
+int64_t draft_gemv_direct_lds_bytes(const Shape& sh, int batch) {
   return lds_bytes(make_geom(sh, batch), sh, batch);
 }
 
-hipError_t launch_draft_gemv_c1(const SpecViewC1& v, const Shape& sh, const uint16_t* x,
-                                int batch, int64_t ldx, float* y, int64_t ldy, hipStream_t s) {
+hipError_t launch_draft_gemv_c1_direct(const SpecViewC1& v, const Shape& sh, const uint16_t* x,
+                                       int batch, int64_t ldx, float* y, int64_t ldy,
+                                       hipStream_t s) {
   if (sh.rows == 0) return hipSuccess;
   const GemvGeom g = make_geom(sh, batch);
   switch (batch) {
@@ -217,8 +219,9 @@ hipError_t launch_draft_gemv_c1(const SpecViewC1& v, const Shape& sh, const uint
   }
 }
 
-hipError_t launch_draft_gemv_c2(const SpecViewC2& v, const Shape& sh, const uint16_t* x,
-                                int batch, int64_t ldx, float* y, int64_t ldy, hipStream_t s) {
+hipError_t launch_draft_gemv_c2_direct(const SpecViewC2& v, const Shape& sh, const uint16_t* x,
+                                       int batch, int64_t ldx, float* y, int64_t ldy,
+                                       hipStream_t s) {
   if (sh.rows == 0) return hipSuccess;
   const GemvGeom g = make_geom(sh, batch);
   switch (batch) {

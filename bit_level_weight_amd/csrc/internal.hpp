@@ -5,7 +5,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "../../include/cassandra.h"
+#include "cassandra.h"
 
 namespace cass {
 
@@ -61,6 +61,9 @@ struct SpecViewC1 {
   const uint16_t* keptb;
   const uint32_t* fields;
   const uint32_t* codes;
+  // 32-bit words from the start of each bit section to the end of the stream
+  // buffer: bulk copies never read past these.
+  int64_t bitmap_limit, fields_limit, codes_limit;
 };
 struct VerifViewC1 {
   const uint8_t* perm;
@@ -75,6 +78,7 @@ struct SpecViewC2 {
   const uint8_t* shexp;
   const uint16_t* keptb;
   const uint32_t* fields;
+  int64_t bitmap_limit, shexp_limit, fields_limit;  // as in SpecViewC1 (shexp: bytes/4)
 };
 struct VerifViewC2 {
   const uint8_t* perm;
@@ -107,10 +111,21 @@ hipError_t launch_pack(const uint16_t* w, const Shape& sh, int format, const Wor
                        const RankTables& rt, uint8_t* spec, const int64_t* spec_sec,
                        uint8_t* verif, const int64_t* verif_sec, hipStream_t s);
 
+// Draft GEMV.  The staged kernels copy each tile's compressed bytes to LDS;
+// the direct kernels read every stream word from global memory and serve
+// shapes whose tiles do not fit in LDS.
 hipError_t launch_draft_gemv_c1(const SpecViewC1& v, const Shape& sh, const uint16_t* x,
                                 int batch, int64_t ldx, float* y, int64_t ldy, hipStream_t s);
 hipError_t launch_draft_gemv_c2(const SpecViewC2& v, const Shape& sh, const uint16_t* x,
                                 int batch, int64_t ldx, float* y, int64_t ldy, hipStream_t s);
+hipError_t launch_draft_gemv_c1_direct(const SpecViewC1& v, const Shape& sh, const uint16_t* x,
+                                       int batch, int64_t ldx, float* y, int64_t ldy,
+                                       hipStream_t s);
+hipError_t launch_draft_gemv_c2_direct(const SpecViewC2& v, const Shape& sh, const uint16_t* x,
+                                       int batch, int64_t ldx, float* y, int64_t ldy,
+                                       hipStream_t s);
+int64_t draft_gemv_direct_lds_bytes(const Shape& sh, int batch);
+bool draft_gemv_staged_fits(const Shape& sh, int batch, int format, int64_t code_limit_words);
 hipError_t launch_decode_c1(const SpecViewC1& sv, const VerifViewC1* vv, const Shape& sh,
                             uint16_t* out, hipStream_t s);
 hipError_t launch_decode_c2(const SpecViewC2& sv, const VerifViewC2* vv, const Shape& sh,

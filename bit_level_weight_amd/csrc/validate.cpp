@@ -7,7 +7,7 @@
 #include <string>
 #include <vector>
 
-#include "../../include/cassandra.h"
+#include "cassandra.h"
 
 namespace {
 

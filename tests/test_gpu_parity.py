@@ -157,6 +157,24 @@ def test_draft_gemv_and_verify_gemm(gpu, orc, case):
         check_product(Y.cpu().numpy(), Y_ref, absY)
 
 
+@pytest.mark.parametrize("fmt", [1, 2])
+def test_direct_gemv_path(gpu, orc, monkeypatch, fmt):
+    """The direct (non-staged) GEMV kernels, selected with CASS_GEMV_DIRECT=1."""
+    torch, cass = gpu
+    R, C, k, m = 70, 4096, 1229, 3
+    w = make_w(R, C, 606)
+    spec_o, _ = orc.encode(w, k, m, fmt=fmt)
+    enc = cass.encode(dev(torch, w), k, m, fmt=fmt)
+    monkeypatch.setenv("CASS_GEMV_DIRECT", "1")
+    for batch in (1, 2):
+        x = synth.activations(batch, C, 5)
+        y = torch.full((batch, R), float("nan"), dtype=torch.float32, device="cuda")
+        cass.cass_draft_gemv(enc.desc, dev(torch, x), y)
+        torch.cuda.synchronize()
+        y_ref, absy = orc.product(spec_o, x)
+        check_product(y.cpu().numpy(), y_ref, absy)
+
+
 def test_strided_operands(gpu, orc):
     """ldx > cols and ldy > rows are honoured (padding untouched)."""
     torch, cass = gpu
