@@ -181,3 +181,65 @@ def product_rows(spec, x, rows, verif=None):
                                   0 if verif is None else verif.size, _p(x), ntok, _p(rows),
                                   rows.size, _p(y), _p(absy)), "product_rows")
     return y, absy
+
+
+# ------------------------------------------------------------------ KV cache
+
+def _kv_lib():
+    L = lib()
+    if not getattr(L, "_kv_ready", False):
+        P, I64 = ctypes.c_void_p, ctypes.c_int64
+        L.orc_kv_layout.argtypes = [I64, I64, ctypes.c_int, I64, I64, I64, P, P,
+                                    ctypes.POINTER(I64), ctypes.POINTER(I64)]
+        L.orc_kv_encode.argtypes = [P, I64, I64, I64, I64, ctypes.c_int, I64, I64, I64, P, P, P]
+        L.orc_kv_decode.argtypes = [P, P, I64, I64, I64, ctypes.c_int, I64, I64, I64, P]
+        L.orc_attention.argtypes = [P, I64, P, P, I64, I64, ctypes.c_double, P, P]
+        L._kv_ready = True
+    return L
+
+
+def kv_layout(D, k, m, T_max, code_cap, vcode_cap):
+    """(spec part offsets[5], verif part offsets[5], spec bytes, verif bytes) of one stream."""
+    so = np.zeros(5, dtype=np.int64)
+    vo = np.zeros(5, dtype=np.int64)
+    sb, vb = ctypes.c_int64(0), ctypes.c_int64(0)
+    _check(_kv_lib().orc_kv_layout(D, k, m, T_max, code_cap, vcode_cap, _p(so), _p(vo),
+                                   ctypes.byref(sb), ctypes.byref(vb)), "kv_layout")
+    return so, vo, sb.value, vb.value
+
+
+def kv_encode(vec, T0, k, m, T_max, code_cap, vcode_cap):
+    """One (head, K|V) stream of all tokens of vec[T, D] -> (spec, verif, tails)."""
+    vec = _u16(vec)
+    T, D = vec.shape
+    _, _, sb, vb = kv_layout(D, k, m, T_max, code_cap, vcode_cap)
+    spec = np.zeros(sb, dtype=np.uint8)
+    verif = np.zeros(vb, dtype=np.uint8)
+    tails = np.zeros(2, dtype=np.uint64)
+    _check(_kv_lib().orc_kv_encode(_p(vec), T, T0, D, k, m, T_max, code_cap, vcode_cap,
+                                   _p(spec), _p(verif), _p(tails)), "kv_encode")
+    return spec, verif, tails
+
+
+def kv_decode(spec, T, D, k, m, T_max, code_cap, vcode_cap, verif=None):
+    spec = np.ascontiguousarray(spec, dtype=np.uint8)
+    if verif is not None:
+        verif = np.ascontiguousarray(verif, dtype=np.uint8)
+    out = np.zeros((T, D), dtype=np.uint16)
+    _check(_kv_lib().orc_kv_decode(_p(spec), _p(verif), T, D, k, m, T_max, code_cap,
+                                   vcode_cap, _p(out)), "kv_decode")
+    return out
+
+
+def attention(q, K, V, scale, visible=None):
+    """fp64 softmax attention of q[nq, D] over K, V [T, D] (bf16 patterns)."""
+    q = _u16(np.atleast_2d(q))
+    K = _u16(K)
+    V = _u16(V)
+    nq, D = q.shape
+    T = K.shape[0]
+    out = np.zeros((nq, D), dtype=np.float64)
+    vis = None if visible is None else np.ascontiguousarray(visible, dtype=np.int64)
+    _check(_kv_lib().orc_attention(_p(q), nq, _p(K), _p(V), T, D, float(scale), _p(vis),
+                                   _p(out)), "attention")
+    return out

@@ -652,3 +652,169 @@ int orc_product_rows(const uint8_t* spec, int64_t spec_len, const uint8_t* verif
   free(row);
   return ORC_OK;
 }
+
+/* ---------------------------------------------------------------- KV cache */
+/* [R31] the KV cache goes through the same value pruning, mantissa truncation
+ * and exponent coding as the weights; [R33] (Cassandra review, section 3.3):
+ * KV entries are produced during inference, so the encoder runs online, one
+ * append at a time.  Group = one token's vector of one head; the rank tables
+ * are those of the first append (a reading: the pages do not say how an
+ * online encoder picks its table). */
+
+static int64_t kv_part(int64_t* pos, int64_t bytes) {
+  const int64_t o = *pos;
+  *pos = align256(*pos + bytes + 16);
+  return o;
+}
+
+int orc_kv_layout(int64_t D, int64_t k, int m, int64_t T_max, int64_t code_cap,
+                  int64_t vcode_cap, int64_t spec_off[5], int64_t verif_off[5],
+                  int64_t* spec_bytes, int64_t* verif_bytes) {
+  if (D <= 0 || D % 32 || D > 65536 || k < 0 || k > D || m < 0 || m > 7 || T_max < 0 ||
+      code_cap < 0 || vcode_cap < 0 || code_cap >= ((int64_t)1 << 32) ||
+      vcode_cap >= ((int64_t)1 << 32))
+    return ORC_ERR_INVALID;
+  int64_t p = 0;
+  spec_off[0] = kv_part(&p, 256);
+  spec_off[1] = kv_part(&p, T_max * D / 8);
+  spec_off[2] = kv_part(&p, 4 * T_max);
+  spec_off[3] = kv_part(&p, (T_max * k * (1 + m) + 7) / 8);
+  spec_off[4] = kv_part(&p, (code_cap + 7) / 8);
+  *spec_bytes = p;
+  p = 0;
+  verif_off[0] = kv_part(&p, 256);
+  verif_off[1] = kv_part(&p, (T_max * k * (7 - m) + 7) / 8);
+  verif_off[2] = kv_part(&p, T_max * (D - k));
+  verif_off[3] = kv_part(&p, 4 * T_max);
+  verif_off[4] = kv_part(&p, (vcode_cap + 7) / 8);
+  *verif_bytes = p;
+  return ORC_OK;
+}
+
+int orc_kv_encode(const uint16_t* vec, int64_t T, int64_t T0, int64_t D, int64_t k, int m,
+                  int64_t T_max, int64_t code_cap, int64_t vcode_cap, uint8_t* spec,
+                  uint8_t* verif, uint64_t tails[2]) {
+  int64_t so[5], vo[5], sb, vb;
+  int st = orc_kv_layout(D, k, m, T_max, code_cap, vcode_cap, so, vo, &sb, &vb);
+  if (st) return st;
+  if (T < 0 || T > T_max || (T > 0 && (T0 < 1 || T0 > T))) return ORC_ERR_INVALID;
+  memset(spec, 0, (size_t)sb);
+  memset(verif, 0, (size_t)vb);
+  uint8_t* keep = (uint8_t*)malloc((size_t)(T * D + 1));
+  if (!keep) return ORC_ERR_CAPACITY;
+  orc_select(vec, T, D, k, keep);  /* pruning per token vector */
+  uint64_t hk[256], hp[256];
+  uint8_t perm_s[256], perm_v[256];
+  int rank_s[256], rank_v[256];
+  orc_histograms(vec, keep, T0 * D, hk, hp);  /* the first append's exponents */
+  orc_rank_table(hk, perm_s);
+  orc_rank_table(hp, perm_v);
+  for (int r = 0; r < 256; r++) { rank_s[perm_s[r]] = r; rank_v[perm_v[r]] = r; }
+  memcpy(spec + so[0], perm_s, 256);
+  memcpy(verif + vo[0], perm_v, 256);
+  uint64_t stail = 0, vtail = 0;
+  for (int64_t t = 0; t < T; t++) {
+    put_u32(spec + so[2] + 4 * t, (uint32_t)stail);
+    put_u32(verif + vo[3] + 4 * t, (uint32_t)vtail);
+    int64_t kept_i = 0, pr_i = 0;
+    for (int64_t j = 0; j < D; j++) {
+      uint16_t b = vec[t * D + j];
+      int s = bf_s(b), e = bf_e(b), f = bf_f(b);
+      if (keep[t * D + j]) {
+        int64_t kin = t * k + kept_i;
+        put_bits(spec + so[1], (uint64_t)(t * D + j), 1, 1);
+        put_bits(spec + so[3], (uint64_t)kin * (1 + m), (uint64_t)((s << m) | (f >> (7 - m))), 1 + m);
+        if (stail + (uint64_t)rank_s[e] + 1 > (uint64_t)code_cap) { free(keep); return ORC_ERR_CAPACITY; }
+        put_unary(spec + so[4], stail, rank_s[e]);
+        stail += (uint64_t)rank_s[e] + 1;
+        put_bits(verif + vo[1], (uint64_t)kin * (7 - m), (uint64_t)(f & ((1 << (7 - m)) - 1)), 7 - m);
+        kept_i++;
+      } else {
+        verif[vo[2] + t * (D - k) + pr_i] = (uint8_t)((s << 7) | f);
+        if (vtail + (uint64_t)rank_v[e] + 1 > (uint64_t)vcode_cap) { free(keep); return ORC_ERR_CAPACITY; }
+        put_unary(verif + vo[4], vtail, rank_v[e]);
+        vtail += (uint64_t)rank_v[e] + 1;
+        pr_i++;
+      }
+    }
+  }
+  tails[0] = stail;
+  tails[1] = vtail;
+  free(keep);
+  return ORC_OK;
+}
+
+int orc_kv_decode(const uint8_t* spec, const uint8_t* verif, int64_t T, int64_t D, int64_t k,
+                  int m, int64_t T_max, int64_t code_cap, int64_t vcode_cap, uint16_t* out) {
+  int64_t so[5], vo[5], sb, vb;
+  int st = orc_kv_layout(D, k, m, T_max, code_cap, vcode_cap, so, vo, &sb, &vb);
+  if (st) return st;
+  if (T < 0 || T > T_max) return ORC_ERR_INVALID;
+  for (int64_t t = 0; t < T; t++) {
+    uint64_t spos = get_u32(spec + so[2] + 4 * t);
+    uint64_t vpos = verif ? get_u32(verif + vo[3] + 4 * t) : 0;
+    int64_t kept_i = 0, pr_i = 0;
+    for (int64_t j = 0; j < D; j++) {
+      if (get_bits(spec + so[1], (uint64_t)(t * D + j), 1)) {
+        if (kept_i >= k) return ORC_ERR_CORRUPT;
+        int64_t kin = t * k + kept_i;
+        int field = (int)get_bits(spec + so[3], (uint64_t)kin * (1 + m), 1 + m);
+        int rank = get_unary(spec + so[4], spos, (uint64_t)code_cap);
+        if (rank < 0) return ORC_ERR_CORRUPT;
+        spos += (uint64_t)rank + 1;
+        int s = field >> m, ft = field & ((1 << m) - 1), e = spec[so[0] + rank];
+        uint16_t d = (uint16_t)((s << 15) | (e << 7) | (ft << (7 - m)));
+        if (verif) d |= (uint16_t)get_bits(verif + vo[1], (uint64_t)kin * (7 - m), 7 - m);
+        out[t * D + j] = d;
+        kept_i++;
+      } else {
+        if (verif) {
+          int byte = verif[vo[2] + t * (D - k) + pr_i];
+          int rank = get_unary(verif + vo[4], vpos, (uint64_t)vcode_cap);
+          if (rank < 0) return ORC_ERR_CORRUPT;
+          vpos += (uint64_t)rank + 1;
+          int e = verif[vo[0] + rank];
+          out[t * D + j] = (uint16_t)(((byte >> 7) << 15) | (e << 7) | (byte & 0x7F));
+        } else {
+          out[t * D + j] = 0x0000;
+        }
+        pr_i++;
+      }
+    }
+    if (kept_i != k) return ORC_ERR_CORRUPT;
+  }
+  return ORC_OK;
+}
+
+/* Attention as defined: softmax of scaled dot products, then the weighted sum
+ * of values; the draft runs it on the zero-filled KV, the target on the exact
+ * KV (Cassandra review, sections 3.1 and 1). */
+int orc_attention(const uint16_t* q, int64_t nq, const uint16_t* K, const uint16_t* V,
+                  int64_t T, int64_t D, double scale, const int64_t* visible, double* out) {
+  double* s = (double*)malloc(sizeof(double) * (size_t)(T > 0 ? T : 1));
+  if (!s) return ORC_ERR_CAPACITY;
+  for (int64_t i = 0; i < nq; i++) {
+    const int64_t n = visible ? visible[i] : T;
+    if (n < 1 || n > T) { free(s); return ORC_ERR_INVALID; }
+    double mx = -INFINITY;
+    for (int64_t t = 0; t < n; t++) {
+      double acc = 0.0;
+      for (int64_t d = 0; d < D; d++)
+        acc += bf16_to_double(q[i * D + d]) * bf16_to_double(K[t * D + d]);
+      s[t] = scale * acc;
+      if (s[t] > mx) mx = s[t];
+    }
+    double sum = 0.0;
+    for (int64_t t = 0; t < n; t++) {
+      s[t] = exp(s[t] - mx);
+      sum += s[t];
+    }
+    for (int64_t d = 0; d < D; d++) {
+      double acc = 0.0;
+      for (int64_t t = 0; t < n; t++) acc += s[t] * bf16_to_double(V[t * D + d]);
+      out[i * D + d] = acc / sum;
+    }
+  }
+  free(s);
+  return ORC_OK;
+}

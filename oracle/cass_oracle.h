@@ -82,6 +82,34 @@ int orc_product_rows(const uint8_t* spec, int64_t spec_len, const uint8_t* verif
 int orc_header(const uint8_t* buf, int64_t len, uint32_t expect_magic, int64_t out[8],
                int64_t sec_off[12], int64_t sec_len[12]);
 
+/* --- KV cache (online compression, one stream = one (head, K|V) sequence) ---
+ * Region layout of one stream (byte offsets from the region start; each part
+ * 256-aligned and followed by >= 16 zero bytes):
+ *   speculation region: perm[256] | bitmap (T_max*D bits, token t at bit t*D)
+ *     | code offsets u32[T_max] (bit offset of token t's first code in the
+ *     code area) | fields ((s<<m)|ft, 1+m bits, token t value i at bit
+ *     (t*k+i)*(1+m)) | codes (code_cap bits)
+ *   verification region: perm[256] | low mantissas (7-m bits at (t*k+i)*(7-m))
+ *     | pruned bytes (token t pruned i at byte t*(D-k)+i) | code offsets
+ *     u32[T_max] | codes (vcode_cap bits)
+ * The rank tables come from the tokens of the first append (t < T0) and are
+ * frozen afterwards.  Returns the region sizes with spec == NULL. */
+int orc_kv_layout(int64_t D, int64_t k, int m, int64_t T_max, int64_t code_cap,
+                  int64_t vcode_cap, int64_t spec_off[5], int64_t verif_off[5],
+                  int64_t* spec_bytes, int64_t* verif_bytes);
+int orc_kv_encode(const uint16_t* vec, int64_t T, int64_t T0, int64_t D, int64_t k, int m,
+                  int64_t T_max, int64_t code_cap, int64_t vcode_cap, uint8_t* spec,
+                  uint8_t* verif, uint64_t tails[2]);
+/* Draft (verif == NULL) or exact vectors of the first T tokens: out[T][D]. */
+int orc_kv_decode(const uint8_t* spec, const uint8_t* verif, int64_t T, int64_t D, int64_t k,
+                  int m, int64_t T_max, int64_t code_cap, int64_t vcode_cap, uint16_t* out);
+
+/* Softmax attention of nq queries over T tokens, fp64:
+ * s_t = scale * sum_d q[d] K[t][d]; p = softmax over t < visible[i];
+ * out[i][d] = sum_t p_t V[t][d].  q, K, V are bf16 patterns. */
+int orc_attention(const uint16_t* q, int64_t nq, const uint16_t* K, const uint16_t* V,
+                  int64_t T, int64_t D, double scale, const int64_t* visible, double* out);
+
 #ifdef __cplusplus
 }
 #endif
