@@ -29,7 +29,12 @@ EXPORTED = (
     "cass_encode_ws_bytes", "cass_encode_plan", "cass_encode_tensor", "cass_tensor_describe",
     "cass_draft_gemv", "cass_verify_gemm", "cass_reconstruct", "cass_draft_decode",
     "cass_tensor_validate", "cass_status_string", "cass_last_error", "cass_version",
+    "cass_kv_bytes", "cass_kv_init", "cass_kv_append_ws_bytes", "cass_kv_append_encode",
+    "cass_kv_status", "cass_kv_decode", "cass_kv_attn_ws_bytes", "cass_kv_draft_attn",
+    "cass_kv_verify_attn",
 )
+CASS_KV_STATE_BYTES = 4096
+CASS_KV_FLAG_TABLES, CASS_KV_FLAG_OVERFLOW = 1, 2
 
 
 class CassParams(ctypes.Structure):
@@ -59,6 +64,20 @@ class CassPlan(ctypes.Structure):
                 ("spec_code_bits", ctypes.c_uint64), ("verif_code_bits", ctypes.c_uint64),
                 ("resid_bits", ctypes.c_uint64),
                 ("ws", ctypes.c_void_p), ("ws_bytes", ctypes.c_int64)]
+
+
+class CassKvParams(ctypes.Structure):
+    _fields_ = [("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("keep", ctypes.c_int32), ("mant_bits", ctypes.c_int32),
+                ("max_tokens", ctypes.c_int64), ("code_cap_bits", ctypes.c_int64),
+                ("vcode_cap_bits", ctypes.c_int64)]
+
+
+class CassKv(ctypes.Structure):
+    _fields_ = [("p", CassKvParams), ("spec", ctypes.c_void_p), ("verif", ctypes.c_void_p),
+                ("state", ctypes.c_void_p), ("spec_stream_bytes", ctypes.c_int64),
+                ("verif_stream_bytes", ctypes.c_int64), ("spec_part", ctypes.c_int64 * 5),
+                ("verif_part", ctypes.c_int64 * 5), ("tokens", ctypes.c_int64)]
 
 
 class CassError(RuntimeError):
@@ -96,6 +115,17 @@ def lib():
         L.cass_last_error.argtypes = []
         L.cass_last_error.restype = ctypes.c_char_p
         L.cass_version.argtypes = []
+        KP, KV = ctypes.POINTER(CassKvParams), ctypes.POINTER(CassKv)
+        L.cass_kv_bytes.argtypes = [KP, ctypes.POINTER(I64), ctypes.POINTER(I64),
+                                    ctypes.POINTER(I64)]
+        L.cass_kv_init.argtypes = [KV, KP, P, P, P, P]
+        L.cass_kv_append_ws_bytes.argtypes = [KV, I32, ctypes.POINTER(I64)]
+        L.cass_kv_append_encode.argtypes = [KV, P, P, I32, P, I64, P]
+        L.cass_kv_status.argtypes = [KV, ctypes.POINTER(I64), ctypes.POINTER(ctypes.c_uint32), P]
+        L.cass_kv_decode.argtypes = [KV, I32, P, P]
+        L.cass_kv_attn_ws_bytes.argtypes = [KV, I32, I32, ctypes.POINTER(I64)]
+        L.cass_kv_draft_attn.argtypes = [KV, P, I32, ctypes.c_float, P, P, I64, P]
+        L.cass_kv_verify_attn.argtypes = [KV, P, I32, I32, ctypes.c_float, P, P, I64, P]
         _lib = L
     return _lib
 
@@ -232,3 +262,93 @@ def encode(w, keep: int, mant_bits: int, block: int = 256, fmt: int = CASS_FMT_C
     enc = Encoded(desc, spec, verif, plan)
     enc._ws = ws  # the workspace must outlive the packing pass
     return enc
+
+
+# ------------------------------------------------------------------ KV cache
+
+
+def cass_kv_bytes(params: CassKvParams):
+    sb, vb, tb = ctypes.c_int64(0), ctypes.c_int64(0), ctypes.c_int64(0)
+    _check(lib().cass_kv_bytes(ctypes.byref(params), ctypes.byref(sb), ctypes.byref(vb),
+                               ctypes.byref(tb)))
+    return sb.value, vb.value, tb.value
+
+
+def cass_kv_init(params: CassKvParams, spec, verif, state, stream=None) -> CassKv:
+    kv = CassKv()
+    _check(lib().cass_kv_init(ctypes.byref(kv), ctypes.byref(params), _ptr(spec), _ptr(verif),
+                              _ptr(state), _stream(stream)))
+    return kv
+
+
+def cass_kv_append_ws_bytes(kv: CassKv, ntok: int) -> int:
+    n = ctypes.c_int64(0)
+    _check(lib().cass_kv_append_ws_bytes(ctypes.byref(kv), ntok, ctypes.byref(n)))
+    return n.value
+
+
+def cass_kv_append_encode(kv: CassKv, k, v, ws, stream=None):
+    """k, v: [ntok, n_kv_heads, head_dim] bf16 patterns on the GPU."""
+    ntok = k.shape[0]
+    _check(lib().cass_kv_append_encode(ctypes.byref(kv), _ptr(k), _ptr(v), ntok, _ptr(ws),
+                                       ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def cass_kv_status(kv: CassKv, stream=None):
+    t, f = ctypes.c_int64(0), ctypes.c_uint32(0)
+    _check(lib().cass_kv_status(ctypes.byref(kv), ctypes.byref(t), ctypes.byref(f),
+                                _stream(stream)))
+    return t.value, f.value
+
+
+def cass_kv_decode(kv: CassKv, exact: bool, out, stream=None):
+    _check(lib().cass_kv_decode(ctypes.byref(kv), int(bool(exact)), _ptr(out), _stream(stream)))
+
+
+def cass_kv_attn_ws_bytes(kv: CassKv, nq: int, n_q_heads: int) -> int:
+    n = ctypes.c_int64(0)
+    _check(lib().cass_kv_attn_ws_bytes(ctypes.byref(kv), nq, n_q_heads, ctypes.byref(n)))
+    return n.value
+
+
+def cass_kv_draft_attn(kv: CassKv, q, scale, out, ws, stream=None):
+    """q: [n_q_heads, head_dim] bf16; out: [n_q_heads, head_dim] float32."""
+    _check(lib().cass_kv_draft_attn(ctypes.byref(kv), _ptr(q), q.shape[0], float(scale),
+                                    _ptr(out), _ptr(ws), ws.numel() * ws.element_size(),
+                                    _stream(stream)))
+
+
+def cass_kv_verify_attn(kv: CassKv, q, scale, out, ws, stream=None):
+    """q: [nq, n_q_heads, head_dim] bf16; out: same shape, float32."""
+    _check(lib().cass_kv_verify_attn(ctypes.byref(kv), _ptr(q), q.shape[0], q.shape[1],
+                                     float(scale), _ptr(out), _ptr(ws),
+                                     ws.numel() * ws.element_size(), _stream(stream)))
+
+
+class KvCache:
+    """Device buffers (torch) of one layer's compressed KV cache and its descriptor."""
+
+    def __init__(self, n_kv_heads, head_dim, keep, mant_bits, max_tokens, code_cap_bits=None,
+                 vcode_cap_bits=None, device="cuda", stream=None):
+        import torch
+        code_cap_bits = code_cap_bits or max_tokens * keep * 8
+        vcode_cap_bits = vcode_cap_bits or max_tokens * (head_dim - keep) * 8
+        self.params = CassKvParams(n_kv_heads, head_dim, keep, mant_bits, max_tokens,
+                                   code_cap_bits, vcode_cap_bits)
+        sb, vb, tb = cass_kv_bytes(self.params)
+        self.spec = torch.empty(sb, dtype=torch.uint8, device=device)
+        self.verif = torch.empty(vb, dtype=torch.uint8, device=device)
+        self.state = torch.empty(tb, dtype=torch.uint8, device=device)
+        self.kv = cass_kv_init(self.params, self.spec, self.verif, self.state, stream)
+        self._ws = None
+
+    def append(self, k, v, stream=None):
+        import torch
+        need = cass_kv_append_ws_bytes(self.kv, k.shape[0])
+        if self._ws is None or self._ws.numel() < need:
+            self._ws = torch.empty(max(need, 1), dtype=torch.uint8, device=k.device)
+        cass_kv_append_encode(self.kv, k, v, self._ws, stream)
+
+    @property
+    def tokens(self):
+        return self.kv.tokens

@@ -218,6 +218,18 @@ int64_t ws_layout(int64_t R, int64_t C, int64_t B, Workspace* ws, uint8_t* base)
 
 }  // namespace
 
+int report(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+void clear_error() { g_last_error.clear(); }
+
 Workspace carve_workspace(void* base, int64_t rows, int64_t cols, int64_t block) {
   Workspace w;
   ws_layout(rows, cols, block, &w, (uint8_t*)base);

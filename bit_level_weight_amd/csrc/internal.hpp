@@ -139,4 +139,8 @@ hipError_t launch_verify_gemm_c2(const SpecViewC2& sv, const VerifViewC2& vv, co
 
 int device_cu_count();
 
+// Sets the calling thread's error text (cass_last_error) and returns status.
+int report(int status, const char* fmt, ...);
+void clear_error();
+
 }  // namespace cass

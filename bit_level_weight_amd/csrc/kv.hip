@@ -1,0 +1,752 @@
+// KV cache: online append-encode, decode, and draft / verification attention
+// on the compressed cache.
+//
+// Method: Cassandra review (marsggbo.github.io), section 3.1 -- the KV cache
+// goes through the same pruning, mantissa truncation and exponent coding as
+// the weights, split into speculation and verification data; section 3.3 --
+// KV entries are produced during inference, so the encoder runs online;
+// section 1 -- the draft guesses tokens and the target verifies them in one
+// parallel pass.  Attention is the usual scaled-dot-product softmax.
+//
+// Stream layout: see include/cassandra.h.  Streams are indexed 2*head + kind
+// (kind 0 = keys, 1 = values); a vector is one token of one head of one kind.
+#include <stdint.h>
+#include <string.h>
+
+#include "bits.hpp"
+#include "internal.hpp"
+
+namespace cass {
+
+namespace {
+
+constexpr int kWaves = 4;  // waves per workgroup in the per-vector kernels
+
+struct KvDev {
+  uint8_t* spec;
+  uint8_t* verif;
+  unsigned long long* state;  // [0] tokens, [1] flags, [2+2s] spec tail, [3+2s] verif tail
+  int64_t sstride, vstride;   // bytes per stream region
+  int64_t so[5], vo[5];       // part offsets inside a region
+  int H, D, k, m;
+  int64_t T_max, ccap, vcap;
+};
+
+// Append workspace (per call, nvec = ntok * 2H vectors).
+struct AppendWs {
+  uint32_t* bm;     // nvec * D/32 keep words
+  uint32_t* lens;   // nvec * 2: speculation / verification code bits
+  uint32_t* start;  // nvec * 2: first code bit (0xFFFFFFFF: not written)
+  uint32_t* hist;   // 2H * 512 exponent counts (first append)
+};
+
+__device__ __forceinline__ int key_of(uint16_t b) { return b & 0x7FFF; }
+
+__device__ __forceinline__ const uint16_t* vec_ptr(const uint16_t* kk, const uint16_t* vv,
+                                                    int64_t t, int h, int kind, int H, int D) {
+  return (kind ? vv : kk) + (t * H + h) * (int64_t)D;
+}
+
+// ---- append, step 1: top-k of each vector (one wave per vector) ----
+__global__ void __launch_bounds__(64 * kWaves) k_kv_select(KvDev kv, const uint16_t* kk,
+                                                           const uint16_t* vv, int ntok, int first,
+                                                           AppendWs ws) {
+  __shared__ uint16_t keys[kWaves][256];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int64_t nvec = (int64_t)ntok * 2 * kv.H;
+  const int64_t vi = (int64_t)blockIdx.x * kWaves + wv;
+  if (vi >= nvec) return;
+  const int kind = (int)(vi & 1);
+  const int64_t th = vi >> 1;
+  const int h = (int)(th % kv.H);
+  const int64_t t = th / kv.H;
+  const int s = 2 * h + kind;
+  const uint16_t* x = vec_ptr(kk, vv, t, h, kind, kv.H, kv.D);
+  for (int j = lane; j < kv.D; j += 64) keys[wv][j] = x[j];
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  for (int c = 0; c < kv.D / 64 + ((kv.D % 64) ? 1 : 0); ++c) {
+    const int j = c * 64 + lane;
+    bool keep = false;
+    if (j < kv.D) {
+      const int kj = key_of(keys[wv][j]);
+      int rank = 0;  // values ordered before j: larger |x|, or equal and lower index
+      for (int i = 0; i < kv.D; ++i) {
+        const int ki = key_of(keys[wv][i]);
+        rank += (ki > kj) || (ki == kj && i < j);
+      }
+      keep = rank < kv.k;
+      if (first) {
+        const int e = (keys[wv][j] >> 7) & 0xFF;
+        atomicAdd(ws.hist + s * 512 + (keep ? 0 : 256) + e, 1u);
+      }
+    }
+    const unsigned long long mask = __ballot(keep);
+    if (lane == 0) {
+      const int w0 = c * 2;
+      if (w0 < kv.D / 32) ws.bm[vi * (kv.D / 32) + w0] = (uint32_t)mask;
+      if (w0 + 1 < kv.D / 32) ws.bm[vi * (kv.D / 32) + w0 + 1] = (uint32_t)(mask >> 32);
+    }
+  }
+}
+
+// ---- append, step 2 (first append only): rank tables from the histograms ----
+__global__ void __launch_bounds__(256) k_kv_ranks(KvDev kv, AppendWs ws) {
+  __shared__ uint32_t cnt[512];
+  const int s = blockIdx.x;
+  const int t = threadIdx.x;
+  cnt[t] = ws.hist[s * 512 + t];
+  cnt[256 + t] = ws.hist[s * 512 + 256 + t];
+  __syncthreads();
+  for (int which = 0; which < 2; ++which) {
+    const uint32_t* c = cnt + which * 256;
+    int rank = 0;  // count descending, symbol ascending
+    for (int u = 0; u < 256; ++u) rank += (c[u] > c[t]) || (c[u] == c[t] && u < t);
+    uint8_t* perm = which ? kv.verif + s * kv.vstride + kv.vo[0] : kv.spec + s * kv.sstride + kv.so[0];
+    perm[rank] = (uint8_t)t;
+  }
+  if (s == 0 && t == 0) kv.state[1] |= (unsigned long long)CASS_KV_FLAG_TABLES;
+}
+
+// Wave-private inverse rank tables (symbol -> rank) of stream s.
+__device__ __forceinline__ void load_ranks(const KvDev& kv, int s, uint8_t* rs, uint8_t* rv,
+                                           int lane) {
+  const uint8_t* ps = kv.spec + s * kv.sstride + kv.so[0];
+  const uint8_t* pv = kv.verif + s * kv.vstride + kv.vo[0];
+  for (int r = lane; r < 256; r += 64) {
+    rs[ps[r]] = (uint8_t)r;
+    rv[pv[r]] = (uint8_t)r;
+  }
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ bool kept_bit(const AppendWs& ws, int64_t vi, int D, int j) {
+  return (ws.bm[vi * (D / 32) + (j >> 5)] >> (j & 31)) & 1u;
+}
+
+__device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// inclusive prefix sum over the 64 lanes
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v, int lane) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t u = __shfl_up(v, o, 64);
+    if (lane >= o) v += u;
+  }
+  return v;
+}
+
+// ---- append, step 3: code bits of each vector ----
+__global__ void __launch_bounds__(64 * kWaves) k_kv_lengths(KvDev kv, const uint16_t* kk,
+                                                            const uint16_t* vv, int ntok,
+                                                            AppendWs ws) {
+  __shared__ uint8_t rs[kWaves][256], rv[kWaves][256];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int64_t nvec = (int64_t)ntok * 2 * kv.H;
+  const int64_t vi = (int64_t)blockIdx.x * kWaves + wv;
+  if (vi >= nvec) return;
+  const int kind = (int)(vi & 1);
+  const int h = (int)((vi >> 1) % kv.H);
+  const int64_t t = (vi >> 1) / kv.H;
+  const int s = 2 * h + kind;
+  load_ranks(kv, s, rs[wv], rv[wv], lane);
+  const uint16_t* x = vec_ptr(kk, vv, t, h, kind, kv.H, kv.D);
+  uint32_t a = 0, b = 0;
+  for (int j = lane; j < kv.D; j += 64) {
+    const int e = (x[j] >> 7) & 0xFF;
+    if (kept_bit(ws, vi, kv.D, j)) a += rs[wv][e] + 1u;
+    else b += rv[wv][e] + 1u;
+  }
+  a = wave_sum(a);
+  b = wave_sum(b);
+  if (lane == 0) {
+    ws.lens[2 * vi] = a;
+    ws.lens[2 * vi + 1] = b;
+  }
+}
+
+// ---- append, step 4: per stream, code positions of the new tokens ----
+__global__ void __launch_bounds__(256) k_kv_scan(KvDev kv, int ntok, int64_t t0, AppendWs ws) {
+  __shared__ unsigned long long tmp[256];
+  __shared__ unsigned long long carry_s[2];
+  const int s = blockIdx.x;
+  const int h = s >> 1, kind = s & 1;
+  const int t = threadIdx.x;
+  unsigned long long base[2] = {kv.state[2 + 2 * s], kv.state[3 + 2 * s]};
+  const unsigned long long cap[2] = {(unsigned long long)kv.ccap, (unsigned long long)kv.vcap};
+  uint32_t* offs[2] = {(uint32_t*)(kv.spec + s * kv.sstride + kv.so[2]),
+                       (uint32_t*)(kv.verif + s * kv.vstride + kv.vo[3])};
+  for (int which = 0; which < 2; ++which) {
+    unsigned long long carry = base[which];
+    bool over = false;
+    for (int c0 = 0; c0 < ntok; c0 += 256) {
+      const int i = c0 + t;
+      const int64_t vi = ((int64_t)i * kv.H + h) * 2 + kind;
+      const unsigned long long len = (i < ntok) ? ws.lens[2 * vi + which] : 0ull;
+      tmp[t] = len;
+      __syncthreads();
+      for (int d = 1; d < 256; d <<= 1) {
+        const unsigned long long add = (t >= d) ? tmp[t - d] : 0ull;
+        __syncthreads();
+        tmp[t] += add;
+        __syncthreads();
+      }
+      const unsigned long long st = carry + tmp[t] - len;
+      if (i < ntok) {
+        const bool fits = st + len <= cap[which];
+        ws.start[2 * vi + which] = fits ? (uint32_t)st : 0xFFFFFFFFu;
+        offs[which][t0 + i] = fits ? (uint32_t)st : 0xFFFFFFFFu;
+        if (!fits) over = true;
+      }
+      if (t == 255) carry_s[which] = carry + tmp[255];
+      __syncthreads();
+      carry = carry_s[which];
+      __syncthreads();
+    }
+    const int any_over = __syncthreads_or(over ? 1 : 0);
+    if (t == 0) {
+      // on overflow the stream is closed: its tail moves to the capacity, so
+      // later appends cannot write over the codes that did fit
+      if (any_over) atomicOr(kv.state + 1, (unsigned long long)CASS_KV_FLAG_OVERFLOW);
+      kv.state[2 + 2 * s + which] = any_over ? cap[which] : carry;
+    }
+  }
+  if (s == 0 && t == 0) kv.state[0] += (unsigned long long)ntok;
+}
+
+__device__ __forceinline__ void or_bits(uint8_t* sec, uint64_t pos, uint32_t v, int width) {
+  // v holds width <= 9 bits; touches at most two 32-bit words
+  if (width == 0 || v == 0) return;
+  uint32_t* w = reinterpret_cast<uint32_t*>(sec) + (pos >> 5);
+  const int sh = (int)(pos & 31);
+  atomicOr(w, v << sh);
+  if (sh + width > 32) atomicOr(w + 1, v >> (32 - sh));
+}
+
+// ---- append, step 5: pack (one wave per vector) ----
+__global__ void __launch_bounds__(64 * kWaves) k_kv_pack(KvDev kv, const uint16_t* kk,
+                                                         const uint16_t* vv, int ntok, int64_t t0,
+                                                         AppendWs ws) {
+  __shared__ uint8_t rs[kWaves][256], rv[kWaves][256];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int64_t nvec = (int64_t)ntok * 2 * kv.H;
+  const int64_t vi = (int64_t)blockIdx.x * kWaves + wv;
+  if (vi >= nvec) return;
+  const int kind = (int)(vi & 1);
+  const int h = (int)((vi >> 1) % kv.H);
+  const int64_t i = (vi >> 1) / kv.H;
+  const int s = 2 * h + kind;
+  const int64_t tok = t0 + i;
+  load_ranks(kv, s, rs[wv], rv[wv], lane);
+  const uint16_t* x = vec_ptr(kk, vv, i, h, kind, kv.H, kv.D);
+  uint8_t* sr = kv.spec + s * kv.sstride;
+  uint8_t* vr = kv.verif + s * kv.vstride;
+  const int D = kv.D, k = kv.k, m = kv.m;
+  if (lane < D / 32) {
+    reinterpret_cast<uint32_t*>(sr + kv.so[1])[tok * (D / 32) + lane] =
+        ws.bm[vi * (D / 32) + lane];
+  }
+  const uint32_t sstart = ws.start[2 * vi], vstart = ws.start[2 * vi + 1];
+  uint32_t kept_carry = 0, scode_carry = 0, vcode_carry = 0;
+  for (int c0 = 0; c0 < D; c0 += 64) {
+    const int j = c0 + lane;
+    const bool in = j < D;
+    const uint16_t b = in ? x[j] : 0;
+    const bool kept = in && kept_bit(ws, vi, D, j);
+    const int sgn = b >> 15, e = (b >> 7) & 0xFF, f = b & 0x7F;
+    const unsigned long long km = __ballot(kept);
+    const unsigned long long pm = __ballot(in && !kept);
+    const uint32_t kidx = kept_carry + (uint32_t)__builtin_popcountll(km & ((1ull << lane) - 1ull));
+    const uint32_t pidx = (uint32_t)(c0 - kept_carry) +
+                          (uint32_t)__builtin_popcountll(pm & ((1ull << lane) - 1ull));
+    const uint32_t slen = kept ? rs[wv][e] + 1u : 0u;
+    const uint32_t vlen = (in && !kept) ? rv[wv][e] + 1u : 0u;
+    const uint32_t sin = wave_incl_scan(slen, lane), vin = wave_incl_scan(vlen, lane);
+    if (kept) {
+      const uint64_t kin = (uint64_t)tok * k + kidx;
+      or_bits(sr + kv.so[3], kin * (uint64_t)(1 + m), (uint32_t)((sgn << m) | (f >> (7 - m))), 1 + m);
+      or_bits(vr + kv.vo[1], kin * (uint64_t)(7 - m), (uint32_t)(f & ((1 << (7 - m)) - 1)), 7 - m);
+      if (sstart != 0xFFFFFFFFu) {  // the code's one bit ends it
+        const uint64_t endbit = (uint64_t)sstart + scode_carry + sin - 1u;
+        or_bits(sr + kv.so[4], endbit, 1u, 1);
+      }
+    } else if (in) {
+      (vr + kv.vo[2])[tok * (D - k) + pidx] = (uint8_t)((sgn << 7) | f);
+      if (vstart != 0xFFFFFFFFu) {
+        const uint64_t endbit = (uint64_t)vstart + vcode_carry + vin - 1u;
+        or_bits(vr + kv.vo[4], endbit, 1u, 1);
+      }
+    }
+    kept_carry += (uint32_t)__builtin_popcountll(km);
+    scode_carry += __shfl(sin, 63, 64);
+    vcode_carry += __shfl(vin, 63, 64);
+  }
+}
+
+// ---- per-lane decoder of one cached vector (token tok of stream s) ----
+template <bool EXACT>
+struct KvVec {
+  BitReader fr, cr, lr, vcr;
+  const uint8_t* perm_s;
+  const uint8_t* perm_v;
+  const uint8_t* pruned;
+  const uint32_t* bm;
+  int m;
+  __device__ __forceinline__ void init(const KvDev& kv, int s, int64_t tok) {
+    const uint8_t* sr = kv.spec + s * kv.sstride;
+    const uint8_t* vr = kv.verif + s * kv.vstride;
+    m = kv.m;
+    bm = reinterpret_cast<const uint32_t*>(sr + kv.so[1]) + tok * (kv.D / 32);
+    perm_s = sr + kv.so[0];
+    fr.init(reinterpret_cast<const uint32_t*>(sr + kv.so[3]), (uint64_t)tok * kv.k * (1 + m));
+    // a token whose codes did not fit (overflow flag) reads code bit 0 instead:
+    // its values are meaningless but every read stays inside the region
+    uint32_t off = reinterpret_cast<const uint32_t*>(sr + kv.so[2])[tok];
+    cr.init(reinterpret_cast<const uint32_t*>(sr + kv.so[4]), off == 0xFFFFFFFFu ? 0u : off);
+    if (EXACT) {
+      perm_v = vr + kv.vo[0];
+      lr.init(reinterpret_cast<const uint32_t*>(vr + kv.vo[1]), (uint64_t)tok * kv.k * (7 - m));
+      pruned = vr + kv.vo[2] + tok * (kv.D - kv.k);
+      off = reinterpret_cast<const uint32_t*>(vr + kv.vo[3])[tok];
+      vcr.init(reinterpret_cast<const uint32_t*>(vr + kv.vo[4]), off == 0xFFFFFFFFu ? 0u : off);
+    }
+  }
+  // bf16 bits of position j (positions are visited in order)
+  __device__ __forceinline__ uint32_t next(uint32_t kept) {
+    if (kept) {
+      const uint32_t f = fr.take(1 + m);
+      const uint32_t e = perm_s[cr.unary()];
+      uint32_t bits = ((f >> m) << 15) | (e << 7) | ((f & ((1u << m) - 1u)) << (7 - m));
+      if (EXACT) bits |= lr.take(7 - m);
+      return bits;
+    }
+    if (!EXACT) return 0u;
+    const uint32_t byte = *pruned++;
+    const uint32_t e = perm_v[vcr.unary()];
+    return ((byte >> 7) << 15) | (e << 7) | (byte & 0x7F);
+  }
+};
+
+// ---- decode the whole cache (tests, checks) ----
+template <bool EXACT>
+__global__ void __launch_bounds__(256) k_kv_decode(KvDev kv, int64_t T, uint16_t* out) {
+  const int64_t n = (int64_t)2 * kv.H * T;
+  for (int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; idx < n;
+       idx += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t tok = idx % T;
+    const int s = (int)(idx / T);  // out is [kind][head][T][D]
+    const int kind = s / kv.H, h = s % kv.H;
+    KvVec<EXACT> dec;
+    dec.init(kv, 2 * h + kind, tok);
+    uint16_t* o = out + idx * kv.D;
+    for (int w = 0; w < kv.D / 32; ++w) {
+      const uint32_t word = dec.bm[w];
+      for (int b = 0; b < 32; ++b) o[w * 32 + b] = (uint16_t)dec.next((word >> b) & 1u);
+    }
+  }
+}
+
+// ---- attention: one workgroup per (KV head, chunk of 256 tokens) ----
+constexpr int kChunk = 256;
+constexpr int kDim = 128;
+constexpr int kVStride = kDim + 2;  // bf16 per LDS row of the value tile (bank spread)
+constexpr int kMaxRows = 32;
+
+struct AttnArgs {
+  const uint16_t* q;  // [nq][Hq][D]
+  int nq, Hq, G;      // G = Hq / H query heads per KV head
+  float scale;
+  int64_t T;          // tokens in the cache
+  int nchunks;
+  float* part;        // [H][nchunks][rows][2 + D]
+};
+
+template <bool EXACT>
+__global__ void __launch_bounds__(256) k_kv_attn(KvDev kv, AttnArgs a) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  float* qf = reinterpret_cast<float*>(smem);                // [rows][128]
+  float* sc = qf + kMaxRows * kDim;                          // [rows][256]
+  uint16_t* vt = reinterpret_cast<uint16_t*>(sc + kMaxRows * kChunk);  // [256][130]
+  __shared__ float red[kMaxRows][4];
+  const int h = blockIdx.x, c = blockIdx.y;
+  const int rows = a.nq * a.G;
+  const int tid = threadIdx.x;
+  // query rows of this KV head: row r = qi * G + g  (query qi, head h*G + g)
+  for (int idx = tid; idx < rows * kDim; idx += 256) {
+    const int r = idx / kDim, d = idx % kDim;
+    const int qi = r / a.G, g = r % a.G;
+    qf[idx] = bf16_bits_to_float(a.q[((int64_t)qi * a.Hq + h * a.G + g) * kDim + d]);
+  }
+  __syncthreads();
+  const int64_t tok = (int64_t)c * kChunk + tid;
+  const bool live = tok < a.T;
+  float s[kMaxRows];
+#pragma unroll
+  for (int r = 0; r < kMaxRows; ++r) s[r] = 0.f;
+  if (live) {  // scores: positions visited in lock-step, so q reads are broadcasts
+    KvVec<EXACT> dec;
+    dec.init(kv, 2 * h, tok);
+    for (int w = 0; w < kDim / 32; ++w) {
+      const uint32_t word = dec.bm[w];
+      for (int b = 0; b < 32; ++b) {
+        const float kvv = bf16_bits_to_float(dec.next((word >> b) & 1u));
+        const int d = w * 32 + b;
+#pragma unroll
+        for (int r = 0; r < kMaxRows; ++r)
+          if (r < rows) s[r] = __builtin_fmaf(kvv, qf[r * kDim + d], s[r]);
+      }
+    }
+  }
+  // causal visibility: query qi sees tokens < T - nq + qi + 1
+#pragma unroll
+  for (int r = 0; r < kMaxRows; ++r) {
+    if (r < rows) {
+      const int qi = r / a.G;
+      const bool vis = live && tok < a.T - a.nq + qi + 1;
+      sc[r * kChunk + tid] = vis ? s[r] * a.scale : -INFINITY;
+    }
+  }
+  // value tile (zero for tokens past the end)
+  {
+    uint16_t* row = vt + tid * kVStride;
+    if (live) {
+      KvVec<EXACT> dec;
+      dec.init(kv, 2 * h + 1, tok);
+      for (int w = 0; w < kDim / 32; ++w) {
+        const uint32_t word = dec.bm[w];
+        for (int b = 0; b < 32; ++b) row[w * 32 + b] = (uint16_t)dec.next((word >> b) & 1u);
+      }
+    } else {
+      for (int d = 0; d < kDim; ++d) row[d] = 0;
+    }
+  }
+  __syncthreads();
+  // per row: max and sum of exp over the chunk
+  const int lane = tid & 63, wv = tid >> 6;
+  for (int r = 0; r < rows; ++r) {
+    float mx = sc[r * kChunk + tid];
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+    if (lane == 0) red[r][wv] = mx;
+  }
+  __syncthreads();
+  for (int r = 0; r < rows; ++r) {
+    const float mx = fmaxf(fmaxf(red[r][0], red[r][1]), fmaxf(red[r][2], red[r][3]));
+    const float sv = sc[r * kChunk + tid];
+    const float p = (mx == -INFINITY || sv == -INFINITY) ? 0.f : __expf(sv - mx);
+    sc[r * kChunk + tid] = p;
+  }
+  __syncthreads();
+  // o[r][d] = sum_t p[r][t] V[t][d]; thread = (d, half of the rows)
+  const int d = tid & (kDim - 1), half = tid >> 7;
+  float* part = a.part + (((int64_t)h * a.nchunks + c) * rows) * (2 + kDim);
+  for (int r = half; r < rows; r += 2) {
+    float acc = 0.f, l = 0.f;
+    for (int t = 0; t < kChunk; ++t) {
+      const float p = sc[r * kChunk + t];
+      acc = __builtin_fmaf(p, bf16_bits_to_float(vt[t * kVStride + d]), acc);
+      l += p;
+    }
+    float* pr = part + (int64_t)r * (2 + kDim);
+    pr[2 + d] = acc;
+    if (d == 0) {
+      const float mx = fmaxf(fmaxf(red[r][0], red[r][1]), fmaxf(red[r][2], red[r][3]));
+      pr[0] = mx;
+      pr[1] = l;
+    }
+  }
+}
+
+// combine the chunk partials: o = sum_c e^{m_c - M} o_c / sum_c e^{m_c - M} l_c
+__global__ void __launch_bounds__(128) k_kv_merge(AttnArgs a, int H, float* out) {
+  const int rows = a.nq * a.G;
+  const int hr = blockIdx.x;  // h * rows + r
+  const int h = hr / rows, r = hr % rows;
+  const int d = threadIdx.x;
+  const float* base = a.part + ((int64_t)h * a.nchunks * rows + r) * (2 + kDim);
+  const int64_t cstride = (int64_t)rows * (2 + kDim);
+  float M = -INFINITY;
+  for (int c = 0; c < a.nchunks; ++c) M = fmaxf(M, base[c * cstride]);
+  float num = 0.f, den = 0.f;
+  for (int c = 0; c < a.nchunks; ++c) {
+    const float mc = base[c * cstride];
+    if (mc == -INFINITY) continue;
+    const float wgt = __expf(mc - M);
+    num += wgt * base[c * cstride + 2 + d];
+    den += wgt * base[c * cstride + 1];
+  }
+  const int qi = r / a.G, g = r % a.G;
+  out[((int64_t)qi * a.Hq + h * a.G + g) * kDim + d] = num / den;
+}
+
+int64_t aln256(int64_t v) { return (v + 255) / 256 * 256; }
+int64_t part_at(int64_t* pos, int64_t bytes) {
+  const int64_t o = *pos;
+  *pos = aln256(*pos + bytes + 16);
+  return o;
+}
+
+int check_kv_params(const cass_kv_params* p) {
+  if (!p) return report(CASS_ERR_INVALID, "kv params is NULL");
+  if (p->n_kv_heads < 1 || p->n_kv_heads > 64 || p->head_dim < 32 || p->head_dim > 256 ||
+      p->head_dim % 32 || p->keep < 0 || p->keep > p->head_dim || p->mant_bits < 0 ||
+      p->mant_bits > 7 || p->max_tokens < 0 || p->code_cap_bits < 0 || p->vcode_cap_bits < 0 ||
+      p->code_cap_bits >= ((int64_t)1 << 32) || p->vcode_cap_bits >= ((int64_t)1 << 32))
+    return report(CASS_ERR_INVALID, "bad kv params");
+  return CASS_OK;
+}
+
+void kv_layout(const cass_kv_params* p, int64_t* so, int64_t* vo, int64_t* sb, int64_t* vb) {
+  const int64_t D = p->head_dim, k = p->keep, m = p->mant_bits, T = p->max_tokens;
+  int64_t pos = 0;
+  so[0] = part_at(&pos, 256);
+  so[1] = part_at(&pos, T * D / 8);
+  so[2] = part_at(&pos, 4 * T);
+  so[3] = part_at(&pos, (T * k * (1 + m) + 7) / 8);
+  so[4] = part_at(&pos, (p->code_cap_bits + 7) / 8);
+  *sb = pos;
+  pos = 0;
+  vo[0] = part_at(&pos, 256);
+  vo[1] = part_at(&pos, (T * k * (7 - m) + 7) / 8);
+  vo[2] = part_at(&pos, T * (D - k));
+  vo[3] = part_at(&pos, 4 * T);
+  vo[4] = part_at(&pos, (p->vcode_cap_bits + 7) / 8);
+  *vb = pos;
+}
+
+KvDev dev_of(const cass_kv* kv) {
+  KvDev d;
+  d.spec = (uint8_t*)kv->spec;
+  d.verif = (uint8_t*)kv->verif;
+  d.state = (unsigned long long*)kv->state;
+  d.sstride = kv->spec_stream_bytes;
+  d.vstride = kv->verif_stream_bytes;
+  for (int i = 0; i < 5; ++i) {
+    d.so[i] = kv->spec_part[i];
+    d.vo[i] = kv->verif_part[i];
+  }
+  d.H = kv->p.n_kv_heads;
+  d.D = kv->p.head_dim;
+  d.k = kv->p.keep;
+  d.m = kv->p.mant_bits;
+  d.T_max = kv->p.max_tokens;
+  d.ccap = kv->p.code_cap_bits;
+  d.vcap = kv->p.vcode_cap_bits;
+  return d;
+}
+
+int check_kv(const cass_kv* kv) {
+  if (!kv) return report(CASS_ERR_INVALID, "kv is NULL");
+  int st = check_kv_params(&kv->p);
+  if (st) return st;
+  if (!kv->spec || !kv->verif || !kv->state) return report(CASS_ERR_INVALID, "kv buffers missing");
+  if (kv->tokens < 0 || kv->tokens > kv->p.max_tokens)
+    return report(CASS_ERR_INVALID, "kv token count out of range");
+  return CASS_OK;
+}
+
+int64_t append_ws_layout(const cass_kv* kv, int ntok, AppendWs* ws, uint8_t* base) {
+  const int64_t nvec = (int64_t)ntok * 2 * kv->p.n_kv_heads;
+  int64_t pos = 0;
+  auto take = [&](int64_t bytes) {
+    uint8_t* p = base ? base + pos : nullptr;
+    pos = aln256(pos + (bytes > 0 ? bytes : 1));
+    return p;
+  };
+  AppendWs w;
+  w.bm = (uint32_t*)take(nvec * (kv->p.head_dim / 32) * 4);
+  w.lens = (uint32_t*)take(nvec * 2 * 4);
+  w.start = (uint32_t*)take(nvec * 2 * 4);
+  w.hist = (uint32_t*)take((int64_t)2 * kv->p.n_kv_heads * 512 * 4);
+  if (ws) *ws = w;
+  return pos;
+}
+
+int64_t attn_ws(const cass_kv* kv, int nq, int G) {
+  const int64_t nchunks = (kv->tokens + kChunk - 1) / kChunk;
+  return (int64_t)kv->p.n_kv_heads * nchunks * nq * G * (2 + kDim) * 4;
+}
+
+unsigned grid_of(int64_t n, int per) {
+  int64_t g = (n + per - 1) / per;
+  return (unsigned)(g < 1 ? 1 : g);
+}
+
+int run_attention(const cass_kv* kv, const uint16_t* q, int nq, int n_q_heads, float scale,
+                  float* out, void* ws, int64_t ws_bytes, hipStream_t stream, bool exact) {
+  int st = check_kv(kv);
+  if (st) return st;
+  const int H = kv->p.n_kv_heads;
+  if (kv->p.head_dim != kDim) return report(CASS_ERR_UNSUPPORTED, "attention needs head_dim 128");
+  if (n_q_heads < H || n_q_heads % H) return report(CASS_ERR_INVALID, "n_q_heads must be a multiple of n_kv_heads");
+  const int G = n_q_heads / H;
+  if (nq < 1 || nq * G > kMaxRows) return report(CASS_ERR_UNSUPPORTED, "nq * heads per group > 32");
+  if (kv->tokens < nq) return report(CASS_ERR_INVALID, "cache holds fewer tokens than queries");
+  if (!q || !out) return report(CASS_ERR_INVALID, "q or out is NULL");
+  const int64_t need = attn_ws(kv, nq, G);
+  if (!ws || ws_bytes < need) return report(CASS_ERR_CAPACITY, "attention workspace too small");
+  AttnArgs a;
+  a.q = q;
+  a.nq = nq;
+  a.Hq = n_q_heads;
+  a.G = G;
+  a.scale = scale;
+  a.T = kv->tokens;
+  a.nchunks = (int)((kv->tokens + kChunk - 1) / kChunk);
+  a.part = (float*)ws;
+  const KvDev d = dev_of(kv);
+  const size_t lds = (size_t)kMaxRows * kDim * 4 + (size_t)kMaxRows * kChunk * 4 +
+                     (size_t)kChunk * kVStride * 2;
+  const void* fn = exact ? (const void*)&k_kv_attn<true> : (const void*)&k_kv_attn<false>;
+  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return report(CASS_ERR_HIP, "attention LDS: %s", hipGetErrorString(e));
+  if (exact)
+    k_kv_attn<true><<<dim3(H, a.nchunks), 256, lds, stream>>>(d, a);
+  else
+    k_kv_attn<false><<<dim3(H, a.nchunks), 256, lds, stream>>>(d, a);
+  if ((e = hipGetLastError()) != hipSuccess) return report(CASS_ERR_HIP, "attention: %s", hipGetErrorString(e));
+  k_kv_merge<<<H * nq * G, kDim, 0, stream>>>(a, H, out);
+  if ((e = hipGetLastError()) != hipSuccess) return report(CASS_ERR_HIP, "merge: %s", hipGetErrorString(e));
+  return CASS_OK;
+}
+
+}  // namespace
+
+}  // namespace cass
+
+using namespace cass;
+
+extern "C" {
+
+int cass_kv_bytes(const cass_kv_params* p, int64_t* spec_bytes, int64_t* verif_bytes,
+                  int64_t* state_bytes) {
+  clear_error();
+  int st = check_kv_params(p);
+  if (st) return st;
+  int64_t so[5], vo[5], sb, vb;
+  kv_layout(p, so, vo, &sb, &vb);
+  if (spec_bytes) *spec_bytes = sb * 2 * p->n_kv_heads;
+  if (verif_bytes) *verif_bytes = vb * 2 * p->n_kv_heads;
+  if (state_bytes) *state_bytes = CASS_KV_STATE_BYTES;
+  return CASS_OK;
+}
+
+int cass_kv_init(cass_kv* kv, const cass_kv_params* p, void* spec, void* verif, void* state,
+                 hipStream_t stream) {
+  clear_error();
+  int st = check_kv_params(p);
+  if (st) return st;
+  if (!kv || !spec || !verif || !state) return report(CASS_ERR_INVALID, "NULL argument");
+  if (((uintptr_t)spec | (uintptr_t)verif | (uintptr_t)state) % 256)
+    return report(CASS_ERR_INVALID, "kv buffers must be 256-byte aligned");
+  memset(kv, 0, sizeof *kv);
+  kv->p = *p;
+  kv->spec = spec;
+  kv->verif = verif;
+  kv->state = state;
+  kv_layout(p, kv->spec_part, kv->verif_part, &kv->spec_stream_bytes, &kv->verif_stream_bytes);
+  kv->tokens = 0;
+  hipError_t e;
+  if ((e = launch_fill_zero(spec, kv->spec_stream_bytes * 2 * p->n_kv_heads, stream)) != hipSuccess ||
+      (e = launch_fill_zero(verif, kv->verif_stream_bytes * 2 * p->n_kv_heads, stream)) != hipSuccess ||
+      (e = launch_fill_zero(state, CASS_KV_STATE_BYTES, stream)) != hipSuccess)
+    return report(CASS_ERR_HIP, "kv init: %s", hipGetErrorString(e));
+  return CASS_OK;
+}
+
+int cass_kv_append_ws_bytes(const cass_kv* kv, int ntok, int64_t* ws_bytes) {
+  clear_error();
+  int st = check_kv(kv);
+  if (st) return st;
+  if (ntok < 0 || !ws_bytes) return report(CASS_ERR_INVALID, "bad ntok or ws_bytes");
+  *ws_bytes = append_ws_layout(kv, ntok, nullptr, nullptr);
+  return CASS_OK;
+}
+
+int cass_kv_append_encode(cass_kv* kv, const uint16_t* k, const uint16_t* v, int ntok, void* ws,
+                          int64_t ws_bytes, hipStream_t stream) {
+  clear_error();
+  int st = check_kv(kv);
+  if (st) return st;
+  if (ntok < 0) return report(CASS_ERR_INVALID, "ntok < 0");
+  if (ntok == 0) return CASS_OK;
+  if (!k || !v) return report(CASS_ERR_INVALID, "k or v is NULL");
+  if (kv->tokens + ntok > kv->p.max_tokens) return report(CASS_ERR_CAPACITY, "cache full");
+  const int64_t need = append_ws_layout(kv, ntok, nullptr, nullptr);
+  if (!ws || ws_bytes < need) return report(CASS_ERR_CAPACITY, "append workspace too small");
+  AppendWs w;
+  append_ws_layout(kv, ntok, &w, (uint8_t*)ws);
+  const KvDev d = dev_of(kv);
+  const int first = kv->tokens == 0;
+  const int64_t nvec = (int64_t)ntok * 2 * kv->p.n_kv_heads;
+  hipError_t e;
+  if (first && (e = launch_fill_zero(w.hist, (int64_t)2 * kv->p.n_kv_heads * 512 * 4, stream)) != hipSuccess)
+    return report(CASS_ERR_HIP, "append: %s", hipGetErrorString(e));
+  k_kv_select<<<grid_of(nvec, kWaves), 64 * kWaves, 0, stream>>>(d, k, v, ntok, first, w);
+  if (first) k_kv_ranks<<<2 * kv->p.n_kv_heads, 256, 0, stream>>>(d, w);
+  k_kv_lengths<<<grid_of(nvec, kWaves), 64 * kWaves, 0, stream>>>(d, k, v, ntok, w);
+  k_kv_scan<<<2 * kv->p.n_kv_heads, 256, 0, stream>>>(d, ntok, kv->tokens, w);
+  k_kv_pack<<<grid_of(nvec, kWaves), 64 * kWaves, 0, stream>>>(d, k, v, ntok, kv->tokens, w);
+  if ((e = hipGetLastError()) != hipSuccess) return report(CASS_ERR_HIP, "append: %s", hipGetErrorString(e));
+  kv->tokens += ntok;
+  return CASS_OK;
+}
+
+int cass_kv_status(const cass_kv* kv, int64_t* tokens, uint32_t* flags, hipStream_t stream) {
+  clear_error();
+  int st = check_kv(kv);
+  if (st) return st;
+  unsigned long long h[2];
+  hipError_t e = hipMemcpyAsync(h, kv->state, sizeof h, hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return report(CASS_ERR_HIP, "kv status: %s", hipGetErrorString(e));
+  if (tokens) *tokens = (int64_t)h[0];
+  if (flags) *flags = (uint32_t)h[1];
+  return CASS_OK;
+}
+
+int cass_kv_decode(const cass_kv* kv, int exact, uint16_t* out, hipStream_t stream) {
+  clear_error();
+  int st = check_kv(kv);
+  if (st) return st;
+  if (kv->tokens == 0) return CASS_OK;
+  if (!out) return report(CASS_ERR_INVALID, "out is NULL");
+  const KvDev d = dev_of(kv);
+  const int64_t n = (int64_t)2 * kv->p.n_kv_heads * kv->tokens;
+  unsigned g = grid_of(n, 256);
+  if (g > 65535u * 4) g = 65535u * 4;
+  if (exact) k_kv_decode<true><<<g, 256, 0, stream>>>(d, kv->tokens, out);
+  else k_kv_decode<false><<<g, 256, 0, stream>>>(d, kv->tokens, out);
+  hipError_t e = hipGetLastError();
+  return e == hipSuccess ? CASS_OK : report(CASS_ERR_HIP, "kv decode: %s", hipGetErrorString(e));
+}
+
+int cass_kv_attn_ws_bytes(const cass_kv* kv, int nq, int n_q_heads, int64_t* ws_bytes) {
+  clear_error();
+  int st = check_kv(kv);
+  if (st) return st;
+  if (nq < 1 || n_q_heads < kv->p.n_kv_heads || n_q_heads % kv->p.n_kv_heads || !ws_bytes)
+    return report(CASS_ERR_INVALID, "bad attention shape");
+  *ws_bytes = attn_ws(kv, nq, n_q_heads / kv->p.n_kv_heads);
+  return CASS_OK;
+}
+
+int cass_kv_draft_attn(const cass_kv* kv, const uint16_t* q, int n_q_heads, float scale, float* out,
+                       void* ws, int64_t ws_bytes, hipStream_t stream) {
+  clear_error();
+  return run_attention(kv, q, 1, n_q_heads, scale, out, ws, ws_bytes, stream, false);
+}
+
+int cass_kv_verify_attn(const cass_kv* kv, const uint16_t* q, int nq, int n_q_heads, float scale,
+                        float* out, void* ws, int64_t ws_bytes, hipStream_t stream) {
+  clear_error();
+  if (nq > 8) return report(CASS_ERR_UNSUPPORTED, "nq > 8");
+  return run_attention(kv, q, nq, n_q_heads, scale, out, ws, ws_bytes, stream, true);
+}
+
+}  // extern "C"

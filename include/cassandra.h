@@ -177,6 +177,86 @@ int cass_draft_decode(const cass_tensor* W, uint16_t* out, hipStream_t stream);
 int cass_tensor_validate(const void* spec, int64_t spec_bytes, const void* verif,
                          int64_t verif_bytes);
 
+/* ------------------------------------------------------------- KV cache
+ * Online compression of one layer's KV cache (Cassandra review, section 3.3:
+ * KV entries are produced during inference, so the encoder runs online;
+ * section 3.1: the KV cache gets the same pruning, truncation and exponent
+ * coding as the weights).  The pruning group is one token's vector of one
+ * head (head_dim values).  Each (head, K|V) pair is one append-only stream,
+ * stream index 2*head + (0 for K, 1 for V), each with its own region of
+ * spec_stream_bytes in `spec` and verif_stream_bytes in `verif`:
+ *   speculation region: rank table (256 B) | keep bitmap (max_tokens *
+ *     head_dim bits) | code offsets (u32 per token: bit offset of the token's
+ *     first code) | fields ((s<<m)|ft, 1+m bits, token t value i at bit
+ *     (t*keep+i)*(1+m)) | codes (code_cap_bits)
+ *   verification region: rank table | low mantissas (7-m bits, same order) |
+ *     pruned bytes (token t, pruned i at byte t*(head_dim-keep)+i) | code
+ *     offsets | codes (vcode_cap_bits)
+ * Each part starts on a multiple of 256 bytes and is followed by >= 16 zero
+ * bytes.  The rank tables are built on the device from the first append's
+ * tokens and frozen afterwards.  `state` (device, CASS_KV_STATE_BYTES) holds
+ * the token count, flags and the code tails of every stream. */
+#define CASS_KV_STATE_BYTES 4096
+enum { CASS_KV_FLAG_TABLES = 1, CASS_KV_FLAG_OVERFLOW = 2 };
+
+typedef struct cass_kv_params {
+  int32_t n_kv_heads;      /* 1..64 */
+  int32_t head_dim;        /* multiple of 32, at most 256 */
+  int32_t keep;            /* values kept per token vector, 0..head_dim */
+  int32_t mant_bits;       /* 0..7 */
+  int64_t max_tokens;
+  int64_t code_cap_bits;   /* speculation code capacity per stream, < 2^32 */
+  int64_t vcode_cap_bits;  /* verification code capacity per stream, < 2^32 */
+} cass_kv_params;
+
+typedef struct cass_kv {
+  cass_kv_params p;
+  void* spec;               /* device, 2*n_kv_heads*spec_stream_bytes */
+  void* verif;              /* device, 2*n_kv_heads*verif_stream_bytes */
+  void* state;              /* device, CASS_KV_STATE_BYTES */
+  int64_t spec_stream_bytes, verif_stream_bytes;
+  int64_t spec_part[5], verif_part[5]; /* part offsets inside a stream region */
+  int64_t tokens;           /* tokens appended so far (host copy, kept by the calls) */
+} cass_kv;
+
+/* Buffer sizes for a cache with these parameters. */
+int cass_kv_bytes(const cass_kv_params* p, int64_t* spec_bytes, int64_t* verif_bytes,
+                  int64_t* state_bytes);
+/* Fill *kv and zero the three device buffers (asynchronous). */
+int cass_kv_init(cass_kv* kv, const cass_kv_params* p, void* spec, void* verif, void* state,
+                 hipStream_t stream);
+/* Workspace bytes cass_kv_append_encode needs for ntok tokens. */
+int cass_kv_append_ws_bytes(const cass_kv* kv, int ntok, int64_t* ws_bytes);
+/* Append ntok tokens: k, v device bf16 [ntok][n_kv_heads][head_dim].  The
+ * first call also builds the rank tables from its tokens.  Pruning, splitting,
+ * coding and packing all run on the device without a host synchronisation;
+ * codes that would exceed a stream's capacity are not written and raise
+ * CASS_KV_FLAG_OVERFLOW (see cass_kv_status).  Advances kv->tokens. */
+int cass_kv_append_encode(cass_kv* kv, const uint16_t* k, const uint16_t* v, int ntok,
+                          void* ws, int64_t ws_bytes, hipStream_t stream);
+/* Token count and flags from the device state (synchronises the stream). */
+int cass_kv_status(const cass_kv* kv, int64_t* tokens, uint32_t* flags, hipStream_t stream);
+/* Decoded cache: out device bf16 [2][n_kv_heads][tokens][head_dim] (K then
+ * V); exact != 0 rebuilds the original values, else the zero-filled draft. */
+int cass_kv_decode(const cass_kv* kv, int exact, uint16_t* out, hipStream_t stream);
+
+/* Workspace bytes for an attention call over the current tokens. */
+int cass_kv_attn_ws_bytes(const cass_kv* kv, int nq, int n_q_heads, int64_t* ws_bytes);
+/* Draft attention of one query (grouped-query: query head g reads KV head
+ * g / (n_q_heads / n_kv_heads)) over all cached tokens, on the zero-filled
+ * draft keys and values: out[g][d] = sum_t softmax_t(scale * q_g . K~_t) V~_t[d].
+ * q: device bf16 [n_q_heads][head_dim]; out: device fp32 [n_q_heads][head_dim].
+ * head_dim must be 128. */
+int cass_kv_draft_attn(const cass_kv* kv, const uint16_t* q, int n_q_heads, float scale,
+                       float* out, void* ws, int64_t ws_bytes, hipStream_t stream);
+/* Verification attention for the nq = k+1 newest tokens (Cassandra review,
+ * section 1: the drafted tokens are verified in one parallel pass) on the
+ * exact keys and values: query i sees tokens 0 .. tokens-nq+i (causal over
+ * the appended block).  q: [nq][n_q_heads][head_dim] bf16; out: fp32, same
+ * shape.  nq <= 8, n_q_heads / n_kv_heads * nq <= 32, head_dim 128. */
+int cass_kv_verify_attn(const cass_kv* kv, const uint16_t* q, int nq, int n_q_heads, float scale,
+                        float* out, void* ws, int64_t ws_bytes, hipStream_t stream);
+
 const char* cass_status_string(int status);
 /* Detail of the last error on the calling thread ("" if none). */
 const char* cass_last_error(void);

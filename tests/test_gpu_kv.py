@@ -1,0 +1,156 @@
+"""GPU parity of the compressed KV cache against the CPU oracle, through the
+C ABI: stream regions byte for byte (one append, and token-at-a-time appends
+after a first chunk), decode bit for bit, draft and verification attention
+within tolerance of the fp64 oracle.
+
+Attention tolerance (the pages fix none): |o - o_ref| <= 2e-3 * sum_t p_t |V_t|
++ 1e-6 per element, with p the oracle's softmax weights; the sum is obtained as
+the oracle's attention of the same queries over |V|.
+"""
+import numpy as np
+import pytest
+
+import synth
+
+pytestmark = pytest.mark.gpu
+
+D = 128
+
+
+@pytest.fixture(scope="module")
+def gpu():
+    import torch
+    import bit_level_weight_amd as cass
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    cass.lib()
+    return torch, cass
+
+
+def dev(torch, a):
+    a = np.ascontiguousarray(a, dtype=np.uint16)
+    return torch.from_numpy(a.view(np.int16)).cuda()
+
+
+def make_kv(T, H, seed):
+    return synth.kv_tensor(T, H, D, seed), synth.kv_tensor(T, H, D, seed + 1)
+
+
+def check_regions(torch, cache, orc, Kt, Vt, T0, k, m):
+    """Every stream region equals the oracle's encoding of that stream."""
+    H = Kt.shape[1]
+    p = cache.params
+    spec = cache.spec.cpu().numpy()
+    verif = cache.verif.cpu().numpy()
+    ss, vs = cache.kv.spec_stream_bytes, cache.kv.verif_stream_bytes
+    for h in range(H):
+        for kind, X in ((0, Kt), (1, Vt)):
+            s = 2 * h + kind
+            so, vo, tails = orc.kv_encode(X[:, h, :], T0, k, m, p.max_tokens, p.code_cap_bits,
+                                          p.vcode_cap_bits)
+            assert np.array_equal(spec[s * ss:(s + 1) * ss], so), f"spec stream {s}"
+            assert np.array_equal(verif[s * vs:(s + 1) * vs], vo), f"verif stream {s}"
+
+
+@pytest.mark.parametrize("T,H,k,m", [(300, 8, 38, 3), (1, 2, 38, 3), (77, 3, 0, 2),
+                                     (64, 2, 128, 7), (130, 4, 64, 0)])
+def test_kv_append_one_call(gpu, orc, T, H, k, m):
+    torch, cass = gpu
+    print("case", T, H, k, m, flush=True)
+    Kt, Vt = make_kv(T, H, 100 + T + k)
+    cache = cass.KvCache(H, D, k, m, max_tokens=T + 16)
+    cache.append(dev(torch, Kt), dev(torch, Vt))
+    torch.cuda.synchronize()
+    assert cass.cass_kv_status(cache.kv) == (T, cass.CASS_KV_FLAG_TABLES)
+    check_regions(torch, cache, orc, Kt, Vt, T, k, m)
+    out = torch.empty((2, H, T, D), dtype=torch.int16, device="cuda")
+    cass.cass_kv_decode(cache.kv, True, out)
+    torch.cuda.synchronize()
+    o = out.cpu().numpy().view(np.uint16)
+    assert np.array_equal(o[0], Kt.transpose(1, 0, 2)) and np.array_equal(o[1], Vt.transpose(1, 0, 2))
+
+
+def test_kv_token_at_a_time_equals_one_call(gpu, orc):
+    """A first chunk of T0 tokens then single-token appends gives the bytes of
+    one encoding with the tables of the first chunk."""
+    torch, cass = gpu
+    T, T0, H, k, m = 96, 40, 8, 38, 3
+    Kt, Vt = make_kv(T, H, 7)
+    cache = cass.KvCache(H, D, k, m, max_tokens=128)
+    cache.append(dev(torch, Kt[:T0]), dev(torch, Vt[:T0]))
+    for t in range(T0, T):
+        cache.append(dev(torch, Kt[t:t + 1]), dev(torch, Vt[t:t + 1]))
+    torch.cuda.synchronize()
+    assert cache.tokens == T
+    check_regions(torch, cache, orc, Kt, Vt, T0, k, m)
+    out = torch.empty((2, H, T, D), dtype=torch.int16, device="cuda")
+    cass.cass_kv_decode(cache.kv, False, out)
+    torch.cuda.synchronize()
+    p = cache.params
+    so, _, _ = orc.kv_encode(Kt[:, 3, :], T0, k, m, p.max_tokens, p.code_cap_bits, p.vcode_cap_bits)
+    draft_ref = orc.kv_decode(so, T, D, k, m, p.max_tokens, p.code_cap_bits, p.vcode_cap_bits)
+    assert np.array_equal(out.cpu().numpy().view(np.uint16)[0, 3], draft_ref)
+
+
+def test_kv_overflow_flag(gpu):
+    torch, cass = gpu
+    Kt, Vt = make_kv(32, 2, 9)
+    cache = cass.KvCache(2, D, 38, 3, max_tokens=64, code_cap_bits=100, vcode_cap_bits=100)
+    cache.append(dev(torch, Kt), dev(torch, Vt))
+    torch.cuda.synchronize()
+    t, flags = cass.cass_kv_status(cache.kv)
+    assert t == 32 and flags & cass.CASS_KV_FLAG_OVERFLOW
+
+
+def attn_check(got, ref, bound):
+    err = np.abs(got.astype(np.float64) - ref)
+    tol = 2e-3 * bound + 1e-6
+    assert (err <= tol).all(), f"worst ratio {(err / tol).max():.3g}"
+
+
+def oracle_attention(orc, q_rows, Kh, Vh, scale, visible=None):
+    out = orc.attention(q_rows, Kh, Vh, scale, visible)
+    absV = Vh & np.uint16(0x7FFF)
+    bound = orc.attention(q_rows, Kh, absV, scale, visible)
+    return out, bound
+
+
+@pytest.mark.parametrize("T", [1, 200, 700])
+def test_draft_and_verify_attention(gpu, orc, T):
+    torch, cass = gpu
+    H, Hq, k, m, nq = 8, 32, 38, 3, 5
+    G = Hq // H
+    Kt, Vt = make_kv(T + nq, H, 50 + T)
+    cache = cass.KvCache(H, D, k, m, max_tokens=T + nq + 8)
+    cache.append(dev(torch, Kt[:T]), dev(torch, Vt[:T]))
+    scale = 1.0 / np.sqrt(D)
+    q1 = synth.activations(Hq, D, 4, t0=T)
+    ws = torch.empty(cass.cass_kv_attn_ws_bytes(cache.kv, nq, Hq) + 256, dtype=torch.uint8, device="cuda")
+    out = torch.empty((Hq, D), dtype=torch.float32, device="cuda")
+    cass.cass_kv_draft_attn(cache.kv, dev(torch, q1), scale, out, ws)
+    torch.cuda.synchronize()
+    p = cache.params
+    got = out.cpu().numpy()
+    for h in range(H):
+        sk, _, _ = orc.kv_encode(Kt[:T, h, :], T, k, m, p.max_tokens, p.code_cap_bits, p.vcode_cap_bits)
+        sv, _, _ = orc.kv_encode(Vt[:T, h, :], T, k, m, p.max_tokens, p.code_cap_bits, p.vcode_cap_bits)
+        Kd = orc.kv_decode(sk, T, D, k, m, p.max_tokens, p.code_cap_bits, p.vcode_cap_bits)
+        Vd = orc.kv_decode(sv, T, D, k, m, p.max_tokens, p.code_cap_bits, p.vcode_cap_bits)
+        ref, bound = oracle_attention(orc, q1[h * G:(h + 1) * G], Kd, Vd, scale)
+        attn_check(got[h * G:(h + 1) * G], ref, bound)
+    # verification: append the nq drafted tokens, then attend causally on exact KV
+    if T < nq:
+        return
+    cache.append(dev(torch, Kt[T:T + nq]), dev(torch, Vt[T:T + nq]))
+    qv = np.stack([synth.activations(Hq, D, 5, t0=T + i) for i in range(nq)])
+    outv = torch.empty((nq, Hq, D), dtype=torch.float32, device="cuda")
+    ws = torch.empty(cass.cass_kv_attn_ws_bytes(cache.kv, nq, Hq) + 256, dtype=torch.uint8, device="cuda")
+    cass.cass_kv_verify_attn(cache.kv, dev(torch, qv), scale, outv, ws)
+    torch.cuda.synchronize()
+    gotv = outv.cpu().numpy()
+    Ttot = T + nq
+    for h in range(H):
+        for g in range(G):
+            rows = qv[:, h * G + g, :]
+            vis = [Ttot - nq + i + 1 for i in range(nq)]
+            ref, bound = oracle_attention(orc, rows, Kt[:Ttot, h, :], Vt[:Ttot, h, :], scale, vis)
+            attn_check(gotv[:, h * G + g, :], ref, bound)
