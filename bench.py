@@ -1,16 +1,23 @@
 #!/usr/bin/env python3
-"""Benchmark: Cassandra draft GEMV on one Llama-3-8B-shaped decoder layer, bs=1.
+"""Benchmark of the Cassandra hot path on one MI355X.
 
-One step = the draft GEMVs of one decode step of the layer, i.e. the four
-fused projections q|k|v (6144x4096), o (4096x4096), gate|up (28672x4096) and
-down (4096x14336), each a cass_draft_gemv call that streams the speculation
-bytes of that matrix from HBM.  Steps rotate over `--copies` distinct encoded
-layers so the bytes come from HBM, not from the 256 MB last-level cache.
+Headline (the printed `value`): draft GEMV throughput on the speculation
+(compressed) bytes of one Llama-3-8B-shaped decoder layer at batch 1, keep 0.3,
+3 mantissa bits, Cassandra-1.  One step = the draft GEMVs of one decode step of
+the layer: the fused projections q|k|v (6144x4096), o (4096x4096), gate|up
+(28672x4096) and down (4096x14336), each one cass_draft_gemv call.  Steps
+rotate over --copies distinct encoded layers so the bytes come from HBM, not
+from the 256 MB last-level cache.
 
-Prints ONE JSON line: value = speculation-stream bytes / second over the timed
-steps (GB/s), plus the roofline of the GEMV kernel (HIP events around every
-launch), per-row timings of the other hot-path calls (encode, verify GEMM N=5,
-reconstruct, draft decode) and the CPU oracle timed on a row sample.
+The same JSON line also carries the roofline of the GEMV kernel (HIP events
+around every launch), the other hot-path calls (encode, verification GEMM for
+5 tokens, reconstruction, draft decode), the keep x mantissa sweep, the
+32-layer stack (tokens/s-equivalent), the compressed KV cache at 32K / 64K
+context (append latency, draft and verification attention), the Qwen3-4B
+Cassandra-2 stack at batch 2, and the CPU oracle timed on a row sample.
+
+Modes for profiling: --mode gemv runs only the timed GEMV steps; --mode copy
+runs a plain 1 GiB device copy (to calibrate the HBM byte counters).
 """
 from __future__ import annotations
 
@@ -38,7 +45,8 @@ def parse():
     ap.add_argument("--mant", type=int, default=3)
     ap.add_argument("--block", type=int, default=256)
     ap.add_argument("--copies", type=int, default=8)
-    ap.add_argument("--sweep", action="store_true", help="also time the 3x3 keep x mant grid")
+    ap.add_argument("--mode", choices=("full", "gemv", "copy"), default="full")
+    ap.add_argument("--no-extras", action="store_true", help="headline and CPU baseline only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     return ap.parse_args()
@@ -49,28 +57,44 @@ def log(*a):
 
 
 def torch_layer(torch, shapes, gen, sigma=0.02, outlier_frac=0.01):
-    """A further seeded layer drawn on the GPU (torch generator), same recipe:
-    N(0, sigma^2) rounded to bf16, 1% of input columns x10."""
-    out = {}
+    """A further seeded layer drawn on the GPU with torch's generator, same
+    recipe: N(0, sigma^2) rounded to bf16, round(1%) of input columns x10."""
     parts = {}
     for name, (r, c) in shapes.items():
         a = torch.randn((r, c), generator=gen, device="cuda", dtype=torch.float32) * sigma
-        cols = torch.randperm(c, generator=gen, device="cuda")[: int(round(outlier_frac * c))]
-        a[:, cols] *= 10.0
+        n_out = int(round(outlier_frac * c))
+        if n_out:
+            cols = torch.randperm(c, generator=gen, device="cuda")[:n_out]
+            a[:, cols] *= 10.0
         parts[name] = a.to(torch.bfloat16).view(torch.int16)
         del a
-    out["qkv"] = torch.cat([parts["q"], parts["k"], parts["v"]], 0)
-    out["o"] = parts["o"]
-    out["gu"] = torch.cat([parts["gate"], parts["up"]], 0)
-    out["down"] = parts["down"]
-    return out
+    return {"qkv": torch.cat([parts["q"], parts["k"], parts["v"]], 0), "o": parts["o"],
+            "gu": torch.cat([parts["gate"], parts["up"]], 0), "down": parts["down"]}
+
+
+class Timer:
+    def __init__(self, torch, stream):
+        self.torch, self.stream = torch, stream
+
+    def ms(self, fn, reps=10, warm=1):
+        torch = self.torch
+        for _ in range(warm):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(self.stream)
+        for _ in range(reps):
+            fn()
+        b.record(self.stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
 
 
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: the draft GEMV streams one GPU's share of the "
-              "weights and needs no collective; run it with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU (the path shards by rows with no exchange besides "
+              "an all-gather of outputs); run it with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -81,9 +105,19 @@ def main():
     cass.lib()
     torch.cuda.set_device(0)
     stream = torch.cuda.current_stream()
+    timer = Timer(torch, stream)
     dev16 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint16).view(np.int16)).cuda()
 
-    # ---- inputs: layer 0 from the numpy recipe, further copies from a seeded torch generator
+    if args.mode == "copy":
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"mode": "copy", "bytes": 1 << 30}))
+        return
+
+    # ---- inputs: layer 0 from the numpy recipe, further copies from torch's generator
     t0 = time.time()
     layer0 = synth.fused_layer(synth.LLAMA3_8B, config=2, layer=0, outlier_frac=0.01)
     layers = [{k: dev16(v) for k, v in layer0.items()}]
@@ -94,23 +128,21 @@ def main():
     torch.cuda.synchronize()
     log(f"inputs ready in {time.time() - t0:.1f}s")
 
-    def encode_layer(L, keep, mant, ws):
-        return {n: cass.encode(L[n], synth.keep_count(keep, L[n].shape[1]), mant,
-                               block=args.block, ws=ws) for n in MATS}
-
     ws = torch.empty(cass.cass_encode_ws_bytes(28672, 4096, cass._params(1, 3, args.block, 1)),
                      dtype=torch.uint8, device="cuda")
-    t0 = time.time()
-    encs = [encode_layer(L, args.keep, args.mant, ws) for L in layers]
-    torch.cuda.synchronize()
-    enc_s = time.time() - t0
-    log(f"encoded {len(encs)} layers in {enc_s:.1f}s")
 
-    # activations (bs=1): x for q|k|v and gate|up (hidden 4096), o input (4096), down input (14336)
+    def encode_layer(L, keep, mant, fmt=cass.CASS_FMT_C1_UNARY):
+        return {n: cass.encode(L[n], synth.keep_count(keep, L[n].shape[1]), mant,
+                               block=args.block, fmt=fmt, ws=ws) for n in L}
+
+    encs = [encode_layer(L, args.keep, args.mant) for L in layers]
+    n_copies = len(encs)
+    torch.cuda.synchronize()
+    log(f"encoded {len(encs)} layers")
+
     xs = {n: dev16(synth.activations(1, layer0[n].shape[1], 2, t0=i)) for i, n in enumerate(MATS)}
     ys = {n: torch.empty((1, layer0[n].shape[0]), dtype=torch.float32, device="cuda") for n in MATS}
     spec_bytes = {n: encs[0][n].spec_bytes for n in MATS}
-    step_bytes_each = [sum(e[n].spec_bytes for n in MATS) for e in encs]
 
     def step(i, events=None):
         e = encs[i % len(encs)]
@@ -124,10 +156,8 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-
-    # timed region 1: whole steps, back to back
+    # timed region: whole steps back to back
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     start.record(stream)
     for i in range(args.steps):
         step(i)
@@ -135,112 +165,45 @@ def main():
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
     ms_per_step = total_ms / args.steps
-    total_bytes = sum(step_bytes_each[i % len(encs)] for i in range(args.steps))
+    total_bytes = sum(sum(encs[i % len(encs)][n].spec_bytes for n in MATS) for i in range(args.steps))
     value = total_bytes / (total_ms * 1e-3) / 1e9
+    if args.mode == "gemv":
+        print(json.dumps({"mode": "gemv", "value": round(value, 2), "unit": "GB/s",
+                          "ms_per_step": round(ms_per_step, 5)}))
+        return
 
-    # timed region 2: HIP events around every GEMV launch (kernel durations)
+    # kernel durations: HIP events around every GEMV launch
     ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in MATS]
           for _ in range(args.steps)]
-    torch.cuda.synchronize()
     for i in range(args.steps):
         step(i, ev[i])
     torch.cuda.synchronize()
     kern_ms = {n: [] for n in MATS}
-    kern_bytes = 0  # speculation bytes
-    alg_bytes = 0   # + x read (2*cols) + y written (4*rows)
+    alg_bytes = 0  # speculation bytes + x read (2*cols) + y written (4*rows)
     for i in range(args.steps):
         for j, n in enumerate(MATS):
             kern_ms[n].append(ev[i][j][0].elapsed_time(ev[i][j][1]))
             e = encs[i % len(encs)][n]
-            kern_bytes += e.spec_bytes
             alg_bytes += e.spec_bytes + 2 * e.cols + 4 * e.rows
     sum_ms = sum(sum(v) for v in kern_ms.values())
-    kernel_gbs = kern_bytes / (sum_ms * 1e-3) / 1e9
-    per_matrix = {n: {"spec_MB": spec_bytes[n] / 1e6,
-                      "avg_us": 1e3 * float(np.mean(kern_ms[n])),
-                      "GB_s": spec_bytes[n] / (float(np.mean(kern_ms[n])) * 1e-3) / 1e9}
+    n_launch = args.steps * len(MATS)
+    avg_launch_ms = sum_ms / n_launch
+    achieved = alg_bytes / n_launch / (avg_launch_ms * 1e-3) / 1e9
+    per_matrix = {n: {"spec_MB": round(spec_bytes[n] / 1e6, 3),
+                      "avg_us": round(1e3 * float(np.mean(kern_ms[n])), 2),
+                      "GB_s": round(spec_bytes[n] / (float(np.mean(kern_ms[n])) * 1e-3) / 1e9, 1)}
                   for n in MATS}
-    avg_launch_ms = sum_ms / (args.steps * len(MATS))
-    avg_launch_bytes = alg_bytes / (args.steps * len(MATS))
-
-    # ---- the other hot-path calls, timed on layer 0
-    rows = {}
-
-    def time_call(fn, reps=10):
-        fn()
-        torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        for _ in range(reps):
-            fn()
-        b.record(stream)
-        torch.cuda.synchronize()
-        return a.elapsed_time(b) / reps
-
-    X5 = {n: dev16(synth.activations(5, layer0[n].shape[1], 2, t0=10 + i)) for i, n in enumerate(MATS)}
-    Y5 = {n: torch.empty((5, layer0[n].shape[0]), dtype=torch.float32, device="cuda") for n in MATS}
-    e0 = encs[0]
-    ver_ms = sum(time_call(lambda n=n: cass.cass_verify_gemm(e0[n].desc, X5[n], Y5[n], stream))
-                 for n in MATS)
-    both_bytes = sum(e0[n].spec_bytes + e0[n].verif_bytes for n in MATS)
-    rows["verify_gemm_n5"] = {"ms_per_layer": ver_ms, "GB_s": both_bytes / (ver_ms * 1e-3) / 1e9,
-                              "spec_plus_verif_MB": both_bytes / 1e6}
-    out = {n: torch.empty_like(layers[0][n]) for n in MATS}
-    rec_ms = sum(time_call(lambda n=n: cass.cass_reconstruct(e0[n].desc, out[n], stream), 3)
-                 for n in MATS)
-    rows["reconstruct"] = {"ms_per_layer": rec_ms,
-                           "GB_s_read": both_bytes / (rec_ms * 1e-3) / 1e9}
-    dd_ms = sum(time_call(lambda n=n: cass.cass_draft_decode(e0[n].desc, out[n], stream), 3)
-                for n in MATS)
-    rows["draft_decode"] = {"ms_per_layer": dd_ms}
-    for n in MATS:  # exactness of the decoded layer on the device
-        cass.cass_reconstruct(e0[n].desc, out[n], stream)
-    torch.cuda.synchronize()
-    exact = all(torch.equal(out[n], layers[0][n]) for n in MATS)
-    t0 = time.time()
-    encode_layer(layers[0], args.keep, args.mant, ws)
-    torch.cuda.synchronize()
-    rows["encode"] = {"ms_per_layer": 1e3 * (time.time() - t0),
-                      "note": "two host synchronisations per tensor (histograms, sizes)"}
     n_values = sum(layers[0][n].numel() for n in MATS)
     bits_per_value = sum(spec_bytes.values()) * 8 / n_values
 
-    sweep = None
-    if args.sweep:
-        sweep = {}
-        for keep in (0.5, 0.3, 0.2):
-            for mant in (2, 3, 4):
-                e = encode_layer(layers[0], keep, mant, ws)
-                b = sum(e[n].spec_bytes for n in MATS)
-                ms = sum(time_call(lambda n=n: cass.cass_draft_gemv(e[n].desc, xs[n], ys[n], stream), 20)
-                         for n in MATS)
-                sweep[f"keep{keep}_m{mant}"] = {"spec_MB": b / 1e6, "GB_s": b / (ms * 1e-3) / 1e9,
-                                               "bits_per_value": b * 8 / n_values}
-                del e
+    extras = {}
+    if not args.no_extras:
+        extras = run_extras(args, torch, cass, synth, timer, stream, layers, encs, layer0,
+                            encode_layer, xs, ys, dev16, gen, n_values)
 
-    # ---- CPU oracle on a row sample of layer 0
     cpu = None
     if not args.no_cpu_baseline:
-        import oracle
-        threads = max(1, min(16, os.cpu_count() or 1))
-        sample = {}
-        for n in MATS:
-            w = layer0[n][::16]
-            sample[n] = oracle.encode(w, synth.keep_count(args.keep, w.shape[1]), args.mant,
-                                      block=args.block)[0]
-        xh = {n: synth.activations(1, layer0[n].shape[1], 2, t0=i) for i, n in enumerate(MATS)}
-        done_bytes, t_start = 0, time.time()
-        while True:
-            for n in MATS:
-                oracle.product(sample[n], xh[n], threads=threads)
-                done_bytes += sample[n].size
-            if time.time() - t_start >= args.cpu_seconds:
-                break
-        dt = time.time() - t_start
-        cpu = {"value": done_bytes / dt / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
-               "sample": "every 16th row of each fused matrix of layer 0, encoded by the oracle; "
-                         "oracle draft product (decode + fp64 multiply-accumulate) repeated for "
-                         f"{dt:.1f}s"}
+        cpu = cpu_baseline(args, synth, layer0)
 
     result = {
         "metric": "draft GEMV GB/s on compressed bytes & % HBM peak, 8B-shape layer bs=1",
@@ -259,7 +222,7 @@ def main():
             "workload": "Llama-3-8B-shaped decoder layer, draft GEMV bs=1 over q|k|v 6144x4096, "
                         "o 4096x4096, gate|up 28672x4096, down 4096x14336",
             "format": "Cassandra-1 unary exponents", "keep": args.keep, "mant_bits": args.mant,
-            "block": args.block, "batch": 1, "layer_copies": len(encs),
+            "block": args.block, "batch": 1, "layer_copies": n_copies,
             "spec_MB_per_layer": round(sum(spec_bytes.values()) / 1e6, 3),
             "spec_bits_per_value": round(bits_per_value, 4),
         },
@@ -267,24 +230,209 @@ def main():
         "tokens_per_s_equiv_layer": round(1e3 / ms_per_step, 1),
         "roofline": {
             "bound": "hbm",
-            "achieved": round(avg_launch_bytes / (avg_launch_ms * 1e-3) / 1e9, 2),
+            "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
-            "frac": round(avg_launch_bytes / (avg_launch_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-            "traffic": None,
-            "kernel": "k_draft_gemv_c1<1>",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic_from_profile(),
+            "kernel": "k_gemv_c1_staged<1>",
             "avg_launch_us": round(avg_launch_ms * 1e3, 3),
-            "algorithmic_bytes_per_launch": round(avg_launch_bytes),
+            "algorithmic_bytes_per_launch": round(alg_bytes / n_launch),
         },
-        "per_matrix": {n: {k: round(v, 3) for k, v in d.items()} for n, d in per_matrix.items()},
-        "kernel_sum_GB_s": round(kernel_gbs, 2),
-        "rows": rows,
-        "reconstruct_exact": exact,
+        "per_matrix": per_matrix,
         "cpu_baseline": cpu,
     }
-    if sweep is not None:
-        result["sweep"] = sweep
+    result.update(extras)
     print(json.dumps(result))
+
+
+def traffic_from_profile():
+    """HBM bytes per GEMV launch from the committed counter summary (FETCH_SIZE +
+    WRITE_SIZE, calibrated on a device copy), when it was taken on the current
+    kernel sources; else null."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "draft_gemv_llama8b_layer_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    try:
+        h = hashlib.sha256()
+        for f in fields["sources"].split():
+            h.update(open(os.path.join(ROOT, f), "rb").read())
+        if h.hexdigest() != fields["sources_sha256"]:
+            return None
+        return int(fields["traffic_bytes_per_launch"])
+    except (KeyError, OSError, ValueError):
+        return None
+
+
+def run_extras(args, torch, cass, synth, timer, stream, layers, encs, layer0, encode_layer,
+               xs, ys, dev16, gen, n_values):
+    out = {}
+    e0 = encs[0]
+    # ---- other calls on the 8B layer
+    X5 = {n: dev16(synth.activations(5, layer0[n].shape[1], 2, t0=10 + i)) for i, n in enumerate(MATS)}
+    Y5 = {n: torch.empty((5, layer0[n].shape[0]), dtype=torch.float32, device="cuda") for n in MATS}
+    both = sum(e0[n].spec_bytes + e0[n].verif_bytes for n in MATS)
+    ver_ms = sum(timer.ms(lambda n=n: cass.cass_verify_gemm(e0[n].desc, X5[n], Y5[n], stream))
+                 for n in MATS)
+    rows = {"verify_gemm_n5": {"ms_per_layer": round(ver_ms, 4),
+                               "GB_s": round(both / (ver_ms * 1e-3) / 1e9, 1),
+                               "spec_plus_verif_MB": round(both / 1e6, 2)}}
+    outb = {n: torch.empty_like(layers[0][n]) for n in MATS}
+    rec_ms = sum(timer.ms(lambda n=n: cass.cass_reconstruct(e0[n].desc, outb[n], stream), 3)
+                 for n in MATS)
+    rows["reconstruct"] = {"ms_per_layer": round(rec_ms, 4),
+                           "GB_s_read": round(both / (rec_ms * 1e-3) / 1e9, 1)}
+    dd_ms = sum(timer.ms(lambda n=n: cass.cass_draft_decode(e0[n].desc, outb[n], stream), 3)
+                for n in MATS)
+    rows["draft_decode"] = {"ms_per_layer": round(dd_ms, 4)}
+    for n in MATS:
+        cass.cass_reconstruct(e0[n].desc, outb[n], stream)
+    torch.cuda.synchronize()
+    rows["reconstruct_exact"] = all(torch.equal(outb[n], layers[0][n]) for n in MATS)
+    del outb
+    t0 = time.time()
+    encode_layer(layers[0], args.keep, args.mant)
+    torch.cuda.synchronize()
+    rows["encode"] = {"ms_per_layer": round(1e3 * (time.time() - t0), 2),
+                      "note": "two host synchronisations per tensor (histograms, sizes)"}
+    out["rows"] = rows
+
+    # ---- keep x mantissa sweep (layer 0)
+    sweep = {}
+    for keep in (0.5, 0.3, 0.2):
+        for mant in (2, 3, 4):
+            e = encode_layer(layers[0], keep, mant)
+            b = sum(e[n].spec_bytes for n in MATS)
+            ms = sum(timer.ms(lambda n=n: cass.cass_draft_gemv(e[n].desc, xs[n], ys[n], stream), 20)
+                     for n in MATS)
+            sweep[f"keep{keep}_m{mant}"] = {"spec_MB": round(b / 1e6, 2),
+                                           "GB_s": round(b / (ms * 1e-3) / 1e9, 1),
+                                           "bits_per_value": round(b * 8 / n_values, 4)}
+            del e
+    out["sweep"] = sweep
+    out["sweep_min_GB_s"] = min(v["GB_s"] for v in sweep.values())
+    del encs[1:]
+    del layers[1:]
+    torch.cuda.empty_cache()
+    log("sweep done")
+
+    # ---- 32-layer stack: one draft step (4 GEMVs per layer) and one N=5 verify pass
+    stack = []
+    for li in range(32):
+        L = torch_layer(torch, synth.LLAMA3_8B, gen)
+        stack.append(encode_layer(L, 0.3, 3))
+        del L
+    torch.cuda.synchronize()
+    sb = sum(e[n].spec_bytes for e in stack for n in MATS)
+    vb = sum(e[n].verif_bytes for e in stack for n in MATS)
+    draft_ms = timer.ms(lambda: [cass.cass_draft_gemv(e[n].desc, xs[n], ys[n], stream)
+                                 for e in stack for n in MATS], 5)
+    verify_ms = timer.ms(lambda: [cass.cass_verify_gemm(e[n].desc, X5[n], Y5[n], stream)
+                                  for e in stack for n in MATS], 2)
+    out["stack32_llama8b"] = {
+        "draft_step_ms": round(draft_ms, 3), "tokens_per_s_equiv": round(1e3 / draft_ms, 1),
+        "draft_GB_s": round(sb / (draft_ms * 1e-3) / 1e9, 1), "spec_GB": round(sb / 1e9, 3),
+        "verify_n5_ms": round(verify_ms, 3), "spec_plus_verif_GB": round((sb + vb) / 1e9, 3),
+        "note": "linear layers only (4 fused GEMVs per layer), keep 0.3, m=3, Cassandra-1"}
+    del stack
+    torch.cuda.empty_cache()
+    log("stack done")
+
+    # ---- Qwen3-4B-shaped 36-layer stack, Cassandra-2 (MX-32), batch 2
+    x2 = {n: None for n in MATS}
+    qstack = []
+    for li in range(36):
+        L = torch_layer(torch, synth.QWEN3_4B, gen, outlier_frac=0.0)
+        qstack.append(encode_layer(L, 0.3, 3, fmt=cass.CASS_FMT_C2_MX32))
+        if li == 0:
+            for i, n in enumerate(MATS):
+                x2[n] = dev16(synth.activations(2, L[n].shape[1], 5, t0=2 * i))
+        del L
+    y2 = {n: torch.empty((2, qstack[0][n].rows), dtype=torch.float32, device="cuda") for n in MATS}
+    qb = sum(e[n].spec_bytes for e in qstack for n in MATS)
+    q_ms = timer.ms(lambda: [cass.cass_draft_gemv(e[n].desc, x2[n], y2[n], stream)
+                             for e in qstack for n in MATS], 5)
+    out["stack36_qwen3_4b_c2_bs2"] = {
+        "draft_step_ms": round(q_ms, 3), "GB_s": round(qb / (q_ms * 1e-3) / 1e9, 1),
+        "spec_GB": round(qb / 1e9, 3), "tokens_per_s_equiv_bs2": round(2e3 / q_ms, 1),
+        "spec_bits_per_value": round(qb * 8 / (36 * sum(int(np.prod(s)) for s in synth.QWEN3_4B.values())), 4)}
+    del qstack
+    torch.cuda.empty_cache()
+    log("qwen done")
+
+    # ---- KV cache at 32K / 64K context (8 KV heads x 128, 32 query heads)
+    kvres = {}
+    for T in (32768, 65536):
+        H, Hq, keep, mant, nq = 8, 32, 38, 3, 5
+        Kt = synth.kv_tensor(T + nq, H, 128, 1_000_000 * 4 + 7)
+        Vt = synth.kv_tensor(T + nq, H, 128, 1_000_000 * 4 + 8)
+        cache = cass.KvCache(H, 128, keep, mant, max_tokens=T + nq + 64)
+        pre = T - 64
+        cache.append(dev16(Kt[:pre]), dev16(Vt[:pre]))
+        torch.cuda.synchronize()
+        tokK = [dev16(Kt[t:t + 1]) for t in range(pre, T)]
+        tokV = [dev16(Vt[t:t + 1]) for t in range(pre, T)]
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for i in range(64):
+            cache.append(tokK[i], tokV[i])
+        b.record(stream)
+        torch.cuda.synchronize()
+        app_us = a.elapsed_time(b) * 1e3 / 64
+        q1 = dev16(synth.activations(Hq, 128, 4, t0=T))
+        wsa = torch.empty(cass.cass_kv_attn_ws_bytes(cache.kv, nq, Hq), dtype=torch.uint8, device="cuda")
+        o1 = torch.empty((Hq, 128), dtype=torch.float32, device="cuda")
+        d_ms = timer.ms(lambda: cass.cass_kv_draft_attn(cache.kv, q1, 1 / np.sqrt(128), o1, wsa, stream), 5)
+        cache.append(dev16(Kt[T:T + nq]), dev16(Vt[T:T + nq]))
+        qv = dev16(np.stack([synth.activations(Hq, 128, 5, t0=T + i) for i in range(nq)]))
+        ov = torch.empty((nq, Hq, 128), dtype=torch.float32, device="cuda")
+        wsv = torch.empty(cass.cass_kv_attn_ws_bytes(cache.kv, nq, Hq), dtype=torch.uint8, device="cuda")
+        v_ms = timer.ms(lambda: cass.cass_kv_verify_attn(cache.kv, qv, 1 / np.sqrt(128), ov, wsv, stream), 3)
+        tokens, flags = cass.cass_kv_status(cache.kv)
+        # bytes the draft attention reads over T tokens: per K|V stream the keep
+        # bitmap, the code offsets, the sign+mantissa fields and the used code bits
+        st = cache.state.cpu().numpy().view(np.int64)
+        code_bytes = sum(int(st[2 + 2 * s]) for s in range(2 * H)) / 8
+        attn_bytes = 2 * H * T * (128 / 8 + 4 + keep * (1 + mant) / 8) + code_bytes * T / tokens
+        kvres[f"T{T}"] = {"append_1tok_us": round(app_us, 2), "draft_attn_us": round(d_ms * 1e3, 1),
+                          "draft_attn_spec_MB": round(attn_bytes / 1e6, 2),
+                          "draft_attn_GB_s": round(attn_bytes / (d_ms * 1e-3) / 1e9, 1),
+                          "verify_attn_n5_us": round(v_ms * 1e3, 1), "tokens": tokens,
+                          "overflow": bool(flags & cass.CASS_KV_FLAG_OVERFLOW)}
+        del cache, Kt, Vt
+        torch.cuda.empty_cache()
+    out["kv_cache"] = kvres
+    log("kv done")
+    return out
+
+
+def cpu_baseline(args, synth, layer0):
+    import oracle
+    threads = max(1, min(16, os.cpu_count() or 1))
+    sample = {}
+    for n in MATS:
+        w = layer0[n][::16]
+        sample[n] = oracle.encode(w, synth.keep_count(args.keep, w.shape[1]), args.mant,
+                                  block=args.block)[0]
+    xh = {n: synth.activations(1, layer0[n].shape[1], 2, t0=i) for i, n in enumerate(MATS)}
+    done, t_start = 0, time.time()
+    while True:
+        for n in MATS:
+            oracle.product(sample[n], xh[n], threads=threads)
+            done += sample[n].size
+        if time.time() - t_start >= args.cpu_seconds:
+            break
+    dt = time.time() - t_start
+    return {"value": round(done / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": "every 16th row of each fused matrix of layer 0, encoded by the oracle; the "
+                      "oracle's draft product (decode + fp64 multiply-accumulate) repeated for "
+                      f"{dt:.1f} s"}
 
 
 if __name__ == "__main__":
