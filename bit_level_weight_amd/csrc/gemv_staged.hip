@@ -17,6 +17,7 @@
 // one LDS table lookup, and multiplies it with x (staged once per workgroup).
 // Block partials of a row are summed in a fixed order (deterministic).
 #include <stdlib.h>
+#include <string.h>
 
 #include <algorithm>
 
@@ -360,6 +361,10 @@ bool draft_gemv_staged_fits(const Shape& sh, int batch, int format, int64_t code
 hipError_t launch_draft_gemv_c1(const SpecViewC1& v, const Shape& sh, const uint16_t* x,
                                 int batch, int64_t ldx, float* y, int64_t ldy, hipStream_t s) {
   if (sh.rows == 0) return hipSuccess;
+  const char* path = getenv("CASS_GEMV_PATH");
+  const bool want_staged = path && strcmp(path, "staged") == 0;
+  if (!force_direct() && !want_staged && draft_gemv_bal_fits(sh, batch, v.codes_limit))
+    return launch_draft_gemv_c1_bal(v, sh, x, batch, ldx, y, ldy, s);
   const StagedGeom g = make_geom(sh, batch, CASS_FMT_C1_UNARY, v.codes_limit);
   if (g.lds_bytes > kMaxLds || force_direct())
     return launch_draft_gemv_c1_direct(v, sh, x, batch, ldx, y, ldy, s);

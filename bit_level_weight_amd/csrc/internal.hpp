@@ -125,6 +125,11 @@ hipError_t launch_draft_gemv_c2_direct(const SpecViewC2& v, const Shape& sh, con
                                        int batch, int64_t ldx, float* y, int64_t ldy,
                                        hipStream_t s);
 int64_t draft_gemv_direct_lds_bytes(const Shape& sh, int batch);
+// Balanced kernel (Cassandra-1): equal kept-value parts per lane.
+bool draft_gemv_bal_fits(const Shape& sh, int batch, int64_t code_limit_words);
+hipError_t launch_draft_gemv_c1_bal(const SpecViewC1& v, const Shape& sh, const uint16_t* x,
+                                    int batch, int64_t ldx, float* y, int64_t ldy,
+                                    hipStream_t s);
 bool draft_gemv_staged_fits(const Shape& sh, int batch, int format, int64_t code_limit_words);
 hipError_t launch_decode_c1(const SpecViewC1& sv, const VerifViewC1* vv, const Shape& sh,
                             uint16_t* out, hipStream_t s);

@@ -60,8 +60,10 @@ __device__ __forceinline__ int select_bit(uint32_t w, int n) {
 
 // Bit position just after the n-th unary code that starts at `pos` (each
 // code ends with its only one bit, so this is a select over one bits).
+// A code is at most 256 bits, so a valid stream ends the loop within
+// 8n + 1 windows; the cap only keeps a corrupt stream from spinning.
 __device__ __forceinline__ uint32_t skip_codes(const uint32_t* w, uint32_t pos, int n) {
-  while (n > 0) {
+  for (int it = 8 * n + 1; n > 0 && it > 0; --it) {
     const uint32_t win = window32(w, pos);
     const int c = __builtin_popcount(win);
     if (c >= n) return pos + (uint32_t)select_bit(win, n) + 1u;

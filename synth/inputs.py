@@ -22,7 +22,7 @@ import numpy as np
 __all__ = [
     "bf16_from_f32", "f32_from_bf16", "seed_for", "act_seed", "keep_count",
     "weight", "activations", "kv_tensor", "all_bf16_patterns",
-    "LLAMA3_8B", "QWEN3_4B", "layer_matrices", "fused_layer",
+    "LLAMA3_8B", "QWEN3_4B", "weight_wide", "layer_matrices", "fused_layer",
 ]
 
 MATRIX_ID = {"q": 0, "k": 1, "v": 2, "o": 3, "gate": 4, "up": 5, "down": 6,
@@ -89,6 +89,15 @@ def activations(n: int, cols: int, config: int, t0: int = 0) -> np.ndarray:
         rng = np.random.default_rng(act_seed(config, t0 + t))
         out[t] = bf16_from_f32(rng.standard_normal(cols, dtype=np.float32))
     return out
+
+
+def weight_wide(rows: int, cols: int, seed: int, binades: int = 48) -> np.ndarray:
+    """bf16 [rows, cols]: N(0,1) times 2^-u with u uniform in [0, binades),
+    so exponents spread over ~binades values (long exponent codes)."""
+    rng = np.random.default_rng(seed)
+    a = rng.standard_normal((rows, cols), dtype=np.float32)
+    a *= np.exp2(-rng.uniform(0.0, binades, size=(rows, cols))).astype(np.float32)
+    return bf16_from_f32(a)
 
 
 def kv_tensor(tokens: int, heads: int, dim: int, seed: int,

@@ -175,6 +175,72 @@ def test_direct_gemv_path(gpu, orc, monkeypatch, fmt):
         check_product(y.cpu().numpy(), y_ref, absy)
 
 
+BAL_CASES = [
+    # rows, cols, keep, mant, block, parts (CASS_GEMV_PARTS; 0 = default), weights
+    (64, 4096, 1229, 3, 256, 0, "normal"),    # q=0.3, 8 values per group
+    (67, 4096, 819, 3, 256, 0, "normal"),     # q=0.2, 4 per group, ragged last round
+    (48, 4096, 1024, 4, 256, 0, "normal"),    # q=0.25, m=4: 6 per group
+    (33, 2048, 1024, 2, 128, 64, "normal"),   # 64 parts of 16, block 128
+    (40, 1024, 307, 3, 32, 1, "normal"),      # one lane per row, block 32
+    (16, 1024, 40, 3, 64, 64, "normal"),      # parts smaller than a group
+    (20, 512, 30, 3, 256, 64, "normal"),      # k < parts: lanes without values
+    (64, 4096, 1229, 3, 256, 16, "wide"),     # codes of 32+ bits: per-value steps
+    (64, 4096, 2048, 5, 256, 8, "onewide"),   # one row's codes exceed the LDS share
+]
+
+
+def bal_weights(R, C, kind, seed):
+    if kind == "normal":
+        return make_w(R, C, seed)
+    if kind == "wide":
+        return synth.weight_wide(R, C, seed)
+    w = make_w(R, C, seed)
+    w[5] = synth.weight_wide(1, C, seed + 1, binades=120)[0]
+    return w
+
+
+@pytest.mark.parametrize("case", BAL_CASES, ids=[str(c) for c in BAL_CASES])
+def test_balanced_gemv_variants(gpu, orc, monkeypatch, case):
+    """The balanced draft GEMV (default Cassandra-1 path) across part counts,
+    keep ratios, blocks, long codes and the global-code fallback."""
+    torch, cass = gpu
+    R, C, k, m, B, parts, kind = case
+    print("case", case, flush=True)
+    w = bal_weights(R, C, kind, 1000 + R + k)
+    spec_o, _ = orc.encode(w, k, m, block=B)
+    enc = cass.encode(dev(torch, w), k, m, block=B)
+    if parts:
+        monkeypatch.setenv("CASS_GEMV_PARTS", str(parts))
+    for batch in (1, 3):
+        x = synth.activations(batch, C, 6, t0=batch)
+        y = torch.full((batch, R), float("nan"), dtype=torch.float32, device="cuda")
+        cass.cass_draft_gemv(enc.desc, dev(torch, x), y)
+        torch.cuda.synchronize()
+        y_ref, absy = orc.product(spec_o, x, threads=4)
+        check_product(y.cpu().numpy(), y_ref, absy)
+
+
+@pytest.mark.parametrize("path", ["staged", "direct"])
+def test_other_gemv_paths(gpu, orc, monkeypatch, path):
+    """The staged and direct kernels, which serve shapes the balanced kernel
+    does not take (selected here by environment)."""
+    torch, cass = gpu
+    R, C, k, m = 45, 4096, 1229, 3
+    w = make_w(R, C, 808)
+    spec_o, _ = orc.encode(w, k, m)
+    enc = cass.encode(dev(torch, w), k, m)
+    if path == "staged":
+        monkeypatch.setenv("CASS_GEMV_PATH", "staged")
+    else:
+        monkeypatch.setenv("CASS_GEMV_DIRECT", "1")
+    x = synth.activations(2, C, 7)
+    y = torch.full((2, R), float("nan"), dtype=torch.float32, device="cuda")
+    cass.cass_draft_gemv(enc.desc, dev(torch, x), y)
+    torch.cuda.synchronize()
+    y_ref, absy = orc.product(spec_o, x)
+    check_product(y.cpu().numpy(), y_ref, absy)
+
+
 def test_strided_operands(gpu, orc):
     """ldx > cols and ldy > rows are honoured (padding untouched)."""
     torch, cass = gpu
