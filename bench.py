@@ -235,7 +235,7 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic_from_profile(),
-            "kernel": "k_gemv_c1_staged<1>",
+            "kernel": "k_gemv_c1_bal<1, 8>",
             "avg_launch_us": round(avg_launch_ms * 1e3, 3),
             "algorithmic_bytes_per_launch": round(alg_bytes / n_launch),
         },

@@ -67,19 +67,43 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// One wave copies words [w0, w1) of src (16-byte aligned section base) to dst
-// with 16-byte loads.  The copy starts at w0 rounded down to 4 words, which is
-// returned, and never reads at or past word `limit` (a multiple of 4).
-__device__ __forceinline__ int64_t wave_stage(uint32_t* dst, const uint32_t* src, int64_t w0,
-                                              int64_t w1, int64_t limit, int lane) {
-  const int64_t a0 = w0 & ~(int64_t)3;
+// A run of 16-byte chunks to copy from global memory to LDS.
+struct Chunks {
+  const u32x4* src;
+  u32x4* dst;
+  int n;
+};
+
+// Chunk range of words [w0, w1) of a section (16-byte aligned base): starts
+// at w0 rounded down to 4 words (returned in a0) and never reaches word
+// `limit` (a multiple of 4).
+__device__ __forceinline__ Chunks chunk_range(const uint32_t* src, uint32_t* dst, int64_t w0,
+                                              int64_t w1, int64_t limit, int64_t& a0) {
+  a0 = w0 & ~(int64_t)3;
   int64_t a1 = (w1 + 3) & ~(int64_t)3;
   if (a1 > limit) a1 = limit;
-  const int64_t n4 = (a1 - a0) >> 2;
-  const u32x4* s4 = reinterpret_cast<const u32x4*>(src + a0);
-  u32x4* d4 = reinterpret_cast<u32x4*>(dst);
-  for (int64_t i = lane; i < n4; i += 64) d4[i] = __builtin_nontemporal_load(s4 + i);
-  return a0;
+  return Chunks{reinterpret_cast<const u32x4*>(src + a0), reinterpret_cast<u32x4*>(dst),
+                (int)((a1 - a0) >> 2)};
+}
+
+constexpr int kBatch = 4;  // 16-byte chunks per thread in flight
+
+// Copies one chunk run with `nthr` threads, kBatch loads in flight per thread
+// (plain loads: used for x, which every workgroup reads).
+__device__ __forceinline__ void copy_run(Chunks a, int t, int nthr) {
+  for (int base = 0; base < a.n; base += nthr * kBatch) {
+    u32x4 r[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int i = base + nthr * j + t;
+      if (i < a.n) r[j] = a.src[i];
+    }
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int i = base + nthr * j + t;
+      if (i < a.n) a.dst[i] = r[j];
+    }
+  }
 }
 
 typedef __attribute__((address_space(3))) const uint16_t lds_u16;
@@ -168,6 +192,37 @@ __device__ __forceinline__ void c1_group(uint32_t lo0, uint32_t hi0, uint32_t wf
   }
 }
 
+// skip_codes with the first 256 bits read at once (nine words, one LDS round
+// trip); longer skips continue word by word.
+__device__ __forceinline__ uint32_t skip_codes8(const uint32_t* w, uint32_t pos, int n) {
+  if (n <= 0) return pos;
+  const uint32_t* q = w + (pos >> 5);
+  const uint32_t sh = pos & 31u;
+  uint32_t qv[9];
+#pragma unroll
+  for (int i = 0; i < 9; ++i) qv[i] = q[i];
+  int rem = n, sel = -1;
+  uint32_t wsel = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t win = __builtin_amdgcn_alignbit(qv[i + 1], qv[i], sh);
+    const int c = __builtin_popcount(win);
+    const bool here = sel < 0 && rem <= c;
+    sel = here ? i : sel;
+    wsel = here ? win : wsel;
+    rem -= (sel < 0) ? c : 0;
+  }
+  if (sel < 0) return skip_codes(w, pos + 256u, rem);
+  return pos + 32u * (uint32_t)sel + (uint32_t)select_bit(wsel, rem) + 1u;
+}
+
+// Where one lane's part stands: bit positions in the staged words.
+struct Part {
+  uint32_t bp, fp, cp, rowbit;
+  int n;
+  int64_t cabs;  // absolute code bit of the part's first value
+};
+
 template <int BATCH, int U>
 __global__ void __launch_bounds__(kBalThreads) k_gemv_c1_bal(SpecViewC1 v, Shape sh, BalGeom g,
                                                              const uint16_t* __restrict__ x,
@@ -179,22 +234,7 @@ __global__ void __launch_bounds__(kBalThreads) k_gemv_c1_bal(SpecViewC1 v, Shape
   const int m = sh.mant, fw = 1 + m;
   const uint32_t fmask = (1u << fw) - 1u;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-
-  // x (bf16 patterns) and the (rank, field) -> fp32 table, once per workgroup
-  for (int bb = 0; bb < BATCH; ++bb) {
-    uint16_t* xr = reinterpret_cast<uint16_t*>(smem + bb * g.xstride);
-    for (int64_t j = threadIdx.x; j < C; j += kBalThreads) xr[j] = x[bb * ldx + j];
-    // zeros after the row: masked slots of a part's last group may read there
-    if (threadIdx.x < 128) xr[C + threadIdx.x] = 0;
-  }
   float* lut = reinterpret_cast<float*>(smem + g.lut_off);
-  for (int i = threadIdx.x; i < (kRanks << fw); i += kBalThreads) {
-    const uint32_t r = (uint32_t)i >> fw, f = (uint32_t)i & fmask;
-    lut[i] = __uint_as_float(((f >> m) << 31) | ((uint32_t)v.perm[r] << 23) |
-                             ((f & ((1u << m) - 1u)) << (23 - m)));
-  }
-  __syncthreads();
-
   uint8_t* reg = smem + g.wave_off + wave * g.wave_bytes;
   uint16_t* kb_l = reinterpret_cast<uint16_t*>(reg + g.kb_off);
   uint32_t* bo_l = reinterpret_cast<uint32_t*>(reg + g.bo_off);
@@ -206,68 +246,219 @@ __global__ void __launch_bounds__(kBalThreads) k_gemv_c1_bal(SpecViewC1 v, Shape
   const int n_min = (int)(k >> g.logP);  // each part has n_min or n_min + 1 values
   const int n_max = (int)((k + g.P - 1) >> g.logP);
   const int G = n_min / U;               // fast groups every part can take
-  const int n_tail = n_max - G * U;      // single steps after them (upper bound)
+  const int n_tail = n_max - G * U;      // values after them (upper bound)
   const int64_t wpr = C / 32;            // bitmap words per row
   const int64_t nwaves = (int64_t)gridDim.x * kBalWaves;
+  const int nlut = kRanks << fw;
 
-  for (int64_t round = (int64_t)blockIdx.x * kBalWaves + wave; round < g.nrounds;
-       round += nwaves) {
-    const int64_t row0 = round * g.rpw;
-    const int rows_here = (int)((R - row0 < g.rpw) ? R - row0 : g.rpw);
-    // ---- stage this round's rows
-    const int64_t bm_a0 = wave_stage(bm_l, v.bitmap, row0 * wpr, (row0 + rows_here) * wpr,
-                                     v.bitmap_limit, lane);
-    const int64_t fb0 = row0 * k * fw, fb1 = (row0 + rows_here) * k * fw;
-    const int64_t f_a0 = wave_stage(f_l, v.fields, fb0 >> 5, (fb1 + 31) >> 5, v.fields_limit,
-                                    lane);
-    const int64_t cb0 = (int64_t)v.rowbase[row0];
-    const int64_t cb1 = (row0 + rows_here < R) ? (int64_t)v.rowbase[row0 + rows_here]
-                                                : v.codes_limit * 32;
-    const int64_t cw0 = (cb0 >> 5) & ~(int64_t)3;
-    int64_t cw1 = (((cb1 + 31) >> 5) + 3) & ~(int64_t)3;
-    if (cw1 > v.codes_limit) cw1 = v.codes_limit;
-    const bool c_in_lds = cw1 - cw0 <= g.c_cap;
-    if (c_in_lds) wave_stage(c_l, v.codes, cb0 >> 5, (cb1 + 31) >> 5, v.codes_limit, lane);
-    for (int i = lane; i < rows_here * nb; i += 64) {
-      kb_l[i] = v.keptb[row0 * nb + i];
-      bo_l[i] = v.blkoff[row0 * nb + i];
+  // ---- one round's copy: its plan (row range, section ranges), the small
+  // per-lane loads issued before the previous round decodes, and the commit
+  // to LDS (every chunk load of the round in flight at once)
+  struct Plan {
+    int64_t row0;
+    int rows_here, nmeta;
+    Chunks bm, f, c;
+    int64_t bm_a0, f_a0, c_a0;
+    bool c_in_lds;
+  };
+  struct Pref {
+    uint32_t kbv[2], bov[2];
+    int64_t rowcb;
+  };
+  auto plan = [&](int64_t round, int64_t cb0, int64_t cb1) {
+    Plan pl;
+    pl.row0 = round * g.rpw;
+    pl.rows_here = (int)((R - pl.row0 < g.rpw) ? R - pl.row0 : g.rpw);
+    pl.nmeta = pl.rows_here * nb;
+    const int64_t fb0 = pl.row0 * k * fw, fb1 = (pl.row0 + pl.rows_here) * k * fw;
+    pl.bm = chunk_range(v.bitmap, bm_l, pl.row0 * wpr, (pl.row0 + pl.rows_here) * wpr,
+                        v.bitmap_limit, pl.bm_a0);
+    pl.f = chunk_range(v.fields, f_l, fb0 >> 5, (fb1 + 31) >> 5, v.fields_limit, pl.f_a0);
+    pl.c = chunk_range(v.codes, c_l, cb0 >> 5, (cb1 + 31) >> 5, v.codes_limit, pl.c_a0);
+    pl.c_in_lds = pl.c.n * 4 <= g.c_cap;
+    if (!pl.c_in_lds) pl.c.n = 0;
+    return pl;
+  };
+  auto code_bounds = [&](int64_t round, int64_t& cb0, int64_t& cb1) {
+    const int64_t r0 = round * g.rpw, r1 = r0 + g.rpw;
+    cb0 = (int64_t)v.rowbase[r0];
+    cb1 = r1 < R ? (int64_t)v.rowbase[r1] : v.codes_limit * 32;
+  };
+  // chunk i of the round's three runs (bitmap, fields, codes)
+  auto chunk_src = [&](const Plan& pl, int i) {
+    const int nab = pl.bm.n + pl.f.n;
+    return i < pl.bm.n ? pl.bm.src + i : (i < nab ? pl.f.src + (i - pl.bm.n) : pl.c.src + (i - nab));
+  };
+  auto chunk_dst = [&](const Plan& pl, int i) {
+    const int nab = pl.bm.n + pl.f.n;
+    return i < pl.bm.n ? pl.bm.dst + i : (i < nab ? pl.f.dst + (i - pl.bm.n) : pl.c.dst + (i - nab));
+  };
+  auto issue = [&](const Plan& pl) {
+    Pref pf;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int i = lane + 64 * j;
+      if (i < pl.nmeta) {
+        pf.kbv[j] = v.keptb[pl.row0 * nb + i];
+        pf.bov[j] = v.blkoff[pl.row0 * nb + i];
+      }
     }
-    wave_sync();
+    pf.rowcb = rl < pl.rows_here ? (int64_t)v.rowbase[pl.row0 + rl] : 0;
+    return pf;
+  };
+  auto commit = [&](const Plan& pl, const Pref& pf) {
+    const int n = pl.bm.n + pl.f.n + pl.c.n;
+    for (int base = 0; base < n; base += 64 * kBatch) {
+      u32x4 r2[kBatch];
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        const int i = base + 64 * j + lane;
+        if (i < n) r2[j] = __builtin_nontemporal_load(chunk_src(pl, i));
+      }
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        const int i = base + 64 * j + lane;
+        if (i < n) *chunk_dst(pl, i) = r2[j];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int i = lane + 64 * j;
+      if (i < pl.nmeta) {
+        kb_l[i] = (uint16_t)pf.kbv[j];
+        bo_l[i] = pf.bov[j];
+      }
+    }
+    for (int i = lane + 128; i < pl.nmeta; i += 64) {  // rounds with more than 128 blocks
+      kb_l[i] = v.keptb[pl.row0 * nb + i];
+      bo_l[i] = v.blkoff[pl.row0 * nb + i];
+    }
+  };
 
-    // ---- where this lane's part starts
-    const int64_t row = row0 + rl;
-    const bool active = rl < rows_here;
+  // Where this lane's part of the round starts.
+  auto locate = [&](const Plan& pl, int64_t rowcb) {
+    Part pt;
+    const int64_t row = pl.row0 + rl;
     const int i0 = (int)(((int64_t)part * k) >> g.logP);
-    const int n = active ? (int)((((int64_t)part + 1) * k) >> g.logP) - i0 : 0;
-    const uint32_t rowbit = (uint32_t)((row0 * wpr - bm_a0) * 32 + (int64_t)rl * C);
-    uint32_t bp = 0, fp = 0, cp = 0;
-    int64_t cabs = 0;  // absolute code bit of the part's first value
-    if (n > 0) {
+    pt.n = rl < pl.rows_here ? (int)((((int64_t)part + 1) * k) >> g.logP) - i0 : 0;
+    pt.rowbit = (uint32_t)((pl.row0 * wpr - pl.bm_a0) * 32 + (int64_t)rl * C);
+    pt.bp = pt.rowbit;
+    pt.fp = 0;
+    pt.cp = 0;
+    pt.cabs = 0;
+    if (pt.n > 0) {
+      // block holding value i0: the kept counts per block are close to
+      // k / nb, so start from that estimate and step (usually zero or one step)
       const uint16_t* kbr = kb_l + rl * nb;
-      int b = 0;
-      for (int s = g.nb_top; s >= 1; s >>= 1)
-        if (b + s < nb && kbr[b + s] <= i0) b += s;
+      int b = (int)(((int64_t)i0 * nb) / k);
+      if (b >= nb) b = nb - 1;
+      for (int it = 0; it < nb; ++it) {
+        const int lo = kbr[b], hi = b + 1 < nb ? kbr[b + 1] : (int)k;
+        if (lo > i0 && b > 0) --b;
+        else if (hi <= i0 && b + 1 < nb) ++b;
+        else break;
+      }
       const int skip = i0 - kbr[b];
-      int rem = skip;
-      const uint32_t* bw = bm_l + (rowbit >> 5) + b * nwb;
-      int wi = 0;
-      uint32_t wd = bw[0];
-      for (;;) {
-        const int c = __builtin_popcount(wd);
-        if (rem < c || wi == nwb - 1) break;  // (the second test: corrupt streams only)
-        rem -= c;
-        wd = bw[++wi];
-      }
-      bp = rowbit + (uint32_t)(b * B + wi * 32 + select_bit(wd, rem + 1));
-      fp = (uint32_t)((row * k + i0) * fw - f_a0 * 32);
-      cabs = (int64_t)v.rowbase[row] + bo_l[rl * nb + b];
-      if (c_in_lds) {
-        cp = skip_codes(c_l, (uint32_t)(cabs - cw0 * 32), skip);
+      // word and bit inside the block: the block's words read at once
+      const uint32_t* bw = bm_l + (pt.rowbit >> 5) + b * nwb;
+      int rem = skip, wsel = nwb - 1;
+      uint32_t wd = 0;
+      if (nwb <= 8) {
+        uint32_t wv[8];
+#pragma unroll
+        for (int w = 0; w < 8; ++w) wv[w] = w < nwb ? bw[w] : 0u;
+        bool found = false;
+#pragma unroll
+        for (int w = 0; w < 8; ++w) {
+          const int c = __builtin_popcount(wv[w]);
+          const bool here = !found && w < nwb && rem < c;
+          wsel = here ? w : wsel;
+          wd = here ? wv[w] : wd;
+          rem -= (!found && !here) ? c : 0;
+          found = found || here;
+        }
       } else {
-        cp = skip_codes(v.codes + (cabs >> 5), (uint32_t)(cabs & 31), skip);
+        int wi = 0;
+        wd = bw[0];
+        for (;;) {
+          const int c = __builtin_popcount(wd);
+          if (rem < c || wi == nwb - 1) break;  // (the second test: corrupt streams only)
+          rem -= c;
+          wd = bw[++wi];
+        }
+        wsel = wi;
       }
+      pt.bp = pt.rowbit + (uint32_t)(b * B + wsel * 32 + select_bit(wd, rem + 1));
+      pt.fp = (uint32_t)((row * k + i0) * fw - pl.f_a0 * 32);
+      pt.cabs = rowcb + bo_l[rl * nb + b];
+      if (pl.c_in_lds)
+        pt.cp = skip_codes8(c_l, (uint32_t)(pt.cabs - pl.c_a0 * 32), skip);
+      else
+        pt.cp = skip_codes(v.codes + (pt.cabs >> 5), (uint32_t)(pt.cabs & 31), skip);
+    }
+    return pt;
+  };
+
+  // ---- first round, x and the (rank, field) -> fp32 table
+  int64_t round = (int64_t)blockIdx.x * kBalWaves + wave;
+  uint32_t prm[8];  // rank table entries for this thread's table slots
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int i = threadIdx.x + kBalThreads * j;
+    if (i < nlut) prm[j] = v.perm[i >> fw];
+  }
+  const bool first = round < g.nrounds;
+  Plan pl{};
+  Pref pf{};
+  if (first) {
+    int64_t cb0, cb1;
+    code_bounds(round, cb0, cb1);
+    pl = plan(round, cb0, cb1);
+    pf = issue(pl);
+  }
+  for (int bb = 0; bb < BATCH; ++bb) {
+    uint16_t* xr = reinterpret_cast<uint16_t*>(smem + bb * g.xstride);
+    const uint16_t* xg = x + bb * ldx;
+    if ((C & 7) == 0 && ((uintptr_t)xg & 15) == 0)
+      copy_run(Chunks{reinterpret_cast<const u32x4*>(xg), reinterpret_cast<u32x4*>(xr),
+                      (int)(C >> 3)},
+               threadIdx.x, kBalThreads);
+    else
+      for (int64_t j = threadIdx.x; j < C; j += kBalThreads) xr[j] = xg[j];
+    // zeros after the row: masked slots of a part's last group may read there
+    if (threadIdx.x < 128) xr[C + threadIdx.x] = 0;
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int i = threadIdx.x + kBalThreads * j;
+    if (i < nlut) {
+      const uint32_t f = (uint32_t)i & fmask;
+      lut[i] = __uint_as_float(((f >> m) << 31) | (prm[j] << 23) |
+                               ((f & ((1u << m) - 1u)) << (23 - m)));
+    }
+  }
+  if (first) commit(pl, pf);
+  __syncthreads();  // x, the table and every wave's first round are in LDS
+  if (!first) return;
+
+  for (;;) {
+    const int64_t rowcb = pf.rowcb;
+    const int64_t next = round + nwaves;
+    const bool more = next < g.nrounds;
+    int64_t ncb0 = 0, ncb1 = 0;
+    if (more) code_bounds(next, ncb0, ncb1);
+    const Part pt = locate(pl, rowcb);
+    // the next round's small loads fly while this round decodes
+    Plan npl{};
+    if (more) {
+      npl = plan(next, ncb0, ncb1);
+      pf = issue(npl);
     }
 
+    const bool active = rl < pl.rows_here;
+    const int n = pt.n;
+    uint32_t bp = pt.bp, fp = pt.fp, cp = pt.cp;
+    const uint32_t rowbit = pt.rowbit;
     float acc[BATCH];
 #pragma unroll
     for (int bb = 0; bb < BATCH; ++bb) acc[bb] = 0.f;
@@ -275,7 +466,7 @@ __global__ void __launch_bounds__(kBalThreads) k_gemv_c1_bal(SpecViewC1 v, Shape
     // rounds where every lane has a part and the codes sit in LDS take the
     // grouped path; others (last partial round, tiny k, codes over the LDS
     // share) decode one value at a time
-    const bool grouped = c_in_lds && rows_here == g.rpw && n_min > 0;
+    const bool grouped = pl.c_in_lds && pl.rows_here == g.rpw && n_min > 0;
     if (grouped) {
       const uint32_t xorg = lds_addr(smem) - 2u * rowbit;  // x address of staged bit 0
       for (int gi = 0; gi <= G; ++gi) {
@@ -300,18 +491,18 @@ __global__ void __launch_bounds__(kBalThreads) k_gemv_c1_bal(SpecViewC1 v, Shape
                                      t, acc);
         } else {
           for (int u = 0; u < t; ++u)
-            c1_step<BATCH>(bm_l, bp, f_l, fp, c_l, cp, rowbit, C, lut, v.perm, m, smem, g.xstride,
-                           acc);
+            c1_step<BATCH>(bm_l, bp, f_l, fp, c_l, cp, rowbit, C, lut, v.perm, m, smem,
+                           g.xstride, acc);
         }
       }
-    } else if (c_in_lds) {
+    } else if (pl.c_in_lds) {
       for (int i = 0; i < n_max; ++i)
         if (i < n)
           c1_step<BATCH>(bm_l, bp, f_l, fp, c_l, cp, rowbit, C, lut, v.perm, m, smem, g.xstride,
                          acc);
     } else {
       // codes straight from global memory (a round whose codes exceed the LDS share)
-      const uint32_t* cg = v.codes + (cabs >> 5);
+      const uint32_t* cg = v.codes + (pt.cabs >> 5);
       uint32_t cpg = cp;
       for (int i = 0; i < n_max; ++i)
         if (i < n)
@@ -329,9 +520,14 @@ __global__ void __launch_bounds__(kBalThreads) k_gemv_c1_bal(SpecViewC1 v, Shape
     }
     if (active && part == 0) {
 #pragma unroll
-      for (int bb = 0; bb < BATCH; ++bb) y[bb * ldy + row] = acc[bb];
+      for (int bb = 0; bb < BATCH; ++bb) y[bb * ldy + pl.row0 + rl] = acc[bb];
     }
     wave_sync();  // every lane is done with the staged words before the next round
+    if (!more) break;
+    commit(npl, pf);
+    wave_sync();
+    pl = npl;
+    round = next;
   }
 }
 
@@ -401,10 +597,14 @@ hipError_t launch_bal(const SpecViewC1& v, const Shape& sh, const BalGeom& g, co
                                        hipFuncAttributeMaxDynamicSharedMemorySize, g.lds_bytes);
     if (e != hipSuccess) return e;
   }
-  const int per_cu = std::max(1, std::min(8, (160 * 1024) / std::max(g.lds_bytes, 1)));
-  int64_t grid = (g.nrounds + kBalWaves - 1) / kBalWaves;
-  const int64_t cap = (int64_t)device_cu_count() * per_cu;
-  if (grid > cap) grid = cap;
+  // every workgroup resident at once (as many per CU as registers and LDS allow)
+  int occ = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, (const void*)kern, kBalThreads,
+                                                   (size_t)g.lds_bytes) != hipSuccess || occ < 1)
+    occ = 1;
+  int64_t grid = (int64_t)device_cu_count() * occ;
+  const int64_t need = (g.nrounds + kBalWaves - 1) / kBalWaves;
+  if (grid > need) grid = need;
   if (grid < 1) grid = 1;
   kern<<<(unsigned)grid, kBalThreads, (size_t)g.lds_bytes, s>>>(v, sh, g, x, ldx, y, ldy);
   return hipGetLastError();
