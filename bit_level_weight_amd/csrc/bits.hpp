@@ -7,28 +7,35 @@
 
 namespace cass {
 
-// Sequential reader of a bit section.  Keeps between 32 and 63 valid bits in
-// a 64-bit buffer so that any take() of up to 32 bits is a shift and a mask.
-// It may fetch up to two words past the last bit it returns; every section is
-// followed by >= 16 bytes of padding, so those reads stay inside the stream.
+// Sequential reader of a bit section.  Keeps between 33 and 64 valid bits in
+// a 64-bit buffer (any take() of up to 32 bits is a shift and a mask) plus the
+// next 32-bit word already requested: a refill uses that word and issues the
+// load of the one after, so the memory latency overlaps the decoding of the
+// 32 bits in between.  It may fetch up to three words past the last bit it
+// returns; every section is followed by >= 16 bytes of padding, so those
+// reads stay inside the stream.
 struct BitReader {
-  const uint32_t* p;  // next word to fetch
+  const uint32_t* p;  // next word to request
   uint64_t buf;
   int n;              // valid bits in buf
+  uint32_t nxt;       // word p[-1], requested ahead
 
   __device__ __forceinline__ void init(const uint32_t* base, uint64_t pos) {
     p = base + (pos >> 5);
     const int s = (int)(pos & 31);
-    buf = (uint64_t)(__builtin_nontemporal_load(p) >> s);
-    ++p;
-    n = 32 - s;
-    refill();
+    const uint32_t w0 = __builtin_nontemporal_load(p);
+    const uint32_t w1 = __builtin_nontemporal_load(p + 1);
+    nxt = __builtin_nontemporal_load(p + 2);
+    p += 3;
+    buf = (uint64_t)(w0 >> s) | ((uint64_t)w1 << (32 - s));
+    n = 64 - s;
   }
   __device__ __forceinline__ void refill() {
     if (n <= 32) {
-      buf |= (uint64_t)__builtin_nontemporal_load(p) << n;
-      ++p;
+      buf |= (uint64_t)nxt << n;
       n += 32;
+      nxt = __builtin_nontemporal_load(p);
+      ++p;
     }
   }
   // width in 0..32

@@ -11,6 +11,17 @@ namespace cass {
 
 namespace {
 
+// The rank tables (rank -> exponent) of both streams, copied to shared memory
+// once per workgroup.
+__device__ __forceinline__ void load_tables(uint8_t* ps, uint8_t* pv, const uint8_t* gs,
+                                            const uint8_t* gv) {
+  for (int i = threadIdx.x; i < 256; i += blockDim.x) {
+    ps[i] = gs ? gs[i] : 0;
+    pv[i] = gv ? gv[i] : 0;
+  }
+  __syncthreads();
+}
+
 // Decode one block into out[pos0 .. pos0+B): 32 positions per bitmap word,
 // written as four 16-byte stores.
 template <typename Dec>
@@ -35,33 +46,39 @@ __device__ __forceinline__ void decode_block_to(Dec& d, const uint32_t* __restri
 
 __global__ void __launch_bounds__(256) k_exact_c1(SpecViewC1 sv, VerifViewC1 vv, Shape sh,
                                                   uint16_t* __restrict__ out) {
+  __shared__ uint8_t ps[256], pv[256];
+  load_tables(ps, pv, sv.perm, vv.perm);
   const int64_t nb = sh.cols / sh.block, nblk = sh.rows * nb;
   for (int64_t bi = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; bi < nblk;
        bi += (int64_t)gridDim.x * blockDim.x) {
     ExactC1 d;
-    d.init(sv, vv, sh, bi / nb, bi % nb);
+    d.init(sv, vv, sh, bi / nb, bi % nb, ps, pv);
     decode_block_to(d, sv.bitmap, bi * sh.block, sh.block, out);
   }
 }
 
 __global__ void __launch_bounds__(256) k_draft_c1(SpecViewC1 sv, Shape sh,
                                                   uint16_t* __restrict__ out) {
+  __shared__ uint8_t ps[256], pv[256];
+  load_tables(ps, pv, sv.perm, nullptr);
   const int64_t nb = sh.cols / sh.block, nblk = sh.rows * nb;
   for (int64_t bi = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; bi < nblk;
        bi += (int64_t)gridDim.x * blockDim.x) {
     DraftC1 d;
-    d.init(sv, sh, bi / nb, bi % nb);
+    d.init(sv, sh, bi / nb, bi % nb, ps);
     decode_block_to(d, sv.bitmap, bi * sh.block, sh.block, out);
   }
 }
 
 __global__ void __launch_bounds__(256) k_exact_c2(SpecViewC2 sv, VerifViewC2 vv, Shape sh,
                                                   uint16_t* __restrict__ out) {
+  __shared__ uint8_t ps[256], pv[256];
+  load_tables(ps, pv, nullptr, vv.perm);
   const int64_t nb = sh.cols / sh.block, nblk = sh.rows * nb;
   for (int64_t bi = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; bi < nblk;
        bi += (int64_t)gridDim.x * blockDim.x) {
     ExactC2 d;
-    d.init(sv, vv, sh, bi / nb, bi % nb);
+    d.init(sv, vv, sh, bi / nb, bi % nb, ps, pv);
     decode_block_to(d, sv.bitmap, bi * sh.block, sh.block, out);
   }
 }

@@ -1,6 +1,9 @@
 // Per-lane block decoders shared by the reconstruction, draft-decode and
 // verification kernels.  A decoder walks one block of `block` positions of
-// one row, 32 positions (one bitmap word) at a time.
+// one row, 32 positions (one bitmap word) at a time.  Every stream, the
+// pruned bytes included, is read through a buffered BitReader; the rank
+// tables (rank -> exponent) are passed in from shared memory, so a value
+// costs no scattered global loads.
 //
 // Method: Cassandra review (marsggbo.github.io), section 3.1 -- the draft
 // zero-fills the speculation data back to bf16; the target reassembles both
@@ -16,15 +19,14 @@ namespace cass {
 
 // Cassandra-1, both streams -> exact original bf16 patterns.
 struct ExactC1 {
-  BitReader fr, er, lr, vr;
-  const uint8_t* perm_s;
-  const uint8_t* perm_v;
-  const uint8_t* pruned;
-  int64_t pidx;
+  BitReader fr, er, lr, vr, pr;
+  const uint8_t* perm_s;  // shared memory
+  const uint8_t* perm_v;  // shared memory
   int m;
 
   __device__ __forceinline__ void init(const SpecViewC1& sv, const VerifViewC1& vv,
-                                       const Shape& sh, int64_t row, int64_t b) {
+                                       const Shape& sh, int64_t row, int64_t b,
+                                       const uint8_t* ps, const uint8_t* pv) {
     const int64_t nb = sh.cols / sh.block;
     const int64_t bi = row * nb + b;
     m = sh.mant;
@@ -34,10 +36,10 @@ struct ExactC1 {
     er.init(sv.codes, sv.rowbase[row] + sv.blkoff[bi]);
     lr.init(vv.lowmant, kin0 * (uint64_t)(7 - m));
     vr.init(vv.codes, vv.rowbase[row] + vv.blkoff[bi]);
-    perm_s = sv.perm;
-    perm_v = vv.perm;
-    pruned = vv.pruned;
-    pidx = row * (sh.cols - sh.keep) + b * sh.block - kb;
+    const uint64_t pidx = (uint64_t)row * (sh.cols - sh.keep) + (uint64_t)(b * sh.block) - kb;
+    pr.init(reinterpret_cast<const uint32_t*>(vv.pruned), pidx * 8u);
+    perm_s = ps;
+    perm_v = pv;
   }
   // one position; kept = its bitmap bit
   __device__ __forceinline__ uint32_t next(uint32_t kept, int /*word*/) {
@@ -48,7 +50,7 @@ struct ExactC1 {
       const uint32_t e = perm_s[r];
       return ((f >> m) << 15) | (e << 7) | ((f & ((1u << m) - 1)) << (7 - m)) | low;
     }
-    const uint32_t byte = pruned[pidx++];
+    const uint32_t byte = pr.take(8);
     const uint32_t e = perm_v[vr.unary()];
     return ((byte >> 7) << 15) | (e << 7) | (byte & 0x7F);
   }
@@ -60,14 +62,14 @@ struct DraftC1 {
   const uint8_t* perm_s;
   int m;
   __device__ __forceinline__ void init(const SpecViewC1& sv, const Shape& sh, int64_t row,
-                                       int64_t b) {
+                                       int64_t b, const uint8_t* ps) {
     const int64_t nb = sh.cols / sh.block;
     const int64_t bi = row * nb + b;
     m = sh.mant;
     const uint32_t kb = sv.keptb[bi];
     fr.init(sv.fields, ((uint64_t)row * sh.keep + kb) * (uint64_t)(1 + m));
     er.init(sv.codes, sv.rowbase[row] + sv.blkoff[bi]);
-    perm_s = sv.perm;
+    perm_s = ps;
   }
   __device__ __forceinline__ uint32_t next(uint32_t kept, int /*word*/) {
     if (!kept) return 0u;
@@ -91,7 +93,7 @@ struct DraftC2 {
   BitReader fr;
   const uint8_t* shexp;
   int64_t g0;
-  int m;
+  int m, cur_word, E;
   __device__ __forceinline__ void init(const SpecViewC2& sv, const Shape& sh, int64_t row,
                                        int64_t b) {
     const int64_t nb = sh.cols / sh.block;
@@ -101,24 +103,30 @@ struct DraftC2 {
     fr.init(sv.fields, ((uint64_t)row * sh.keep + kb) * (uint64_t)(2 + m));
     shexp = sv.shexp;
     g0 = bi * sh.block / 32;
+    cur_word = -1;
+    E = 0;
   }
   __device__ __forceinline__ uint32_t next(uint32_t kept, int word) {
     if (!kept) return 0u;
+    if (word != cur_word) {  // one shared exponent per 32 positions
+      E = shexp[g0 + word];
+      cur_word = word;
+    }
     const uint32_t f = fr.take(2 + m);
-    return mx_value_bits(f >> (m + 1), f & ((2u << m) - 1), shexp[g0 + word], m);
+    return mx_value_bits(f >> (m + 1), f & ((2u << m) - 1), E, m);
   }
 };
 
 // Cassandra-2, both streams -> exact original bf16 patterns.
 struct ExactC2 {
-  BitReader fr, kr, vr;
+  BitReader fr, kr, vr, pr;
   const uint8_t* shexp;
-  const uint8_t* perm_v;
-  const uint8_t* pruned;
-  int64_t g0, pidx;
-  int m;
+  const uint8_t* perm_v;  // shared memory
+  int64_t g0;
+  int m, cur_word, E;
   __device__ __forceinline__ void init(const SpecViewC2& sv, const VerifViewC2& vv,
-                                       const Shape& sh, int64_t row, int64_t b) {
+                                       const Shape& sh, int64_t row, int64_t b,
+                                       const uint8_t* /*ps*/, const uint8_t* pv) {
     const int64_t nb = sh.cols / sh.block;
     const int64_t bi = row * nb + b;
     m = sh.mant;
@@ -126,25 +134,30 @@ struct ExactC2 {
     fr.init(sv.fields, ((uint64_t)row * sh.keep + kb) * (uint64_t)(2 + m));
     kr.init(vv.resid, vv.rowbase_k[row] + vv.blkoff_k[bi]);
     vr.init(vv.codes, vv.rowbase_p[row] + vv.blkoff_p[bi]);
+    const uint64_t pidx = (uint64_t)row * (sh.cols - sh.keep) + (uint64_t)(b * sh.block) - kb;
+    pr.init(reinterpret_cast<const uint32_t*>(vv.pruned), pidx * 8u);
     shexp = sv.shexp;
-    perm_v = vv.perm;
-    pruned = vv.pruned;
+    perm_v = pv;
     g0 = bi * sh.block / 32;
-    pidx = row * (sh.cols - sh.keep) + b * sh.block - kb;
+    cur_word = -1;
+    E = 0;
   }
   __device__ __forceinline__ uint32_t next(uint32_t kept, int word) {
     if (kept) {
+      if (word != cur_word) {  // one shared exponent per 32 positions
+        E = shexp[g0 + word];
+        cur_word = word;
+      }
       const uint32_t f = fr.take(2 + m);
       const uint32_t s = f >> (m + 1), a = f & ((2u << m) - 1);
       const int d = kr.unary();
       const int wd = (7 - m + d < 8) ? 7 - m + d : 8;
       const uint32_t L = kr.take(wd);
       const uint32_t M = (wd < 8) ? ((a << wd) | L) : L;
-      const int E = shexp[g0 + word];
       const uint32_t e = (M >= 128u) ? (uint32_t)(E - d) : 0u;
       return (s << 15) | ((e & 0xFF) << 7) | (M & 0x7F);
     }
-    const uint32_t byte = pruned[pidx++];
+    const uint32_t byte = pr.take(8);
     const uint32_t e = perm_v[vr.unary()];
     return ((byte >> 7) << 15) | (e << 7) | (byte & 0x7F);
   }

@@ -19,6 +19,9 @@ namespace {
 typedef short v4s __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
+__device__ __forceinline__ const uint8_t* spec_perm_of(const SpecViewC1& s) { return s.perm; }
+__device__ __forceinline__ const uint8_t* spec_perm_of(const SpecViewC2&) { return nullptr; }
+
 constexpr int kTileStride = 17;  // u32 per LDS tile row (16 used + 1 pad against bank conflicts)
 
 __global__ void __launch_bounds__(256) k_zero_rows(float* Y, int ntok, int64_t rows, int64_t ldy) {
@@ -34,7 +37,14 @@ __global__ void __launch_bounds__(64) k_verify(SV sv, VV vv, Shape sh,
                                                int64_t ldx, float* __restrict__ Y, int64_t ldy,
                                                int64_t blocks_per_split) {
   __shared__ uint32_t tile[64 * kTileStride];
+  __shared__ uint8_t ps[256], pv[256];
   const int lane = threadIdx.x;
+  const uint8_t* gps = spec_perm_of(sv);
+  for (int i = lane; i < 256; i += 64) {  // rank tables to shared memory
+    ps[i] = gps ? gps[i] : 0;
+    pv[i] = vv.perm[i];
+  }
+  __syncthreads();
   const int64_t nb = sh.cols / sh.block;
   const int64_t row0 = (int64_t)blockIdx.x * 64;
   const int64_t row = row0 + lane;
@@ -49,7 +59,7 @@ __global__ void __launch_bounds__(64) k_verify(SV sv, VV vv, Shape sh,
 
   for (int64_t b = b0; b < b1; ++b) {
     Dec d;
-    if (row_ok) d.init(sv, vv, sh, row, b);
+    if (row_ok) d.init(sv, vv, sh, row, b, ps, pv);
     for (int64_t wi = 0; wi < sh.block / 32; ++wi) {
       if (row_ok) {
         const uint32_t bw = sv.bitmap[(row * nb + b) * (sh.block / 32) + wi];
@@ -110,7 +120,7 @@ hipError_t launch_verify(const SV& sv, const VV& vv, const Shape& sh, const uint
   }
   const int64_t nb = sh.cols / sh.block;
   const int64_t gx = (sh.rows + 63) / 64;
-  const int64_t want_waves = (int64_t)device_cu_count() * 8;
+  const int64_t want_waves = (int64_t)device_cu_count() * 32;
   int64_t nsplit = (want_waves + gx - 1) / gx;
   if (nsplit > nb) nsplit = nb;
   if (nsplit < 1) nsplit = 1;
