@@ -22,75 +22,77 @@ __device__ __forceinline__ void load_tables(uint8_t* ps, uint8_t* pv, const uint
   __syncthreads();
 }
 
-// Decode one block into out[pos0 .. pos0+B): 32 positions per bitmap word,
-// written as four 16-byte stores.
+// Decode one block into out[pos0 .. pos0+B), one bitmap word (32 positions)
+// at a time: the word's kept positions, then its pruned positions, into this
+// thread's 64-byte slot of shared memory, then four 16-byte stores.
 template <typename Dec>
 __device__ __forceinline__ void decode_block_to(Dec& d, const uint32_t* __restrict__ bitmap,
-                                                int64_t pos0, int64_t B, uint16_t* __restrict__ out) {
+                                                int64_t pos0, int64_t B, uint16_t* slot,
+                                                uint16_t* __restrict__ out) {
   for (int64_t wi = 0; wi < B / 32; ++wi) {
     const uint32_t bw = bitmap[pos0 / 32 + wi];
-    uint32_t v[16];
-#pragma unroll
-    for (int j = 0; j < 32; j += 2) {
-      const uint32_t lo = d.next((bw >> j) & 1u, (int)wi);
-      const uint32_t hi = d.next((bw >> (j + 1)) & 1u, (int)wi);
-      v[j / 2] = lo | (hi << 16);
-    }
+    for (uint32_t km = bw; km; km &= km - 1u) slot[__builtin_ctz(km)] = (uint16_t)d.kept((int)wi);
+    for (uint32_t pm = ~bw; pm; pm &= pm - 1u) slot[__builtin_ctz(pm)] = (uint16_t)d.pruned();
+    const uint4* sl = reinterpret_cast<const uint4*>(slot);
     uint4* o = reinterpret_cast<uint4*>(out + pos0 + wi * 32);
-    o[0] = make_uint4(v[0], v[1], v[2], v[3]);
-    o[1] = make_uint4(v[4], v[5], v[6], v[7]);
-    o[2] = make_uint4(v[8], v[9], v[10], v[11]);
-    o[3] = make_uint4(v[12], v[13], v[14], v[15]);
+    o[0] = sl[0];
+    o[1] = sl[1];
+    o[2] = sl[2];
+    o[3] = sl[3];
   }
 }
 
 __global__ void __launch_bounds__(256) k_exact_c1(SpecViewC1 sv, VerifViewC1 vv, Shape sh,
                                                   uint16_t* __restrict__ out) {
   __shared__ uint8_t ps[256], pv[256];
+  __shared__ __align__(16) uint16_t slots[256 * 32];
   load_tables(ps, pv, sv.perm, vv.perm);
   const int64_t nb = sh.cols / sh.block, nblk = sh.rows * nb;
   for (int64_t bi = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; bi < nblk;
        bi += (int64_t)gridDim.x * blockDim.x) {
     ExactC1 d;
     d.init(sv, vv, sh, bi / nb, bi % nb, ps, pv);
-    decode_block_to(d, sv.bitmap, bi * sh.block, sh.block, out);
+    decode_block_to(d, sv.bitmap, bi * sh.block, sh.block, slots + threadIdx.x * 32, out);
   }
 }
 
 __global__ void __launch_bounds__(256) k_draft_c1(SpecViewC1 sv, Shape sh,
                                                   uint16_t* __restrict__ out) {
   __shared__ uint8_t ps[256], pv[256];
+  __shared__ __align__(16) uint16_t slots[256 * 32];
   load_tables(ps, pv, sv.perm, nullptr);
   const int64_t nb = sh.cols / sh.block, nblk = sh.rows * nb;
   for (int64_t bi = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; bi < nblk;
        bi += (int64_t)gridDim.x * blockDim.x) {
     DraftC1 d;
     d.init(sv, sh, bi / nb, bi % nb, ps);
-    decode_block_to(d, sv.bitmap, bi * sh.block, sh.block, out);
+    decode_block_to(d, sv.bitmap, bi * sh.block, sh.block, slots + threadIdx.x * 32, out);
   }
 }
 
 __global__ void __launch_bounds__(256) k_exact_c2(SpecViewC2 sv, VerifViewC2 vv, Shape sh,
                                                   uint16_t* __restrict__ out) {
   __shared__ uint8_t ps[256], pv[256];
+  __shared__ __align__(16) uint16_t slots[256 * 32];
   load_tables(ps, pv, nullptr, vv.perm);
   const int64_t nb = sh.cols / sh.block, nblk = sh.rows * nb;
   for (int64_t bi = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; bi < nblk;
        bi += (int64_t)gridDim.x * blockDim.x) {
     ExactC2 d;
     d.init(sv, vv, sh, bi / nb, bi % nb, ps, pv);
-    decode_block_to(d, sv.bitmap, bi * sh.block, sh.block, out);
+    decode_block_to(d, sv.bitmap, bi * sh.block, sh.block, slots + threadIdx.x * 32, out);
   }
 }
 
 __global__ void __launch_bounds__(256) k_draft_c2(SpecViewC2 sv, Shape sh,
                                                   uint16_t* __restrict__ out) {
+  __shared__ __align__(16) uint16_t slots[256 * 32];
   const int64_t nb = sh.cols / sh.block, nblk = sh.rows * nb;
   for (int64_t bi = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; bi < nblk;
        bi += (int64_t)gridDim.x * blockDim.x) {
     DraftC2 d;
     d.init(sv, sh, bi / nb, bi % nb);
-    decode_block_to(d, sv.bitmap, bi * sh.block, sh.block, out);
+    decode_block_to(d, sv.bitmap, bi * sh.block, sh.block, slots + threadIdx.x * 32, out);
   }
 }
 

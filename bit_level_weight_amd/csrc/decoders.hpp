@@ -1,6 +1,8 @@
 // Per-lane block decoders shared by the reconstruction, draft-decode and
 // verification kernels.  A decoder walks one block of `block` positions of
-// one row, 32 positions (one bitmap word) at a time.  Every stream, the
+// one row: kept() gives the block's kept values in position order, pruned()
+// its pruned values, so a caller takes each bitmap word's kept positions and
+// then its pruned positions in two loops (no per-position branch).  Every stream, the
 // pruned bytes included, is read through a buffered BitReader; the rank
 // tables (rank -> exponent) are passed in from shared memory, so a value
 // costs no scattered global loads.
@@ -41,19 +43,21 @@ struct ExactC1 {
     perm_s = ps;
     perm_v = pv;
   }
-  // one position; kept = its bitmap bit
-  __device__ __forceinline__ uint32_t next(uint32_t kept, int /*word*/) {
-    if (kept) {
-      const uint32_t f = fr.take(1 + m);
-      const int r = er.unary();
-      const uint32_t low = lr.take(7 - m);
-      const uint32_t e = perm_s[r];
-      return ((f >> m) << 15) | (e << 7) | ((f & ((1u << m) - 1)) << (7 - m)) | low;
-    }
+  // the next kept value of the block (kept values come in position order)
+  __device__ __forceinline__ uint32_t kept(int /*word*/) {
+    const uint32_t f = fr.take(1 + m);
+    const int r = er.unary();
+    const uint32_t low = lr.take(7 - m);
+    const uint32_t e = perm_s[r];
+    return ((f >> m) << 15) | (e << 7) | ((f & ((1u << m) - 1)) << (7 - m)) | low;
+  }
+  // the next pruned value of the block
+  __device__ __forceinline__ uint32_t pruned() {
     const uint32_t byte = pr.take(8);
     const uint32_t e = perm_v[vr.unary()];
     return ((byte >> 7) << 15) | (e << 7) | (byte & 0x7F);
   }
+  static constexpr bool kHasPruned = true;
 };
 
 // Cassandra-1 speculation stream -> zero-filled draft.
@@ -71,12 +75,13 @@ struct DraftC1 {
     er.init(sv.codes, sv.rowbase[row] + sv.blkoff[bi]);
     perm_s = ps;
   }
-  __device__ __forceinline__ uint32_t next(uint32_t kept, int /*word*/) {
-    if (!kept) return 0u;
+  __device__ __forceinline__ uint32_t kept(int /*word*/) {
     const uint32_t f = fr.take(1 + m);
     const uint32_t e = perm_s[er.unary()];
     return ((f >> m) << 15) | (e << 7) | ((f & ((1u << m) - 1)) << (7 - m));
   }
+  __device__ __forceinline__ uint32_t pruned() { return 0u; }  // zero-filled
+  static constexpr bool kHasPruned = false;
 };
 
 // bf16 pattern of sign * a * 2^(E-127-m): normalise the (m+1)-bit significand.
@@ -106,8 +111,7 @@ struct DraftC2 {
     cur_word = -1;
     E = 0;
   }
-  __device__ __forceinline__ uint32_t next(uint32_t kept, int word) {
-    if (!kept) return 0u;
+  __device__ __forceinline__ uint32_t kept(int word) {
     if (word != cur_word) {  // one shared exponent per 32 positions
       E = shexp[g0 + word];
       cur_word = word;
@@ -115,6 +119,8 @@ struct DraftC2 {
     const uint32_t f = fr.take(2 + m);
     return mx_value_bits(f >> (m + 1), f & ((2u << m) - 1), E, m);
   }
+  __device__ __forceinline__ uint32_t pruned() { return 0u; }  // zero-filled
+  static constexpr bool kHasPruned = false;
 };
 
 // Cassandra-2, both streams -> exact original bf16 patterns.
@@ -142,25 +148,26 @@ struct ExactC2 {
     cur_word = -1;
     E = 0;
   }
-  __device__ __forceinline__ uint32_t next(uint32_t kept, int word) {
-    if (kept) {
-      if (word != cur_word) {  // one shared exponent per 32 positions
-        E = shexp[g0 + word];
-        cur_word = word;
-      }
-      const uint32_t f = fr.take(2 + m);
-      const uint32_t s = f >> (m + 1), a = f & ((2u << m) - 1);
-      const int d = kr.unary();
-      const int wd = (7 - m + d < 8) ? 7 - m + d : 8;
-      const uint32_t L = kr.take(wd);
-      const uint32_t M = (wd < 8) ? ((a << wd) | L) : L;
-      const uint32_t e = (M >= 128u) ? (uint32_t)(E - d) : 0u;
-      return (s << 15) | ((e & 0xFF) << 7) | (M & 0x7F);
+  __device__ __forceinline__ uint32_t kept(int word) {
+    if (word != cur_word) {  // one shared exponent per 32 positions
+      E = shexp[g0 + word];
+      cur_word = word;
     }
+    const uint32_t f = fr.take(2 + m);
+    const uint32_t s = f >> (m + 1), a = f & ((2u << m) - 1);
+    const int d = kr.unary();
+    const int wd = (7 - m + d < 8) ? 7 - m + d : 8;
+    const uint32_t L = kr.take(wd);
+    const uint32_t M = (wd < 8) ? ((a << wd) | L) : L;
+    const uint32_t e = (M >= 128u) ? (uint32_t)(E - d) : 0u;
+    return (s << 15) | ((e & 0xFF) << 7) | (M & 0x7F);
+  }
+  __device__ __forceinline__ uint32_t pruned() {
     const uint32_t byte = pr.take(8);
     const uint32_t e = perm_v[vr.unary()];
     return ((byte >> 7) << 15) | (e << 7) | (byte & 0x7F);
   }
+  static constexpr bool kHasPruned = true;
 };
 
 }  // namespace cass

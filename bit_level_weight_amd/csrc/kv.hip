@@ -289,12 +289,14 @@ __global__ void __launch_bounds__(64 * kWaves) k_kv_pack(KvDev kv, const uint16_
 }
 
 // ---- per-lane decoder of one cached vector (token tok of stream s) ----
+// kept() gives the vector's kept values in position order, pruned() its
+// pruned values (exact decoding only); callers walk the keep-bitmap words
+// with two loops, kept positions then pruned positions.
 template <bool EXACT>
 struct KvVec {
-  BitReader fr, cr, lr, vcr;
+  BitReader fr, cr, lr, vcr, pr;
   const uint8_t* perm_s;
   const uint8_t* perm_v;
-  const uint8_t* pruned;
   const uint32_t* bm;
   int m;
   __device__ __forceinline__ void init(const KvDev& kv, int s, int64_t tok) {
@@ -311,24 +313,33 @@ struct KvVec {
     if (EXACT) {
       perm_v = vr + kv.vo[0];
       lr.init(reinterpret_cast<const uint32_t*>(vr + kv.vo[1]), (uint64_t)tok * kv.k * (7 - m));
-      pruned = vr + kv.vo[2] + tok * (kv.D - kv.k);
+      pr.init(reinterpret_cast<const uint32_t*>(vr + kv.vo[2]), (uint64_t)tok * (kv.D - kv.k) * 8u);
       off = reinterpret_cast<const uint32_t*>(vr + kv.vo[3])[tok];
       vcr.init(reinterpret_cast<const uint32_t*>(vr + kv.vo[4]), off == 0xFFFFFFFFu ? 0u : off);
     }
   }
-  // bf16 bits of position j (positions are visited in order)
-  __device__ __forceinline__ uint32_t next(uint32_t kept) {
-    if (kept) {
-      const uint32_t f = fr.take(1 + m);
-      const uint32_t e = perm_s[cr.unary()];
-      uint32_t bits = ((f >> m) << 15) | (e << 7) | ((f & ((1u << m) - 1u)) << (7 - m));
-      if (EXACT) bits |= lr.take(7 - m);
-      return bits;
-    }
-    if (!EXACT) return 0u;
-    const uint32_t byte = *pruned++;
+  __device__ __forceinline__ uint32_t kept() {
+    const uint32_t f = fr.take(1 + m);
+    const uint32_t e = perm_s[cr.unary()];
+    uint32_t bits = ((f >> m) << 15) | (e << 7) | ((f & ((1u << m) - 1u)) << (7 - m));
+    if (EXACT) bits |= lr.take(7 - m);
+    return bits;
+  }
+  __device__ __forceinline__ uint32_t pruned() {
+    const uint32_t byte = pr.take(8);
     const uint32_t e = perm_v[vcr.unary()];
     return ((byte >> 7) << 15) | (e << 7) | (byte & 0x7F);
+  }
+  // all D positions into o[0..D)
+  __device__ __forceinline__ void all(int D, uint16_t* o) {
+    for (int w = 0; w < D / 32; ++w) {
+      const uint32_t word = bm[w];
+      if (!EXACT)
+        for (int b = 0; b < 32; ++b) o[w * 32 + b] = 0;
+      for (uint32_t km = word; km; km &= km - 1u) o[w * 32 + __builtin_ctz(km)] = (uint16_t)kept();
+      if (EXACT)
+        for (uint32_t pm = ~word; pm; pm &= pm - 1u) o[w * 32 + __builtin_ctz(pm)] = (uint16_t)pruned();
+    }
   }
 };
 
@@ -343,11 +354,7 @@ __global__ void __launch_bounds__(256) k_kv_decode(KvDev kv, int64_t T, uint16_t
     const int kind = s / kv.H, h = s % kv.H;
     KvVec<EXACT> dec;
     dec.init(kv, 2 * h + kind, tok);
-    uint16_t* o = out + idx * kv.D;
-    for (int w = 0; w < kv.D / 32; ++w) {
-      const uint32_t word = dec.bm[w];
-      for (int b = 0; b < 32; ++b) o[w * 32 + b] = (uint16_t)dec.next((word >> b) & 1u);
-    }
+    dec.all(kv.D, out + idx * kv.D);
   }
 }
 
@@ -366,7 +373,8 @@ struct AttnArgs {
   float* part;        // [H][nchunks][rows][2 + D]
 };
 
-template <bool EXACT>
+// MAXR: a bound on the query rows (nq * G) the launch serves
+template <bool EXACT, int MAXR>
 __global__ void __launch_bounds__(256) k_kv_attn(KvDev kv, AttnArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
   float* qf = reinterpret_cast<float*>(smem);                // [rows][128]
@@ -377,34 +385,42 @@ __global__ void __launch_bounds__(256) k_kv_attn(KvDev kv, AttnArgs a) {
   const int rows = a.nq * a.G;
   const int tid = threadIdx.x;
   // query rows of this KV head: row r = qi * G + g  (query qi, head h*G + g)
-  for (int idx = tid; idx < rows * kDim; idx += 256) {
+  for (int idx = tid; idx < MAXR * kDim; idx += 256) {  // rows past `rows` stay zero
     const int r = idx / kDim, d = idx % kDim;
     const int qi = r / a.G, g = r % a.G;
-    qf[idx] = bf16_bits_to_float(a.q[((int64_t)qi * a.Hq + h * a.G + g) * kDim + d]);
+    qf[idx] = r < rows ? bf16_bits_to_float(a.q[((int64_t)qi * a.Hq + h * a.G + g) * kDim + d])
+                       : 0.f;
   }
   __syncthreads();
   const int64_t tok = (int64_t)c * kChunk + tid;
   const bool live = tok < a.T;
-  float s[kMaxRows];
+  float s[MAXR];
 #pragma unroll
-  for (int r = 0; r < kMaxRows; ++r) s[r] = 0.f;
-  if (live) {  // scores: positions visited in lock-step, so q reads are broadcasts
+  for (int r = 0; r < MAXR; ++r) s[r] = 0.f;
+  if (live) {  // scores: kept positions, then (exact) pruned positions
     KvVec<EXACT> dec;
     dec.init(kv, 2 * h, tok);
     for (int w = 0; w < kDim / 32; ++w) {
       const uint32_t word = dec.bm[w];
-      for (int b = 0; b < 32; ++b) {
-        const float kvv = bf16_bits_to_float(dec.next((word >> b) & 1u));
-        const int d = w * 32 + b;
+      for (uint32_t km = word; km; km &= km - 1u) {
+        const float kvv = bf16_bits_to_float(dec.kept());
+        const int d = w * 32 + __builtin_ctz(km);
 #pragma unroll
-        for (int r = 0; r < kMaxRows; ++r)
-          if (r < rows) s[r] = __builtin_fmaf(kvv, qf[r * kDim + d], s[r]);
+        for (int r = 0; r < MAXR; ++r) s[r] = __builtin_fmaf(kvv, qf[r * kDim + d], s[r]);
+      }
+      if (EXACT) {
+        for (uint32_t pm = ~word; pm; pm &= pm - 1u) {
+          const float kvv = bf16_bits_to_float(dec.pruned());
+          const int d = w * 32 + __builtin_ctz(pm);
+#pragma unroll
+          for (int r = 0; r < MAXR; ++r) s[r] = __builtin_fmaf(kvv, qf[r * kDim + d], s[r]);
+        }
       }
     }
   }
   // causal visibility: query qi sees tokens < T - nq + qi + 1
 #pragma unroll
-  for (int r = 0; r < kMaxRows; ++r) {
+  for (int r = 0; r < MAXR; ++r) {
     if (r < rows) {
       const int qi = r / a.G;
       const bool vis = live && tok < a.T - a.nq + qi + 1;
@@ -417,10 +433,7 @@ __global__ void __launch_bounds__(256) k_kv_attn(KvDev kv, AttnArgs a) {
     if (live) {
       KvVec<EXACT> dec;
       dec.init(kv, 2 * h + 1, tok);
-      for (int w = 0; w < kDim / 32; ++w) {
-        const uint32_t word = dec.bm[w];
-        for (int b = 0; b < 32; ++b) row[w * 32 + b] = (uint16_t)dec.next((word >> b) & 1u);
-      }
+      dec.all(kDim, row);
     } else {
       for (int d = 0; d < kDim; ++d) row[d] = 0;
     }
@@ -577,6 +590,15 @@ unsigned grid_of(int64_t n, int per) {
   return (unsigned)(g < 1 ? 1 : g);
 }
 
+template <bool EXACT, int MAXR>
+hipError_t attn_launch(const KvDev& d, const AttnArgs& a, int H, size_t lds, hipStream_t stream) {
+  hipError_t e = hipFuncSetAttribute((const void*)&k_kv_attn<EXACT, MAXR>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  k_kv_attn<EXACT, MAXR><<<dim3(H, a.nchunks), 256, lds, stream>>>(d, a);
+  return hipGetLastError();
+}
+
 int run_attention(const cass_kv* kv, const uint16_t* q, int nq, int n_q_heads, float scale,
                   float* out, void* ws, int64_t ws_bytes, hipStream_t stream, bool exact) {
   int st = check_kv(kv);
@@ -602,14 +624,16 @@ int run_attention(const cass_kv* kv, const uint16_t* q, int nq, int n_q_heads, f
   const KvDev d = dev_of(kv);
   const size_t lds = (size_t)kMaxRows * kDim * 4 + (size_t)kMaxRows * kChunk * 4 +
                      (size_t)kChunk * kVStride * 2;
-  const void* fn = exact ? (const void*)&k_kv_attn<true> : (const void*)&k_kv_attn<false>;
-  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  if (e != hipSuccess) return report(CASS_ERR_HIP, "attention LDS: %s", hipGetErrorString(e));
-  if (exact)
-    k_kv_attn<true><<<dim3(H, a.nchunks), 256, lds, stream>>>(d, a);
-  else
-    k_kv_attn<false><<<dim3(H, a.nchunks), 256, lds, stream>>>(d, a);
-  if ((e = hipGetLastError()) != hipSuccess) return report(CASS_ERR_HIP, "attention: %s", hipGetErrorString(e));
+  const int rows = nq * G;
+  hipError_t e = exact ? (rows <= 4    ? attn_launch<true, 4>(d, a, H, lds, stream)
+                          : rows <= 8  ? attn_launch<true, 8>(d, a, H, lds, stream)
+                          : rows <= 16 ? attn_launch<true, 16>(d, a, H, lds, stream)
+                                       : attn_launch<true, 32>(d, a, H, lds, stream))
+                       : (rows <= 4    ? attn_launch<false, 4>(d, a, H, lds, stream)
+                          : rows <= 8  ? attn_launch<false, 8>(d, a, H, lds, stream)
+                          : rows <= 16 ? attn_launch<false, 16>(d, a, H, lds, stream)
+                                       : attn_launch<false, 32>(d, a, H, lds, stream));
+  if (e != hipSuccess) return report(CASS_ERR_HIP, "attention: %s", hipGetErrorString(e));
   k_kv_merge<<<H * nq * G, kDim, 0, stream>>>(a, H, out);
   if ((e = hipGetLastError()) != hipSuccess) return report(CASS_ERR_HIP, "merge: %s", hipGetErrorString(e));
   return CASS_OK;

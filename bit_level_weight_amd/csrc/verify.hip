@@ -63,12 +63,11 @@ __global__ void __launch_bounds__(64) k_verify(SV sv, VV vv, Shape sh,
     for (int64_t wi = 0; wi < sh.block / 32; ++wi) {
       if (row_ok) {
         const uint32_t bw = sv.bitmap[(row * nb + b) * (sh.block / 32) + wi];
-#pragma unroll
-        for (int j = 0; j < 32; j += 2) {
-          const uint32_t lo = d.next((bw >> j) & 1u, (int)wi);
-          const uint32_t hi = d.next((bw >> (j + 1)) & 1u, (int)wi);
-          tile[lane * kTileStride + j / 2] = lo | (hi << 16);
-        }
+        // the word's kept positions, then its pruned ones (two loops, no
+        // per-position branch), straight into this lane's tile row
+        uint16_t* trow = reinterpret_cast<uint16_t*>(tile + lane * kTileStride);
+        for (uint32_t km = bw; km; km &= km - 1u) trow[__builtin_ctz(km)] = (uint16_t)d.kept((int)wi);
+        for (uint32_t pm = ~bw; pm; pm &= pm - 1u) trow[__builtin_ctz(pm)] = (uint16_t)d.pruned();
       } else {
 #pragma unroll
         for (int j = 0; j < 16; ++j) tile[lane * kTileStride + j] = 0u;
