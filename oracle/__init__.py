@@ -189,44 +189,46 @@ def _kv_lib():
     L = lib()
     if not getattr(L, "_kv_ready", False):
         P, I64 = ctypes.c_void_p, ctypes.c_int64
-        L.orc_kv_layout.argtypes = [I64, I64, ctypes.c_int, I64, I64, I64, P, P,
+        L.orc_kv_layout.argtypes = [ctypes.c_int, I64, I64, ctypes.c_int, I64, I64, I64, P, P,
                                     ctypes.POINTER(I64), ctypes.POINTER(I64)]
-        L.orc_kv_encode.argtypes = [P, I64, I64, I64, I64, ctypes.c_int, I64, I64, I64, P, P, P]
-        L.orc_kv_decode.argtypes = [P, P, I64, I64, I64, ctypes.c_int, I64, I64, I64, P]
+        L.orc_kv_encode.argtypes = [ctypes.c_int, P, I64, I64, I64, I64, ctypes.c_int, I64, I64,
+                                    I64, P, P, P]
+        L.orc_kv_decode.argtypes = [ctypes.c_int, P, P, I64, I64, I64, ctypes.c_int, I64, I64,
+                                    I64, P]
         L.orc_attention.argtypes = [P, I64, P, P, I64, I64, ctypes.c_double, P, P]
         L._kv_ready = True
     return L
 
 
-def kv_layout(D, k, m, T_max, code_cap, vcode_cap):
+def kv_layout(D, k, m, T_max, code_cap, vcode_cap, fmt=FMT_C1):
     """(spec part offsets[5], verif part offsets[5], spec bytes, verif bytes) of one stream."""
     so = np.zeros(5, dtype=np.int64)
     vo = np.zeros(5, dtype=np.int64)
     sb, vb = ctypes.c_int64(0), ctypes.c_int64(0)
-    _check(_kv_lib().orc_kv_layout(D, k, m, T_max, code_cap, vcode_cap, _p(so), _p(vo),
+    _check(_kv_lib().orc_kv_layout(fmt, D, k, m, T_max, code_cap, vcode_cap, _p(so), _p(vo),
                                    ctypes.byref(sb), ctypes.byref(vb)), "kv_layout")
     return so, vo, sb.value, vb.value
 
 
-def kv_encode(vec, T0, k, m, T_max, code_cap, vcode_cap):
+def kv_encode(vec, T0, k, m, T_max, code_cap, vcode_cap, fmt=FMT_C1):
     """One (head, K|V) stream of all tokens of vec[T, D] -> (spec, verif, tails)."""
     vec = _u16(vec)
     T, D = vec.shape
-    _, _, sb, vb = kv_layout(D, k, m, T_max, code_cap, vcode_cap)
+    _, _, sb, vb = kv_layout(D, k, m, T_max, code_cap, vcode_cap, fmt)
     spec = np.zeros(sb, dtype=np.uint8)
     verif = np.zeros(vb, dtype=np.uint8)
     tails = np.zeros(2, dtype=np.uint64)
-    _check(_kv_lib().orc_kv_encode(_p(vec), T, T0, D, k, m, T_max, code_cap, vcode_cap,
+    _check(_kv_lib().orc_kv_encode(fmt, _p(vec), T, T0, D, k, m, T_max, code_cap, vcode_cap,
                                    _p(spec), _p(verif), _p(tails)), "kv_encode")
     return spec, verif, tails
 
 
-def kv_decode(spec, T, D, k, m, T_max, code_cap, vcode_cap, verif=None):
+def kv_decode(spec, T, D, k, m, T_max, code_cap, vcode_cap, verif=None, fmt=FMT_C1):
     spec = np.ascontiguousarray(spec, dtype=np.uint8)
     if verif is not None:
         verif = np.ascontiguousarray(verif, dtype=np.uint8)
     out = np.zeros((T, D), dtype=np.uint16)
-    _check(_kv_lib().orc_kv_decode(_p(spec), _p(verif), T, D, k, m, T_max, code_cap,
+    _check(_kv_lib().orc_kv_decode(fmt, _p(spec), _p(verif), T, D, k, m, T_max, code_cap,
                                    vcode_cap, _p(out)), "kv_decode")
     return out
 

@@ -667,35 +667,44 @@ static int64_t kv_part(int64_t* pos, int64_t bytes) {
   return o;
 }
 
-int orc_kv_layout(int64_t D, int64_t k, int m, int64_t T_max, int64_t code_cap,
+int orc_kv_layout(int fmt, int64_t D, int64_t k, int m, int64_t T_max, int64_t code_cap,
                   int64_t vcode_cap, int64_t spec_off[5], int64_t verif_off[5],
                   int64_t* spec_bytes, int64_t* verif_bytes) {
-  if (D <= 0 || D % 32 || D > 65536 || k < 0 || k > D || m < 0 || m > 7 || T_max < 0 ||
-      code_cap < 0 || vcode_cap < 0 || code_cap >= ((int64_t)1 << 32) ||
-      vcode_cap >= ((int64_t)1 << 32))
+  if ((fmt != ORC_FMT_C1 && fmt != ORC_FMT_C2) || D <= 0 || D % 32 || D > 65536 || k < 0 ||
+      k > D || m < 0 || m > 7 || T_max < 0 || code_cap < 0 || vcode_cap < 0 ||
+      code_cap >= ((int64_t)1 << 32) || vcode_cap >= ((int64_t)1 << 32))
     return ORC_ERR_INVALID;
   int64_t p = 0;
   spec_off[0] = kv_part(&p, 256);
   spec_off[1] = kv_part(&p, T_max * D / 8);
-  spec_off[2] = kv_part(&p, 4 * T_max);
-  spec_off[3] = kv_part(&p, (T_max * k * (1 + m) + 7) / 8);
-  spec_off[4] = kv_part(&p, (code_cap + 7) / 8);
+  if (fmt == ORC_FMT_C1) {
+    spec_off[2] = kv_part(&p, 4 * T_max);
+    spec_off[3] = kv_part(&p, (T_max * k * (1 + m) + 7) / 8);
+    spec_off[4] = kv_part(&p, (code_cap + 7) / 8);
+  } else {
+    spec_off[2] = kv_part(&p, T_max * D / 32);               /* shared exponents */
+    spec_off[3] = kv_part(&p, (T_max * k * (2 + m) + 7) / 8); /* sign + aligned significand */
+    spec_off[4] = kv_part(&p, 0);
+  }
   *spec_bytes = p;
   p = 0;
   verif_off[0] = kv_part(&p, 256);
-  verif_off[1] = kv_part(&p, (T_max * k * (7 - m) + 7) / 8);
+  if (fmt == ORC_FMT_C1)
+    verif_off[1] = kv_part(&p, (T_max * k * (7 - m) + 7) / 8);
+  else
+    verif_off[1] = kv_part(&p, (code_cap + 7) / 8);          /* kept residues */
   verif_off[2] = kv_part(&p, T_max * (D - k));
-  verif_off[3] = kv_part(&p, 4 * T_max);
+  verif_off[3] = kv_part(&p, (fmt == ORC_FMT_C1 ? 4 : 8) * T_max);
   verif_off[4] = kv_part(&p, (vcode_cap + 7) / 8);
   *verif_bytes = p;
   return ORC_OK;
 }
 
-int orc_kv_encode(const uint16_t* vec, int64_t T, int64_t T0, int64_t D, int64_t k, int m,
-                  int64_t T_max, int64_t code_cap, int64_t vcode_cap, uint8_t* spec,
+int orc_kv_encode(int fmt, const uint16_t* vec, int64_t T, int64_t T0, int64_t D, int64_t k,
+                  int m, int64_t T_max, int64_t code_cap, int64_t vcode_cap, uint8_t* spec,
                   uint8_t* verif, uint64_t tails[2]) {
   int64_t so[5], vo[5], sb, vb;
-  int st = orc_kv_layout(D, k, m, T_max, code_cap, vcode_cap, so, vo, &sb, &vb);
+  int st = orc_kv_layout(fmt, D, k, m, T_max, code_cap, vcode_cap, so, vo, &sb, &vb);
   if (st) return st;
   if (T < 0 || T > T_max || (T > 0 && (T0 < 1 || T0 > T))) return ORC_ERR_INVALID;
   memset(spec, 0, (size_t)sb);
@@ -710,12 +719,25 @@ int orc_kv_encode(const uint16_t* vec, int64_t T, int64_t T0, int64_t D, int64_t
   orc_rank_table(hk, perm_s);
   orc_rank_table(hp, perm_v);
   for (int r = 0; r < 256; r++) { rank_s[perm_s[r]] = r; rank_v[perm_v[r]] = r; }
-  memcpy(spec + so[0], perm_s, 256);
+  if (fmt == ORC_FMT_C1) memcpy(spec + so[0], perm_s, 256);
   memcpy(verif + vo[0], perm_v, 256);
-  uint64_t stail = 0, vtail = 0;
+  uint64_t stail = 0, vtail = 0;  /* C-2: stail counts residue bits */
   for (int64_t t = 0; t < T; t++) {
-    put_u32(spec + so[2] + 4 * t, (uint32_t)stail);
-    put_u32(verif + vo[3] + 4 * t, (uint32_t)vtail);
+    if (fmt == ORC_FMT_C1) {
+      put_u32(spec + so[2] + 4 * t, (uint32_t)stail);
+      put_u32(verif + vo[3] + 4 * t, (uint32_t)vtail);
+    } else {
+      put_u32(verif + vo[3] + 8 * t, (uint32_t)stail);
+      put_u32(verif + vo[3] + 8 * t + 4, (uint32_t)vtail);
+      /* shared exponent of each 32 positions: the largest max(e,1) over the
+       * kept values, 0 when none is kept [MX] */
+      for (int64_t g = 0; g < D / 32; g++) {
+        int E = 0;
+        for (int64_t j = g * 32; j < g * 32 + 32; j++)
+          if (keep[t * D + j] && mx_eff(vec[t * D + j]) > E) E = mx_eff(vec[t * D + j]);
+        spec[so[2] + t * (D / 32) + g] = (uint8_t)E;
+      }
+    }
     int64_t kept_i = 0, pr_i = 0;
     for (int64_t j = 0; j < D; j++) {
       uint16_t b = vec[t * D + j];
@@ -723,11 +745,23 @@ int orc_kv_encode(const uint16_t* vec, int64_t T, int64_t T0, int64_t D, int64_t
       if (keep[t * D + j]) {
         int64_t kin = t * k + kept_i;
         put_bits(spec + so[1], (uint64_t)(t * D + j), 1, 1);
-        put_bits(spec + so[3], (uint64_t)kin * (1 + m), (uint64_t)((s << m) | (f >> (7 - m))), 1 + m);
-        if (stail + (uint64_t)rank_s[e] + 1 > (uint64_t)code_cap) { free(keep); return ORC_ERR_CAPACITY; }
-        put_unary(spec + so[4], stail, rank_s[e]);
-        stail += (uint64_t)rank_s[e] + 1;
-        put_bits(verif + vo[1], (uint64_t)kin * (7 - m), (uint64_t)(f & ((1 << (7 - m)) - 1)), 7 - m);
+        if (fmt == ORC_FMT_C1) {
+          put_bits(spec + so[3], (uint64_t)kin * (1 + m), (uint64_t)((s << m) | (f >> (7 - m))), 1 + m);
+          if (stail + (uint64_t)rank_s[e] + 1 > (uint64_t)code_cap) { free(keep); return ORC_ERR_CAPACITY; }
+          put_unary(spec + so[4], stail, rank_s[e]);
+          stail += (uint64_t)rank_s[e] + 1;
+          put_bits(verif + vo[1], (uint64_t)kin * (7 - m), (uint64_t)(f & ((1 << (7 - m)) - 1)), 7 - m);
+        } else {
+          const int E = spec[so[2] + t * (D / 32) + j / 32];
+          const int d = E - mx_eff(b), M = mx_sig(b), shift = 7 - m + d;
+          const int a = shift >= 8 ? 0 : M >> shift, wdt = shift < 8 ? shift : 8;
+          put_bits(spec + so[3], (uint64_t)kin * (2 + m), (uint64_t)((s << (m + 1)) | a), 2 + m);
+          if (stail + (uint64_t)d + 1 + (uint64_t)wdt > (uint64_t)code_cap) { free(keep); return ORC_ERR_CAPACITY; }
+          put_unary(verif + vo[1], stail, d);
+          stail += (uint64_t)d + 1;
+          put_bits(verif + vo[1], stail, (uint64_t)(M & ((1 << wdt) - 1)), wdt);
+          stail += (uint64_t)wdt;
+        }
         kept_i++;
       } else {
         verif[vo[2] + t * (D - k) + pr_i] = (uint8_t)((s << 7) | f);
@@ -744,28 +778,54 @@ int orc_kv_encode(const uint16_t* vec, int64_t T, int64_t T0, int64_t D, int64_t
   return ORC_OK;
 }
 
-int orc_kv_decode(const uint8_t* spec, const uint8_t* verif, int64_t T, int64_t D, int64_t k,
-                  int m, int64_t T_max, int64_t code_cap, int64_t vcode_cap, uint16_t* out) {
+int orc_kv_decode(int fmt, const uint8_t* spec, const uint8_t* verif, int64_t T, int64_t D,
+                  int64_t k, int m, int64_t T_max, int64_t code_cap, int64_t vcode_cap,
+                  uint16_t* out) {
   int64_t so[5], vo[5], sb, vb;
-  int st = orc_kv_layout(D, k, m, T_max, code_cap, vcode_cap, so, vo, &sb, &vb);
+  int st = orc_kv_layout(fmt, D, k, m, T_max, code_cap, vcode_cap, so, vo, &sb, &vb);
   if (st) return st;
   if (T < 0 || T > T_max) return ORC_ERR_INVALID;
   for (int64_t t = 0; t < T; t++) {
-    uint64_t spos = get_u32(spec + so[2] + 4 * t);
-    uint64_t vpos = verif ? get_u32(verif + vo[3] + 4 * t) : 0;
+    uint64_t spos, vpos = 0;
+    if (fmt == ORC_FMT_C1) {
+      spos = get_u32(spec + so[2] + 4 * t);
+      if (verif) vpos = get_u32(verif + vo[3] + 4 * t);
+    } else {
+      spos = verif ? get_u32(verif + vo[3] + 8 * t) : 0;
+      if (verif) vpos = get_u32(verif + vo[3] + 8 * t + 4);
+    }
     int64_t kept_i = 0, pr_i = 0;
     for (int64_t j = 0; j < D; j++) {
       if (get_bits(spec + so[1], (uint64_t)(t * D + j), 1)) {
         if (kept_i >= k) return ORC_ERR_CORRUPT;
         int64_t kin = t * k + kept_i;
-        int field = (int)get_bits(spec + so[3], (uint64_t)kin * (1 + m), 1 + m);
-        int rank = get_unary(spec + so[4], spos, (uint64_t)code_cap);
-        if (rank < 0) return ORC_ERR_CORRUPT;
-        spos += (uint64_t)rank + 1;
-        int s = field >> m, ft = field & ((1 << m) - 1), e = spec[so[0] + rank];
-        uint16_t d = (uint16_t)((s << 15) | (e << 7) | (ft << (7 - m)));
-        if (verif) d |= (uint16_t)get_bits(verif + vo[1], (uint64_t)kin * (7 - m), 7 - m);
-        out[t * D + j] = d;
+        if (fmt == ORC_FMT_C1) {
+          int field = (int)get_bits(spec + so[3], (uint64_t)kin * (1 + m), 1 + m);
+          int rank = get_unary(spec + so[4], spos, (uint64_t)code_cap);
+          if (rank < 0) return ORC_ERR_CORRUPT;
+          spos += (uint64_t)rank + 1;
+          int s = field >> m, ft = field & ((1 << m) - 1), e = spec[so[0] + rank];
+          uint16_t d = (uint16_t)((s << 15) | (e << 7) | (ft << (7 - m)));
+          if (verif) d |= (uint16_t)get_bits(verif + vo[1], (uint64_t)kin * (7 - m), 7 - m);
+          out[t * D + j] = d;
+        } else {
+          int field = (int)get_bits(spec + so[3], (uint64_t)kin * (2 + m), 2 + m);
+          int s = field >> (m + 1), a = field & ((2 << m) - 1);
+          int E = spec[so[2] + t * (D / 32) + j / 32];
+          if (!verif) {
+            out[t * D + j] = mx_draft_bits(s, a, E, m);
+          } else {
+            int d = get_unary(verif + vo[1], spos, (uint64_t)code_cap);
+            if (d < 0) return ORC_ERR_CORRUPT;
+            spos += (uint64_t)d + 1;
+            int wdt = 7 - m + d < 8 ? 7 - m + d : 8;
+            int L = (int)get_bits(verif + vo[1], spos, wdt);
+            spos += (uint64_t)wdt;
+            int M = wdt < 8 ? ((a << wdt) | L) : L;
+            int e = M >= 128 ? E - d : 0;
+            out[t * D + j] = (uint16_t)((s << 15) | ((e & 0xFF) << 7) | (M & 0x7F));
+          }
+        }
         kept_i++;
       } else {
         if (verif) {

@@ -92,17 +92,27 @@ int orc_header(const uint8_t* buf, int64_t len, uint32_t expect_magic, int64_t o
  *   verification region: perm[256] | low mantissas (7-m bits at (t*k+i)*(7-m))
  *     | pruned bytes (token t pruned i at byte t*(D-k)+i) | code offsets
  *     u32[T_max] | codes (vcode_cap bits)
+ * Cassandra-2 (fmt = ORC_FMT_C2; OCP MX shared exponent per 32 positions):
+ *   speculation region: (256 unused bytes) | bitmap | shared exponents
+ *     (u8 per 32 positions, token t group g at byte t*D/32+g) | fields
+ *     ((s<<(m+1))|a, m+2 bits at (t*k+i)*(m+2)) | (empty)
+ *   verification region: perm[256] of pruned exponents | kept residues
+ *     (unary(d) then min(8, 7-m+d) low significand bits, code_cap bits) |
+ *     pruned bytes | offsets u32[2*T_max] (token t: residue bit, pruned-code
+ *     bit) | pruned codes (vcode_cap bits)
  * The rank tables come from the tokens of the first append (t < T0) and are
- * frozen afterwards.  Returns the region sizes with spec == NULL. */
-int orc_kv_layout(int64_t D, int64_t k, int m, int64_t T_max, int64_t code_cap,
+ * frozen afterwards.  tails[0] counts the speculation codes (C-1) or the
+ * residue bits (C-2), tails[1] the pruned codes. */
+int orc_kv_layout(int fmt, int64_t D, int64_t k, int m, int64_t T_max, int64_t code_cap,
                   int64_t vcode_cap, int64_t spec_off[5], int64_t verif_off[5],
                   int64_t* spec_bytes, int64_t* verif_bytes);
-int orc_kv_encode(const uint16_t* vec, int64_t T, int64_t T0, int64_t D, int64_t k, int m,
-                  int64_t T_max, int64_t code_cap, int64_t vcode_cap, uint8_t* spec,
+int orc_kv_encode(int fmt, const uint16_t* vec, int64_t T, int64_t T0, int64_t D, int64_t k,
+                  int m, int64_t T_max, int64_t code_cap, int64_t vcode_cap, uint8_t* spec,
                   uint8_t* verif, uint64_t tails[2]);
 /* Draft (verif == NULL) or exact vectors of the first T tokens: out[T][D]. */
-int orc_kv_decode(const uint8_t* spec, const uint8_t* verif, int64_t T, int64_t D, int64_t k,
-                  int m, int64_t T_max, int64_t code_cap, int64_t vcode_cap, uint16_t* out);
+int orc_kv_decode(int fmt, const uint8_t* spec, const uint8_t* verif, int64_t T, int64_t D,
+                  int64_t k, int m, int64_t T_max, int64_t code_cap, int64_t vcode_cap,
+                  uint16_t* out);
 
 /* Softmax attention of nq queries over T tokens, fp64:
  * s_t = scale * sum_d q[d] K[t][d]; p = softmax over t < visible[i];
