@@ -70,7 +70,7 @@ class CassKvParams(ctypes.Structure):
     _fields_ = [("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("keep", ctypes.c_int32), ("mant_bits", ctypes.c_int32),
                 ("max_tokens", ctypes.c_int64), ("code_cap_bits", ctypes.c_int64),
-                ("vcode_cap_bits", ctypes.c_int64)]
+                ("vcode_cap_bits", ctypes.c_int64), ("format", ctypes.c_int32)]
 
 
 class CassKv(ctypes.Structure):
@@ -329,12 +329,14 @@ class KvCache:
     """Device buffers (torch) of one layer's compressed KV cache and its descriptor."""
 
     def __init__(self, n_kv_heads, head_dim, keep, mant_bits, max_tokens, code_cap_bits=None,
-                 vcode_cap_bits=None, device="cuda", stream=None):
+                 vcode_cap_bits=None, device="cuda", stream=None, fmt=CASS_FMT_C1_UNARY):
         import torch
-        code_cap_bits = code_cap_bits or max_tokens * keep * 8
+        # default capacities: 8 bits per kept (C-1 codes) or 24 per kept
+        # (C-2 residues), 8 per pruned value
+        code_cap_bits = code_cap_bits or max_tokens * keep * (8 if fmt == CASS_FMT_C1_UNARY else 24)
         vcode_cap_bits = vcode_cap_bits or max_tokens * (head_dim - keep) * 8
         self.params = CassKvParams(n_kv_heads, head_dim, keep, mant_bits, max_tokens,
-                                   code_cap_bits, vcode_cap_bits)
+                                   code_cap_bits, vcode_cap_bits, fmt)
         sb, vb, tb = cass_kv_bytes(self.params)
         self.spec = torch.empty(sb, dtype=torch.uint8, device=device)
         self.verif = torch.empty(vb, dtype=torch.uint8, device=device)

@@ -14,6 +14,7 @@
 #include <string.h>
 
 #include "bits.hpp"
+#include "decoders.hpp"
 #include "internal.hpp"
 
 namespace cass {
@@ -30,6 +31,7 @@ struct KvDev {
   int64_t so[5], vo[5];       // part offsets inside a region
   int H, D, k, m;
   int64_t T_max, ccap, vcap;
+  int fmt;                    // CASS_FMT_C1_UNARY or CASS_FMT_C2_MX32
 };
 
 // Append workspace (per call, nvec = ntok * 2H vectors).
@@ -99,6 +101,7 @@ __global__ void __launch_bounds__(256) k_kv_ranks(KvDev kv, AppendWs ws) {
   cnt[256 + t] = ws.hist[s * 512 + 256 + t];
   __syncthreads();
   for (int which = 0; which < 2; ++which) {
+    if (which == 0 && kv.fmt != CASS_FMT_C1_UNARY) continue;  // C-2 codes pruned exponents only
     const uint32_t* c = cnt + which * 256;
     int rank = 0;  // count descending, symbol ascending
     for (int u = 0; u < 256; ++u) rank += (c[u] > c[t]) || (c[u] == c[t] && u < t);
@@ -141,6 +144,18 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v, int lane) {
   return v;
 }
 
+// Shared exponent of the lane's 32 positions (lanes 0-31 and 32-63 each hold
+// one group): the largest max(e,1) over the group's kept values, 0 if none.
+__device__ __forceinline__ int group_shexp(bool kept, int e) {
+  int E = kept ? (e > 0 ? e : 1) : 0;
+#pragma unroll
+  for (int o = 16; o >= 1; o >>= 1) {
+    const int u = __shfl_xor(E, o, 64);
+    E = u > E ? u : E;
+  }
+  return E;
+}
+
 // ---- append, step 3: code bits of each vector ----
 __global__ void __launch_bounds__(64 * kWaves) k_kv_lengths(KvDev kv, const uint16_t* kk,
                                                             const uint16_t* vv, int ntok,
@@ -157,10 +172,24 @@ __global__ void __launch_bounds__(64 * kWaves) k_kv_lengths(KvDev kv, const uint
   load_ranks(kv, s, rs[wv], rv[wv], lane);
   const uint16_t* x = vec_ptr(kk, vv, t, h, kind, kv.H, kv.D);
   uint32_t a = 0, b = 0;
-  for (int j = lane; j < kv.D; j += 64) {
-    const int e = (x[j] >> 7) & 0xFF;
-    if (kept_bit(ws, vi, kv.D, j)) a += rs[wv][e] + 1u;
-    else b += rv[wv][e] + 1u;
+  if (kv.fmt == CASS_FMT_C1_UNARY) {
+    for (int j = lane; j < kv.D; j += 64) {
+      const int e = (x[j] >> 7) & 0xFF;
+      if (kept_bit(ws, vi, kv.D, j)) a += rs[wv][e] + 1u;
+      else b += rv[wv][e] + 1u;
+    }
+  } else {
+    // Cassandra-2: a kept value's residue is unary(d) and min(8, 7-m+d) bits
+    for (int c0 = 0; c0 < kv.D; c0 += 64) {
+      const int j = c0 + lane;
+      const bool in = j < kv.D;
+      const int e = in ? (x[j] >> 7) & 0xFF : 0;
+      const bool kept = in && kept_bit(ws, vi, kv.D, j);
+      const int d = group_shexp(kept, e) - (e > 0 ? e : 1);
+      const int w = 7 - kv.m + d < 8 ? 7 - kv.m + d : 8;
+      if (kept) a += (uint32_t)(d + 1 + w);
+      else if (in) b += rv[wv][e] + 1u;
+    }
   }
   a = wave_sum(a);
   b = wave_sum(b);
@@ -179,8 +208,12 @@ __global__ void __launch_bounds__(256) k_kv_scan(KvDev kv, int ntok, int64_t t0,
   const int t = threadIdx.x;
   unsigned long long base[2] = {kv.state[2 + 2 * s], kv.state[3 + 2 * s]};
   const unsigned long long cap[2] = {(unsigned long long)kv.ccap, (unsigned long long)kv.vcap};
-  uint32_t* offs[2] = {(uint32_t*)(kv.spec + s * kv.sstride + kv.so[2]),
-                       (uint32_t*)(kv.verif + s * kv.vstride + kv.vo[3])};
+  // token offsets: C-1 spec code / pruned code; C-2 a (residue, pruned code) pair
+  const bool c1 = kv.fmt == CASS_FMT_C1_UNARY;
+  uint32_t* vofs = (uint32_t*)(kv.verif + s * kv.vstride + kv.vo[3]);
+  uint32_t* offs[2] = {c1 ? (uint32_t*)(kv.spec + s * kv.sstride + kv.so[2]) : vofs,
+                       c1 ? vofs : vofs + 1};
+  const int ostride = c1 ? 1 : 2;
   for (int which = 0; which < 2; ++which) {
     unsigned long long carry = base[which];
     bool over = false;
@@ -200,7 +233,7 @@ __global__ void __launch_bounds__(256) k_kv_scan(KvDev kv, int ntok, int64_t t0,
       if (i < ntok) {
         const bool fits = st + len <= cap[which];
         ws.start[2 * vi + which] = fits ? (uint32_t)st : 0xFFFFFFFFu;
-        offs[which][t0 + i] = fits ? (uint32_t)st : 0xFFFFFFFFu;
+        offs[which][(t0 + i) * ostride] = fits ? (uint32_t)st : 0xFFFFFFFFu;
         if (!fits) over = true;
       }
       if (t == 255) carry_s[which] = carry + tmp[255];
@@ -253,6 +286,48 @@ __global__ void __launch_bounds__(64 * kWaves) k_kv_pack(KvDev kv, const uint16_
   }
   const uint32_t sstart = ws.start[2 * vi], vstart = ws.start[2 * vi + 1];
   uint32_t kept_carry = 0, scode_carry = 0, vcode_carry = 0;
+  if (kv.fmt != CASS_FMT_C1_UNARY) {
+    // Cassandra-2: shared exponents, aligned significands, residues
+    for (int c0 = 0; c0 < D; c0 += 64) {
+      const int j = c0 + lane;
+      const bool in = j < D;
+      const uint16_t b = in ? x[j] : 0;
+      const bool kept = in && kept_bit(ws, vi, D, j);
+      const int sgn = b >> 15, e = (b >> 7) & 0xFF, f = b & 0x7F;
+      const int eff = e > 0 ? e : 1, M = ((e > 0) << 7) | f;
+      const int E = group_shexp(kept, e);
+      const int d = E - eff, shift = 7 - m + d;
+      const int a = shift >= 8 ? 0 : M >> shift, w = shift < 8 ? shift : 8;
+      const unsigned long long km = __ballot(kept);
+      const unsigned long long pm = __ballot(in && !kept);
+      const uint32_t kidx = kept_carry + (uint32_t)__builtin_popcountll(km & ((1ull << lane) - 1ull));
+      const uint32_t pidx = (uint32_t)(c0 - kept_carry) +
+                            (uint32_t)__builtin_popcountll(pm & ((1ull << lane) - 1ull));
+      const uint32_t rlen = kept ? (uint32_t)(d + 1 + w) : 0u;
+      const uint32_t vlen = (in && !kept) ? rv[wv][e] + 1u : 0u;
+      const uint32_t rin = wave_incl_scan(rlen, lane), vin = wave_incl_scan(vlen, lane);
+      if (in && (j & 31) == 0) (sr + kv.so[2])[tok * (D / 32) + j / 32] = (uint8_t)E;
+      if (kept) {
+        const uint64_t kin = (uint64_t)tok * k + kidx;
+        or_bits(sr + kv.so[3], kin * (uint64_t)(2 + m), (uint32_t)((sgn << (m + 1)) | a), 2 + m);
+        if (sstart != 0xFFFFFFFFu) {
+          const uint64_t pos = (uint64_t)sstart + scode_carry + rin - rlen;
+          or_bits(vr + kv.vo[1], pos + (uint64_t)d, 1u, 1);  // unary(d): its one bit
+          or_bits(vr + kv.vo[1], pos + (uint64_t)d + 1u, (uint32_t)(M & ((1 << w) - 1)), w);
+        }
+      } else if (in) {
+        (vr + kv.vo[2])[tok * (D - k) + pidx] = (uint8_t)((sgn << 7) | f);
+        if (vstart != 0xFFFFFFFFu) {
+          const uint64_t endbit = (uint64_t)vstart + vcode_carry + vin - 1u;
+          or_bits(vr + kv.vo[4], endbit, 1u, 1);
+        }
+      }
+      kept_carry += (uint32_t)__builtin_popcountll(km);
+      scode_carry += __shfl(rin, 63, 64);
+      vcode_carry += __shfl(vin, 63, 64);
+    }
+    return;
+  }
   for (int c0 = 0; c0 < D; c0 += 64) {
     const int j = c0 + lane;
     const bool in = j < D;
@@ -289,14 +364,17 @@ __global__ void __launch_bounds__(64 * kWaves) k_kv_pack(KvDev kv, const uint16_
 }
 
 // ---- per-lane decoder of one cached vector (token tok of stream s) ----
-// kept() gives the vector's kept values in position order, pruned() its
-// pruned values (exact decoding only); callers walk the keep-bitmap words
-// with two loops, kept positions then pruned positions.
-template <bool EXACT>
+// kept(w) gives the vector's kept values in position order (w: the bitmap
+// word the value sits in), pruned() its pruned values (exact decoding only);
+// callers walk the keep-bitmap words with two loops, kept positions then
+// pruned positions.  FMT: Cassandra-1 (unary exponent codes) or Cassandra-2
+// (shared exponent per 32 positions, residues for the exact values).
+template <bool EXACT, int FMT>
 struct KvVec {
   BitReader fr, cr, lr, vcr, pr;
   const uint8_t* perm_s;
   const uint8_t* perm_v;
+  const uint8_t* shexp;
   const uint32_t* bm;
   int m;
   __device__ __forceinline__ void init(const KvDev& kv, int s, int64_t tok) {
@@ -304,26 +382,51 @@ struct KvVec {
     const uint8_t* vr = kv.verif + s * kv.vstride;
     m = kv.m;
     bm = reinterpret_cast<const uint32_t*>(sr + kv.so[1]) + tok * (kv.D / 32);
-    perm_s = sr + kv.so[0];
-    fr.init(reinterpret_cast<const uint32_t*>(sr + kv.so[3]), (uint64_t)tok * kv.k * (1 + m));
     // a token whose codes did not fit (overflow flag) reads code bit 0 instead:
     // its values are meaningless but every read stays inside the region
-    uint32_t off = reinterpret_cast<const uint32_t*>(sr + kv.so[2])[tok];
-    cr.init(reinterpret_cast<const uint32_t*>(sr + kv.so[4]), off == 0xFFFFFFFFu ? 0u : off);
+    if (FMT == CASS_FMT_C1_UNARY) {
+      perm_s = sr + kv.so[0];
+      fr.init(reinterpret_cast<const uint32_t*>(sr + kv.so[3]), (uint64_t)tok * kv.k * (1 + m));
+      const uint32_t off = reinterpret_cast<const uint32_t*>(sr + kv.so[2])[tok];
+      cr.init(reinterpret_cast<const uint32_t*>(sr + kv.so[4]), off == 0xFFFFFFFFu ? 0u : off);
+    } else {
+      shexp = sr + kv.so[2] + tok * (kv.D / 32);
+      fr.init(reinterpret_cast<const uint32_t*>(sr + kv.so[3]), (uint64_t)tok * kv.k * (2 + m));
+    }
     if (EXACT) {
       perm_v = vr + kv.vo[0];
-      lr.init(reinterpret_cast<const uint32_t*>(vr + kv.vo[1]), (uint64_t)tok * kv.k * (7 - m));
       pr.init(reinterpret_cast<const uint32_t*>(vr + kv.vo[2]), (uint64_t)tok * (kv.D - kv.k) * 8u);
-      off = reinterpret_cast<const uint32_t*>(vr + kv.vo[3])[tok];
-      vcr.init(reinterpret_cast<const uint32_t*>(vr + kv.vo[4]), off == 0xFFFFFFFFu ? 0u : off);
+      const uint32_t* ofs = reinterpret_cast<const uint32_t*>(vr + kv.vo[3]);
+      uint32_t poff;
+      if (FMT == CASS_FMT_C1_UNARY) {
+        lr.init(reinterpret_cast<const uint32_t*>(vr + kv.vo[1]), (uint64_t)tok * kv.k * (7 - m));
+        poff = ofs[tok];
+      } else {
+        const uint32_t roff = ofs[2 * tok];
+        lr.init(reinterpret_cast<const uint32_t*>(vr + kv.vo[1]), roff == 0xFFFFFFFFu ? 0u : roff);
+        poff = ofs[2 * tok + 1];
+      }
+      vcr.init(reinterpret_cast<const uint32_t*>(vr + kv.vo[4]), poff == 0xFFFFFFFFu ? 0u : poff);
     }
   }
-  __device__ __forceinline__ uint32_t kept() {
-    const uint32_t f = fr.take(1 + m);
-    const uint32_t e = perm_s[cr.unary()];
-    uint32_t bits = ((f >> m) << 15) | (e << 7) | ((f & ((1u << m) - 1u)) << (7 - m));
-    if (EXACT) bits |= lr.take(7 - m);
-    return bits;
+  __device__ __forceinline__ uint32_t kept(int w) {
+    if (FMT == CASS_FMT_C1_UNARY) {
+      const uint32_t f = fr.take(1 + m);
+      const uint32_t e = perm_s[cr.unary()];
+      uint32_t bits = ((f >> m) << 15) | (e << 7) | ((f & ((1u << m) - 1u)) << (7 - m));
+      if (EXACT) bits |= lr.take(7 - m);
+      return bits;
+    }
+    const int E = shexp[w];
+    const uint32_t f = fr.take(2 + m);
+    const uint32_t sg = f >> (m + 1), a = f & ((2u << m) - 1u);
+    if (!EXACT) return mx_value_bits(sg, a, E, m);
+    const int d = lr.unary();
+    const int wd = (7 - m + d < 8) ? 7 - m + d : 8;
+    const uint32_t L = lr.take(wd);
+    const uint32_t M = (wd < 8) ? ((a << wd) | L) : L;
+    const uint32_t e = (M >= 128u) ? (uint32_t)(E - d) : 0u;
+    return (sg << 15) | ((e & 0xFF) << 7) | (M & 0x7F);
   }
   __device__ __forceinline__ uint32_t pruned() {
     const uint32_t byte = pr.take(8);
@@ -336,7 +439,7 @@ struct KvVec {
       const uint32_t word = bm[w];
       if (!EXACT)
         for (int b = 0; b < 32; ++b) o[w * 32 + b] = 0;
-      for (uint32_t km = word; km; km &= km - 1u) o[w * 32 + __builtin_ctz(km)] = (uint16_t)kept();
+      for (uint32_t km = word; km; km &= km - 1u) o[w * 32 + __builtin_ctz(km)] = (uint16_t)kept(w);
       if (EXACT)
         for (uint32_t pm = ~word; pm; pm &= pm - 1u) o[w * 32 + __builtin_ctz(pm)] = (uint16_t)pruned();
     }
@@ -344,7 +447,7 @@ struct KvVec {
 };
 
 // ---- decode the whole cache (tests, checks) ----
-template <bool EXACT>
+template <bool EXACT, int FMT>
 __global__ void __launch_bounds__(256) k_kv_decode(KvDev kv, int64_t T, uint16_t* out) {
   const int64_t n = (int64_t)2 * kv.H * T;
   for (int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; idx < n;
@@ -352,7 +455,7 @@ __global__ void __launch_bounds__(256) k_kv_decode(KvDev kv, int64_t T, uint16_t
     const int64_t tok = idx % T;
     const int s = (int)(idx / T);  // out is [kind][head][T][D]
     const int kind = s / kv.H, h = s % kv.H;
-    KvVec<EXACT> dec;
+    KvVec<EXACT, FMT> dec;
     dec.init(kv, 2 * h + kind, tok);
     dec.all(kv.D, out + idx * kv.D);
   }
@@ -374,7 +477,7 @@ struct AttnArgs {
 };
 
 // MAXR: a bound on the query rows (nq * G) the launch serves
-template <bool EXACT, int MAXR>
+template <bool EXACT, int MAXR, int FMT>
 __global__ void __launch_bounds__(256) k_kv_attn(KvDev kv, AttnArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
   float* qf = reinterpret_cast<float*>(smem);                // [rows][128]
@@ -398,12 +501,12 @@ __global__ void __launch_bounds__(256) k_kv_attn(KvDev kv, AttnArgs a) {
 #pragma unroll
   for (int r = 0; r < MAXR; ++r) s[r] = 0.f;
   if (live) {  // scores: kept positions, then (exact) pruned positions
-    KvVec<EXACT> dec;
+    KvVec<EXACT, FMT> dec;
     dec.init(kv, 2 * h, tok);
     for (int w = 0; w < kDim / 32; ++w) {
       const uint32_t word = dec.bm[w];
       for (uint32_t km = word; km; km &= km - 1u) {
-        const float kvv = bf16_bits_to_float(dec.kept());
+        const float kvv = bf16_bits_to_float(dec.kept(w));
         const int d = w * 32 + __builtin_ctz(km);
 #pragma unroll
         for (int r = 0; r < MAXR; ++r) s[r] = __builtin_fmaf(kvv, qf[r * kDim + d], s[r]);
@@ -431,7 +534,7 @@ __global__ void __launch_bounds__(256) k_kv_attn(KvDev kv, AttnArgs a) {
   {
     uint16_t* row = vt + tid * kVStride;
     if (live) {
-      KvVec<EXACT> dec;
+      KvVec<EXACT, FMT> dec;
       dec.init(kv, 2 * h + 1, tok);
       dec.all(kDim, row);
     } else {
@@ -504,6 +607,10 @@ int64_t part_at(int64_t* pos, int64_t bytes) {
   return o;
 }
 
+int fmt_of(const cass_kv_params* p) {
+  return p->format == 0 ? CASS_FMT_C1_UNARY : p->format;
+}
+
 int check_kv_params(const cass_kv_params* p) {
   if (!p) return report(CASS_ERR_INVALID, "kv params is NULL");
   if (p->n_kv_heads < 1 || p->n_kv_heads > 64 || p->head_dim < 32 || p->head_dim > 256 ||
@@ -511,23 +618,31 @@ int check_kv_params(const cass_kv_params* p) {
       p->mant_bits > 7 || p->max_tokens < 0 || p->code_cap_bits < 0 || p->vcode_cap_bits < 0 ||
       p->code_cap_bits >= ((int64_t)1 << 32) || p->vcode_cap_bits >= ((int64_t)1 << 32))
     return report(CASS_ERR_INVALID, "bad kv params");
+  if (fmt_of(p) != CASS_FMT_C1_UNARY && fmt_of(p) != CASS_FMT_C2_MX32)
+    return report(CASS_ERR_INVALID, "bad kv format %d", p->format);
   return CASS_OK;
 }
-
 void kv_layout(const cass_kv_params* p, int64_t* so, int64_t* vo, int64_t* sb, int64_t* vb) {
   const int64_t D = p->head_dim, k = p->keep, m = p->mant_bits, T = p->max_tokens;
+  const bool c1 = fmt_of(p) == CASS_FMT_C1_UNARY;
   int64_t pos = 0;
   so[0] = part_at(&pos, 256);
   so[1] = part_at(&pos, T * D / 8);
-  so[2] = part_at(&pos, 4 * T);
-  so[3] = part_at(&pos, (T * k * (1 + m) + 7) / 8);
-  so[4] = part_at(&pos, (p->code_cap_bits + 7) / 8);
+  if (c1) {
+    so[2] = part_at(&pos, 4 * T);
+    so[3] = part_at(&pos, (T * k * (1 + m) + 7) / 8);
+    so[4] = part_at(&pos, (p->code_cap_bits + 7) / 8);
+  } else {
+    so[2] = part_at(&pos, T * D / 32);
+    so[3] = part_at(&pos, (T * k * (2 + m) + 7) / 8);
+    so[4] = part_at(&pos, 0);
+  }
   *sb = pos;
   pos = 0;
   vo[0] = part_at(&pos, 256);
-  vo[1] = part_at(&pos, (T * k * (7 - m) + 7) / 8);
+  vo[1] = c1 ? part_at(&pos, (T * k * (7 - m) + 7) / 8) : part_at(&pos, (p->code_cap_bits + 7) / 8);
   vo[2] = part_at(&pos, T * (D - k));
-  vo[3] = part_at(&pos, 4 * T);
+  vo[3] = part_at(&pos, (c1 ? 4 : 8) * T);
   vo[4] = part_at(&pos, (p->vcode_cap_bits + 7) / 8);
   *vb = pos;
 }
@@ -550,6 +665,7 @@ KvDev dev_of(const cass_kv* kv) {
   d.T_max = kv->p.max_tokens;
   d.ccap = kv->p.code_cap_bits;
   d.vcap = kv->p.vcode_cap_bits;
+  d.fmt = fmt_of(&kv->p);
   return d;
 }
 
@@ -590,13 +706,19 @@ unsigned grid_of(int64_t n, int per) {
   return (unsigned)(g < 1 ? 1 : g);
 }
 
-template <bool EXACT, int MAXR>
-hipError_t attn_launch(const KvDev& d, const AttnArgs& a, int H, size_t lds, hipStream_t stream) {
-  hipError_t e = hipFuncSetAttribute((const void*)&k_kv_attn<EXACT, MAXR>,
+template <bool EXACT, int MAXR, int FMT>
+hipError_t attn_launch_f(const KvDev& d, const AttnArgs& a, int H, size_t lds, hipStream_t stream) {
+  hipError_t e = hipFuncSetAttribute((const void*)&k_kv_attn<EXACT, MAXR, FMT>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  k_kv_attn<EXACT, MAXR><<<dim3(H, a.nchunks), 256, lds, stream>>>(d, a);
+  k_kv_attn<EXACT, MAXR, FMT><<<dim3(H, a.nchunks), 256, lds, stream>>>(d, a);
   return hipGetLastError();
+}
+
+template <bool EXACT, int MAXR>
+hipError_t attn_launch(const KvDev& d, const AttnArgs& a, int H, size_t lds, hipStream_t stream) {
+  return d.fmt == CASS_FMT_C1_UNARY ? attn_launch_f<EXACT, MAXR, CASS_FMT_C1_UNARY>(d, a, H, lds, stream)
+                                    : attn_launch_f<EXACT, MAXR, CASS_FMT_C2_MX32>(d, a, H, lds, stream);
 }
 
 int run_attention(const cass_kv* kv, const uint16_t* q, int nq, int n_q_heads, float scale,
@@ -744,8 +866,13 @@ int cass_kv_decode(const cass_kv* kv, int exact, uint16_t* out, hipStream_t stre
   const int64_t n = (int64_t)2 * kv->p.n_kv_heads * kv->tokens;
   unsigned g = grid_of(n, 256);
   if (g > 65535u * 4) g = 65535u * 4;
-  if (exact) k_kv_decode<true><<<g, 256, 0, stream>>>(d, kv->tokens, out);
-  else k_kv_decode<false><<<g, 256, 0, stream>>>(d, kv->tokens, out);
+  if (d.fmt == CASS_FMT_C1_UNARY) {
+    if (exact) k_kv_decode<true, CASS_FMT_C1_UNARY><<<g, 256, 0, stream>>>(d, kv->tokens, out);
+    else k_kv_decode<false, CASS_FMT_C1_UNARY><<<g, 256, 0, stream>>>(d, kv->tokens, out);
+  } else {
+    if (exact) k_kv_decode<true, CASS_FMT_C2_MX32><<<g, 256, 0, stream>>>(d, kv->tokens, out);
+    else k_kv_decode<false, CASS_FMT_C2_MX32><<<g, 256, 0, stream>>>(d, kv->tokens, out);
+  }
   hipError_t e = hipGetLastError();
   return e == hipSuccess ? CASS_OK : report(CASS_ERR_HIP, "kv decode: %s", hipGetErrorString(e));
 }

@@ -192,6 +192,16 @@ int cass_tensor_validate(const void* spec, int64_t spec_bytes, const void* verif
  *   verification region: rank table | low mantissas (7-m bits, same order) |
  *     pruned bytes (token t, pruned i at byte t*(head_dim-keep)+i) | code
  *     offsets | codes (vcode_cap_bits)
+ * With format CASS_FMT_C2_MX32 (OCP MX: one shared exponent per 32
+ * positions, here the largest max(e,1) over the kept values, 0 if none):
+ *   speculation region: 256 unused bytes | keep bitmap | shared exponents
+ *     (u8 per 32 positions, token t group g at byte t*head_dim/32+g) | fields
+ *     ((s<<(m+1))|a, m+2 bits, a = the significand aligned to the shared
+ *     exponent and cut to m+1 bits) | (empty)
+ *   verification region: rank table of pruned exponents | kept residues
+ *     (unary(d) then the min(8, 7-m+d) bits the draft dropped, d = shared -
+ *     own exponent; code_cap_bits) | pruned bytes | offsets (u32 pair per
+ *     token: first residue bit, first pruned-code bit) | pruned codes
  * Each part starts on a multiple of 256 bytes and is followed by >= 16 zero
  * bytes.  The rank tables are built on the device from the first append's
  * tokens and frozen afterwards.  `state` (device, CASS_KV_STATE_BYTES) holds
@@ -207,6 +217,7 @@ typedef struct cass_kv_params {
   int64_t max_tokens;
   int64_t code_cap_bits;   /* speculation code capacity per stream, < 2^32 */
   int64_t vcode_cap_bits;  /* verification code capacity per stream, < 2^32 */
+  int32_t format;          /* CASS_FMT_C1_UNARY (0 means this) or CASS_FMT_C2_MX32 */
 } cass_kv_params;
 
 typedef struct cass_kv {

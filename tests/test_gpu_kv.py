@@ -1,7 +1,8 @@
 """GPU parity of the compressed KV cache against the CPU oracle, through the
-C ABI: stream regions byte for byte (one append, and token-at-a-time appends
-after a first chunk), decode bit for bit, draft and verification attention
-within tolerance of the fp64 oracle.
+C ABI, for Cassandra-1 (unary exponent codes) and Cassandra-2 (shared MX
+exponent per 32 positions): stream regions byte for byte (one append, and
+token-at-a-time appends after a first chunk), decode bit for bit, draft and
+verification attention within tolerance of the fp64 oracle.
 
 Attention tolerance (the pages fix none): |o - o_ref| <= 2e-3 * sum_t p_t |V_t|
 + 1e-6 per element, with p the oracle's softmax weights; the sum is obtained as
@@ -35,7 +36,10 @@ def make_kv(T, H, seed):
     return synth.kv_tensor(T, H, D, seed), synth.kv_tensor(T, H, D, seed + 1)
 
 
-def check_regions(torch, cache, orc, Kt, Vt, T0, k, m):
+FMTS = [1, 2]
+
+
+def check_regions(torch, cache, orc, Kt, Vt, T0, k, m, fmt=1):
     """Every stream region equals the oracle's encoding of that stream."""
     H = Kt.shape[1]
     p = cache.params
@@ -46,22 +50,23 @@ def check_regions(torch, cache, orc, Kt, Vt, T0, k, m):
         for kind, X in ((0, Kt), (1, Vt)):
             s = 2 * h + kind
             so, vo, tails = orc.kv_encode(X[:, h, :], T0, k, m, p.max_tokens, p.code_cap_bits,
-                                          p.vcode_cap_bits)
+                                          p.vcode_cap_bits, fmt=fmt)
             assert np.array_equal(spec[s * ss:(s + 1) * ss], so), f"spec stream {s}"
             assert np.array_equal(verif[s * vs:(s + 1) * vs], vo), f"verif stream {s}"
 
 
+@pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("T,H,k,m", [(300, 8, 38, 3), (1, 2, 38, 3), (77, 3, 0, 2),
                                      (64, 2, 128, 7), (130, 4, 64, 0)])
-def test_kv_append_one_call(gpu, orc, T, H, k, m):
+def test_kv_append_one_call(gpu, orc, T, H, k, m, fmt):
     torch, cass = gpu
-    print("case", T, H, k, m, flush=True)
+    print("case", T, H, k, m, fmt, flush=True)
     Kt, Vt = make_kv(T, H, 100 + T + k)
-    cache = cass.KvCache(H, D, k, m, max_tokens=T + 16)
+    cache = cass.KvCache(H, D, k, m, max_tokens=T + 16, fmt=fmt)
     cache.append(dev(torch, Kt), dev(torch, Vt))
     torch.cuda.synchronize()
     assert cass.cass_kv_status(cache.kv) == (T, cass.CASS_KV_FLAG_TABLES)
-    check_regions(torch, cache, orc, Kt, Vt, T, k, m)
+    check_regions(torch, cache, orc, Kt, Vt, T, k, m, fmt)
     out = torch.empty((2, H, T, D), dtype=torch.int16, device="cuda")
     cass.cass_kv_decode(cache.kv, True, out)
     torch.cuda.synchronize()
@@ -69,32 +74,36 @@ def test_kv_append_one_call(gpu, orc, T, H, k, m):
     assert np.array_equal(o[0], Kt.transpose(1, 0, 2)) and np.array_equal(o[1], Vt.transpose(1, 0, 2))
 
 
-def test_kv_token_at_a_time_equals_one_call(gpu, orc):
+@pytest.mark.parametrize("fmt", FMTS)
+def test_kv_token_at_a_time_equals_one_call(gpu, orc, fmt):
     """A first chunk of T0 tokens then single-token appends gives the bytes of
     one encoding with the tables of the first chunk."""
     torch, cass = gpu
     T, T0, H, k, m = 96, 40, 8, 38, 3
     Kt, Vt = make_kv(T, H, 7)
-    cache = cass.KvCache(H, D, k, m, max_tokens=128)
+    cache = cass.KvCache(H, D, k, m, max_tokens=128, fmt=fmt)
     cache.append(dev(torch, Kt[:T0]), dev(torch, Vt[:T0]))
     for t in range(T0, T):
         cache.append(dev(torch, Kt[t:t + 1]), dev(torch, Vt[t:t + 1]))
     torch.cuda.synchronize()
     assert cache.tokens == T
-    check_regions(torch, cache, orc, Kt, Vt, T0, k, m)
+    check_regions(torch, cache, orc, Kt, Vt, T0, k, m, fmt)
     out = torch.empty((2, H, T, D), dtype=torch.int16, device="cuda")
     cass.cass_kv_decode(cache.kv, False, out)
     torch.cuda.synchronize()
     p = cache.params
-    so, _, _ = orc.kv_encode(Kt[:, 3, :], T0, k, m, p.max_tokens, p.code_cap_bits, p.vcode_cap_bits)
-    draft_ref = orc.kv_decode(so, T, D, k, m, p.max_tokens, p.code_cap_bits, p.vcode_cap_bits)
+    so, _, _ = orc.kv_encode(Kt[:, 3, :], T0, k, m, p.max_tokens, p.code_cap_bits, p.vcode_cap_bits,
+                             fmt=fmt)
+    draft_ref = orc.kv_decode(so, T, D, k, m, p.max_tokens, p.code_cap_bits, p.vcode_cap_bits,
+                              fmt=fmt)
     assert np.array_equal(out.cpu().numpy().view(np.uint16)[0, 3], draft_ref)
 
 
-def test_kv_overflow_flag(gpu):
+@pytest.mark.parametrize("fmt", FMTS)
+def test_kv_overflow_flag(gpu, fmt):
     torch, cass = gpu
     Kt, Vt = make_kv(32, 2, 9)
-    cache = cass.KvCache(2, D, 38, 3, max_tokens=64, code_cap_bits=100, vcode_cap_bits=100)
+    cache = cass.KvCache(2, D, 38, 3, max_tokens=64, code_cap_bits=100, vcode_cap_bits=100, fmt=fmt)
     cache.append(dev(torch, Kt), dev(torch, Vt))
     torch.cuda.synchronize()
     t, flags = cass.cass_kv_status(cache.kv)
@@ -114,13 +123,14 @@ def oracle_attention(orc, q_rows, Kh, Vh, scale, visible=None):
     return out, bound
 
 
+@pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("T", [1, 200, 700])
-def test_draft_and_verify_attention(gpu, orc, T):
+def test_draft_and_verify_attention(gpu, orc, T, fmt):
     torch, cass = gpu
     H, Hq, k, m, nq = 8, 32, 38, 3, 5
     G = Hq // H
     Kt, Vt = make_kv(T + nq, H, 50 + T)
-    cache = cass.KvCache(H, D, k, m, max_tokens=T + nq + 8)
+    cache = cass.KvCache(H, D, k, m, max_tokens=T + nq + 8, fmt=fmt)
     cache.append(dev(torch, Kt[:T]), dev(torch, Vt[:T]))
     scale = 1.0 / np.sqrt(D)
     q1 = synth.activations(Hq, D, 4, t0=T)
@@ -131,10 +141,11 @@ def test_draft_and_verify_attention(gpu, orc, T):
     p = cache.params
     got = out.cpu().numpy()
     for h in range(H):
-        sk, _, _ = orc.kv_encode(Kt[:T, h, :], T, k, m, p.max_tokens, p.code_cap_bits, p.vcode_cap_bits)
-        sv, _, _ = orc.kv_encode(Vt[:T, h, :], T, k, m, p.max_tokens, p.code_cap_bits, p.vcode_cap_bits)
-        Kd = orc.kv_decode(sk, T, D, k, m, p.max_tokens, p.code_cap_bits, p.vcode_cap_bits)
-        Vd = orc.kv_decode(sv, T, D, k, m, p.max_tokens, p.code_cap_bits, p.vcode_cap_bits)
+        caps = (p.max_tokens, p.code_cap_bits, p.vcode_cap_bits)
+        sk, _, _ = orc.kv_encode(Kt[:T, h, :], T, k, m, *caps, fmt=fmt)
+        sv, _, _ = orc.kv_encode(Vt[:T, h, :], T, k, m, *caps, fmt=fmt)
+        Kd = orc.kv_decode(sk, T, D, k, m, *caps, fmt=fmt)
+        Vd = orc.kv_decode(sv, T, D, k, m, *caps, fmt=fmt)
         ref, bound = oracle_attention(orc, q1[h * G:(h + 1) * G], Kd, Vd, scale)
         attn_check(got[h * G:(h + 1) * G], ref, bound)
     # verification: append the nq drafted tokens, then attend causally on exact KV
