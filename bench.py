@@ -14,7 +14,8 @@ around every launch), the other hot-path calls (encode, verification GEMM for
 5 tokens, reconstruction, draft decode), the keep x mantissa sweep, the
 32-layer stack (tokens/s-equivalent), the compressed KV cache at 32K / 64K
 context (append latency, draft and verification attention), the Qwen3-4B
-Cassandra-2 stack at batch 2, and the CPU oracle timed on a row sample.
+Cassandra-2 stack at batch 2 with its 128K-token Cassandra-2 KV cache, and the
+CPU oracle timed on a row sample.
 
 Modes for profiling: --mode gemv runs only the timed GEMV steps; --mode copy
 runs a plain 1 GiB device copy (to calibrate the HBM byte counters).
@@ -409,6 +410,40 @@ def run_extras(args, torch, cass, synth, timer, stream, layers, encs, layer0, en
         torch.cuda.empty_cache()
     out["kv_cache"] = kvres
     log("kv done")
+
+    # ---- Qwen3-4B-shaped KV at 128K tokens, Cassandra-2 (one layer timed)
+    T, H, Hq, keep, mant = 131072, 8, 32, 38, 3
+    Kt = synth.kv_tensor(T, H, 128, 1_000_000 * 5 + 7)
+    Vt = synth.kv_tensor(T, H, 128, 1_000_000 * 5 + 8)
+    cache = cass.KvCache(H, 128, keep, mant, max_tokens=T + 64, fmt=cass.CASS_FMT_C2_MX32)
+    cache.append(dev16(Kt[:T - 64]), dev16(Vt[:T - 64]))
+    torch.cuda.synchronize()
+    tokK = [dev16(Kt[t:t + 1]) for t in range(T - 64, T)]
+    tokV = [dev16(Vt[t:t + 1]) for t in range(T - 64, T)]
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for i in range(64):
+        cache.append(tokK[i], tokV[i])
+    b.record(stream)
+    torch.cuda.synchronize()
+    q1 = dev16(synth.activations(Hq, 128, 5, t0=T))
+    wsa = torch.empty(cass.cass_kv_attn_ws_bytes(cache.kv, 1, Hq), dtype=torch.uint8, device="cuda")
+    o1 = torch.empty((Hq, 128), dtype=torch.float32, device="cuda")
+    d_ms = timer.ms(lambda: cass.cass_kv_draft_attn(cache.kv, q1, 1 / np.sqrt(128), o1, wsa, stream), 3)
+    tokens, flags = cass.cass_kv_status(cache.kv)
+    # draft attention reads, per K|V stream and token: bitmap, shared exponents, fields
+    attn_bytes = 2 * H * T * (128 / 8 + 128 / 32 + keep * (2 + mant) / 8)
+    out["kv_cache_qwen3_4b_c2_128k"] = {
+        "append_1tok_us": round(a.elapsed_time(b) * 1e3 / 64, 2),
+        "draft_attn_us": round(d_ms * 1e3, 1), "draft_attn_spec_MB": round(attn_bytes / 1e6, 2),
+        "draft_attn_GB_s": round(attn_bytes / (d_ms * 1e-3) / 1e9, 1), "tokens": tokens,
+        "overflow": bool(flags & cass.CASS_KV_FLAG_OVERFLOW),
+        "spec_MB_per_layer": round(cache.spec.numel() / 1e6, 1),
+        "verif_MB_per_layer": round(cache.verif.numel() / 1e6, 1),
+        "bf16_MB_per_layer": round(2 * T * H * 128 * 2 / 1e6, 1)}
+    del cache, Kt, Vt
+    torch.cuda.empty_cache()
+    log("qwen kv done")
     return out
 
 
