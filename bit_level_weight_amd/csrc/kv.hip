@@ -409,6 +409,11 @@ struct KvVec {
       vcr.init(reinterpret_cast<const uint32_t*>(vr + kv.vo[4]), poff == 0xFFFFFFFFu ? 0u : poff);
     }
   }
+  // read the rank tables from (shared-memory) copies instead
+  __device__ __forceinline__ void use_tables(const uint8_t* ps, const uint8_t* pv) {
+    perm_s = ps;
+    perm_v = pv;
+  }
   __device__ __forceinline__ uint32_t kept(int w) {
     if (FMT == CASS_FMT_C1_UNARY) {
       const uint32_t f = fr.take(1 + m);
@@ -461,11 +466,12 @@ __global__ void __launch_bounds__(256) k_kv_decode(KvDev kv, int64_t T, uint16_t
   }
 }
 
-// ---- attention: one workgroup per (KV head, chunk of 256 tokens) ----
-constexpr int kChunk = 256;
+// ---- attention: one workgroup per (KV head, chunk of 128 tokens) ----
+constexpr int kChunk = 128;  // tokens per workgroup, one per thread
 constexpr int kDim = 128;
 constexpr int kVStride = kDim + 2;  // bf16 per LDS row of the value tile (bank spread)
 constexpr int kMaxRows = 32;
+constexpr int kMaxChunksMerge = 4096;  // tokens up to 4096 * kChunk = 512K per merge
 
 struct AttnArgs {
   const uint16_t* q;  // [nq][Hq][D]
@@ -476,86 +482,103 @@ struct AttnArgs {
   float* part;        // [H][nchunks][rows][2 + D]
 };
 
-// MAXR: a bound on the query rows (nq * G) the launch serves
+// MAXR: a bound on the query rows (nq * G) the launch serves.  Shared
+// memory: queries [MAXR][128] fp32, scores [MAXR][kChunk] fp32, value tile
+// [kChunk][130] bf16 (about 37 KB for one query of four heads).
 template <bool EXACT, int MAXR, int FMT>
-__global__ void __launch_bounds__(256) k_kv_attn(KvDev kv, AttnArgs a) {
+__global__ void __launch_bounds__(2 * kChunk) k_kv_attn(KvDev kv, AttnArgs a) {
+  // threads 0..kChunk-1: one token's key and its scores; threads kChunk..:
+  // the same token's value row into the tile (the two decodes run side by side)
   extern __shared__ __align__(16) uint8_t smem[];
-  float* qf = reinterpret_cast<float*>(smem);                // [rows][128]
-  float* sc = qf + kMaxRows * kDim;                          // [rows][256]
-  uint16_t* vt = reinterpret_cast<uint16_t*>(sc + kMaxRows * kChunk);  // [256][130]
-  __shared__ float red[kMaxRows][4];
+  float* qf = reinterpret_cast<float*>(smem);                // [MAXR][128]
+  float* sc = qf + MAXR * kDim;                              // [MAXR][kChunk]
+  uint16_t* vt = reinterpret_cast<uint16_t*>(sc + MAXR * kChunk);  // [kChunk][130]
+  __shared__ float red[MAXR][kChunk / 64];
+  __shared__ uint8_t tabs[4][256];  // rank tables: K spec, K verif, V spec, V verif
   const int h = blockIdx.x, c = blockIdx.y;
   const int rows = a.nq * a.G;
   const int tid = threadIdx.x;
+  for (int i = tid; i < 4 * 256; i += 2 * kChunk) {
+    const int s = 2 * h + (i >> 9), which = (i >> 8) & 1;
+    const uint8_t* src = which ? kv.verif + s * kv.vstride + kv.vo[0] : kv.spec + s * kv.sstride + kv.so[0];
+    tabs[i >> 8][i & 255] = src[i & 255];
+  }
   // query rows of this KV head: row r = qi * G + g  (query qi, head h*G + g)
-  for (int idx = tid; idx < MAXR * kDim; idx += 256) {  // rows past `rows` stay zero
+  for (int idx = tid; idx < MAXR * kDim; idx += 2 * kChunk) {  // rows past `rows` stay zero
     const int r = idx / kDim, d = idx % kDim;
     const int qi = r / a.G, g = r % a.G;
     qf[idx] = r < rows ? bf16_bits_to_float(a.q[((int64_t)qi * a.Hq + h * a.G + g) * kDim + d])
                        : 0.f;
   }
   __syncthreads();
-  const int64_t tok = (int64_t)c * kChunk + tid;
+  const int ti = tid & (kChunk - 1);
+  const int64_t tok = (int64_t)c * kChunk + ti;
   const bool live = tok < a.T;
-  float s[MAXR];
+  if (tid < kChunk) {
+    float s[MAXR];
 #pragma unroll
-  for (int r = 0; r < MAXR; ++r) s[r] = 0.f;
-  if (live) {  // scores: kept positions, then (exact) pruned positions
-    KvVec<EXACT, FMT> dec;
-    dec.init(kv, 2 * h, tok);
-    for (int w = 0; w < kDim / 32; ++w) {
-      const uint32_t word = dec.bm[w];
-      for (uint32_t km = word; km; km &= km - 1u) {
-        const float kvv = bf16_bits_to_float(dec.kept(w));
-        const int d = w * 32 + __builtin_ctz(km);
-#pragma unroll
-        for (int r = 0; r < MAXR; ++r) s[r] = __builtin_fmaf(kvv, qf[r * kDim + d], s[r]);
-      }
-      if (EXACT) {
-        for (uint32_t pm = ~word; pm; pm &= pm - 1u) {
-          const float kvv = bf16_bits_to_float(dec.pruned());
-          const int d = w * 32 + __builtin_ctz(pm);
+    for (int r = 0; r < MAXR; ++r) s[r] = 0.f;
+    if (live) {  // scores: kept positions, then (exact) pruned positions
+      KvVec<EXACT, FMT> dec;
+      dec.init(kv, 2 * h, tok);
+      dec.use_tables(tabs[0], tabs[1]);
+      for (int w = 0; w < kDim / 32; ++w) {
+        const uint32_t word = dec.bm[w];
+        for (uint32_t km = word; km; km &= km - 1u) {
+          const float kvv = bf16_bits_to_float(dec.kept(w));
+          const int d = w * 32 + __builtin_ctz(km);
 #pragma unroll
           for (int r = 0; r < MAXR; ++r) s[r] = __builtin_fmaf(kvv, qf[r * kDim + d], s[r]);
         }
+        if (EXACT) {
+          for (uint32_t pm = ~word; pm; pm &= pm - 1u) {
+            const float kvv = bf16_bits_to_float(dec.pruned());
+            const int d = w * 32 + __builtin_ctz(pm);
+#pragma unroll
+            for (int r = 0; r < MAXR; ++r) s[r] = __builtin_fmaf(kvv, qf[r * kDim + d], s[r]);
+          }
+        }
       }
     }
-  }
-  // causal visibility: query qi sees tokens < T - nq + qi + 1
+    // causal visibility: query qi sees tokens < T - nq + qi + 1
 #pragma unroll
-  for (int r = 0; r < MAXR; ++r) {
-    if (r < rows) {
-      const int qi = r / a.G;
-      const bool vis = live && tok < a.T - a.nq + qi + 1;
-      sc[r * kChunk + tid] = vis ? s[r] * a.scale : -INFINITY;
+    for (int r = 0; r < MAXR; ++r) {
+      if (r < rows) {
+        const int qi = r / a.G;
+        const bool vis = live && tok < a.T - a.nq + qi + 1;
+        sc[r * kChunk + ti] = vis ? s[r] * a.scale : -INFINITY;
+      }
     }
-  }
-  // value tile (zero for tokens past the end)
-  {
-    uint16_t* row = vt + tid * kVStride;
+  } else {
+    // value tile (zero for tokens past the end)
+    uint16_t* row = vt + ti * kVStride;
     if (live) {
       KvVec<EXACT, FMT> dec;
       dec.init(kv, 2 * h + 1, tok);
+      dec.use_tables(tabs[2], tabs[3]);
       dec.all(kDim, row);
     } else {
       for (int d = 0; d < kDim; ++d) row[d] = 0;
     }
   }
   __syncthreads();
-  // per row: max and sum of exp over the chunk
+  // per row: max over the chunk, then p = e^{s - max}
   const int lane = tid & 63, wv = tid >> 6;
-  for (int r = 0; r < rows; ++r) {
-    float mx = sc[r * kChunk + tid];
+  if (tid < kChunk) {
+    for (int r = 0; r < rows; ++r) {
+      float mx = sc[r * kChunk + ti];
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
-    if (lane == 0) red[r][wv] = mx;
+      for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+      if (lane == 0) red[r][wv] = mx;
+    }
   }
   __syncthreads();
-  for (int r = 0; r < rows; ++r) {
-    const float mx = fmaxf(fmaxf(red[r][0], red[r][1]), fmaxf(red[r][2], red[r][3]));
-    const float sv = sc[r * kChunk + tid];
-    const float p = (mx == -INFINITY || sv == -INFINITY) ? 0.f : __expf(sv - mx);
-    sc[r * kChunk + tid] = p;
+  if (tid < kChunk) {
+    for (int r = 0; r < rows; ++r) {
+      const float mx = fmaxf(red[r][0], red[r][1]);
+      const float sv = sc[r * kChunk + ti];
+      sc[r * kChunk + ti] = (mx == -INFINITY || sv == -INFINITY) ? 0.f : __expf(sv - mx);
+    }
   }
   __syncthreads();
   // o[r][d] = sum_t p[r][t] V[t][d]; thread = (d, half of the rows)
@@ -563,6 +586,7 @@ __global__ void __launch_bounds__(256) k_kv_attn(KvDev kv, AttnArgs a) {
   float* part = a.part + (((int64_t)h * a.nchunks + c) * rows) * (2 + kDim);
   for (int r = half; r < rows; r += 2) {
     float acc = 0.f, l = 0.f;
+#pragma unroll 8
     for (int t = 0; t < kChunk; ++t) {
       const float p = sc[r * kChunk + t];
       acc = __builtin_fmaf(p, bf16_bits_to_float(vt[t * kVStride + d]), acc);
@@ -571,8 +595,7 @@ __global__ void __launch_bounds__(256) k_kv_attn(KvDev kv, AttnArgs a) {
     float* pr = part + (int64_t)r * (2 + kDim);
     pr[2 + d] = acc;
     if (d == 0) {
-      const float mx = fmaxf(fmaxf(red[r][0], red[r][1]), fmaxf(red[r][2], red[r][3]));
-      pr[0] = mx;
+      pr[0] = fmaxf(red[r][0], red[r][1]);
       pr[1] = l;
     }
   }
@@ -580,22 +603,42 @@ __global__ void __launch_bounds__(256) k_kv_attn(KvDev kv, AttnArgs a) {
 
 // combine the chunk partials: o = sum_c e^{m_c - M} o_c / sum_c e^{m_c - M} l_c
 __global__ void __launch_bounds__(128) k_kv_merge(AttnArgs a, int H, float* out) {
+  __shared__ float wgt[kMaxChunksMerge];
+  __shared__ float red[2][4];
   const int rows = a.nq * a.G;
   const int hr = blockIdx.x;  // h * rows + r
   const int h = hr / rows, r = hr % rows;
-  const int d = threadIdx.x;
+  const int d = threadIdx.x, lane = d & 63, wv = d >> 6;
   const float* base = a.part + ((int64_t)h * a.nchunks * rows + r) * (2 + kDim);
   const int64_t cstride = (int64_t)rows * (2 + kDim);
+  // chunk maxima and their overall maximum (the loads of every chunk in flight at once)
   float M = -INFINITY;
-  for (int c = 0; c < a.nchunks; ++c) M = fmaxf(M, base[c * cstride]);
-  float num = 0.f, den = 0.f;
-  for (int c = 0; c < a.nchunks; ++c) {
+  for (int c = d; c < a.nchunks; c += 128) {
     const float mc = base[c * cstride];
-    if (mc == -INFINITY) continue;
-    const float wgt = __expf(mc - M);
-    num += wgt * base[c * cstride + 2 + d];
-    den += wgt * base[c * cstride + 1];
+    wgt[c] = mc;
+    M = fmaxf(M, mc);
   }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+  if (lane == 0) red[0][wv] = M;
+  __syncthreads();
+  M = fmaxf(red[0][0], red[0][1]);
+  // chunk weights e^{m_c - M} and the denominator sum_c w_c l_c (fixed order)
+  float den = 0.f;
+  for (int c = d; c < a.nchunks; c += 128) {
+    const float mc = wgt[c];
+    const float w = mc == -INFINITY ? 0.f : __expf(mc - M);
+    wgt[c] = w;
+    den += w * base[c * cstride + 1];
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) den += __shfl_xor(den, o, 64);
+  if (lane == 0) red[1][wv] = den;
+  __syncthreads();
+  den = red[1][0] + red[1][1];
+  float num = 0.f;
+#pragma unroll 8
+  for (int c = 0; c < a.nchunks; ++c) num += wgt[c] * base[c * cstride + 2 + d];
   const int qi = r / a.G, g = r % a.G;
   out[((int64_t)qi * a.Hq + h * a.G + g) * kDim + d] = num / den;
 }
@@ -707,11 +750,13 @@ unsigned grid_of(int64_t n, int per) {
 }
 
 template <bool EXACT, int MAXR, int FMT>
-hipError_t attn_launch_f(const KvDev& d, const AttnArgs& a, int H, size_t lds, hipStream_t stream) {
+hipError_t attn_launch_f(const KvDev& d, const AttnArgs& a, int H, size_t, hipStream_t stream) {
+  const size_t lds = (size_t)MAXR * kDim * 4 + (size_t)MAXR * kChunk * 4 +
+                     (size_t)kChunk * kVStride * 2;
   hipError_t e = hipFuncSetAttribute((const void*)&k_kv_attn<EXACT, MAXR, FMT>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  k_kv_attn<EXACT, MAXR, FMT><<<dim3(H, a.nchunks), 256, lds, stream>>>(d, a);
+  k_kv_attn<EXACT, MAXR, FMT><<<dim3(H, a.nchunks), 2 * kChunk, lds, stream>>>(d, a);
   return hipGetLastError();
 }
 
@@ -742,10 +787,10 @@ int run_attention(const cass_kv* kv, const uint16_t* q, int nq, int n_q_heads, f
   a.scale = scale;
   a.T = kv->tokens;
   a.nchunks = (int)((kv->tokens + kChunk - 1) / kChunk);
+  if (a.nchunks > kMaxChunksMerge) return report(CASS_ERR_UNSUPPORTED, "attention over more than 512K tokens");
   a.part = (float*)ws;
   const KvDev d = dev_of(kv);
-  const size_t lds = (size_t)kMaxRows * kDim * 4 + (size_t)kMaxRows * kChunk * 4 +
-                     (size_t)kChunk * kVStride * 2;
+  const size_t lds = 0;  // per launch, from the row bound (attn_launch_f)
   const int rows = nq * G;
   hipError_t e = exact ? (rows <= 4    ? attn_launch<true, 4>(d, a, H, lds, stream)
                           : rows <= 8  ? attn_launch<true, 8>(d, a, H, lds, stream)
