@@ -602,18 +602,21 @@ __global__ void __launch_bounds__(2 * kChunk) k_kv_attn(KvDev kv, AttnArgs a) {
 }
 
 // combine the chunk partials: o = sum_c e^{m_c - M} o_c / sum_c e^{m_c - M} l_c
-__global__ void __launch_bounds__(128) k_kv_merge(AttnArgs a, int H, float* out) {
+constexpr int kMergeParts = 4;  // chunk ranges summed side by side per output
+
+__global__ void __launch_bounds__(128 * kMergeParts) k_kv_merge(AttnArgs a, int H, float* out) {
   __shared__ float wgt[kMaxChunksMerge];
-  __shared__ float red[2][4];
+  __shared__ float red[2][8];
+  __shared__ float nums[kMergeParts][kDim];
   const int rows = a.nq * a.G;
   const int hr = blockIdx.x;  // h * rows + r
   const int h = hr / rows, r = hr % rows;
-  const int d = threadIdx.x, lane = d & 63, wv = d >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, nw = blockDim.x / 64;
   const float* base = a.part + ((int64_t)h * a.nchunks * rows + r) * (2 + kDim);
   const int64_t cstride = (int64_t)rows * (2 + kDim);
   // chunk maxima and their overall maximum (the loads of every chunk in flight at once)
   float M = -INFINITY;
-  for (int c = d; c < a.nchunks; c += 128) {
+  for (int c = tid; c < a.nchunks; c += blockDim.x) {
     const float mc = base[c * cstride];
     wgt[c] = mc;
     M = fmaxf(M, mc);
@@ -622,10 +625,11 @@ __global__ void __launch_bounds__(128) k_kv_merge(AttnArgs a, int H, float* out)
   for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
   if (lane == 0) red[0][wv] = M;
   __syncthreads();
-  M = fmaxf(red[0][0], red[0][1]);
+  M = red[0][0];
+  for (int i = 1; i < nw; ++i) M = fmaxf(M, red[0][i]);
   // chunk weights e^{m_c - M} and the denominator sum_c w_c l_c (fixed order)
   float den = 0.f;
-  for (int c = d; c < a.nchunks; c += 128) {
+  for (int c = tid; c < a.nchunks; c += blockDim.x) {
     const float mc = wgt[c];
     const float w = mc == -INFINITY ? 0.f : __expf(mc - M);
     wgt[c] = w;
@@ -635,12 +639,21 @@ __global__ void __launch_bounds__(128) k_kv_merge(AttnArgs a, int H, float* out)
   for (int o = 32; o >= 1; o >>= 1) den += __shfl_xor(den, o, 64);
   if (lane == 0) red[1][wv] = den;
   __syncthreads();
-  den = red[1][0] + red[1][1];
+  den = 0.f;
+  for (int i = 0; i < nw; ++i) den += red[1][i];
+  // numerator: thread (d, part) sums chunks part, part + kMergeParts, ...
+  const int d = tid & (kDim - 1), q = tid >> 7;
   float num = 0.f;
 #pragma unroll 8
-  for (int c = 0; c < a.nchunks; ++c) num += wgt[c] * base[c * cstride + 2 + d];
-  const int qi = r / a.G, g = r % a.G;
-  out[((int64_t)qi * a.Hq + h * a.G + g) * kDim + d] = num / den;
+  for (int c = q; c < a.nchunks; c += kMergeParts) num += wgt[c] * base[c * cstride + 2 + d];
+  nums[q][d] = num;
+  __syncthreads();
+  if (q == 0) {
+    float tot = 0.f;
+    for (int i = 0; i < kMergeParts; ++i) tot += nums[i][d];
+    const int qi = r / a.G, g = r % a.G;
+    out[((int64_t)qi * a.Hq + h * a.G + g) * kDim + d] = tot / den;
+  }
 }
 
 int64_t aln256(int64_t v) { return (v + 255) / 256 * 256; }
@@ -792,16 +805,19 @@ int run_attention(const cass_kv* kv, const uint16_t* q, int nq, int n_q_heads, f
   const KvDev d = dev_of(kv);
   const size_t lds = 0;  // per launch, from the row bound (attn_launch_f)
   const int rows = nq * G;
+  // row bounds: one query of 4 heads (draft), 5 queries of 4 heads (verify), ...
   hipError_t e = exact ? (rows <= 4    ? attn_launch<true, 4>(d, a, H, lds, stream)
                           : rows <= 8  ? attn_launch<true, 8>(d, a, H, lds, stream)
                           : rows <= 16 ? attn_launch<true, 16>(d, a, H, lds, stream)
+                          : rows <= 20 ? attn_launch<true, 20>(d, a, H, lds, stream)
                                        : attn_launch<true, 32>(d, a, H, lds, stream))
                        : (rows <= 4    ? attn_launch<false, 4>(d, a, H, lds, stream)
                           : rows <= 8  ? attn_launch<false, 8>(d, a, H, lds, stream)
                           : rows <= 16 ? attn_launch<false, 16>(d, a, H, lds, stream)
+                          : rows <= 20 ? attn_launch<false, 20>(d, a, H, lds, stream)
                                        : attn_launch<false, 32>(d, a, H, lds, stream));
   if (e != hipSuccess) return report(CASS_ERR_HIP, "attention: %s", hipGetErrorString(e));
-  k_kv_merge<<<H * nq * G, kDim, 0, stream>>>(a, H, out);
+  k_kv_merge<<<H * nq * G, kDim * kMergeParts, 0, stream>>>(a, H, out);
   if ((e = hipGetLastError()) != hipSuccess) return report(CASS_ERR_HIP, "merge: %s", hipGetErrorString(e));
   return CASS_OK;
 }
