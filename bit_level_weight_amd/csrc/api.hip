@@ -153,7 +153,8 @@ SpecViewC1 spec_c1(const cass_tensor* W) {
                     (const uint32_t*)(b + o[S1_BLKOFF]), (const uint16_t*)(b + o[S1_KEPTB]),
                     (const uint32_t*)(b + o[S1_FIELDS]), (const uint32_t*)(b + o[S1_CODES]),
                     word_limit(W->spec_bytes, o[S1_BITMAP]), word_limit(W->spec_bytes, o[S1_FIELDS]),
-                    word_limit(W->spec_bytes, o[S1_CODES])};
+                    word_limit(W->spec_bytes, o[S1_CODES]), word_limit(W->spec_bytes, o[S1_BLKOFF]),
+                    2 * word_limit(W->spec_bytes, o[S1_KEPTB])};
 }
 VerifViewC1 verif_c1(const cass_tensor* W) {
   const uint8_t* b = (const uint8_t*)W->verif;

@@ -52,6 +52,7 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 struct BalGeom {
   int P, logP, rpw;     // parts per row, log2(P), rows per wave round (64 / P)
   int nb_top;           // largest power of two <= blocks per row
+  float nb_per_k;       // blocks per row / kept per row (block estimate of a value)
   int64_t nrounds;      // wave rounds: ceil(rows / rpw)
   int lut_off;          // LDS byte offsets (x at 0)
   int wave_off, wave_bytes;
@@ -67,43 +68,24 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// A run of 16-byte chunks to copy from global memory to LDS.
-struct Chunks {
-  const u32x4* src;
-  u32x4* dst;
-  int n;
-};
+typedef __attribute__((address_space(3))) void lds_void;
 
-// Chunk range of words [w0, w1) of a section (16-byte aligned base): starts
-// at w0 rounded down to 4 words (returned in a0) and never reaches word
-// `limit` (a multiple of 4).
-__device__ __forceinline__ Chunks chunk_range(const uint32_t* src, uint32_t* dst, int64_t w0,
-                                              int64_t w1, int64_t limit, int64_t& a0) {
-  a0 = w0 & ~(int64_t)3;
-  int64_t a1 = (w1 + 3) & ~(int64_t)3;
-  if (a1 > limit) a1 = limit;
-  return Chunks{reinterpret_cast<const u32x4*>(src + a0), reinterpret_cast<u32x4*>(dst),
-                (int)((a1 - a0) >> 2)};
+// Issues the copy of n 16-byte chunks from global memory to LDS by LDS DMA:
+// one instruction per 64 chunks, lane i's chunk landing at dst + 16 i (the
+// LDS address is the wave's, so dst must be uniform).  Nontemporal: each
+// byte is read once.  Completion is awaited by wait_dma.
+__device__ __forceinline__ void dma_run(const u32x4* src, u32x4* dst, int n, int lane) {
+  for (int base = 0; base < n; base += 64)
+    if (base + lane < n)
+      __builtin_amdgcn_global_load_lds((const void*)(src + base + lane), (lds_void*)(dst + base),
+                                       16, 0, 2 /* nt */);
 }
 
-constexpr int kBatch = 4;  // 16-byte chunks per thread in flight
-
-// Copies one chunk run with `nthr` threads, kBatch loads in flight per thread
-// (plain loads: used for x, which every workgroup reads).
-__device__ __forceinline__ void copy_run(Chunks a, int t, int nthr) {
-  for (int base = 0; base < a.n; base += nthr * kBatch) {
-    u32x4 r[kBatch];
-#pragma unroll
-    for (int j = 0; j < kBatch; ++j) {
-      const int i = base + nthr * j + t;
-      if (i < a.n) r[j] = a.src[i];
-    }
-#pragma unroll
-    for (int j = 0; j < kBatch; ++j) {
-      const int i = base + nthr * j + t;
-      if (i < a.n) a.dst[i] = r[j];
-    }
-  }
+// Waits for every global load and LDS DMA of the wave (vmcnt 0), then makes
+// the LDS contents visible to all its lanes.
+__device__ __forceinline__ void wait_dma() {
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  wave_sync();
 }
 
 typedef __attribute__((address_space(3))) const uint16_t lds_u16;
@@ -153,15 +135,49 @@ __device__ __forceinline__ void c1_step(const uint32_t* bm_l, uint32_t& bp, cons
     acc[bb] = __builtin_fmaf(wv, x_at(xs, xa + bb * xstride), acc[bb]);
 }
 
-// U values from the windows at (bp, fp, cp): lo0/hi0 the 64 keep bits at bp,
-// wf the 32 field bits at fp, wc0 the 32 code bits at cp, each holding at
-// least U values.  With MASKED, slots u >= t add nothing (the part's last
-// group); otherwise the positions advance past the U values.
+// The raw LDS words behind a group's three windows: three bitmap words at
+// bp, two field words at fp, two code words at cp.  They are read one group
+// ahead, together with the current group's table and x reads, so a group
+// waits for LDS once.
+struct Raw {
+  uint32_t q0, q1, q2, f0, f1, c0, c1;
+};
+
+__device__ __forceinline__ Raw load_raw(const uint32_t* bm_l, const uint32_t* f_l,
+                                        const uint32_t* c_l, uint32_t bp, uint32_t fp,
+                                        uint32_t cp) {
+  const uint32_t* qb = bm_l + (bp >> 5);
+  const uint32_t* qf = f_l + (fp >> 5);
+  const uint32_t* qc = c_l + (cp >> 5);
+  return Raw{qb[0], qb[1], qb[2], qf[0], qf[1], qc[0], qc[1]};
+}
+
+typedef __attribute__((address_space(3))) const float lds_f32;
+
+// U values from the windows in `w` (read at bp, fp, cp), each window holding
+// at least U values: 64 keep bits, 32 field bits, 32 code bits.  Three phases:
+// positions, ranks and fields for all U values (VALU only); every table and x
+// read of the group plus the next group's window words (LDS only); the U
+// products.  With MASKED, slots u >= t add nothing (the part's last group)
+// and no next windows are read; otherwise the positions advance past the U
+// values and `w` receives the next group's words.
+//   lutb  LDS byte address of the (rank, field) -> fp32 table
+//   xorg  LDS byte address of x for staged bitmap bit 0
 template <int BATCH, int U, bool MASKED>
-__device__ __forceinline__ void c1_group(uint32_t lo0, uint32_t hi0, uint32_t wf, uint32_t wc0,
-                                         uint32_t& bp, uint32_t& fp, uint32_t& cp,
-                                         uint32_t xorg, const float* lut, int fw,
-                                         uint32_t xstride, int t, float* acc) {
+__device__ __forceinline__ void c1_group(Raw& w, uint32_t& bp, uint32_t& fp, uint32_t& cp,
+                                         const uint32_t* bm_l, const uint32_t* f_l,
+                                         const uint32_t* c_l, uint32_t xorg, uint32_t lutb,
+                                         int fw, uint32_t xstride, int t, float* acc) {
+  const uint32_t sb = bp & 31u;
+  const uint32_t lo0 = __builtin_amdgcn_alignbit(w.q1, w.q0, sb);
+  // (MASKED: the windows may hold only t values; a set bit 63 keeps the
+  // positions of slots u >= t inside the window, and a set code bit 31 their
+  // ranks inside the table)
+  const uint32_t hi0 = __builtin_amdgcn_alignbit(w.q2, w.q1, sb) | (MASKED ? 0x80000000u : 0u);
+  const uint32_t wf = __builtin_amdgcn_alignbit(w.f1, w.f0, fp & 31u);
+  const uint32_t wc0 = __builtin_amdgcn_alignbit(w.c1, w.c0, cp & 31u);
+  // phase 1: addresses
+  uint32_t la[U], xa[U];
   uint32_t lo = lo0, wc = wc0, p = 0;
   const uint32_t xlo = xorg + 2u * bp, xhi = xlo + 64u;
   uint32_t xs = xlo;
@@ -173,15 +189,12 @@ __device__ __forceinline__ void c1_group(uint32_t lo0, uint32_t hi0, uint32_t wf
     xs = z ? xhi : xs;
     p = (uint32_t)__builtin_ctz(lo);
     lo &= lo - 1u;
-    const uint32_t r = (uint32_t)__builtin_ctz(wc);  // code = r zeros, then a one
+    // code = r zeros, then a one
+    const uint32_t r = (uint32_t)__builtin_ctz(MASKED ? wc | 0x80000000u : wc);
     wc = (wc >> r) >> 1;
     const uint32_t f = __builtin_amdgcn_ubfe(wf, (uint32_t)(u * fw), (uint32_t)fw);
-    float wv = lut[(r << fw) | f];
-    if (MASKED) wv = u < t ? wv : 0.f;
-    const uint32_t xa = xs + 2u * p;
-#pragma unroll
-    for (int bb = 0; bb < BATCH; ++bb)
-      acc[bb] = __builtin_fmaf(wv, x_at_addr(xa + bb * xstride), acc[bb]);
+    la[u] = lutb + 4u * ((r << fw) | f);
+    xa[u] = xs + 2u * p;
   }
   if (!MASKED) {
     bp += ((xs - xlo) >> 1) + p + 1u;
@@ -189,6 +202,26 @@ __device__ __forceinline__ void c1_group(uint32_t lo0, uint32_t hi0, uint32_t wf
     // bits the U codes took: the window was shifted right by that many
     const uint32_t c0 = (uint32_t)__builtin_clz(wc0);
     cp += (wc ? (uint32_t)__builtin_clz(wc) : 32u) - c0;
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  // phase 2: every LDS read of the group
+  float wv[U], xv[BATCH][U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    wv[u] = *(lds_f32*)(uintptr_t)la[u];
+#pragma unroll
+    for (int bb = 0; bb < BATCH; ++bb) xv[bb][u] = x_at_addr(xa[u] + bb * xstride);
+  }
+  if (!MASKED) w = load_raw(bm_l, f_l, c_l, bp, fp, cp);
+  __builtin_amdgcn_sched_barrier(0);
+  // phase 3: products
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+#pragma unroll
+    for (int bb = 0; bb < BATCH; ++bb) {
+      const float a = __builtin_fmaf(wv[u], xv[bb][u], acc[bb]);
+      acc[bb] = (MASKED && u >= t) ? acc[bb] : a;
+    }
   }
 }
 
@@ -251,92 +284,68 @@ __global__ void __launch_bounds__(kBalThreads) k_gemv_c1_bal(SpecViewC1 v, Shape
   const int64_t nwaves = (int64_t)gridDim.x * kBalWaves;
   const int nlut = kRanks << fw;
 
-  // ---- one round's copy: its plan (row range, section ranges), the small
-  // per-lane loads issued before the previous round decodes, and the commit
-  // to LDS (every chunk load of the round in flight at once)
+  // ---- one round's staging.  Every section of the round is copied to the
+  // wave's LDS region by LDS DMA (64 chunks of 16 bytes per instruction), all
+  // in flight at once; only the codes wait for the row bases.
   struct Plan {
     int64_t row0;
-    int rows_here, nmeta;
-    Chunks bm, f, c;
-    int64_t bm_a0, f_a0, c_a0;
+    int rows_here;
+    int kb_sh, bo_sh;             // entries before the round's first one in the staged kb / bo
+    int64_t bm_a0, f_a0, c_a0;    // first staged word of bitmap, fields and codes
     bool c_in_lds;
   };
-  struct Pref {
-    uint32_t kbv[2], bov[2];
-    int64_t rowcb;
-  };
-  auto plan = [&](int64_t round, int64_t cb0, int64_t cb1) {
+  auto plan = [&](int64_t round) {
     Plan pl;
     pl.row0 = round * g.rpw;
     pl.rows_here = (int)((R - pl.row0 < g.rpw) ? R - pl.row0 : g.rpw);
-    pl.nmeta = pl.rows_here * nb;
-    const int64_t fb0 = pl.row0 * k * fw, fb1 = (pl.row0 + pl.rows_here) * k * fw;
-    pl.bm = chunk_range(v.bitmap, bm_l, pl.row0 * wpr, (pl.row0 + pl.rows_here) * wpr,
-                        v.bitmap_limit, pl.bm_a0);
-    pl.f = chunk_range(v.fields, f_l, fb0 >> 5, (fb1 + 31) >> 5, v.fields_limit, pl.f_a0);
-    pl.c = chunk_range(v.codes, c_l, cb0 >> 5, (cb1 + 31) >> 5, v.codes_limit, pl.c_a0);
-    pl.c_in_lds = pl.c.n * 4 <= g.c_cap;
-    if (!pl.c_in_lds) pl.c.n = 0;
+    pl.kb_sh = (int)((pl.row0 * nb) & 7);
+    pl.bo_sh = (int)((pl.row0 * nb) & 3);
+    pl.bm_a0 = (pl.row0 * wpr) & ~(int64_t)3;
+    pl.f_a0 = ((pl.row0 * k * fw) >> 5) & ~(int64_t)3;
+    pl.c_a0 = 0;
+    pl.c_in_lds = false;
     return pl;
   };
-  auto code_bounds = [&](int64_t round, int64_t& cb0, int64_t& cb1) {
+  // block metadata, bitmap words and fields (no dependence on loaded data)
+  auto stage_fixed = [&](const Plan& pl) {
+    const int64_t e0 = pl.row0 * nb, e1 = e0 + (int64_t)pl.rows_here * nb;
+    const int64_t kb1 = std::min<int64_t>((e1 + 7) & ~(int64_t)7, v.keptb_limit);
+    dma_run(reinterpret_cast<const u32x4*>(v.keptb + (e0 - pl.kb_sh)),
+            reinterpret_cast<u32x4*>(kb_l), (int)((kb1 - (e0 - pl.kb_sh)) >> 3), lane);
+    const int64_t bo1 = std::min<int64_t>((e1 + 3) & ~(int64_t)3, v.blkoff_limit);
+    dma_run(reinterpret_cast<const u32x4*>(v.blkoff + (e0 - pl.bo_sh)),
+            reinterpret_cast<u32x4*>(bo_l), (int)((bo1 - (e0 - pl.bo_sh)) >> 2), lane);
+    const int64_t bm1 = std::min<int64_t>(((pl.row0 + pl.rows_here) * wpr + 3) & ~(int64_t)3,
+                                          v.bitmap_limit);
+    dma_run(reinterpret_cast<const u32x4*>(v.bitmap + pl.bm_a0), reinterpret_cast<u32x4*>(bm_l),
+            (int)((bm1 - pl.bm_a0) >> 2), lane);
+    const int64_t fb1 = (pl.row0 + pl.rows_here) * k * fw;
+    const int64_t f1 = std::min<int64_t>((((fb1 + 31) >> 5) + 3) & ~(int64_t)3, v.fields_limit);
+    dma_run(reinterpret_cast<const u32x4*>(v.fields + pl.f_a0), reinterpret_cast<u32x4*>(f_l),
+            (int)((f1 - pl.f_a0) >> 2), lane);
+  };
+  // the codes of the round's rows, bits [cb0, cb1)
+  auto stage_codes = [&](Plan& pl, int64_t cb0, int64_t cb1) {
+    pl.c_a0 = (cb0 >> 5) & ~(int64_t)3;
+    const int64_t c1 = std::min<int64_t>((((cb1 + 31) >> 5) + 3) & ~(int64_t)3, v.codes_limit);
+    const int n = (int)((c1 - pl.c_a0) >> 2);
+    pl.c_in_lds = n * 4 <= g.c_cap;
+    if (pl.c_in_lds)
+      dma_run(reinterpret_cast<const u32x4*>(v.codes + pl.c_a0), reinterpret_cast<u32x4*>(c_l), n,
+              lane);
+  };
+  auto load_bounds = [&](int64_t round, int64_t& cb0, int64_t& cb1, int64_t& rowcb) {
     const int64_t r0 = round * g.rpw, r1 = r0 + g.rpw;
     cb0 = (int64_t)v.rowbase[r0];
     cb1 = r1 < R ? (int64_t)v.rowbase[r1] : v.codes_limit * 32;
-  };
-  // chunk i of the round's three runs (bitmap, fields, codes)
-  auto chunk_src = [&](const Plan& pl, int i) {
-    const int nab = pl.bm.n + pl.f.n;
-    return i < pl.bm.n ? pl.bm.src + i : (i < nab ? pl.f.src + (i - pl.bm.n) : pl.c.src + (i - nab));
-  };
-  auto chunk_dst = [&](const Plan& pl, int i) {
-    const int nab = pl.bm.n + pl.f.n;
-    return i < pl.bm.n ? pl.bm.dst + i : (i < nab ? pl.f.dst + (i - pl.bm.n) : pl.c.dst + (i - nab));
-  };
-  auto issue = [&](const Plan& pl) {
-    Pref pf;
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int i = lane + 64 * j;
-      if (i < pl.nmeta) {
-        pf.kbv[j] = v.keptb[pl.row0 * nb + i];
-        pf.bov[j] = v.blkoff[pl.row0 * nb + i];
-      }
-    }
-    pf.rowcb = rl < pl.rows_here ? (int64_t)v.rowbase[pl.row0 + rl] : 0;
-    return pf;
-  };
-  auto commit = [&](const Plan& pl, const Pref& pf) {
-    const int n = pl.bm.n + pl.f.n + pl.c.n;
-    for (int base = 0; base < n; base += 64 * kBatch) {
-      u32x4 r2[kBatch];
-#pragma unroll
-      for (int j = 0; j < kBatch; ++j) {
-        const int i = base + 64 * j + lane;
-        if (i < n) r2[j] = __builtin_nontemporal_load(chunk_src(pl, i));
-      }
-#pragma unroll
-      for (int j = 0; j < kBatch; ++j) {
-        const int i = base + 64 * j + lane;
-        if (i < n) *chunk_dst(pl, i) = r2[j];
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int i = lane + 64 * j;
-      if (i < pl.nmeta) {
-        kb_l[i] = (uint16_t)pf.kbv[j];
-        bo_l[i] = pf.bov[j];
-      }
-    }
-    for (int i = lane + 128; i < pl.nmeta; i += 64) {  // rounds with more than 128 blocks
-      kb_l[i] = v.keptb[pl.row0 * nb + i];
-      bo_l[i] = v.blkoff[pl.row0 * nb + i];
-    }
+    rowcb = r0 + rl < R ? (int64_t)v.rowbase[r0 + rl] : 0;
   };
 
-  // Where this lane's part of the round starts.
-  auto locate = [&](const Plan& pl, int64_t rowcb) {
+  // Where this lane's part of the round starts in the bitmap and fields (from
+  // the staged kept counts and bitmap words); `skip` and `blk` carry the code
+  // search to locate_codes.
+  int skip = 0, blk = 0;
+  auto locate_bits = [&](const Plan& pl) {
     Part pt;
     const int64_t row = pl.row0 + rl;
     const int i0 = (int)(((int64_t)part * k) >> g.logP);
@@ -346,19 +355,22 @@ __global__ void __launch_bounds__(kBalThreads) k_gemv_c1_bal(SpecViewC1 v, Shape
     pt.fp = 0;
     pt.cp = 0;
     pt.cabs = 0;
+    skip = 0;
+    blk = 0;
     if (pt.n > 0) {
       // block holding value i0: the kept counts per block are close to
       // k / nb, so start from that estimate and step (usually zero or one step)
-      const uint16_t* kbr = kb_l + rl * nb;
-      int b = (int)(((int64_t)i0 * nb) / k);
-      if (b >= nb) b = nb - 1;
+      const uint16_t* kbr = kb_l + pl.kb_sh + rl * nb;
+      int b = (int)((float)i0 * g.nb_per_k);
+      b = b < 0 ? 0 : (b >= nb ? nb - 1 : b);
       for (int it = 0; it < nb; ++it) {
         const int lo = kbr[b], hi = b + 1 < nb ? kbr[b + 1] : (int)k;
         if (lo > i0 && b > 0) --b;
         else if (hi <= i0 && b + 1 < nb) ++b;
         else break;
       }
-      const int skip = i0 - kbr[b];
+      skip = i0 - kbr[b];
+      blk = b;
       // word and bit inside the block: the block's words read at once
       const uint32_t* bw = bm_l + (pt.rowbit >> 5) + b * nwb;
       int rem = skip, wsel = nwb - 1;
@@ -390,13 +402,18 @@ __global__ void __launch_bounds__(kBalThreads) k_gemv_c1_bal(SpecViewC1 v, Shape
       }
       pt.bp = pt.rowbit + (uint32_t)(b * B + wsel * 32 + select_bit(wd, rem + 1));
       pt.fp = (uint32_t)((row * k + i0) * fw - pl.f_a0 * 32);
-      pt.cabs = rowcb + bo_l[rl * nb + b];
+    }
+    return pt;
+  };
+  // ... and in the codes: the block's code offset, then `skip` codes on
+  auto locate_codes = [&](const Plan& pl, Part& pt, int64_t rowcb) {
+    if (pt.n > 0) {
+      pt.cabs = rowcb + bo_l[pl.bo_sh + rl * nb + blk];
       if (pl.c_in_lds)
         pt.cp = skip_codes8(c_l, (uint32_t)(pt.cabs - pl.c_a0 * 32), skip);
       else
         pt.cp = skip_codes(v.codes + (pt.cabs >> 5), (uint32_t)(pt.cabs & 31), skip);
     }
-    return pt;
   };
 
   // ---- first round, x and the (rank, field) -> fp32 table
@@ -409,25 +426,30 @@ __global__ void __launch_bounds__(kBalThreads) k_gemv_c1_bal(SpecViewC1 v, Shape
   }
   const bool first = round < g.nrounds;
   Plan pl{};
-  Pref pf{};
+  int64_t cb0 = 0, cb1 = 0, rowcb = 0;
   if (first) {
-    int64_t cb0, cb1;
-    code_bounds(round, cb0, cb1);
-    pl = plan(round, cb0, cb1);
-    pf = issue(pl);
+    load_bounds(round, cb0, cb1, rowcb);
+    pl = plan(round);
+    stage_fixed(pl);
   }
+  const bool x_dma = (C & 7) == 0 && ((uintptr_t)x & 15) == 0 && (ldx & 7) == 0;
   for (int bb = 0; bb < BATCH; ++bb) {
     uint16_t* xr = reinterpret_cast<uint16_t*>(smem + bb * g.xstride);
     const uint16_t* xg = x + bb * ldx;
-    if ((C & 7) == 0 && ((uintptr_t)xg & 15) == 0)
-      copy_run(Chunks{reinterpret_cast<const u32x4*>(xg), reinterpret_cast<u32x4*>(xr),
-                      (int)(C >> 3)},
-               threadIdx.x, kBalThreads);
-    else
+    if (x_dma) {
+      // the workgroup's waves take interleaved runs of 64 chunks
+      const int nx = (int)(C >> 3);
+      for (int base = wave * 64; base < nx; base += kBalThreads)
+        dma_run(reinterpret_cast<const u32x4*>(xg) + base, reinterpret_cast<u32x4*>(xr) + base,
+                nx - base < 64 ? nx - base : 64, lane);
+    } else {
       for (int64_t j = threadIdx.x; j < C; j += kBalThreads) xr[j] = xg[j];
+    }
     // zeros after the row: masked slots of a part's last group may read there
     if (threadIdx.x < 128) xr[C + threadIdx.x] = 0;
   }
+  wait_dma();  // the row bases, this wave's sections and x chunks
+  if (first) stage_codes(pl, cb0, cb1);
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const int i = threadIdx.x + kBalThreads * j;
@@ -437,23 +459,19 @@ __global__ void __launch_bounds__(kBalThreads) k_gemv_c1_bal(SpecViewC1 v, Shape
                                ((f & ((1u << m) - 1u)) << (23 - m)));
     }
   }
-  if (first) commit(pl, pf);
-  __syncthreads();  // x, the table and every wave's first round are in LDS
+  Part pt{};
+  if (first) pt = locate_bits(pl);  // overlaps the codes' copy
+  wait_dma();
+  if (first) locate_codes(pl, pt, rowcb);
+  __syncthreads();  // x (every wave's chunks) and the table are in LDS
   if (!first) return;
 
   for (;;) {
-    const int64_t rowcb = pf.rowcb;
     const int64_t next = round + nwaves;
     const bool more = next < g.nrounds;
-    int64_t ncb0 = 0, ncb1 = 0;
-    if (more) code_bounds(next, ncb0, ncb1);
-    const Part pt = locate(pl, rowcb);
-    // the next round's small loads fly while this round decodes
-    Plan npl{};
-    if (more) {
-      npl = plan(next, ncb0, ncb1);
-      pf = issue(npl);
-    }
+    // the next round's row bases load while this round decodes
+    int64_t ncb0 = 0, ncb1 = 0, nrowcb = 0;
+    if (more) load_bounds(next, ncb0, ncb1, nrowcb);
 
     const bool active = rl < pl.rows_here;
     const int n = pt.n;
@@ -469,30 +487,44 @@ __global__ void __launch_bounds__(kBalThreads) k_gemv_c1_bal(SpecViewC1 v, Shape
     const bool grouped = pl.c_in_lds && pl.rows_here == g.rpw && n_min > 0;
     if (grouped) {
       const uint32_t xorg = lds_addr(smem) - 2u * rowbit;  // x address of staged bit 0
-      for (int gi = 0; gi <= G; ++gi) {
-        // gi == G: the part's last t = n - G*U <= U values, slots u >= t masked
-        const int t = gi < G ? U : n - G * U;
-        if (gi == G && n_tail == 0) break;
-        const uint32_t* qb = bm_l + (bp >> 5);
-        const uint32_t sb = bp & 31u;
-        const uint32_t q0 = qb[0], q1 = qb[1], q2 = qb[2];
-        const uint32_t lo0 = __builtin_amdgcn_alignbit(q1, q0, sb);
-        const uint32_t hi0 = __builtin_amdgcn_alignbit(q2, q1, sb);
-        const uint32_t wf = window32(f_l, fp);
-        const uint32_t wc0 = window32(c_l, cp);
-        const int have = __builtin_popcount(lo0) + __builtin_popcount(hi0);
-        const bool ok = min(have, __builtin_popcount(wc0)) >= U;
-        if (__all(ok)) {
-          if (gi < G)
-            c1_group<BATCH, U, false>(lo0, hi0, wf, wc0, bp, fp, cp, xorg, lut, fw, g.xstride,
-                                      U, acc);
-          else
-            c1_group<BATCH, U, true>(lo0, hi0, wf, wc0, bp, fp, cp, xorg, lut, fw, g.xstride,
-                                     t, acc);
-        } else {
-          for (int u = 0; u < t; ++u)
+      const uint32_t lutb = lds_addr(reinterpret_cast<const uint8_t*>(lut));
+      Raw w = load_raw(bm_l, f_l, c_l, bp, fp, cp);
+      // full groups: runs of fast groups; a group whose windows fall short
+      // for some lane goes value by value
+      int gi = 0;
+      while (gi < G) {
+        for (; gi < G; ++gi) {
+          const uint32_t sb = bp & 31u;
+          const int have = __builtin_popcount(__builtin_amdgcn_alignbit(w.q1, w.q0, sb)) +
+                           __builtin_popcount(__builtin_amdgcn_alignbit(w.q2, w.q1, sb));
+          const int ncode = __builtin_popcount(__builtin_amdgcn_alignbit(w.c1, w.c0, cp & 31u));
+          if (!__all(min(have, ncode) >= U)) break;
+          c1_group<BATCH, U, false>(w, bp, fp, cp, bm_l, f_l, c_l, xorg, lutb, fw, g.xstride, U,
+                                    acc);
+        }
+        if (gi < G) {
+          for (int u = 0; u < U; ++u)
             c1_step<BATCH>(bm_l, bp, f_l, fp, c_l, cp, rowbit, C, lut, v.perm, m, smem,
                            g.xstride, acc);
+          ++gi;
+          w = load_raw(bm_l, f_l, c_l, bp, fp, cp);
+        }
+      }
+      // the part's last t = n - G*U <= U values
+      if (n_tail > 0) {
+        const int t = n - G * U;
+        const uint32_t sb = bp & 31u;
+        const int have = __builtin_popcount(__builtin_amdgcn_alignbit(w.q1, w.q0, sb)) +
+                         __builtin_popcount(__builtin_amdgcn_alignbit(w.q2, w.q1, sb));
+        const int ncode = __builtin_popcount(__builtin_amdgcn_alignbit(w.c1, w.c0, cp & 31u));
+        if (__all(min(have, ncode) >= t)) {
+          c1_group<BATCH, U, true>(w, bp, fp, cp, bm_l, f_l, c_l, xorg, lutb, fw, g.xstride, t,
+                                   acc);
+        } else {
+          for (int u = 0; u < U; ++u)
+            if (u < t)
+              c1_step<BATCH>(bm_l, bp, f_l, fp, c_l, cp, rowbit, C, lut, v.perm, m, smem,
+                             g.xstride, acc);
         }
       }
     } else if (pl.c_in_lds) {
@@ -522,11 +554,14 @@ __global__ void __launch_bounds__(kBalThreads) k_gemv_c1_bal(SpecViewC1 v, Shape
 #pragma unroll
       for (int bb = 0; bb < BATCH; ++bb) y[bb * ldy + pl.row0 + rl] = acc[bb];
     }
-    wave_sync();  // every lane is done with the staged words before the next round
     if (!more) break;
-    commit(npl, pf);
-    wave_sync();
-    pl = npl;
+    wave_sync();  // every lane is done with the staged words before they are replaced
+    pl = plan(next);
+    stage_fixed(pl);
+    stage_codes(pl, ncb0, ncb1);
+    wait_dma();
+    pt = locate_bits(pl);
+    locate_codes(pl, pt, nrowcb);
     round = next;
   }
 }
@@ -562,16 +597,18 @@ BalGeom make_bal_geom(const Shape& sh, int batch, int64_t code_limit_words) {
   g.nb_top = 1;
   while (2 * g.nb_top < nb) g.nb_top *= 2;
   g.nrounds = (R + g.rpw - 1) / g.rpw;
+  g.nb_per_k = k > 0 ? (float)nb / (float)k : 0.f;
   g.xstride = (uint32_t)a16(2 * C + 256);
   int64_t pos = (int64_t)batch * g.xstride;
   g.lut_off = (int)pos;
   pos += a16((int64_t)(kRanks << fw) * 4);
   g.wave_off = (int)pos;
   int64_t w = 0;
+  // staged runs start up to one chunk early and end up to one chunk late
   g.kb_off = (int)w;
-  w += a16((int64_t)g.rpw * nb * 2);
+  w += a16((int64_t)g.rpw * nb * 2 + 32);
   g.bo_off = (int)w;
-  w += a16((int64_t)g.rpw * nb * 4);
+  w += a16(((int64_t)g.rpw * nb + 8) * 4);
   g.bm_off = (int)w;
   w += a16((g.rpw * C / 32 + 4 + kSlack) * 4);
   g.f_off = (int)w;

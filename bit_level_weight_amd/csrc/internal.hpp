@@ -64,6 +64,8 @@ struct SpecViewC1 {
   // 32-bit words from the start of each bit section to the end of the stream
   // buffer: bulk copies never read past these.
   int64_t bitmap_limit, fields_limit, codes_limit;
+  int64_t blkoff_limit;  // the same for the block offsets (words)
+  int64_t keptb_limit;   // and for the kept-before counts (16-bit entries)
 };
 struct VerifViewC1 {
   const uint8_t* perm;
