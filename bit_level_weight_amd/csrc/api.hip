@@ -141,6 +141,13 @@ Shape shape_of(const cass_tensor* W) {
 
 // Whole 16-byte units between a section start and the end of the buffer, in
 // 32-bit words: the bulk copies of the staged kernels stay below this.
+// The staged exact decoders serve Cassandra-1 verification and reconstruction
+// unless CASS_EXACT_PATH=direct selects the per-thread stream readers.
+bool staged_exact_enabled() {
+  const char* e = getenv("CASS_EXACT_PATH");
+  return !(e && strcmp(e, "direct") == 0);
+}
+
 int64_t word_limit(int64_t buffer_bytes, int64_t section_off) {
   return (buffer_bytes - section_off) / 16 * 4;
 }
@@ -161,7 +168,9 @@ VerifViewC1 verif_c1(const cass_tensor* W) {
   const int64_t* o = W->verif_sec;
   return VerifViewC1{b + o[V1_RANK], (const unsigned long long*)(b + o[V1_ROWBASE]),
                      (const uint32_t*)(b + o[V1_BLKOFF]), (const uint32_t*)(b + o[V1_LOWMANT]),
-                     b + o[V1_PRUNED], (const uint32_t*)(b + o[V1_CODES])};
+                     b + o[V1_PRUNED], (const uint32_t*)(b + o[V1_CODES]),
+                     word_limit(W->verif_bytes, o[V1_LOWMANT]), word_limit(W->verif_bytes, o[V1_PRUNED]),
+                     word_limit(W->verif_bytes, o[V1_CODES])};
 }
 SpecViewC2 spec_c2(const cass_tensor* W) {
   const uint8_t* b = (const uint8_t*)W->spec;
@@ -479,9 +488,16 @@ int cass_verify_gemm(const cass_tensor* W, const uint16_t* X, int ntok, int64_t 
   if (!X || !Y) return fail(CASS_ERR_INVALID, "X or Y is NULL");
   if (ldx < W->cols || ldy < W->rows) return fail(CASS_ERR_INVALID, "ldx < cols or ldy < rows");
   const Shape sh = shape_of(W);
-  hipError_t e = W->format == CASS_FMT_C1_UNARY
-                     ? launch_verify_gemm_c1(spec_c1(W), verif_c1(W), sh, X, ntok, ldx, Y, ldy, stream)
-                     : launch_verify_gemm_c2(spec_c2(W), verif_c2(W), sh, X, ntok, ldx, Y, ldy, stream);
+  hipError_t e;
+  if (W->format == CASS_FMT_C1_UNARY) {
+    const SpecViewC1 sv = spec_c1(W);
+    const VerifViewC1 vv = verif_c1(W);
+    e = staged_exact_enabled() && exact_staged_fits(sh, sv, vv)
+            ? launch_verify_gemm_c1_staged(sv, vv, sh, X, ntok, ldx, Y, ldy, stream)
+            : launch_verify_gemm_c1(sv, vv, sh, X, ntok, ldx, Y, ldy, stream);
+  } else {
+    e = launch_verify_gemm_c2(spec_c2(W), verif_c2(W), sh, X, ntok, ldx, Y, ldy, stream);
+  }
   return e == hipSuccess ? CASS_OK : hip_fail(e, "verify gemm launch");
 }
 
@@ -494,8 +510,11 @@ int cass_reconstruct(const cass_tensor* W, uint16_t* out, hipStream_t stream) {
   const Shape sh = shape_of(W);
   hipError_t e;
   if (W->format == CASS_FMT_C1_UNARY) {
+    const SpecViewC1 sv = spec_c1(W);
     const VerifViewC1 vv = verif_c1(W);
-    e = launch_decode_c1(spec_c1(W), &vv, sh, out, stream);
+    e = staged_exact_enabled() && exact_staged_fits(sh, sv, vv)
+            ? launch_reconstruct_c1_staged(sv, vv, sh, out, stream)
+            : launch_decode_c1(sv, &vv, sh, out, stream);
   } else {
     const VerifViewC2 vv = verif_c2(W);
     e = launch_decode_c2(spec_c2(W), &vv, sh, out, stream);

@@ -1,0 +1,772 @@
+// Verification GEMM and exact reconstruction for Cassandra-1, decoded from
+// streams staged in LDS.
+//
+// Method: Cassandra review (marsggbo.github.io), section 1 -- the target
+// model checks the drafted tokens in one parallel pass; section 3.1 -- it
+// loads both streams and reassembles the original weights losslessly;
+// section 3.2 -- a unary exponent code is decoded by counting the zeros up to
+// its one; section 3.3 -- the keep bitmap is de-sparsified.
+//
+// Work split.  A workgroup is one wave and takes 16 rows; it walks their
+// columns in stages of Wb blocks.  A stage copies, for every row, the row's
+// range of each section -- bitmap, fields, low mantissas, pruned bytes and
+// both code sections -- into LDS by LDS DMA: per section the 16 runs are
+// packed back to back and every instruction moves 64 chunks of 16 bytes, so
+// a stage takes a handful of instructions, all in flight at once, and every
+// stream byte is read from HBM once.
+//
+// Decode.  Four lanes serve each row.  The row's kept values of the stage are
+// cut into four equal parts, one per lane, and so are its pruned values, so
+// all lanes run the same number of steps.  A lane finds where its part starts
+// (block from the kept-before counts, word and bit by popcounts and a select,
+// code start by skipping codes) and then decodes U values per group from LDS
+// windows in three phases -- positions, ranks and fields (VALU only); every
+// table read of the group plus the next group's window words (LDS only);
+// the values, written to their columns of a 16 x (Wb*B) bf16 tile.  The
+// verification GEMM multiplies the tile with the matching columns of X on the
+// matrix cores (v_mfma_f32_16x16x16_bf16, tokens padded to 16); the
+// reconstruction copies the tile rows to the output.
+#include <stdlib.h>
+
+#include <algorithm>
+
+#include "internal.hpp"
+#include "staged_decode.hpp"
+
+namespace cass {
+
+namespace {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) const uint8_t lds_u8c;
+typedef __attribute__((address_space(3))) const uint16_t lds_u16c;
+typedef __attribute__((address_space(3))) uint16_t lds_u16;
+typedef __attribute__((address_space(3))) const uint32_t lds_u32c;
+
+constexpr int kRows = 16;   // rows per workgroup
+constexpr int kSec = 6;     // bitmap, fields, low mantissas, pruned bytes, spec codes, verif codes
+constexpr int kPU = 6;      // pruned values per group (6 codes nearly always fit 32 bits)
+
+struct XGeom {
+  int Wb;                    // blocks per stage
+  int TS;                    // u16 per tile row (Wb*B + 2)
+  int64_t nstage, stages_per_split;
+  int nsplit;
+  int perm_off, klut_off, plut_off, tab_off, dummy_off, tile_off;
+  int fix_off, fix_cap, cod_off, cod_cap, lds_bytes;
+};
+
+__device__ __forceinline__ void wsync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ uint32_t lds_addr_of(const uint8_t* p) {
+  return (uint32_t)(uintptr_t)(lds_u8c*)p;
+}
+__device__ __forceinline__ uint32_t ldw(uint32_t a) { return *(lds_u32c*)(uintptr_t)a; }
+__device__ __forceinline__ uint32_t ldh(uint32_t a) { return *(lds_u16c*)(uintptr_t)a; }
+__device__ __forceinline__ void sth(uint32_t a, uint32_t v) { *(lds_u16*)(uintptr_t)a = (uint16_t)v; }
+
+__device__ __forceinline__ void wait_all() {
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  wsync();
+}
+
+// 32 bits of the LDS bit stream at byte address base, bit offset pos.
+__device__ __forceinline__ uint32_t lwin(uint32_t base, uint32_t pos) {
+  const uint32_t a = base + ((pos >> 5) << 2);
+  return __builtin_amdgcn_alignbit(ldw(a + 4), ldw(a), pos & 31u);
+}
+
+// Unary code at LDS bit pos (up to 256 bits); advances pos.
+__device__ __forceinline__ int lunary(uint32_t base, uint32_t& pos) {
+  uint32_t win = lwin(base, pos);
+  int r = 0;
+  for (int it = 0; it < 8 && win == 0u; ++it) {
+    pos += 32;
+    r += 32;
+    win = lwin(base, pos);
+  }
+  if (win == 0u) {
+    pos += 32;
+    return 255;
+  }
+  const int t = __builtin_ctz(win);
+  pos += (uint32_t)t + 1u;
+  return r + t;
+}
+
+// Inclusive sum over the 16 lanes of each row group (lane & 15 = row).
+__device__ __forceinline__ int scan16(int v, int lane) {
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) {
+    const int u = __shfl_up(v, o, 16);
+    if ((lane & 15) >= o) v += u;
+  }
+  return v;
+}
+
+// ---- groups
+// Window words of a kept group: bitmap (3 words at bp), fields (2 at fp),
+// low mantissas (2 at lp), spec codes (2 at cp).  Bit positions are LDS bit
+// offsets from the start of shared memory.
+struct KRaw {
+  uint32_t q0, q1, q2, f0, f1, l0, l1, c0, c1;
+};
+__device__ __forceinline__ KRaw kraw(uint32_t sb, uint32_t bp, uint32_t fp, uint32_t lp,
+                                     uint32_t cp) {
+  const uint32_t qa = sb + ((bp >> 5) << 2), fa = sb + ((fp >> 5) << 2);
+  const uint32_t la = sb + ((lp >> 5) << 2), ca = sb + ((cp >> 5) << 2);
+  return KRaw{ldw(qa), ldw(qa + 4), ldw(qa + 8), ldw(fa), ldw(fa + 4),
+              ldw(la), ldw(la + 4), ldw(ca), ldw(ca + 4)};
+}
+
+// Pruned group: bitmap (3 words at bp, inverted on use), pruned bytes (3 at
+// yp), verification codes (2 at cp).
+struct PRaw {
+  uint32_t q0, q1, q2, y0, y1, y2, c0, c1;
+};
+__device__ __forceinline__ PRaw praw(uint32_t sb, uint32_t bp, uint32_t yp, uint32_t cp) {
+  const uint32_t qa = sb + ((bp >> 5) << 2), ya = sb + ((yp >> 5) << 2);
+  const uint32_t ca = sb + ((cp >> 5) << 2);
+  return PRaw{ldw(qa), ldw(qa + 4), ldw(qa + 8), ldw(ya), ldw(ya + 4), ldw(ya + 8),
+              ldw(ca), ldw(ca + 4)};
+}
+
+// U kept values.  With MASKED, slots u >= t write to the lane's dummy slot (a
+// set bit 63 of the keep window and a set code bit 31 keep their positions
+// and ranks in range), and only lanes with t == U move on: a lane with fewer
+// has finished its part.
+//   torg   LDS byte address of the lane's tile row minus 2 * the bitmap bit of
+//          its column 0 (a value at bitmap bit b goes to torg + 2 b)
+template <int U, bool KLUT, bool MASKED>
+__device__ __forceinline__ void kept_group(KRaw& w, uint32_t& bp, uint32_t& fp, uint32_t& lp,
+                                           uint32_t& cp, uint32_t sb, uint32_t torg,
+                                           uint32_t klutb, uint32_t dummy, int fw, int lw,
+                                           int m, int t) {
+  const uint32_t sbit = bp & 31u;
+  const uint32_t lo0 = __builtin_amdgcn_alignbit(w.q1, w.q0, sbit);
+  const uint32_t hi0 = __builtin_amdgcn_alignbit(w.q2, w.q1, sbit) | (MASKED ? 0x80000000u : 0u);
+  const uint32_t wf = __builtin_amdgcn_alignbit(w.f1, w.f0, fp & 31u);
+  const uint32_t wl = __builtin_amdgcn_alignbit(w.l1, w.l0, lp & 31u);
+  const uint32_t wc0 = __builtin_amdgcn_alignbit(w.c1, w.c0, cp & 31u);
+  // phase 1: table addresses and tile addresses
+  uint32_t la[U], ta[U], low[U], fv[U];
+  uint32_t lo = lo0, wc = wc0, p = 0, base = bp;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    // the window holds U keep bits: lo runs out at most once
+    const bool z = lo == 0u;
+    lo = z ? hi0 : lo;
+    base = z ? bp + 32u : base;
+    p = (uint32_t)__builtin_ctz(lo);
+    lo &= lo - 1u;
+    const uint32_t r = (uint32_t)__builtin_ctz(MASKED ? wc | 0x80000000u : wc);
+    wc = (wc >> r) >> 1;
+    const uint32_t f = __builtin_amdgcn_ubfe(wf, (uint32_t)(u * fw), (uint32_t)fw);
+    low[u] = __builtin_amdgcn_ubfe(wl, (uint32_t)(u * lw), (uint32_t)lw);
+    fv[u] = f;
+    la[u] = KLUT ? klutb + 2u * ((r << fw) | f) : klutb + 2u * r;
+    const uint32_t a = torg + 2u * (base + p);
+    ta[u] = (MASKED && u >= t) ? dummy : a;
+  }
+  {
+    const bool go = !MASKED || t == U;
+    bp = go ? base + p + 1u : bp;
+    fp = go ? fp + (uint32_t)(U * fw) : fp;
+    lp = go ? lp + (uint32_t)(U * lw) : lp;
+    // bits the U codes took: the window was shifted right by that many
+    const uint32_t c0 = (uint32_t)__builtin_clz(wc0);
+    const uint32_t cn = cp + (wc ? (uint32_t)__builtin_clz(wc) : 32u) - c0;
+    cp = go ? cn : cp;
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  // phase 2: every table read of the group and the next group's words
+  uint32_t hv[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) hv[u] = ldh(la[u]);
+  w = kraw(sb, bp, fp, lp, cp);
+  __builtin_amdgcn_sched_barrier(0);
+  // phase 3: the values
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    uint32_t v;
+    if (KLUT) {
+      v = hv[u] | low[u];
+    } else {
+      const uint32_t f = fv[u];
+      v = ((f >> m) << 15) | hv[u] | ((f & ((1u << m) - 1u)) << lw) | low[u];
+    }
+    sth(ta[u], v);
+  }
+}
+
+// kPU pruned values (positions: zero bits of the bitmap); MASKED as for the
+// kept groups.
+template <bool MASKED>
+__device__ __forceinline__ void pruned_group(PRaw& w, uint32_t& bp, uint32_t& yp, uint32_t& cp,
+                                             uint32_t sb, uint32_t torg, uint32_t plutb,
+                                             uint32_t dummy, int t) {
+  constexpr int U = kPU;
+  const uint32_t sbit = bp & 31u;
+  const uint32_t lo0 = ~__builtin_amdgcn_alignbit(w.q1, w.q0, sbit);
+  const uint32_t hi0 = ~__builtin_amdgcn_alignbit(w.q2, w.q1, sbit) | (MASKED ? 0x80000000u : 0u);
+  const uint32_t ysh = yp & 31u;
+  const uint32_t ylo = __builtin_amdgcn_alignbit(w.y1, w.y0, ysh);
+  const uint32_t yhi = __builtin_amdgcn_alignbit(w.y2, w.y1, ysh);
+  const uint32_t wc0 = __builtin_amdgcn_alignbit(w.c1, w.c0, cp & 31u);
+  uint32_t la[U], ta[U], mt[U];
+  uint32_t lo = lo0, wc = wc0, p = 0, base = bp;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const bool z = lo == 0u;
+    lo = z ? hi0 : lo;
+    base = z ? bp + 32u : base;
+    p = (uint32_t)__builtin_ctz(lo);
+    lo &= lo - 1u;
+    const uint32_t r = (uint32_t)__builtin_ctz(MASKED ? wc | 0x80000000u : wc);
+    wc = (wc >> r) >> 1;
+    const uint32_t yw = u < 4 ? ylo : yhi;  // (u is a constant: no select)
+    const uint32_t sh = (uint32_t)(8 * (u & 3));
+    const uint32_t sgn = __builtin_amdgcn_ubfe(yw, sh + 7u, 1u);
+    mt[u] = __builtin_amdgcn_ubfe(yw, sh, 7u);
+    la[u] = plutb + 2u * ((r << 1) | sgn);
+    const uint32_t a = torg + 2u * (base + p);
+    ta[u] = (MASKED && u >= t) ? dummy : a;
+  }
+  {
+    const bool go = !MASKED || t == U;
+    bp = go ? base + p + 1u : bp;
+    yp = go ? yp + (uint32_t)(8 * U) : yp;
+    const uint32_t c0 = (uint32_t)__builtin_clz(wc0);
+    const uint32_t cn = cp + (wc ? (uint32_t)__builtin_clz(wc) : 32u) - c0;
+    cp = go ? cn : cp;
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  uint32_t hv[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) hv[u] = ldh(la[u]);
+  w = praw(sb, bp, yp, cp);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int u = 0; u < U; ++u) sth(ta[u], hv[u] | mt[u]);
+}
+
+// One kept value, any code length (codes from LDS, or from global memory at
+// cg when it is set).
+__device__ __forceinline__ void kept_step(uint32_t sb, uint32_t& bp, uint32_t bp_end,
+                                          uint32_t& fp, uint32_t& lp, uint32_t& cp,
+                                          const uint32_t* cg, uint32_t torg, const uint8_t* ps,
+                                          int fw, int lw, int m) {
+  uint32_t w = lwin(sb, bp);
+  // a valid part has its next value inside the row's stage; the bound only
+  // keeps a corrupt stream from spinning
+  for (; w == 0u && bp < bp_end;) {
+    bp += 32u;
+    w = lwin(sb, bp);
+  }
+  const uint32_t pos = bp + (uint32_t)__builtin_ctz(w);
+  bp = pos + 1u;
+  const uint32_t f = lwin(sb, fp) & ((1u << fw) - 1u);
+  fp += (uint32_t)fw;
+  const uint32_t low = lw ? (lwin(sb, lp) & ((1u << lw) - 1u)) : 0u;
+  lp += (uint32_t)lw;
+  const int r = cg ? unary_at(cg, cp) : lunary(sb, cp);
+  const uint32_t e = ps[r];
+  sth(torg + 2u * pos, ((f >> m) << 15) | (e << 7) | ((f & ((1u << m) - 1u)) << lw) | low);
+}
+
+__device__ __forceinline__ void pruned_step(uint32_t sb, uint32_t& bp, uint32_t bp_end,
+                                            uint32_t& yp, uint32_t& cp, const uint32_t* cg,
+                                            uint32_t torg, const uint8_t* pv) {
+  uint32_t w = ~lwin(sb, bp);
+  for (; w == 0u && bp < bp_end;) {
+    bp += 32u;
+    w = ~lwin(sb, bp);
+  }
+  const uint32_t pos = bp + (uint32_t)__builtin_ctz(w);
+  bp = pos + 1u;
+  const uint32_t byte = lwin(sb, yp) & 0xFFu;
+  yp += 8u;
+  const int r = cg ? unary_at(cg, cp) : lunary(sb, cp);
+  const uint32_t e = pv[r];
+  sth(torg + 2u * pos, ((byte >> 7) << 15) | (e << 7) | (byte & 0x7Fu));
+}
+
+// Bit offset, inside the nwb words at LDS byte address wa, of the
+// (skip+1)-th set bit (zero bit when INV); the count lies inside them.
+template <bool INV>
+__device__ __forceinline__ uint32_t find_in_block(uint32_t wa, int nwb, int skip) {
+  int rem = skip, wsel = nwb - 1;
+  uint32_t wd = 0;
+  if (nwb <= 8) {
+    uint32_t wv[8];
+#pragma unroll
+    for (int w = 0; w < 8; ++w) wv[w] = w < nwb ? (INV ? ~ldw(wa + 4 * w) : ldw(wa + 4 * w)) : 0u;
+    bool found = false;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      const int c = __builtin_popcount(wv[w]);
+      const bool here = !found && w < nwb && rem < c;
+      wsel = here ? w : wsel;
+      wd = here ? wv[w] : wd;
+      rem -= (!found && !here) ? c : 0;
+      found = found || here;
+    }
+  } else {
+    int wi = 0;
+    wd = INV ? ~ldw(wa) : ldw(wa);
+    for (;;) {
+      const int c = __builtin_popcount(wd);
+      if (rem < c || wi == nwb - 1) break;  // (the second test: corrupt streams only)
+      rem -= c;
+      ++wi;
+      wd = INV ? ~ldw(wa + 4 * wi) : ldw(wa + 4 * wi);
+    }
+    wsel = wi;
+  }
+  return (uint32_t)(wsel * 32 + select_bit(wd, rem + 1));
+}
+
+template <int MODE, int KU, bool KLUT>  // MODE 0: verification GEMM into Y, 1: reconstruction
+__global__ void __launch_bounds__(64) k_exact_staged(SpecViewC1 sv, VerifViewC1 vv, Shape sh,
+                                                     XGeom g, const uint16_t* __restrict__ X,
+                                                     int ntok, int64_t ldx,
+                                                     float* __restrict__ Y, int64_t ldy,
+                                                     uint16_t* __restrict__ out) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  const int lane = threadIdx.x;
+  const int64_t R = sh.rows, C = sh.cols, k = sh.keep, B = sh.block, nb = C / B;
+  const int m = sh.mant, fw = 1 + m, lw = 7 - m;
+  const int nwb = (int)(B / 32);
+  const uint32_t sb = lds_addr_of(smem);
+  const uint32_t* sm32 = reinterpret_cast<const uint32_t*>(smem);
+
+  // rank tables: bytes for the one-value steps, bf16 templates for the groups
+  uint8_t* ps = smem + g.perm_off;
+  uint8_t* pv = ps + 256;
+  uint16_t* klut = reinterpret_cast<uint16_t*>(smem + g.klut_off);
+  uint16_t* plut = reinterpret_cast<uint16_t*>(smem + g.plut_off);
+  for (int i = lane; i < 256; i += 64) {
+    ps[i] = sv.perm[i];
+    pv[i] = vv.perm[i];
+  }
+  if (KLUT) {
+    for (int i = lane; i < (32 << fw); i += 64) {
+      const uint32_t f = (uint32_t)i & ((1u << fw) - 1u);
+      klut[i] = (uint16_t)(((f >> m) << 15) | ((uint32_t)sv.perm[i >> fw] << 7) |
+                           ((f & ((1u << m) - 1u)) << lw));
+    }
+  } else if (lane < 32) {
+    klut[lane] = (uint16_t)((uint32_t)sv.perm[lane] << 7);
+  }
+  plut[lane] = (uint16_t)(((uint32_t)(lane & 1) << 15) | ((uint32_t)vv.perm[lane >> 1] << 7));
+  const uint32_t klutb = sb + g.klut_off, plutb = sb + g.plut_off;
+  const uint32_t dummy = sb + g.dummy_off + 4u * lane;
+  int* tab_pre = reinterpret_cast<int*>(smem + g.tab_off);                     // [6][16]
+  int64_t* tab_c0 = reinterpret_cast<int64_t*>(smem + g.tab_off + kSec * 64);  // [6][16]
+  const uint32_t tileb = sb + g.tile_off;
+
+  const int r = lane & 15, j = lane >> 4;
+  const int64_t row0 = (int64_t)blockIdx.x * kRows;
+  const int64_t row = row0 + r;
+  const bool row_ok = row < R;
+  const int64_t rowc = row_ok ? row : R - 1;  // clamped for loads
+  const int64_t st0 = (int64_t)blockIdx.y * g.stages_per_split;
+  const int64_t st1 = std::min<int64_t>(st0 + g.stages_per_split, g.nstage);
+  const int64_t rbs = (int64_t)sv.rowbase[rowc], rbv = (int64_t)vv.rowbase[rowc];
+  const int64_t rbs_next = rowc + 1 < R ? (int64_t)sv.rowbase[rowc + 1] : sv.codes_limit * 32;
+  const int64_t rbv_next = rowc + 1 < R ? (int64_t)vv.rowbase[rowc + 1] : vv.codes_limit * 32;
+  const uint8_t* sec_base[kSec] = {
+      reinterpret_cast<const uint8_t*>(sv.bitmap), reinterpret_cast<const uint8_t*>(sv.fields),
+      reinterpret_cast<const uint8_t*>(vv.lowmant), vv.pruned,
+      reinterpret_cast<const uint8_t*>(sv.codes), reinterpret_cast<const uint8_t*>(vv.codes)};
+  const int64_t sec_lim[kSec] = {sv.bitmap_limit / 4, sv.fields_limit / 4,
+                                 vv.lowmant_limit / 4, vv.pruned_limit / 4,
+                                 sv.codes_limit / 4,   vv.codes_limit / 4};  // in chunks
+  v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
+
+  // kept-before and code starts at a stage's block boundaries (i = 0..Wb),
+  // loaded one stage ahead
+  struct Meta {
+    int64_t kbv[3], bos[3], bov[3];
+  };
+  auto load_meta = [&](int64_t stg) {
+    Meta md;
+    const int64_t bf = stg * g.Wb;
+    const int64_t be = std::min<int64_t>(bf + g.Wb, nb);
+    const int nbs = (int)(be - bf);
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      const int64_t bb = bf + i;
+      if (i > nbs) {
+        md.kbv[i] = md.kbv[i - 1];
+        md.bos[i] = md.bos[i - 1];
+        md.bov[i] = md.bov[i - 1];
+      } else if (bb < nb) {
+        md.kbv[i] = sv.keptb[rowc * nb + bb];
+        md.bos[i] = rbs + sv.blkoff[rowc * nb + bb];
+        md.bov[i] = rbv + vv.blkoff[rowc * nb + bb];
+      } else {
+        md.kbv[i] = k;
+        md.bos[i] = rbs_next;
+        md.bov[i] = rbv_next;
+      }
+    }
+    return md;
+  };
+  Meta md_next{};
+  if (st0 < st1) md_next = load_meta(st0);
+
+  for (int64_t st = st0; st < st1; ++st) {
+    const int64_t bf = st * g.Wb;
+    const int64_t be = std::min<int64_t>(bf + g.Wb, nb);
+    const int nbs = (int)(be - bf);  // 1 or 2
+    const Meta md = md_next;
+    const int64_t* kbv = md.kbv;
+    const int64_t* bos = md.bos;
+    const int64_t* bov = md.bov;
+    const int64_t kbe = nbs > 1 ? kbv[2] : kbv[1];
+    const int64_t bose = nbs > 1 ? bos[2] : bos[1];
+    const int64_t bove = nbs > 1 ? bov[2] : bov[1];
+    int64_t lo[kSec], hi[kSec];
+    lo[0] = (rowc * nb + bf) * B;
+    hi[0] = (rowc * nb + be) * B;
+    lo[1] = (rowc * k + kbv[0]) * fw;
+    hi[1] = (rowc * k + kbe) * fw;
+    lo[2] = (rowc * k + kbv[0]) * lw;
+    hi[2] = (rowc * k + kbe) * lw;
+    lo[3] = (rowc * (C - k) + bf * B - kbv[0]) * 8;
+    hi[3] = (rowc * (C - k) + be * B - kbe) * 8;
+    lo[4] = bos[0];
+    hi[4] = bose;
+    lo[5] = bov[0];
+    hi[5] = bove;
+
+    // ---- staging: per section, the 16 row runs packed back to back
+    int64_t bias[kSec];
+    int nsec[kSec];
+    int foff = 0, coff = 0;
+    bool overflow = false;
+#pragma unroll
+    for (int sec = 0; sec < kSec; ++sec) {
+      const int64_t c0 = lo[sec] >> 7;
+      int64_t c1 = (hi[sec] + 127) >> 7;
+      if (c1 > sec_lim[sec]) c1 = sec_lim[sec];
+      const int n = (row_ok && hi[sec] > lo[sec] && c1 > c0) ? (int)(c1 - c0) : 0;
+      const int incl = scan16(n, lane);
+      const int pre = incl - n;
+      const int N = __builtin_amdgcn_readlane(incl, 15);
+      int off;
+      if (sec < 4) {
+        off = g.fix_off + foff;
+        foff += 16 * N;
+      } else {
+        if (coff + 16 * N > g.cod_cap) overflow = true;
+        off = g.cod_off + coff;
+        coff += 16 * N;
+      }
+      nsec[sec] = (sec < 4 || !overflow) ? N : 0;
+      bias[sec] = (int64_t)(off + 16 * pre) * 8 - c0 * 128;
+      if (j == 0) {
+        tab_pre[sec * 16 + r] = pre;
+        tab_c0[sec * 16 + r] = c0;
+      }
+    }
+    wsync();  // the row tables
+    {
+      int off_f = g.fix_off, off_c = g.cod_off;
+#pragma unroll
+      for (int sec = 0; sec < kSec; ++sec) {
+        const int N = nsec[sec];
+        const int off = sec < 4 ? off_f : off_c;
+        for (int base = 0; base < N; base += 64) {
+          const int c = base + lane;
+          if (c < N) {
+            // the row whose run holds packed chunk c: the last row starting at or before it
+            int rr = 0;
+#pragma unroll
+            for (int step = 8; step >= 1; step >>= 1)
+              if (tab_pre[sec * 16 + rr + step] <= c) rr += step;
+            const int64_t src = tab_c0[sec * 16 + rr] + (c - tab_pre[sec * 16 + rr]);
+            __builtin_amdgcn_global_load_lds((const void*)(sec_base[sec] + 16 * src),
+                                             (lds_void*)(smem + off + 16 * base), 16, 0, 2);
+          }
+        }
+        if (sec < 4) off_f += 16 * N;
+        else off_c += 16 * N;
+      }
+    }
+    wait_all();
+    if (st + 1 < st1) md_next = load_meta(st + 1);  // lands while this stage decodes
+
+    // ---- decode: kept values, then pruned values, into the tile
+    const uint32_t bm_row = (uint32_t)(bias[0] + (rowc * nb + bf) * B);  // bitmap bit of column 0
+    const uint32_t torg = tileb + 2u * (uint32_t)(r * g.TS) - 2u * bm_row;
+    const uint32_t bm_end = bm_row + (uint32_t)(nbs * B);
+    {
+      const int64_t K = kbe - kbv[0];
+      const int64_t i0 = (K * j) >> 2;
+      const int n = row_ok ? (int)(((K * (j + 1)) >> 2) - i0) : 0;
+      const int64_t kidx = kbv[0] + i0;  // row-relative kept index of the part's first value
+      uint32_t bp = bm_row, fp = 0, lp = 0, cp = 0;
+      const uint32_t* cg = nullptr;
+      if (n > 0) {
+        const int bi = (nbs > 1 && kidx >= kbv[1]) ? 1 : 0;
+        const int skip = (int)(kidx - kbv[bi]);
+        const uint32_t blk = bm_row + (uint32_t)(bi * B);
+        bp = blk + find_in_block<false>(sb + (blk >> 3), nwb, skip);
+        fp = (uint32_t)(bias[1] + (rowc * k + kidx) * fw);
+        lp = (uint32_t)(bias[2] + (rowc * k + kidx) * lw);
+        if (!overflow) {
+          cp = skip_codes8(sm32, (uint32_t)(bias[4] + bos[bi]), skip);
+        } else {
+          cg = sv.codes + (bos[bi] >> 5);
+          cp = skip_codes(cg, (uint32_t)(bos[bi] & 31), skip);
+        }
+      }
+      int nmax = n;
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) nmax = max(nmax, __shfl_xor(nmax, o, 64));
+      if (!overflow) {
+        KRaw w = kraw(sb, bp, fp, lp, cp);
+        for (int done = 0; done < nmax; done += KU) {
+          const int t = min(max(n - done, 0), KU);
+          const uint32_t sbit = bp & 31u;
+          const int have = __builtin_popcount(__builtin_amdgcn_alignbit(w.q1, w.q0, sbit)) +
+                           __builtin_popcount(__builtin_amdgcn_alignbit(w.q2, w.q1, sbit));
+          const int ncode = __builtin_popcount(__builtin_amdgcn_alignbit(w.c1, w.c0, cp & 31u));
+          const bool ok = min(have, ncode) >= t;
+          if (__all(t == KU && ok)) {
+            kept_group<KU, KLUT, false>(w, bp, fp, lp, cp, sb, torg, klutb, dummy, fw, lw, m, KU);
+          } else if (__all(ok)) {
+            // some part ends inside this group
+            kept_group<KU, KLUT, true>(w, bp, fp, lp, cp, sb, torg, klutb, dummy, fw, lw, m, t);
+          } else {
+            for (int u = 0; u < KU; ++u)
+              if (u < t) kept_step(sb, bp, bm_end, fp, lp, cp, nullptr, torg, ps, fw, lw, m);
+            w = kraw(sb, bp, fp, lp, cp);
+          }
+        }
+      } else {
+        for (int i = 0; i < nmax; ++i)
+          if (i < n) kept_step(sb, bp, bm_end, fp, lp, cp, cg, torg, ps, fw, lw, m);
+      }
+    }
+    {
+      const int64_t P = (int64_t)nbs * B - (kbe - kbv[0]);
+      const int64_t i0 = (P * j) >> 2;
+      const int n = row_ok ? (int)(((P * (j + 1)) >> 2) - i0) : 0;
+      const int64_t pidx = bf * B - kbv[0] + i0;  // row-relative pruned index
+      uint32_t bp = bm_row, yp = 0, cp = 0;
+      const uint32_t* cg = nullptr;
+      if (n > 0) {
+        const int64_t pb1 = (bf + 1) * B - kbv[1];
+        const int bi = (nbs > 1 && pidx >= pb1) ? 1 : 0;
+        const int skip = (int)(pidx - (bi ? pb1 : bf * B - kbv[0]));
+        const uint32_t blk = bm_row + (uint32_t)(bi * B);
+        bp = blk + find_in_block<true>(sb + (blk >> 3), nwb, skip);
+        yp = (uint32_t)(bias[3] + (rowc * (C - k) + pidx) * 8);
+        if (!overflow) {
+          cp = skip_codes8(sm32, (uint32_t)(bias[5] + bov[bi]), skip);
+        } else {
+          cg = vv.codes + (bov[bi] >> 5);
+          cp = skip_codes(cg, (uint32_t)(bov[bi] & 31), skip);
+        }
+      }
+      int nmax = n;
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) nmax = max(nmax, __shfl_xor(nmax, o, 64));
+      if (!overflow) {
+        PRaw w = praw(sb, bp, yp, cp);
+        for (int done = 0; done < nmax; done += kPU) {
+          const int t = min(max(n - done, 0), kPU);
+          const uint32_t sbit = bp & 31u;
+          const int have = __builtin_popcount(~__builtin_amdgcn_alignbit(w.q1, w.q0, sbit)) +
+                           __builtin_popcount(~__builtin_amdgcn_alignbit(w.q2, w.q1, sbit));
+          const int ncode = __builtin_popcount(__builtin_amdgcn_alignbit(w.c1, w.c0, cp & 31u));
+          const bool ok = min(have, ncode) >= t;
+          if (__all(t == kPU && ok)) {
+            pruned_group<false>(w, bp, yp, cp, sb, torg, plutb, dummy, kPU);
+          } else if (__all(ok)) {
+            pruned_group<true>(w, bp, yp, cp, sb, torg, plutb, dummy, t);
+          } else {
+            for (int u = 0; u < kPU; ++u)
+              if (u < t) pruned_step(sb, bp, bm_end, yp, cp, nullptr, torg, pv);
+            w = praw(sb, bp, yp, cp);
+          }
+        }
+      } else {
+        for (int i = 0; i < nmax; ++i)
+          if (i < n) pruned_step(sb, bp, bm_end, yp, cp, cg, torg, pv);
+      }
+    }
+    wsync();  // the tile is complete
+
+    if (MODE == 0) {
+      const int n = lane & 15, kq = lane >> 4;
+      const int64_t col0 = bf * B;
+      for (int ks = 0; ks < nbs * (int)B / 16; ++ks) {
+        v4s bop = v4s{0, 0, 0, 0};
+        if (n < ntok) {
+          const uint16_t* xp = X + (int64_t)n * ldx + col0 + ks * 16 + 4 * kq;
+          bop = v4s{(short)xp[0], (short)xp[1], (short)xp[2], (short)xp[3]};
+        }
+        const uint32_t ta = tileb + 2u * (uint32_t)(n * g.TS + ks * 16 + 4 * kq);
+        const uint32_t a0 = ldw(ta), a1 = ldw(ta + 4);
+        const v4s aop = v4s{(short)(a0 & 0xFFFF), (short)(a0 >> 16), (short)(a1 & 0xFFFF),
+                            (short)(a1 >> 16)};
+        acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(aop, bop, acc, 0, 0, 0);
+      }
+    } else {
+      const int cpr = nbs * (int)B / 8;  // 16-byte chunks per tile row
+      for (int c = lane; c < kRows * cpr; c += 64) {
+        const int rr = c / cpr, cc = c - rr * cpr;
+        if (row0 + rr < R) {
+          const uint32_t ta = tileb + 2u * (uint32_t)(rr * g.TS + cc * 8);
+          const u32x4 v = u32x4{ldw(ta), ldw(ta + 4), ldw(ta + 8), ldw(ta + 12)};
+          *reinterpret_cast<u32x4*>(out + (row0 + rr) * C + bf * B + cc * 8) = v;
+        }
+      }
+    }
+    wsync();  // every lane is done with the tile and the staged runs
+  }
+
+  if (MODE == 0) {
+    // D[i][j]: this lane holds rows 4 kq + e of the 16, token n
+    const int n = lane & 15, kq = lane >> 4;
+    if (n < ntok) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int64_t rr = row0 + 4 * kq + e;
+        if (rr < R) {
+          if (g.nsplit == 1) Y[(int64_t)n * ldy + rr] = acc[e];
+          else atomicAdd(Y + (int64_t)n * ldy + rr, acc[e]);
+        }
+      }
+    }
+  }
+}
+
+__global__ void __launch_bounds__(256) k_zero_y(float* Y, int ntok, int64_t rows, int64_t ldy) {
+  const int64_t n = (int64_t)ntok * rows;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x)
+    Y[(i / rows) * ldy + (i % rows)] = 0.f;
+}
+
+int a16(int64_t v) { return (int)((v + 15) / 16 * 16); }
+
+constexpr int64_t kMaxLds = 64 * 1024;
+
+XGeom make_xgeom(const Shape& sh, const SpecViewC1& sv, const VerifViewC1& vv) {
+  XGeom g = {};
+  const int64_t B = sh.block, nb = sh.cols / B;
+  const int fw = 1 + sh.mant;
+  g.Wb = B >= 256 ? 1 : 2;
+  if (const char* e = getenv("CASS_EXACT_BLOCKS")) {
+    const int w = atoi(e);
+    if (w >= 1 && w <= 2) g.Wb = w;
+  }
+  g.TS = (int)(g.Wb * B + 2);
+  g.nstage = (nb + g.Wb - 1) / g.Wb;
+  const int64_t pos = (int64_t)g.Wb * B;  // positions per row per stage
+  // fixed-width sections: 1 + 8 bits per position, plus chunk rounding
+  const int64_t fix_row = (9 * pos + 127) / 128 * 16 + 7 * 16;
+  // codes: twice the tensor's average code bits per position, at least 4
+  const double tot = (double)(sv.codes_limit + vv.codes_limit) * 32.0;
+  const double avg = sh.rows * sh.cols > 0 ? tot / ((double)sh.rows * (double)sh.cols) : 4.0;
+  const double cbits = std::max(4.0, 2.0 * avg + 0.5);
+  const int64_t cod_row = ((int64_t)(pos * cbits / 128.0) + 4) * 16;
+  int64_t o = 0;
+  g.perm_off = (int)o;
+  o += 512;
+  g.klut_off = (int)o;
+  o += a16(fw <= 5 ? (int64_t)(32 << fw) * 2 : 64);
+  g.plut_off = (int)o;
+  o += 128;
+  g.tab_off = (int)o;
+  o += kSec * 64 + kSec * 128;
+  g.dummy_off = (int)o;
+  o += 256;
+  g.tile_off = (int)o;
+  o += a16((int64_t)kRows * g.TS * 2);
+  g.fix_off = (int)o;
+  g.fix_cap = (int)(kRows * fix_row);
+  o += g.fix_cap + 64;  // window look-ahead
+  g.cod_off = (int)o;
+  g.cod_cap = (int)std::min<int64_t>(kRows * cod_row, 24 * 1024);
+  o += g.cod_cap + 64;
+  g.lds_bytes = (int)o;
+  return g;
+}
+
+template <int MODE, int KU, bool KLUT>
+hipError_t launch_staged_t(const SpecViewC1& sv, const VerifViewC1& vv, const Shape& sh,
+                           XGeom g, const uint16_t* X, int ntok, int64_t ldx, float* Y,
+                           int64_t ldy, uint16_t* out, hipStream_t s) {
+  auto kern = k_exact_staged<MODE, KU, KLUT>;
+  if (g.lds_bytes > kMaxLds) return hipErrorInvalidValue;
+  int occ = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, (const void*)kern, 64,
+                                                   (size_t)g.lds_bytes) != hipSuccess || occ < 1)
+    occ = 1;
+  const int64_t gx = (sh.rows + kRows - 1) / kRows;
+  const int64_t want = (int64_t)device_cu_count() * occ;
+  int64_t nsplit = (want + gx - 1) / gx;
+  if (nsplit > g.nstage) nsplit = g.nstage;
+  if (nsplit < 1) nsplit = 1;
+  g.stages_per_split = (g.nstage + nsplit - 1) / nsplit;
+  nsplit = (g.nstage + g.stages_per_split - 1) / g.stages_per_split;
+  g.nsplit = (int)nsplit;
+  if (MODE == 0 && nsplit > 1) {
+    int64_t gz = ((int64_t)ntok * sh.rows + 255) / 256;
+    if (gz > 4096) gz = 4096;
+    k_zero_y<<<(unsigned)gz, 256, 0, s>>>(Y, ntok, sh.rows, ldy);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  kern<<<dim3((unsigned)gx, (unsigned)nsplit), 64, (size_t)g.lds_bytes, s>>>(sv, vv, sh, g, X,
+                                                                            ntok, ldx, Y, ldy,
+                                                                            out);
+  return hipGetLastError();
+}
+
+template <int MODE>
+hipError_t launch_staged(const SpecViewC1& sv, const VerifViewC1& vv, const Shape& sh,
+                         const uint16_t* X, int ntok, int64_t ldx, float* Y, int64_t ldy,
+                         uint16_t* out, hipStream_t s) {
+  const XGeom g = make_xgeom(sh, sv, vv);
+  if (sh.mant == 3)
+    return launch_staged_t<MODE, 8, true>(sv, vv, sh, g, X, ntok, ldx, Y, ldy, out, s);
+  if (sh.mant <= 4)
+    return launch_staged_t<MODE, 4, true>(sv, vv, sh, g, X, ntok, ldx, Y, ldy, out, s);
+  return launch_staged_t<MODE, 4, false>(sv, vv, sh, g, X, ntok, ldx, Y, ldy, out, s);
+}
+
+}  // namespace
+
+bool exact_staged_fits(const Shape& sh, const SpecViewC1& sv, const VerifViewC1& vv) {
+  if (sh.block < 32 || sh.block % 32) return false;
+  return make_xgeom(sh, sv, vv).lds_bytes <= kMaxLds;
+}
+
+hipError_t launch_verify_gemm_c1_staged(const SpecViewC1& sv, const VerifViewC1& vv,
+                                        const Shape& sh, const uint16_t* X, int ntok,
+                                        int64_t ldx, float* Y, int64_t ldy, hipStream_t s) {
+  if (sh.rows == 0 || ntok == 0) return hipSuccess;
+  return launch_staged<0>(sv, vv, sh, X, ntok, ldx, Y, ldy, nullptr, s);
+}
+
+hipError_t launch_reconstruct_c1_staged(const SpecViewC1& sv, const VerifViewC1& vv,
+                                        const Shape& sh, uint16_t* out, hipStream_t s) {
+  if (sh.rows == 0) return hipSuccess;
+  return launch_staged<1>(sv, vv, sh, nullptr, 0, 0, nullptr, 0, out, s);
+}
+
+}  // namespace cass

@@ -225,30 +225,6 @@ __device__ __forceinline__ void c1_group(Raw& w, uint32_t& bp, uint32_t& fp, uin
   }
 }
 
-// skip_codes with the first 256 bits read at once (nine words, one LDS round
-// trip); longer skips continue word by word.
-__device__ __forceinline__ uint32_t skip_codes8(const uint32_t* w, uint32_t pos, int n) {
-  if (n <= 0) return pos;
-  const uint32_t* q = w + (pos >> 5);
-  const uint32_t sh = pos & 31u;
-  uint32_t qv[9];
-#pragma unroll
-  for (int i = 0; i < 9; ++i) qv[i] = q[i];
-  int rem = n, sel = -1;
-  uint32_t wsel = 0;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const uint32_t win = __builtin_amdgcn_alignbit(qv[i + 1], qv[i], sh);
-    const int c = __builtin_popcount(win);
-    const bool here = sel < 0 && rem <= c;
-    sel = here ? i : sel;
-    wsel = here ? win : wsel;
-    rem -= (sel < 0) ? c : 0;
-  }
-  if (sel < 0) return skip_codes(w, pos + 256u, rem);
-  return pos + 32u * (uint32_t)sel + (uint32_t)select_bit(wsel, rem) + 1u;
-}
-
 // Where one lane's part stands: bit positions in the staged words.
 struct Part {
   uint32_t bp, fp, cp, rowbit;

@@ -74,6 +74,9 @@ struct VerifViewC1 {
   const uint32_t* lowmant;
   const uint8_t* pruned;
   const uint32_t* codes;
+  // 32-bit words from the start of each bit section to the end of the stream
+  // buffer (whole 16-byte units): bulk copies never read past these.
+  int64_t lowmant_limit, pruned_limit, codes_limit;
 };
 struct SpecViewC2 {
   const uint32_t* bitmap;
@@ -140,6 +143,13 @@ hipError_t launch_decode_c2(const SpecViewC2& sv, const VerifViewC2* vv, const S
 hipError_t launch_verify_gemm_c1(const SpecViewC1& sv, const VerifViewC1& vv, const Shape& sh,
                                  const uint16_t* X, int ntok, int64_t ldx, float* Y,
                                  int64_t ldy, hipStream_t s);
+// Staged exact decoders for Cassandra-1 (verification GEMM, reconstruction).
+bool exact_staged_fits(const Shape& sh, const SpecViewC1& sv, const VerifViewC1& vv);
+hipError_t launch_verify_gemm_c1_staged(const SpecViewC1& sv, const VerifViewC1& vv,
+                                        const Shape& sh, const uint16_t* X, int ntok,
+                                        int64_t ldx, float* Y, int64_t ldy, hipStream_t s);
+hipError_t launch_reconstruct_c1_staged(const SpecViewC1& sv, const VerifViewC1& vv,
+                                        const Shape& sh, uint16_t* out, hipStream_t s);
 hipError_t launch_verify_gemm_c2(const SpecViewC2& sv, const VerifViewC2& vv, const Shape& sh,
                                  const uint16_t* X, int ntok, int64_t ldx, float* Y,
                                  int64_t ldy, hipStream_t s);

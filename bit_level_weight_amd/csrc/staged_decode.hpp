@@ -73,6 +73,30 @@ __device__ __forceinline__ uint32_t skip_codes(const uint32_t* w, uint32_t pos, 
   return pos;
 }
 
+// skip_codes with the first 256 bits read at once (nine words, one LDS round
+// trip); longer skips continue word by word.
+__device__ __forceinline__ uint32_t skip_codes8(const uint32_t* w, uint32_t pos, int n) {
+  if (n <= 0) return pos;
+  const uint32_t* q = w + (pos >> 5);
+  const uint32_t sh = pos & 31u;
+  uint32_t qv[9];
+#pragma unroll
+  for (int i = 0; i < 9; ++i) qv[i] = q[i];
+  int rem = n, sel = -1;
+  uint32_t wsel = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t win = __builtin_amdgcn_alignbit(qv[i + 1], qv[i], sh);
+    const int c = __builtin_popcount(win);
+    const bool here = sel < 0 && rem <= c;
+    sel = here ? i : sel;
+    wsel = here ? win : wsel;
+    rem -= (sel < 0) ? c : 0;
+  }
+  if (sel < 0) return skip_codes(w, pos + 256u, rem);
+  return pos + 32u * (uint32_t)sel + (uint32_t)select_bit(wsel, rem) + 1u;
+}
+
 // Byte offset of x element e in LDS: two bf16 of padding after every 32
 // elements (one bitmap word), so lanes working on different parts of a row
 // hit different banks.  Consecutive words of positions are 68 bytes apart.

@@ -157,6 +157,50 @@ def test_draft_gemv_and_verify_gemm(gpu, orc, case):
         check_product(Y.cpu().numpy(), Y_ref, absY)
 
 
+EXACT_CASES = [
+    # rows, cols, keep, mant, block, weights
+    (37, 4096, 1229, 3, 256, "normal"),
+    (16, 512, 205, 0, 32, "normal"),
+    (20, 14336, 4301, 2, 256, "normal"),
+    (9, 1024, 0, 3, 128, "normal"),
+    (9, 1024, 1024, 7, 64, "normal"),
+    (33, 2048, 614, 3, 256, "wide"),   # long codes: past the LDS code share
+    (19, 1280, 384, 5, 256, "normal"),  # odd block count, mantissa without the value table
+    (40, 1024, 307, 1, 64, "normal"),
+]
+
+
+@pytest.mark.parametrize("path", ["default", "blocks1", "blocks2", "direct"])
+def test_exact_paths(gpu, orc, monkeypatch, path):
+    """Reconstruction and verification GEMM (Cassandra-1) through each exact
+    decoder: the staged kernel with its default stage width, with stages of
+    one or two blocks (CASS_EXACT_BLOCKS), and the per-thread stream readers
+    (CASS_EXACT_PATH=direct)."""
+    torch, cass = gpu
+    if path == "blocks1":
+        monkeypatch.setenv("CASS_EXACT_BLOCKS", "1")
+    elif path == "blocks2":
+        monkeypatch.setenv("CASS_EXACT_BLOCKS", "2")
+    elif path == "direct":
+        monkeypatch.setenv("CASS_EXACT_PATH", "direct")
+    for case in EXACT_CASES:
+        R, C, k, m, B, kind = case
+        print("case", path, case, flush=True)
+        w = (synth.weight_wide(R, C, 31 + R) if kind == "wide" else make_w(R, C, 41 + R + C))
+        spec_o, verif_o = orc.encode(w, k, m, block=B)
+        enc = cass.encode(dev(torch, w), k, m, block=B)
+        out = torch.empty((R, C), dtype=torch.int16, device="cuda")
+        cass.cass_reconstruct(enc.desc, out)
+        torch.cuda.synchronize()
+        assert np.array_equal(host_u16(out), w), case
+        X = synth.activations(5, C, 3, t0=R)
+        Y = torch.full((5, R), float("nan"), dtype=torch.float32, device="cuda")
+        cass.cass_verify_gemm(enc.desc, dev(torch, X), Y)
+        torch.cuda.synchronize()
+        Y_ref, absY = orc.product(spec_o, X, verif=verif_o, threads=4)
+        check_product(Y.cpu().numpy(), Y_ref, absY)
+
+
 @pytest.mark.parametrize("fmt", [1, 2])
 def test_direct_gemv_path(gpu, orc, monkeypatch, fmt):
     """The direct (non-staged) GEMV kernels, selected with CASS_GEMV_DIRECT=1."""
