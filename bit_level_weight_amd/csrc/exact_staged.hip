@@ -55,7 +55,7 @@ struct XGeom {
   int TS;                    // u16 per tile row (Wb*B + 2)
   int64_t nstage, stages_per_split;
   int nsplit;
-  int perm_off, klut_off, plut_off, tab_off, dummy_off, tile_off;
+  int perm_off, klut_off, plut_off, meta_off, dummy_off, tile_off;
   int fix_off, fix_cap, cod_off, cod_cap, lds_bytes;
 };
 
@@ -101,13 +101,12 @@ __device__ __forceinline__ int lunary(uint32_t base, uint32_t& pos) {
   return r + t;
 }
 
-// Inclusive sum over the 16 lanes of each row group (lane & 15 = row).
-__device__ __forceinline__ int scan16(int v, int lane) {
-#pragma unroll
-  for (int o = 1; o < 16; o <<= 1) {
-    const int u = __shfl_up(v, o, 16);
-    if ((lane & 15) >= o) v += u;
-  }
+// Inclusive sum over each row of 16 lanes (DPP row shifts, zero fill).
+__device__ __forceinline__ int scan16(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);  // row_shr:8
   return v;
 }
 
@@ -368,8 +367,6 @@ __global__ void __launch_bounds__(64) k_exact_staged(SpecViewC1 sv, VerifViewC1 
   plut[lane] = (uint16_t)(((uint32_t)(lane & 1) << 15) | ((uint32_t)vv.perm[lane >> 1] << 7));
   const uint32_t klutb = sb + g.klut_off, plutb = sb + g.plut_off;
   const uint32_t dummy = sb + g.dummy_off + 4u * lane;
-  int* tab_pre = reinterpret_cast<int*>(smem + g.tab_off);                     // [6][16]
-  int64_t* tab_c0 = reinterpret_cast<int64_t*>(smem + g.tab_off + kSec * 64);  // [6][16]
   const uint32_t tileb = sb + g.tile_off;
 
   const int r = lane & 15, j = lane >> 4;
@@ -391,46 +388,70 @@ __global__ void __launch_bounds__(64) k_exact_staged(SpecViewC1 sv, VerifViewC1 
                                  sv.codes_limit / 4,   vv.codes_limit / 4};  // in chunks
   v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
 
-  // kept-before and code starts at a stage's block boundaries (i = 0..Wb),
-  // loaded one stage ahead
-  struct Meta {
-    int64_t kbv[3], bos[3], bov[3];
+  // kept-before and code offsets at a stage's block boundaries (i = 0..Wb),
+  // loaded one stage ahead as plain words (indices clamped, so the loads are
+  // unconditional and nothing waits for them until the next stage)
+  struct MetaRaw {
+    uint32_t kb[3], bs[3], bv[3];
   };
   auto load_meta = [&](int64_t stg) {
-    Meta md;
+    MetaRaw mr;
     const int64_t bf = stg * g.Wb;
-    const int64_t be = std::min<int64_t>(bf + g.Wb, nb);
-    const int nbs = (int)(be - bf);
 #pragma unroll
     for (int i = 0; i < 3; ++i) {
-      const int64_t bb = bf + i;
-      if (i > nbs) {
-        md.kbv[i] = md.kbv[i - 1];
-        md.bos[i] = md.bos[i - 1];
-        md.bov[i] = md.bov[i - 1];
-      } else if (bb < nb) {
-        md.kbv[i] = sv.keptb[rowc * nb + bb];
-        md.bos[i] = rbs + sv.blkoff[rowc * nb + bb];
-        md.bov[i] = rbv + vv.blkoff[rowc * nb + bb];
-      } else {
-        md.kbv[i] = k;
-        md.bos[i] = rbs_next;
-        md.bov[i] = rbv_next;
+      const int64_t bb = std::min<int64_t>(bf + i, nb - 1);
+      mr.kb[i] = sv.keptb[rowc * nb + bb];
+      mr.bs[i] = sv.blkoff[rowc * nb + bb];
+      mr.bv[i] = vv.blkoff[rowc * nb + bb];
+    }
+    return mr;
+  };
+  // the current stage's words sit in shared memory: written at the end of the
+  // previous stage (so their loads have had the whole decode to land)
+  uint32_t* meta_s = reinterpret_cast<uint32_t*>(smem + g.meta_off);  // [16][9]
+  auto put_meta = [&](const MetaRaw& mr) {
+    if (j == 0) {
+#pragma unroll
+      for (int i = 0; i < 3; ++i) {
+        meta_s[r * 9 + i] = mr.kb[i];
+        meta_s[r * 9 + 3 + i] = mr.bs[i];
+        meta_s[r * 9 + 6 + i] = mr.bv[i];
       }
     }
-    return md;
   };
-  Meta md_next{};
-  if (st0 < st1) md_next = load_meta(st0);
+  if (st0 < st1) put_meta(load_meta(st0));
+  wsync();
 
   for (int64_t st = st0; st < st1; ++st) {
     const int64_t bf = st * g.Wb;
     const int64_t be = std::min<int64_t>(bf + g.Wb, nb);
     const int nbs = (int)(be - bf);  // 1 or 2
-    const Meta md = md_next;
-    const int64_t* kbv = md.kbv;
-    const int64_t* bos = md.bos;
-    const int64_t* bov = md.bov;
+    int64_t kbv[3], bos[3], bov[3];
+    {
+      MetaRaw mr;
+#pragma unroll
+      for (int i = 0; i < 3; ++i) {
+        mr.kb[i] = meta_s[r * 9 + i];
+        mr.bs[i] = meta_s[r * 9 + 3 + i];
+        mr.bv[i] = meta_s[r * 9 + 6 + i];
+      }
+#pragma unroll
+      for (int i = 0; i < 3; ++i) {
+        if (i > nbs) {
+          kbv[i] = kbv[i - 1];
+          bos[i] = bos[i - 1];
+          bov[i] = bov[i - 1];
+        } else if (bf + i < nb) {
+          kbv[i] = mr.kb[i];
+          bos[i] = rbs + mr.bs[i];
+          bov[i] = rbv + mr.bv[i];
+        } else {
+          kbv[i] = k;
+          bos[i] = rbs_next;
+          bov[i] = rbv_next;
+        }
+      }
+    }
     const int64_t kbe = nbs > 1 ? kbv[2] : kbv[1];
     const int64_t bose = nbs > 1 ? bos[2] : bos[1];
     const int64_t bove = nbs > 1 ? bov[2] : bov[1];
@@ -451,6 +472,8 @@ __global__ void __launch_bounds__(64) k_exact_staged(SpecViewC1 sv, VerifViewC1 
     // ---- staging: per section, the 16 row runs packed back to back
     int64_t bias[kSec];
     int nsec[kSec];
+    int inc_l[kSec];      // this lane's row: inclusive packed chunk count
+    int64_t d_l[kSec];    // and first source chunk - first packed chunk
     int foff = 0, coff = 0;
     bool overflow = false;
 #pragma unroll
@@ -459,7 +482,7 @@ __global__ void __launch_bounds__(64) k_exact_staged(SpecViewC1 sv, VerifViewC1 
       int64_t c1 = (hi[sec] + 127) >> 7;
       if (c1 > sec_lim[sec]) c1 = sec_lim[sec];
       const int n = (row_ok && hi[sec] > lo[sec] && c1 > c0) ? (int)(c1 - c0) : 0;
-      const int incl = scan16(n, lane);
+      const int incl = scan16(n);
       const int pre = incl - n;
       const int N = __builtin_amdgcn_readlane(incl, 15);
       int off;
@@ -473,29 +496,36 @@ __global__ void __launch_bounds__(64) k_exact_staged(SpecViewC1 sv, VerifViewC1 
       }
       nsec[sec] = (sec < 4 || !overflow) ? N : 0;
       bias[sec] = (int64_t)(off + 16 * pre) * 8 - c0 * 128;
-      if (j == 0) {
-        tab_pre[sec * 16 + r] = pre;
-        tab_c0[sec * 16 + r] = c0;
-      }
+      inc_l[sec] = incl;
+      d_l[sec] = c0 - pre;
     }
-    wsync();  // the row tables
     {
       int off_f = g.fix_off, off_c = g.cod_off;
 #pragma unroll
       for (int sec = 0; sec < kSec; ++sec) {
         const int N = nsec[sec];
         const int off = sec < 4 ? off_f : off_c;
-        for (int base = 0; base < N; base += 64) {
-          const int c = base + lane;
-          if (c < N) {
-            // the row whose run holds packed chunk c: the last row starting at or before it
-            int rr = 0;
+        if (N > 0) {
+          // the section's row table in scalars (lanes 0..15 hold rows 0..15)
+          int inc[16];
+          int64_t dd[16];
 #pragma unroll
-            for (int step = 8; step >= 1; step >>= 1)
-              if (tab_pre[sec * 16 + rr + step] <= c) rr += step;
-            const int64_t src = tab_c0[sec * 16 + rr] + (c - tab_pre[sec * 16 + rr]);
-            __builtin_amdgcn_global_load_lds((const void*)(sec_base[sec] + 16 * src),
-                                             (lds_void*)(smem + off + 16 * base), 16, 0, 2);
+          for (int q = 0; q < 16; ++q) {
+            inc[q] = __builtin_amdgcn_readlane(inc_l[sec], q);
+            const uint32_t dlo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)d_l[sec], q);
+            const uint32_t dhi = (uint32_t)__builtin_amdgcn_readlane((int)(d_l[sec] >> 32), q);
+            dd[q] = (int64_t)(((uint64_t)dhi << 32) | dlo);
+          }
+          for (int base = 0; base < N; base += 64) {
+            const int c = base + lane;
+            if (c < N) {
+              // row of packed chunk c: past every row whose run ends at or before it
+              int64_t d = dd[0];
+#pragma unroll
+              for (int q = 0; q < 15; ++q) d = inc[q] <= c ? dd[q + 1] : d;
+              __builtin_amdgcn_global_load_lds((const void*)(sec_base[sec] + 16 * (c + d)),
+                                               (lds_void*)(smem + off + 16 * base), 16, 0, 2);
+            }
           }
         }
         if (sec < 4) off_f += 16 * N;
@@ -503,7 +533,9 @@ __global__ void __launch_bounds__(64) k_exact_staged(SpecViewC1 sv, VerifViewC1 
       }
     }
     wait_all();
-    if (st + 1 < st1) md_next = load_meta(st + 1);  // lands while this stage decodes
+    const bool more = st + 1 < st1;
+    MetaRaw mr_next{};
+    if (more) mr_next = load_meta(st + 1);  // lands while this stage decodes
 
     // ---- decode: kept values, then pruned values, into the tile
     const uint32_t bm_row = (uint32_t)(bias[0] + (rowc * nb + bf) * B);  // bitmap bit of column 0
@@ -634,7 +666,9 @@ __global__ void __launch_bounds__(64) k_exact_staged(SpecViewC1 sv, VerifViewC1 
         }
       }
     }
-    wsync();  // every lane is done with the tile and the staged runs
+    wsync();  // every lane is done with the tile, the staged runs and the stage's words
+    if (more) put_meta(mr_next);
+    wsync();
   }
 
   if (MODE == 0) {
@@ -690,8 +724,8 @@ XGeom make_xgeom(const Shape& sh, const SpecViewC1& sv, const VerifViewC1& vv) {
   o += a16(fw <= 5 ? (int64_t)(32 << fw) * 2 : 64);
   g.plut_off = (int)o;
   o += 128;
-  g.tab_off = (int)o;
-  o += kSec * 64 + kSec * 128;
+  g.meta_off = (int)o;
+  o += kRows * 9 * 4;
   g.dummy_off = (int)o;
   o += 256;
   g.tile_off = (int)o;
