@@ -17,7 +17,8 @@ context (append latency, draft and verification attention), the Qwen3-4B
 Cassandra-2 stack at batch 2 with its 128K-token Cassandra-2 KV cache, and the
 CPU oracle timed on a row sample.
 
-Modes for profiling: --mode gemv runs only the timed GEMV steps; --mode copy
+Modes for profiling: --mode gemv runs only the timed GEMV steps; --mode exact
+runs the verification GEMM (N = 5) and the reconstruction of each matrix; --mode copy
 runs a plain 1 GiB device copy (to calibrate the HBM byte counters).
 """
 from __future__ import annotations
@@ -46,7 +47,7 @@ def parse():
     ap.add_argument("--mant", type=int, default=3)
     ap.add_argument("--block", type=int, default=256)
     ap.add_argument("--copies", type=int, default=8)
-    ap.add_argument("--mode", choices=("full", "gemv", "copy"), default="full")
+    ap.add_argument("--mode", choices=("full", "gemv", "exact", "copy"), default="full")
     ap.add_argument("--no-extras", action="store_true", help="headline and CPU baseline only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -140,6 +141,22 @@ def main():
     n_copies = len(encs)
     torch.cuda.synchronize()
     log(f"encoded {len(encs)} layers")
+
+    if args.mode == "exact":
+        # verification GEMM (N = 5) and exact reconstruction of each matrix, steps rotating copies
+        X5 = {n: dev16(synth.activations(5, layer0[n].shape[1], 2, t0=10 + i))
+              for i, n in enumerate(MATS)}
+        Y5 = {n: torch.empty((5, layer0[n].shape[0]), dtype=torch.float32, device="cuda") for n in MATS}
+        outb = {n: torch.empty_like(layers[0][n]) for n in MATS}
+        for i in range(args.warmup + args.steps):
+            e = encs[i % len(encs)]
+            for n in MATS:
+                cass.cass_verify_gemm(e[n].desc, X5[n], Y5[n], stream)
+            for n in MATS:
+                cass.cass_reconstruct(e[n].desc, outb[n], stream)
+        torch.cuda.synchronize()
+        print(json.dumps({"mode": "exact", "steps": args.steps}))
+        return
 
     xs = {n: dev16(synth.activations(1, layer0[n].shape[1], 2, t0=i)) for i, n in enumerate(MATS)}
     ys = {n: torch.empty((1, layer0[n].shape[0]), dtype=torch.float32, device="cuda") for n in MATS}
