@@ -529,9 +529,16 @@ int cass_draft_decode(const cass_tensor* W, uint16_t* out, hipStream_t stream) {
   if (W->rows == 0) return CASS_OK;
   if (!out || ((uintptr_t)out % 16)) return fail(CASS_ERR_INVALID, "out must be 16-byte aligned");
   const Shape sh = shape_of(W);
-  hipError_t e = W->format == CASS_FMT_C1_UNARY
-                     ? launch_decode_c1(spec_c1(W), nullptr, sh, out, stream)
-                     : launch_decode_c2(spec_c2(W), nullptr, sh, out, stream);
+  hipError_t e;
+  if (W->format == CASS_FMT_C1_UNARY) {
+    const SpecViewC1 sv = spec_c1(W);
+    const VerifViewC1 none = {};
+    e = staged_exact_enabled() && exact_staged_fits(sh, sv, none)
+            ? launch_draft_decode_c1_staged(sv, sh, out, stream)
+            : launch_decode_c1(sv, nullptr, sh, out, stream);
+  } else {
+    e = launch_decode_c2(spec_c2(W), nullptr, sh, out, stream);
+  }
   return e == hipSuccess ? CASS_OK : hip_fail(e, "draft decode launch");
 }
 

@@ -143,11 +143,13 @@ __device__ __forceinline__ PRaw praw(uint32_t sb, uint32_t bp, uint32_t yp, uint
 // has finished its part.
 //   torg   LDS byte address of the lane's tile row minus 2 * the bitmap bit of
 //          its column 0 (a value at bitmap bit b goes to torg + 2 b)
+//   lw     shift of the mantissa field's low end (7 - m); lwid the width of the
+//          low-mantissa field read (7 - m, or 0 for the zero-filled draft)
 template <int U, bool KLUT, bool MASKED>
 __device__ __forceinline__ void kept_group(KRaw& w, uint32_t& bp, uint32_t& fp, uint32_t& lp,
                                            uint32_t& cp, uint32_t sb, uint32_t torg,
                                            uint32_t klutb, uint32_t dummy, int fw, int lw,
-                                           int m, int t) {
+                                           int lwid, int m, int t) {
   const uint32_t sbit = bp & 31u;
   const uint32_t lo0 = __builtin_amdgcn_alignbit(w.q1, w.q0, sbit);
   const uint32_t hi0 = __builtin_amdgcn_alignbit(w.q2, w.q1, sbit) | (MASKED ? 0x80000000u : 0u);
@@ -168,7 +170,7 @@ __device__ __forceinline__ void kept_group(KRaw& w, uint32_t& bp, uint32_t& fp, 
     const uint32_t r = (uint32_t)__builtin_ctz(MASKED ? wc | 0x80000000u : wc);
     wc = (wc >> r) >> 1;
     const uint32_t f = __builtin_amdgcn_ubfe(wf, (uint32_t)(u * fw), (uint32_t)fw);
-    low[u] = __builtin_amdgcn_ubfe(wl, (uint32_t)(u * lw), (uint32_t)lw);
+    low[u] = __builtin_amdgcn_ubfe(wl, (uint32_t)(u * lwid), (uint32_t)lwid);
     fv[u] = f;
     la[u] = KLUT ? klutb + 2u * ((r << fw) | f) : klutb + 2u * r;
     const uint32_t a = torg + 2u * (base + p);
@@ -178,7 +180,7 @@ __device__ __forceinline__ void kept_group(KRaw& w, uint32_t& bp, uint32_t& fp, 
     const bool go = !MASKED || t == U;
     bp = go ? base + p + 1u : bp;
     fp = go ? fp + (uint32_t)(U * fw) : fp;
-    lp = go ? lp + (uint32_t)(U * lw) : lp;
+    lp = go ? lp + (uint32_t)(U * lwid) : lp;
     // bits the U codes took: the window was shifted right by that many
     const uint32_t c0 = (uint32_t)__builtin_clz(wc0);
     const uint32_t cn = cp + (wc ? (uint32_t)__builtin_clz(wc) : 32u) - c0;
@@ -261,7 +263,7 @@ __device__ __forceinline__ void pruned_group(PRaw& w, uint32_t& bp, uint32_t& yp
 __device__ __forceinline__ void kept_step(uint32_t sb, uint32_t& bp, uint32_t bp_end,
                                           uint32_t& fp, uint32_t& lp, uint32_t& cp,
                                           const uint32_t* cg, uint32_t torg, const uint8_t* ps,
-                                          int fw, int lw, int m) {
+                                          int fw, int lw, int lwid, int m) {
   uint32_t w = lwin(sb, bp);
   // a valid part has its next value inside the row's stage; the bound only
   // keeps a corrupt stream from spinning
@@ -273,8 +275,8 @@ __device__ __forceinline__ void kept_step(uint32_t sb, uint32_t& bp, uint32_t bp
   bp = pos + 1u;
   const uint32_t f = lwin(sb, fp) & ((1u << fw) - 1u);
   fp += (uint32_t)fw;
-  const uint32_t low = lw ? (lwin(sb, lp) & ((1u << lw) - 1u)) : 0u;
-  lp += (uint32_t)lw;
+  const uint32_t low = lwid ? (lwin(sb, lp) & ((1u << lwid) - 1u)) : 0u;
+  lp += (uint32_t)lwid;
   const int r = cg ? unary_at(cg, cp) : lunary(sb, cp);
   const uint32_t e = ps[r];
   sth(torg + 2u * pos, ((f >> m) << 15) | (e << 7) | ((f & ((1u << m) - 1u)) << lw) | low);
@@ -332,7 +334,9 @@ __device__ __forceinline__ uint32_t find_in_block(uint32_t wa, int nwb, int skip
   return (uint32_t)(wsel * 32 + select_bit(wd, rem + 1));
 }
 
-template <int MODE, int KU, bool KLUT>  // MODE 0: verification GEMM into Y, 1: reconstruction
+// MODE 0: verification GEMM into Y; 1: reconstruction; 2: zero-filled draft
+// (speculation stream only: vv is not read)
+template <int MODE, int KU, bool KLUT>
 __global__ void __launch_bounds__(64) k_exact_staged(SpecViewC1 sv, VerifViewC1 vv, Shape sh,
                                                      XGeom g, const uint16_t* __restrict__ X,
                                                      int ntok, int64_t ldx,
@@ -343,6 +347,7 @@ __global__ void __launch_bounds__(64) k_exact_staged(SpecViewC1 sv, VerifViewC1 
   const int64_t R = sh.rows, C = sh.cols, k = sh.keep, B = sh.block, nb = C / B;
   const int m = sh.mant, fw = 1 + m, lw = 7 - m;
   const int nwb = (int)(B / 32);
+  const int lwid = MODE == 2 ? 0 : lw;
   const uint32_t sb = lds_addr_of(smem);
   const uint32_t* sm32 = reinterpret_cast<const uint32_t*>(smem);
 
@@ -353,7 +358,7 @@ __global__ void __launch_bounds__(64) k_exact_staged(SpecViewC1 sv, VerifViewC1 
   uint16_t* plut = reinterpret_cast<uint16_t*>(smem + g.plut_off);
   for (int i = lane; i < 256; i += 64) {
     ps[i] = sv.perm[i];
-    pv[i] = vv.perm[i];
+    pv[i] = MODE == 2 ? 0 : vv.perm[i];
   }
   if (KLUT) {
     for (int i = lane; i < (32 << fw); i += 64) {
@@ -364,7 +369,8 @@ __global__ void __launch_bounds__(64) k_exact_staged(SpecViewC1 sv, VerifViewC1 
   } else if (lane < 32) {
     klut[lane] = (uint16_t)((uint32_t)sv.perm[lane] << 7);
   }
-  plut[lane] = (uint16_t)(((uint32_t)(lane & 1) << 15) | ((uint32_t)vv.perm[lane >> 1] << 7));
+  if (MODE != 2)
+    plut[lane] = (uint16_t)(((uint32_t)(lane & 1) << 15) | ((uint32_t)vv.perm[lane >> 1] << 7));
   const uint32_t klutb = sb + g.klut_off, plutb = sb + g.plut_off;
   const uint32_t dummy = sb + g.dummy_off + 4u * lane;
   const uint32_t tileb = sb + g.tile_off;
@@ -376,9 +382,11 @@ __global__ void __launch_bounds__(64) k_exact_staged(SpecViewC1 sv, VerifViewC1 
   const int64_t rowc = row_ok ? row : R - 1;  // clamped for loads
   const int64_t st0 = (int64_t)blockIdx.y * g.stages_per_split;
   const int64_t st1 = std::min<int64_t>(st0 + g.stages_per_split, g.nstage);
-  const int64_t rbs = (int64_t)sv.rowbase[rowc], rbv = (int64_t)vv.rowbase[rowc];
+  const int64_t rbs = (int64_t)sv.rowbase[rowc];
+  const int64_t rbv = MODE == 2 ? 0 : (int64_t)vv.rowbase[rowc];
   const int64_t rbs_next = rowc + 1 < R ? (int64_t)sv.rowbase[rowc + 1] : sv.codes_limit * 32;
-  const int64_t rbv_next = rowc + 1 < R ? (int64_t)vv.rowbase[rowc + 1] : vv.codes_limit * 32;
+  const int64_t rbv_next =
+      MODE == 2 ? 0 : (rowc + 1 < R ? (int64_t)vv.rowbase[rowc + 1] : vv.codes_limit * 32);
   const uint8_t* sec_base[kSec] = {
       reinterpret_cast<const uint8_t*>(sv.bitmap), reinterpret_cast<const uint8_t*>(sv.fields),
       reinterpret_cast<const uint8_t*>(vv.lowmant), vv.pruned,
@@ -402,7 +410,7 @@ __global__ void __launch_bounds__(64) k_exact_staged(SpecViewC1 sv, VerifViewC1 
       const int64_t bb = std::min<int64_t>(bf + i, nb - 1);
       mr.kb[i] = sv.keptb[rowc * nb + bb];
       mr.bs[i] = sv.blkoff[rowc * nb + bb];
-      mr.bv[i] = vv.blkoff[rowc * nb + bb];
+      mr.bv[i] = MODE == 2 ? 0u : vv.blkoff[rowc * nb + bb];
     }
     return mr;
   };
@@ -481,7 +489,9 @@ __global__ void __launch_bounds__(64) k_exact_staged(SpecViewC1 sv, VerifViewC1 
       const int64_t c0 = lo[sec] >> 7;
       int64_t c1 = (hi[sec] + 127) >> 7;
       if (c1 > sec_lim[sec]) c1 = sec_lim[sec];
-      const int n = (row_ok && hi[sec] > lo[sec] && c1 > c0) ? (int)(c1 - c0) : 0;
+      // (the draft stages the speculation sections only)
+      const bool used = MODE != 2 || sec == 0 || sec == 1 || sec == 4;
+      const int n = (used && row_ok && hi[sec] > lo[sec] && c1 > c0) ? (int)(c1 - c0) : 0;
       const int incl = scan16(n);
       const int pre = incl - n;
       const int N = __builtin_amdgcn_readlane(incl, 15);
@@ -541,6 +551,14 @@ __global__ void __launch_bounds__(64) k_exact_staged(SpecViewC1 sv, VerifViewC1 
     const uint32_t bm_row = (uint32_t)(bias[0] + (rowc * nb + bf) * B);  // bitmap bit of column 0
     const uint32_t torg = tileb + 2u * (uint32_t)(r * g.TS) - 2u * bm_row;
     const uint32_t bm_end = bm_row + (uint32_t)(nbs * B);
+    if (MODE == 2) {
+      // zero-filled draft: clear the stage's columns of every row, then the
+      // kept pass writes its values over them
+      if (row_ok)
+        for (int w = j; w < nbs * (int)B / 2; w += 4)
+          *(__attribute__((address_space(3))) uint32_t*)(uintptr_t)(tileb + 4u * (uint32_t)(r * (g.TS / 2) + w)) = 0u;
+      wsync();
+    }
     {
       const int64_t K = kbe - kbv[0];
       const int64_t i0 = (K * j) >> 2;
@@ -575,22 +593,24 @@ __global__ void __launch_bounds__(64) k_exact_staged(SpecViewC1 sv, VerifViewC1 
           const int ncode = __builtin_popcount(__builtin_amdgcn_alignbit(w.c1, w.c0, cp & 31u));
           const bool ok = min(have, ncode) >= t;
           if (__all(t == KU && ok)) {
-            kept_group<KU, KLUT, false>(w, bp, fp, lp, cp, sb, torg, klutb, dummy, fw, lw, m, KU);
+            kept_group<KU, KLUT, false>(w, bp, fp, lp, cp, sb, torg, klutb, dummy, fw, lw, lwid, m,
+                                        KU);
           } else if (__all(ok)) {
             // some part ends inside this group
-            kept_group<KU, KLUT, true>(w, bp, fp, lp, cp, sb, torg, klutb, dummy, fw, lw, m, t);
+            kept_group<KU, KLUT, true>(w, bp, fp, lp, cp, sb, torg, klutb, dummy, fw, lw, lwid, m,
+                                       t);
           } else {
             for (int u = 0; u < KU; ++u)
-              if (u < t) kept_step(sb, bp, bm_end, fp, lp, cp, nullptr, torg, ps, fw, lw, m);
+              if (u < t) kept_step(sb, bp, bm_end, fp, lp, cp, nullptr, torg, ps, fw, lw, lwid, m);
             w = kraw(sb, bp, fp, lp, cp);
           }
         }
       } else {
         for (int i = 0; i < nmax; ++i)
-          if (i < n) kept_step(sb, bp, bm_end, fp, lp, cp, cg, torg, ps, fw, lw, m);
+          if (i < n) kept_step(sb, bp, bm_end, fp, lp, cp, cg, torg, ps, fw, lw, lwid, m);
       }
     }
-    {
+    if (MODE != 2) {
       const int64_t P = (int64_t)nbs * B - (kbe - kbv[0]);
       const int64_t i0 = (P * j) >> 2;
       const int n = row_ok ? (int)(((P * (j + 1)) >> 2) - i0) : 0;
@@ -801,6 +821,13 @@ hipError_t launch_reconstruct_c1_staged(const SpecViewC1& sv, const VerifViewC1&
                                         const Shape& sh, uint16_t* out, hipStream_t s) {
   if (sh.rows == 0) return hipSuccess;
   return launch_staged<1>(sv, vv, sh, nullptr, 0, 0, nullptr, 0, out, s);
+}
+
+hipError_t launch_draft_decode_c1_staged(const SpecViewC1& sv, const Shape& sh, uint16_t* out,
+                                         hipStream_t s) {
+  if (sh.rows == 0) return hipSuccess;
+  const VerifViewC1 none = {};
+  return launch_staged<2>(sv, none, sh, nullptr, 0, 0, nullptr, 0, out, s);
 }
 
 }  // namespace cass

@@ -150,6 +150,8 @@ hipError_t launch_verify_gemm_c1_staged(const SpecViewC1& sv, const VerifViewC1&
                                         int64_t ldx, float* Y, int64_t ldy, hipStream_t s);
 hipError_t launch_reconstruct_c1_staged(const SpecViewC1& sv, const VerifViewC1& vv,
                                         const Shape& sh, uint16_t* out, hipStream_t s);
+hipError_t launch_draft_decode_c1_staged(const SpecViewC1& sv, const Shape& sh, uint16_t* out,
+                                         hipStream_t s);
 hipError_t launch_verify_gemm_c2(const SpecViewC2& sv, const VerifViewC2& vv, const Shape& sh,
                                  const uint16_t* X, int ntok, int64_t ldx, float* Y,
                                  int64_t ldy, hipStream_t s);

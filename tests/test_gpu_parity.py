@@ -172,9 +172,9 @@ EXACT_CASES = [
 
 @pytest.mark.parametrize("path", ["default", "blocks1", "blocks2", "direct"])
 def test_exact_paths(gpu, orc, monkeypatch, path):
-    """Reconstruction and verification GEMM (Cassandra-1) through each exact
-    decoder: the staged kernel with its default stage width, with stages of
-    one or two blocks (CASS_EXACT_BLOCKS), and the per-thread stream readers
+    """Reconstruction, draft decode and verification GEMM (Cassandra-1) through
+    each decoder: the staged kernel with its default stage width, with stages
+    of one or two blocks (CASS_EXACT_BLOCKS), and the per-thread stream readers
     (CASS_EXACT_PATH=direct)."""
     torch, cass = gpu
     if path == "blocks1":
@@ -193,6 +193,9 @@ def test_exact_paths(gpu, orc, monkeypatch, path):
         cass.cass_reconstruct(enc.desc, out)
         torch.cuda.synchronize()
         assert np.array_equal(host_u16(out), w), case
+        cass.cass_draft_decode(enc.desc, out)
+        torch.cuda.synchronize()
+        assert np.array_equal(host_u16(out), orc.draft_decode(spec_o)), case
         X = synth.activations(5, C, 3, t0=R)
         Y = torch.full((5, R), float("nan"), dtype=torch.float32, device="cuda")
         cass.cass_verify_gemm(enc.desc, dev(torch, X), Y)
