@@ -178,7 +178,7 @@ SpecViewC2 spec_c2(const cass_tensor* W) {
   return SpecViewC2{(const uint32_t*)(b + o[S2_BITMAP]), b + o[S2_SHEXP],
                     (const uint16_t*)(b + o[S2_KEPTB]), (const uint32_t*)(b + o[S2_FIELDS]),
                     word_limit(W->spec_bytes, o[S2_BITMAP]), word_limit(W->spec_bytes, o[S2_SHEXP]),
-                    word_limit(W->spec_bytes, o[S2_FIELDS])};
+                    word_limit(W->spec_bytes, o[S2_FIELDS]), 2 * word_limit(W->spec_bytes, o[S2_KEPTB])};
 }
 VerifViewC2 verif_c2(const cass_tensor* W) {
   const uint8_t* b = (const uint8_t*)W->verif;

@@ -542,6 +542,327 @@ __global__ void __launch_bounds__(kBalThreads) k_gemv_c1_bal(SpecViewC1 v, Shape
   }
 }
 
+
+// ---- Cassandra-2: no exponent codes; the exponent of a kept value is the
+// shared exponent of its 32-position group (one byte per bitmap word).  A
+// value is ldexp(+-a, E - 127 - m) for its (m+2)-bit field (sign, aligned
+// significand a): a table gives +-a as fp32, v_ldexp_f32 the scaling (exact,
+// subnormal results included).  Same work split, staging and three-phase
+// groups as the Cassandra-1 kernel; a part's start needs no code search.
+// (Method: Cassandra review, section 3.2, Cassandra-2; OCP MX specification.)
+
+struct C2Raw {
+  uint32_t q0, q1, q2, f0, f1;
+};
+__device__ __forceinline__ C2Raw c2raw(const uint32_t* bm_l, const uint32_t* f_l, uint32_t bp,
+                                       uint32_t fp) {
+  const uint32_t* qb = bm_l + (bp >> 5);
+  const uint32_t* qf = f_l + (fp >> 5);
+  return C2Raw{qb[0], qb[1], qb[2], qf[0], qf[1]};
+}
+
+typedef __attribute__((address_space(3))) const uint8_t lds_u8v;
+
+// U values from the windows in w.  MASKED: slots u >= t add nothing (the
+// part's last group; bit 63 of the keep window set keeps their reads in range).
+//   eorg  LDS byte address of the shared exponent of staged bitmap word 0
+template <int BATCH, int U, bool MASKED>
+__device__ __forceinline__ void c2_group(C2Raw& w, uint32_t& bp, uint32_t& fp,
+                                         const uint32_t* bm_l, const uint32_t* f_l,
+                                         uint32_t xorg, uint32_t eorg, uint32_t lutb, int fw,
+                                         int ebias, uint32_t xstride, int t, float* acc) {
+  const uint32_t sbit = bp & 31u;
+  const uint32_t lo0 = __builtin_amdgcn_alignbit(w.q1, w.q0, sbit);
+  const uint32_t hi0 = __builtin_amdgcn_alignbit(w.q2, w.q1, sbit) | (MASKED ? 0x80000000u : 0u);
+  const uint32_t wf = __builtin_amdgcn_alignbit(w.f1, w.f0, fp & 31u);
+  uint32_t la[U], xa[U], ea[U];
+  uint32_t lo = lo0, p = 0, base = bp;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const bool z = lo == 0u;
+    lo = z ? hi0 : lo;
+    base = z ? bp + 32u : base;
+    p = (uint32_t)__builtin_ctz(lo);
+    lo &= lo - 1u;
+    const uint32_t pos = base + p;  // staged bitmap bit
+    const uint32_t f = __builtin_amdgcn_ubfe(wf, (uint32_t)(u * fw), (uint32_t)fw);
+    la[u] = lutb + 4u * f;
+    xa[u] = xorg + 2u * pos;
+    ea[u] = eorg + (pos >> 5);
+  }
+  if (!MASKED) {
+    bp = base + p + 1u;
+    fp += (uint32_t)(U * fw);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  float lv[U], xv[BATCH][U];
+  int ev[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    lv[u] = *(lds_f32*)(uintptr_t)la[u];
+    ev[u] = *(lds_u8v*)(uintptr_t)ea[u];
+#pragma unroll
+    for (int bb = 0; bb < BATCH; ++bb) xv[bb][u] = x_at_addr(xa[u] + bb * xstride);
+  }
+  if (!MASKED) w = c2raw(bm_l, f_l, bp, fp);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const float wv = __builtin_amdgcn_ldexpf(lv[u], ev[u] - ebias);
+#pragma unroll
+    for (int bb = 0; bb < BATCH; ++bb) {
+      const float a = __builtin_fmaf(wv, xv[bb][u], acc[bb]);
+      acc[bb] = (MASKED && u >= t) ? acc[bb] : a;
+    }
+  }
+}
+
+// One value at any sparsity: the next kept position at or after bp.
+template <int BATCH>
+__device__ __forceinline__ void c2_step(const uint32_t* bm_l, uint32_t& bp, const uint32_t* f_l,
+                                        uint32_t& fp, uint32_t rowbit, int64_t row_len,
+                                        const float* lut, const uint8_t* eb0, int fw, int ebias,
+                                        const uint8_t* xs, uint32_t xstride, float* acc) {
+  uint32_t w = window32(bm_l, bp);
+  for (uint32_t lim = rowbit + (uint32_t)row_len; w == 0u && bp < lim;) {
+    bp += 32u;
+    w = window32(bm_l, bp);
+  }
+  const uint32_t pos = bp + (uint32_t)__builtin_ctz(w);
+  bp = pos + 1u;
+  const uint32_t f = window32(f_l, fp) & ((1u << fw) - 1u);
+  fp += (uint32_t)fw;
+  const float wv = __builtin_amdgcn_ldexpf(lut[f], (int)eb0[pos >> 5] - ebias);
+  const uint32_t xa = 2u * (pos - rowbit);
+#pragma unroll
+  for (int bb = 0; bb < BATCH; ++bb)
+    acc[bb] = __builtin_fmaf(wv, x_at(xs, xa + bb * xstride), acc[bb]);
+}
+
+template <int BATCH, int U>
+__global__ void __launch_bounds__(kBalThreads) k_gemv_c2_bal(SpecViewC2 v, Shape sh, BalGeom g,
+                                                             const uint16_t* __restrict__ x,
+                                                             int64_t ldx, float* __restrict__ y,
+                                                             int64_t ldy) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  const int64_t R = sh.rows, C = sh.cols, k = sh.keep;
+  const int B = (int)sh.block, nb = (int)(C / B), nwb = B / 32;
+  const int m = sh.mant, fw = 2 + m;
+  const int ebias = 127 + m;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  float* lut = reinterpret_cast<float*>(smem + g.lut_off);
+  uint8_t* reg = smem + g.wave_off + wave * g.wave_bytes;
+  uint16_t* kb_l = reinterpret_cast<uint16_t*>(reg + g.kb_off);
+  uint32_t* bm_l = reinterpret_cast<uint32_t*>(reg + g.bm_off);
+  uint32_t* f_l = reinterpret_cast<uint32_t*>(reg + g.f_off);
+  uint8_t* e_l = reg + g.c_off;  // shared exponents (one byte per bitmap word)
+
+  const int rl = lane >> g.logP, part = lane & (g.P - 1);
+  const int n_min = (int)(k >> g.logP);
+  const int n_max = (int)((k + g.P - 1) >> g.logP);
+  const int G = n_min / U;
+  const int n_tail = n_max - G * U;
+  const int64_t wpr = C / 32;
+  const int64_t nwaves = (int64_t)gridDim.x * kBalWaves;
+
+  struct Plan {
+    int64_t row0;
+    int rows_here, kb_sh;
+    int64_t bm_a0, f_a0, e_a0;
+  };
+  auto plan = [&](int64_t round) {
+    Plan pl;
+    pl.row0 = round * g.rpw;
+    pl.rows_here = (int)((R - pl.row0 < g.rpw) ? R - pl.row0 : g.rpw);
+    pl.kb_sh = (int)((pl.row0 * nb) & 7);
+    pl.bm_a0 = (pl.row0 * wpr) & ~(int64_t)3;
+    pl.f_a0 = ((pl.row0 * k * fw) >> 5) & ~(int64_t)3;
+    pl.e_a0 = (pl.row0 * wpr) & ~(int64_t)15;
+    return pl;
+  };
+  auto stage = [&](const Plan& pl) {
+    const int64_t e0 = pl.row0 * nb, e1 = e0 + (int64_t)pl.rows_here * nb;
+    const int64_t kb1 = std::min<int64_t>((e1 + 7) & ~(int64_t)7, v.keptb_limit);
+    dma_run(reinterpret_cast<const u32x4*>(v.keptb + (e0 - pl.kb_sh)),
+            reinterpret_cast<u32x4*>(kb_l), (int)((kb1 - (e0 - pl.kb_sh)) >> 3), lane);
+    const int64_t w1 = (pl.row0 + pl.rows_here) * wpr;
+    const int64_t bm1 = std::min<int64_t>((w1 + 3) & ~(int64_t)3, v.bitmap_limit);
+    dma_run(reinterpret_cast<const u32x4*>(v.bitmap + pl.bm_a0), reinterpret_cast<u32x4*>(bm_l),
+            (int)((bm1 - pl.bm_a0) >> 2), lane);
+    const int64_t fb1 = (pl.row0 + pl.rows_here) * k * fw;
+    const int64_t f1 = std::min<int64_t>((((fb1 + 31) >> 5) + 3) & ~(int64_t)3, v.fields_limit);
+    dma_run(reinterpret_cast<const u32x4*>(v.fields + pl.f_a0), reinterpret_cast<u32x4*>(f_l),
+            (int)((f1 - pl.f_a0) >> 2), lane);
+    const int64_t e1b = std::min<int64_t>((w1 + 15) & ~(int64_t)15, v.shexp_limit * 4);
+    dma_run(reinterpret_cast<const u32x4*>(v.shexp + pl.e_a0), reinterpret_cast<u32x4*>(e_l),
+            (int)((e1b - pl.e_a0) >> 4), lane);
+  };
+  auto locate = [&](const Plan& pl) {
+    Part pt;
+    const int64_t row = pl.row0 + rl;
+    const int i0 = (int)(((int64_t)part * k) >> g.logP);
+    pt.n = rl < pl.rows_here ? (int)((((int64_t)part + 1) * k) >> g.logP) - i0 : 0;
+    pt.rowbit = (uint32_t)((pl.row0 * wpr - pl.bm_a0) * 32 + (int64_t)rl * C);
+    pt.bp = pt.rowbit;
+    pt.fp = 0;
+    pt.cp = 0;
+    pt.cabs = 0;
+    if (pt.n > 0) {
+      const uint16_t* kbr = kb_l + pl.kb_sh + rl * nb;
+      int b = (int)((float)i0 * g.nb_per_k);
+      b = b < 0 ? 0 : (b >= nb ? nb - 1 : b);
+      for (int it = 0; it < nb; ++it) {
+        const int lo = kbr[b], hi = b + 1 < nb ? kbr[b + 1] : (int)k;
+        if (lo > i0 && b > 0) --b;
+        else if (hi <= i0 && b + 1 < nb) ++b;
+        else break;
+      }
+      const int skip = i0 - kbr[b];
+      const uint32_t* bw = bm_l + (pt.rowbit >> 5) + b * nwb;
+      int rem = skip, wsel = nwb - 1;
+      uint32_t wd = 0;
+      if (nwb <= 8) {
+        uint32_t wv[8];
+#pragma unroll
+        for (int w = 0; w < 8; ++w) wv[w] = w < nwb ? bw[w] : 0u;
+        bool found = false;
+#pragma unroll
+        for (int w = 0; w < 8; ++w) {
+          const int c = __builtin_popcount(wv[w]);
+          const bool here = !found && w < nwb && rem < c;
+          wsel = here ? w : wsel;
+          wd = here ? wv[w] : wd;
+          rem -= (!found && !here) ? c : 0;
+          found = found || here;
+        }
+      } else {
+        int wi = 0;
+        wd = bw[0];
+        for (;;) {
+          const int c = __builtin_popcount(wd);
+          if (rem < c || wi == nwb - 1) break;  // (the second test: corrupt streams only)
+          rem -= c;
+          wd = bw[++wi];
+        }
+        wsel = wi;
+      }
+      pt.bp = pt.rowbit + (uint32_t)(b * B + wsel * 32 + select_bit(wd, rem + 1));
+      pt.fp = (uint32_t)((row * k + i0) * fw - pl.f_a0 * 32);
+    }
+    return pt;
+  };
+
+  // ---- first round, x and the +-significand table
+  int64_t round = (int64_t)blockIdx.x * kBalWaves + wave;
+  const bool first = round < g.nrounds;
+  Plan pl{};
+  if (first) {
+    pl = plan(round);
+    stage(pl);
+  }
+  const bool x_dma = (C & 7) == 0 && ((uintptr_t)x & 15) == 0 && (ldx & 7) == 0;
+  for (int bb = 0; bb < BATCH; ++bb) {
+    uint16_t* xr = reinterpret_cast<uint16_t*>(smem + bb * g.xstride);
+    const uint16_t* xg = x + bb * ldx;
+    if (x_dma) {
+      const int nx = (int)(C >> 3);
+      for (int base = wave * 64; base < nx; base += kBalThreads)
+        dma_run(reinterpret_cast<const u32x4*>(xg) + base, reinterpret_cast<u32x4*>(xr) + base,
+                nx - base < 64 ? nx - base : 64, lane);
+    } else {
+      for (int64_t j = threadIdx.x; j < C; j += kBalThreads) xr[j] = xg[j];
+    }
+    if (threadIdx.x < 128) xr[C + threadIdx.x] = 0;
+  }
+  for (int i = threadIdx.x; i < (1 << fw); i += kBalThreads) {
+    const float a = (float)(i & ((1 << (m + 1)) - 1));
+    lut[i] = (i >> (m + 1)) ? -a : a;
+  }
+  wait_dma();
+  Part pt{};
+  if (first) pt = locate(pl);
+  __syncthreads();  // x (every wave's chunks) and the table are in LDS
+  if (!first) return;
+
+  for (;;) {
+    const int64_t next = round + nwaves;
+    const bool more = next < g.nrounds;
+    const bool active = rl < pl.rows_here;
+    const int n = pt.n;
+    uint32_t bp = pt.bp, fp = pt.fp;
+    const uint32_t rowbit = pt.rowbit;
+    const uint8_t* eb0 = e_l + (pl.bm_a0 - pl.e_a0);  // exponent of staged bitmap word 0
+    float acc[BATCH];
+#pragma unroll
+    for (int bb = 0; bb < BATCH; ++bb) acc[bb] = 0.f;
+
+    if (pl.rows_here == g.rpw && n_min > 0) {
+      const uint32_t xorg = lds_addr(smem) - 2u * rowbit;
+      const uint32_t eorg = lds_addr(eb0);
+      const uint32_t lutb = lds_addr(reinterpret_cast<const uint8_t*>(lut));
+      C2Raw w = c2raw(bm_l, f_l, bp, fp);
+      int gi = 0;
+      while (gi < G) {
+        for (; gi < G; ++gi) {
+          const uint32_t sb = bp & 31u;
+          const int have = __builtin_popcount(__builtin_amdgcn_alignbit(w.q1, w.q0, sb)) +
+                           __builtin_popcount(__builtin_amdgcn_alignbit(w.q2, w.q1, sb));
+          if (!__all(have >= U)) break;
+          c2_group<BATCH, U, false>(w, bp, fp, bm_l, f_l, xorg, eorg, lutb, fw, ebias,
+                                    g.xstride, U, acc);
+        }
+        if (gi < G) {
+          for (int u = 0; u < U; ++u)
+            c2_step<BATCH>(bm_l, bp, f_l, fp, rowbit, C, lut, eb0, fw, ebias, smem, g.xstride,
+                           acc);
+          ++gi;
+          w = c2raw(bm_l, f_l, bp, fp);
+        }
+      }
+      if (n_tail > 0) {
+        const int t = n - G * U;
+        const uint32_t sb = bp & 31u;
+        const int have = __builtin_popcount(__builtin_amdgcn_alignbit(w.q1, w.q0, sb)) +
+                         __builtin_popcount(__builtin_amdgcn_alignbit(w.q2, w.q1, sb));
+        if (__all(have >= t)) {
+          c2_group<BATCH, U, true>(w, bp, fp, bm_l, f_l, xorg, eorg, lutb, fw, ebias, g.xstride,
+                                   t, acc);
+        } else {
+          for (int u = 0; u < U; ++u)
+            if (u < t)
+              c2_step<BATCH>(bm_l, bp, f_l, fp, rowbit, C, lut, eb0, fw, ebias, smem, g.xstride,
+                             acc);
+        }
+      }
+    } else {
+      for (int i = 0; i < n_max; ++i)
+        if (i < n)
+          c2_step<BATCH>(bm_l, bp, f_l, fp, rowbit, C, lut, eb0, fw, ebias, smem, g.xstride,
+                         acc);
+    }
+
+    if (n == 0) {
+#pragma unroll
+      for (int bb = 0; bb < BATCH; ++bb) acc[bb] = 0.f;
+    }
+    for (int o = g.P >> 1; o >= 1; o >>= 1) {
+#pragma unroll
+      for (int bb = 0; bb < BATCH; ++bb) acc[bb] += __shfl_xor(acc[bb], o, 64);
+    }
+    if (active && part == 0) {
+#pragma unroll
+      for (int bb = 0; bb < BATCH; ++bb) y[bb * ldy + pl.row0 + rl] = acc[bb];
+    }
+    if (!more) break;
+    wave_sync();  // every lane is done with the staged words before they are replaced
+    pl = plan(next);
+    stage(pl);
+    wait_dma();
+    pt = locate(pl);
+    round = next;
+  }
+}
+
 int a16(int64_t v) { return (int)((v + 15) / 16 * 16); }
 
 int pick_u(const Shape& sh) {
@@ -633,6 +954,79 @@ hipError_t launch_bal_u(const SpecViewC1& v, const Shape& sh, const BalGeom& g, 
   }
 }
 
+
+// LDS plan for Cassandra-2 (the code region holds the shared exponents).
+BalGeom make_bal_geom_c2(const Shape& sh, int batch) {
+  BalGeom g = {};
+  const int64_t R = sh.rows, C = sh.cols, k = sh.keep, nb = C / sh.block;
+  const int fw = 2 + sh.mant;
+  int P = R >= 16384 ? 16 : 32;
+  while (P > 1 && k / P < 16) P /= 2;
+  if (const char* e = getenv("CASS_GEMV_PARTS")) {
+    const int p = atoi(e);
+    if (p >= 1 && p <= 64 && (p & (p - 1)) == 0) P = p;
+  }
+  g.P = P;
+  g.logP = __builtin_ctz(P);
+  g.rpw = 64 / P;
+  g.nrounds = (R + g.rpw - 1) / g.rpw;
+  g.nb_per_k = k > 0 ? (float)nb / (float)k : 0.f;
+  g.xstride = (uint32_t)a16(2 * C + 256);
+  int64_t pos = (int64_t)batch * g.xstride;
+  g.lut_off = (int)pos;
+  pos += a16((int64_t)(1 << fw) * 4);
+  g.wave_off = (int)pos;
+  int64_t w = 0;
+  g.kb_off = (int)w;
+  w += a16((int64_t)g.rpw * nb * 2 + 32);
+  g.bm_off = (int)w;
+  w += a16((g.rpw * C / 32 + 4 + kSlack) * 4);
+  g.f_off = (int)w;
+  w += a16(((g.rpw * k * fw + 31) / 32 + 8 + kSlack) * 4);
+  g.c_off = (int)w;
+  w += a16(g.rpw * C / 32 + 32);  // exponents: one byte per word, a chunk either side
+  g.wave_bytes = (int)w;
+  pos += (int64_t)kBalWaves * w;
+  g.lds_bytes = (fw > 9 || pos > kBalMaxLds) ? (int)(kBalMaxLds + 1) : (int)pos;
+  return g;
+}
+
+template <int BATCH, int U>
+hipError_t launch_bal_c2(const SpecViewC2& v, const Shape& sh, const BalGeom& g,
+                         const uint16_t* x, int64_t ldx, float* y, int64_t ldy, hipStream_t s) {
+  auto kern = k_gemv_c2_bal<BATCH, U>;
+  if (g.lds_bytes > 64 * 1024) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, g.lds_bytes);
+    if (e != hipSuccess) return e;
+  }
+  int occ = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, (const void*)kern, kBalThreads,
+                                                   (size_t)g.lds_bytes) != hipSuccess || occ < 1)
+    occ = 1;
+  int64_t grid = (int64_t)device_cu_count() * occ;
+  const int64_t need = (g.nrounds + kBalWaves - 1) / kBalWaves;
+  if (grid > need) grid = need;
+  if (grid < 1) grid = 1;
+  kern<<<(unsigned)grid, kBalThreads, (size_t)g.lds_bytes, s>>>(v, sh, g, x, ldx, y, ldy);
+  return hipGetLastError();
+}
+
+template <int BATCH>
+hipError_t launch_bal_c2_u(const SpecViewC2& v, const Shape& sh, const BalGeom& g,
+                           const uint16_t* x, int64_t ldx, float* y, int64_t ldy,
+                           hipStream_t s) {
+  // values per group: as many fields as a 32-bit window holds, at most 8
+  const int fw = 2 + sh.mant;
+  const int u = std::min(8, 32 / fw);
+  switch (u) {
+    case 8: return launch_bal_c2<BATCH, 8>(v, sh, g, x, ldx, y, ldy, s);
+    case 6: return launch_bal_c2<BATCH, 6>(v, sh, g, x, ldx, y, ldy, s);
+    case 5: return launch_bal_c2<BATCH, 5>(v, sh, g, x, ldx, y, ldy, s);
+    case 4: return launch_bal_c2<BATCH, 4>(v, sh, g, x, ldx, y, ldy, s);
+    default: return launch_bal_c2<BATCH, 3>(v, sh, g, x, ldx, y, ldy, s);
+  }
+}
 }  // namespace
 
 bool draft_gemv_bal_fits(const Shape& sh, int batch, int64_t code_limit_words) {
@@ -655,6 +1049,29 @@ hipError_t launch_draft_gemv_c1_bal(const SpecViewC1& v, const Shape& sh, const 
     case 6: return launch_bal_u<6>(v, sh, g, U, x, ldx, y, ldy, s);
     case 7: return launch_bal_u<7>(v, sh, g, U, x, ldx, y, ldy, s);
     case 8: return launch_bal_u<8>(v, sh, g, U, x, ldx, y, ldy, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+bool draft_gemv_bal_c2_fits(const Shape& sh, int batch) {
+  return make_bal_geom_c2(sh, batch).lds_bytes <= kBalMaxLds;
+}
+
+hipError_t launch_draft_gemv_c2_bal(const SpecViewC2& v, const Shape& sh, const uint16_t* x,
+                                    int batch, int64_t ldx, float* y, int64_t ldy,
+                                    hipStream_t s) {
+  if (sh.rows == 0) return hipSuccess;
+  const BalGeom g = make_bal_geom_c2(sh, batch);
+  if (g.lds_bytes > kBalMaxLds) return hipErrorInvalidValue;
+  switch (batch) {
+    case 1: return launch_bal_c2_u<1>(v, sh, g, x, ldx, y, ldy, s);
+    case 2: return launch_bal_c2_u<2>(v, sh, g, x, ldx, y, ldy, s);
+    case 3: return launch_bal_c2_u<3>(v, sh, g, x, ldx, y, ldy, s);
+    case 4: return launch_bal_c2_u<4>(v, sh, g, x, ldx, y, ldy, s);
+    case 5: return launch_bal_c2_u<5>(v, sh, g, x, ldx, y, ldy, s);
+    case 6: return launch_bal_c2_u<6>(v, sh, g, x, ldx, y, ldy, s);
+    case 7: return launch_bal_c2_u<7>(v, sh, g, x, ldx, y, ldy, s);
+    case 8: return launch_bal_c2_u<8>(v, sh, g, x, ldx, y, ldy, s);
     default: return hipErrorInvalidValue;
   }
 }

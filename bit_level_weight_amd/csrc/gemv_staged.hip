@@ -374,6 +374,10 @@ hipError_t launch_draft_gemv_c1(const SpecViewC1& v, const Shape& sh, const uint
 hipError_t launch_draft_gemv_c2(const SpecViewC2& v, const Shape& sh, const uint16_t* x,
                                 int batch, int64_t ldx, float* y, int64_t ldy, hipStream_t s) {
   if (sh.rows == 0) return hipSuccess;
+  const char* path = getenv("CASS_GEMV_PATH");
+  const bool want_staged = path && strcmp(path, "staged") == 0;
+  if (!force_direct() && !want_staged && draft_gemv_bal_c2_fits(sh, batch))
+    return launch_draft_gemv_c2_bal(v, sh, x, batch, ldx, y, ldy, s);
   const StagedGeom g = make_geom(sh, batch, CASS_FMT_C2_MX32, 0);
   if (g.lds_bytes > kMaxLds || force_direct())
     return launch_draft_gemv_c2_direct(v, sh, x, batch, ldx, y, ldy, s);

@@ -84,6 +84,7 @@ struct SpecViewC2 {
   const uint16_t* keptb;
   const uint32_t* fields;
   int64_t bitmap_limit, shexp_limit, fields_limit;  // as in SpecViewC1 (shexp: bytes/4)
+  int64_t keptb_limit;  // (16-bit entries)
 };
 struct VerifViewC2 {
   const uint8_t* perm;
@@ -132,6 +133,10 @@ hipError_t launch_draft_gemv_c2_direct(const SpecViewC2& v, const Shape& sh, con
 int64_t draft_gemv_direct_lds_bytes(const Shape& sh, int batch);
 // Balanced kernel (Cassandra-1): equal kept-value parts per lane.
 bool draft_gemv_bal_fits(const Shape& sh, int batch, int64_t code_limit_words);
+bool draft_gemv_bal_c2_fits(const Shape& sh, int batch);
+hipError_t launch_draft_gemv_c2_bal(const SpecViewC2& v, const Shape& sh, const uint16_t* x,
+                                    int batch, int64_t ldx, float* y, int64_t ldy,
+                                    hipStream_t s);
 hipError_t launch_draft_gemv_c1_bal(const SpecViewC1& v, const Shape& sh, const uint16_t* x,
                                     int batch, int64_t ldx, float* y, int64_t ldy,
                                     hipStream_t s);

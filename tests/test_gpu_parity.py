@@ -236,6 +236,39 @@ BAL_CASES = [
 ]
 
 
+BAL_C2_CASES = [
+    # rows, cols, keep, mant, block, parts (CASS_GEMV_PARTS; 0 = default), weights
+    (64, 2560, 768, 3, 256, 0, "normal"),     # Qwen3-4B width, 6 fields per group
+    (67, 4096, 819, 3, 256, 0, "normal"),     # ragged last round
+    (33, 2048, 1024, 0, 128, 64, "normal"),   # sign-only significand: 8 per group
+    (40, 1024, 307, 7, 32, 1, "normal"),      # 9-bit fields: 3 per group, one lane per row
+    (20, 512, 30, 3, 256, 64, "normal"),      # k < parts
+    (64, 4096, 1229, 3, 256, 16, "wide"),     # wide exponents (large shared-exponent offsets)
+    (8, 1024, 1024, 5, 256, 0, "normal"),     # keep everything
+]
+
+
+@pytest.mark.parametrize("case", BAL_C2_CASES, ids=[str(c) for c in BAL_C2_CASES])
+def test_balanced_gemv_c2(gpu, orc, monkeypatch, case):
+    """The balanced draft GEMV for Cassandra-2 (shared exponent per 32
+    positions) across part counts, mantissa widths and batches."""
+    torch, cass = gpu
+    R, C, k, m, B, parts, kind = case
+    print("case", case, flush=True)
+    w = bal_weights(R, C, kind, 2000 + R + k)
+    spec_o, _ = orc.encode(w, k, m, block=B, fmt=2)
+    enc = cass.encode(dev(torch, w), k, m, block=B, fmt=2)
+    if parts:
+        monkeypatch.setenv("CASS_GEMV_PARTS", str(parts))
+    for batch in (1, 2, 3):
+        x = synth.activations(batch, C, 7, t0=batch)
+        y = torch.full((batch, R), float("nan"), dtype=torch.float32, device="cuda")
+        cass.cass_draft_gemv(enc.desc, dev(torch, x), y)
+        torch.cuda.synchronize()
+        y_ref, absy = orc.product(spec_o, x, threads=4)
+        check_product(y.cpu().numpy(), y_ref, absy)
+
+
 def bal_weights(R, C, kind, seed):
     if kind == "normal":
         return make_w(R, C, seed)
