@@ -205,6 +205,9 @@ def main():
             alg_bytes += e.spec_bytes + 2 * e.cols + 4 * e.rows
     sum_ms = sum(sum(v) for v in kern_ms.values())
     n_launch = args.steps * len(MATS)
+    layer_ms = [sum(kern_ms[n][i] for n in MATS) for i in range(args.steps)]
+    step_pct = {f"p{q}": round(float(np.percentile(layer_ms, q)) * 1e3, 2) for q in (10, 50, 90)}
+    ceiling = read_ceiling(torch, stream)
     avg_launch_ms = sum_ms / n_launch
     achieved = alg_bytes / n_launch / (avg_launch_ms * 1e-3) / 1e9
     per_matrix = {n: {"spec_MB": round(spec_bytes[n] / 1e6, 3),
@@ -219,9 +222,10 @@ def main():
         extras = run_extras(args, torch, cass, synth, timer, stream, layers, encs, layer0,
                             encode_layer, xs, ys, dev16, gen, n_values)
 
-    cpu = None
+    cpu = cpu1 = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(args, synth, layer0)
+        cpu1 = cpu_baseline(args, synth, layer0, threads=1, seconds=max(2.0, args.cpu_seconds / 3))
 
     result = {
         "metric": "draft GEMV GB/s on compressed bytes & % HBM peak, 8B-shape layer bs=1",
@@ -245,6 +249,9 @@ def main():
             "spec_bits_per_value": round(bits_per_value, 4),
         },
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "hbm_read_ceiling": ceiling,
+        "pct_of_read_ceiling": round(100 * value / ceiling["GB_s"], 2),
+        "layer_us_by_events": step_pct,
         "tokens_per_s_equiv_layer": round(1e3 / ms_per_step, 1),
         "roofline": {
             "bound": "hbm",
@@ -259,6 +266,7 @@ def main():
         },
         "per_matrix": per_matrix,
         "cpu_baseline": cpu,
+        "cpu_baseline_1core": cpu1,
     }
     result.update(extras)
     print(json.dumps(result))
@@ -300,12 +308,16 @@ def run_extras(args, torch, cass, synth, timer, stream, layers, encs, layer0, en
                  for n in MATS)
     rows = {"verify_gemm_n5": {"ms_per_layer": round(ver_ms, 4),
                                "GB_s": round(both / (ver_ms * 1e-3) / 1e9, 1),
+                               "pct_hbm_peak": round(100 * both / (ver_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
                                "spec_plus_verif_MB": round(both / 1e6, 2)}}
     outb = {n: torch.empty_like(layers[0][n]) for n in MATS}
     rec_ms = sum(timer.ms(lambda n=n: cass.cass_reconstruct(e0[n].desc, outb[n], stream), 3)
                  for n in MATS)
+    out_b = sum(2 * layers[0][n].numel() for n in MATS)
     rows["reconstruct"] = {"ms_per_layer": round(rec_ms, 4),
-                           "GB_s_read": round(both / (rec_ms * 1e-3) / 1e9, 1)}
+                           "GB_s_read": round(both / (rec_ms * 1e-3) / 1e9, 1),
+                           "pct_hbm_peak_read_plus_write":
+                               round(100 * (both + out_b) / (rec_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)}
     dd_ms = sum(timer.ms(lambda n=n: cass.cass_draft_decode(e0[n].desc, outb[n], stream), 3)
                 for n in MATS)
     rows["draft_decode"] = {"ms_per_layer": round(dd_ms, 4)}
@@ -464,9 +476,30 @@ def run_extras(args, torch, cass, synth, timer, stream, layers, encs, layer0, en
     return out
 
 
-def cpu_baseline(args, synth, layer0):
+def read_ceiling(torch, stream):
+    """Achievable HBM read rate of a plain streaming read on this GPU: torch's
+    sum over a 2 GiB fp32 tensor (one read of every byte), best of 5."""
+    t = torch.ones(1 << 29, dtype=torch.float32, device="cuda")
+    best = None
+    for _ in range(6):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        t.sum()
+        b.record(stream)
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b)
+        best = ms if best is None else min(best, ms)
+    gbs = t.numel() * 4 / (best * 1e-3) / 1e9
+    del t
+    torch.cuda.empty_cache()
+    return {"GB_s": round(gbs, 1), "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+            "kernel": "torch sum over 2 GiB fp32 (best of 6)"}
+
+
+def cpu_baseline(args, synth, layer0, threads=None, seconds=None):
     import oracle
-    threads = max(1, min(16, os.cpu_count() or 1))
+    threads = threads or max(1, min(16, os.cpu_count() or 1))
+    seconds = seconds or args.cpu_seconds
     sample = {}
     for n in MATS:
         w = layer0[n][::16]
@@ -478,7 +511,7 @@ def cpu_baseline(args, synth, layer0):
         for n in MATS:
             oracle.product(sample[n], xh[n], threads=threads)
             done += sample[n].size
-        if time.time() - t_start >= args.cpu_seconds:
+        if time.time() - t_start >= seconds:
             break
     dt = time.time() - t_start
     return {"value": round(done / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",

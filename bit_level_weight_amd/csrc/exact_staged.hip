@@ -46,7 +46,8 @@ typedef __attribute__((address_space(3))) const uint16_t lds_u16c;
 typedef __attribute__((address_space(3))) uint16_t lds_u16;
 typedef __attribute__((address_space(3))) const uint32_t lds_u32c;
 
-constexpr int kRows = 16;   // rows per workgroup
+constexpr int kRows = 16;   // rows per wave
+constexpr int kWaves = 4;   // waves per workgroup (sharing the rank tables)
 constexpr int kSec = 6;     // bitmap, fields, low mantissas, pruned bytes, spec codes, verif codes
 constexpr int kPU = 6;      // pruned values per group (6 codes nearly always fit 32 bits)
 
@@ -55,7 +56,8 @@ struct XGeom {
   int TS;                    // u16 per tile row (Wb*B + 2)
   int64_t nstage, stages_per_split;
   int nsplit;
-  int perm_off, klut_off, plut_off, meta_off, dummy_off, tile_off;
+  int perm_off, klut_off, plut_off, wave_off, wave_bytes;  // shared tables, wave regions
+  int meta_off, dummy_off, tile_off;                       // inside a wave region
   int fix_off, fix_cap, cod_off, cod_cap, lds_bytes;
 };
 
@@ -337,13 +339,13 @@ __device__ __forceinline__ uint32_t find_in_block(uint32_t wa, int nwb, int skip
 // MODE 0: verification GEMM into Y; 1: reconstruction; 2: zero-filled draft
 // (speculation stream only: vv is not read)
 template <int MODE, int KU, bool KLUT>
-__global__ void __launch_bounds__(64) k_exact_staged(SpecViewC1 sv, VerifViewC1 vv, Shape sh,
+__global__ void __launch_bounds__(64 * kWaves) k_exact_staged(SpecViewC1 sv, VerifViewC1 vv, Shape sh,
                                                      XGeom g, const uint16_t* __restrict__ X,
                                                      int ntok, int64_t ldx,
                                                      float* __restrict__ Y, int64_t ldy,
                                                      uint16_t* __restrict__ out) {
   extern __shared__ __align__(16) uint8_t smem[];
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t R = sh.rows, C = sh.cols, k = sh.keep, B = sh.block, nb = C / B;
   const int m = sh.mant, fw = 1 + m, lw = 7 - m;
   const int nwb = (int)(B / 32);
@@ -356,27 +358,33 @@ __global__ void __launch_bounds__(64) k_exact_staged(SpecViewC1 sv, VerifViewC1 
   uint8_t* pv = ps + 256;
   uint16_t* klut = reinterpret_cast<uint16_t*>(smem + g.klut_off);
   uint16_t* plut = reinterpret_cast<uint16_t*>(smem + g.plut_off);
-  for (int i = lane; i < 256; i += 64) {
+  // (tables shared by the workgroup's waves)
+  for (int i = threadIdx.x; i < 256; i += 64 * kWaves) {
     ps[i] = sv.perm[i];
     pv[i] = MODE == 2 ? 0 : vv.perm[i];
   }
   if (KLUT) {
-    for (int i = lane; i < (32 << fw); i += 64) {
+    for (int i = threadIdx.x; i < (32 << fw); i += 64 * kWaves) {
       const uint32_t f = (uint32_t)i & ((1u << fw) - 1u);
       klut[i] = (uint16_t)(((f >> m) << 15) | ((uint32_t)sv.perm[i >> fw] << 7) |
                            ((f & ((1u << m) - 1u)) << lw));
     }
-  } else if (lane < 32) {
-    klut[lane] = (uint16_t)((uint32_t)sv.perm[lane] << 7);
+  } else if (threadIdx.x < 32) {
+    klut[threadIdx.x] = (uint16_t)((uint32_t)sv.perm[threadIdx.x] << 7);
   }
-  if (MODE != 2)
+  if (MODE != 2 && threadIdx.x < 64)
     plut[lane] = (uint16_t)(((uint32_t)(lane & 1) << 15) | ((uint32_t)vv.perm[lane >> 1] << 7));
+  __syncthreads();  // the tables
+  // this wave's region: 16 rows of its own
+  const int wbase = g.wave_off + wave * g.wave_bytes;
+  uint8_t* wsm = smem + wbase;
   const uint32_t klutb = sb + g.klut_off, plutb = sb + g.plut_off;
-  const uint32_t dummy = sb + g.dummy_off + 4u * lane;
-  const uint32_t tileb = sb + g.tile_off;
+  const uint32_t dummy = sb + wbase + g.dummy_off + 4u * lane;
+  const uint32_t tileb = sb + wbase + g.tile_off;
 
   const int r = lane & 15, j = lane >> 4;
-  const int64_t row0 = (int64_t)blockIdx.x * kRows;
+  const int64_t row0 = ((int64_t)blockIdx.x * kWaves + wave) * kRows;
+  if (row0 >= R) return;
   const int64_t row = row0 + r;
   const bool row_ok = row < R;
   const int64_t rowc = row_ok ? row : R - 1;  // clamped for loads
@@ -416,7 +424,7 @@ __global__ void __launch_bounds__(64) k_exact_staged(SpecViewC1 sv, VerifViewC1 
   };
   // the current stage's words sit in shared memory: written at the end of the
   // previous stage (so their loads have had the whole decode to land)
-  uint32_t* meta_s = reinterpret_cast<uint32_t*>(smem + g.meta_off);  // [16][9]
+  uint32_t* meta_s = reinterpret_cast<uint32_t*>(wsm + g.meta_off);  // [16][9]
   auto put_meta = [&](const MetaRaw& mr) {
     if (j == 0) {
 #pragma unroll
@@ -497,11 +505,11 @@ __global__ void __launch_bounds__(64) k_exact_staged(SpecViewC1 sv, VerifViewC1 
       const int N = __builtin_amdgcn_readlane(incl, 15);
       int off;
       if (sec < 4) {
-        off = g.fix_off + foff;
+        off = wbase + g.fix_off + foff;
         foff += 16 * N;
       } else {
         if (coff + 16 * N > g.cod_cap) overflow = true;
-        off = g.cod_off + coff;
+        off = wbase + g.cod_off + coff;
         coff += 16 * N;
       }
       nsec[sec] = (sec < 4 || !overflow) ? N : 0;
@@ -510,7 +518,7 @@ __global__ void __launch_bounds__(64) k_exact_staged(SpecViewC1 sv, VerifViewC1 
       d_l[sec] = c0 - pre;
     }
     {
-      int off_f = g.fix_off, off_c = g.cod_off;
+      int off_f = wbase + g.fix_off, off_c = wbase + g.cod_off;
 #pragma unroll
       for (int sec = 0; sec < kSec; ++sec) {
         const int N = nsec[sec];
@@ -716,7 +724,7 @@ __global__ void __launch_bounds__(256) k_zero_y(float* Y, int ntok, int64_t rows
 
 int a16(int64_t v) { return (int)((v + 15) / 16 * 16); }
 
-constexpr int64_t kMaxLds = 64 * 1024;
+constexpr int64_t kMaxLds = 150 * 1024;
 
 XGeom make_xgeom(const Shape& sh, const SpecViewC1& sv, const VerifViewC1& vv) {
   XGeom g = {};
@@ -744,19 +752,22 @@ XGeom make_xgeom(const Shape& sh, const SpecViewC1& sv, const VerifViewC1& vv) {
   o += a16(fw <= 5 ? (int64_t)(32 << fw) * 2 : 64);
   g.plut_off = (int)o;
   o += 128;
-  g.meta_off = (int)o;
-  o += kRows * 9 * 4;
-  g.dummy_off = (int)o;
-  o += 256;
-  g.tile_off = (int)o;
-  o += a16((int64_t)kRows * g.TS * 2);
-  g.fix_off = (int)o;
+  g.wave_off = (int)o;
+  int64_t w = 0;  // one wave's region
+  g.meta_off = (int)w;
+  w += kRows * 9 * 4;
+  g.dummy_off = (int)w;
+  w += 256;
+  g.tile_off = (int)w;
+  w += a16((int64_t)kRows * g.TS * 2);
+  g.fix_off = (int)w;
   g.fix_cap = (int)(kRows * fix_row);
-  o += g.fix_cap + 64;  // window look-ahead
-  g.cod_off = (int)o;
+  w += g.fix_cap + 64;  // window look-ahead
+  g.cod_off = (int)w;
   g.cod_cap = (int)std::min<int64_t>(kRows * cod_row, 24 * 1024);
-  o += g.cod_cap + 64;
-  g.lds_bytes = (int)o;
+  w += g.cod_cap + 64;
+  g.wave_bytes = (int)a16(w);
+  g.lds_bytes = (int)(o + kWaves * g.wave_bytes);
   return g;
 }
 
@@ -767,11 +778,18 @@ hipError_t launch_staged_t(const SpecViewC1& sv, const VerifViewC1& vv, const Sh
   auto kern = k_exact_staged<MODE, KU, KLUT>;
   if (g.lds_bytes > kMaxLds) return hipErrorInvalidValue;
   int occ = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, (const void*)kern, 64,
+  if (g.lds_bytes > 64 * 1024) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, g.lds_bytes);
+    if (e != hipSuccess) return e;
+  }
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, (const void*)kern, 64 * kWaves,
                                                    (size_t)g.lds_bytes) != hipSuccess || occ < 1)
     occ = 1;
-  const int64_t gx = (sh.rows + kRows - 1) / kRows;
-  const int64_t want = (int64_t)device_cu_count() * occ;
+  const int64_t gx = (sh.rows + kRows * kWaves - 1) / (kRows * kWaves);
+  // about four workgroups per resident slot: the dispatcher hands them out as
+  // slots free up, which evens out the finish across CUs
+  const int64_t want = (int64_t)device_cu_count() * occ * 4;
   int64_t nsplit = (want + gx - 1) / gx;
   if (nsplit > g.nstage) nsplit = g.nstage;
   if (nsplit < 1) nsplit = 1;
@@ -785,7 +803,7 @@ hipError_t launch_staged_t(const SpecViewC1& sv, const VerifViewC1& vv, const Sh
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  kern<<<dim3((unsigned)gx, (unsigned)nsplit), 64, (size_t)g.lds_bytes, s>>>(sv, vv, sh, g, X,
+  kern<<<dim3((unsigned)gx, (unsigned)nsplit), 64 * kWaves, (size_t)g.lds_bytes, s>>>(sv, vv, sh, g, X,
                                                                             ntok, ldx, Y, ldy,
                                                                             out);
   return hipGetLastError();
