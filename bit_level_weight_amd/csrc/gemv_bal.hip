@@ -57,6 +57,7 @@ struct BalGeom {
   int lut_off;          // LDS byte offsets (x at 0)
   int wave_off, wave_bytes;
   int kb_off, bo_off, bm_off, f_off, c_off;  // inside a wave region
+  int perm_off;         // inside a wave region: the wave's copy of the rank table (C-1)
   int c_cap;            // code words a wave region holds
   int lds_bytes;
   uint32_t xstride;     // LDS bytes between the batch rows of x
@@ -69,6 +70,7 @@ __device__ __forceinline__ void wave_sync() {
 }
 
 typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(4))) const unsigned long long const_u64;
 
 // Issues the copy of n 16-byte chunks from global memory to LDS by LDS DMA:
 // one instruction per 64 chunks, lane i's chunk landing at dst + 16 i (the
@@ -242,7 +244,9 @@ __global__ void __launch_bounds__(kBalThreads) k_gemv_c1_bal(SpecViewC1 v, Shape
   const int B = (int)sh.block, nb = (int)(C / B), nwb = B / 32;
   const int m = sh.mant, fw = 1 + m;
   const uint32_t fmask = (1u << fw) - 1u;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // (wave index made visibly uniform so that per-round values and the row
+  // bases of the first round come through scalar registers and loads)
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   float* lut = reinterpret_cast<float*>(smem + g.lut_off);
   uint8_t* reg = smem + g.wave_off + wave * g.wave_bytes;
   uint16_t* kb_l = reinterpret_cast<uint16_t*>(reg + g.kb_off);
@@ -312,8 +316,11 @@ __global__ void __launch_bounds__(kBalThreads) k_gemv_c1_bal(SpecViewC1 v, Shape
   };
   auto load_bounds = [&](int64_t round, int64_t& cb0, int64_t& cb1, int64_t& rowcb) {
     const int64_t r0 = round * g.rpw, r1 = r0 + g.rpw;
-    cb0 = (int64_t)v.rowbase[r0];
-    cb1 = r1 < R ? (int64_t)v.rowbase[r1] : v.codes_limit * 32;
+    // the round's two bounds through the scalar cache (the table is read-only
+    // here), so that the codes' copy waits for nothing else
+    const const_u64* rb = (const const_u64*)v.rowbase;
+    cb0 = (int64_t)rb[r0];
+    cb1 = r1 < R ? (int64_t)rb[r1] : v.codes_limit * 32;
     rowcb = r0 + rl < R ? (int64_t)v.rowbase[r0 + rl] : 0;
   };
 
@@ -392,19 +399,17 @@ __global__ void __launch_bounds__(kBalThreads) k_gemv_c1_bal(SpecViewC1 v, Shape
     }
   };
 
-  // ---- first round, x and the (rank, field) -> fp32 table
+  // ---- first round, x and the (rank, field) -> fp32 table.  Every copy of
+  // the first round is in flight at once: the rank table, the sections, the
+  // codes (whose range needs only the two row bases, scalar loads) and x.
   int64_t round = (int64_t)blockIdx.x * kBalWaves + wave;
-  uint32_t prm[8];  // rank table entries for this thread's table slots
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int i = threadIdx.x + kBalThreads * j;
-    if (i < nlut) prm[j] = v.perm[i >> fw];
-  }
+  const uint8_t* perm_l = reg + g.perm_off;
+  dma_run(reinterpret_cast<const u32x4*>(v.perm), reinterpret_cast<u32x4*>(reg + g.perm_off), 16,
+          lane);
   const bool first = round < g.nrounds;
   Plan pl{};
   int64_t cb0 = 0, cb1 = 0, rowcb = 0;
   if (first) {
-    load_bounds(round, cb0, cb1, rowcb);
     pl = plan(round);
     stage_fixed(pl);
   }
@@ -424,21 +429,27 @@ __global__ void __launch_bounds__(kBalThreads) k_gemv_c1_bal(SpecViewC1 v, Shape
     // zeros after the row: masked slots of a part's last group may read there
     if (threadIdx.x < 128) xr[C + threadIdx.x] = 0;
   }
-  wait_dma();  // the row bases, this wave's sections and x chunks
-  if (first) stage_codes(pl, cb0, cb1);
+  // (after every copy that does not need them: a scalar-load wait covers all
+  // scalar loads in flight)
+  if (first) {
+    load_bounds(round, cb0, cb1, rowcb);
+    stage_codes(pl, cb0, cb1);
+  }
+  wait_dma();  // the rank table, this wave's sections and codes, its x chunks
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const int i = threadIdx.x + kBalThreads * j;
     if (i < nlut) {
       const uint32_t f = (uint32_t)i & fmask;
-      lut[i] = __uint_as_float(((f >> m) << 31) | (prm[j] << 23) |
+      lut[i] = __uint_as_float(((f >> m) << 31) | ((uint32_t)perm_l[i >> fw] << 23) |
                                ((f & ((1u << m) - 1u)) << (23 - m)));
     }
   }
   Part pt{};
-  if (first) pt = locate_bits(pl);  // overlaps the codes' copy
-  wait_dma();
-  if (first) locate_codes(pl, pt, rowcb);
+  if (first) {
+    pt = locate_bits(pl);
+    locate_codes(pl, pt, rowcb);
+  }
   __syncthreads();  // x (every wave's chunks) and the table are in LDS
   if (!first) return;
 
@@ -480,7 +491,7 @@ __global__ void __launch_bounds__(kBalThreads) k_gemv_c1_bal(SpecViewC1 v, Shape
         }
         if (gi < G) {
           for (int u = 0; u < U; ++u)
-            c1_step<BATCH>(bm_l, bp, f_l, fp, c_l, cp, rowbit, C, lut, v.perm, m, smem,
+            c1_step<BATCH>(bm_l, bp, f_l, fp, c_l, cp, rowbit, C, lut, perm_l, m, smem,
                            g.xstride, acc);
           ++gi;
           w = load_raw(bm_l, f_l, c_l, bp, fp, cp);
@@ -499,14 +510,14 @@ __global__ void __launch_bounds__(kBalThreads) k_gemv_c1_bal(SpecViewC1 v, Shape
         } else {
           for (int u = 0; u < U; ++u)
             if (u < t)
-              c1_step<BATCH>(bm_l, bp, f_l, fp, c_l, cp, rowbit, C, lut, v.perm, m, smem,
+              c1_step<BATCH>(bm_l, bp, f_l, fp, c_l, cp, rowbit, C, lut, perm_l, m, smem,
                              g.xstride, acc);
         }
       }
     } else if (pl.c_in_lds) {
       for (int i = 0; i < n_max; ++i)
         if (i < n)
-          c1_step<BATCH>(bm_l, bp, f_l, fp, c_l, cp, rowbit, C, lut, v.perm, m, smem, g.xstride,
+          c1_step<BATCH>(bm_l, bp, f_l, fp, c_l, cp, rowbit, C, lut, perm_l, m, smem, g.xstride,
                          acc);
     } else {
       // codes straight from global memory (a round whose codes exceed the LDS share)
@@ -514,7 +525,7 @@ __global__ void __launch_bounds__(kBalThreads) k_gemv_c1_bal(SpecViewC1 v, Shape
       uint32_t cpg = cp;
       for (int i = 0; i < n_max; ++i)
         if (i < n)
-          c1_step<BATCH>(bm_l, bp, f_l, fp, cg, cpg, rowbit, C, lut, v.perm, m, smem, g.xstride,
+          c1_step<BATCH>(bm_l, bp, f_l, fp, cg, cpg, rowbit, C, lut, perm_l, m, smem, g.xstride,
                          acc);
     }
 
@@ -916,6 +927,8 @@ BalGeom make_bal_geom(const Shape& sh, int batch, int64_t code_limit_words) {
   if (cap > 4096) cap = 4096;
   g.c_cap = (int)cap;
   w += a16((cap + 4 + kSlack) * 4);
+  g.perm_off = (int)w;
+  w += 256;
   g.wave_bytes = (int)w;
   pos += (int64_t)kBalWaves * w;
   g.lds_bytes = (fw > kMaxFw || pos > kBalMaxLds) ? (int)(kBalMaxLds + 1) : (int)pos;
