@@ -264,6 +264,7 @@ def main():
             "avg_launch_us": round(avg_launch_ms * 1e3, 3),
             "algorithmic_bytes_per_launch": round(alg_bytes / n_launch),
         },
+        "valu_ceiling": valu_from_profile(step_pct["p50"]),
         "per_matrix": per_matrix,
         "cpu_baseline": cpu,
         "cpu_baseline_1core": cpu1,
@@ -272,12 +273,12 @@ def main():
     print(json.dumps(result))
 
 
-def traffic_from_profile():
-    """HBM bytes per GEMV launch from the committed counter summary (FETCH_SIZE +
-    WRITE_SIZE, calibrated on a device copy), when it was taken on the current
-    kernel sources; else null."""
+def profile_fields(name):
+    """Key: value lines of a committed counter summary under profiles/, when it
+    was taken on the current kernel sources (sha256 of the listed files); else
+    None."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", "draft_gemv_llama8b_layer_traffic.txt")
+    path = os.path.join(ROOT, "profiles", name)
     if not os.path.exists(path):
         return None
     fields = {}
@@ -291,8 +292,35 @@ def traffic_from_profile():
             h.update(open(os.path.join(ROOT, f), "rb").read())
         if h.hexdigest() != fields["sources_sha256"]:
             return None
-        return int(fields["traffic_bytes_per_launch"])
-    except (KeyError, OSError, ValueError):
+    except (KeyError, OSError):
+        return None
+    return fields
+
+
+def traffic_from_profile():
+    """HBM bytes per GEMV launch from the committed counter summary (FETCH_SIZE +
+    WRITE_SIZE, calibrated on a device copy), when it was taken on the current
+    kernel sources; else null."""
+    f = profile_fields("draft_gemv_llama8b_layer_traffic.txt")
+    try:
+        return int(f["traffic_bytes_per_launch"]) if f else None
+    except (KeyError, ValueError):
+        return None
+
+
+def valu_from_profile(layer_us):
+    """The secondary (VALU issue) ceiling of the GEMV from the committed SQ
+    counter summary: lane instructions per kept value and the time the layer's
+    VALU instructions need at one wave64 instruction per 4 cycles per SIMD
+    (256 CUs x 4 SIMDs, 2.4 GHz, i.e. 39.3 T lane-ops/s); null when the
+    counters were taken on other kernel sources."""
+    f = profile_fields("draft_gemv_llama8b_layer_sq_counters.txt")
+    try:
+        floor = float(f["valu_issue_floor_us_per_layer"])
+        return {"lane_instr_per_kept_value": float(f["valu_lane_instr_per_kept_value"]),
+                "issue_floor_us_per_layer": floor, "peak_lane_ops_per_s": 39.3e12,
+                "frac_of_layer_time": round(floor / layer_us, 3)}
+    except (TypeError, KeyError, ValueError):
         return None
 
 
