@@ -69,6 +69,28 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Bit index of the set bit of rank n (0-based) in the 256-bit little-endian
+// word array q, or ~0 when q holds n or fewer set bits: binary search over
+// popcounts of halves, quarters and words, then a select inside the word.
+__device__ __forceinline__ uint32_t select256(const uint32_t (&q)[8], int n) {
+  const int c4 = __builtin_popcount(q[0]) + __builtin_popcount(q[1]) + __builtin_popcount(q[2]) +
+                 __builtin_popcount(q[3]);
+  const bool h = n >= c4;
+  n -= h ? c4 : 0;
+  const uint32_t a0 = h ? q[4] : q[0], a1 = h ? q[5] : q[1], a2 = h ? q[6] : q[2],
+                 a3 = h ? q[7] : q[3];
+  const int c2 = __builtin_popcount(a0) + __builtin_popcount(a1);
+  const bool hq = n >= c2;
+  n -= hq ? c2 : 0;
+  const uint32_t b0 = hq ? a2 : a0, b1 = hq ? a3 : a1;
+  const int c1 = __builtin_popcount(b0);
+  const bool hw = n >= c1;
+  n -= hw ? c1 : 0;
+  const uint32_t wd = hw ? b1 : b0;
+  if (n >= __builtin_popcount(wd)) return ~0u;
+  return (h ? 128u : 0u) + (hq ? 64u : 0u) + (hw ? 32u : 0u) + (uint32_t)select_bit(wd, n + 1);
+}
+
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(4))) const unsigned long long const_u64;
 
@@ -324,79 +346,87 @@ __global__ void __launch_bounds__(kBalThreads) k_gemv_c1_bal(SpecViewC1 v, Shape
     rowcb = r0 + rl < R ? (int64_t)v.rowbase[r0 + rl] : 0;
   };
 
-  // Where this lane's part of the round starts in the bitmap and fields (from
-  // the staged kept counts and bitmap words); `skip` and `blk` carry the code
-  // search to locate_codes.
-  int skip = 0, blk = 0;
-  auto locate_bits = [&](const Plan& pl) {
+  // Where this lane's part of the round starts.  The block holding its first
+  // value: the kept counts of the estimated block and its neighbours, read at
+  // once (the estimate k / nb values per block is almost always within one
+  // block; otherwise a stepping search).  The bit inside the block: binary
+  // search over popcounts of the block's words.  The code: the same select
+  // over the code ones, from the block's code offset.  Per-lane offsets are
+  // 32-bit (bit positions in the staged regions, kept indices in a row); the
+  // round's bases are uniform.
+  auto locate = [&](const Plan& pl, int64_t rowcb) {
     Part pt;
-    const int64_t row = pl.row0 + rl;
-    const int i0 = (int)(((int64_t)part * k) >> g.logP);
-    pt.n = rl < pl.rows_here ? (int)((((int64_t)part + 1) * k) >> g.logP) - i0 : 0;
-    pt.rowbit = (uint32_t)((pl.row0 * wpr - pl.bm_a0) * 32 + (int64_t)rl * C);
+    const uint32_t uk = (uint32_t)k;
+    const uint32_t i0 = ((uint32_t)part * uk) >> g.logP;
+    pt.n = rl < pl.rows_here ? (int)((((uint32_t)part + 1u) * uk) >> g.logP) - (int)i0 : 0;
+    pt.rowbit = (uint32_t)((pl.row0 * wpr - pl.bm_a0) * 32) + (uint32_t)rl * (uint32_t)C;
     pt.bp = pt.rowbit;
     pt.fp = 0;
     pt.cp = 0;
     pt.cabs = 0;
-    skip = 0;
-    blk = 0;
-    if (pt.n > 0) {
-      // block holding value i0: the kept counts per block are close to
-      // k / nb, so start from that estimate and step (usually zero or one step)
-      const uint16_t* kbr = kb_l + pl.kb_sh + rl * nb;
-      int b = (int)((float)i0 * g.nb_per_k);
-      b = b < 0 ? 0 : (b >= nb ? nb - 1 : b);
+    if (pt.n <= 0) return pt;
+    const uint16_t* kbr = kb_l + pl.kb_sh + rl * nb;
+    // kept before block j, for any j (0 before the row, k after it)
+    auto kb_at = [&](int j) -> int { return j <= 0 ? 0 : (j >= nb ? (int)k : (int)kbr[j]); };
+    int e = (int)((float)i0 * g.nb_per_k);
+    e = e < 0 ? 0 : (e >= nb ? nb - 1 : e);
+    const int km = kb_at(e - 1), k0 = kb_at(e), k1 = kb_at(e + 1), k2 = kb_at(e + 2);
+    const int ii = (int)i0;
+    int b = e - 1 + (k0 <= ii ? 1 : 0) + (k1 <= ii ? 1 : 0);
+    int kbb = b == e - 1 ? km : (b == e ? k0 : k1);
+    if (!(km <= ii && ii < k2)) {
+      // (rare) the estimate is two or more blocks off
+      b = e;
       for (int it = 0; it < nb; ++it) {
-        const int lo = kbr[b], hi = b + 1 < nb ? kbr[b + 1] : (int)k;
-        if (lo > i0 && b > 0) --b;
-        else if (hi <= i0 && b + 1 < nb) ++b;
+        const int lo = kb_at(b), hi = kb_at(b + 1);
+        if (lo > ii && b > 0) --b;
+        else if (hi <= ii && b + 1 < nb) ++b;
         else break;
       }
-      skip = i0 - kbr[b];
-      blk = b;
-      // word and bit inside the block: the block's words read at once
-      const uint32_t* bw = bm_l + (pt.rowbit >> 5) + b * nwb;
-      int rem = skip, wsel = nwb - 1;
-      uint32_t wd = 0;
-      if (nwb <= 8) {
-        uint32_t wv[8];
+      kbb = kb_at(b);
+    }
+    const int skip = ii - kbb;
+    const uint32_t* bw = bm_l + (pt.rowbit >> 5) + b * nwb;
+    uint32_t inblk;
+    if (nwb == 8) {
+      uint32_t q[8];
 #pragma unroll
-        for (int w = 0; w < 8; ++w) wv[w] = w < nwb ? bw[w] : 0u;
-        bool found = false;
-#pragma unroll
-        for (int w = 0; w < 8; ++w) {
-          const int c = __builtin_popcount(wv[w]);
-          const bool here = !found && w < nwb && rem < c;
-          wsel = here ? w : wsel;
-          wd = here ? wv[w] : wd;
-          rem -= (!found && !here) ? c : 0;
-          found = found || here;
-        }
-      } else {
-        int wi = 0;
-        wd = bw[0];
-        for (;;) {
-          const int c = __builtin_popcount(wd);
-          if (rem < c || wi == nwb - 1) break;  // (the second test: corrupt streams only)
-          rem -= c;
-          wd = bw[++wi];
-        }
-        wsel = wi;
+      for (int w = 0; w < 8; ++w) q[w] = bw[w];
+      inblk = select256(q, skip);
+      inblk = inblk == ~0u ? 0u : inblk;  // (corrupt streams only: stay inside the block)
+    } else {
+      int wi = 0, rem = skip;
+      uint32_t wd = bw[0];
+      for (;;) {
+        const int c = __builtin_popcount(wd);
+        if (rem < c || wi == nwb - 1) break;  // (the second test: corrupt streams only)
+        rem -= c;
+        wd = bw[++wi];
       }
-      pt.bp = pt.rowbit + (uint32_t)(b * B + wsel * 32 + select_bit(wd, rem + 1));
-      pt.fp = (uint32_t)((row * k + i0) * fw - pl.f_a0 * 32);
+      inblk = (uint32_t)(wi * 32 + select_bit(wd, rem + 1));
+    }
+    pt.bp = pt.rowbit + (uint32_t)(b * B) + inblk;
+    pt.fp = (uint32_t)(pl.row0 * k * fw - pl.f_a0 * 32) + ((uint32_t)rl * uk + i0) * (uint32_t)fw;
+    // the codes: the block's code offset, then `skip` codes on
+    const uint32_t bo = bo_l[pl.bo_sh + rl * nb + b];
+    pt.cabs = rowcb + bo;
+    if (pl.c_in_lds) {
+      const uint32_t cpos = (uint32_t)(rowcb - pl.c_a0 * 32) + bo;
+      pt.cp = cpos;
+      if (skip > 0) {
+        // the skip-th one bit at or after cpos, among the next 256 - (cpos & 31) bits
+        uint32_t q[8];
+        const uint32_t* qc = c_l + (cpos >> 5);
+#pragma unroll
+        for (int w = 0; w < 8; ++w) q[w] = qc[w];
+        q[0] &= ~0u << (cpos & 31u);
+        const uint32_t idx = select256(q, skip - 1);
+        pt.cp = idx != ~0u ? (cpos & ~31u) + idx + 1u : skip_codes(c_l, cpos, skip);
+      }
+    } else {
+      pt.cp = skip_codes(v.codes + (pt.cabs >> 5), (uint32_t)(pt.cabs & 31), skip);
     }
     return pt;
-  };
-  // ... and in the codes: the block's code offset, then `skip` codes on
-  auto locate_codes = [&](const Plan& pl, Part& pt, int64_t rowcb) {
-    if (pt.n > 0) {
-      pt.cabs = rowcb + bo_l[pl.bo_sh + rl * nb + blk];
-      if (pl.c_in_lds)
-        pt.cp = skip_codes8(c_l, (uint32_t)(pt.cabs - pl.c_a0 * 32), skip);
-      else
-        pt.cp = skip_codes(v.codes + (pt.cabs >> 5), (uint32_t)(pt.cabs & 31), skip);
-    }
   };
 
   // ---- first round, x and the (rank, field) -> fp32 table.  Every copy of
@@ -446,10 +476,7 @@ __global__ void __launch_bounds__(kBalThreads) k_gemv_c1_bal(SpecViewC1 v, Shape
     }
   }
   Part pt{};
-  if (first) {
-    pt = locate_bits(pl);
-    locate_codes(pl, pt, rowcb);
-  }
+  if (first) pt = locate(pl, rowcb);
   __syncthreads();  // x (every wave's chunks) and the table are in LDS
   if (!first) return;
 
@@ -547,8 +574,7 @@ __global__ void __launch_bounds__(kBalThreads) k_gemv_c1_bal(SpecViewC1 v, Shape
     stage_fixed(pl);
     stage_codes(pl, ncb0, ncb1);
     wait_dma();
-    pt = locate_bits(pl);
-    locate_codes(pl, pt, nrowcb);
+    pt = locate(pl, nrowcb);
     round = next;
   }
 }
