@@ -61,6 +61,8 @@ struct BalGeom {
   int c_cap;            // code words a wave region holds
   int lds_bytes;
   uint32_t xstride;     // LDS bytes between the batch rows of x
+  uint32_t word_bits;   // 27: width of a word index in a bit position (a kernel
+                        // argument, so the extract stays one instruction)
 };
 
 __device__ __forceinline__ void wave_sync() {
@@ -167,12 +169,21 @@ struct Raw {
   uint32_t q0, q1, q2, f0, f1, c0, c1;
 };
 
-__device__ __forceinline__ Raw load_raw(const uint32_t* bm_l, const uint32_t* f_l,
-                                        const uint32_t* c_l, uint32_t bp, uint32_t fp,
-                                        uint32_t cp) {
-  const uint32_t* qb = bm_l + (bp >> 5);
-  const uint32_t* qf = f_l + (fp >> 5);
-  const uint32_t* qc = c_l + (cp >> 5);
+typedef __attribute__((address_space(3))) const uint32_t lds_u32;
+
+// LDS word holding bit `pos` of a stream staged at LDS byte address `base`:
+// word index by bit-field extract, then one shift-and-add.  `wb` = 27 comes
+// from a kernel argument; with a literal width the extract is rewritten into
+// a shift and a mask (three instructions instead of two).
+__device__ __forceinline__ lds_u32* word_at(uint32_t base, uint32_t pos, uint32_t wb) {
+  return (lds_u32*)(uintptr_t)(base + (__builtin_amdgcn_ubfe(pos, 5u, wb) << 2));
+}
+
+__device__ __forceinline__ Raw load_raw(uint32_t bm_b, uint32_t f_b, uint32_t c_b, uint32_t bp,
+                                        uint32_t fp, uint32_t cp, uint32_t wb) {
+  lds_u32* qb = word_at(bm_b, bp, wb);
+  lds_u32* qf = word_at(f_b, fp, wb);
+  lds_u32* qc = word_at(c_b, cp, wb);
   return Raw{qb[0], qb[1], qb[2], qf[0], qf[1], qc[0], qc[1]};
 }
 
@@ -189,9 +200,9 @@ typedef __attribute__((address_space(3))) const float lds_f32;
 //   xorg  LDS byte address of x for staged bitmap bit 0
 template <int BATCH, int U, bool MASKED>
 __device__ __forceinline__ void c1_group(Raw& w, uint32_t& bp, uint32_t& fp, uint32_t& cp,
-                                         const uint32_t* bm_l, const uint32_t* f_l,
-                                         const uint32_t* c_l, uint32_t xorg, uint32_t lutb,
-                                         int fw, uint32_t xstride, int t, float* acc) {
+                                         uint32_t bm_b, uint32_t f_b, uint32_t c_b,
+                                         uint32_t xorg, uint32_t lutb,
+                                         int fw, uint32_t xstride, uint32_t wb, int t, float* acc) {
   const uint32_t sb = bp & 31u;
   const uint32_t lo0 = __builtin_amdgcn_alignbit(w.q1, w.q0, sb);
   // (MASKED: the windows may hold only t values; a set bit 63 keeps the
@@ -236,7 +247,7 @@ __device__ __forceinline__ void c1_group(Raw& w, uint32_t& bp, uint32_t& fp, uin
 #pragma unroll
     for (int bb = 0; bb < BATCH; ++bb) xv[bb][u] = x_at_addr(xa[u] + bb * xstride);
   }
-  if (!MASKED) w = load_raw(bm_l, f_l, c_l, bp, fp, cp);
+  if (!MASKED) w = load_raw(bm_b, f_b, c_b, bp, fp, cp, wb);
   __builtin_amdgcn_sched_barrier(0);
   // phase 3: products
 #pragma unroll
@@ -502,7 +513,10 @@ __global__ void __launch_bounds__(kBalThreads) k_gemv_c1_bal(SpecViewC1 v, Shape
     if (grouped) {
       const uint32_t xorg = lds_addr(smem) - 2u * rowbit;  // x address of staged bit 0
       const uint32_t lutb = lds_addr(reinterpret_cast<const uint8_t*>(lut));
-      Raw w = load_raw(bm_l, f_l, c_l, bp, fp, cp);
+      const uint32_t bm_b = lds_addr(reinterpret_cast<const uint8_t*>(bm_l));
+      const uint32_t f_b = lds_addr(reinterpret_cast<const uint8_t*>(f_l));
+      const uint32_t c_b = lds_addr(reinterpret_cast<const uint8_t*>(c_l));
+      Raw w = load_raw(bm_b, f_b, c_b, bp, fp, cp, g.word_bits);
       // full groups: runs of fast groups; a group whose windows fall short
       // for some lane goes value by value
       int gi = 0;
@@ -513,7 +527,7 @@ __global__ void __launch_bounds__(kBalThreads) k_gemv_c1_bal(SpecViewC1 v, Shape
                            __builtin_popcount(__builtin_amdgcn_alignbit(w.q2, w.q1, sb));
           const int ncode = __builtin_popcount(__builtin_amdgcn_alignbit(w.c1, w.c0, cp & 31u));
           if (!__all(min(have, ncode) >= U)) break;
-          c1_group<BATCH, U, false>(w, bp, fp, cp, bm_l, f_l, c_l, xorg, lutb, fw, g.xstride, U,
+          c1_group<BATCH, U, false>(w, bp, fp, cp, bm_b, f_b, c_b, xorg, lutb, fw, g.xstride, g.word_bits, U,
                                     acc);
         }
         if (gi < G) {
@@ -521,7 +535,7 @@ __global__ void __launch_bounds__(kBalThreads) k_gemv_c1_bal(SpecViewC1 v, Shape
             c1_step<BATCH>(bm_l, bp, f_l, fp, c_l, cp, rowbit, C, lut, perm_l, m, smem,
                            g.xstride, acc);
           ++gi;
-          w = load_raw(bm_l, f_l, c_l, bp, fp, cp);
+          w = load_raw(bm_b, f_b, c_b, bp, fp, cp, g.word_bits);
         }
       }
       // the part's last t = n - G*U <= U values
@@ -532,7 +546,7 @@ __global__ void __launch_bounds__(kBalThreads) k_gemv_c1_bal(SpecViewC1 v, Shape
                          __builtin_popcount(__builtin_amdgcn_alignbit(w.q2, w.q1, sb));
         const int ncode = __builtin_popcount(__builtin_amdgcn_alignbit(w.c1, w.c0, cp & 31u));
         if (__all(min(have, ncode) >= t)) {
-          c1_group<BATCH, U, true>(w, bp, fp, cp, bm_l, f_l, c_l, xorg, lutb, fw, g.xstride, t,
+          c1_group<BATCH, U, true>(w, bp, fp, cp, bm_b, f_b, c_b, xorg, lutb, fw, g.xstride, g.word_bits, t,
                                    acc);
         } else {
           for (int u = 0; u < U; ++u)
@@ -933,6 +947,7 @@ BalGeom make_bal_geom(const Shape& sh, int batch, int64_t code_limit_words) {
   g.nrounds = (R + g.rpw - 1) / g.rpw;
   g.nb_per_k = k > 0 ? (float)nb / (float)k : 0.f;
   g.xstride = (uint32_t)a16(2 * C + 256);
+  g.word_bits = 27;
   int64_t pos = (int64_t)batch * g.xstride;
   g.lut_off = (int)pos;
   pos += a16((int64_t)(kRanks << fw) * 4);
