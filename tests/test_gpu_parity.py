@@ -233,6 +233,9 @@ BAL_CASES = [
     (20, 512, 30, 3, 256, 64, "normal"),      # k < parts: lanes without values
     (64, 4096, 1229, 3, 256, 16, "wide"),     # codes of 32+ bits: per-value steps
     (64, 4096, 2048, 5, 256, 8, "onewide"),   # one row's codes exceed the LDS share
+    (64, 4096, 1229, 3, 256, 0, "ramp"),      # kept values pile up in the last blocks
+    (64, 4096, 1229, 3, 256, 16, "clustered"),  # two full blocks: block estimates 2+ off
+    (37, 4096, 1229, 3, 256, 0, "clustered"),
 ]
 
 
@@ -245,6 +248,7 @@ BAL_C2_CASES = [
     (20, 512, 30, 3, 256, 64, "normal"),      # k < parts
     (64, 4096, 1229, 3, 256, 16, "wide"),     # wide exponents (large shared-exponent offsets)
     (8, 1024, 1024, 5, 256, 0, "normal"),     # keep everything
+    (64, 2560, 768, 3, 256, 0, "clustered"),  # two full blocks, most others sparse
 ]
 
 
@@ -274,6 +278,18 @@ def bal_weights(R, C, kind, seed):
         return make_w(R, C, seed)
     if kind == "wide":
         return synth.weight_wide(R, C, seed)
+    if kind in ("ramp", "clustered"):
+        # the per-row kept values are far from uniform over the blocks, so a
+        # lane's block estimate (kept count / blocks) misses by several blocks
+        # and many blocks keep nothing
+        rng = np.random.default_rng(seed)
+        a = rng.standard_normal((R, C), dtype=np.float32) * np.float32(0.02)
+        if kind == "ramp":
+            a *= np.exp2(np.linspace(0.0, 12.0, C, dtype=np.float32))[None, :]
+        else:
+            for b in (2, 9):
+                a[:, b * 256:(b + 1) * 256] *= np.float32(100.0)
+        return synth.bf16_from_f32(a)
     w = make_w(R, C, seed)
     w[5] = synth.weight_wide(1, C, seed + 1, binades=120)[0]
     return w
