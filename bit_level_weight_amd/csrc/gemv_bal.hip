@@ -531,11 +531,27 @@ __global__ void __launch_bounds__(kBalThreads) k_gemv_c1_bal(SpecViewC1 v, Shape
                                     acc);
         }
         if (gi < G) {
-          for (int u = 0; u < U; ++u)
-            c1_step<BATCH>(bm_l, bp, f_l, fp, c_l, cp, rowbit, C, lut, perm_l, m, smem,
-                           g.xstride, acc);
+          // some lane's windows hold fewer than U values: the group as two halves
+          // (windows short of U/2 values are far rarer), value by value only if
+          // a half falls short too (codes of 32+ bits, long runs of pruned values)
+          constexpr int H = U / 2;
+#pragma unroll
+          for (int half = 0; half < 2; ++half) {
+            const uint32_t sbh = bp & 31u;
+            const int hv = __builtin_popcount(__builtin_amdgcn_alignbit(w.q1, w.q0, sbh)) +
+                           __builtin_popcount(__builtin_amdgcn_alignbit(w.q2, w.q1, sbh));
+            const int hc = __builtin_popcount(__builtin_amdgcn_alignbit(w.c1, w.c0, cp & 31u));
+            if (__all(min(hv, hc) >= H)) {
+              c1_group<BATCH, H, false>(w, bp, fp, cp, bm_b, f_b, c_b, xorg, lutb, fw, g.xstride,
+                                        g.word_bits, H, acc);
+            } else {
+              for (int u = 0; u < H; ++u)
+                c1_step<BATCH>(bm_l, bp, f_l, fp, c_l, cp, rowbit, C, lut, perm_l, m, smem,
+                               g.xstride, acc);
+              w = load_raw(bm_b, f_b, c_b, bp, fp, cp, g.word_bits);
+            }
+          }
           ++gi;
-          w = load_raw(bm_b, f_b, c_b, bp, fp, cp, g.word_bits);
         }
       }
       // the part's last t = n - G*U <= U values
