@@ -193,12 +193,13 @@ typedef __attribute__((address_space(3))) const float lds_f32;
 // at least U values: 64 keep bits, 32 field bits, 32 code bits.  Three phases:
 // positions, ranks and fields for all U values (VALU only); every table and x
 // read of the group plus the next group's window words (LDS only); the U
-// products.  With MASKED, slots u >= t add nothing (the part's last group)
-// and no next windows are read; otherwise the positions advance past the U
-// values and `w` receives the next group's words.
+// products.  With MASKED, slots u >= t add nothing (the part's last group).
+// With ADVANCE (the default when not MASKED) the positions advance past the U
+// slots and `w` receives the next group's words; a masked group advances
+// correctly only for lanes whose t is U (the others have no values left).
 //   lutb  LDS byte address of the (rank, field) -> fp32 table
 //   xorg  LDS byte address of x for staged bitmap bit 0
-template <int BATCH, int U, bool MASKED>
+template <int BATCH, int U, bool MASKED, bool ADVANCE = !MASKED>
 __device__ __forceinline__ void c1_group(Raw& w, uint32_t& bp, uint32_t& fp, uint32_t& cp,
                                          uint32_t bm_b, uint32_t f_b, uint32_t c_b,
                                          uint32_t xorg, uint32_t lutb,
@@ -231,7 +232,7 @@ __device__ __forceinline__ void c1_group(Raw& w, uint32_t& bp, uint32_t& fp, uin
     la[u] = lutb + 4u * ((r << fw) | f);
     xa[u] = xs + 2u * p;
   }
-  if (!MASKED) {
+  if (ADVANCE) {
     bp += ((xs - xlo) >> 1) + p + 1u;
     fp += (uint32_t)(U * fw);
     // bits the U codes took: the window was shifted right by that many
@@ -247,7 +248,7 @@ __device__ __forceinline__ void c1_group(Raw& w, uint32_t& bp, uint32_t& fp, uin
 #pragma unroll
     for (int bb = 0; bb < BATCH; ++bb) xv[bb][u] = x_at_addr(xa[u] + bb * xstride);
   }
-  if (!MASKED) w = load_raw(bm_b, f_b, c_b, bp, fp, cp, wb);
+  if (ADVANCE) w = load_raw(bm_b, f_b, c_b, bp, fp, cp, wb);
   __builtin_amdgcn_sched_barrier(0);
   // phase 3: products
 #pragma unroll
@@ -565,10 +566,31 @@ __global__ void __launch_bounds__(kBalThreads) k_gemv_c1_bal(SpecViewC1 v, Shape
           c1_group<BATCH, U, true>(w, bp, fp, cp, bm_b, f_b, c_b, xorg, lutb, fw, g.xstride, g.word_bits, t,
                                    acc);
         } else {
-          for (int u = 0; u < U; ++u)
-            if (u < t)
-              c1_step<BATCH>(bm_l, bp, f_l, fp, c_l, cp, rowbit, C, lut, perm_l, m, smem,
-                             g.xstride, acc);
+          // in two halves, as for a full group that falls short
+          constexpr int H = U / 2;
+          const int t1 = t < H ? t : H, t2 = t - t1;
+          if (__all(min(have, ncode) >= t1)) {
+            c1_group<BATCH, H, true, true>(w, bp, fp, cp, bm_b, f_b, c_b, xorg, lutb, fw,
+                                           g.xstride, g.word_bits, t1, acc);
+            const uint32_t sb2 = bp & 31u;
+            const int have2 = __builtin_popcount(__builtin_amdgcn_alignbit(w.q1, w.q0, sb2)) +
+                              __builtin_popcount(__builtin_amdgcn_alignbit(w.q2, w.q1, sb2));
+            const int ncode2 = __builtin_popcount(__builtin_amdgcn_alignbit(w.c1, w.c0, cp & 31u));
+            if (__all(min(have2, ncode2) >= t2)) {
+              c1_group<BATCH, H, true>(w, bp, fp, cp, bm_b, f_b, c_b, xorg, lutb, fw, g.xstride,
+                                       g.word_bits, t2, acc);
+            } else {
+              for (int u = 0; u < H; ++u)
+                if (u < t2)
+                  c1_step<BATCH>(bm_l, bp, f_l, fp, c_l, cp, rowbit, C, lut, perm_l, m, smem,
+                                 g.xstride, acc);
+            }
+          } else {
+            for (int u = 0; u < U; ++u)
+              if (u < t)
+                c1_step<BATCH>(bm_l, bp, f_l, fp, c_l, cp, rowbit, C, lut, perm_l, m, smem,
+                               g.xstride, acc);
+          }
         }
       }
     } else if (pl.c_in_lds) {
