@@ -652,10 +652,20 @@ __device__ __forceinline__ C2Raw c2raw(const uint32_t* bm_l, const uint32_t* f_l
 
 typedef __attribute__((address_space(3))) const uint8_t lds_u8v;
 
+// Kept positions in the 64-bit keep window of w at bp.
+__device__ __forceinline__ int c2_have(const C2Raw& w, uint32_t bp) {
+  const uint32_t sb = bp & 31u;
+  return __builtin_popcount(__builtin_amdgcn_alignbit(w.q1, w.q0, sb)) +
+         __builtin_popcount(__builtin_amdgcn_alignbit(w.q2, w.q1, sb));
+}
+
 // U values from the windows in w.  MASKED: slots u >= t add nothing (the
 // part's last group; bit 63 of the keep window set keeps their reads in range).
+// ADVANCE (the default when not MASKED): the positions move past the U slots
+// and w receives the next windows (for a masked group, right only for lanes
+// whose t is U).
 //   eorg  LDS byte address of the shared exponent of staged bitmap word 0
-template <int BATCH, int U, bool MASKED>
+template <int BATCH, int U, bool MASKED, bool ADVANCE = !MASKED>
 __device__ __forceinline__ void c2_group(C2Raw& w, uint32_t& bp, uint32_t& fp,
                                          const uint32_t* bm_l, const uint32_t* f_l,
                                          uint32_t xorg, uint32_t eorg, uint32_t lutb, int fw,
@@ -679,7 +689,7 @@ __device__ __forceinline__ void c2_group(C2Raw& w, uint32_t& bp, uint32_t& fp,
     xa[u] = xorg + 2u * pos;
     ea[u] = eorg + (pos >> 5);
   }
-  if (!MASKED) {
+  if (ADVANCE) {
     bp = base + p + 1u;
     fp += (uint32_t)(U * fw);
   }
@@ -693,7 +703,7 @@ __device__ __forceinline__ void c2_group(C2Raw& w, uint32_t& bp, uint32_t& fp,
 #pragma unroll
     for (int bb = 0; bb < BATCH; ++bb) xv[bb][u] = x_at_addr(xa[u] + bb * xstride);
   }
-  if (!MASKED) w = c2raw(bm_l, f_l, bp, fp);
+  if (ADVANCE) w = c2raw(bm_l, f_l, bp, fp);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int u = 0; u < U; ++u) {
@@ -901,11 +911,28 @@ __global__ void __launch_bounds__(kBalThreads) k_gemv_c2_bal(SpecViewC2 v, Shape
                                     g.xstride, U, acc);
         }
         if (gi < G) {
-          for (int u = 0; u < U; ++u)
-            c2_step<BATCH>(bm_l, bp, f_l, fp, rowbit, C, lut, eb0, fw, ebias, smem, g.xstride,
-                           acc);
+          // some lane's keep window holds fewer than U positions: the group as
+          // two parts on the fast path, value by value only if a part falls short
+          constexpr int H1 = U / 2, H2 = U - U / 2;
+          if (__all(c2_have(w, bp) >= H1)) {
+            c2_group<BATCH, H1, false>(w, bp, fp, bm_l, f_l, xorg, eorg, lutb, fw, ebias,
+                                       g.xstride, H1, acc);
+          } else {
+            for (int u = 0; u < H1; ++u)
+              c2_step<BATCH>(bm_l, bp, f_l, fp, rowbit, C, lut, eb0, fw, ebias, smem, g.xstride,
+                             acc);
+            w = c2raw(bm_l, f_l, bp, fp);
+          }
+          if (__all(c2_have(w, bp) >= H2)) {
+            c2_group<BATCH, H2, false>(w, bp, fp, bm_l, f_l, xorg, eorg, lutb, fw, ebias,
+                                       g.xstride, H2, acc);
+          } else {
+            for (int u = 0; u < H2; ++u)
+              c2_step<BATCH>(bm_l, bp, f_l, fp, rowbit, C, lut, eb0, fw, ebias, smem, g.xstride,
+                             acc);
+            w = c2raw(bm_l, f_l, bp, fp);
+          }
           ++gi;
-          w = c2raw(bm_l, f_l, bp, fp);
         }
       }
       if (n_tail > 0) {
@@ -917,10 +944,26 @@ __global__ void __launch_bounds__(kBalThreads) k_gemv_c2_bal(SpecViewC2 v, Shape
           c2_group<BATCH, U, true>(w, bp, fp, bm_l, f_l, xorg, eorg, lutb, fw, ebias, g.xstride,
                                    t, acc);
         } else {
-          for (int u = 0; u < U; ++u)
-            if (u < t)
-              c2_step<BATCH>(bm_l, bp, f_l, fp, rowbit, C, lut, eb0, fw, ebias, smem, g.xstride,
-                             acc);
+          constexpr int H1 = U / 2, H2 = U - U / 2;
+          const int t1 = t < H1 ? t : H1, t2 = t - t1;
+          if (__all(have >= t1)) {
+            c2_group<BATCH, H1, true, true>(w, bp, fp, bm_l, f_l, xorg, eorg, lutb, fw, ebias,
+                                            g.xstride, t1, acc);
+            if (__all(c2_have(w, bp) >= t2)) {
+              c2_group<BATCH, H2, true>(w, bp, fp, bm_l, f_l, xorg, eorg, lutb, fw, ebias,
+                                        g.xstride, t2, acc);
+            } else {
+              for (int u = 0; u < H2; ++u)
+                if (u < t2)
+                  c2_step<BATCH>(bm_l, bp, f_l, fp, rowbit, C, lut, eb0, fw, ebias, smem,
+                                 g.xstride, acc);
+            }
+          } else {
+            for (int u = 0; u < U; ++u)
+              if (u < t)
+                c2_step<BATCH>(bm_l, bp, f_l, fp, rowbit, C, lut, eb0, fw, ebias, smem, g.xstride,
+                               acc);
+          }
         }
       }
     } else {
