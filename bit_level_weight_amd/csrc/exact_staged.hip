@@ -139,6 +139,23 @@ __device__ __forceinline__ PRaw praw(uint32_t sb, uint32_t bp, uint32_t yp, uint
               ldw(ca), ldw(ca + 4)};
 }
 
+// Whether the windows in w hold t values: t keep (or pruned) positions in the
+// 64-bit window at bp and t codes in the 32-bit window at cp.
+__device__ __forceinline__ bool ok1_kept(const KRaw& w, uint32_t bp, uint32_t cp, int t) {
+  const uint32_t sbit = bp & 31u;
+  const int have = __builtin_popcount(__builtin_amdgcn_alignbit(w.q1, w.q0, sbit)) +
+                   __builtin_popcount(__builtin_amdgcn_alignbit(w.q2, w.q1, sbit));
+  const int ncode = __builtin_popcount(__builtin_amdgcn_alignbit(w.c1, w.c0, cp & 31u));
+  return min(have, ncode) >= t;
+}
+__device__ __forceinline__ bool ok1_pruned(const PRaw& w, uint32_t bp, uint32_t cp, int t) {
+  const uint32_t sbit = bp & 31u;
+  const int have = __builtin_popcount(~__builtin_amdgcn_alignbit(w.q1, w.q0, sbit)) +
+                   __builtin_popcount(~__builtin_amdgcn_alignbit(w.q2, w.q1, sbit));
+  const int ncode = __builtin_popcount(__builtin_amdgcn_alignbit(w.c1, w.c0, cp & 31u));
+  return min(have, ncode) >= t;
+}
+
 // U kept values.  With MASKED, slots u >= t write to the lane's dummy slot (a
 // set bit 63 of the keep window and a set code bit 31 keep their positions
 // and ranks in range), and only lanes with t == U move on: a lane with fewer
@@ -209,13 +226,13 @@ __device__ __forceinline__ void kept_group(KRaw& w, uint32_t& bp, uint32_t& fp, 
   }
 }
 
-// kPU pruned values (positions: zero bits of the bitmap); MASKED as for the
-// kept groups.
-template <bool MASKED>
+// U <= kPU pruned values (positions: zero bits of the bitmap); MASKED as for
+// the kept groups.
+template <int U, bool MASKED>
 __device__ __forceinline__ void pruned_group(PRaw& w, uint32_t& bp, uint32_t& yp, uint32_t& cp,
                                              uint32_t sb, uint32_t torg, uint32_t plutb,
                                              uint32_t dummy, int t) {
-  constexpr int U = kPU;
+  static_assert(U <= 8, "pruned bytes come from two 32-bit windows");
   const uint32_t sbit = bp & 31u;
   const uint32_t lo0 = ~__builtin_amdgcn_alignbit(w.q1, w.q0, sbit);
   const uint32_t hi0 = ~__builtin_amdgcn_alignbit(w.q2, w.q1, sbit) | (MASKED ? 0x80000000u : 0u);
@@ -608,9 +625,28 @@ __global__ void __launch_bounds__(64 * kWaves) k_exact_staged(SpecViewC1 sv, Ver
             kept_group<KU, KLUT, true>(w, bp, fp, lp, cp, sb, torg, klutb, dummy, fw, lw, lwid, m,
                                        t);
           } else {
-            for (int u = 0; u < KU; ++u)
-              if (u < t) kept_step(sb, bp, bm_end, fp, lp, cp, nullptr, torg, ps, fw, lw, lwid, m);
-            w = kraw(sb, bp, fp, lp, cp);
+            // some lane's windows hold fewer than its t values: the group in two
+            // halves on the fast path (a lane whose first half is short of its
+            // slots has no second half), value by value only if a half falls short
+            constexpr int H1 = KU / 2, H2 = KU - KU / 2;
+            const int t1 = t < H1 ? t : H1, t2 = t - t1;
+            if (__all(ok1_kept(w, bp, cp, t1))) {
+              kept_group<H1, KLUT, true>(w, bp, fp, lp, cp, sb, torg, klutb, dummy, fw, lw, lwid,
+                                         m, t1);
+              if (__all(ok1_kept(w, bp, cp, t2))) {
+                kept_group<H2, KLUT, true>(w, bp, fp, lp, cp, sb, torg, klutb, dummy, fw, lw,
+                                           lwid, m, t2);
+              } else {
+                for (int u = 0; u < H2; ++u)
+                  if (u < t2)
+                    kept_step(sb, bp, bm_end, fp, lp, cp, nullptr, torg, ps, fw, lw, lwid, m);
+                w = kraw(sb, bp, fp, lp, cp);
+              }
+            } else {
+              for (int u = 0; u < KU; ++u)
+                if (u < t) kept_step(sb, bp, bm_end, fp, lp, cp, nullptr, torg, ps, fw, lw, lwid, m);
+              w = kraw(sb, bp, fp, lp, cp);
+            }
           }
         }
       } else {
@@ -652,13 +688,27 @@ __global__ void __launch_bounds__(64 * kWaves) k_exact_staged(SpecViewC1 sv, Ver
           const int ncode = __builtin_popcount(__builtin_amdgcn_alignbit(w.c1, w.c0, cp & 31u));
           const bool ok = min(have, ncode) >= t;
           if (__all(t == kPU && ok)) {
-            pruned_group<false>(w, bp, yp, cp, sb, torg, plutb, dummy, kPU);
+            pruned_group<kPU, false>(w, bp, yp, cp, sb, torg, plutb, dummy, kPU);
           } else if (__all(ok)) {
-            pruned_group<true>(w, bp, yp, cp, sb, torg, plutb, dummy, t);
+            pruned_group<kPU, true>(w, bp, yp, cp, sb, torg, plutb, dummy, t);
           } else {
-            for (int u = 0; u < kPU; ++u)
-              if (u < t) pruned_step(sb, bp, bm_end, yp, cp, nullptr, torg, pv);
-            w = praw(sb, bp, yp, cp);
+            // in two halves, as for the kept values
+            constexpr int H1 = kPU / 2, H2 = kPU - kPU / 2;
+            const int t1 = t < H1 ? t : H1, t2 = t - t1;
+            if (__all(ok1_pruned(w, bp, cp, t1))) {
+              pruned_group<H1, true>(w, bp, yp, cp, sb, torg, plutb, dummy, t1);
+              if (__all(ok1_pruned(w, bp, cp, t2))) {
+                pruned_group<H2, true>(w, bp, yp, cp, sb, torg, plutb, dummy, t2);
+              } else {
+                for (int u = 0; u < H2; ++u)
+                  if (u < t2) pruned_step(sb, bp, bm_end, yp, cp, nullptr, torg, pv);
+                w = praw(sb, bp, yp, cp);
+              }
+            } else {
+              for (int u = 0; u < kPU; ++u)
+                if (u < t) pruned_step(sb, bp, bm_end, yp, cp, nullptr, torg, pv);
+              w = praw(sb, bp, yp, cp);
+            }
           }
         }
       } else {
