@@ -409,6 +409,30 @@ struct KvVec {
       vcr.init(reinterpret_cast<const uint32_t*>(vr + kv.vo[4]), poff == 0xFFFFFFFFu ? 0u : poff);
     }
   }
+  // Draft decode from copies of the chunk's speculation sections in shared
+  // memory (see StagedSpec): bitmap words, fields from bit fbit of fl, shared
+  // exponents (C-2) and, when cl is set, codes from bit cbit of cl.  Without
+  // cl the codes are read from global memory as in init.
+  __device__ __forceinline__ void init_staged(const KvDev& kv, int s, int64_t tok,
+                                              const uint32_t* bml, const uint32_t* fl,
+                                              uint64_t fbit, const uint8_t* shl,
+                                              const uint32_t* cl, uint64_t cbit) {
+    const uint8_t* sr = kv.spec + s * kv.sstride;
+    m = kv.m;
+    bm = bml;
+    fr.init(fl, fbit);
+    if (FMT == CASS_FMT_C1_UNARY) {
+      perm_s = sr + kv.so[0];
+      if (cl) {
+        cr.init(cl, cbit);
+      } else {
+        const uint32_t off = reinterpret_cast<const uint32_t*>(sr + kv.so[2])[tok];
+        cr.init(reinterpret_cast<const uint32_t*>(sr + kv.so[4]), off == 0xFFFFFFFFu ? 0u : off);
+      }
+    } else {
+      shexp = shl;
+    }
+  }
   // read the rank tables from (shared-memory) copies instead
   __device__ __forceinline__ void use_tables(const uint8_t* ps, const uint8_t* pv) {
     perm_s = ps;
@@ -480,7 +504,18 @@ struct AttnArgs {
   int64_t T;          // tokens in the cache
   int nchunks;
   float* part;        // [H][nchunks][rows][2 + D]
+  int fcap, ccap;     // draft: shared-memory words per stream for fields and codes
 };
+
+// Draft attention: the chunk's speculation sections of K and V, copied to
+// shared memory before the decode (words past a section's end read as 0).
+// Per stream: keep words [kChunk][D/32], fields (fcap words from the word
+// holding the chunk's first field bit), codes (C-1: ccap words from the word
+// holding the first token's first code bit) or shared exponents (C-2:
+// [kChunk][D/32] bytes).
+__host__ __device__ __forceinline__ int staged_words(int fcap, int ccap, int fmt) {
+  return kChunk * (kDim / 32) + fcap + (fmt == CASS_FMT_C1_UNARY ? ccap : kChunk);
+}
 
 // MAXR: a bound on the query rows (nq * G) the launch serves.  Shared
 // memory: queries [MAXR][128] fp32, scores [MAXR][kChunk] fp32, value tile
@@ -510,17 +545,89 @@ __global__ void __launch_bounds__(2 * kChunk) k_kv_attn(KvDev kv, AttnArgs a) {
     qf[idx] = r < rows ? bf16_bits_to_float(a.q[((int64_t)qi * a.Hq + h * a.G + g) * kDim + d])
                        : 0.f;
   }
+  // draft: stage the chunk's speculation sections of K and V
+  const int64_t t0 = (int64_t)c * kChunk;
+  const int fwid = FMT == CASS_FMT_C1_UNARY ? 1 + kv.m : 2 + kv.m;
+  const int sw = staged_words(a.fcap, a.ccap, FMT);
+  uint32_t* stg = reinterpret_cast<uint32_t*>(vt + kChunk * kVStride);
+  const int64_t fw0 = (t0 * kv.k * fwid) >> 5;  // first staged field word
+  int64_t cw0[2] = {0, 0};                        // first staged code word per stream
+  if (!EXACT) {
+    for (int j = 0; j < 2; ++j) {
+      const uint8_t* sr = kv.spec + (2 * h + j) * kv.sstride;
+      uint32_t* base = stg + j * sw;
+      const uint32_t* bmg = reinterpret_cast<const uint32_t*>(sr + kv.so[1]);
+      const int64_t bm_words = kv.T_max * (kDim / 32);
+      for (int i = tid; i < kChunk * (kDim / 32); i += 2 * kChunk) {
+        const int64_t gi = t0 * (kDim / 32) + i;
+        base[i] = gi < bm_words ? bmg[gi] : 0u;
+      }
+      const uint32_t* fg = reinterpret_cast<const uint32_t*>(sr + kv.so[3]);
+      const int64_t f_words = (kv.T_max * kv.k * fwid + 31) / 32;
+      for (int i = tid; i < a.fcap; i += 2 * kChunk) {
+        const int64_t gi = fw0 + i;
+        base[kChunk * (kDim / 32) + i] = gi < f_words ? fg[gi] : 0u;
+      }
+      uint32_t* rest = base + kChunk * (kDim / 32) + a.fcap;
+      if (FMT == CASS_FMT_C1_UNARY) {
+        const uint32_t o0 = reinterpret_cast<const uint32_t*>(sr + kv.so[2])[t0];
+        cw0[j] = o0 == 0xFFFFFFFFu ? 0 : (int64_t)(o0 >> 5);
+        const uint32_t* cg = reinterpret_cast<const uint32_t*>(sr + kv.so[4]);
+        const int64_t c_words = (kv.ccap + 31) / 32;
+        for (int i = tid; i < a.ccap; i += 2 * kChunk) {
+          const int64_t gi = cw0[j] + i;
+          rest[i] = gi < c_words ? cg[gi] : 0u;
+        }
+      } else {
+        // shared exponents: D/32 = 4 bytes, one word, per token
+        const uint32_t* eg = reinterpret_cast<const uint32_t*>(sr + kv.so[2]);
+        for (int i = tid; i < kChunk; i += 2 * kChunk) {
+          const int64_t gi = t0 + i;
+          rest[i] = gi < kv.T_max ? eg[gi] : 0u;
+        }
+      }
+    }
+  }
   __syncthreads();
   const int ti = tid & (kChunk - 1);
   const int64_t tok = (int64_t)c * kChunk + ti;
   const bool live = tok < a.T;
+  // the draft decoder of this thread's token in stream j (0: K, 1: V) over
+  // the staged words; its codes from shared memory when they lie inside the
+  // staged run, else from global memory
+  auto init_draft = [&](KvVec<EXACT, FMT>& dec, int j) {
+    const int s = 2 * h + j;
+    uint32_t* base = stg + j * sw;
+    uint32_t* rest = base + kChunk * (kDim / 32) + a.fcap;
+    const uint64_t fbit = (uint64_t)tok * kv.k * fwid - (uint64_t)fw0 * 32;
+    const uint32_t* cl = nullptr;
+    uint64_t cbit = 0;
+    if (FMT == CASS_FMT_C1_UNARY) {
+      const uint8_t* sr = kv.spec + s * kv.sstride;
+      const uint32_t* offs = reinterpret_cast<const uint32_t*>(sr + kv.so[2]);
+      const uint32_t off = offs[tok];
+      const unsigned long long end = tok + 1 < a.T ? (unsigned long long)offs[tok + 1]
+                                                   : kv.state[2 + 2 * s];
+      // (the reader looks up to three words past the code it is on)
+      if (off != 0xFFFFFFFFu && end != 0xFFFFFFFFull && (int64_t)(off >> 5) >= cw0[j] &&
+          (int64_t)(end >> 5) + 4 < cw0[j] + a.ccap) {
+        cl = rest;
+        cbit = (uint64_t)off - (uint64_t)cw0[j] * 32;
+      }
+    }
+    dec.init_staged(kv, s, tok, base + ti * (kDim / 32), base + kChunk * (kDim / 32), fbit,
+                    reinterpret_cast<const uint8_t*>(rest + ti), cl, cbit);
+  };
   if (tid < kChunk) {
     float s[MAXR];
 #pragma unroll
     for (int r = 0; r < MAXR; ++r) s[r] = 0.f;
     if (live) {  // scores: kept positions, then (exact) pruned positions
       KvVec<EXACT, FMT> dec;
-      dec.init(kv, 2 * h, tok);
+      if (EXACT)
+        dec.init(kv, 2 * h, tok);
+      else
+        init_draft(dec, 0);
       dec.use_tables(tabs[0], tabs[1]);
       for (int w = 0; w < kDim / 32; ++w) {
         const uint32_t word = dec.bm[w];
@@ -554,7 +661,10 @@ __global__ void __launch_bounds__(2 * kChunk) k_kv_attn(KvDev kv, AttnArgs a) {
     uint16_t* row = vt + ti * kVStride;
     if (live) {
       KvVec<EXACT, FMT> dec;
-      dec.init(kv, 2 * h + 1, tok);
+      if (EXACT)
+        dec.init(kv, 2 * h + 1, tok);
+      else
+        init_draft(dec, 1);
       dec.use_tables(tabs[2], tabs[3]);
       dec.all(kDim, row);
     } else {
@@ -765,7 +875,8 @@ unsigned grid_of(int64_t n, int per) {
 template <bool EXACT, int MAXR, int FMT>
 hipError_t attn_launch_f(const KvDev& d, const AttnArgs& a, int H, size_t, hipStream_t stream) {
   const size_t lds = (size_t)MAXR * kDim * 4 + (size_t)MAXR * kChunk * 4 +
-                     (size_t)kChunk * kVStride * 2;
+                     (size_t)kChunk * kVStride * 2 +
+                     (EXACT ? 0 : (size_t)2 * staged_words(a.fcap, a.ccap, FMT) * 4);
   hipError_t e = hipFuncSetAttribute((const void*)&k_kv_attn<EXACT, MAXR, FMT>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
@@ -802,6 +913,13 @@ int run_attention(const cass_kv* kv, const uint16_t* q, int nq, int n_q_heads, f
   a.nchunks = (int)((kv->tokens + kChunk - 1) / kChunk);
   if (a.nchunks > kMaxChunksMerge) return report(CASS_ERR_UNSUPPORTED, "attention over more than 512K tokens");
   a.part = (float*)ws;
+  {
+    // draft staging: every field of the chunk, and codes averaging up to 4
+    // bits per kept value (longer runs read their codes from global memory)
+    const int fwid = fmt_of(&kv->p) == CASS_FMT_C1_UNARY ? 1 + kv->p.mant_bits : 2 + kv->p.mant_bits;
+    a.fcap = (int)(((int64_t)kChunk * kv->p.keep * fwid + 31) / 32) + 8;
+    a.ccap = (int)((int64_t)kChunk * kv->p.keep * 4 / 32) + 64;
+  }
   const KvDev d = dev_of(kv);
   const size_t lds = 0;  // per launch, from the row bound (attn_launch_f)
   const int rows = nq * G;
