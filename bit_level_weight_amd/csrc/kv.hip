@@ -518,14 +518,14 @@ __host__ __device__ __forceinline__ int staged_words(int fcap, int ccap, int fmt
 }
 
 // MAXR: a bound on the query rows (nq * G) the launch serves.  Shared
-// memory: queries [MAXR][128] fp32, scores [MAXR][kChunk] fp32, value tile
+// memory: queries [128][MAXR] fp32 (a key position's entries side by side), scores [MAXR][kChunk] fp32, value tile
 // [kChunk][130] bf16 (about 37 KB for one query of four heads).
 template <bool EXACT, int MAXR, int FMT>
 __global__ void __launch_bounds__(2 * kChunk) k_kv_attn(KvDev kv, AttnArgs a) {
   // threads 0..kChunk-1: one token's key and its scores; threads kChunk..:
   // the same token's value row into the tile (the two decodes run side by side)
   extern __shared__ __align__(16) uint8_t smem[];
-  float* qf = reinterpret_cast<float*>(smem);                // [MAXR][128]
+  float* qf = reinterpret_cast<float*>(smem);                // [128][MAXR]
   float* sc = qf + MAXR * kDim;                              // [MAXR][kChunk]
   uint16_t* vt = reinterpret_cast<uint16_t*>(sc + MAXR * kChunk);  // [kChunk][130]
   __shared__ float red[MAXR][kChunk / 64];
@@ -542,8 +542,8 @@ __global__ void __launch_bounds__(2 * kChunk) k_kv_attn(KvDev kv, AttnArgs a) {
   for (int idx = tid; idx < MAXR * kDim; idx += 2 * kChunk) {  // rows past `rows` stay zero
     const int r = idx / kDim, d = idx % kDim;
     const int qi = r / a.G, g = r % a.G;
-    qf[idx] = r < rows ? bf16_bits_to_float(a.q[((int64_t)qi * a.Hq + h * a.G + g) * kDim + d])
-                       : 0.f;
+    qf[d * MAXR + r] = r < rows ? bf16_bits_to_float(a.q[((int64_t)qi * a.Hq + h * a.G + g) * kDim + d])
+                                : 0.f;
   }
   // draft: stage the chunk's speculation sections of K and V
   const int64_t t0 = (int64_t)c * kChunk;
@@ -635,14 +635,14 @@ __global__ void __launch_bounds__(2 * kChunk) k_kv_attn(KvDev kv, AttnArgs a) {
           const float kvv = bf16_bits_to_float(dec.kept(w));
           const int d = w * 32 + __builtin_ctz(km);
 #pragma unroll
-          for (int r = 0; r < MAXR; ++r) s[r] = __builtin_fmaf(kvv, qf[r * kDim + d], s[r]);
+          for (int r = 0; r < MAXR; ++r) s[r] = __builtin_fmaf(kvv, qf[d * MAXR + r], s[r]);
         }
         if (EXACT) {
           for (uint32_t pm = ~word; pm; pm &= pm - 1u) {
             const float kvv = bf16_bits_to_float(dec.pruned());
             const int d = w * 32 + __builtin_ctz(pm);
 #pragma unroll
-            for (int r = 0; r < MAXR; ++r) s[r] = __builtin_fmaf(kvv, qf[r * kDim + d], s[r]);
+            for (int r = 0; r < MAXR; ++r) s[r] = __builtin_fmaf(kvv, qf[d * MAXR + r], s[r]);
           }
         }
       }
