@@ -462,6 +462,11 @@ struct KvVec {
     const uint32_t e = perm_v[vcr.unary()];
     return ((byte >> 7) << 15) | (e << 7) | (byte & 0x7F);
   }
+  // the kept values into their positions of o[0..D) (the rest left as they are)
+  __device__ __forceinline__ void kept_into(int D, uint16_t* o) {
+    for (int w = 0; w < D / 32; ++w)
+      for (uint32_t km = bm[w]; km; km &= km - 1u) o[w * 32 + __builtin_ctz(km)] = (uint16_t)kept(w);
+  }
   // all D positions into o[0..D)
   __device__ __forceinline__ void all(int D, uint16_t* o) {
     for (int w = 0; w < D / 32; ++w) {
@@ -588,6 +593,13 @@ __global__ void __launch_bounds__(2 * kChunk) k_kv_attn(KvDev kv, AttnArgs a) {
       }
     }
   }
+  if (!EXACT) {
+    // the draft value tile starts zero-filled (pruned positions and tokens past
+    // the end); the decoders write the kept values only
+    typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+    u32x4v* vt4 = reinterpret_cast<u32x4v*>(vt);
+    for (int i = tid; i < kChunk * kVStride * 2 / 16; i += 2 * kChunk) vt4[i] = u32x4v{0, 0, 0, 0};
+  }
   __syncthreads();
   const int ti = tid & (kChunk - 1);
   const int64_t tok = (int64_t)c * kChunk + ti;
@@ -661,13 +673,16 @@ __global__ void __launch_bounds__(2 * kChunk) k_kv_attn(KvDev kv, AttnArgs a) {
     uint16_t* row = vt + ti * kVStride;
     if (live) {
       KvVec<EXACT, FMT> dec;
-      if (EXACT)
+      if (EXACT) {
         dec.init(kv, 2 * h + 1, tok);
-      else
+        dec.use_tables(tabs[2], tabs[3]);
+        dec.all(kDim, row);
+      } else {
         init_draft(dec, 1);
-      dec.use_tables(tabs[2], tabs[3]);
-      dec.all(kDim, row);
-    } else {
+        dec.use_tables(tabs[2], tabs[3]);
+        dec.kept_into(kDim, row);
+      }
+    } else if (EXACT) {
       for (int d = 0; d < kDim; ++d) row[d] = 0;
     }
   }
