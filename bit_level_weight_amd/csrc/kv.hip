@@ -462,6 +462,47 @@ struct KvVec {
     const uint32_t e = perm_v[vcr.unary()];
     return ((byte >> 7) << 15) | (e << 7) | (byte & 0x7F);
   }
+  // Draft decode (Cassandra-1) of the vector's k kept values in groups of 8:
+  // positions, fields and ranks of a group first (shift registers over the
+  // D = 128 keep bits, bit readers), then every rank-table read of the group
+  // at once, then use(d, bits) per value, so a group waits on shared memory
+  // once instead of once per value.  Needs every keep word non-empty (the
+  // caller checks; each word then holds the next values when the current one
+  // runs out).
+  template <typename F>
+  __device__ __forceinline__ void kept_grouped(int k, F&& use) {
+    uint32_t w0 = bm[0], w1 = bm[1], w2 = bm[2], w3 = bm[3];
+    uint32_t base = 0;
+    for (int i0 = 0; i0 < k; i0 += 8) {
+      uint32_t dd[8], ff[8], rr[8], ee[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (i0 + u < k) {
+          const bool adv = w0 == 0u;
+          w0 = adv ? w1 : w0;
+          w1 = adv ? w2 : w1;
+          w2 = adv ? w3 : w2;
+          w3 = adv ? 0u : w3;
+          base += adv ? 32u : 0u;
+          // (the mask keeps a corrupt vector's positions inside the row)
+          dd[u] = (base + (uint32_t)__builtin_ctz(w0)) & 127u;
+          w0 &= w0 - 1u;
+          ff[u] = fr.take(1 + m);
+          rr[u] = (uint32_t)cr.unary();
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (i0 + u < k) ee[u] = perm_s[rr[u]];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (i0 + u < k) {
+          const uint32_t f = ff[u];
+          use(dd[u], ((f >> m) << 15) | (ee[u] << 7) | ((f & ((1u << m) - 1u)) << (7 - m)));
+        }
+      }
+    }
+  }
   // the kept values into their positions of o[0..D) (the rest left as they are)
   __device__ __forceinline__ void kept_into(int D, uint16_t* o) {
     for (int w = 0; w < D / 32; ++w)
@@ -641,6 +682,14 @@ __global__ void __launch_bounds__(2 * kChunk) k_kv_attn(KvDev kv, AttnArgs a) {
       else
         init_draft(dec, 0);
       dec.use_tables(tabs[0], tabs[1]);
+      if (!EXACT && FMT == CASS_FMT_C1_UNARY && MAXR <= 8 &&
+          __all(dec.bm[0] != 0u && dec.bm[1] != 0u && dec.bm[2] != 0u && dec.bm[3] != 0u)) {
+        dec.kept_grouped(kv.k, [&](uint32_t d, uint32_t bits) {
+          const float kvv = bf16_bits_to_float(bits);
+#pragma unroll
+          for (int r = 0; r < MAXR; ++r) s[r] = __builtin_fmaf(kvv, qf[d * MAXR + r], s[r]);
+        });
+      } else
       for (int w = 0; w < kDim / 32; ++w) {
         const uint32_t word = dec.bm[w];
         for (uint32_t km = word; km; km &= km - 1u) {
@@ -680,7 +729,11 @@ __global__ void __launch_bounds__(2 * kChunk) k_kv_attn(KvDev kv, AttnArgs a) {
       } else {
         init_draft(dec, 1);
         dec.use_tables(tabs[2], tabs[3]);
-        dec.kept_into(kDim, row);
+        if (FMT == CASS_FMT_C1_UNARY &&
+            __all(dec.bm[0] != 0u && dec.bm[1] != 0u && dec.bm[2] != 0u && dec.bm[3] != 0u))
+          dec.kept_grouped(kv.k, [&](uint32_t d, uint32_t bits) { row[d] = (uint16_t)bits; });
+        else
+          dec.kept_into(kDim, row);
       }
     } else if (EXACT) {
       for (int d = 0; d < kDim; ++d) row[d] = 0;
