@@ -559,6 +559,26 @@ struct AttnArgs {
 // holding the chunk's first field bit), codes (C-1: ccap words from the word
 // holding the first token's first code bit) or shared exponents (C-2:
 // [kChunk][D/32] bytes).
+// n words src[g0 + i] (0 past word `lim`) to dst[i], by nthr threads: eight
+// loads per thread issued before their stores, so a batch waits on memory once.
+__device__ __forceinline__ void copy_words(uint32_t* dst, const uint32_t* src, int64_t g0, int n,
+                                           int64_t lim, int tid, int nthr) {
+  for (int b = 0; b < n; b += 8 * nthr) {
+    uint32_t v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int i = b + j * nthr + tid;
+      const int64_t g = g0 + i;
+      v[j] = (i < n && g < lim) ? src[g] : 0u;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int i = b + j * nthr + tid;
+      if (i < n) dst[i] = v[j];
+    }
+  }
+}
+
 __host__ __device__ __forceinline__ int staged_words(int fcap, int ccap, int fmt) {
   return kChunk * (kDim / 32) + fcap + (fmt == CASS_FMT_C1_UNARY ? ccap : kChunk);
 }
@@ -579,12 +599,14 @@ __global__ void __launch_bounds__(2 * kChunk) k_kv_attn(KvDev kv, AttnArgs a) {
   const int h = blockIdx.x, c = blockIdx.y;
   const int rows = a.nq * a.G;
   const int tid = threadIdx.x;
+#pragma unroll
   for (int i = tid; i < 4 * 256; i += 2 * kChunk) {
     const int s = 2 * h + (i >> 9), which = (i >> 8) & 1;
     const uint8_t* src = which ? kv.verif + s * kv.vstride + kv.vo[0] : kv.spec + s * kv.sstride + kv.so[0];
     tabs[i >> 8][i & 255] = src[i & 255];
   }
   // query rows of this KV head: row r = qi * G + g  (query qi, head h*G + g)
+#pragma unroll
   for (int idx = tid; idx < MAXR * kDim; idx += 2 * kChunk) {  // rows past `rows` stay zero
     const int r = idx / kDim, d = idx % kDim;
     const int qi = r / a.G, g = r % a.G;
@@ -602,35 +624,20 @@ __global__ void __launch_bounds__(2 * kChunk) k_kv_attn(KvDev kv, AttnArgs a) {
     for (int j = 0; j < 2; ++j) {
       const uint8_t* sr = kv.spec + (2 * h + j) * kv.sstride;
       uint32_t* base = stg + j * sw;
-      const uint32_t* bmg = reinterpret_cast<const uint32_t*>(sr + kv.so[1]);
-      const int64_t bm_words = kv.T_max * (kDim / 32);
-      for (int i = tid; i < kChunk * (kDim / 32); i += 2 * kChunk) {
-        const int64_t gi = t0 * (kDim / 32) + i;
-        base[i] = gi < bm_words ? bmg[gi] : 0u;
-      }
-      const uint32_t* fg = reinterpret_cast<const uint32_t*>(sr + kv.so[3]);
-      const int64_t f_words = (kv.T_max * kv.k * fwid + 31) / 32;
-      for (int i = tid; i < a.fcap; i += 2 * kChunk) {
-        const int64_t gi = fw0 + i;
-        base[kChunk * (kDim / 32) + i] = gi < f_words ? fg[gi] : 0u;
-      }
+      copy_words(base, reinterpret_cast<const uint32_t*>(sr + kv.so[1]), t0 * (kDim / 32),
+                 kChunk * (kDim / 32), kv.T_max * (kDim / 32), tid, 2 * kChunk);
+      copy_words(base + kChunk * (kDim / 32), reinterpret_cast<const uint32_t*>(sr + kv.so[3]), fw0,
+                 a.fcap, (kv.T_max * kv.k * fwid + 31) / 32, tid, 2 * kChunk);
       uint32_t* rest = base + kChunk * (kDim / 32) + a.fcap;
       if (FMT == CASS_FMT_C1_UNARY) {
         const uint32_t o0 = reinterpret_cast<const uint32_t*>(sr + kv.so[2])[t0];
         cw0[j] = o0 == 0xFFFFFFFFu ? 0 : (int64_t)(o0 >> 5);
-        const uint32_t* cg = reinterpret_cast<const uint32_t*>(sr + kv.so[4]);
-        const int64_t c_words = (kv.ccap + 31) / 32;
-        for (int i = tid; i < a.ccap; i += 2 * kChunk) {
-          const int64_t gi = cw0[j] + i;
-          rest[i] = gi < c_words ? cg[gi] : 0u;
-        }
+        copy_words(rest, reinterpret_cast<const uint32_t*>(sr + kv.so[4]), cw0[j], a.ccap,
+                   (kv.ccap + 31) / 32, tid, 2 * kChunk);
       } else {
         // shared exponents: D/32 = 4 bytes, one word, per token
-        const uint32_t* eg = reinterpret_cast<const uint32_t*>(sr + kv.so[2]);
-        for (int i = tid; i < kChunk; i += 2 * kChunk) {
-          const int64_t gi = t0 + i;
-          rest[i] = gi < kv.T_max ? eg[gi] : 0u;
-        }
+        copy_words(rest, reinterpret_cast<const uint32_t*>(sr + kv.so[2]), t0, kChunk, kv.T_max,
+                   tid, 2 * kChunk);
       }
     }
   }
