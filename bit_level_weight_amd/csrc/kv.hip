@@ -16,6 +16,7 @@
 #include "bits.hpp"
 #include "decoders.hpp"
 #include "internal.hpp"
+#include "staged_decode.hpp"
 
 namespace cass {
 
@@ -372,6 +373,10 @@ __global__ void __launch_bounds__(64 * kWaves) k_kv_pack(KvDev kv, const uint16_
 template <bool EXACT, int FMT>
 struct KvVec {
   BitReader fr, cr, lr, vcr, pr;
+  // staged draft decode: field and code bit positions in shared-memory words
+  const uint32_t* fw_l;
+  const uint32_t* cw_l;
+  uint32_t fpos, cpos;
   const uint8_t* perm_s;
   const uint8_t* perm_v;
   const uint8_t* shexp;
@@ -421,6 +426,10 @@ struct KvVec {
     m = kv.m;
     bm = bml;
     fr.init(fl, fbit);
+    fw_l = fl;
+    fpos = (uint32_t)fbit;
+    cw_l = cl;
+    cpos = (uint32_t)cbit;
     if (FMT == CASS_FMT_C1_UNARY) {
       perm_s = sr + kv.so[0];
       if (cl) {
@@ -497,6 +506,84 @@ struct KvVec {
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         if (i0 + u < k) {
+          const uint32_t f = ff[u];
+          use(dd[u], ((f >> m) << 15) | (ee[u] << 7) | ((f & ((1u << m) - 1u)) << (7 - m)));
+        }
+      }
+    }
+  }
+  // The same, Cassandra-1 with the token's fields and codes staged (fw_l,
+  // cw_l): 32-bit field and code windows read from shared memory (two words
+  // and a funnel shift each), a rank as the zeros before the window's next
+  // one, eight values per window.  A group whose code window holds fewer ones
+  // than its values for some lane is decoded value by value.  Needs 1 + m <= 4
+  // and every keep word non-empty (the caller checks).
+  template <typename F>
+  __device__ __forceinline__ void kept_windows(int k, F&& use) {
+    uint32_t w0 = bm[0], w1 = bm[1], w2 = bm[2], w3 = bm[3];
+    uint32_t base = 0;
+    const uint32_t fw = 1u + (uint32_t)m, fmask = (1u << fw) - 1u;
+    for (int i0 = 0; i0 < k; i0 += 8) {
+      const int ng = k - i0 < 8 ? k - i0 : 8;  // values in this group (the same for every lane)
+      const uint32_t wf = window32(fw_l, fpos);
+      const uint32_t wc0 = window32(cw_l, cpos);
+      uint32_t dd[8], ff[8], rr[8], ee[8];
+      if (__all(__builtin_popcount(wc0) >= ng)) {
+        uint32_t wc = wc0;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          if (u < ng) {
+            const bool adv = w0 == 0u;
+            w0 = adv ? w1 : w0;
+            w1 = adv ? w2 : w1;
+            w2 = adv ? w3 : w2;
+            w3 = adv ? 0u : w3;
+            base += adv ? 32u : 0u;
+            dd[u] = (base + (uint32_t)__builtin_ctz(w0)) & 127u;
+            w0 &= w0 - 1u;
+            ff[u] = __builtin_amdgcn_ubfe(wf, (uint32_t)u * fw, fw);
+            const uint32_t r = (uint32_t)__builtin_ctz(wc);
+            rr[u] = r;
+            wc = (wc >> r) >> 1;
+          }
+        }
+        // bits the codes took: the window was shifted right by that many
+        cpos += (wc ? (uint32_t)__builtin_clz(wc) : 32u) - (uint32_t)__builtin_clz(wc0);
+      } else {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          if (u < ng) {
+            const bool adv = w0 == 0u;
+            w0 = adv ? w1 : w0;
+            w1 = adv ? w2 : w1;
+            w2 = adv ? w3 : w2;
+            w3 = adv ? 0u : w3;
+            base += adv ? 32u : 0u;
+            dd[u] = (base + (uint32_t)__builtin_ctz(w0)) & 127u;
+            w0 &= w0 - 1u;
+            ff[u] = window32(fw_l, fpos + (uint32_t)u * fw) & fmask;
+            // a code of any length (at most 256 bits; the bound keeps a
+            // corrupt stream from running on)
+            uint32_t r = 0, wv = window32(cw_l, cpos);
+            for (int it = 0; it < 8 && wv == 0u; ++it) {
+              r += 32u;
+              cpos += 32u;
+              wv = window32(cw_l, cpos);
+            }
+            const uint32_t t = (uint32_t)__builtin_ctz(wv | (wv ? 0u : 0x80000000u));
+            r += t;
+            cpos += t + 1u;
+            rr[u] = r < 256u ? r : 255u;
+          }
+        }
+      }
+      fpos += (uint32_t)ng * fw;
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (u < ng) ee[u] = perm_s[rr[u]];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (u < ng) {
           const uint32_t f = ff[u];
           use(dd[u], ((f >> m) << 15) | (ee[u] << 7) | ((f & ((1u << m) - 1u)) << (7 - m)));
         }
@@ -689,7 +776,15 @@ __global__ void __launch_bounds__(2 * kChunk) k_kv_attn(KvDev kv, AttnArgs a) {
       else
         init_draft(dec, 0);
       dec.use_tables(tabs[0], tabs[1]);
-      if (!EXACT && FMT == CASS_FMT_C1_UNARY && MAXR <= 8 &&
+      if (!EXACT && FMT == CASS_FMT_C1_UNARY && MAXR <= 8 && kv.m <= 3 &&
+          __all(dec.bm[0] != 0u && dec.bm[1] != 0u && dec.bm[2] != 0u && dec.bm[3] != 0u &&
+                dec.cw_l != nullptr)) {
+        dec.kept_windows(kv.k, [&](uint32_t d, uint32_t bits) {
+          const float kvv = bf16_bits_to_float(bits);
+#pragma unroll
+          for (int r = 0; r < MAXR; ++r) s[r] = __builtin_fmaf(kvv, qf[d * MAXR + r], s[r]);
+        });
+      } else if (!EXACT && FMT == CASS_FMT_C1_UNARY && MAXR <= 8 &&
           __all(dec.bm[0] != 0u && dec.bm[1] != 0u && dec.bm[2] != 0u && dec.bm[3] != 0u)) {
         dec.kept_grouped(kv.k, [&](uint32_t d, uint32_t bits) {
           const float kvv = bf16_bits_to_float(bits);
@@ -736,7 +831,11 @@ __global__ void __launch_bounds__(2 * kChunk) k_kv_attn(KvDev kv, AttnArgs a) {
       } else {
         init_draft(dec, 1);
         dec.use_tables(tabs[2], tabs[3]);
-        if (FMT == CASS_FMT_C1_UNARY &&
+        if (FMT == CASS_FMT_C1_UNARY && kv.m <= 3 &&
+            __all(dec.bm[0] != 0u && dec.bm[1] != 0u && dec.bm[2] != 0u && dec.bm[3] != 0u &&
+                  dec.cw_l != nullptr))
+          dec.kept_windows(kv.k, [&](uint32_t d, uint32_t bits) { row[d] = (uint16_t)bits; });
+        else if (FMT == CASS_FMT_C1_UNARY &&
             __all(dec.bm[0] != 0u && dec.bm[1] != 0u && dec.bm[2] != 0u && dec.bm[3] != 0u))
           dec.kept_grouped(kv.k, [&](uint32_t d, uint32_t bits) { row[d] = (uint16_t)bits; });
         else
