@@ -590,6 +590,38 @@ struct KvVec {
       }
     }
   }
+  // Cassandra-2 draft decode of the k kept values from the staged fields: four
+  // (sign, significand) fields per 32-bit window (fields of up to 8 bits), the
+  // shared exponent of a value's 32-position group from the token's four
+  // exponent bytes (one word).  Needs every keep word non-empty.
+  template <typename F>
+  __device__ __forceinline__ void kept_windows_c2(int k, F&& use) {
+    uint32_t w0 = bm[0], w1 = bm[1], w2 = bm[2], w3 = bm[3];
+    const uint32_t e4 = *reinterpret_cast<const uint32_t*>(shexp);
+    uint32_t base = 0;
+    const uint32_t fw = 2u + (uint32_t)m;
+    for (int i0 = 0; i0 < k; i0 += 4) {
+      const int ng = k - i0 < 4 ? k - i0 : 4;  // values in this group (the same for every lane)
+      const uint32_t wf = window32(fw_l, fpos);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (u < ng) {
+          const bool adv = w0 == 0u;
+          w0 = adv ? w1 : w0;
+          w1 = adv ? w2 : w1;
+          w2 = adv ? w3 : w2;
+          w3 = adv ? 0u : w3;
+          base += adv ? 32u : 0u;
+          const uint32_t d = (base + (uint32_t)__builtin_ctz(w0)) & 127u;
+          w0 &= w0 - 1u;
+          const uint32_t f = __builtin_amdgcn_ubfe(wf, (uint32_t)u * fw, fw);
+          const int E = (int)((e4 >> (8u * ((base >> 5) & 3u))) & 0xFFu);
+          use(d, mx_value_bits(f >> (m + 1), f & ((2u << m) - 1u), E, m));
+        }
+      }
+      fpos += (uint32_t)ng * fw;
+    }
+  }
   // the kept values into their positions of o[0..D) (the rest left as they are)
   __device__ __forceinline__ void kept_into(int D, uint16_t* o) {
     for (int w = 0; w < D / 32; ++w)
@@ -776,7 +808,14 @@ __global__ void __launch_bounds__(2 * kChunk) k_kv_attn(KvDev kv, AttnArgs a) {
       else
         init_draft(dec, 0);
       dec.use_tables(tabs[0], tabs[1]);
-      if (!EXACT && FMT == CASS_FMT_C1_UNARY && MAXR <= 8 && kv.m <= 3 &&
+      if (!EXACT && FMT == CASS_FMT_C2_MX32 && MAXR <= 8 && kv.m <= 6 &&
+          __all(dec.bm[0] != 0u && dec.bm[1] != 0u && dec.bm[2] != 0u && dec.bm[3] != 0u)) {
+        dec.kept_windows_c2(kv.k, [&](uint32_t d, uint32_t bits) {
+          const float kvv = bf16_bits_to_float(bits);
+#pragma unroll
+          for (int r = 0; r < MAXR; ++r) s[r] = __builtin_fmaf(kvv, qf[d * MAXR + r], s[r]);
+        });
+      } else if (!EXACT && FMT == CASS_FMT_C1_UNARY && MAXR <= 8 && kv.m <= 3 &&
           __all(dec.bm[0] != 0u && dec.bm[1] != 0u && dec.bm[2] != 0u && dec.bm[3] != 0u &&
                 dec.cw_l != nullptr)) {
         dec.kept_windows(kv.k, [&](uint32_t d, uint32_t bits) {
@@ -831,7 +870,10 @@ __global__ void __launch_bounds__(2 * kChunk) k_kv_attn(KvDev kv, AttnArgs a) {
       } else {
         init_draft(dec, 1);
         dec.use_tables(tabs[2], tabs[3]);
-        if (FMT == CASS_FMT_C1_UNARY && kv.m <= 3 &&
+        if (FMT == CASS_FMT_C2_MX32 && kv.m <= 6 &&
+            __all(dec.bm[0] != 0u && dec.bm[1] != 0u && dec.bm[2] != 0u && dec.bm[3] != 0u))
+          dec.kept_windows_c2(kv.k, [&](uint32_t d, uint32_t bits) { row[d] = (uint16_t)bits; });
+        else if (FMT == CASS_FMT_C1_UNARY && kv.m <= 3 &&
             __all(dec.bm[0] != 0u && dec.bm[1] != 0u && dec.bm[2] != 0u && dec.bm[3] != 0u &&
                   dec.cw_l != nullptr))
           dec.kept_windows(kv.k, [&](uint32_t d, uint32_t bits) { row[d] = (uint16_t)bits; });
