@@ -165,3 +165,43 @@ def test_draft_and_verify_attention(gpu, orc, T, fmt):
             vis = [Ttot - nq + i + 1 for i in range(nq)]
             ref, bound = oracle_attention(orc, rows, Kt[:Ttot, h, :], Vt[:Ttot, h, :], scale, vis)
             attn_check(gotv[:, h * G + g, :], ref, bound)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_draft_attention_uneven_tokens(gpu, orc, fmt):
+    """Draft attention on tokens the grouped decoders cannot take whole: a first
+    chunk whose keep bitmaps leave the first 32 positions empty (channels 0-31
+    scaled down) and, appended after the rank tables froze, tokens whose
+    exponents the first append never saw (long codes, short code windows)."""
+    torch, cass = gpu
+    H, Hq, k, m, T0, T = 2, 8, 38, 3, 200, 300
+    G = Hq // H
+    Kt, Vt = make_kv(T, H, 4242)
+    Kf, Vf = synth.f32_from_bf16(Kt).copy(), synth.f32_from_bf16(Vt).copy()
+    Kf[:100, :, :32] *= np.float32(1e-4)
+    Vf[:100, :, :32] *= np.float32(1e-4)
+    Kf[T0:] *= np.float32(2.0 ** -30)
+    Vf[T0:] *= np.float32(2.0 ** 12)
+    Kt, Vt = synth.bf16_from_f32(Kf), synth.bf16_from_f32(Vf)
+    cap = T + 8
+    cache = cass.KvCache(H, D, k, m, max_tokens=cap, code_cap_bits=cap * k * 64,
+                         vcode_cap_bits=cap * (D - k) * 64, fmt=fmt)
+    cache.append(dev(torch, Kt[:T0]), dev(torch, Vt[:T0]))
+    cache.append(dev(torch, Kt[T0:]), dev(torch, Vt[T0:]))
+    scale = 1.0 / np.sqrt(D)
+    q1 = synth.activations(Hq, D, 4, t0=T)
+    ws = torch.empty(cass.cass_kv_attn_ws_bytes(cache.kv, 1, Hq) + 256, dtype=torch.uint8, device="cuda")
+    out = torch.empty((Hq, D), dtype=torch.float32, device="cuda")
+    cass.cass_kv_draft_attn(cache.kv, dev(torch, q1), scale, out, ws)
+    torch.cuda.synchronize()
+    p = cache.params
+    got = out.cpu().numpy()
+    caps = (p.max_tokens, p.code_cap_bits, p.vcode_cap_bits)
+    for h in range(H):
+        sk, _, _ = orc.kv_encode(Kt[:, h, :], T0, k, m, *caps, fmt=fmt)
+        sv, _, _ = orc.kv_encode(Vt[:, h, :], T0, k, m, *caps, fmt=fmt)
+        Kd = orc.kv_decode(sk, T, D, k, m, *caps, fmt=fmt)
+        Vd = orc.kv_decode(sv, T, D, k, m, *caps, fmt=fmt)
+        assert not (Kd[:100, :32].any() or Vd[:100, :32].any()), "first keep word not empty"
+        ref, bound = oracle_attention(orc, q1[h * G:(h + 1) * G], Kd, Vd, scale)
+        attn_check(got[h * G:(h + 1) * G], ref, bound)
