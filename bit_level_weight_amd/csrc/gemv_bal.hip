@@ -748,7 +748,7 @@ __global__ void __launch_bounds__(kBalThreads) k_gemv_c2_bal(SpecViewC2 v, Shape
   const int B = (int)sh.block, nb = (int)(C / B), nwb = B / 32;
   const int m = sh.mant, fw = 2 + m;
   const int ebias = 127 + m;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   float* lut = reinterpret_cast<float*>(smem + g.lut_off);
   uint8_t* reg = smem + g.wave_off + wave * g.wave_bytes;
   uint16_t* kb_l = reinterpret_cast<uint16_t*>(reg + g.kb_off);
@@ -796,58 +796,60 @@ __global__ void __launch_bounds__(kBalThreads) k_gemv_c2_bal(SpecViewC2 v, Shape
     dma_run(reinterpret_cast<const u32x4*>(v.shexp + pl.e_a0), reinterpret_cast<u32x4*>(e_l),
             (int)((e1b - pl.e_a0) >> 4), lane);
   };
+  // Where this lane's part starts: as in the Cassandra-1 kernel (the block
+  // from the kept counts of the estimated block and its neighbours in one
+  // round trip, the bit by binary search over popcounts); no code search.
   auto locate = [&](const Plan& pl) {
     Part pt;
-    const int64_t row = pl.row0 + rl;
-    const int i0 = (int)(((int64_t)part * k) >> g.logP);
-    pt.n = rl < pl.rows_here ? (int)((((int64_t)part + 1) * k) >> g.logP) - i0 : 0;
-    pt.rowbit = (uint32_t)((pl.row0 * wpr - pl.bm_a0) * 32 + (int64_t)rl * C);
+    const uint32_t uk = (uint32_t)k;
+    const uint32_t i0 = ((uint32_t)part * uk) >> g.logP;
+    pt.n = rl < pl.rows_here ? (int)((((uint32_t)part + 1u) * uk) >> g.logP) - (int)i0 : 0;
+    pt.rowbit = (uint32_t)((pl.row0 * wpr - pl.bm_a0) * 32) + (uint32_t)rl * (uint32_t)C;
     pt.bp = pt.rowbit;
     pt.fp = 0;
     pt.cp = 0;
     pt.cabs = 0;
-    if (pt.n > 0) {
-      const uint16_t* kbr = kb_l + pl.kb_sh + rl * nb;
-      int b = (int)((float)i0 * g.nb_per_k);
-      b = b < 0 ? 0 : (b >= nb ? nb - 1 : b);
+    if (pt.n <= 0) return pt;
+    const uint16_t* kbr = kb_l + pl.kb_sh + rl * nb;
+    auto kb_at = [&](int j) -> int { return j <= 0 ? 0 : (j >= nb ? (int)k : (int)kbr[j]); };
+    int e = (int)((float)i0 * g.nb_per_k);
+    e = e < 0 ? 0 : (e >= nb ? nb - 1 : e);
+    const int km = kb_at(e - 1), k0 = kb_at(e), k1 = kb_at(e + 1), k2 = kb_at(e + 2);
+    const int ii = (int)i0;
+    int b = e - 1 + (k0 <= ii ? 1 : 0) + (k1 <= ii ? 1 : 0);
+    int kbb = b == e - 1 ? km : (b == e ? k0 : k1);
+    if (!(km <= ii && ii < k2)) {
+      b = e;
       for (int it = 0; it < nb; ++it) {
-        const int lo = kbr[b], hi = b + 1 < nb ? kbr[b + 1] : (int)k;
-        if (lo > i0 && b > 0) --b;
-        else if (hi <= i0 && b + 1 < nb) ++b;
+        const int lo = kb_at(b), hi = kb_at(b + 1);
+        if (lo > ii && b > 0) --b;
+        else if (hi <= ii && b + 1 < nb) ++b;
         else break;
       }
-      const int skip = i0 - kbr[b];
-      const uint32_t* bw = bm_l + (pt.rowbit >> 5) + b * nwb;
-      int rem = skip, wsel = nwb - 1;
-      uint32_t wd = 0;
-      if (nwb <= 8) {
-        uint32_t wv[8];
-#pragma unroll
-        for (int w = 0; w < 8; ++w) wv[w] = w < nwb ? bw[w] : 0u;
-        bool found = false;
-#pragma unroll
-        for (int w = 0; w < 8; ++w) {
-          const int c = __builtin_popcount(wv[w]);
-          const bool here = !found && w < nwb && rem < c;
-          wsel = here ? w : wsel;
-          wd = here ? wv[w] : wd;
-          rem -= (!found && !here) ? c : 0;
-          found = found || here;
-        }
-      } else {
-        int wi = 0;
-        wd = bw[0];
-        for (;;) {
-          const int c = __builtin_popcount(wd);
-          if (rem < c || wi == nwb - 1) break;  // (the second test: corrupt streams only)
-          rem -= c;
-          wd = bw[++wi];
-        }
-        wsel = wi;
-      }
-      pt.bp = pt.rowbit + (uint32_t)(b * B + wsel * 32 + select_bit(wd, rem + 1));
-      pt.fp = (uint32_t)((row * k + i0) * fw - pl.f_a0 * 32);
+      kbb = kb_at(b);
     }
+    const int skip = ii - kbb;
+    const uint32_t* bw = bm_l + (pt.rowbit >> 5) + b * nwb;
+    uint32_t inblk;
+    if (nwb == 8) {
+      uint32_t q[8];
+#pragma unroll
+      for (int w = 0; w < 8; ++w) q[w] = bw[w];
+      inblk = select256(q, skip);
+      inblk = inblk == ~0u ? 0u : inblk;  // (corrupt streams only: stay inside the block)
+    } else {
+      int wi = 0, rem = skip;
+      uint32_t wd = bw[0];
+      for (;;) {
+        const int c = __builtin_popcount(wd);
+        if (rem < c || wi == nwb - 1) break;  // (the second test: corrupt streams only)
+        rem -= c;
+        wd = bw[++wi];
+      }
+      inblk = (uint32_t)(wi * 32 + select_bit(wd, rem + 1));
+    }
+    pt.bp = pt.rowbit + (uint32_t)(b * B) + inblk;
+    pt.fp = (uint32_t)(pl.row0 * k * fw - pl.f_a0 * 32) + ((uint32_t)rl * uk + i0) * (uint32_t)fw;
     return pt;
   };
 
