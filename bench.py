@@ -518,10 +518,25 @@ def read_ceiling(torch, stream):
         ms = a.elapsed_time(b)
         best = ms if best is None else min(best, ms)
     gbs = t.numel() * 4 / (best * 1e-3) / 1e9
-    del t
+    # a device copy of 1 GiB: bytes read plus bytes written per second
+    src = t.view(torch.uint8)[: 1 << 30]
+    dst = torch.empty_like(src)
+    cbest = None
+    for _ in range(6):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        dst.copy_(src)
+        b.record(stream)
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b)
+        cbest = ms if cbest is None else min(cbest, ms)
+    copy_gbs = 2 * src.numel() / (cbest * 1e-3) / 1e9
+    del t, src, dst
     torch.cuda.empty_cache()
     return {"GB_s": round(gbs, 1), "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
-            "kernel": "torch sum over 2 GiB fp32 (best of 6)"}
+            "kernel": "torch sum over 2 GiB fp32 (best of 6)",
+            "copy_read_plus_write_GB_s": round(copy_gbs, 1),
+            "copy_pct_hbm_peak": round(100 * copy_gbs / HBM_PEAK_GBS, 2)}
 
 
 def cpu_baseline(args, synth, layer0, threads=None, seconds=None):
