@@ -703,8 +703,9 @@ __host__ __device__ __forceinline__ int staged_words(int fcap, int ccap, int fmt
 }
 
 // MAXR: a bound on the query rows (nq * G) the launch serves.  Shared
-// memory: queries [128][MAXR] fp32 (a key position's entries side by side), scores [MAXR][kChunk] fp32, value tile
-// [kChunk][130] bf16 (about 37 KB for one query of four heads).
+// memory: queries [128][MAXR] fp32 (a key position's entries side by side),
+// scores [MAXR][kChunk] fp32, value tile [kChunk][130] bf16 (about 37 KB for
+// one query of four heads), then for the draft the staged sections.
 template <bool EXACT, int MAXR, int FMT>
 __global__ void __launch_bounds__(2 * kChunk) k_kv_attn(KvDev kv, AttnArgs a) {
   // threads 0..kChunk-1: one token's key and its scores; threads kChunk..:
@@ -718,14 +719,12 @@ __global__ void __launch_bounds__(2 * kChunk) k_kv_attn(KvDev kv, AttnArgs a) {
   const int h = blockIdx.x, c = blockIdx.y;
   const int rows = a.nq * a.G;
   const int tid = threadIdx.x;
-#pragma unroll
   for (int i = tid; i < 4 * 256; i += 2 * kChunk) {
     const int s = 2 * h + (i >> 9), which = (i >> 8) & 1;
     const uint8_t* src = which ? kv.verif + s * kv.vstride + kv.vo[0] : kv.spec + s * kv.sstride + kv.so[0];
     tabs[i >> 8][i & 255] = src[i & 255];
   }
   // query rows of this KV head: row r = qi * G + g  (query qi, head h*G + g)
-#pragma unroll
   for (int idx = tid; idx < MAXR * kDim; idx += 2 * kChunk) {  // rows past `rows` stay zero
     const int r = idx / kDim, d = idx % kDim;
     const int qi = r / a.G, g = r % a.G;
