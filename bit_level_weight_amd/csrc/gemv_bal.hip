@@ -17,17 +17,18 @@
 // with 16-byte loads, each byte once, and decodes from there.  x is staged
 // once per workgroup.
 //
-// Decode.  A lane first finds where its part starts: binary search over the
-// row's kept-before counts, popcounts inside the block, a select inside the
-// word, and a select over the code ones.  Then it takes U values per group
-// from three windows read at its bit positions (two LDS words and a funnel
-// shift each): 64 keep bits, 32 code bits and 32 field bits.  Per value:
-// position = find-first-set of the keep window, rank = count-trailing-zeros
-// of the code window, field = bit-field extract, weight = one LDS table entry
-// indexed by (rank, field).  A group whose windows do not hold U values for
-// every lane of the wave (rare at the shipped keep ratios) is decoded one
-// value at a time by the general step, which also serves the last few values
-// of each part and codes of 32 bits or more.
+// Decode.  A lane first finds where its part starts: the block from the
+// kept-before counts of the estimated block and its neighbours, the bit inside
+// the block and the start of its code by binary search over popcounts.  Then
+// it takes U values per group from three windows read at its bit positions
+// (two LDS words and a funnel shift each): 64 keep bits, 32 code bits and 32
+// field bits.  Per value: position = find-first-set of the keep window, rank
+// = count-trailing-zeros of the code window, field = bit-field extract, weight
+// = one LDS table entry indexed by (rank, field).  A group whose windows do
+// not hold U values for every lane of the wave runs as two half groups; only a
+// half that still falls short (codes of 32 bits or more, long runs of pruned
+// positions) is decoded one value at a time by the general step.  The part's
+// last group is masked.
 #include <stdlib.h>
 #include <string.h>
 
