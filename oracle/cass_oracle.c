@@ -106,19 +106,27 @@ static int cmp_salience(const void* a, const void* b) {
 
 int orc_select(const uint16_t* w, int64_t R, int64_t C, int64_t k, uint8_t* keep) {
   if (R < 0 || C <= 0 || k < 0 || k > C) return ORC_ERR_INVALID;
-  keyed* order = (keyed*)malloc(sizeof(keyed) * (size_t)C);
-  if (!order) return ORC_ERR_CAPACITY;
-  for (int64_t r = 0; r < R; r++) {
-    for (int64_t j = 0; j < C; j++) {
-      order[j].key = bf_key(w[r * C + j]);
-      order[j].idx = j;
+  int bad = 0;
+  /* rows are independent groups: each row is sorted on its own (threads
+   * only split the rows among them) */
+#pragma omp parallel reduction(| : bad)
+  {
+    keyed* order = (keyed*)malloc(sizeof(keyed) * (size_t)C);
+    if (!order) bad |= 1;
+#pragma omp for schedule(static)
+    for (int64_t r = 0; r < R; r++) {
+      if (!order) continue;
+      for (int64_t j = 0; j < C; j++) {
+        order[j].key = bf_key(w[r * C + j]);
+        order[j].idx = j;
+      }
+      qsort(order, (size_t)C, sizeof(keyed), cmp_salience);
+      memset(keep + r * C, 0, (size_t)C);
+      for (int64_t i = 0; i < k; i++) keep[r * C + order[i].idx] = 1;
     }
-    qsort(order, (size_t)C, sizeof(keyed), cmp_salience);
-    memset(keep + r * C, 0, (size_t)C);
-    for (int64_t i = 0; i < k; i++) keep[r * C + order[i].idx] = 1;
+    free(order);
   }
-  free(order);
-  return ORC_OK;
+  return bad ? ORC_ERR_CAPACITY : ORC_OK;
 }
 
 /* --------------------------------------------------- exponent statistics */

@@ -311,6 +311,32 @@ def test_product_exact_fraction_8x8(orc, fmt):
                 assert abs(Fraction(Y[t, n]) - ex) <= Fraction(1, 10 ** 12) * (ab + 1)
 
 
+@pytest.mark.parametrize("fmt", [1, 2])
+def test_product_rows_exact_fraction(orc, fmt):
+    """The row-restricted product: for a shuffled subset of rows (with a
+    repeat), y[t][i] is the exact sum over row rows[i] -- draft weights without
+    verif, original weights with it -- and the |w||x| sums likewise."""
+    rng = np.random.default_rng(29 + fmt)
+    w = synth.bf16_from_f32((rng.standard_normal((8, 64)) * 0.05).astype(np.float32))
+    x = synth.bf16_from_f32(rng.standard_normal((3, 64)).astype(np.float32))
+    rows = np.array([5, 0, 7, 5, 2])
+    for k, m in [(19, 3), (64, 7), (0, 2)]:
+        spec, verif = orc.encode(w, k, m, block=32, fmt=fmt)
+        keep = orc.select(w, k)
+        d = semantic_draft_c1(w, keep, m) if fmt == 1 else mx_semantic_draft(w, keep, m)[0]
+        for wt, vf in ((d, None), (w, verif)):
+            y, absy = orc.product_rows(spec, x, rows, verif=vf)
+            assert y.shape == (3, rows.size)
+            for t in range(3):
+                for i, n in enumerate(rows):
+                    ex = sum(exact(wt[n, j]) * exact(x[t, j]) for j in range(64))
+                    ab = sum(abs(exact(wt[n, j]) * exact(x[t, j])) for j in range(64))
+                    assert abs(Fraction(y[t, i]) - ex) <= Fraction(1, 10 ** 12) * (ab + 1)
+                    assert abs(Fraction(absy[t, i]) - ab) <= Fraction(1, 10 ** 12) * (ab + 1)
+    with pytest.raises(orc.OracleError):
+        orc.product_rows(spec, x, np.array([8]))
+
+
 def test_product_dense_special_cases(orc):
     """keep=all with m=7 is the plain dense product; the verification product is
     the dense product of the original weights for any k, m; keep=0 gives 0."""
