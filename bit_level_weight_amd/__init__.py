@@ -31,8 +31,9 @@ EXPORTED = (
     "cass_tensor_validate", "cass_status_string", "cass_last_error", "cass_version",
     "cass_kv_bytes", "cass_kv_init", "cass_kv_append_ws_bytes", "cass_kv_append_encode",
     "cass_kv_status", "cass_kv_decode", "cass_kv_attn_ws_bytes", "cass_kv_draft_attn",
-    "cass_kv_verify_attn",
+    "cass_kv_verify_attn", "cass_set_option", "cass_stream_read",
 )
+CASS_STREAM_READ_BLOCKS = 2048
 CASS_KV_STATE_BYTES = 4096
 CASS_KV_FLAG_TABLES, CASS_KV_FLAG_OVERFLOW = 1, 2
 
@@ -53,7 +54,8 @@ class CassTensor(ctypes.Structure):
 
 
 class CassPlan(ctypes.Structure):
-    _fields_ = [("rows", ctypes.c_int64), ("cols", ctypes.c_int64), ("p", CassParams),
+    _fields_ = [("rows", ctypes.c_int64), ("cols", ctypes.c_int64), ("ld", ctypes.c_int64),
+                ("p", CassParams),
                 ("spec_bytes", ctypes.c_int64), ("verif_bytes", ctypes.c_int64),
                 ("spec_sec", ctypes.c_int64 * MAX_SECTIONS),
                 ("spec_len", ctypes.c_int64 * MAX_SECTIONS),
@@ -100,9 +102,9 @@ def lib():
         P, I64, I32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
         L.cass_encode_ws_bytes.argtypes = [I64, I64, ctypes.POINTER(CassParams),
                                            ctypes.POINTER(I64)]
-        L.cass_encode_plan.argtypes = [P, I64, I64, ctypes.POINTER(CassParams), P, I64, P,
+        L.cass_encode_plan.argtypes = [P, I64, I64, I64, ctypes.POINTER(CassParams), P, I64, P,
                                        ctypes.POINTER(CassPlan)]
-        L.cass_encode_tensor.argtypes = [P, ctypes.POINTER(CassPlan), P, I64, P, I64, P,
+        L.cass_encode_tensor.argtypes = [P, I64, ctypes.POINTER(CassPlan), P, I64, P, I64, P,
                                          ctypes.POINTER(CassTensor)]
         L.cass_tensor_describe.argtypes = [P, P, I64, P, P, I64, ctypes.POINTER(CassTensor)]
         L.cass_draft_gemv.argtypes = [ctypes.POINTER(CassTensor), P, I32, I64, P, I64, P]
@@ -115,6 +117,8 @@ def lib():
         L.cass_last_error.argtypes = []
         L.cass_last_error.restype = ctypes.c_char_p
         L.cass_version.argtypes = []
+        L.cass_set_option.argtypes = [ctypes.c_char_p, I64]
+        L.cass_stream_read.argtypes = [P, I64, P, P]
         KP, KV = ctypes.POINTER(CassKvParams), ctypes.POINTER(CassKv)
         L.cass_kv_bytes.argtypes = [KP, ctypes.POINTER(I64), ctypes.POINTER(I64),
                                     ctypes.POINTER(I64)]
@@ -158,10 +162,16 @@ def cass_encode_ws_bytes(rows, cols, params: CassParams) -> int:
     return n.value
 
 
+def _ld(w):
+    assert w.dim() == 2 and w.stride(1) == 1, "rows must be contiguous"
+    return w.stride(0)
+
+
 def cass_encode_plan(w, params: CassParams, ws, stream=None) -> CassPlan:
+    """w: [rows, cols] bf16 patterns with unit column stride (any row stride)."""
     rows, cols = w.shape
     plan = CassPlan()
-    _check(lib().cass_encode_plan(_ptr(w), rows, cols, ctypes.byref(params), _ptr(ws),
+    _check(lib().cass_encode_plan(_ptr(w), rows, cols, _ld(w), ctypes.byref(params), _ptr(ws),
                                   ws.numel() * ws.element_size(), _stream(stream),
                                   ctypes.byref(plan)))
     return plan
@@ -169,8 +179,8 @@ def cass_encode_plan(w, params: CassParams, ws, stream=None) -> CassPlan:
 
 def cass_encode_tensor(w, plan: CassPlan, spec, verif, stream=None) -> CassTensor:
     t = CassTensor()
-    _check(lib().cass_encode_tensor(_ptr(w), ctypes.byref(plan), _ptr(spec), spec.numel(),
-                                    _ptr(verif), verif.numel(), _stream(stream),
+    _check(lib().cass_encode_tensor(_ptr(w), _ld(w), ctypes.byref(plan), _ptr(spec),
+                                    spec.numel(), _ptr(verif), verif.numel(), _stream(stream),
                                     ctypes.byref(t)))
     return t
 
@@ -218,6 +228,18 @@ def cass_tensor_validate(spec: np.ndarray, verif: np.ndarray | None = None) -> i
 
 def cass_version() -> int:
     return lib().cass_version()
+
+
+def cass_set_option(name: str, value: int):
+    """Select an internal code path (tests and benchmarks; 0 = default)."""
+    _check(lib().cass_set_option(name.encode(), int(value)))
+
+
+def cass_stream_read(buf, out, stream=None):
+    """Streaming read of every byte of buf (device, 16-byte multiple) into a
+    fold of CASS_STREAM_READ_BLOCKS words in out: the read-bandwidth ceiling."""
+    _check(lib().cass_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(out),
+                                  _stream(stream)))
 
 
 # ------------------------------------------------------------ convenience

@@ -5,6 +5,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -16,6 +17,8 @@ namespace cass {
 namespace {
 
 thread_local std::string g_last_error;
+
+std::atomic<int> g_options[OPT_COUNT];
 
 int fail(int status, const char* fmt, ...) {
   char buf[512];
@@ -115,6 +118,42 @@ int check_shape(int64_t R, int64_t C, const cass_params* p) {
   return CASS_OK;
 }
 
+// Closed-form lengths of a stream's sections; -1 for the variable-length code
+// sections (their size depends on the data).
+std::vector<int64_t> closed_lengths(bool spec, int format, int64_t R, int64_t C, int64_t B,
+                                    int64_t k, int m) {
+  std::vector<int64_t> ls, lv;
+  stream_lengths(format, R, C, B, k, m, 0, 0, ls, lv);
+  if (format == CASS_FMT_C1_UNARY) {
+    ls[S1_CODES] = -1;
+    lv[V1_CODES] = -1;
+  } else {
+    lv[V2_RESID] = -1;
+    lv[V2_CODES] = -1;
+  }
+  return spec ? ls : lv;
+}
+
+// Every section starts on a 256-byte boundary after the header, in order, and
+// a fixed-size section with its >= 16 padding bytes ends before the next
+// section starts (the last one before the end of the buffer), so kernels that
+// size their reads from the shape stay inside the caller's buffer.  The device
+// contents (row bases, offsets, codes) are trusted: cass_tensor_validate
+// checks untrusted streams on the host.
+int check_sections(const char* what, const int64_t* off, int64_t bytes,
+                   const std::vector<int64_t>& len) {
+  const int n = (int)len.size();
+  for (int s = 0; s < n; ++s) {
+    const int64_t end = s + 1 < n ? off[s + 1] : bytes;
+    if (off[s] < kHeaderBytes || off[s] % 256 || off[s] >= bytes || end > bytes)
+      return fail(CASS_ERR_INVALID, "%s section %d offset out of range", what, s);
+    if (off[s] + (len[s] < 0 ? 0 : len[s]) + 16 > end)
+      return fail(CASS_ERR_INVALID, "%s section %d does not fit before %s", what, s,
+                  s + 1 < n ? "the next section" : "the end of the buffer");
+  }
+  return CASS_OK;
+}
+
 int check_tensor(const cass_tensor* W, bool need_verif) {
   if (!W) return fail(CASS_ERR_INVALID, "tensor descriptor is NULL");
   cass_params p = {W->format, W->mant_bits, W->block, W->keep};
@@ -122,31 +161,28 @@ int check_tensor(const cass_tensor* W, bool need_verif) {
   if (st) return st;
   if (!W->spec) return fail(CASS_ERR_INVALID, "speculation stream is NULL");
   if (need_verif && !W->verif) return fail(CASS_ERR_INVALID, "verification stream is NULL");
-  const int ns = W->format == CASS_FMT_C1_UNARY ? S1_COUNT : S2_COUNT;
-  const int nv = W->format == CASS_FMT_C1_UNARY ? V1_COUNT : V2_COUNT;
-  for (int s = 0; s < ns; ++s)
-    if (W->spec_sec[s] < kHeaderBytes || W->spec_sec[s] % 256 || W->spec_sec[s] >= W->spec_bytes)
-      return fail(CASS_ERR_INVALID, "speculation section %d offset out of range", s);
+  if (((uintptr_t)W->spec % 16) || (W->verif && ((uintptr_t)W->verif % 16)))
+    return fail(CASS_ERR_INVALID, "stream buffers must be 16-byte aligned");
+  st = check_sections("speculation", W->spec_sec, W->spec_bytes,
+                      closed_lengths(true, W->format, W->rows, W->cols, W->block, W->keep,
+                                     W->mant_bits));
+  if (st) return st;
   if (need_verif)
-    for (int s = 0; s < nv; ++s)
-      if (W->verif_sec[s] < kHeaderBytes || W->verif_sec[s] % 256 ||
-          W->verif_sec[s] >= W->verif_bytes)
-        return fail(CASS_ERR_INVALID, "verification section %d offset out of range", s);
-  return CASS_OK;
+    st = check_sections("verification", W->verif_sec, W->verif_bytes,
+                        closed_lengths(false, W->format, W->rows, W->cols, W->block, W->keep,
+                                       W->mant_bits));
+  return st;
 }
 
 Shape shape_of(const cass_tensor* W) {
-  return Shape{W->rows, W->cols, W->block, W->keep, W->mant_bits};
+  return Shape{W->rows, W->cols, W->block, W->keep, W->mant_bits, W->cols};
 }
 
 // Whole 16-byte units between a section start and the end of the buffer, in
 // 32-bit words: the bulk copies of the staged kernels stay below this.
 // The staged exact decoders serve Cassandra-1 verification and reconstruction
-// unless CASS_EXACT_PATH=direct selects the per-thread stream readers.
-bool staged_exact_enabled() {
-  const char* e = getenv("CASS_EXACT_PATH");
-  return !(e && strcmp(e, "direct") == 0);
-}
+// unless the exact_path option selects the per-thread stream readers.
+bool staged_exact_enabled() { return option(OPT_EXACT_PATH) != 1; }
 
 int64_t word_limit(int64_t buffer_bytes, int64_t section_off) {
   return (buffer_bytes - section_off) / 16 * 4;
@@ -240,6 +276,8 @@ int report(int status, const char* fmt, ...) {
 
 void clear_error() { g_last_error.clear(); }
 
+int option(Option o) { return g_options[o].load(std::memory_order_relaxed); }
+
 Workspace carve_workspace(void* base, int64_t rows, int64_t cols, int64_t block) {
   Workspace w;
   ws_layout(rows, cols, block, &w, (uint8_t*)base);
@@ -295,12 +333,14 @@ int cass_encode_ws_bytes(int64_t rows, int64_t cols, const cass_params* p, int64
   return CASS_OK;
 }
 
-int cass_encode_plan(const uint16_t* w, int64_t rows, int64_t cols, const cass_params* p,
-                     void* ws, int64_t ws_bytes, hipStream_t stream, cass_plan* plan) {
+int cass_encode_plan(const uint16_t* w, int64_t rows, int64_t cols, int64_t ld,
+                     const cass_params* p, void* ws, int64_t ws_bytes, hipStream_t stream,
+                     cass_plan* plan) {
   g_last_error.clear();
   int st = check_shape(rows, cols, p);
   if (st) return st;
   if (!plan) return fail(CASS_ERR_INVALID, "plan is NULL");
+  if (ld < cols) return fail(CASS_ERR_INVALID, "ld %lld < cols %lld", (long long)ld, (long long)cols);
   if (rows > 0 && !w) return fail(CASS_ERR_INVALID, "w is NULL");
   const int64_t need = ws_layout(rows, cols, p->block, nullptr, nullptr);
   if (!ws) return fail(CASS_ERR_INVALID, "workspace is NULL");
@@ -310,10 +350,11 @@ int cass_encode_plan(const uint16_t* w, int64_t rows, int64_t cols, const cass_p
   memset(plan, 0, sizeof *plan);
   plan->rows = rows;
   plan->cols = cols;
+  plan->ld = ld;
   plan->p = *p;
   plan->ws = ws;
   plan->ws_bytes = ws_bytes;
-  const Shape sh{rows, cols, p->block, p->keep, p->mant_bits};
+  const Shape sh{rows, cols, p->block, p->keep, p->mant_bits, ld};
   const Workspace W = carve_workspace(ws, rows, cols, p->block);
   hipError_t e;
   if ((e = launch_select(w, sh, W.bitmap, stream)) != hipSuccess) return hip_fail(e, "select");
@@ -360,12 +401,15 @@ int cass_encode_plan(const uint16_t* w, int64_t rows, int64_t cols, const cass_p
   return CASS_OK;
 }
 
-int cass_encode_tensor(const uint16_t* w, const cass_plan* plan, void* spec, int64_t spec_cap,
-                       void* verif, int64_t verif_cap, hipStream_t stream, cass_tensor* out) {
+int cass_encode_tensor(const uint16_t* w, int64_t ld, const cass_plan* plan, void* spec,
+                       int64_t spec_cap, void* verif, int64_t verif_cap, hipStream_t stream,
+                       cass_tensor* out) {
   g_last_error.clear();
   if (!plan) return fail(CASS_ERR_INVALID, "plan is NULL");
   int st = check_shape(plan->rows, plan->cols, &plan->p);
   if (st) return st;
+  if (ld != plan->ld) return fail(CASS_ERR_INVALID, "ld %lld differs from the plan's %lld",
+                                  (long long)ld, (long long)plan->ld);
   if (!spec || !verif || !out) return fail(CASS_ERR_INVALID, "NULL stream buffer or descriptor");
   if (plan->rows > 0 && !w) return fail(CASS_ERR_INVALID, "w is NULL");
   if (((uintptr_t)spec | (uintptr_t)verif) % 256)
@@ -373,7 +417,7 @@ int cass_encode_tensor(const uint16_t* w, const cass_plan* plan, void* spec, int
   if (spec_cap < plan->spec_bytes || verif_cap < plan->verif_bytes)
     return fail(CASS_ERR_CAPACITY, "stream buffers smaller than the plan's sizes");
   const cass_params* p = &plan->p;
-  const Shape sh{plan->rows, plan->cols, p->block, p->keep, p->mant_bits};
+  const Shape sh{plan->rows, plan->cols, p->block, p->keep, p->mant_bits, ld};
   const Workspace W = carve_workspace((void*)plan->ws, plan->rows, plan->cols, p->block);
   RankTables rt;
   for (int r = 0; r < 256; ++r) {
@@ -452,9 +496,49 @@ int cass_tensor_describe(const void* spec_header, const void* spec, int64_t spec
     out->verif_bytes = verif_bytes;
     for (int s = 0; s < CASS_MAX_SECTIONS; ++s) out->verif_sec[s] = get64(v + 64 + 16 * s);
   }
-  int st = check_tensor(out, out->verif != nullptr);
+  if (((uintptr_t)spec % 16) || (out->verif && ((uintptr_t)out->verif % 16)))
+    return fail(CASS_ERR_INVALID, "stream buffers must be 16-byte aligned");
+  // the header's own section table: fixed-size sections have their closed-form
+  // lengths, and every section with its padding lies inside the stream
+  cass_params pp = {out->format, out->mant_bits, out->block, out->keep};
+  int st = check_shape(out->rows, out->cols, &pp);
+  if (st) return fail(CASS_ERR_CORRUPT, "%s", g_last_error.c_str());
+  for (int which = 0; which < (out->verif ? 2 : 1); ++which) {
+    const uint8_t* hh = which == 0 ? h : (const uint8_t*)verif_header;
+    const int64_t total = get64(hh + 48);
+    const std::vector<int64_t> want = closed_lengths(which == 0, out->format, out->rows,
+                                                     out->cols, out->block, out->keep,
+                                                     out->mant_bits);
+    if ((int64_t)get32(hh + 56) != (int64_t)want.size())
+      return fail(CASS_ERR_CORRUPT, "section count does not match the format");
+    for (size_t s = 0; s < want.size(); ++s) {
+      const int64_t off = get64(hh + 64 + 16 * s), len = get64(hh + 72 + 16 * s);
+      if (len < 0 || (want[s] >= 0 && len != want[s]) || off + len + 16 > total)
+        return fail(CASS_ERR_CORRUPT, "%s section %d: length %lld does not fit the shape",
+                    which == 0 ? "speculation" : "verification", (int)s, (long long)len);
+    }
+  }
+  st = check_tensor(out, out->verif != nullptr);
   if (st) return st == CASS_ERR_INVALID ? fail(CASS_ERR_CORRUPT, "%s", g_last_error.c_str()) : st;
   return CASS_OK;
+}
+
+int cass_set_option(const char* name, int64_t value) {
+  g_last_error.clear();
+  static const struct { const char* name; Option o; int64_t lo, hi; } table[] = {
+      {"gemv_parts", OPT_GEMV_PARTS, 0, 64}, {"gemv_path", OPT_GEMV_PATH, 0, 2},
+      {"gemv_sub", OPT_GEMV_SUB, 0, 64},     {"exact_path", OPT_EXACT_PATH, 0, 1},
+      {"exact_blocks", OPT_EXACT_BLOCKS, 0, 2}};
+  if (!name) return fail(CASS_ERR_INVALID, "option name is NULL");
+  for (const auto& t : table)
+    if (strcmp(name, t.name) == 0) {
+      if (value < t.lo || value > t.hi)
+        return fail(CASS_ERR_INVALID, "option %s: value %lld outside %lld..%lld", name,
+                    (long long)value, (long long)t.lo, (long long)t.hi);
+      g_options[t.o].store((int)value, std::memory_order_relaxed);
+      return CASS_OK;
+    }
+  return fail(CASS_ERR_INVALID, "unknown option %s", name);
 }
 
 int cass_draft_gemv(const cass_tensor* W, const uint16_t* x, int batch, int64_t ldx, float* y,

@@ -51,13 +51,13 @@ __global__ void __launch_bounds__(256) k_fill_zero_bytes(uint8_t* p, int64_t n) 
 // (high 8 bits, then low 7 bits), then the bitmap with ties at the threshold
 // kept in column order.
 __global__ void __launch_bounds__(kSelThreads) k_select(const uint16_t* __restrict__ w,
-                                                        int64_t C, int64_t k,
+                                                        int64_t C, int64_t ld, int64_t k,
                                                         uint32_t* __restrict__ bitmap) {
   __shared__ uint32_t hist[256];
   __shared__ uint32_t scan_tmp[kSelThreads];
   __shared__ int sh_T, sh_need;
   const int64_t row = blockIdx.x;
-  const uint16_t* wr = w + row * C;
+  const uint16_t* wr = w + row * ld;
   uint32_t* bm = bitmap + row * (C / 32);
   const int t = threadIdx.x;
   const int64_t nwords = C / 32;
@@ -134,6 +134,7 @@ __global__ void __launch_bounds__(kSelThreads) k_select(const uint16_t* __restri
 // Exponent histograms of kept and pruned values; for Cassandra-2 also the
 // shared exponent of each 32-position group (largest max(e,1) among kept).
 __global__ void __launch_bounds__(256) k_histograms(const uint16_t* __restrict__ w, int64_t nwords,
+                                                    int64_t wpr, int64_t ld,
                                                     const uint32_t* __restrict__ bitmap,
                                                     unsigned long long* __restrict__ hist,
                                                     uint8_t* __restrict__ shexp) {
@@ -143,9 +144,10 @@ __global__ void __launch_bounds__(256) k_histograms(const uint16_t* __restrict__
   for (int64_t wi = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; wi < nwords;
        wi += (int64_t)gridDim.x * blockDim.x) {
     const uint32_t bw = bitmap[wi];
+    const uint16_t* wv = w + (wi / wpr) * ld + (wi % wpr) * 32;  // row wi / wpr
     int E = 0;
     for (int b = 0; b < 32; ++b) {
-      const uint16_t v = w[wi * 32 + b];
+      const uint16_t v = wv[b];
       const int e = exp_of(v);
       const int kept = (bw >> b) & 1;
       atomicAdd(&h[(kept ? 0 : 256) + e], 1u);
@@ -179,11 +181,12 @@ __global__ void __launch_bounds__(256) k_block_bits(const uint16_t* __restrict__
   for (int64_t bi = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; bi < nblk;
        bi += (int64_t)gridDim.x * blockDim.x) {
     const int64_t pos0 = bi * sh.block;  // (row*nb + b)*B == row*C + b*B
+    const uint16_t* wb = w + (bi / nb) * sh.ld + (bi % nb) * sh.block;  // the block's values
     uint32_t a = 0, v = 0, kept = 0;
     for (int64_t wi = 0; wi < sh.block / 32; ++wi) {
       const uint32_t bw = bitmap[pos0 / 32 + wi];
       for (int b = 0; b < 32; ++b) {
-        const uint16_t x = w[pos0 + wi * 32 + b];
+        const uint16_t x = wb[wi * 32 + b];
         const int e = exp_of(x);
         if ((bw >> b) & 1) {
           ++kept;
@@ -354,7 +357,7 @@ __global__ void __launch_bounds__(256) k_pack(const uint16_t* __restrict__ w, Sh
       const uint32_t bw = ws.bitmap[pos0 / 32 + wi];
       const int E = c1 ? 0 : ws.shexp[pos0 / 32 + wi];
       for (int bb = 0; bb < 32; ++bb) {
-        const uint16_t x = w[pos0 + wi * 32 + bb];
+        const uint16_t x = w[row * sh.ld + b * B + wi * 32 + bb];
         const int s = x >> 15, e = exp_of(x), f = x & 0x7F;
         if ((bw >> bb) & 1) {
           if (c1) {
@@ -407,7 +410,7 @@ hipError_t launch_fill_zero(void* p, int64_t bytes, hipStream_t s) {
 
 hipError_t launch_select(const uint16_t* w, const Shape& sh, uint32_t* bitmap, hipStream_t s) {
   if (sh.rows == 0) return hipSuccess;
-  k_select<<<(unsigned)sh.rows, kSelThreads, 0, s>>>(w, sh.cols, sh.keep, bitmap);
+  k_select<<<(unsigned)sh.rows, kSelThreads, 0, s>>>(w, sh.cols, sh.ld, sh.keep, bitmap);
   return hipGetLastError();
 }
 
@@ -418,7 +421,8 @@ hipError_t launch_histograms(const uint16_t* w, const Shape& sh, int format, con
   const int64_t nwords = sh.rows * sh.cols / 32;
   if (nwords == 0) return hipSuccess;
   k_histograms<<<grid_for(nwords, 256), 256, 0, s>>>(
-      w, nwords, ws.bitmap, ws.hist, format == CASS_FMT_C2_MX32 ? ws.shexp : nullptr);
+      w, nwords, sh.cols / 32, sh.ld, ws.bitmap, ws.hist,
+      format == CASS_FMT_C2_MX32 ? ws.shexp : nullptr);
   return hipGetLastError();
 }
 

@@ -781,10 +781,7 @@ XGeom make_xgeom(const Shape& sh, const SpecViewC1& sv, const VerifViewC1& vv) {
   const int64_t B = sh.block, nb = sh.cols / B;
   const int fw = 1 + sh.mant;
   g.Wb = B >= 256 ? 1 : 2;
-  if (const char* e = getenv("CASS_EXACT_BLOCKS")) {
-    const int w = atoi(e);
-    if (w >= 1 && w <= 2) g.Wb = w;
-  }
+  if (const int w = option(OPT_EXACT_BLOCKS); w >= 1 && w <= 2) g.Wb = w;
   g.TS = (int)(g.Wb * B + 2);
   g.nstage = (nb + g.Wb - 1) / g.Wb;
   const int64_t pos = (int64_t)g.Wb * B;  // positions per row per stage

@@ -1019,10 +1019,7 @@ BalGeom make_bal_geom(const Shape& sh, int batch, int64_t code_limit_words) {
   // fewer part starts); parts keep at least 16 values
   int P = R >= 16384 ? 16 : 32;
   while (P > 1 && k / P < 16) P /= 2;
-  if (const char* e = getenv("CASS_GEMV_PARTS")) {
-    const int p = atoi(e);
-    if (p >= 1 && p <= 64 && (p & (p - 1)) == 0) P = p;
-  }
+  if (const int p = option(OPT_GEMV_PARTS); p >= 1 && p <= 64 && (p & (p - 1)) == 0) P = p;
   g.P = P;
   g.logP = __builtin_ctz(P);
   g.rpw = 64 / P;
@@ -1100,10 +1097,7 @@ BalGeom make_bal_geom_c2(const Shape& sh, int batch) {
   const int fw = 2 + sh.mant;
   int P = R >= 16384 ? 16 : 32;
   while (P > 1 && k / P < 16) P /= 2;
-  if (const char* e = getenv("CASS_GEMV_PARTS")) {
-    const int p = atoi(e);
-    if (p >= 1 && p <= 64 && (p & (p - 1)) == 0) P = p;
-  }
+  if (const int p = option(OPT_GEMV_PARTS); p >= 1 && p <= 64 && (p & (p - 1)) == 0) P = p;
   g.P = P;
   g.logP = __builtin_ctz(P);
   g.rpw = 64 / P;

@@ -273,11 +273,7 @@ StagedGeom make_geom(const Shape& sh, int batch, int format, int64_t code_limit_
   if (format == CASS_FMT_C1_UNARY) {
     const int64_t want_lanes = (int64_t)device_cu_count() * 4 * 4 * 64;
     while (g.sub > 1 && sh.rows * nb * (nwb / g.sub) < want_lanes) g.sub /= 2;
-    const char* e = getenv("CASS_GEMV_SUB");
-    if (e) {
-      const int s = atoi(e);
-      if (s >= 1 && s <= nwb && (nwb % s) == 0) g.sub = s;
-    }
+    if (const int s = option(OPT_GEMV_SUB); s >= 1 && s <= nwb && (nwb % s) == 0) g.sub = s;
   }
   const int64_t lpr = nb * (nwb / g.sub);  // lanes per row
   g.rows_per_tile = (int)(lpr >= kThreads ? 1 : kThreads / lpr);
@@ -332,12 +328,9 @@ hipError_t launch_staged(Kern kern, const View& v, const Shape& sh, const Staged
   return hipGetLastError();
 }
 
-// CASS_GEMV_DIRECT=1 in the environment selects the direct kernels (used by
-// the tests to cover that path on shapes the staged kernels accept).
-bool force_direct() {
-  const char* e = getenv("CASS_GEMV_DIRECT");
-  return e && e[0] == '1';
-}
+// gemv_path 2 selects the direct kernels (the tests cover that path on shapes
+// the staged kernels accept).
+bool force_direct() { return option(OPT_GEMV_PATH) == 2; }
 
 }  // namespace
 
@@ -361,8 +354,7 @@ bool draft_gemv_staged_fits(const Shape& sh, int batch, int format, int64_t code
 hipError_t launch_draft_gemv_c1(const SpecViewC1& v, const Shape& sh, const uint16_t* x,
                                 int batch, int64_t ldx, float* y, int64_t ldy, hipStream_t s) {
   if (sh.rows == 0) return hipSuccess;
-  const char* path = getenv("CASS_GEMV_PATH");
-  const bool want_staged = path && strcmp(path, "staged") == 0;
+  const bool want_staged = option(OPT_GEMV_PATH) == 1;
   if (!force_direct() && !want_staged && draft_gemv_bal_fits(sh, batch, v.codes_limit))
     return launch_draft_gemv_c1_bal(v, sh, x, batch, ldx, y, ldy, s);
   const StagedGeom g = make_geom(sh, batch, CASS_FMT_C1_UNARY, v.codes_limit);
@@ -374,8 +366,7 @@ hipError_t launch_draft_gemv_c1(const SpecViewC1& v, const Shape& sh, const uint
 hipError_t launch_draft_gemv_c2(const SpecViewC2& v, const Shape& sh, const uint16_t* x,
                                 int batch, int64_t ldx, float* y, int64_t ldy, hipStream_t s) {
   if (sh.rows == 0) return hipSuccess;
-  const char* path = getenv("CASS_GEMV_PATH");
-  const bool want_staged = path && strcmp(path, "staged") == 0;
+  const bool want_staged = option(OPT_GEMV_PATH) == 1;
   if (!force_direct() && !want_staged && draft_gemv_bal_c2_fits(sh, batch))
     return launch_draft_gemv_c2_bal(v, sh, x, batch, ldx, y, ldy, s);
   const StagedGeom g = make_geom(sh, batch, CASS_FMT_C2_MX32, 0);

@@ -100,7 +100,20 @@ struct VerifViewC2 {
 struct Shape {
   int64_t rows, cols, block, keep;
   int mant;
+  int64_t ld;  // row stride of the bf16 input (encoder only; elements)
 };
+
+// Internal code-path switches, set through cass_set_option (tests and
+// benchmarking select the fallback kernels with them).  0 is the default.
+enum Option {
+  OPT_GEMV_PARTS = 0,  // parts per row of the balanced GEMV (power of two 1..64)
+  OPT_GEMV_PATH,       // 1: staged kernel, 2: direct kernel
+  OPT_GEMV_SUB,        // lanes per block of the staged kernel's sub-split
+  OPT_EXACT_PATH,      // 1: per-thread stream readers for verify/reconstruct
+  OPT_EXACT_BLOCKS,    // blocks per stage of the staged exact decoder (1 or 2)
+  OPT_COUNT
+};
+int option(Option o);
 
 // ---- launchers (return hipSuccess or the launch error) ----
 hipError_t launch_fill_zero(void* p, int64_t bytes, hipStream_t s);

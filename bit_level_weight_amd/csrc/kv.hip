@@ -1139,10 +1139,15 @@ int run_attention(const cass_kv* kv, const uint16_t* q, int nq, int n_q_heads, f
   const size_t lds = 0;  // per launch, from the row bound (attn_launch_f)
   const int rows = nq * G;
   // row bounds: one query of 4 heads (draft), 5 queries of 4 heads (verify), ...
+  // (the 20-row instance of the exact Cassandra-2 kernel gave results that
+  // changed from run to run in workgroups sharing a CU with another one, and
+  // the cause is not known; that case takes the 32-row instance, which is
+  // checked for identical results over repeated runs)
+  const bool r20 = rows <= 20 && !(exact && d.fmt == CASS_FMT_C2_MX32);
   hipError_t e = exact ? (rows <= 4    ? attn_launch<true, 4>(d, a, H, lds, stream)
                           : rows <= 8  ? attn_launch<true, 8>(d, a, H, lds, stream)
                           : rows <= 16 ? attn_launch<true, 16>(d, a, H, lds, stream)
-                          : rows <= 20 ? attn_launch<true, 20>(d, a, H, lds, stream)
+                          : r20        ? attn_launch<true, 20>(d, a, H, lds, stream)
                                        : attn_launch<true, 32>(d, a, H, lds, stream))
                        : (rows <= 4    ? attn_launch<false, 4>(d, a, H, lds, stream)
                           : rows <= 8  ? attn_launch<false, 8>(d, a, H, lds, stream)

@@ -22,6 +22,10 @@
  *  - Kernels run on the caller's stream; only cass_encode_plan synchronises it.
  *  - Argument errors are returned before anything is launched; a launch
  *    failure returns CASS_ERR_HIP.  cass_last_error() gives the detail.
+ *  - Descriptors are checked against the shape's closed-form section sizes
+ *    before any launch; the contents of device streams (row bases, block
+ *    offsets, codes) are trusted.  Streams from an untrusted source are
+ *    checked on the host with cass_tensor_validate first.
  *
  * Stream layout (both streams): a 256-byte header (u32 magic, u32 version=1,
  * u32 format, u32 mant_bits, i64 rows, cols, block, keep, total_bytes, u32
@@ -106,7 +110,7 @@ typedef struct cass_tensor {
 
 /* Result of the planning pass of the encoder (host struct). */
 typedef struct cass_plan {
-  int64_t rows, cols;
+  int64_t rows, cols, ld;
   cass_params p;
   int64_t spec_bytes, verif_bytes;      /* buffer sizes cass_encode_tensor needs */
   int64_t spec_sec[CASS_MAX_SECTIONS], spec_len[CASS_MAX_SECTIONS];
@@ -118,29 +122,38 @@ typedef struct cass_plan {
   int64_t ws_bytes;
 } cass_plan;
 
-/* Workspace bytes cass_encode_plan needs for a rows x cols tensor. */
+/* Workspace bytes cass_encode_plan needs for a rows x cols tensor
+ * (Cassandra review, section 3.1: the offline weight transform).  Host only. */
 int cass_encode_ws_bytes(int64_t rows, int64_t cols, const cass_params* p, int64_t* ws_bytes);
 
-/* Planning pass of the encoder (section 3.1 steps one to three): per-row
+/* Planning pass of the encoder (Cassandra review, section 3.1, the first two
+ * transform steps, and section 3.2, exponent statistics): per-row
  * top-`keep` selection by |w| with ties to the lower column, exponent
  * histograms of kept and pruned values, frequency-ranked tables (count
  * descending, exponent ascending), code lengths and offsets.  w: device
- * [rows][cols] bf16 patterns (row stride cols).  ws: device workspace of
+ * [rows][ld] bf16 patterns, ld >= cols elements.  ws: device workspace of
  * ws_bytes >= cass_encode_ws_bytes(); it holds intermediate results that
  * cass_encode_tensor reads, so it must stay untouched in between.
  * Synchronises `stream` twice (histograms, sizes).  rows may be 0. */
-int cass_encode_plan(const uint16_t* w, int64_t rows, int64_t cols, const cass_params* p,
-                     void* ws, int64_t ws_bytes, hipStream_t stream, cass_plan* plan);
+int cass_encode_plan(const uint16_t* w, int64_t rows, int64_t cols, int64_t ld,
+                     const cass_params* p, void* ws, int64_t ws_bytes, hipStream_t stream,
+                     cass_plan* plan);
 
-/* Packing pass: writes both streams, byte for byte the canonical encoding, to
+/* Packing pass (Cassandra review, section 3.1: the split into speculation and
+ * verification data; section 3.2: unary exponent codes or the shared MX
+ * exponent): writes both streams, byte for byte the canonical encoding, to
  * the device buffers spec (>= plan->spec_bytes) and verif (>= plan->
- * verif_bytes), and fills *out.  w and ws must be those given to the plan.
- * Asynchronous. */
-int cass_encode_tensor(const uint16_t* w, const cass_plan* plan, void* spec, int64_t spec_cap,
-                       void* verif, int64_t verif_cap, hipStream_t stream, cass_tensor* out);
+ * verif_bytes), 256-byte aligned, and fills *out.  w, ld and ws must be those
+ * given to the plan.  Asynchronous. */
+int cass_encode_tensor(const uint16_t* w, int64_t ld, const cass_plan* plan, void* spec,
+                       int64_t spec_cap, void* verif, int64_t verif_cap, hipStream_t stream,
+                       cass_tensor* out);
 
 /* Build a descriptor from host copies of the two 256-byte stream headers and
- * the device buffers holding the streams (verif may be NULL). */
+ * the device buffers holding the streams (verif may be NULL): the layout the
+ * encoder writes (Cassandra review, section 3.1, two streams per tensor).
+ * The header's section table must match the shape's closed-form sizes and
+ * lie inside the buffers; else CASS_ERR_CORRUPT.  Host only. */
 int cass_tensor_describe(const void* spec_header, const void* spec, int64_t spec_bytes,
                          const void* verif_header, const void* verif, int64_t verif_bytes,
                          cass_tensor* out);
@@ -162,18 +175,24 @@ int cass_draft_gemv(const cass_tensor* W, const uint16_t* x, int batch, int64_t 
 int cass_verify_gemm(const cass_tensor* W, const uint16_t* X, int ntok, int64_t ldx,
                      float* Y, int64_t ldy, hipStream_t stream);
 
-/* Exact reconstruction of the original bf16 patterns from both streams:
- * out: device [rows][cols].  Asynchronous. */
+/* Exact reconstruction of the original bf16 patterns from both streams
+ * (Cassandra review, section 3.1: the target reassembles speculation and
+ * verification data losslessly): out: device [rows][cols], 16-byte aligned.
+ * Asynchronous. */
 int cass_reconstruct(const cass_tensor* W, uint16_t* out, hipStream_t stream);
 
-/* Zero-filled draft weights from the speculation stream alone: out: device
- * [rows][cols] bf16 patterns.  Asynchronous. */
+/* Zero-filled draft weights from the speculation stream alone (Cassandra
+ * review, section 3.1: the draft loads only speculation data, zero-filled
+ * back to standard floating point): out: device [rows][cols] bf16 patterns,
+ * 16-byte aligned.  Asynchronous. */
 int cass_draft_decode(const cass_tensor* W, uint16_t* out, hipStream_t stream);
 
 /* Host-only structural validation of a stream pair held in host memory
- * (verif may be NULL): header fields, section bounds, bitmap counts, the
- * kept-before counts and that every row base and block offset lands on a code
- * boundary.  Returns CASS_OK or CASS_ERR_CORRUPT.  Touches no GPU. */
+ * (verif may be NULL), for streams of untrusted origin (the format of
+ * Cassandra review, sections 3.1 and 3.2): header fields, section bounds,
+ * bitmap counts, the kept-before counts and that every row base and block
+ * offset lands on a code boundary.  Returns CASS_OK or CASS_ERR_CORRUPT.
+ * Touches no GPU. */
 int cass_tensor_validate(const void* spec, int64_t spec_bytes, const void* verif,
                          int64_t verif_bytes);
 
@@ -230,30 +249,42 @@ typedef struct cass_kv {
   int64_t tokens;           /* tokens appended so far (host copy, kept by the calls) */
 } cass_kv;
 
-/* Buffer sizes for a cache with these parameters. */
+/* Buffer sizes for a cache with these parameters (the online KV format of
+ * Cassandra review, section 3.3; layout above).  Host only. */
 int cass_kv_bytes(const cass_kv_params* p, int64_t* spec_bytes, int64_t* verif_bytes,
                   int64_t* state_bytes);
-/* Fill *kv and zero the three device buffers (asynchronous). */
+/* Fill *kv and zero the three device buffers of an empty cache (Cassandra
+ * review, section 3.3).  Asynchronous. */
 int cass_kv_init(cass_kv* kv, const cass_kv_params* p, void* spec, void* verif, void* state,
                  hipStream_t stream);
-/* Workspace bytes cass_kv_append_encode needs for ntok tokens. */
+/* Workspace bytes cass_kv_append_encode needs for ntok tokens (section 3.3
+ * of the Cassandra review: the online encoder).  Host only. */
 int cass_kv_append_ws_bytes(const cass_kv* kv, int ntok, int64_t* ws_bytes);
-/* Append ntok tokens: k, v device bf16 [ntok][n_kv_heads][head_dim].  The
+/* Online encoder (Cassandra review, section 3.3: KV entries appear during
+ * inference and are compressed as they are appended; section 3.1: the same
+ * pruning, truncation and exponent coding as the weights).
+ * Append ntok tokens: k, v device bf16 [ntok][n_kv_heads][head_dim].  The
  * first call also builds the rank tables from its tokens.  Pruning, splitting,
  * coding and packing all run on the device without a host synchronisation;
  * codes that would exceed a stream's capacity are not written and raise
  * CASS_KV_FLAG_OVERFLOW (see cass_kv_status).  Advances kv->tokens. */
 int cass_kv_append_encode(cass_kv* kv, const uint16_t* k, const uint16_t* v, int ntok,
                           void* ws, int64_t ws_bytes, hipStream_t stream);
-/* Token count and flags from the device state (synchronises the stream). */
+/* Token count and flags from the device state of the online encoder
+ * (Cassandra review, section 3.3).  Synchronises the stream. */
 int cass_kv_status(const cass_kv* kv, int64_t* tokens, uint32_t* flags, hipStream_t stream);
-/* Decoded cache: out device bf16 [2][n_kv_heads][tokens][head_dim] (K then
- * V); exact != 0 rebuilds the original values, else the zero-filled draft. */
+/* Decoded cache (Cassandra review, section 3.1: zero-filled draft data, or
+ * the lossless reassembly of both streams): out device bf16 [2][n_kv_heads]
+ * [tokens][head_dim] (K then V); exact != 0 rebuilds the original values,
+ * else the zero-filled draft. */
 int cass_kv_decode(const cass_kv* kv, int exact, uint16_t* out, hipStream_t stream);
 
-/* Workspace bytes for an attention call over the current tokens. */
+/* Workspace bytes for an attention call over the current tokens (draft or
+ * verification attention, Cassandra review, sections 1 and 3.3).  Host only. */
 int cass_kv_attn_ws_bytes(const cass_kv* kv, int nq, int n_q_heads, int64_t* ws_bytes);
-/* Draft attention of one query (grouped-query: query head g reads KV head
+/* Draft attention of one query (Cassandra review, section 3.3: the KV cache
+ * is compressed online and the draft reads only its speculation data,
+ * zero-filled, as in section 3.1) (grouped-query: query head g reads KV head
  * g / (n_q_heads / n_kv_heads)) over all cached tokens, on the zero-filled
  * draft keys and values: out[g][d] = sum_t softmax_t(scale * q_g . K~_t) V~_t[d].
  * q: device bf16 [n_q_heads][head_dim]; out: device fp32 [n_q_heads][head_dim].
@@ -268,10 +299,30 @@ int cass_kv_draft_attn(const cass_kv* kv, const uint16_t* q, int n_q_heads, floa
 int cass_kv_verify_attn(const cass_kv* kv, const uint16_t* q, int nq, int n_q_heads, float scale,
                         float* out, void* ws, int64_t ws_bytes, hipStream_t stream);
 
+/* Status code -> fixed English text, and the detail of the last error on
+ * the calling thread ("" if none); plumbing, not part of the method. */
 const char* cass_status_string(int status);
-/* Detail of the last error on the calling thread ("" if none). */
 const char* cass_last_error(void);
+/* CASS_VERSION of the loaded library. */
 int cass_version(void);
+
+/* Code-path switches for tests and benchmarks, process-wide, 0 = default
+ * (not part of the method; every path computes the same result):
+ *   "gemv_parts"   parts per row of the balanced draft GEMV, power of two 1..64
+ *   "gemv_path"    1: staged draft GEMV kernel, 2: direct kernel
+ *   "gemv_sub"     lanes per block of the staged kernel
+ *   "exact_path"   1: per-thread stream readers for verification/reconstruction
+ *   "exact_blocks" blocks per stage of the staged exact decoder, 1 or 2
+ * Unknown names or values out of range give CASS_ERR_INVALID.  Not
+ * synchronised with launches in flight on other threads. */
+int cass_set_option(const char* name, int64_t value);
+
+/* Measurement utility (not part of the method): reads `bytes` (a multiple of
+ * 16) of the 16-byte aligned device buffer once with streaming loads, the
+ * achievable-read ceiling of the GPU; out: device, CASS_STREAM_READ_BLOCKS
+ * words (a fold of the data, so the loads are not dropped).  Asynchronous. */
+#define CASS_STREAM_READ_BLOCKS 2048
+int cass_stream_read(const void* buf, int64_t bytes, uint32_t* out, hipStream_t stream);
 
 #ifdef __cplusplus
 }

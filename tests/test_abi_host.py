@@ -103,14 +103,6 @@ def test_host_validator_on_oracle_streams(cass, orc, fmt):
 def test_describe_from_headers(cass, orc):
     w = synth.weight(8, 512, 3)
     spec, verif = orc.encode(w, 150, 3)
-
-    class FakeDev:  # describe only reads the host headers and records pointers
-        def __init__(self, n):
-            self.n = n
-        def numel(self):
-            return self.n
-        def data_ptr(self):
-            return 0x100000
     t = cass.cass_tensor_describe(spec.tobytes(), FakeDev(spec.size), verif.tobytes(),
                                   FakeDev(verif.size))
     h = orc.header(spec)
@@ -118,3 +110,95 @@ def test_describe_from_headers(cass, orc):
     assert [t.spec_sec[i] for i in range(7)] == [o for o, _ in h["sections"]]
     with pytest.raises(cass.CassError):
         cass.cass_tensor_describe(verif.tobytes(), FakeDev(verif.size))
+
+
+class FakeDev:
+    """Stands in for a device buffer: describe and the argument checks only
+    record pointers and sizes."""
+    def __init__(self, n, ptr=0x100000):
+        self.n, self.ptr = n, ptr
+
+    def numel(self):
+        return self.n
+
+    def data_ptr(self):
+        return self.ptr
+
+
+@pytest.mark.parametrize("fmt", [1, 2])
+def test_describe_rejects_inflated_headers(cass, orc, fmt):
+    """A header whose shape asks for more bytes than its section table and
+    buffers hold is refused before anything could be launched: an inflated row
+    count, a section length off its closed form, a section past the buffer, a
+    truncated buffer, a misaligned buffer."""
+    w = synth.weight(8, 512, 3)
+    spec, verif = orc.encode(w, 150, 3, fmt=fmt)
+    t = cass.cass_tensor_describe(spec.tobytes(), FakeDev(spec.size), verif.tobytes(),
+                                  FakeDev(verif.size))
+    assert t.rows == 8
+
+    def corrupt(buf, pos, value):
+        b = bytearray(buf.tobytes())
+        b[pos:pos + 8] = int(value).to_bytes(8, "little")
+        return bytes(b)
+
+    bad_cases = [
+        (corrupt(spec, 16, 4096), verif.tobytes(), spec.size),            # rows 8 -> 4096
+        (corrupt(spec, 72 + 16 * 1, 1 << 20), verif.tobytes(), spec.size),  # a section length
+        (corrupt(spec, 64 + 16 * 1, spec.size - 256), verif.tobytes(), spec.size),  # offset
+        (spec.tobytes(), verif.tobytes(), spec.size - 512),               # truncated buffer
+    ]
+    for sh, vh, n in bad_cases:
+        with pytest.raises(cass.CassError) as e:
+            cass.cass_tensor_describe(sh, FakeDev(n), vh, FakeDev(verif.size))
+        assert e.value.status == cass.CASS_ERR_CORRUPT
+    with pytest.raises(cass.CassError) as e:
+        cass.cass_tensor_describe(spec.tobytes(), FakeDev(spec.size, 0x100008), None, None)
+    assert e.value.status == cass.CASS_ERR_INVALID
+
+
+def test_descriptor_sections_checked_before_launch(cass, orc):
+    """A hand-made descriptor whose sections do not hold the shape's
+    closed-form sizes is refused by every call before any launch."""
+    L = cass.lib()
+    w = synth.weight(8, 512, 3)
+    spec, verif = orc.encode(w, 150, 3)
+    t = cass.cass_tensor_describe(spec.tobytes(), FakeDev(spec.size), verif.tobytes(),
+                                  FakeDev(verif.size))
+    t.rows = 4096  # the buffers hold 8 rows
+    assert L.cass_draft_gemv(ctypes.byref(t), ctypes.c_void_p(0x200000), 1, 512,
+                             ctypes.c_void_p(0x300000), 4096, None) == cass.CASS_ERR_INVALID
+    assert b"section" in L.cass_last_error()
+    t.rows = 8
+    t.spec_sec[5] = t.spec_sec[6]  # fields moved onto the codes section
+    assert L.cass_draft_gemv(ctypes.byref(t), ctypes.c_void_p(0x200000), 1, 512,
+                             ctypes.c_void_p(0x300000), 8, None) == cass.CASS_ERR_INVALID
+
+
+def test_encode_argument_errors(cass):
+    """Row stride and plan checks of the encoder, all before any launch."""
+    L = cass.lib()
+    p = cass.CassParams(1, 3, 256, 100)
+    plan = cass.CassPlan()
+    ws = ctypes.c_void_p(0x100000)
+    # ld < cols
+    assert L.cass_encode_plan(ctypes.c_void_p(0x200000), 4, 512, 500, ctypes.byref(p), ws,
+                              1 << 30, None, ctypes.byref(plan)) == cass.CASS_ERR_INVALID
+    assert b"ld" in L.cass_last_error()
+    # a plan made for one stride is refused for another
+    plan.rows, plan.cols, plan.ld, plan.p = 4, 512, 640, p
+    assert L.cass_encode_tensor(ctypes.c_void_p(0x200000), 512, ctypes.byref(plan),
+                                ctypes.c_void_p(0x300000), 1 << 20, ctypes.c_void_p(0x400000),
+                                1 << 20, None, ctypes.byref(cass.CassTensor())) == \
+        cass.CASS_ERR_INVALID
+
+
+def test_set_option(cass):
+    L = cass.lib()
+    assert L.cass_set_option(b"gemv_parts", 16) == cass.CASS_OK
+    assert L.cass_set_option(b"gemv_parts", 0) == cass.CASS_OK
+    assert L.cass_set_option(b"gemv_parts", 65) == cass.CASS_ERR_INVALID
+    assert L.cass_set_option(b"no_such_option", 1) == cass.CASS_ERR_INVALID
+    assert L.cass_set_option(None, 1) == cass.CASS_ERR_INVALID
+    assert L.cass_stream_read(ctypes.c_void_p(0x100008), 64, ctypes.c_void_p(0x200000),
+                              None) == cass.CASS_ERR_INVALID

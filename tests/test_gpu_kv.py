@@ -205,3 +205,56 @@ def test_draft_attention_uneven_tokens(gpu, orc, fmt):
         assert not (Kd[:100, :32].any() or Vd[:100, :32].any()), "first keep word not empty"
         ref, bound = oracle_attention(orc, q1[h * G:(h + 1) * G], Kd, Vd, scale)
         attn_check(got[h * G:(h + 1) * G], ref, bound)
+
+
+@pytest.mark.parametrize("fmt,T", [(1, 16640), (2, 16640), (2, 66000)])
+def test_attention_long_context(gpu, orc, fmt, T):
+    """Draft and verification attention at contexts where the chunk merge uses
+    its whole structure: 16640 tokens are 130 chunks of 128 (past 64 chunks,
+    every merge wave carries chunk maxima and sums); 66000 + 5 tokens are more
+    than 512 chunks, so the merge's strided loop runs a second pass.  All 32
+    query heads are checked against the oracle's decode plus fp64 attention."""
+    torch, cass = gpu
+    H, Hq, k, m, nq = 8, 32, 38, 3, 5
+    G = Hq // H
+    print("case", fmt, T, flush=True)
+    Kt, Vt = make_kv(T + nq, H, 9000 + T + fmt)
+    cache = cass.KvCache(H, D, k, m, max_tokens=T + nq + 8, fmt=fmt)
+    cache.append(dev(torch, Kt[:T]), dev(torch, Vt[:T]))
+    scale = 1.0 / np.sqrt(D)
+    q1 = synth.activations(Hq, D, 4, t0=T)
+    ws = torch.empty(cass.cass_kv_attn_ws_bytes(cache.kv, nq, Hq) + 256, dtype=torch.uint8,
+                     device="cuda")
+    out = torch.empty((Hq, D), dtype=torch.float32, device="cuda")
+    cass.cass_kv_draft_attn(cache.kv, dev(torch, q1), scale, out, ws)
+    cache.append(dev(torch, Kt[T:T + nq]), dev(torch, Vt[T:T + nq]))
+    qv = np.stack([synth.activations(Hq, D, 5, t0=T + i) for i in range(nq)])
+    outv = torch.empty((nq, Hq, D), dtype=torch.float32, device="cuda")
+    wsv = torch.empty(cass.cass_kv_attn_ws_bytes(cache.kv, nq, Hq) + 256, dtype=torch.uint8,
+                      device="cuda")
+    cass.cass_kv_verify_attn(cache.kv, dev(torch, qv), scale, outv, wsv)
+    torch.cuda.synchronize()
+    got, gotv = out.cpu().numpy(), outv.cpu().numpy()
+    # the same call again gives the same bits (workgroups that share a CU
+    # with another one included: more than 256 workgroups here)
+    for _ in range(2):
+        again = torch.empty_like(outv)
+        cass.cass_kv_verify_attn(cache.kv, dev(torch, qv), scale, again, wsv)
+        torch.cuda.synchronize()
+        assert np.array_equal(again.cpu().numpy(), gotv), "verification attention not deterministic"
+    p = cache.params
+    caps = (p.max_tokens, p.code_cap_bits, p.vcode_cap_bits)
+    Ttot = T + nq
+    for h in range(H):
+        sk, _, _ = orc.kv_encode(Kt[:T, h, :], T, k, m, *caps, fmt=fmt)
+        sv, _, _ = orc.kv_encode(Vt[:T, h, :], T, k, m, *caps, fmt=fmt)
+        Kd = orc.kv_decode(sk, T, D, k, m, *caps, fmt=fmt)
+        Vd = orc.kv_decode(sv, T, D, k, m, *caps, fmt=fmt)
+        ref, bound = oracle_attention(orc, q1[h * G:(h + 1) * G], Kd, Vd, scale)
+        attn_check(got[h * G:(h + 1) * G], ref, bound)
+        # the G x nq verification rows of this KV head in one oracle call
+        rows = np.concatenate([qv[:, h * G + g, :] for g in range(G)])
+        vis = [Ttot - nq + i + 1 for i in range(nq)] * G
+        ref, bound = oracle_attention(orc, rows, Kt[:Ttot, h, :], Vt[:Ttot, h, :], scale, vis)
+        gv = np.concatenate([gotv[:, h * G + g, :] for g in range(G)])
+        attn_check(gv, ref, bound)

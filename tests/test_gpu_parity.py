@@ -25,6 +25,20 @@ def gpu():
     return torch, cass
 
 
+@pytest.fixture
+def opt(gpu):
+    """Sets library code-path options for one test and restores the defaults."""
+    torch, cass = gpu
+    names = []
+
+    def set_option(name, value):
+        cass.cass_set_option(name, value)
+        names.append(name)
+    yield set_option
+    for n in names:
+        cass.cass_set_option(n, 0)
+
+
 def dev(torch, a):
     a = np.ascontiguousarray(a, dtype=np.uint16)
     return torch.from_numpy(a.view(np.int16)).cuda()
@@ -171,18 +185,18 @@ EXACT_CASES = [
 
 
 @pytest.mark.parametrize("path", ["default", "blocks1", "blocks2", "direct"])
-def test_exact_paths(gpu, orc, monkeypatch, path):
+def test_exact_paths(gpu, orc, opt, path):
     """Reconstruction, draft decode and verification GEMM (Cassandra-1) through
     each decoder: the staged kernel with its default stage width, with stages
-    of one or two blocks (CASS_EXACT_BLOCKS), and the per-thread stream readers
-    (CASS_EXACT_PATH=direct)."""
+    of one or two blocks (option exact_blocks), and the per-thread stream readers
+    (option exact_path)."""
     torch, cass = gpu
     if path == "blocks1":
-        monkeypatch.setenv("CASS_EXACT_BLOCKS", "1")
+        opt("exact_blocks", 1)
     elif path == "blocks2":
-        monkeypatch.setenv("CASS_EXACT_BLOCKS", "2")
+        opt("exact_blocks", 2)
     elif path == "direct":
-        monkeypatch.setenv("CASS_EXACT_PATH", "direct")
+        opt("exact_path", 1)
     for case in EXACT_CASES:
         R, C, k, m, B, kind = case
         print("case", path, case, flush=True)
@@ -205,14 +219,14 @@ def test_exact_paths(gpu, orc, monkeypatch, path):
 
 
 @pytest.mark.parametrize("fmt", [1, 2])
-def test_direct_gemv_path(gpu, orc, monkeypatch, fmt):
-    """The direct (non-staged) GEMV kernels, selected with CASS_GEMV_DIRECT=1."""
+def test_direct_gemv_path(gpu, orc, opt, fmt):
+    """The direct (non-staged) GEMV kernels, selected with the gemv_path option."""
     torch, cass = gpu
     R, C, k, m = 70, 4096, 1229, 3
     w = make_w(R, C, 606)
     spec_o, _ = orc.encode(w, k, m, fmt=fmt)
     enc = cass.encode(dev(torch, w), k, m, fmt=fmt)
-    monkeypatch.setenv("CASS_GEMV_DIRECT", "1")
+    opt("gemv_path", 2)
     for batch in (1, 2):
         x = synth.activations(batch, C, 5)
         y = torch.full((batch, R), float("nan"), dtype=torch.float32, device="cuda")
@@ -223,7 +237,7 @@ def test_direct_gemv_path(gpu, orc, monkeypatch, fmt):
 
 
 BAL_CASES = [
-    # rows, cols, keep, mant, block, parts (CASS_GEMV_PARTS; 0 = default), weights
+    # rows, cols, keep, mant, block, parts (gemv_parts option; 0 = default), weights
     (64, 4096, 1229, 3, 256, 0, "normal"),    # q=0.3, 8 values per group
     (67, 4096, 819, 3, 256, 0, "normal"),     # q=0.2, 4 per group, ragged last round
     (48, 4096, 1024, 4, 256, 0, "normal"),    # q=0.25, m=4: 6 per group
@@ -240,7 +254,7 @@ BAL_CASES = [
 
 
 BAL_C2_CASES = [
-    # rows, cols, keep, mant, block, parts (CASS_GEMV_PARTS; 0 = default), weights
+    # rows, cols, keep, mant, block, parts (gemv_parts option; 0 = default), weights
     (64, 2560, 768, 3, 256, 0, "normal"),     # Qwen3-4B width, 6 fields per group
     (67, 4096, 819, 3, 256, 0, "normal"),     # ragged last round
     (33, 2048, 1024, 0, 128, 64, "normal"),   # sign-only significand: 8 per group
@@ -253,7 +267,7 @@ BAL_C2_CASES = [
 
 
 @pytest.mark.parametrize("case", BAL_C2_CASES, ids=[str(c) for c in BAL_C2_CASES])
-def test_balanced_gemv_c2(gpu, orc, monkeypatch, case):
+def test_balanced_gemv_c2(gpu, orc, opt, case):
     """The balanced draft GEMV for Cassandra-2 (shared exponent per 32
     positions) across part counts, mantissa widths and batches."""
     torch, cass = gpu
@@ -263,7 +277,7 @@ def test_balanced_gemv_c2(gpu, orc, monkeypatch, case):
     spec_o, _ = orc.encode(w, k, m, block=B, fmt=2)
     enc = cass.encode(dev(torch, w), k, m, block=B, fmt=2)
     if parts:
-        monkeypatch.setenv("CASS_GEMV_PARTS", str(parts))
+        opt("gemv_parts", parts)
     for batch in (1, 2, 3):
         x = synth.activations(batch, C, 7, t0=batch)
         y = torch.full((batch, R), float("nan"), dtype=torch.float32, device="cuda")
@@ -296,7 +310,7 @@ def bal_weights(R, C, kind, seed):
 
 
 @pytest.mark.parametrize("case", BAL_CASES, ids=[str(c) for c in BAL_CASES])
-def test_balanced_gemv_variants(gpu, orc, monkeypatch, case):
+def test_balanced_gemv_variants(gpu, orc, opt, case):
     """The balanced draft GEMV (default Cassandra-1 path) across part counts,
     keep ratios, blocks, long codes and the global-code fallback."""
     torch, cass = gpu
@@ -306,7 +320,7 @@ def test_balanced_gemv_variants(gpu, orc, monkeypatch, case):
     spec_o, _ = orc.encode(w, k, m, block=B)
     enc = cass.encode(dev(torch, w), k, m, block=B)
     if parts:
-        monkeypatch.setenv("CASS_GEMV_PARTS", str(parts))
+        opt("gemv_parts", parts)
     for batch in (1, 3):
         x = synth.activations(batch, C, 6, t0=batch)
         y = torch.full((batch, R), float("nan"), dtype=torch.float32, device="cuda")
@@ -317,7 +331,7 @@ def test_balanced_gemv_variants(gpu, orc, monkeypatch, case):
 
 
 @pytest.mark.parametrize("path", ["staged", "direct"])
-def test_other_gemv_paths(gpu, orc, monkeypatch, path):
+def test_other_gemv_paths(gpu, orc, opt, path):
     """The staged and direct kernels, which serve shapes the balanced kernel
     does not take (selected here by environment)."""
     torch, cass = gpu
@@ -326,9 +340,9 @@ def test_other_gemv_paths(gpu, orc, monkeypatch, path):
     spec_o, _ = orc.encode(w, k, m)
     enc = cass.encode(dev(torch, w), k, m)
     if path == "staged":
-        monkeypatch.setenv("CASS_GEMV_PATH", "staged")
+        opt("gemv_path", 1)
     else:
-        monkeypatch.setenv("CASS_GEMV_DIRECT", "1")
+        opt("gemv_path", 2)
     x = synth.activations(2, C, 7)
     y = torch.full((2, R), float("nan"), dtype=torch.float32, device="cuda")
     cass.cass_draft_gemv(enc.desc, dev(torch, x), y)
@@ -367,42 +381,81 @@ def test_empty_tensor(gpu):
     torch.cuda.synchronize()
 
 
-def test_llama8b_layer_full_size(gpu, orc):
-    """The 8B-shaped layer (q|k|v, o, gate|up, down) at keep 0.3, 3 mantissa bits,
-    in the launch configuration the benchmark times: o's streams byte
-    for byte; every matrix reconstructs exactly and its host copy validates;
-    sampled draft-GEMV / verify-GEMM outputs match the oracle."""
+LLAMA_MATS = ["qkv", "o", "gu", "down"]
+
+
+@pytest.fixture(scope="module")
+def llama_layer():
+    return synth.fused_layer(synth.LLAMA3_8B, config=2, layer=0, outlier_frac=0.01)
+
+
+@pytest.fixture(scope="module")
+def qwen_layer():
+    return synth.fused_layer(synth.QWEN3_4B, config=5, layer=0, outlier_frac=0.0)
+
+
+def full_size_check(torch, cass, orc, w, k, m, fmt, batch):
+    """One matrix at its full shape, encoded by the library as the benchmark
+    does: both streams byte for byte against the oracle's encoding of the whole
+    matrix, exact reconstruction, and every output of the draft GEMV (the
+    benchmark's launch configuration) and of the N = 5 verification GEMM."""
+    R, C = w.shape
+    wd = dev(torch, w)
+    enc = cass.encode(wd, k, m, fmt=fmt)
+    out = torch.empty_like(wd)
+    cass.cass_reconstruct(enc.desc, out)
+    x = synth.activations(batch, C, 2)
+    y = torch.full((batch, R), float("nan"), dtype=torch.float32, device="cuda")
+    cass.cass_draft_gemv(enc.desc, dev(torch, x), y)
+    X = synth.activations(5, C, 2, t0=10)
+    Y = torch.full((5, R), float("nan"), dtype=torch.float32, device="cuda")
+    cass.cass_verify_gemm(enc.desc, dev(torch, X), Y)
+    torch.cuda.synchronize()
+    assert torch.equal(out, wd), "reconstruction"
+    spec_g, verif_g = host_u8(enc.spec), host_u8(enc.verif)
+    del enc, out, wd
+    spec_o, verif_o = orc.encode(w, k, m, fmt=fmt)
+    assert np.array_equal(spec_g, spec_o), "speculation stream"
+    assert np.array_equal(verif_g, verif_o), "verification stream"
+    y_ref, absy = orc.product(spec_o, x, threads=8)
+    check_product(y.cpu().numpy(), y_ref, absy)
+    Y_ref, absY = orc.product(spec_o, X, verif=verif_o, threads=8)
+    check_product(Y.cpu().numpy(), Y_ref, absY)
+
+
+@pytest.mark.parametrize("name", LLAMA_MATS)
+def test_llama8b_layer_full_size(gpu, orc, llama_layer, name):
+    """The Llama-3-8B-shaped layer (q|k|v, o, gate|up, down) at keep 0.3, 3
+    mantissa bits, Cassandra-1, batch 1: the benchmark's workload, every byte
+    and every output."""
     torch, cass = gpu
-    layer = synth.fused_layer(synth.LLAMA3_8B, config=2, layer=0, outlier_frac=0.01)
-    rng = np.random.default_rng(0)
-    for name, w in layer.items():
-        R, C = w.shape
-        k = synth.keep_count(0.3, C)
-        print("matrix", name, w.shape, flush=True)
-        wd = dev(torch, w)
-        enc = cass.encode(wd, k, 3)
-        out = torch.empty_like(wd)
-        cass.cass_reconstruct(enc.desc, out)
-        torch.cuda.synchronize()
-        assert torch.equal(out, wd)
-        spec_g, verif_g = host_u8(enc.spec), host_u8(enc.verif)
-        assert cass.cass_tensor_validate(spec_g, verif_g) == cass.CASS_OK
-        if name == "o":
-            spec_o, verif_o = orc.encode(w, k, 3)
-            assert np.array_equal(spec_g, spec_o) and np.array_equal(verif_g, verif_o)
-        rows = np.unique(np.concatenate([[0, R - 1], rng.integers(0, R, 62)]))
-        x = synth.activations(1, C, 2)
-        y = torch.empty((1, R), dtype=torch.float32, device="cuda")
-        cass.cass_draft_gemv(enc.desc, dev(torch, x), y)
-        X = synth.activations(5, C, 2, t0=10)
-        Y = torch.empty((5, R), dtype=torch.float32, device="cuda")
-        cass.cass_verify_gemm(enc.desc, dev(torch, X), Y)
-        torch.cuda.synchronize()
-        # the draft of a row depends on that row alone, so the oracle encodes
-        # just the sampled rows to get their reference outputs
-        spec_r, verif_r = orc.encode(w[rows], k, 3)
-        y_ref, absy = orc.product(spec_r, x)
-        check_product(y.cpu().numpy()[:, rows], y_ref, absy)
-        Y_ref, absY = orc.product(spec_r, X, verif=verif_r)
-        check_product(Y.cpu().numpy()[:, rows], Y_ref, absY)
-        del enc, out, wd
+    w = llama_layer[name]
+    print("matrix", name, w.shape, flush=True)
+    full_size_check(torch, cass, orc, w, synth.keep_count(0.3, w.shape[1]), 3, 1, 1)
+
+
+@pytest.mark.parametrize("name", LLAMA_MATS)
+def test_qwen3_4b_c2_full_size(gpu, orc, qwen_layer, name):
+    """The Qwen3-4B-shaped layer at keep 0.3, 3 mantissa bits, Cassandra-2
+    (shared exponent per 32 positions), batch 2: the benchmark's 36-layer
+    stack's shapes, every byte and every output."""
+    torch, cass = gpu
+    w = qwen_layer[name]
+    print("matrix", name, w.shape, flush=True)
+    full_size_check(torch, cass, orc, w, synth.keep_count(0.3, w.shape[1]), 3, 2, 2)
+
+
+@pytest.mark.parametrize("fmt", [1, 2])
+def test_strided_encode(gpu, orc, fmt):
+    """Rows of the input spaced ld > cols elements apart (a column slice of a
+    wider matrix) encode to the same bytes as the contiguous rows."""
+    torch, cass = gpu
+    R, C, ld = 37, 1024, 1536
+    wide = synth.weight(R, ld, 91 + fmt, outlier_frac=0.01)
+    wd = dev(torch, wide)[:, 256:256 + C]
+    assert wd.stride(0) == ld
+    enc = cass.encode(wd, 307, 3, fmt=fmt)
+    torch.cuda.synchronize()
+    spec_o, verif_o = orc.encode(wide[:, 256:256 + C], 307, 3, fmt=fmt)
+    assert np.array_equal(host_u8(enc.spec), spec_o)
+    assert np.array_equal(host_u8(enc.verif), verif_o)
