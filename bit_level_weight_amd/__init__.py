@@ -31,10 +31,11 @@ EXPORTED = (
     "cass_tensor_validate", "cass_status_string", "cass_last_error", "cass_version",
     "cass_kv_bytes", "cass_kv_init", "cass_kv_append_ws_bytes", "cass_kv_append_encode",
     "cass_kv_status", "cass_kv_decode", "cass_kv_attn_ws_bytes", "cass_kv_draft_attn",
-    "cass_kv_verify_attn", "cass_set_option", "cass_stream_read",
+    "cass_kv_verify_attn", "cass_set_option", "cass_stream_read", "cass_kv_draft_attn_static",
 )
 CASS_STREAM_READ_BLOCKS = 2048
 CASS_KV_STATE_BYTES = 4096
+CASS_KV_STATIC_SCRATCH_BYTES = 32 << 20
 CASS_KV_FLAG_TABLES, CASS_KV_FLAG_OVERFLOW = 1, 2
 
 
@@ -130,6 +131,7 @@ def lib():
         L.cass_kv_attn_ws_bytes.argtypes = [KV, I32, I32, ctypes.POINTER(I64)]
         L.cass_kv_draft_attn.argtypes = [KV, P, I32, ctypes.c_float, P, P, I64, P]
         L.cass_kv_verify_attn.argtypes = [KV, P, I32, I32, ctypes.c_float, P, P, I64, P]
+        L.cass_kv_draft_attn_static.argtypes = [KV, P, I32, ctypes.c_float, P, P]
         _lib = L
     return _lib
 
@@ -338,6 +340,13 @@ def cass_kv_draft_attn(kv: CassKv, q, scale, out, ws, stream=None):
     _check(lib().cass_kv_draft_attn(ctypes.byref(kv), _ptr(q), q.shape[0], float(scale),
                                     _ptr(out), _ptr(ws), ws.numel() * ws.element_size(),
                                     _stream(stream)))
+
+
+def cass_kv_draft_attn_static(kv: CassKv, q, scale, out, stream=None):
+    """cass_kv_draft_attn with the library's fixed device scratch instead of a
+    workspace (allocates nothing; calls on one device must not overlap)."""
+    _check(lib().cass_kv_draft_attn_static(ctypes.byref(kv), _ptr(q), q.shape[0], float(scale),
+                                           _ptr(out), _stream(stream)))
 
 
 def cass_kv_verify_attn(kv: CassKv, q, scale, out, ws, stream=None):

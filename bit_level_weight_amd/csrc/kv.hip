@@ -13,6 +13,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "bits.hpp"
 #include "decoders.hpp"
 #include "internal.hpp"
@@ -1160,6 +1162,36 @@ int run_attention(const cass_kv* kv, const uint16_t* q, int nq, int n_q_heads, f
   return CASS_OK;
 }
 
+// Fixed scratch of the allocation-free draft attention: the per-chunk
+// partials live in this array instead of a caller workspace.  Each device the
+// library runs on holds its own copy until the process ends; host code uses
+// the address hipGetSymbolAddress returns for the current device, never the
+// array's name (which on the host is only a stand-in).
+constexpr int64_t kStaticScratchBytes = CASS_KV_STATIC_SCRATCH_BYTES;
+__device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// Device address of the current device's scratch (looked up once per device).
+int static_scratch(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return report(CASS_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return report(CASS_ERR_UNSUPPORTED, "device index %d", dev);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return report(CASS_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return CASS_OK;
+}
+
 }  // namespace
 
 }  // namespace cass
@@ -1290,6 +1322,22 @@ int cass_kv_draft_attn(const cass_kv* kv, const uint16_t* q, int n_q_heads, floa
                        void* ws, int64_t ws_bytes, hipStream_t stream) {
   clear_error();
   return run_attention(kv, q, 1, n_q_heads, scale, out, ws, ws_bytes, stream, false);
+}
+
+int cass_kv_draft_attn_static(const cass_kv* kv, const uint16_t* q, int n_q_heads, float scale,
+                              float* out, hipStream_t stream) {
+  clear_error();
+  int st = check_kv(kv);
+  if (st) return st;
+  if (n_q_heads < kv->p.n_kv_heads || n_q_heads % kv->p.n_kv_heads)
+    return report(CASS_ERR_INVALID, "n_q_heads must be a multiple of n_kv_heads");
+  const int64_t need = attn_ws(kv, 1, n_q_heads / kv->p.n_kv_heads);
+  if (need > kStaticScratchBytes)
+    return report(CASS_ERR_CAPACITY, "draft attention needs %lld scratch bytes, the fixed scratch holds %lld",
+                  (long long)need, (long long)kStaticScratchBytes);
+  void* ws = nullptr;
+  if ((st = static_scratch(&ws))) return st;
+  return run_attention(kv, q, 1, n_q_heads, scale, out, ws, kStaticScratchBytes, stream, false);
 }
 
 int cass_kv_verify_attn(const cass_kv* kv, const uint16_t* q, int nq, int n_q_heads, float scale,

@@ -299,6 +299,21 @@ int cass_kv_draft_attn(const cass_kv* kv, const uint16_t* q, int n_q_heads, floa
 int cass_kv_verify_attn(const cass_kv* kv, const uint16_t* q, int nq, int n_q_heads, float scale,
                         float* out, void* ws, int64_t ws_bytes, hipStream_t stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * cass_kv_draft_attn with no workspace argument.  Its per-chunk partials go
+ * to a fixed scratch array of CASS_KV_STATIC_SCRATCH_BYTES that the library
+ * holds on each device it runs on (until the process ends); the call
+ * allocates nothing.  The partials take n_kv_heads * ceil(tokens / 128) *
+ * (n_q_heads / n_kv_heads) * 520 bytes (128K tokens of 32 query heads fit);
+ * a larger call returns CASS_ERR_CAPACITY before launching anything.  Every
+ * call on one device shares that device's scratch: calls that overlap in
+ * time on one device (two streams, two threads) race and must be ordered by
+ * the caller.  Same arguments and results as cass_kv_draft_attn. */
+#define CASS_KV_STATIC_SCRATCH_BYTES (32ll << 20)
+int cass_kv_draft_attn_static(const cass_kv* kv, const uint16_t* q, int n_q_heads, float scale,
+                              float* out, hipStream_t stream);
+
 /* Status code -> fixed English text, and the detail of the last error on
  * the calling thread ("" if none); plumbing, not part of the method. */
 const char* cass_status_string(int status);
