@@ -19,7 +19,9 @@ CPU oracle timed on a row sample.
 
 Modes for profiling: --mode gemv runs only the timed GEMV steps; --mode exact
 runs the verification GEMM (N = 5) and the reconstruction of each matrix; --mode copy
-runs a plain 1 GiB device copy (to calibrate the HBM byte counters).
+runs a plain 1 GiB device copy (to calibrate the HBM byte counters); --mode spec
+runs only the speculative step over the 32-layer stack (and, without
+--no-extras, the dense bf16 context).
 """
 from __future__ import annotations
 
@@ -47,7 +49,7 @@ def parse():
     ap.add_argument("--mant", type=int, default=3)
     ap.add_argument("--block", type=int, default=256)
     ap.add_argument("--copies", type=int, default=8)
-    ap.add_argument("--mode", choices=("full", "gemv", "exact", "copy"), default="full")
+    ap.add_argument("--mode", choices=("full", "gemv", "exact", "copy", "spec"), default="full")
     ap.add_argument("--no-extras", action="store_true", help="headline and CPU baseline only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -117,6 +119,28 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"mode": "copy", "bytes": 1 << 30}))
+        return
+
+    if args.mode == "spec":
+        # the speculative step over 32 layers and the dense context, nothing else
+        gen = torch.Generator(device="cuda")
+        gen.manual_seed(2_000_001)
+        ws = torch.empty(cass.cass_encode_ws_bytes(28672, 4096, cass._params(1, 3, args.block, 1)),
+                         dtype=torch.uint8, device="cuda")
+        stack = []
+        for _ in range(32):
+            L = torch_layer(torch, synth.LLAMA3_8B, gen)
+            stack.append({n: cass.encode(L[n], synth.keep_count(0.3, L[n].shape[1]), 3,
+                                         block=args.block, ws=ws) for n in L})
+            del L
+        torch.cuda.synchronize()
+        log("stack encoded")
+        res = {"mode": "spec", "spec_step_llama8b": run_spec_step(torch, cass, synth, stack, dev16)}
+        del stack
+        torch.cuda.empty_cache()
+        if not args.no_extras:
+            res["dense_bf16_llama8b_context"] = run_dense_stack(torch, synth)
+        print(json.dumps(res))
         return
 
     # ---- inputs: layer 0 from the numpy recipe, further copies from torch's generator
@@ -398,7 +422,11 @@ def run_extras(args, torch, cass, synth, timer, stream, layers, encs, layer0, en
         "draft_GB_s": round(sb / (draft_ms * 1e-3) / 1e9, 1), "spec_GB": round(sb / 1e9, 3),
         "verify_n5_ms": round(verify_ms, 3), "spec_plus_verif_GB": round((sb + vb) / 1e9, 3),
         "note": "linear layers only (4 fused GEMVs per layer), keep 0.3, m=3, Cassandra-1"}
+    out["spec_step_llama8b"] = run_spec_step(torch, cass, synth, stack, dev16)
     del stack
+    torch.cuda.empty_cache()
+    log("spec step done")
+    out["dense_bf16_llama8b_context"] = run_dense_stack(torch, synth)
     torch.cuda.empty_cache()
     log("stack done")
 
@@ -502,6 +530,108 @@ def run_extras(args, torch, cass, synth, timer, stream, layers, encs, layer0, en
     torch.cuda.empty_cache()
     log("qwen kv done")
     return out
+
+
+def graph_ms(torch, g, reps):
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    g.replay()
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(reps):
+        g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps
+
+
+def run_spec_step(torch, cass, synth, stack, dev16, T=32768, k=4):
+    """One self-speculative step over the 32 encoded layers, each with its own
+    compressed KV cache at T tokens (8 KV heads x 128, 32 query heads): k draft
+    passes (draft GEMVs, one-token KV append, draft attention) and one
+    verification pass of k+1 tokens (verification GEMMs, KV append,
+    verification attention), acceptance stubbed."""
+    from bit_level_weight_amd.spec_step import SpecStep, draw_accepted, expected_tokens
+    H, Hq, D, kk, mant = 8, 32, 128, 38, 3
+    Kd = dev16(synth.kv_tensor(T, H, D, 7_000_001))
+    Vd = dev16(synth.kv_tensor(T, H, D, 7_000_002))
+    caches = []
+    for _ in stack:
+        c = cass.KvCache(H, D, kk, mant, max_tokens=T + 64)
+        c.append(Kd, Vd)
+        caches.append(c)
+    del Kd, Vd
+    st = SpecStep(stack, caches, Hq, k=k, seed=11)
+    torch.cuda.synchronize()
+    res = {"context_tokens": T, "k": k, "layers": len(stack), "kv": "Cassandra-1 keep 38/128 m3"}
+    # eager (host-driven calls), fixed context
+    st.run("step")
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(3):
+        st.run("step")
+    b.record()
+    torch.cuda.synchronize()
+    res["step_ms_eager"] = round(a.elapsed_time(b) / 3, 3)
+    # HIP graphs of the whole step and of its two phases
+    for phase in ("step", "draft", "verify"):
+        g = st.capture(phase)
+        res[f"{phase}_ms_graph"] = round(graph_ms(torch, g, 5 if phase != "step" else 5), 3)
+        del g
+    step_ms = res["step_ms_graph"]
+    res["tokens_per_s_equiv"] = {f"alpha{al}": round(1e3 * expected_tokens(al, k) / step_ms, 1)
+                                 for al in (0.74, 0.80, 0.91)}
+    res["expected_tokens_per_step"] = {f"alpha{al}": round(expected_tokens(al, k), 4)
+                                       for al in (0.74, 0.80, 0.91)}
+    # the loop with drawn acceptance (alpha 0.8): the context grows by the kept tokens
+    rng = np.random.default_rng(1234)
+    made = 0
+    a.record()
+    for _ in range(8):
+        made += st.step(draw_accepted(rng, 0.8, k))
+    b.record()
+    torch.cuda.synchronize()
+    res["drawn_alpha0.8_eager"] = {"steps": 8, "tokens": made,
+                                   "tokens_per_s": round(made / (a.elapsed_time(b) * 1e-3), 1),
+                                   "final_context": st.tokens()}
+    res["note"] = ("activations between the linear maps, queries and new K/V are resident "
+                   "synthetic bf16; norms, rotary embedding, gated activation and LM head not run")
+    del st, caches
+    return res
+
+
+def run_dense_stack(torch, synth, nl=32):
+    """Context only: the same 32-layer linear stack as dense bf16 weights,
+    torch.nn.functional.linear (the vendor BLAS) at batch 1 and 5, in a graph."""
+    import torch.nn.functional as F
+    shapes = {"qkv": (6144, 4096), "o": (4096, 4096), "gu": (28672, 4096), "down": (4096, 14336)}
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(3_000_001)
+    Ws = [{m: (torch.randn(r, c, generator=gen, device="cuda") * 0.02).to(torch.bfloat16)
+           for m, (r, c) in shapes.items()} for _ in range(nl)]
+    res = {}
+    for n in (1, 5):
+        xs = {m: torch.randn(n, c, generator=gen, device="cuda").to(torch.bfloat16)
+              for m, (r, c) in shapes.items()}
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for L in Ws:
+                for m in shapes:
+                    F.linear(xs[m], L[m])
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            ys = [F.linear(xs[m], L[m]) for L in Ws for m in shapes]
+        ms = graph_ms(torch, g, 10)
+        byts = sum(2 * r * c for r, c in shapes.values()) * nl
+        res[f"bs{n}"] = {"ms": round(ms, 3), "GB_s": round(byts / (ms * 1e-3) / 1e9, 1)}
+        del g, ys
+    res["tokens_per_s_bs1"] = round(1e3 / res["bs1"]["ms"], 1)
+    res["note"] = "dense bf16 linear maps only (no attention), measured as context, not a target"
+    del Ws
+    return res
 
 
 def read_ceiling(torch, stream):

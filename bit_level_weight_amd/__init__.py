@@ -32,6 +32,7 @@ EXPORTED = (
     "cass_kv_bytes", "cass_kv_init", "cass_kv_append_ws_bytes", "cass_kv_append_encode",
     "cass_kv_status", "cass_kv_decode", "cass_kv_attn_ws_bytes", "cass_kv_draft_attn",
     "cass_kv_verify_attn", "cass_set_option", "cass_stream_read", "cass_kv_draft_attn_static",
+    "cass_kv_truncate",
 )
 CASS_STREAM_READ_BLOCKS = 2048
 CASS_KV_STATE_BYTES = 4096
@@ -132,6 +133,7 @@ def lib():
         L.cass_kv_draft_attn.argtypes = [KV, P, I32, ctypes.c_float, P, P, I64, P]
         L.cass_kv_verify_attn.argtypes = [KV, P, I32, I32, ctypes.c_float, P, P, I64, P]
         L.cass_kv_draft_attn_static.argtypes = [KV, P, I32, ctypes.c_float, P, P]
+        L.cass_kv_truncate.argtypes = [KV, I64, P]
         _lib = L
     return _lib
 
@@ -318,6 +320,10 @@ def cass_kv_append_encode(kv: CassKv, k, v, ws, stream=None):
                                        ws.numel() * ws.element_size(), _stream(stream)))
 
 
+def cass_kv_truncate(kv: CassKv, tokens: int, stream=None):
+    _check(lib().cass_kv_truncate(ctypes.byref(kv), int(tokens), _stream(stream)))
+
+
 def cass_kv_status(kv: CassKv, stream=None):
     t, f = ctypes.c_int64(0), ctypes.c_uint32(0)
     _check(lib().cass_kv_status(ctypes.byref(kv), ctypes.byref(t), ctypes.byref(f),
@@ -381,6 +387,9 @@ class KvCache:
         if self._ws is None or self._ws.numel() < need:
             self._ws = torch.empty(max(need, 1), dtype=torch.uint8, device=k.device)
         cass_kv_append_encode(self.kv, k, v, self._ws, stream)
+
+    def truncate(self, tokens, stream=None):
+        cass_kv_truncate(self.kv, tokens, stream)
 
     @property
     def tokens(self):

@@ -366,6 +366,68 @@ __global__ void __launch_bounds__(64 * kWaves) k_kv_pack(KvDev kv, const uint16_
   }
 }
 
+// ---- truncation: drop the newest tokens of every stream ----
+// Bits [b0, b1) of a bit section set to zero (one thread per word).
+__device__ void clear_bits(uint8_t* sec, uint64_t b0, uint64_t b1, int tid, int nthr) {
+  if (b1 <= b0) return;
+  uint32_t* w = reinterpret_cast<uint32_t*>(sec);
+  for (uint64_t i = (b0 >> 5) + tid; i <= (b1 - 1) >> 5; i += nthr) {
+    const uint64_t lo = i * 32 > b0 ? i * 32 : b0, hi = i * 32 + 32 < b1 ? i * 32 + 32 : b1;
+    const uint32_t width = (uint32_t)(hi - lo), sh = (uint32_t)(lo - i * 32);
+    const uint32_t mask = width == 32 ? 0xFFFFFFFFu : ((1u << width) - 1u) << sh;
+    w[i] &= ~mask;
+  }
+}
+
+__device__ void clear_bytes(uint8_t* sec, int64_t b0, int64_t b1, int tid, int nthr) {
+  for (int64_t i = b0 + tid; i < b1; i += nthr) sec[i] = 0;
+}
+
+// One workgroup per stream.  Keeps tokens [0, t_new) of the t_old cached:
+// every per-token part past t_new goes back to zero and each code tail moves
+// back to the first code bit of token t_new, so the stream holds exactly the
+// bytes of t_new appended tokens (a stream closed by an overflow stays closed
+// if token t_new's codes were not written).
+__global__ void __launch_bounds__(256) k_kv_truncate(KvDev kv, int64_t t_new, int64_t t_old) {
+  const int s = blockIdx.x, tid = threadIdx.x, nthr = blockDim.x;
+  uint8_t* sr = kv.spec + s * kv.sstride;
+  uint8_t* vr = kv.verif + s * kv.vstride;
+  const int64_t D = kv.D, k = kv.k, m = kv.m;
+  const bool c1 = kv.fmt == CASS_FMT_C1_UNARY;
+  // first code bit of token t_new: C-1 speculation codes / pruned codes;
+  // C-2 kept residues / pruned codes
+  const uint32_t* vofs = reinterpret_cast<const uint32_t*>(vr + kv.vo[3]);
+  const uint32_t first[2] = {c1 ? reinterpret_cast<const uint32_t*>(sr + kv.so[2])[t_new]
+                                 : vofs[2 * t_new],
+                             c1 ? vofs[t_new] : vofs[2 * t_new + 1]};
+  uint8_t* code_sec[2] = {c1 ? sr + kv.so[4] : vr + kv.vo[1], vr + kv.vo[4]};
+  __shared__ unsigned long long tail_s[2];
+  if (tid < 2) tail_s[tid] = kv.state[2 + 2 * s + tid];
+  __syncthreads();
+  for (int which = 0; which < 2; ++which) {
+    if (first[which] == 0xFFFFFFFFu) continue;  // closed before t_new: nothing written since
+    clear_bits(code_sec[which], first[which], tail_s[which], tid, nthr);
+  }
+  // fixed-size per-token parts
+  clear_bytes(sr + kv.so[1], t_new * D / 8, t_old * D / 8, tid, nthr);  // keep bitmap
+  if (c1) {
+    clear_bytes(sr + kv.so[2], 4 * t_new, 4 * t_old, tid, nthr);        // code offsets
+    clear_bits(sr + kv.so[3], (uint64_t)(t_new * k * (1 + m)), (uint64_t)(t_old * k * (1 + m)),
+               tid, nthr);                                               // sign + top mantissa
+    clear_bits(vr + kv.vo[1], (uint64_t)(t_new * k * (7 - m)), (uint64_t)(t_old * k * (7 - m)),
+               tid, nthr);                                               // low mantissa
+  } else {
+    clear_bytes(sr + kv.so[2], t_new * D / 32, t_old * D / 32, tid, nthr);  // shared exponents
+    clear_bits(sr + kv.so[3], (uint64_t)(t_new * k * (2 + m)), (uint64_t)(t_old * k * (2 + m)),
+               tid, nthr);                                               // sign + significand
+  }
+  clear_bytes(vr + kv.vo[2], t_new * (D - k), t_old * (D - k), tid, nthr);  // pruned bytes
+  clear_bytes(vr + kv.vo[3], (c1 ? 4 : 8) * t_new, (c1 ? 4 : 8) * t_old, tid, nthr);  // offsets
+  __syncthreads();
+  if (tid < 2 && first[tid] != 0xFFFFFFFFu) kv.state[2 + 2 * s + tid] = first[tid];
+  if (s == 0 && tid == 0) kv.state[0] = (unsigned long long)t_new;
+}
+
 // ---- per-lane decoder of one cached vector (token tok of stream s) ----
 // kept(w) gives the vector's kept values in position order (w: the bitmap
 // word the value sits in), pruned() its pruned values (exact decoding only);
@@ -1271,6 +1333,20 @@ int cass_kv_append_encode(cass_kv* kv, const uint16_t* k, const uint16_t* v, int
   k_kv_pack<<<grid_of(nvec, kWaves), 64 * kWaves, 0, stream>>>(d, k, v, ntok, kv->tokens, w);
   if ((e = hipGetLastError()) != hipSuccess) return report(CASS_ERR_HIP, "append: %s", hipGetErrorString(e));
   kv->tokens += ntok;
+  return CASS_OK;
+}
+
+int cass_kv_truncate(cass_kv* kv, int64_t tokens, hipStream_t stream) {
+  clear_error();
+  int st = check_kv(kv);
+  if (st) return st;
+  if (tokens < 0 || tokens > kv->tokens) return report(CASS_ERR_INVALID, "truncate to %lld of %lld tokens",
+                                                       (long long)tokens, (long long)kv->tokens);
+  if (tokens == kv->tokens) return CASS_OK;
+  k_kv_truncate<<<2 * kv->p.n_kv_heads, 256, 0, stream>>>(dev_of(kv), tokens, kv->tokens);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return report(CASS_ERR_HIP, "truncate: %s", hipGetErrorString(e));
+  kv->tokens = tokens;
   return CASS_OK;
 }
 

@@ -270,6 +270,19 @@ int cass_kv_append_ws_bytes(const cass_kv* kv, int ntok, int64_t* ws_bytes);
  * CASS_KV_FLAG_OVERFLOW (see cass_kv_status).  Advances kv->tokens. */
 int cass_kv_append_encode(cass_kv* kv, const uint16_t* k, const uint16_t* v, int ntok,
                           void* ws, int64_t ws_bytes, hipStream_t stream);
+/* Drop the newest tokens: keep tokens [0, tokens) of the kv->tokens cached
+ * (Cassandra review, section 1: drafted tokens that the target's parallel
+ * verification rejects are discarded, and the draft's own keys and values of
+ * the drafted tokens give way to the target's).  Every per-token part past
+ * the kept tokens returns to zero and each code tail moves back, so the
+ * regions hold exactly the bytes of appending the kept tokens (the rank
+ * tables stay frozen; truncating to 0 makes the next append build them
+ * again).  A stream closed by an overflow reopens when the codes of the
+ * first dropped token had been written (else it stays closed, its tail at the
+ * capacity); CASS_KV_FLAG_OVERFLOW stays set.  0 <= tokens <=
+ * kv->tokens, else CASS_ERR_INVALID.  One launch, no host synchronisation;
+ * sets kv->tokens. */
+int cass_kv_truncate(cass_kv* kv, int64_t tokens, hipStream_t stream);
 /* Token count and flags from the device state of the online encoder
  * (Cassandra review, section 3.3).  Synchronises the stream. */
 int cass_kv_status(const cass_kv* kv, int64_t* tokens, uint32_t* flags, hipStream_t stream);
