@@ -19,7 +19,7 @@ _SRC = os.path.join(_HERE, "cass_oracle.c")
 _LIB = os.path.join(_HERE, "libcass_oracle.so")
 
 OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_OVERFLOW, ERR_CORRUPT, ERR_CAPACITY = range(6)
-FMT_C1, FMT_C2 = 1, 2
+FMT_C1, FMT_C2, FMT_C2T = 1, 2, 3
 MAGIC_SPEC, MAGIC_VERIF = 0x50535343, 0x46565343
 
 
@@ -61,6 +61,7 @@ def lib():
         L.orc_product.argtypes = [P, I64, P, I64, P, I64, P, P, ctypes.c_int]
         L.orc_product_rows.argtypes = [P, I64, P, I64, P, I64, P, I64, P, P]
         L.orc_header.argtypes = [P, I64, ctypes.c_uint32, P, P, P]
+        L.orc_mx_target.argtypes = [P, I64, I64, P]
         _lib = L
     return _lib
 
@@ -117,6 +118,17 @@ def encode(w, k: int, m: int, block: int = 256, fmt: int = FMT_C1):
     _check(L.orc_encode(_p(w), R, C, k, m, block, fmt, _p(spec), spec.size, _p(verif),
                         verif.size, ctypes.byref(sb), ctypes.byref(vb)), "encode")
     return spec, verif
+
+
+def mx_target(w) -> np.ndarray:
+    """Target weights of format 3 (Cassandra-2 with an MX-quantised target):
+    per 32 positions of a row, every value's significand aligned to the
+    group's largest exponent and chopped to 8 bits (orc_mx_target)."""
+    w = _u16(w)
+    R, C = w.shape
+    out = np.zeros((R, C), dtype=np.uint16)
+    _check(lib().orc_mx_target(_p(w), R, C, _p(out)), "mx_target")
+    return out
 
 
 def header(buf, magic: int = MAGIC_SPEC):

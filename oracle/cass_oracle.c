@@ -197,7 +197,8 @@ static int read_header(const uint8_t* buf, int64_t len, uint32_t magic, hdr_t* h
   h->total = (int64_t)get_u64(buf + 48);
   h->nsec = get_u32(buf + 56);
   if (h->magic != magic || h->version != 1) return ORC_ERR_CORRUPT;
-  if (h->format != ORC_FMT_C1 && h->format != ORC_FMT_C2) return ORC_ERR_CORRUPT;
+  if (h->format != ORC_FMT_C1 && h->format != ORC_FMT_C2 && h->format != ORC_FMT_C2T)
+    return ORC_ERR_CORRUPT;
   if (h->mant > 7 || h->R < 0 || h->C <= 0 || h->B <= 0 || h->C % h->B || h->B % 32 ||
       h->k < 0 || h->k > h->C || h->C > 65536 || h->total > len || h->nsec > MAX_SEC)
     return ORC_ERR_CORRUPT;
@@ -244,6 +245,10 @@ enum { V1_RANK = 0, V1_ROWBASE, V1_BLKOFF, V1_LOWMANT, V1_PRUNED, V1_CODES, V1_N
 enum { S2_BITMAP = 0, S2_SHEXP, S2_KEPTB, S2_FIELDS, S2_N };
 enum { V2_RANK = 0, V2_ROWBASE_K, V2_BLKOFF_K, V2_RESID, V2_PRUNED, V2_ROWBASE_P,
        V2_BLKOFF_P, V2_CODES, V2_N };
+/* format 3: the speculation stream is Cassandra-2's; the verification stream
+ * holds the target's group exponents, the kept values' low 7-m bits of t and
+ * the pruned values' (sign, t) in 9 bits, all at fixed positions */
+enum { V3_GEXP = 0, V3_LOW, V3_PRUNED, V3_N };
 
 /* ----------------------------------------------------- Cassandra-2 helpers */
 
@@ -263,14 +268,42 @@ static uint16_t mx_draft_bits(int s, int a, int E, int m) {
   return (uint16_t)((s << 15) | (a << (E - m + 6))); /* subnormal result */
 }
 
+/* Group exponent of the target: the largest max(e,1) over 32 positions. */
+static int mx_group_exp(const uint16_t* g) {
+  int X = 0;
+  for (int i = 0; i < 32; i++)
+    if (mx_eff(g[i]) > X) X = mx_eff(g[i]);
+  return X;
+}
+
+/* The value's 8-bit significand aligned to the group exponent X, chopped. */
+static int mx_target_sig(uint16_t b, int X) {
+  int d = X - mx_eff(b);
+  return d >= 8 ? 0 : mx_sig(b) >> d;
+}
+
+int orc_mx_target(const uint16_t* w, int64_t R, int64_t C, uint16_t* out) {
+  if (R < 0 || C <= 0 || C % 32 || (R > 0 && (!w || !out))) return ORC_ERR_INVALID;
+  for (int64_t r = 0; r < R; r++)
+    for (int64_t g = 0; g < C; g += 32) {
+      const uint16_t* src = w + r * C + g;
+      int X = mx_group_exp(src);
+      for (int i = 0; i < 32; i++)
+        out[r * C + g + i] = mx_draft_bits(bf_s(src[i]), mx_target_sig(src[i], X), X, 7);
+    }
+  return ORC_OK;
+}
+
 /* ------------------------------------------------------------------ encode */
 
 int orc_encode(const uint16_t* w, int64_t R, int64_t C, int64_t k, int m, int64_t B,
                int format, uint8_t* spec, int64_t spec_cap, uint8_t* verif,
                int64_t verif_cap, int64_t* spec_bytes, int64_t* verif_bytes) {
   if (R < 0 || C <= 0 || C > 65536 || B < 32 || (B & (B - 1)) || C % B || k < 0 || k > C ||
-      m < 0 || m > 7 || (format != ORC_FMT_C1 && format != ORC_FMT_C2))
+      m < 0 || m > 7 || (format != ORC_FMT_C1 && format != ORC_FMT_C2 && format != ORC_FMT_C2T))
     return ORC_ERR_INVALID;
+  /* format 3 shares Cassandra-2's speculation stream */
+  const int c2 = format != ORC_FMT_C1;
   if (R > 0 && !w) return ORC_ERR_INVALID;
   const int64_t n = R * C, nb = C / B;
 
@@ -290,7 +323,7 @@ int orc_encode(const uint16_t* w, int64_t R, int64_t C, int64_t k, int m, int64_
 
   /* Cassandra-2: shared exponent per 32 positions over the kept values [MX] */
   uint8_t* shexp = NULL;
-  if (format == ORC_FMT_C2) {
+  if (c2) {
     shexp = (uint8_t*)calloc((size_t)(n / 32 + 1), 1);
     for (int64_t g = 0; g < n / 32; g++) {
       int E = 0;
@@ -310,12 +343,12 @@ int orc_encode(const uint16_t* w, int64_t R, int64_t C, int64_t k, int m, int64_
       if (keep[r * C + j]) {
         if (format == ORC_FMT_C1) {
           sbits[r] += (uint64_t)rank_s[bf_e(b)] + 1;
-        } else {
+        } else if (format == ORC_FMT_C2) {
           int d = shexp[(r * C + j) / 32] - mx_eff(b);
           int wdt = 7 - m + d < 8 ? 7 - m + d : 8;
           kbits[r] += (uint64_t)d + 1 + (uint64_t)wdt;
         }
-      } else {
+      } else if (format != ORC_FMT_C2T) {
         vbits[r] += (uint64_t)rank_v[bf_e(b)] + 1;
       }
     }
@@ -338,12 +371,17 @@ int orc_encode(const uint16_t* w, int64_t R, int64_t C, int64_t k, int m, int64_
                         (int64_t)((vtot + 7) / 8)};
     layout(&hs, S1_N, ls);
     layout(&hv, V1_N, lv);
-  } else {
+  } else if (format == ORC_FMT_C2) {
     int64_t ls[S2_N] = {n / 8, n / 32, 2 * R * nb, (R * k * (2 + m) + 7) / 8};
     int64_t lv[V2_N] = {256, 8 * R, 4 * R * nb, (int64_t)((ktot + 7) / 8), R * (C - k),
                         8 * R, 4 * R * nb, (int64_t)((vtot + 7) / 8)};
     layout(&hs, S2_N, ls);
     layout(&hv, V2_N, lv);
+  } else {
+    int64_t ls[S2_N] = {n / 8, n / 32, 2 * R * nb, (R * k * (2 + m) + 7) / 8};
+    int64_t lv[V3_N] = {n / 32, (R * k * (7 - m) + 7) / 8, (R * (C - k) * 9 + 7) / 8};
+    layout(&hs, S2_N, ls);
+    layout(&hv, V3_N, lv);
   }
   if (spec_bytes) *spec_bytes = hs.total;
   if (verif_bytes) *verif_bytes = hv.total;
@@ -364,7 +402,7 @@ int orc_encode(const uint16_t* w, int64_t R, int64_t C, int64_t k, int m, int64_
         if (format == ORC_FMT_C1) {
           put_u64(spec + hs.off[S1_ROWBASE] + 8 * r, sbase);
           put_u64(verif + hv.off[V1_ROWBASE] + 8 * r, vbase);
-        } else {
+        } else if (format == ORC_FMT_C2) {
           put_u64(verif + hv.off[V2_ROWBASE_K] + 8 * r, kbase);
           put_u64(verif + hv.off[V2_ROWBASE_P] + 8 * r, vbase);
         }
@@ -377,10 +415,15 @@ int orc_encode(const uint16_t* w, int64_t R, int64_t C, int64_t k, int m, int64_
               put_u32(verif + hv.off[V1_BLKOFF] + 4 * blk, (uint32_t)(vpos - vbase));
             } else {
               put_u16(spec + hs.off[S2_KEPTB] + 2 * blk, (uint16_t)kept_i);
-              put_u32(verif + hv.off[V2_BLKOFF_K] + 4 * blk, (uint32_t)(kpos - kbase));
-              put_u32(verif + hv.off[V2_BLKOFF_P] + 4 * blk, (uint32_t)(vpos - vbase));
+              if (format == ORC_FMT_C2) {
+                put_u32(verif + hv.off[V2_BLKOFF_K] + 4 * blk, (uint32_t)(kpos - kbase));
+                put_u32(verif + hv.off[V2_BLKOFF_P] + 4 * blk, (uint32_t)(vpos - vbase));
+              }
             }
           }
+          /* format 3: the target's group exponent, once per 32 positions */
+          const int X = format == ORC_FMT_C2T ? mx_group_exp(w + r * C + j / 32 * 32) : 0;
+          if (format == ORC_FMT_C2T && j % 32 == 0) verif[hv.off[V3_GEXP] + (r * C + j) / 32] = (uint8_t)X;
           uint16_t b = w[r * C + j];
           int s = bf_s(b), e = bf_e(b), f = bf_f(b);
           if (keep[r * C + j]) {
@@ -403,12 +446,25 @@ int orc_encode(const uint16_t* w, int64_t R, int64_t C, int64_t k, int m, int64_
               int wdt = shift < 8 ? shift : 8;
               put_bits(spec + hs.off[S2_FIELDS], (uint64_t)kin * (2 + m),
                        (uint64_t)((s << (m + 1)) | a), 2 + m);
-              put_unary(verif + hv.off[V2_RESID], kpos, d);
-              kpos += (uint64_t)d + 1;
-              put_bits(verif + hv.off[V2_RESID], kpos, (uint64_t)(M & ((1 << wdt) - 1)), wdt);
-              kpos += (uint64_t)wdt;
+              if (format == ORC_FMT_C2) {
+                put_unary(verif + hv.off[V2_RESID], kpos, d);
+                kpos += (uint64_t)d + 1;
+                put_bits(verif + hv.off[V2_RESID], kpos, (uint64_t)(M & ((1 << wdt) - 1)), wdt);
+                kpos += (uint64_t)wdt;
+              } else {
+                /* the target's t; its top m+1 bits are the draft's a (X == E here) */
+                int t = mx_target_sig(b, X);
+                put_bits(verif + hv.off[V3_LOW], (uint64_t)kin * (7 - m),
+                         (uint64_t)(t & ((1 << (7 - m)) - 1)), 7 - m);
+              }
             }
             kept_i++;
+          } else if (format == ORC_FMT_C2T) {
+            /* pruned, format 3: sign and t aligned to the group exponent */
+            int64_t pin = r * (C - k) + pr_i;
+            put_bits(verif + hv.off[V3_PRUNED], (uint64_t)pin * 9,
+                     (uint64_t)((s << 8) | mx_target_sig(b, X)), 9);
+            pr_i++;
           } else {
             /* pruned: sign and full mantissa byte plus the coded exponent to verif */
             int64_t pin = r * (C - k) + pr_i;
@@ -424,7 +480,8 @@ int orc_encode(const uint16_t* w, int64_t R, int64_t C, int64_t k, int m, int64_
       }
       if (format == ORC_FMT_C1) memcpy(spec + hs.off[S1_RANK], perm_s, 256);
       else memcpy(spec + hs.off[S2_SHEXP], shexp, (size_t)(n / 32));
-      memcpy(verif + (format == ORC_FMT_C1 ? hv.off[V1_RANK] : hv.off[V2_RANK]), perm_v, 256);
+      if (format != ORC_FMT_C2T)
+        memcpy(verif + (format == ORC_FMT_C1 ? hv.off[V1_RANK] : hv.off[V2_RANK]), perm_v, 256);
     }
   }
   free(keep); free(shexp); free(sbits); free(vbits); free(kbits);
@@ -502,8 +559,9 @@ static int decode_row(const uint8_t* spec, const hdr_t* hs, const uint8_t* verif
   const uint8_t* bm = spec + hs->off[S2_BITMAP];
   const uint8_t* shexp = spec + hs->off[S2_SHEXP];
   const uint8_t* fields = spec + hs->off[S2_FIELDS];
+  const int c2t = hs->format == ORC_FMT_C2T;
   uint64_t kbase = 0, kpos = 0, kend = 0, vbase = 0, vpos = 0, vend = 0;
-  if (verif) {
+  if (verif && !c2t) {
     kbase = get_u64(verif + hv->off[V2_ROWBASE_K] + 8 * r);
     vbase = get_u64(verif + hv->off[V2_ROWBASE_P] + 8 * r);
     kpos = kbase; vpos = vbase;
@@ -514,10 +572,13 @@ static int decode_row(const uint8_t* spec, const hdr_t* hs, const uint8_t* verif
     if (j % B == 0) {
       int64_t blk = r * nb + j / B;
       if (get_u16(spec + hs->off[S2_KEPTB] + 2 * blk) != (uint16_t)kept_i) return ORC_ERR_CORRUPT;
-      if (verif && (get_u32(verif + hv->off[V2_BLKOFF_K] + 4 * blk) != kpos - kbase ||
-                    get_u32(verif + hv->off[V2_BLKOFF_P] + 4 * blk) != vpos - vbase))
+      if (verif && !c2t && (get_u32(verif + hv->off[V2_BLKOFF_K] + 4 * blk) != kpos - kbase ||
+                            get_u32(verif + hv->off[V2_BLKOFF_P] + 4 * blk) != vpos - vbase))
         return ORC_ERR_CORRUPT;
     }
+    /* format 3: the target's group exponent (at least 1 in a valid stream) */
+    const int X = verif && c2t ? verif[hv->off[V3_GEXP] + (r * C + j) / 32] : 0;
+    if (verif && c2t && X < 1) return ORC_ERR_CORRUPT;
     if (get_bits(bm, (uint64_t)(r * C + j), 1)) {
       if (kept_i >= k) return ORC_ERR_CORRUPT;
       int64_t kin = r * k + kept_i;
@@ -526,6 +587,12 @@ static int decode_row(const uint8_t* spec, const hdr_t* hs, const uint8_t* verif
       int E = shexp[(r * C + j) / 32];
       if (!verif) {
         out[j] = mx_draft_bits(s, a, E, m);
+      } else if (c2t) {
+        /* t = the draft's a followed by the 7-m low bits; X equals E where
+         * the group keeps anything */
+        if (X != E) return ORC_ERR_CORRUPT;
+        int low = (int)get_bits(verif + hv->off[V3_LOW], (uint64_t)kin * (7 - m), 7 - m);
+        out[j] = mx_draft_bits(s, (a << (7 - m)) | low, X, 7);
       } else {
         int d = get_unary(verif + hv->off[V2_RESID], kpos, kend);
         if (d < 0) return ORC_ERR_CORRUPT;
@@ -541,7 +608,11 @@ static int decode_row(const uint8_t* spec, const hdr_t* hs, const uint8_t* verif
       }
       kept_i++;
     } else {
-      if (verif) {
+      if (verif && c2t) {
+        if (pr_i >= C - k) return ORC_ERR_CORRUPT;
+        int v = (int)get_bits(verif + hv->off[V3_PRUNED], (uint64_t)(r * (C - k) + pr_i) * 9, 9);
+        out[j] = mx_draft_bits(v >> 8, v & 0xFF, X, 7);
+      } else if (verif) {
         if (pr_i >= C - k) return ORC_ERR_CORRUPT;
         int byte = verif[hv->off[V2_PRUNED] + r * (C - k) + pr_i];
         int rank = get_unary(verif + hv->off[V2_CODES], vpos, vend);

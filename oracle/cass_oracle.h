@@ -31,7 +31,7 @@ extern "C" {
 
 enum { ORC_OK = 0, ORC_ERR_INVALID = 1, ORC_ERR_UNSUPPORTED = 2, ORC_ERR_OVERFLOW = 3,
        ORC_ERR_CORRUPT = 4, ORC_ERR_CAPACITY = 5 };
-enum { ORC_FMT_C1 = 1, ORC_FMT_C2 = 2 };
+enum { ORC_FMT_C1 = 1, ORC_FMT_C2 = 2, ORC_FMT_C2T = 3 };
 
 #define ORC_MAGIC_SPEC  0x50535343u /* "CSSP" */
 #define ORC_MAGIC_VERIF 0x46565343u /* "CSVF" */
@@ -49,6 +49,15 @@ int orc_histograms(const uint16_t* w, const uint8_t* keep, int64_t n,
 /* Frequency ranking: perm[r] = symbol of rank r, symbols ordered by count
  * descending, ties (and absent symbols) by symbol ascending. */
 void orc_rank_table(const uint64_t hist[256], uint8_t perm[256]);
+
+/* Cassandra-2 with an MX-quantised target (format 3, the reading in which the
+ * "slight loss" of Cassandra-2 reaches the target too): the target weights of
+ * w[R][C].  Per group of 32 positions of a row, X = the largest max(e,1) over
+ * all 32 values; each value keeps its sign and the top bits of its 8-bit
+ * significand M (hidden bit included) aligned to X, t = M >> (X - max(e,1))
+ * (0 when the shift reaches 8), i.e. the value t * 2^(X-134) written as a bf16
+ * pattern (+0 when t = 0).  Chopping, never rounding, as the draft does. */
+int orc_mx_target(const uint16_t* w, int64_t R, int64_t C, uint16_t* out);
 
 /* --- Cassandra-1 (unary exponents, lossless) and Cassandra-2 (MX-32) --- */
 
