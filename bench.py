@@ -21,7 +21,8 @@ Modes for profiling: --mode gemv runs only the timed GEMV steps; --mode exact
 runs the verification GEMM (N = 5) and the reconstruction of each matrix; --mode copy
 runs a plain 1 GiB device copy (to calibrate the HBM byte counters); --mode spec
 runs only the speculative step over the 32-layer stack (and, without
---no-extras, the dense bf16 context).
+--no-extras, the dense bf16 context); --mode mxt compares Cassandra-2 with
+a lossless and with an MX-quantised target on one Qwen3-4B-shaped layer.
 """
 from __future__ import annotations
 
@@ -49,7 +50,8 @@ def parse():
     ap.add_argument("--mant", type=int, default=3)
     ap.add_argument("--block", type=int, default=256)
     ap.add_argument("--copies", type=int, default=8)
-    ap.add_argument("--mode", choices=("full", "gemv", "exact", "copy", "spec"), default="full")
+    ap.add_argument("--mode", choices=("full", "gemv", "exact", "copy", "spec", "mxt"),
+                    default="full")
     ap.add_argument("--no-extras", action="store_true", help="headline and CPU baseline only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -119,6 +121,11 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"mode": "copy", "bytes": 1 << 30}))
+        return
+
+    if args.mode == "mxt":
+        print(json.dumps({"mode": "mxt", "c2_mx_target_qwen3_4b_layer":
+                          run_mx_target(torch, cass, synth, timer, stream, dev16)}))
         return
 
     if args.mode == "spec":
@@ -451,6 +458,9 @@ def run_extras(args, torch, cass, synth, timer, stream, layers, encs, layer0, en
     del qstack
     torch.cuda.empty_cache()
     log("qwen done")
+    out["c2_mx_target_qwen3_4b_layer"] = run_mx_target(torch, cass, synth, timer, stream, dev16)
+    torch.cuda.empty_cache()
+    log("mx target done")
 
     # ---- KV cache at 32K / 64K context (8 KV heads x 128, 32 query heads)
     kvres = {}
@@ -530,6 +540,59 @@ def run_extras(args, torch, cass, synth, timer, stream, layers, encs, layer0, en
     torch.cuda.empty_cache()
     log("qwen kv done")
     return out
+
+
+def run_mx_target(torch, cass, synth, timer, stream, dev16):
+    """Cassandra-2 with a lossless target (format 2) against Cassandra-2 with
+    an MX-quantised target (format 3) on one Qwen3-4B-shaped layer (keep 0.3,
+    m = 3): stream sizes, verification GEMM (N = 5) and reconstruction time,
+    and how far the quantised target's products move from the exact ones."""
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(5_000_001)
+    L = torch_layer(torch, synth.QWEN3_4B, gen, outlier_frac=0.0)
+    res = {"layer": "Qwen3-4B-shaped q|k|v 6144x2560, o 2560x4096, gate|up 19456x2560, "
+                    "down 2560x9728; keep 0.3, m 3"}
+    n_values = sum(L[n].numel() for n in MATS)
+    X5 = {n: dev16(synth.activations(5, L[n].shape[1], 5, t0=20 + i)) for i, n in enumerate(MATS)}
+    Y = {}
+    for fmt, name in ((cass.CASS_FMT_C2_MX32, "lossless_target"),
+                      (cass.CASS_FMT_C2_MX_TARGET, "mx_target")):
+        enc = {n: cass.encode(L[n], synth.keep_count(0.3, L[n].shape[1]), 3, fmt=fmt) for n in MATS}
+        Y[name] = {n: torch.empty((5, enc[n].rows), dtype=torch.float32, device="cuda") for n in MATS}
+        outb = {n: torch.empty_like(L[n]) for n in MATS}
+        ver_ms = sum(timer.ms(lambda n=n: cass.cass_verify_gemm(enc[n].desc, X5[n], Y[name][n], stream), 3)
+                     for n in MATS)
+        rec_ms = sum(timer.ms(lambda n=n: cass.cass_reconstruct(enc[n].desc, outb[n], stream), 3)
+                     for n in MATS)
+        for n in MATS:
+            cass.cass_verify_gemm(enc[n].desc, X5[n], Y[name][n], stream)
+        sb = sum(enc[n].spec_bytes for n in MATS)
+        vb = sum(enc[n].verif_bytes for n in MATS)
+        res[name] = {"spec_bits_per_value": round(8 * sb / n_values, 4),
+                     "verif_bits_per_value": round(8 * vb / n_values, 4),
+                     "verify_n5_ms_per_layer": round(ver_ms, 4),
+                     "verify_GB_s": round((sb + vb) / (ver_ms * 1e-3) / 1e9, 1),
+                     "reconstruct_ms_per_layer": round(rec_ms, 4)}
+        if fmt == cass.CASS_FMT_C2_MX32:
+            torch.cuda.synchronize()
+            res[name]["reconstruct_exact"] = all(torch.equal(outb[n], L[n]) for n in MATS)
+        else:
+            # the quantised target's deviation from the original weights
+            torch.cuda.synchronize()
+            num = den = 0.0
+            for n in MATS:
+                wt = outb[n].view(torch.bfloat16).float()
+                wo = L[n].view(torch.bfloat16).float()
+                num += float((wt - wo).abs().sum())
+                den += float(wo.abs().sum())
+            res[name]["weight_rel_l1_change"] = round(num / den, 6)
+        del enc, outb
+    dev_max = 0.0
+    for n in MATS:
+        a, b = Y["mx_target"][n], Y["lossless_target"][n]
+        dev_max = max(dev_max, float(((a - b).abs() / b.abs().clamp_min(1e-30)).median()))
+    res["verify_output_median_rel_change"] = round(dev_max, 6)
+    return res
 
 
 def graph_ms(torch, g, reps):

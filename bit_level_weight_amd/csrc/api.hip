@@ -68,10 +68,13 @@ void stream_lengths(int format, int64_t R, int64_t C, int64_t B, int64_t k, int 
           (int64_t)((code_a + 7) / 8)};
     lv = {256, 8 * R, 4 * R * nb, (R * k * (7 - m) + 7) / 8, R * (C - k),
           (int64_t)((code_v + 7) / 8)};
-  } else {
+  } else if (format == CASS_FMT_C2_MX32) {
     ls = {n / 8, n / 32, 2 * R * nb, (R * k * (2 + m) + 7) / 8};
     lv = {256, 8 * R, 4 * R * nb, (int64_t)((code_a + 7) / 8), R * (C - k), 8 * R, 4 * R * nb,
           (int64_t)((code_v + 7) / 8)};
+  } else {
+    ls = {n / 8, n / 32, 2 * R * nb, (R * k * (2 + m) + 7) / 8};
+    lv = {n / 32, (R * k * (7 - m) + 7) / 8, (R * (C - k) * 9 + 7) / 8};
   }
 }
 
@@ -103,7 +106,8 @@ void write_header(uint8_t* h, uint32_t magic, int format, int m, int64_t R, int6
 
 int check_shape(int64_t R, int64_t C, const cass_params* p) {
   if (!p) return fail(CASS_ERR_INVALID, "params is NULL");
-  if (p->format != CASS_FMT_C1_UNARY && p->format != CASS_FMT_C2_MX32)
+  if (p->format != CASS_FMT_C1_UNARY && p->format != CASS_FMT_C2_MX32 &&
+      p->format != CASS_FMT_C2_MX_TARGET)
     return fail(CASS_ERR_INVALID, "unknown format %d", p->format);
   if (p->mant_bits < 0 || p->mant_bits > 7)
     return fail(CASS_ERR_INVALID, "mant_bits %d outside 0..7", p->mant_bits);
@@ -127,10 +131,10 @@ std::vector<int64_t> closed_lengths(bool spec, int format, int64_t R, int64_t C,
   if (format == CASS_FMT_C1_UNARY) {
     ls[S1_CODES] = -1;
     lv[V1_CODES] = -1;
-  } else {
+  } else if (format == CASS_FMT_C2_MX32) {
     lv[V2_RESID] = -1;
     lv[V2_CODES] = -1;
-  }
+  }  // format 3: every section has a closed form
   return spec ? ls : lv;
 }
 
@@ -223,6 +227,13 @@ VerifViewC2 verif_c2(const cass_tensor* W) {
                      (const uint32_t*)(b + o[V2_BLKOFF_K]), (const uint32_t*)(b + o[V2_RESID]),
                      b + o[V2_PRUNED], (const unsigned long long*)(b + o[V2_ROWBASE_P]),
                      (const uint32_t*)(b + o[V2_BLKOFF_P]), (const uint32_t*)(b + o[V2_CODES])};
+}
+
+VerifViewC3 verif_c3(const cass_tensor* W) {
+  const uint8_t* b = (const uint8_t*)W->verif;
+  const int64_t* o = W->verif_sec;
+  return VerifViewC3{b + o[V3_GEXP], (const uint32_t*)(b + o[V3_LOW]),
+                     (const uint32_t*)(b + o[V3_PRUNED])};
 }
 
 // frequency ranking: count descending, exponent ascending among equal counts
@@ -442,7 +453,8 @@ int cass_encode_tensor(const uint16_t* w, int64_t ld, const cass_plan* plan, voi
   if ((e = launch_fill_zero(spec, Ls.total, stream)) != hipSuccess) return hip_fail(e, "zero fill");
   if ((e = launch_fill_zero(verif, Lv.total, stream)) != hipSuccess) return hip_fail(e, "zero fill");
   const int64_t srank = p->format == CASS_FMT_C1_UNARY ? Ls.off[S1_RANK] : 0;
-  if ((e = launch_write_headers(hb, (uint8_t*)spec, srank, (uint8_t*)verif, Lv.off[V1_RANK],
+  const int64_t vrank = p->format == CASS_FMT_C2_MX_TARGET ? 0 : Lv.off[V1_RANK];
+  if ((e = launch_write_headers(hb, (uint8_t*)spec, srank, (uint8_t*)verif, vrank,
                                 stream)) != hipSuccess)
     return hip_fail(e, "headers");
   if ((e = launch_pack(w, sh, p->format, W, rt, (uint8_t*)spec, Ls.off, (uint8_t*)verif, Lv.off,
@@ -579,8 +591,10 @@ int cass_verify_gemm(const cass_tensor* W, const uint16_t* X, int ntok, int64_t 
     e = staged_exact_enabled() && exact_staged_fits(sh, sv, vv)
             ? launch_verify_gemm_c1_staged(sv, vv, sh, X, ntok, ldx, Y, ldy, stream)
             : launch_verify_gemm_c1(sv, vv, sh, X, ntok, ldx, Y, ldy, stream);
-  } else {
+  } else if (W->format == CASS_FMT_C2_MX32) {
     e = launch_verify_gemm_c2(spec_c2(W), verif_c2(W), sh, X, ntok, ldx, Y, ldy, stream);
+  } else {
+    e = launch_verify_gemm_c3(spec_c2(W), verif_c3(W), sh, X, ntok, ldx, Y, ldy, stream);
   }
   return e == hipSuccess ? CASS_OK : hip_fail(e, "verify gemm launch");
 }
@@ -599,9 +613,11 @@ int cass_reconstruct(const cass_tensor* W, uint16_t* out, hipStream_t stream) {
     e = staged_exact_enabled() && exact_staged_fits(sh, sv, vv)
             ? launch_reconstruct_c1_staged(sv, vv, sh, out, stream)
             : launch_decode_c1(sv, &vv, sh, out, stream);
-  } else {
+  } else if (W->format == CASS_FMT_C2_MX32) {
     const VerifViewC2 vv = verif_c2(W);
     e = launch_decode_c2(spec_c2(W), &vv, sh, out, stream);
+  } else {
+    e = launch_decode_c3(spec_c2(W), verif_c3(W), sh, out, stream);
   }
   return e == hipSuccess ? CASS_OK : hip_fail(e, "reconstruct launch");
 }

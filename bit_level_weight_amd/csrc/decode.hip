@@ -1,5 +1,5 @@
-// Whole-tensor decoders: exact reconstruction (both streams) and the
-// zero-filled draft (speculation stream only).
+// Whole-tensor decoders: exact reconstruction (both streams), the zero-filled
+// draft (speculation stream only), and the MX-quantised target of format 3.
 //
 // Method: Cassandra review (marsggbo.github.io), section 3.1 -- the draft
 // loads only speculation data and zero-fills it back to standard floating
@@ -32,7 +32,7 @@ __device__ __forceinline__ void decode_block_to(Dec& d, const uint32_t* __restri
   for (int64_t wi = 0; wi < B / 32; ++wi) {
     const uint32_t bw = bitmap[pos0 / 32 + wi];
     for (uint32_t km = bw; km; km &= km - 1u) slot[__builtin_ctz(km)] = (uint16_t)d.kept((int)wi);
-    for (uint32_t pm = ~bw; pm; pm &= pm - 1u) slot[__builtin_ctz(pm)] = (uint16_t)d.pruned();
+    for (uint32_t pm = ~bw; pm; pm &= pm - 1u) slot[__builtin_ctz(pm)] = (uint16_t)d.pruned((int)wi);
     const uint4* sl = reinterpret_cast<const uint4*>(slot);
     uint4* o = reinterpret_cast<uint4*>(out + pos0 + wi * 32);
     o[0] = sl[0];
@@ -96,6 +96,18 @@ __global__ void __launch_bounds__(256) k_draft_c2(SpecViewC2 sv, Shape sh,
   }
 }
 
+__global__ void __launch_bounds__(256) k_target_c3(SpecViewC2 sv, VerifViewC3 vv, Shape sh,
+                                                   uint16_t* __restrict__ out) {
+  __shared__ __align__(16) uint16_t slots[256 * 32];
+  const int64_t nb = sh.cols / sh.block, nblk = sh.rows * nb;
+  for (int64_t bi = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; bi < nblk;
+       bi += (int64_t)gridDim.x * blockDim.x) {
+    TargetC3 d;
+    d.init(sv, vv, sh, bi / nb, bi % nb, nullptr, nullptr);
+    decode_block_to(d, sv.bitmap, bi * sh.block, sh.block, slots + threadIdx.x * 32, out);
+  }
+}
+
 unsigned grid_blocks(int64_t nblk) {
   int64_t g = (nblk + 255) / 256;
   const int64_t cap = (int64_t)device_cu_count() * 8;
@@ -120,6 +132,14 @@ hipError_t launch_decode_c2(const SpecViewC2& sv, const VerifViewC2* vv, const S
   if (nblk == 0) return hipSuccess;
   if (vv) k_exact_c2<<<grid_blocks(nblk), 256, 0, s>>>(sv, *vv, sh, out);
   else k_draft_c2<<<grid_blocks(nblk), 256, 0, s>>>(sv, sh, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_c3(const SpecViewC2& sv, const VerifViewC3& vv, const Shape& sh,
+                            uint16_t* out, hipStream_t s) {
+  const int64_t nblk = sh.rows * (sh.cols / sh.block);
+  if (nblk == 0) return hipSuccess;
+  k_target_c3<<<grid_blocks(nblk), 256, 0, s>>>(sv, vv, sh, out);
   return hipGetLastError();
 }
 

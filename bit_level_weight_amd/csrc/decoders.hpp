@@ -51,8 +51,8 @@ struct ExactC1 {
     const uint32_t e = perm_s[r];
     return ((f >> m) << 15) | (e << 7) | ((f & ((1u << m) - 1)) << (7 - m)) | low;
   }
-  // the next pruned value of the block
-  __device__ __forceinline__ uint32_t pruned() {
+  // the next pruned value of the block (word: its bitmap word in the block)
+  __device__ __forceinline__ uint32_t pruned(int /*word*/) {
     const uint32_t byte = pr.take(8);
     const uint32_t e = perm_v[vr.unary()];
     return ((byte >> 7) << 15) | (e << 7) | (byte & 0x7F);
@@ -80,7 +80,7 @@ struct DraftC1 {
     const uint32_t e = perm_s[er.unary()];
     return ((f >> m) << 15) | (e << 7) | ((f & ((1u << m) - 1)) << (7 - m));
   }
-  __device__ __forceinline__ uint32_t pruned() { return 0u; }  // zero-filled
+  __device__ __forceinline__ uint32_t pruned(int /*word*/) { return 0u; }  // zero-filled
   static constexpr bool kHasPruned = false;
 };
 
@@ -119,7 +119,7 @@ struct DraftC2 {
     const uint32_t f = fr.take(2 + m);
     return mx_value_bits(f >> (m + 1), f & ((2u << m) - 1), E, m);
   }
-  __device__ __forceinline__ uint32_t pruned() { return 0u; }  // zero-filled
+  __device__ __forceinline__ uint32_t pruned(int /*word*/) { return 0u; }  // zero-filled
   static constexpr bool kHasPruned = false;
 };
 
@@ -162,10 +162,55 @@ struct ExactC2 {
     const uint32_t e = (M >= 128u) ? (uint32_t)(E - d) : 0u;
     return (s << 15) | ((e & 0xFF) << 7) | (M & 0x7F);
   }
-  __device__ __forceinline__ uint32_t pruned() {
+  __device__ __forceinline__ uint32_t pruned(int /*word*/) {
     const uint32_t byte = pr.take(8);
     const uint32_t e = perm_v[vr.unary()];
     return ((byte >> 7) << 15) | (e << 7) | (byte & 0x7F);
+  }
+  static constexpr bool kHasPruned = true;
+};
+
+// Format 3: Cassandra-2 speculation stream plus the fixed-width verification
+// sections -> the MX-quantised target (sign * t * 2^(X-134) per value, X the
+// group exponent of its 32 positions).
+struct TargetC3 {
+  BitReader fr, lr, pr;
+  const uint8_t* gexp;
+  int64_t g0;
+  int m, cur_word, X;
+  __device__ __forceinline__ void init(const SpecViewC2& sv, const VerifViewC3& vv,
+                                       const Shape& sh, int64_t row, int64_t b,
+                                       const uint8_t* /*ps*/, const uint8_t* /*pv*/) {
+    const int64_t nb = sh.cols / sh.block;
+    const int64_t bi = row * nb + b;
+    m = sh.mant;
+    const uint32_t kb = sv.keptb[bi];
+    const uint64_t kin0 = (uint64_t)row * sh.keep + kb;
+    fr.init(sv.fields, kin0 * (uint64_t)(2 + m));
+    lr.init(vv.low, kin0 * (uint64_t)(7 - m));
+    const uint64_t pidx = (uint64_t)row * (sh.cols - sh.keep) + (uint64_t)(b * sh.block) - kb;
+    pr.init(vv.pruned, pidx * 9u);
+    gexp = vv.gexp;
+    g0 = bi * sh.block / 32;
+    cur_word = -1;
+    X = 0;
+  }
+  __device__ __forceinline__ void group(int word) {
+    if (word != cur_word) {
+      X = gexp[g0 + word];
+      cur_word = word;
+    }
+  }
+  __device__ __forceinline__ uint32_t kept(int word) {
+    group(word);
+    const uint32_t f = fr.take(2 + m);
+    const uint32_t t = ((f & ((2u << m) - 1)) << (7 - m)) | lr.take(7 - m);
+    return mx_value_bits(f >> (m + 1), t, X, 7);
+  }
+  __device__ __forceinline__ uint32_t pruned(int word) {
+    group(word);
+    const uint32_t v = pr.take(9);
+    return mx_value_bits(v >> 8, v & 0xFF, X, 7);
   }
   static constexpr bool kHasPruned = true;
 };

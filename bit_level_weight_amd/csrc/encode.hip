@@ -190,7 +190,9 @@ __global__ void __launch_bounds__(256) k_block_bits(const uint16_t* __restrict__
         const int e = exp_of(x);
         if ((bw >> b) & 1) {
           ++kept;
-          if (format == CASS_FMT_C1_UNARY) {
+          if (format == CASS_FMT_C2_MX_TARGET) {
+            // fixed-width verification sections: no code bits
+          } else if (format == CASS_FMT_C1_UNARY) {
             a += rk[e] + 1u;
           } else {
             const int E = shexp[pos0 / 32 + wi];
@@ -198,7 +200,7 @@ __global__ void __launch_bounds__(256) k_block_bits(const uint16_t* __restrict__
             const int wd = (7 - m + d < 8) ? 7 - m + d : 8;
             a += (uint32_t)(d + 1 + wd);
           }
-        } else {
+        } else if (format != CASS_FMT_C2_MX_TARGET) {
           v += rp[e] + 1u;
         }
       }
@@ -299,6 +301,9 @@ struct PackPtrs {
   unsigned long long* v_rowbase_p;  // C-2
   uint32_t* v_blkoff_p;             // C-2
   uint32_t* v_codes;
+  uint8_t* v_gexp;                  // format 3: X per 32 positions
+  uint32_t* v_low;                  // format 3: kept low 7-m bits of t
+  uint32_t* v_pr9;                  // format 3: pruned (s<<8)|t
 };
 
 // One thread per (row, block): writes every section's share of that block.
@@ -315,12 +320,57 @@ __global__ void __launch_bounds__(256) k_pack(const uint16_t* __restrict__ w, Sh
   const int64_t nblk = sh.rows * nb;
   const int m = sh.mant;
   const bool c1 = format == CASS_FMT_C1_UNARY;
+  const bool c3 = format == CASS_FMT_C2_MX_TARGET;
   for (int64_t bi = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; bi < nblk;
        bi += (int64_t)gridDim.x * blockDim.x) {
     const int64_t row = bi / nb, b = bi % nb;
     const int64_t pos0 = bi * B;
     const uint32_t kb = ws.keptb[bi];
     const int64_t pb = b * B - kb;  // pruned before the block in the row
+    if (c3) {
+      // Cassandra-2 speculation sections; the target's fixed-width verification
+      // sections: X per 32 positions, low 7-m bits of each kept t, (s, t) of each
+      // pruned value
+      for (int64_t wi = 0; wi < B / 32; ++wi) {
+        P.s_bitmap[pos0 / 32 + wi] = ws.bitmap[pos0 / 32 + wi];
+        P.s_shexp[pos0 / 32 + wi] = ws.shexp[pos0 / 32 + wi];
+      }
+      P.s_keptb[bi] = (uint16_t)kb;
+      const uint64_t kin0 = (uint64_t)row * k + kb;
+      BitWriter fw, lw, pw;
+      fw.init(P.s_fields, kin0 * (uint64_t)(2 + m));
+      lw.init(P.v_low, kin0 * (uint64_t)(7 - m));
+      pw.init(P.v_pr9, (uint64_t)(row * (C - k) + pb) * 9u);
+      for (int64_t wi = 0; wi < B / 32; ++wi) {
+        const uint32_t bw = ws.bitmap[pos0 / 32 + wi];
+        const uint16_t* xw = w + row * sh.ld + b * B + wi * 32;
+        int X = 0;
+        for (int bb = 0; bb < 32; ++bb) {
+          const int e = exp_of(xw[bb]);
+          X = (e > 0 ? e : 1) > X ? (e > 0 ? e : 1) : X;
+        }
+        P.v_gexp[pos0 / 32 + wi] = (uint8_t)X;
+        for (int bb = 0; bb < 32; ++bb) {
+          const uint16_t x = xw[bb];
+          const int s = x >> 15, e = exp_of(x), f = x & 0x7F;
+          const int M = ((e > 0) << 7) | f;
+          const int d = X - (e > 0 ? e : 1);
+          const int t = d >= 8 ? 0 : (M >> d);
+          if ((bw >> bb) & 1) {
+            // a group that keeps anything has its maximum among the kept
+            // values, so t's top m+1 bits are the Cassandra-2 field
+            fw.put((uint32_t)((s << (m + 1)) | (t >> (7 - m))), 2 + m);
+            lw.put((uint32_t)(t & ((1 << (7 - m)) - 1)), 7 - m);
+          } else {
+            pw.put((uint32_t)((s << 8) | t), 9);
+          }
+        }
+      }
+      fw.finish();
+      lw.finish();
+      pw.finish();
+      continue;
+    }
     const unsigned long long base_a = ws.row_a[row], base_v = ws.row_v[row];
     // fixed sections
     for (int64_t wi = 0; wi < B / 32; ++wi) P.s_bitmap[pos0 / 32 + wi] = ws.bitmap[pos0 / 32 + wi];
@@ -422,7 +472,7 @@ hipError_t launch_histograms(const uint16_t* w, const Shape& sh, int format, con
   if (nwords == 0) return hipSuccess;
   k_histograms<<<grid_for(nwords, 256), 256, 0, s>>>(
       w, nwords, sh.cols / 32, sh.ld, ws.bitmap, ws.hist,
-      format == CASS_FMT_C2_MX32 ? ws.shexp : nullptr);
+      format != CASS_FMT_C1_UNARY ? ws.shexp : nullptr);
   return hipGetLastError();
 }
 
@@ -474,6 +524,14 @@ hipError_t launch_pack(const uint16_t* w, const Shape& sh, int format, const Wor
     P.v_lowmant = (uint32_t*)(verif + vs[V1_LOWMANT]);
     P.v_pruned = verif + vs[V1_PRUNED];
     P.v_codes = (uint32_t*)(verif + vs[V1_CODES]);
+  } else if (format == CASS_FMT_C2_MX_TARGET) {
+    P.s_bitmap = (uint32_t*)(spec + ss[S2_BITMAP]);
+    P.s_shexp = spec + ss[S2_SHEXP];
+    P.s_keptb = (uint16_t*)(spec + ss[S2_KEPTB]);
+    P.s_fields = (uint32_t*)(spec + ss[S2_FIELDS]);
+    P.v_gexp = verif + vs[V3_GEXP];
+    P.v_low = (uint32_t*)(verif + vs[V3_LOW]);
+    P.v_pr9 = (uint32_t*)(verif + vs[V3_PRUNED]);
   } else {
     P.s_bitmap = (uint32_t*)(spec + ss[S2_BITMAP]);
     P.s_shexp = spec + ss[S2_SHEXP];

@@ -19,6 +19,8 @@ enum VerifC1 { V1_RANK = 0, V1_ROWBASE, V1_BLKOFF, V1_LOWMANT, V1_PRUNED, V1_COD
 enum SpecC2 { S2_BITMAP = 0, S2_SHEXP, S2_KEPTB, S2_FIELDS, S2_COUNT };
 enum VerifC2 { V2_RANK = 0, V2_ROWBASE_K, V2_BLKOFF_K, V2_RESID, V2_PRUNED, V2_ROWBASE_P,
                V2_BLKOFF_P, V2_CODES, V2_COUNT };
+// Format 3 (MX-quantised target): the speculation stream is Cassandra-2's.
+enum VerifC3 { V3_GEXP = 0, V3_LOW, V3_PRUNED, V3_COUNT };
 
 // Tables passed to kernels by value.
 struct RankTables {
@@ -97,6 +99,12 @@ struct VerifViewC2 {
   const uint32_t* codes;
 };
 
+struct VerifViewC3 {
+  const uint8_t* gexp;    // X per 32 positions
+  const uint32_t* low;    // kept values' low 7-m bits of t
+  const uint32_t* pruned; // pruned values' (s<<8)|t, 9 bits
+};
+
 struct Shape {
   int64_t rows, cols, block, keep;
   int mant;
@@ -171,6 +179,11 @@ hipError_t launch_reconstruct_c1_staged(const SpecViewC1& sv, const VerifViewC1&
 hipError_t launch_draft_decode_c1_staged(const SpecViewC1& sv, const Shape& sh, uint16_t* out,
                                          hipStream_t s);
 hipError_t launch_verify_gemm_c2(const SpecViewC2& sv, const VerifViewC2& vv, const Shape& sh,
+                                 const uint16_t* X, int ntok, int64_t ldx, float* Y,
+                                 int64_t ldy, hipStream_t s);
+hipError_t launch_decode_c3(const SpecViewC2& sv, const VerifViewC3& vv, const Shape& sh,
+                            uint16_t* out, hipStream_t s);
+hipError_t launch_verify_gemm_c3(const SpecViewC2& sv, const VerifViewC3& vv, const Shape& sh,
                                  const uint16_t* X, int ntok, int64_t ldx, float* Y,
                                  int64_t ldy, hipStream_t s);
 

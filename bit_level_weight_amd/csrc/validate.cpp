@@ -32,13 +32,14 @@ bool parse(const uint8_t* b, int64_t n, uint32_t magic, Hdr* h) {
   h->k = rd64(b + 40);
   h->total = rd64(b + 48);
   h->nsec = rd32(b + 56);
-  if (h->format != 1 && h->format != 2) return false;
+  if (h->format != 1 && h->format != 2 && h->format != 3) return false;
   if (h->mant > 7 || h->R < 0 || h->C <= 0 || h->C > 65536 || h->B < 32 || (h->B & (h->B - 1)) ||
       h->C % h->B || h->k < 0 || h->k > h->C || h->total > n || h->total < 256 ||
       h->nsec > CASS_MAX_SECTIONS)
     return false;
   if (h->R > ((int64_t)1 << 40) / h->C) return false;
-  const uint32_t want = magic == kMagicSpec ? (h->format == 1 ? 7u : 4u) : (h->format == 1 ? 6u : 8u);
+  const uint32_t want = magic == kMagicSpec ? (h->format == 1 ? 7u : 4u)
+                                            : (h->format == 1 ? 6u : h->format == 2 ? 8u : 3u);
   if (h->nsec != want) return false;
   for (int s = 0; s < CASS_MAX_SECTIONS; ++s) {
     h->off[s] = rd64(b + 64 + 16 * s);
@@ -97,6 +98,33 @@ extern "C" int cass_tensor_validate(const void* spec_v, int64_t spec_bytes, cons
   if (c1 && (hs.len[0] != 256 || hs.len[2] != 8 * R || hs.len[3] != 4 * R * nb))
     return CASS_ERR_CORRUPT;
   if (!c1 && hs.len[1] != R * C / 32) return CASS_ERR_CORRUPT;
+  if (hs.format == 3) {
+    // MX-quantised target: fixed-size verification sections; each group
+    // exponent is at least 1 and equals the speculation stream's shared
+    // exponent wherever the group keeps a value
+    const uint8_t* bmb = spec + hs.off[0];
+    for (int64_t r = 0; r < R; ++r) {
+      uint16_t kbv;
+      int64_t kept = 0;
+      for (int64_t j = 0; j < C; ++j) {
+        if (j % B == 0) {
+          memcpy(&kbv, spec + hs.off[2] + 2 * (r * nb + j / B), 2);
+          if (kbv != (uint16_t)kept) return CASS_ERR_CORRUPT;
+        }
+        kept += (bmb[(r * C + j) >> 3] >> ((r * C + j) & 7)) & 1;
+      }
+      if (kept != k) return CASS_ERR_CORRUPT;
+    }
+    if (!verif) return CASS_OK;
+    if (hv.len[0] != R * C / 32 || hv.len[1] != (R * k * (7 - m) + 7) / 8 ||
+        hv.len[2] != (R * (C - k) * 9 + 7) / 8)
+      return CASS_ERR_CORRUPT;
+    const uint8_t* shexp = spec + hs.off[1];
+    const uint8_t* gexp = verif + hv.off[0];
+    for (int64_t g = 0; g < R * C / 32; ++g)
+      if (gexp[g] < 1 || (shexp[g] != 0 && shexp[g] != gexp[g])) return CASS_ERR_CORRUPT;
+    return CASS_OK;
+  }
   if (verif) {
     if (hv.len[0] != 256 || hv.len[1] != 8 * R || hv.len[2] != 4 * R * nb) return CASS_ERR_CORRUPT;
     if (c1 && (hv.len[3] != (R * k * (7 - m) + 7) / 8 || hv.len[4] != R * (C - k)))

@@ -1,5 +1,6 @@
 // Verification GEMM for the k+1 drafted tokens: Y[t][n] = sum_j W[n][j] X[t][j]
-// with W rebuilt exactly from both streams inside the kernel.
+// with W rebuilt exactly from both streams inside the kernel (format 3: the
+// MX-quantised target rebuilt from them).
 //
 // Method: Cassandra review (marsggbo.github.io), section 1 -- the target
 // model checks the drafted tokens in one parallel pass; section 3.1 -- it
@@ -21,6 +22,9 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ const uint8_t* spec_perm_of(const SpecViewC1& s) { return s.perm; }
 __device__ __forceinline__ const uint8_t* spec_perm_of(const SpecViewC2&) { return nullptr; }
+__device__ __forceinline__ const uint8_t* verif_perm_of(const VerifViewC1& v) { return v.perm; }
+__device__ __forceinline__ const uint8_t* verif_perm_of(const VerifViewC2& v) { return v.perm; }
+__device__ __forceinline__ const uint8_t* verif_perm_of(const VerifViewC3&) { return nullptr; }
 
 constexpr int kTileStride = 17;  // u32 per LDS tile row (16 used + 1 pad against bank conflicts)
 
@@ -40,9 +44,10 @@ __global__ void __launch_bounds__(64) k_verify(SV sv, VV vv, Shape sh,
   __shared__ uint8_t ps[256], pv[256];
   const int lane = threadIdx.x;
   const uint8_t* gps = spec_perm_of(sv);
+  const uint8_t* gpv = verif_perm_of(vv);
   for (int i = lane; i < 256; i += 64) {  // rank tables to shared memory
     ps[i] = gps ? gps[i] : 0;
-    pv[i] = vv.perm[i];
+    pv[i] = gpv ? gpv[i] : 0;
   }
   __syncthreads();
   const int64_t nb = sh.cols / sh.block;
@@ -67,7 +72,7 @@ __global__ void __launch_bounds__(64) k_verify(SV sv, VV vv, Shape sh,
         // per-position branch), straight into this lane's tile row
         uint16_t* trow = reinterpret_cast<uint16_t*>(tile + lane * kTileStride);
         for (uint32_t km = bw; km; km &= km - 1u) trow[__builtin_ctz(km)] = (uint16_t)d.kept((int)wi);
-        for (uint32_t pm = ~bw; pm; pm &= pm - 1u) trow[__builtin_ctz(pm)] = (uint16_t)d.pruned();
+        for (uint32_t pm = ~bw; pm; pm &= pm - 1u) trow[__builtin_ctz(pm)] = (uint16_t)d.pruned((int)wi);
       } else {
 #pragma unroll
         for (int j = 0; j < 16; ++j) tile[lane * kTileStride + j] = 0u;
@@ -142,6 +147,12 @@ hipError_t launch_verify_gemm_c2(const SpecViewC2& sv, const VerifViewC2& vv, co
                                  const uint16_t* X, int ntok, int64_t ldx, float* Y, int64_t ldy,
                                  hipStream_t s) {
   return launch_verify<ExactC2>(sv, vv, sh, X, ntok, ldx, Y, ldy, s);
+}
+
+hipError_t launch_verify_gemm_c3(const SpecViewC2& sv, const VerifViewC3& vv, const Shape& sh,
+                                 const uint16_t* X, int ntok, int64_t ldx, float* Y, int64_t ldy,
+                                 hipStream_t s) {
+  return launch_verify<TargetC3>(sv, vv, sh, X, ntok, ldx, Y, ldy, s);
 }
 
 }  // namespace cass

@@ -54,6 +54,19 @@
  *   min(8, 7-m+d) bits the draft dropped, d = shared - own exponent),
  *   4 pruned bytes, 5 pruned-code row bases, 6 pruned-code block offsets,
  *   7 pruned exponent codes.
+ *  Format 3, Cassandra-2 with an MX-quantised target (the reading of section
+ *   3.2 in which Cassandra-2's slight precision loss reaches the target too):
+ *   the target is not the original tensor but its MX-32 quantisation -- per
+ *   group of 32 positions of a row, X = the largest max(e,1) over all 32
+ *   values, and each value keeps its sign and t = its 8-bit significand
+ *   (hidden bit included) shifted right by X - max(e,1) (0 from a shift of 8),
+ *   i.e. it is truncated toward zero to a multiple of 2^(X-134) (zero -> +0).
+ *   The speculation stream is the Cassandra-2 one (its field a is the top m+1
+ *   bits of t).  Verification sections, all at fixed positions: 0 X (u8 per
+ *   32 positions), 1 low 7-m bits of each kept value's t (value i of row r at
+ *   bit (r*keep+i)*(7-m)), 2 pruned values' (s<<8)|t, 9 bits each (pruned
+ *   value i of row r at bit (r*(cols-keep)+i)*9).  cass_reconstruct returns
+ *   the quantised target and cass_verify_gemm multiplies with it.
  */
 #ifndef CASSANDRA_H
 #define CASSANDRA_H
@@ -79,7 +92,7 @@ enum cass_status {
   CASS_ERR_HIP = 6          /* a HIP runtime call or launch failed */
 };
 
-enum cass_format { CASS_FMT_C1_UNARY = 1, CASS_FMT_C2_MX32 = 2 };
+enum cass_format { CASS_FMT_C1_UNARY = 1, CASS_FMT_C2_MX32 = 2, CASS_FMT_C2_MX_TARGET = 3 };
 
 #define CASS_MAX_SECTIONS 12
 

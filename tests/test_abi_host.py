@@ -54,7 +54,7 @@ def test_ws_bytes_and_argument_errors(cass):
     n = ctypes.c_int64(0)
     assert L.cass_encode_ws_bytes(4096, 4096, ctypes.byref(p), ctypes.byref(n)) == 0
     assert n.value >= 4096 * 4096 // 8
-    for bad in [cass.CassParams(3, 3, 256, 10), cass.CassParams(1, 8, 256, 10),
+    for bad in [cass.CassParams(4, 3, 256, 10), cass.CassParams(1, 8, 256, 10),
                 cass.CassParams(1, 3, 100, 10), cass.CassParams(1, 3, 256, 5000),
                 cass.CassParams(1, 3, 16, 10)]:
         assert L.cass_encode_ws_bytes(16, 4096, ctypes.byref(bad), ctypes.byref(n)) == \
@@ -202,3 +202,27 @@ def test_set_option(cass):
     assert L.cass_set_option(None, 1) == cass.CASS_ERR_INVALID
     assert L.cass_stream_read(ctypes.c_void_p(0x100008), 64, ctypes.c_void_p(0x200000),
                               None) == cass.CASS_ERR_INVALID
+
+
+def test_format3_validate_and_describe(cass, orc):
+    """Format 3 (MX-quantised target): oracle streams validate and describe
+    with closed-form section lengths; a group exponent of 0, or one that
+    differs from the shared exponent of a group that keeps values, is corrupt."""
+    w = synth.weight(16, 1024, 8, outlier_frac=0.01)
+    spec, verif = orc.encode(w, 307, 3, fmt=3)
+    assert cass.cass_tensor_validate(spec, verif) == cass.CASS_OK
+    assert cass.cass_tensor_validate(spec) == cass.CASS_OK
+    t = cass.cass_tensor_describe(spec.tobytes(), FakeDev(spec.size), verif.tobytes(),
+                                  FakeDev(verif.size))
+    assert (t.format, t.rows, t.cols, t.keep) == (3, 16, 1024, 307)
+    hv = orc.header(verif, orc.MAGIC_VERIF)
+    off = hv["sections"][0][0]
+    for pos, val in ((off, 0), (off + 3, int(verif[off + 3]) ^ 1)):
+        bad = verif.copy()
+        bad[pos] = val
+        assert cass.cass_tensor_validate(spec, bad) == cass.CASS_ERR_CORRUPT
+    # a length off its closed form is refused by describe
+    b = bytearray(verif.tobytes())
+    b[72 + 16:80 + 16] = (int(hv["sections"][1][1]) + 1).to_bytes(8, "little")
+    with pytest.raises(cass.CassError):
+        cass.cass_tensor_describe(spec.tobytes(), FakeDev(spec.size), bytes(b), FakeDev(verif.size))
