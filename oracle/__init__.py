@@ -62,6 +62,11 @@ def lib():
         L.orc_product_rows.argtypes = [P, I64, P, I64, P, I64, P, I64, P, P]
         L.orc_header.argtypes = [P, I64, ctypes.c_uint32, P, P, P]
         L.orc_mx_target.argtypes = [P, I64, I64, P]
+        L.orc_huffman_lengths.argtypes = [P, ctypes.c_int, P]
+        L.orc_canonical_codes.argtypes = [P, P]
+        L.orc_unary_code.argtypes = [P, P, P]
+        L.orc_prefix_encode.argtypes = [P, I64, I64, P, P, P, I64, P, ctypes.POINTER(I64)]
+        L.orc_prefix_decode.argtypes = [P, I64, I64, P, P, P]
         _lib = L
     return _lib
 
@@ -128,6 +133,51 @@ def mx_target(w) -> np.ndarray:
     R, C = w.shape
     out = np.zeros((R, C), dtype=np.uint16)
     _check(lib().orc_mx_target(_p(w), R, C, _p(out)), "mx_target")
+    return out
+
+
+def huffman_code(hist, max_len: int = 32):
+    """(lengths u8[256], canonical codes u32[256]) of a length-limited Huffman code."""
+    h = np.ascontiguousarray(hist, dtype=np.uint64)
+    ln = np.zeros(256, dtype=np.uint8)
+    code = np.zeros(256, dtype=np.uint32)
+    _check(lib().orc_huffman_lengths(_p(h), max_len, _p(ln)), "huffman_lengths")
+    _check(lib().orc_canonical_codes(_p(ln), _p(code)), "canonical_codes")
+    return ln, code
+
+
+def unary_code(hist):
+    """(lengths, codes) of Cassandra-1's frequency-ranked unary code."""
+    h = np.ascontiguousarray(hist, dtype=np.uint64)
+    ln = np.zeros(256, dtype=np.uint8)
+    code = np.zeros(256, dtype=np.uint32)
+    _check(lib().orc_unary_code(_p(h), _p(ln), _p(code)), "unary_code")
+    return ln, code
+
+
+def prefix_encode(sym, block, ln, code):
+    """-> (stream bytes (zero padded to a multiple of 16, plus 16), block offsets, bits)."""
+    sym = np.ascontiguousarray(sym, dtype=np.uint8)
+    ln = np.ascontiguousarray(ln, dtype=np.uint8)
+    code = np.ascontiguousarray(code, dtype=np.uint32)
+    bits = ctypes.c_int64(0)
+    _check(lib().orc_prefix_encode(_p(sym), sym.size, block, _p(ln), _p(code), None, 0, None,
+                                   ctypes.byref(bits)), "prefix_encode sizes")
+    nbytes = (bits.value + 7) // 8
+    stream = np.zeros((nbytes + 15) // 16 * 16 + 16, dtype=np.uint8)
+    blkoff = np.zeros(max(1, (sym.size + block - 1) // block), dtype=np.uint32)
+    _check(lib().orc_prefix_encode(_p(sym), sym.size, block, _p(ln), _p(code), _p(stream),
+                                   stream.size, _p(blkoff), ctypes.byref(bits)), "prefix_encode")
+    return stream, blkoff, bits.value
+
+
+def prefix_decode(stream, n, ln, code):
+    stream = np.ascontiguousarray(stream, dtype=np.uint8)
+    out = np.zeros(n, dtype=np.uint8)
+    _check(lib().orc_prefix_decode(_p(stream), stream.size, n,
+                                   _p(np.ascontiguousarray(ln, dtype=np.uint8)),
+                                   _p(np.ascontiguousarray(code, dtype=np.uint32)), _p(out)),
+           "prefix_decode")
     return out
 
 

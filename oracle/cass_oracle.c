@@ -957,3 +957,168 @@ int orc_attention(const uint16_t* q, int64_t nq, const uint16_t* K, const uint16
   free(s);
   return ORC_OK;
 }
+
+/* ------------------------------------------- comparison exponent codes */
+
+/* [R32] also weighs Huffman codes against the unary code: Huffman codes are a
+ * little shorter but are parsed serially, by bit or through a table of 2^N
+ * entries (N = the longest code), while unary codes can be split anywhere by
+ * counting ones.  These functions build both as prefix codes so the two can be
+ * compared on the same exponent sequences. */
+
+/* Length-limited Huffman code lengths by package-merge (Larmore and
+ * Hirschberg's coin-collector formulation): at each of max_len levels the
+ * list holds the leaves and the pairs formed from the previous level's list,
+ * in weight order; a leaf's code length is the number of times it occurs in
+ * the first 2n-2 items of the last list.  Order among equal weights: leaves
+ * before packages, leaves by (count, symbol), packages in the order formed. */
+typedef struct {
+  uint64_t w;
+  int leaf;           /* leaf index, or -1 for a package */
+  uint16_t* mult;     /* occurrences of each leaf inside the item */
+} pm_item;
+
+int orc_huffman_lengths(const uint64_t hist[256], int max_len, uint8_t len[256]) {
+  if (max_len < 1 || max_len > 32) return ORC_ERR_INVALID;
+  memset(len, 0, 256);
+  int sym[256], n = 0;
+  for (int s = 0; s < 256; s++)
+    if (hist[s]) sym[n++] = s;
+  if (n == 0) return ORC_OK;
+  if (n == 1) { len[sym[0]] = 1; return ORC_OK; }
+  if (max_len < 32 && ((int64_t)1 << max_len) < n) return ORC_ERR_INVALID;
+  /* leaves by (count, symbol) ascending: insertion sort */
+  for (int i = 1; i < n; i++) {
+    int s = sym[i], j = i - 1;
+    while (j >= 0 && (hist[sym[j]] > hist[s] || (hist[sym[j]] == hist[s] && sym[j] > s))) {
+      sym[j + 1] = sym[j];
+      j--;
+    }
+    sym[j + 1] = s;
+  }
+  const int cap = 2 * n + 2;
+  pm_item* cur = (pm_item*)calloc((size_t)cap, sizeof(pm_item));
+  pm_item* nxt = (pm_item*)calloc((size_t)cap, sizeof(pm_item));
+  uint16_t* pool_a = (uint16_t*)calloc((size_t)cap * n, sizeof(uint16_t));
+  uint16_t* pool_b = (uint16_t*)calloc((size_t)cap * n, sizeof(uint16_t));
+  if (!cur || !nxt || !pool_a || !pool_b) {
+    free(cur); free(nxt); free(pool_a); free(pool_b);
+    return ORC_ERR_CAPACITY;
+  }
+  for (int i = 0; i < cap; i++) { cur[i].mult = pool_a + (size_t)i * n; nxt[i].mult = pool_b + (size_t)i * n; }
+  /* deepest level: the leaves alone */
+  int ncur = n;
+  for (int i = 0; i < n; i++) {
+    cur[i].w = hist[sym[i]];
+    cur[i].leaf = i;
+    memset(cur[i].mult, 0, (size_t)n * sizeof(uint16_t));
+    cur[i].mult[i] = 1;
+  }
+  for (int level = max_len - 1; level >= 1; level--) {
+    /* packages: adjacent pairs of the current list */
+    int npk = ncur / 2, li = 0, pi = 0, nn = 0;
+    while (li < n || pi < npk) {
+      int take_leaf;
+      if (li >= n) take_leaf = 0;
+      else if (pi >= npk) take_leaf = 1;
+      else take_leaf = hist[sym[li]] <= cur[2 * pi].w + cur[2 * pi + 1].w;
+      pm_item* it = &nxt[nn++];
+      if (take_leaf) {
+        it->w = hist[sym[li]];
+        it->leaf = li;
+        memset(it->mult, 0, (size_t)n * sizeof(uint16_t));
+        it->mult[li] = 1;
+        li++;
+      } else {
+        const pm_item* a = &cur[2 * pi];
+        const pm_item* b = &cur[2 * pi + 1];
+        it->w = a->w + b->w;
+        it->leaf = -1;
+        for (int i = 0; i < n; i++) it->mult[i] = (uint16_t)(a->mult[i] + b->mult[i]);
+        pi++;
+      }
+    }
+    pm_item* t = cur; cur = nxt; nxt = t;
+    uint16_t* tp = pool_a; pool_a = pool_b; pool_b = tp;
+    ncur = nn;
+  }
+  /* code lengths: occurrences in the first 2n-2 items */
+  for (int i = 0; i < 2 * n - 2 && i < ncur; i++)
+    for (int j = 0; j < n; j++) len[sym[j]] = (uint8_t)(len[sym[j]] + cur[i].mult[j]);
+  free(cur); free(nxt); free(pool_a); free(pool_b);
+  return ORC_OK;
+}
+
+/* Canonical code values from lengths: symbols ordered by (length, symbol),
+ * each code the previous one plus one, shifted left when the length grows. */
+int orc_canonical_codes(const uint8_t len[256], uint32_t code[256]) {
+  memset(code, 0, 256 * sizeof(uint32_t));
+  uint32_t c = 0;
+  int prev = 0, first = 1;
+  for (int l = 1; l <= 32; l++)
+    for (int s = 0; s < 256; s++) {
+      if (len[s] != l) continue;
+      if (first) { c = 0; first = 0; }
+      else c = (c + 1) << (l - prev);
+      prev = l;
+      code[s] = c;
+    }
+  return ORC_OK;
+}
+
+/* Cassandra-1's frequency-ranked unary code as a prefix code: rank r is r
+ * zeros then a one (in stream order), i.e. length r+1 and value 1. */
+int orc_unary_code(const uint64_t hist[256], uint8_t len[256], uint32_t code[256]) {
+  uint8_t perm[256];
+  orc_rank_table(hist, perm);
+  for (int r = 0; r < 256; r++) {
+    len[perm[r]] = (uint8_t)(r + 1 > 255 ? 255 : r + 1);
+    code[perm[r]] = 1;
+  }
+  return ORC_OK;
+}
+
+/* Concatenate the codes of sym[0..n) (most significant code bit first, in
+ * stream bit order); blkoff[b] = bit offset of symbol b*block.  The stream
+ * must be zeroed.  *bits receives the total length. */
+int orc_prefix_encode(const uint8_t* sym, int64_t n, int64_t block, const uint8_t len[256],
+                      const uint32_t code[256], uint8_t* stream, int64_t cap_bytes,
+                      uint32_t* blkoff, int64_t* bits) {
+  if (n < 0 || block < 1) return ORC_ERR_INVALID;
+  uint64_t pos = 0;
+  for (int64_t i = 0; i < n; i++) {
+    int l = len[sym[i]];
+    if (l == 0 || l > 32) return ORC_ERR_INVALID;
+    if (i % block == 0 && blkoff) blkoff[i / block] = (uint32_t)pos;
+    for (int j = l - 1; j >= 0; j--) {
+      if (stream) {
+        if ((int64_t)(pos >> 3) >= cap_bytes) return ORC_ERR_CAPACITY;
+        if ((code[sym[i]] >> j) & 1) stream[pos >> 3] |= (uint8_t)(1u << (pos & 7));
+      }
+      pos++;
+    }
+  }
+  if (bits) *bits = (int64_t)pos;
+  return ORC_OK;
+}
+
+/* Decode n symbols bit by bit: extend the code one bit at a time and stop at
+ * the first (length, value) pair some symbol owns. */
+int orc_prefix_decode(const uint8_t* stream, int64_t bytes, int64_t n, const uint8_t len[256],
+                      const uint32_t code[256], uint8_t* out) {
+  uint64_t pos = 0;
+  for (int64_t i = 0; i < n; i++) {
+    uint32_t c = 0;
+    int found = -1;
+    for (int l = 1; l <= 32 && found < 0; l++) {
+      if ((int64_t)(pos >> 3) >= bytes) return ORC_ERR_CORRUPT;
+      c = (c << 1) | ((stream[pos >> 3] >> (pos & 7)) & 1u);
+      pos++;
+      for (int s = 0; s < 256; s++)
+        if (len[s] == l && code[s] == c) { found = s; break; }
+    }
+    if (found < 0) return ORC_ERR_CORRUPT;
+    out[i] = (uint8_t)found;
+  }
+  return ORC_OK;
+}

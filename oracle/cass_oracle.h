@@ -86,6 +86,22 @@ int orc_product_rows(const uint8_t* spec, int64_t spec_len, const uint8_t* verif
                      int64_t verif_len, const uint16_t* x, int64_t ntok, const int64_t* rows,
                      int64_t nrows, double* y, double* absy);
 
+/* --- comparison exponent codes (Cassandra review, section 3.2: Huffman
+ * codes are a little shorter than the unary code but parse serially) --- */
+/* Length-limited Huffman code lengths (package-merge); len = 0 for absent
+ * symbols, 1 for a lone symbol. */
+int orc_huffman_lengths(const uint64_t hist[256], int max_len, uint8_t len[256]);
+/* Canonical code values for the lengths (order by length, then symbol). */
+int orc_canonical_codes(const uint8_t len[256], uint32_t code[256]);
+/* Cassandra-1's frequency-ranked unary code as (length, value) pairs. */
+int orc_unary_code(const uint64_t hist[256], uint8_t len[256], uint32_t code[256]);
+/* Concatenated codes, most significant bit first; block offsets in bits. */
+int orc_prefix_encode(const uint8_t* sym, int64_t n, int64_t block, const uint8_t len[256],
+                      const uint32_t code[256], uint8_t* stream, int64_t cap_bytes,
+                      uint32_t* blkoff, int64_t* bits);
+int orc_prefix_decode(const uint8_t* stream, int64_t bytes, int64_t n, const uint8_t len[256],
+                      const uint32_t code[256], uint8_t* out);
+
 /* Read header fields: out[0..7] = format, mant_bits, rows, cols, block, keep,
  * total_bytes, n_sections; sec_off/sec_len receive the 12 section entries. */
 int orc_header(const uint8_t* buf, int64_t len, uint32_t expect_magic, int64_t out[8],
