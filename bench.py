@@ -22,7 +22,8 @@ runs the verification GEMM (N = 5) and the reconstruction of each matrix; --mode
 runs a plain 1 GiB device copy (to calibrate the HBM byte counters); --mode spec
 runs only the speculative step over the 32-layer stack (and, without
 --no-extras, the dense bf16 context); --mode mxt compares Cassandra-2 with
-a lossless and with an MX-quantised target on one Qwen3-4B-shaped layer.
+a lossless and with an MX-quantised target on one Qwen3-4B-shaped layer;
+--mode codecs compares the exponent codes (Huffman, unary) and their decoders.
 """
 from __future__ import annotations
 
@@ -50,7 +51,7 @@ def parse():
     ap.add_argument("--mant", type=int, default=3)
     ap.add_argument("--block", type=int, default=256)
     ap.add_argument("--copies", type=int, default=8)
-    ap.add_argument("--mode", choices=("full", "gemv", "exact", "copy", "spec", "mxt"),
+    ap.add_argument("--mode", choices=("full", "gemv", "exact", "copy", "spec", "mxt", "codecs"),
                     default="full")
     ap.add_argument("--no-extras", action="store_true", help="headline and CPU baseline only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -121,6 +122,14 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"mode": "copy", "bytes": 1 << 30}))
+        return
+
+    if args.mode == "codecs":
+        gen = torch.Generator(device="cuda")
+        gen.manual_seed(2_000_001)
+        L = torch_layer(torch, synth.LLAMA3_8B, gen)
+        print(json.dumps({"mode": "codecs", "exponent_codecs_llama8b_layer":
+                          run_prefix_codecs(torch, cass, timer, stream, L)}))
         return
 
     if args.mode == "mxt":
@@ -391,6 +400,8 @@ def run_extras(args, torch, cass, synth, timer, stream, layers, encs, layer0, en
     rows["encode"] = {"ms_per_layer": round(1e3 * (time.time() - t0), 2),
                       "note": "two host synchronisations per tensor (histograms, sizes)"}
     out["rows"] = rows
+    out["exponent_codecs_llama8b_layer"] = run_prefix_codecs(torch, cass, timer, stream, layers[0])
+    log("codecs done")
 
     # ---- keep x mantissa sweep (layer 0)
     sweep = {}
@@ -592,6 +603,64 @@ def run_mx_target(torch, cass, synth, timer, stream, dev16):
         a, b = Y["mx_target"][n], Y["lossless_target"][n]
         dev_max = max(dev_max, float(((a - b).abs() / b.abs().clamp_min(1e-30)).median()))
     res["verify_output_median_rel_change"] = round(dev_max, 6)
+    return res
+
+
+def run_prefix_codecs(torch, cass, timer, stream, layer, keep=0.3):
+    """The exponent codes compared on one Llama-3-8B-shaped layer's kept
+    exponents (top 30 % by magnitude per row) and pruned exponents (the rest),
+    each sequence coded both ways: bits per exponent of a 12-bit-limited
+    canonical Huffman code and of the frequency-ranked unary code against the
+    entropy, and how fast each decoder turns the stream back into exponents."""
+    kept, pruned = [], []
+    for n in MATS:
+        w = layer[n]
+        a = (w & 0x7FFF).to(torch.int32)  # magnitude order of bf16 patterns
+        k = max(1, int(round(keep * w.shape[1])))
+        thr = torch.topk(a, k, dim=1).values[:, -1:]
+        e = ((w.to(torch.int32) >> 7) & 0xFF).to(torch.uint8)
+        kept.append(e[a >= thr])
+        pruned.append(e[a < thr])
+    out = {"kept": codec_compare(torch, cass, timer, stream, torch.cat(kept))}
+    del kept
+    out["pruned"] = codec_compare(torch, cass, timer, stream, torch.cat(pruned))
+    return out
+
+
+def codec_compare(torch, cass, timer, stream, sym):
+    sym = sym[: sym.numel() // 16 * 16].contiguous()
+    n = sym.numel()
+    hist = torch.bincount(sym.to(torch.int64), minlength=256).cpu().numpy().astype(np.uint64)
+    p = hist[hist > 0].astype(np.float64) / n
+    res = {"symbols": n, "entropy_bits": round(float(-(p * np.log2(p)).sum()), 4),
+           "distinct": int((hist > 0).sum())}
+    block = 256
+    codes = [("huffman12", cass.cass_prefix_code_huffman(hist, 12))]
+    if res["distinct"] <= 32:  # unary codes of ranks past 31 exceed 32 bits
+        codes.append(("unary", cass.cass_prefix_code_unary(hist)))
+    blkoff = torch.empty(((n + block - 1) // block,), dtype=torch.int32, device="cuda")
+    for name, code in codes:
+        bits = cass.cass_prefix_stream_bits(code, hist)
+        sb = ((bits + 7) // 8 + 15) // 16 * 16 + 16
+        st = torch.empty((sb,), dtype=torch.uint8, device="cuda")
+        enc_ms = timer.ms(lambda: cass.cass_prefix_encode(code, sym, block, st, blkoff, stream), 3)
+        ws = torch.empty((cass.cass_prefix_decode_ws_bytes(sb),), dtype=torch.uint8, device="cuda")
+        out = torch.empty_like(sym)
+        row = {"bits_per_exponent": round(bits / n, 4), "max_len": code.max_len,
+               "encode_ms": round(enc_ms, 3)}
+        methods = [("table", cass.CASS_PREFIX_TABLE)] if code.max_len <= 12 else []
+        if name == "unary":
+            methods += [("serial", cass.CASS_PREFIX_UNARY_SERIAL),
+                        ("parallel", cass.CASS_PREFIX_UNARY_PARALLEL)]
+        for mname, m in methods:
+            ms = timer.ms(lambda: cass.cass_prefix_decode(code, st, blkoff, n, block, m, out, ws,
+                                                          stream), 5)
+            torch.cuda.synchronize()
+            row[f"decode_{mname}"] = {"ms": round(ms, 3), "Gexp_s": round(n / (ms * 1e-3) / 1e9, 2),
+                                      "stream_GB_s": round(sb / (ms * 1e-3) / 1e9, 1),
+                                      "exact": bool(torch.equal(out, sym))}
+        res[name] = row
+        del st, ws, out
     return res
 
 

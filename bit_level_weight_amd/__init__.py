@@ -32,8 +32,11 @@ EXPORTED = (
     "cass_kv_bytes", "cass_kv_init", "cass_kv_append_ws_bytes", "cass_kv_append_encode",
     "cass_kv_status", "cass_kv_decode", "cass_kv_attn_ws_bytes", "cass_kv_draft_attn",
     "cass_kv_verify_attn", "cass_set_option", "cass_stream_read", "cass_kv_draft_attn_static",
-    "cass_kv_truncate",
+    "cass_kv_truncate", "cass_prefix_code_huffman", "cass_prefix_code_unary",
+    "cass_prefix_stream_bits", "cass_prefix_encode", "cass_prefix_decode_ws_bytes",
+    "cass_prefix_decode",
 )
+CASS_PREFIX_TABLE, CASS_PREFIX_UNARY_SERIAL, CASS_PREFIX_UNARY_PARALLEL = 1, 2, 3
 CASS_STREAM_READ_BLOCKS = 2048
 CASS_KV_STATE_BYTES = 4096
 CASS_KV_STATIC_SCRATCH_BYTES = 32 << 20
@@ -82,6 +85,11 @@ class CassKv(ctypes.Structure):
                 ("state", ctypes.c_void_p), ("spec_stream_bytes", ctypes.c_int64),
                 ("verif_stream_bytes", ctypes.c_int64), ("spec_part", ctypes.c_int64 * 5),
                 ("verif_part", ctypes.c_int64 * 5), ("tokens", ctypes.c_int64)]
+
+
+class CassPrefixCode(ctypes.Structure):
+    _fields_ = [("max_len", ctypes.c_int32), ("len", ctypes.c_uint8 * 256),
+                ("code", ctypes.c_uint32 * 256)]
 
 
 class CassError(RuntimeError):
@@ -134,6 +142,13 @@ def lib():
         L.cass_kv_verify_attn.argtypes = [KV, P, I32, I32, ctypes.c_float, P, P, I64, P]
         L.cass_kv_draft_attn_static.argtypes = [KV, P, I32, ctypes.c_float, P, P]
         L.cass_kv_truncate.argtypes = [KV, I64, P]
+        PC = ctypes.POINTER(CassPrefixCode)
+        L.cass_prefix_code_huffman.argtypes = [P, I32, PC]
+        L.cass_prefix_code_unary.argtypes = [P, PC]
+        L.cass_prefix_stream_bits.argtypes = [PC, P, ctypes.POINTER(I64)]
+        L.cass_prefix_encode.argtypes = [PC, P, I64, I64, P, I64, P, P]
+        L.cass_prefix_decode_ws_bytes.argtypes = [I64, ctypes.POINTER(I64)]
+        L.cass_prefix_decode.argtypes = [PC, P, I64, P, I64, I64, I32, P, P, I64, P]
         _lib = L
     return _lib
 
@@ -288,6 +303,57 @@ def encode(w, keep: int, mant_bits: int, block: int = 256, fmt: int = CASS_FMT_C
     enc = Encoded(desc, spec, verif, plan)
     enc._ws = ws  # the workspace must outlive the packing pass
     return enc
+
+
+# ------------------------------------------------- comparison exponent codecs
+
+
+def _hist_arg(hist):
+    h = np.ascontiguousarray(hist, dtype=np.uint64)
+    assert h.size == 256
+    return h, h.ctypes.data_as(ctypes.c_void_p)
+
+
+def cass_prefix_code_huffman(hist, max_len: int) -> CassPrefixCode:
+    c = CassPrefixCode()
+    h, hp = _hist_arg(hist)
+    _check(lib().cass_prefix_code_huffman(hp, max_len, ctypes.byref(c)))
+    return c
+
+
+def cass_prefix_code_unary(hist) -> CassPrefixCode:
+    c = CassPrefixCode()
+    h, hp = _hist_arg(hist)
+    _check(lib().cass_prefix_code_unary(hp, ctypes.byref(c)))
+    return c
+
+
+def cass_prefix_stream_bits(code: CassPrefixCode, hist) -> int:
+    n = ctypes.c_int64(0)
+    h, hp = _hist_arg(hist)
+    _check(lib().cass_prefix_stream_bits(ctypes.byref(code), hp, ctypes.byref(n)))
+    return n.value
+
+
+def cass_prefix_encode(code: CassPrefixCode, sym, block, stream, blkoff, stream_h=None):
+    _check(lib().cass_prefix_encode(ctypes.byref(code), _ptr(sym), sym.numel(), block, _ptr(stream),
+                                    stream.numel() * stream.element_size(), _ptr(blkoff),
+                                    _stream(stream_h)))
+
+
+def cass_prefix_decode_ws_bytes(stream_bytes: int) -> int:
+    n = ctypes.c_int64(0)
+    _check(lib().cass_prefix_decode_ws_bytes(stream_bytes, ctypes.byref(n)))
+    return n.value
+
+
+def cass_prefix_decode(code: CassPrefixCode, stream, blkoff, n, block, method, out, ws=None,
+                       stream_h=None):
+    _check(lib().cass_prefix_decode(ctypes.byref(code), _ptr(stream),
+                                    stream.numel() * stream.element_size(), _ptr(blkoff), n, block,
+                                    method, _ptr(out), _ptr(ws),
+                                    0 if ws is None else ws.numel() * ws.element_size(),
+                                    _stream(stream_h)))
 
 
 # ------------------------------------------------------------------ KV cache

@@ -340,6 +340,57 @@ int cass_kv_verify_attn(const cass_kv* kv, const uint16_t* q, int nq, int n_q_he
 int cass_kv_draft_attn_static(const cass_kv* kv, const uint16_t* q, int n_q_heads, float scale,
                               float* out, hipStream_t stream);
 
+/* ------------------------------------------- comparison exponent codecs
+ * Cassandra review, section 3.2: the unary exponent code is preferred to a
+ * Huffman code although Huffman codes are a little shorter, because a Huffman
+ * stream parses serially (bit by bit, or through a table of 2^N entries for
+ * N-bit codes) while unary codes decode in parallel.  These calls build both
+ * codes for a sequence of exponent symbols (u8) and decode them three ways,
+ * so the trade can be measured.  A code is a prefix code given by (length,
+ * value) per symbol; a code's value is written most significant bit first, in
+ * stream bit order (bit i of a stream is bit i & 31 of 32-bit word i >> 5).
+ * A stream is the concatenation of the symbols' codes; blkoff[b] is the bit
+ * offset of symbol b * block. */
+typedef struct cass_prefix_code {
+  int32_t max_len;     /* the longest length in len[] */
+  uint8_t len[256];    /* code length of each symbol, 0..32 (0: no code) */
+  uint32_t code[256];  /* code value (its low len bits) */
+} cass_prefix_code;
+enum { CASS_PREFIX_TABLE = 1, CASS_PREFIX_UNARY_SERIAL = 2, CASS_PREFIX_UNARY_PARALLEL = 3 };
+/* Length-limited Huffman code for a symbol histogram (package-merge; among
+ * equal weights leaves precede pairs, leaves ordered by (count, symbol)), with
+ * canonical values (symbols ordered by (length, symbol), consecutive values,
+ * shifted left as the length grows).  Absent symbols get no code; a lone
+ * symbol gets a 1-bit code.  max_len in 1..32.  Host only. */
+int cass_prefix_code_huffman(const uint64_t* hist, int max_len, cass_prefix_code* out);
+/* Cassandra-1's frequency-ranked unary code (rank r: r zero bits then a one,
+ * i.e. length r+1, value 1; ranks by count, ties to the smaller symbol);
+ * ranks past 31 get no code.  Host only. */
+int cass_prefix_code_unary(const uint64_t* hist, cass_prefix_code* out);
+/* Total code bits of a histogram under a code (CASS_ERR_INVALID if a
+ * present symbol has no code).  Host only. */
+int cass_prefix_stream_bits(const cass_prefix_code* c, const uint64_t* hist, int64_t* bits);
+/* Encode sym[0..n) (device) into stream (device, 16-byte aligned, a multiple
+ * of 16 bytes, at least the code bits plus 16 zero bytes, below 2^29 bytes)
+ * and blkoff (device, u32 per block; block a multiple of 16).  Every symbol
+ * must have a code; blocks whose codes would not fit the buffer are left
+ * unwritten.  Four launches, no host synchronisation. */
+int cass_prefix_encode(const cass_prefix_code* c, const uint8_t* sym, int64_t n, int64_t block,
+                       void* stream, int64_t stream_bytes, uint32_t* blkoff, hipStream_t stream_h);
+/* Workspace of the parallel unary decoder for a stream of stream_bytes. */
+int cass_prefix_decode_ws_bytes(int64_t stream_bytes, int64_t* ws_bytes);
+/* Decode n symbols (n a multiple of 16) into out (device, 16-byte aligned):
+ * CASS_PREFIX_TABLE -- one thread per block with a 2^max_len table in shared
+ * memory (max_len <= 12, any prefix code); CASS_PREFIX_UNARY_SERIAL -- one
+ * thread per block counting trailing zeros (unary codes); CASS_PREFIX_UNARY_
+ * PARALLEL -- no block offsets (blkoff may be NULL): each word of the stream
+ * on its own, code index from a prefix count of one bits (unary codes; ws
+ * from cass_prefix_decode_ws_bytes).  Reads stay inside stream_bytes whatever
+ * the stream holds. */
+int cass_prefix_decode(const cass_prefix_code* c, const void* stream, int64_t stream_bytes,
+                       const uint32_t* blkoff, int64_t n, int64_t block, int method, uint8_t* out,
+                       void* ws, int64_t ws_bytes, hipStream_t stream_h);
+
 /* Status code -> fixed English text, and the detail of the last error on
  * the calling thread ("" if none); plumbing, not part of the method. */
 const char* cass_status_string(int status);

@@ -226,3 +226,69 @@ def test_format3_validate_and_describe(cass, orc):
     b[72 + 16:80 + 16] = (int(hv["sections"][1][1]) + 1).to_bytes(8, "little")
     with pytest.raises(cass.CassError):
         cass.cass_tensor_describe(spec.tobytes(), FakeDev(spec.size), bytes(b), FakeDev(verif.size))
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_prefix_code_tables_match_oracle(cass, orc, seed):
+    """The library's host-built Huffman (package-merge, canonical values) and
+    unary code tables equal the oracle's, on histograms of kept exponents and
+    on random ones."""
+    rng = np.random.default_rng(seed)
+    if seed < 3:
+        w = synth.weight(64, 1024, 40 + seed, outlier_frac=0.01)
+        keep = orc.select(w, 307)
+        hist = np.bincount(((w[keep] >> 7) & 0xFF).astype(np.int64), minlength=256).astype(np.uint64)
+    else:
+        hist = np.zeros(256, dtype=np.uint64)
+        syms = rng.choice(256, size=int(rng.integers(2, 120)), replace=False)
+        hist[syms] = (2.0 ** rng.uniform(0, 20, size=syms.size)).astype(np.uint64) + 1
+    for L in (12, 16, 32):
+        if (1 << L) < np.count_nonzero(hist):
+            continue
+        c = cass.cass_prefix_code_huffman(hist, L)
+        ln, code = orc.huffman_code(hist, L)
+        assert list(c.len) == list(ln) and list(c.code) == list(code), L
+        assert c.max_len == int(ln.max())
+        assert cass.cass_prefix_stream_bits(c, hist) == int((hist * ln).sum())
+    u = cass.cass_prefix_code_unary(hist)
+    ln, code = orc.unary_code(hist)
+    short = ln <= 32
+    assert np.array_equal(np.array(u.len)[short], ln[short])
+    assert np.all(np.array(u.code)[short] == 1)
+
+
+def test_prefix_argument_errors(cass):
+    L = cass.lib()
+    hist = np.zeros(256, dtype=np.uint64)
+    hist[[3, 5, 9]] = [10, 3, 1]
+    huff = cass.cass_prefix_code_huffman(hist, 12)
+    P = ctypes.c_void_p
+    # a Huffman code is not a unary code
+    assert L.cass_prefix_decode(ctypes.byref(huff), P(0x100000), 4096, P(0x200000), 64, 64,
+                                cass.CASS_PREFIX_UNARY_SERIAL, P(0x300000), None, 0,
+                                None) == cass.CASS_ERR_INVALID
+    # unknown method, misaligned output, n not a multiple of 16
+    assert L.cass_prefix_decode(ctypes.byref(huff), P(0x100000), 4096, P(0x200000), 64, 64, 9,
+                                P(0x300000), None, 0, None) == cass.CASS_ERR_INVALID
+    assert L.cass_prefix_decode(ctypes.byref(huff), P(0x100000), 4096, P(0x200000), 64, 64,
+                                cass.CASS_PREFIX_TABLE, P(0x300001), None, 0,
+                                None) == cass.CASS_ERR_INVALID
+    assert L.cass_prefix_decode(ctypes.byref(huff), P(0x100000), 4096, P(0x200000), 60, 64,
+                                cass.CASS_PREFIX_TABLE, P(0x300000), None, 0,
+                                None) == cass.CASS_ERR_INVALID
+    # table decoding needs codes of at most 12 bits
+    long = cass.cass_prefix_code_unary(hist)
+    long.len[7], long.code[7], long.max_len = 20, 1, 20
+    assert L.cass_prefix_decode(ctypes.byref(long), P(0x100000), 4096, P(0x200000), 64, 64,
+                                cass.CASS_PREFIX_TABLE, P(0x300000), None, 0,
+                                None) != cass.CASS_OK
+    # Kraft's inequality
+    bad = cass.cass_prefix_code_huffman(hist, 12)
+    bad.len[100], bad.code[100] = 1, 0
+    assert L.cass_prefix_encode(ctypes.byref(bad), P(0x100000), 64, 64, P(0x200000), 4096,
+                                P(0x300000), None) == cass.CASS_ERR_INVALID
+    # a present symbol without a code
+    hist2 = hist.copy()
+    hist2[200] = 1
+    with pytest.raises(cass.CassError):
+        cass.cass_prefix_stream_bits(huff, hist2)
