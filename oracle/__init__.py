@@ -19,7 +19,8 @@ _SRC = os.path.join(_HERE, "cass_oracle.c")
 _LIB = os.path.join(_HERE, "libcass_oracle.so")
 
 OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_OVERFLOW, ERR_CORRUPT, ERR_CAPACITY = range(6)
-FMT_C1, FMT_C2, FMT_C2T = 1, 2, 3
+FMT_C1, FMT_C2, FMT_C2T, FMT_C1S = 1, 2, 3, 4
+SUPERBLOCK_BLOCKS = 16
 MAGIC_SPEC, MAGIC_VERIF = 0x50535343, 0x46565343
 
 

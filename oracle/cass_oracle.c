@@ -163,6 +163,7 @@ typedef struct {
   uint32_t magic, version, format, mant;
   int64_t R, C, B, k, total;
   uint32_t nsec;
+  uint32_t sblocks; /* format 4: blocks per superblock (the header's u32 at byte 60) */
   int64_t off[MAX_SEC], len[MAX_SEC];
 } hdr_t;
 
@@ -178,6 +179,7 @@ static void write_header(uint8_t* buf, const hdr_t* h) {
   put_u64(buf + 40, (uint64_t)h->k);
   put_u64(buf + 48, (uint64_t)h->total);
   put_u32(buf + 56, h->nsec);
+  put_u32(buf + 60, h->sblocks);
   for (int s = 0; s < MAX_SEC; s++) {
     put_u64(buf + 64 + 16 * s, (uint64_t)h->off[s]);
     put_u64(buf + 72 + 16 * s, (uint64_t)h->len[s]);
@@ -196,9 +198,12 @@ static int read_header(const uint8_t* buf, int64_t len, uint32_t magic, hdr_t* h
   h->k = (int64_t)get_u64(buf + 40);
   h->total = (int64_t)get_u64(buf + 48);
   h->nsec = get_u32(buf + 56);
+  h->sblocks = get_u32(buf + 60);
   if (h->magic != magic || h->version != 1) return ORC_ERR_CORRUPT;
-  if (h->format != ORC_FMT_C1 && h->format != ORC_FMT_C2 && h->format != ORC_FMT_C2T)
+  if (h->format != ORC_FMT_C1 && h->format != ORC_FMT_C2 && h->format != ORC_FMT_C2T &&
+      h->format != ORC_FMT_C1S)
     return ORC_ERR_CORRUPT;
+  if (h->sblocks != (h->format == ORC_FMT_C1S ? ORC_SUPERBLOCK_BLOCKS : 0u)) return ORC_ERR_CORRUPT;
   if (h->mant > 7 || h->R < 0 || h->C <= 0 || h->B <= 0 || h->C % h->B || h->B % 32 ||
       h->k < 0 || h->k > h->C || h->C > 65536 || h->total > len || h->nsec > MAX_SEC)
     return ORC_ERR_CORRUPT;
@@ -300,10 +305,14 @@ int orc_encode(const uint16_t* w, int64_t R, int64_t C, int64_t k, int m, int64_
                int format, uint8_t* spec, int64_t spec_cap, uint8_t* verif,
                int64_t verif_cap, int64_t* spec_bytes, int64_t* verif_bytes) {
   if (R < 0 || C <= 0 || C > 65536 || B < 32 || (B & (B - 1)) || C % B || k < 0 || k > C ||
-      m < 0 || m > 7 || (format != ORC_FMT_C1 && format != ORC_FMT_C2 && format != ORC_FMT_C2T))
+      m < 0 || m > 7 ||
+      (format != ORC_FMT_C1 && format != ORC_FMT_C2 && format != ORC_FMT_C2T && format != ORC_FMT_C1S))
     return ORC_ERR_INVALID;
-  /* format 3 shares Cassandra-2's speculation stream */
-  const int c2 = format != ORC_FMT_C1;
+  /* format 3 shares Cassandra-2's speculation stream; format 4 is Cassandra-1
+   * with superblock metadata */
+  const int c1 = format == ORC_FMT_C1 || format == ORC_FMT_C1S;
+  const int c2 = !c1;
+  const int64_t SB = ORC_SUPERBLOCK_BLOCKS, nsb = (C / B + SB - 1) / SB;
   if (R > 0 && !w) return ORC_ERR_INVALID;
   const int64_t n = R * C, nb = C / B;
 
@@ -341,7 +350,7 @@ int orc_encode(const uint16_t* w, int64_t R, int64_t C, int64_t k, int m, int64_
     for (int64_t j = 0; j < C; j++) {
       uint16_t b = w[r * C + j];
       if (keep[r * C + j]) {
-        if (format == ORC_FMT_C1) {
+        if (c1) {
           sbits[r] += (uint64_t)rank_s[bf_e(b)] + 1;
         } else if (format == ORC_FMT_C2) {
           int d = shexp[(r * C + j) / 32] - mx_eff(b);
@@ -364,9 +373,14 @@ int orc_encode(const uint16_t* w, int64_t R, int64_t C, int64_t k, int m, int64_
   hs.format = hv.format = (uint32_t)format;
   hs.mant = hv.mant = (uint32_t)m;
   hs.R = hv.R = R; hs.C = hv.C = C; hs.B = hv.B = B; hs.k = hv.k = k;
-  if (format == ORC_FMT_C1) {
+  if (c1) {
     int64_t ls[S1_N] = {256, n / 8, 8 * R, 4 * R * nb, 2 * R * nb,
                         (R * k * (1 + m) + 7) / 8, (int64_t)((stot + 7) / 8)};
+    if (format == ORC_FMT_C1S) { /* u64 per superblock, u16 per block */
+      ls[S1_ROWBASE] = 8 * R * nsb;
+      ls[S1_BLKOFF] = 2 * R * nb;
+      hs.sblocks = hv.sblocks = (uint32_t)SB;
+    }
     int64_t lv[V1_N] = {256, 8 * R, 4 * R * nb, (R * k * (7 - m) + 7) / 8, R * (C - k),
                         (int64_t)((vtot + 7) / 8)};
     layout(&hs, S1_N, ls);
@@ -395,12 +409,12 @@ int orc_encode(const uint16_t* w, int64_t R, int64_t C, int64_t k, int m, int64_
       memset(verif, 0, (size_t)hv.total);
       write_header(spec, &hs);
       write_header(verif, &hv);
-      uint64_t sbase = 0, vbase = 0, kbase = 0;
-      for (int64_t r = 0; r < R; r++) {
+      uint64_t sbase = 0, vbase = 0, kbase = 0, sb_base = 0;
+      for (int64_t r = 0; r < R && status == ORC_OK; r++) {
         int64_t kept_i = 0, pr_i = 0;        /* kept / pruned index within the row */
         uint64_t spos = sbase, vpos = vbase, kpos = kbase;
-        if (format == ORC_FMT_C1) {
-          put_u64(spec + hs.off[S1_ROWBASE] + 8 * r, sbase);
+        if (c1) {
+          if (format == ORC_FMT_C1) put_u64(spec + hs.off[S1_ROWBASE] + 8 * r, sbase);
           put_u64(verif + hv.off[V1_ROWBASE] + 8 * r, vbase);
         } else if (format == ORC_FMT_C2) {
           put_u64(verif + hv.off[V2_ROWBASE_K] + 8 * r, kbase);
@@ -409,7 +423,18 @@ int orc_encode(const uint16_t* w, int64_t R, int64_t C, int64_t k, int m, int64_
         for (int64_t j = 0; j < C; j++) {
           if (j % B == 0) { /* per-block offsets and kept-before counts */
             int64_t blk = r * nb + j / B;
-            if (format == ORC_FMT_C1) {
+            if (format == ORC_FMT_C1S) {
+              /* superblock of SB blocks: u64 base at its first block, u16
+               * offsets from that base */
+              if ((j / B) % SB == 0) {
+                sb_base = spos;
+                put_u64(spec + hs.off[S1_ROWBASE] + 8 * (r * nsb + (j / B) / SB), sb_base);
+              }
+              if (spos - sb_base > 65535) { status = ORC_ERR_OVERFLOW; break; }
+              put_u16(spec + hs.off[S1_BLKOFF] + 2 * blk, (uint16_t)(spos - sb_base));
+              put_u16(spec + hs.off[S1_KEPTB] + 2 * blk, (uint16_t)kept_i);
+              put_u32(verif + hv.off[V1_BLKOFF] + 4 * blk, (uint32_t)(vpos - vbase));
+            } else if (format == ORC_FMT_C1) {
               put_u32(spec + hs.off[S1_BLKOFF] + 4 * blk, (uint32_t)(spos - sbase));
               put_u16(spec + hs.off[S1_KEPTB] + 2 * blk, (uint16_t)kept_i);
               put_u32(verif + hv.off[V1_BLKOFF] + 4 * blk, (uint32_t)(vpos - vbase));
@@ -428,7 +453,7 @@ int orc_encode(const uint16_t* w, int64_t R, int64_t C, int64_t k, int m, int64_
           int s = bf_s(b), e = bf_e(b), f = bf_f(b);
           if (keep[r * C + j]) {
             int64_t kin = r * k + kept_i; /* kept index in the tensor */
-            if (format == ORC_FMT_C1) {
+            if (c1) {
               /* step 2: top m mantissa bits with the sign to spec, the rest to verif */
               put_bits(spec + hs.off[S1_BITMAP], (uint64_t)(r * C + j), 1, 1);
               int ft = f >> (7 - m), fl = f & ((1 << (7 - m)) - 1);
@@ -468,8 +493,8 @@ int orc_encode(const uint16_t* w, int64_t R, int64_t C, int64_t k, int m, int64_
           } else {
             /* pruned: sign and full mantissa byte plus the coded exponent to verif */
             int64_t pin = r * (C - k) + pr_i;
-            int pbyte_sec = format == ORC_FMT_C1 ? V1_PRUNED : V2_PRUNED;
-            int code_sec = format == ORC_FMT_C1 ? V1_CODES : V2_CODES;
+            int pbyte_sec = c1 ? V1_PRUNED : V2_PRUNED;
+            int code_sec = c1 ? V1_CODES : V2_CODES;
             verif[hv.off[pbyte_sec] + pin] = (uint8_t)((s << 7) | f);
             put_unary(verif + hv.off[code_sec], vpos, rank_v[e]);
             vpos += (uint64_t)rank_v[e] + 1;
@@ -478,10 +503,10 @@ int orc_encode(const uint16_t* w, int64_t R, int64_t C, int64_t k, int m, int64_
         }
         sbase = spos; vbase = vpos; kbase = kpos;
       }
-      if (format == ORC_FMT_C1) memcpy(spec + hs.off[S1_RANK], perm_s, 256);
+      if (c1) memcpy(spec + hs.off[S1_RANK], perm_s, 256);
       else memcpy(spec + hs.off[S2_SHEXP], shexp, (size_t)(n / 32));
       if (format != ORC_FMT_C2T)
-        memcpy(verif + (format == ORC_FMT_C1 ? hv.off[V1_RANK] : hv.off[V2_RANK]), perm_v, 256);
+        memcpy(verif + (c1 ? hv.off[V1_RANK] : hv.off[V2_RANK]), perm_v, 256);
     }
   }
   free(keep); free(shexp); free(sbits); free(vbits); free(kbits);
@@ -497,13 +522,16 @@ static int decode_row(const uint8_t* spec, const hdr_t* hs, const uint8_t* verif
   const int64_t C = hs->C, B = hs->B, k = hs->k, nb = C / B;
   const int m = (int)hs->mant;
   int64_t kept_i = 0, pr_i = 0;
-  if (hs->format == ORC_FMT_C1) {
+  if (hs->format == ORC_FMT_C1 || hs->format == ORC_FMT_C1S) {
+    const int sbm = hs->format == ORC_FMT_C1S;
+    const int64_t SB = ORC_SUPERBLOCK_BLOCKS, nsb = (nb + SB - 1) / SB;
+    uint64_t sb_base = 0;
     const uint8_t* perm_s = spec + hs->off[S1_RANK];
     const uint8_t* bm = spec + hs->off[S1_BITMAP];
     const uint8_t* fields = spec + hs->off[S1_FIELDS];
     const uint8_t* codes = spec + hs->off[S1_CODES];
     uint64_t send = (uint64_t)hs->len[S1_CODES] * 8;
-    uint64_t sbase = get_u64(spec + hs->off[S1_ROWBASE] + 8 * r), spos = sbase;
+    uint64_t sbase = get_u64(spec + hs->off[S1_ROWBASE] + 8 * (sbm ? r * nsb : r)), spos = sbase;
     uint64_t vbase = 0, vpos = 0, vend = 0;
     if (verif) {
       vbase = get_u64(verif + hv->off[V1_ROWBASE] + 8 * r);
@@ -513,7 +541,15 @@ static int decode_row(const uint8_t* spec, const hdr_t* hs, const uint8_t* verif
     for (int64_t j = 0; j < C; j++) {
       if (j % B == 0) {
         int64_t blk = r * nb + j / B;
-        if (get_u32(spec + hs->off[S1_BLKOFF] + 4 * blk) != spos - sbase) return ORC_ERR_CORRUPT;
+        if (sbm) {
+          if ((j / B) % SB == 0) {
+            sb_base = get_u64(spec + hs->off[S1_ROWBASE] + 8 * (r * nsb + (j / B) / SB));
+            if (sb_base != spos) return ORC_ERR_CORRUPT;
+          }
+          if (get_u16(spec + hs->off[S1_BLKOFF] + 2 * blk) != spos - sb_base) return ORC_ERR_CORRUPT;
+        } else if (get_u32(spec + hs->off[S1_BLKOFF] + 4 * blk) != spos - sbase) {
+          return ORC_ERR_CORRUPT;
+        }
         if (get_u16(spec + hs->off[S1_KEPTB] + 2 * blk) != (uint16_t)kept_i) return ORC_ERR_CORRUPT;
         if (verif && get_u32(verif + hv->off[V1_BLKOFF] + 4 * blk) != vpos - vbase)
           return ORC_ERR_CORRUPT;
@@ -549,7 +585,7 @@ static int decode_row(const uint8_t* spec, const hdr_t* hs, const uint8_t* verif
       }
     }
     if (kept_i != k) return ORC_ERR_CORRUPT;
-    if (r + 1 < hs->R && get_u64(spec + hs->off[S1_ROWBASE] + 8 * (r + 1)) != spos)
+    if (r + 1 < hs->R && get_u64(spec + hs->off[S1_ROWBASE] + 8 * (sbm ? (r + 1) * nsb : r + 1)) != spos)
       return ORC_ERR_CORRUPT;
     if (verif && r + 1 < hs->R && get_u64(verif + hv->off[V1_ROWBASE] + 8 * (r + 1)) != vpos)
       return ORC_ERR_CORRUPT;

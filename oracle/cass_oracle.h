@@ -31,7 +31,17 @@ extern "C" {
 
 enum { ORC_OK = 0, ORC_ERR_INVALID = 1, ORC_ERR_UNSUPPORTED = 2, ORC_ERR_OVERFLOW = 3,
        ORC_ERR_CORRUPT = 4, ORC_ERR_CAPACITY = 5 };
-enum { ORC_FMT_C1 = 1, ORC_FMT_C2 = 2, ORC_FMT_C2T = 3 };
+enum { ORC_FMT_C1 = 1, ORC_FMT_C2 = 2, ORC_FMT_C2T = 3, ORC_FMT_C1S = 4 };
+/* Format 4, Cassandra-1 with superblock metadata (pith.science review,
+ * Figure 11: superblock-based data management): the speculation stream's
+ * row bases and u32 block offsets give way to a u64 code base per
+ * superblock of ORC_SUPERBLOCK_BLOCKS blocks of a row (the last one of a row
+ * may be shorter; superblock j of row r at entry r*ceil(nb/16)+j of section 2)
+ * and u16 block offsets from their superblock's base (section 3).  Everything
+ * else is Cassandra-1's.  Encoding fails with ORC_ERR_OVERFLOW when a block
+ * starts 2^16 or more code bits after its superblock's base.  Both headers
+ * hold ORC_SUPERBLOCK_BLOCKS in the u32 at byte 60 (0 in other formats). */
+#define ORC_SUPERBLOCK_BLOCKS 16
 
 #define ORC_MAGIC_SPEC  0x50535343u /* "CSSP" */
 #define ORC_MAGIC_VERIF 0x46565343u /* "CSVF" */
