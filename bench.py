@@ -23,7 +23,8 @@ runs a plain 1 GiB device copy (to calibrate the HBM byte counters); --mode spec
 runs only the speculative step over the 32-layer stack (and, without
 --no-extras, the dense bf16 context); --mode mxt compares Cassandra-2 with
 a lossless and with an MX-quantised target on one Qwen3-4B-shaped layer;
---mode codecs compares the exponent codes (Huffman, unary) and their decoders.
+--mode codecs compares the exponent codes (Huffman, unary) and their decoders;
+--mode superblock compares the superblock metadata layout with the flat one.
 """
 from __future__ import annotations
 
@@ -51,8 +52,8 @@ def parse():
     ap.add_argument("--mant", type=int, default=3)
     ap.add_argument("--block", type=int, default=256)
     ap.add_argument("--copies", type=int, default=8)
-    ap.add_argument("--mode", choices=("full", "gemv", "exact", "copy", "spec", "mxt", "codecs"),
-                    default="full")
+    ap.add_argument("--mode", choices=("full", "gemv", "exact", "copy", "spec", "mxt", "codecs",
+                                       "superblock"), default="full")
     ap.add_argument("--no-extras", action="store_true", help="headline and CPU baseline only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -122,6 +123,15 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"mode": "copy", "bytes": 1 << 30}))
+        return
+
+    if args.mode == "superblock":
+        gen = torch.Generator(device="cuda")
+        gen.manual_seed(2_000_001)
+        L = torch_layer(torch, synth.LLAMA3_8B, gen)
+        xs = {n: dev16(synth.activations(1, L[n].shape[1], 2, t0=i)) for i, n in enumerate(MATS)}
+        print(json.dumps({"mode": "superblock", "superblock_metadata_llama8b_layer":
+                          run_superblock(torch, cass, timer, stream, L, xs)}))
         return
 
     if args.mode == "codecs":
@@ -402,6 +412,8 @@ def run_extras(args, torch, cass, synth, timer, stream, layers, encs, layer0, en
     out["rows"] = rows
     out["exponent_codecs_llama8b_layer"] = run_prefix_codecs(torch, cass, timer, stream, layers[0])
     log("codecs done")
+    out["superblock_metadata_llama8b_layer"] = run_superblock(torch, cass, timer, stream, layers[0], xs)
+    log("superblock done")
 
     # ---- keep x mantissa sweep (layer 0)
     sweep = {}
@@ -662,6 +674,54 @@ def codec_compare(torch, cass, timer, stream, sym):
         res[name] = row
         del st, ws, out
     return res
+
+
+def run_superblock(torch, cass, timer, stream, layer, xs):
+    """Cassandra-1 with superblock metadata (format 4) against the flat
+    metadata (format 1) on one Llama-3-8B-shaped layer (keep 0.3, m 3):
+    speculation bits per value, metadata bits per value, and the draft GEMV of
+    the per-thread stream-reader kernel (the one format 4 runs on) for both,
+    with format 1's default kernel as context."""
+    import synth
+    res = {}
+    n_values = sum(layer[n].numel() for n in MATS)
+    enc = {}
+    for fmt, name in ((cass.CASS_FMT_C1_UNARY, "flat"), (cass.CASS_FMT_C1_SUPERBLOCK, "superblock")):
+        enc[name] = {n: cass.encode(layer[n], synth.keep_count(0.3, layer[n].shape[1]), 3, fmt=fmt)
+                     for n in MATS}
+        sb = sum(enc[name][n].spec_bytes for n in MATS)
+        meta = 0
+        for n in MATS:
+            meta += sum(int(enc[name][n].plan.spec_len[i]) for i in (2, 3, 4))
+        res[name] = {"spec_bits_per_value": round(8 * sb / n_values, 4),
+                     "metadata_bits_per_value": round(8 * meta / n_values, 4)}
+    cass.cass_set_option("gemv_path", 2)
+    try:
+        for name in ("flat", "superblock"):
+            e = enc[name]
+            ms = sum(timer.ms(lambda n=n: cass.cass_draft_gemv(e[n].desc, xs[n], ys_of(torch, e[n]),
+                                                               stream), 10) for n in MATS)
+            res[name]["draft_gemv_direct_kernel_ms_per_layer"] = round(ms, 4)
+    finally:
+        cass.cass_set_option("gemv_path", 0)
+    e = enc["flat"]
+    res["flat"]["draft_gemv_default_kernel_ms_per_layer"] = round(
+        sum(timer.ms(lambda n=n: cass.cass_draft_gemv(e[n].desc, xs[n], ys_of(torch, e[n]), stream), 10)
+            for n in MATS), 4)
+    res["spec_bytes_saved_pct"] = round(
+        100 * (1 - res["superblock"]["spec_bits_per_value"] / res["flat"]["spec_bits_per_value"]), 3)
+    del enc
+    return res
+
+
+_ys = {}
+
+
+def ys_of(torch, e):
+    key = e.rows
+    if key not in _ys:
+        _ys[key] = torch.empty((1, e.rows), dtype=torch.float32, device="cuda")
+    return _ys[key]
 
 
 def graph_ms(torch, g, reps):

@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(_HERE, "libcassandra.so")
 
 CASS_OK, CASS_ERR_INVALID, CASS_ERR_UNSUPPORTED, CASS_ERR_OVERFLOW, CASS_ERR_CORRUPT, \
     CASS_ERR_CAPACITY, CASS_ERR_HIP = range(7)
-CASS_FMT_C1_UNARY, CASS_FMT_C2_MX32, CASS_FMT_C2_MX_TARGET = 1, 2, 3
+CASS_FMT_C1_UNARY, CASS_FMT_C2_MX32, CASS_FMT_C2_MX_TARGET, CASS_FMT_C1_SUPERBLOCK = 1, 2, 3, 4
 MAX_SECTIONS = 12
 
 # symbols include/cassandra.h declares

@@ -63,11 +63,15 @@ void stream_lengths(int format, int64_t R, int64_t C, int64_t B, int64_t k, int 
                     uint64_t code_a, uint64_t code_v, std::vector<int64_t>& ls,
                     std::vector<int64_t>& lv) {
   const int64_t n = R * C, nb = C / B;
-  if (format == CASS_FMT_C1_UNARY) {
+  if (is_c1_format(format)) {
     ls = {256, n / 8, 8 * R, 4 * R * nb, 2 * R * nb, (R * k * (1 + m) + 7) / 8,
           (int64_t)((code_a + 7) / 8)};
     lv = {256, 8 * R, 4 * R * nb, (R * k * (7 - m) + 7) / 8, R * (C - k),
           (int64_t)((code_v + 7) / 8)};
+    if (format == CASS_FMT_C1_SUPERBLOCK) {  // u64 per superblock, u16 per block
+      ls[S1_ROWBASE] = 8 * R * ((nb + CASS_SUPERBLOCK_BLOCKS - 1) / CASS_SUPERBLOCK_BLOCKS);
+      ls[S1_BLKOFF] = 2 * R * nb;
+    }
   } else if (format == CASS_FMT_C2_MX32) {
     ls = {n / 8, n / 32, 2 * R * nb, (R * k * (2 + m) + 7) / 8};
     lv = {256, 8 * R, 4 * R * nb, (int64_t)((code_a + 7) / 8), R * (C - k), 8 * R, 4 * R * nb,
@@ -96,6 +100,7 @@ void write_header(uint8_t* h, uint32_t magic, int format, int m, int64_t R, int6
   put64(h + 40, k);
   put64(h + 48, L.total);
   put32(h + 56, (uint32_t)L.nsec);
+  put32(h + 60, format == CASS_FMT_C1_SUPERBLOCK ? CASS_SUPERBLOCK_BLOCKS : 0u);
   for (int s = 0; s < CASS_MAX_SECTIONS; ++s) {
     put64(h + 64 + 16 * s, L.off[s]);
     put64(h + 72 + 16 * s, L.len[s]);
@@ -107,7 +112,7 @@ void write_header(uint8_t* h, uint32_t magic, int format, int m, int64_t R, int6
 int check_shape(int64_t R, int64_t C, const cass_params* p) {
   if (!p) return fail(CASS_ERR_INVALID, "params is NULL");
   if (p->format != CASS_FMT_C1_UNARY && p->format != CASS_FMT_C2_MX32 &&
-      p->format != CASS_FMT_C2_MX_TARGET)
+      p->format != CASS_FMT_C2_MX_TARGET && p->format != CASS_FMT_C1_SUPERBLOCK)
     return fail(CASS_ERR_INVALID, "unknown format %d", p->format);
   if (p->mant_bits < 0 || p->mant_bits > 7)
     return fail(CASS_ERR_INVALID, "mant_bits %d outside 0..7", p->mant_bits);
@@ -128,7 +133,7 @@ std::vector<int64_t> closed_lengths(bool spec, int format, int64_t R, int64_t C,
                                     int64_t k, int m) {
   std::vector<int64_t> ls, lv;
   stream_lengths(format, R, C, B, k, m, 0, 0, ls, lv);
-  if (format == CASS_FMT_C1_UNARY) {
+  if (is_c1_format(format)) {
     ls[S1_CODES] = -1;
     lv[V1_CODES] = -1;
   } else if (format == CASS_FMT_C2_MX32) {
@@ -201,7 +206,21 @@ SpecViewC1 spec_c1(const cass_tensor* W) {
                     (const uint32_t*)(b + o[S1_FIELDS]), (const uint32_t*)(b + o[S1_CODES]),
                     word_limit(W->spec_bytes, o[S1_BITMAP]), word_limit(W->spec_bytes, o[S1_FIELDS]),
                     word_limit(W->spec_bytes, o[S1_CODES]), word_limit(W->spec_bytes, o[S1_BLKOFF]),
-                    2 * word_limit(W->spec_bytes, o[S1_KEPTB])};
+                    2 * word_limit(W->spec_bytes, o[S1_KEPTB]), nullptr, nullptr, -1, 0};
+}
+// Format 4: the row-base / block-offset sections hold superblock bases and
+// 16-bit block offsets.
+SpecViewC1 spec_c1s(const cass_tensor* W) {
+  SpecViewC1 v = spec_c1(W);
+  const uint8_t* b = (const uint8_t*)W->spec;
+  const int64_t nb = W->cols / W->block;
+  v.sbbase = (const unsigned long long*)(b + W->spec_sec[S1_ROWBASE]);
+  v.blkoff16 = (const uint16_t*)(b + W->spec_sec[S1_BLKOFF]);
+  v.rowbase = nullptr;
+  v.blkoff = nullptr;
+  v.sb_log = 4;
+  v.nsb = (nb + CASS_SUPERBLOCK_BLOCKS - 1) / CASS_SUPERBLOCK_BLOCKS;
+  return v;
 }
 VerifViewC1 verif_c1(const cass_tensor* W) {
   const uint8_t* b = (const uint8_t*)W->verif;
@@ -267,7 +286,7 @@ int64_t ws_layout(int64_t R, int64_t C, int64_t B, Workspace* ws, uint8_t* base)
   w.keptb = (uint16_t*)take(2 * nblk);
   w.row_a = (unsigned long long*)take(8 * R);
   w.row_v = (unsigned long long*)take(8 * R);
-  w.totals = (unsigned long long*)take(16);
+  w.totals = (unsigned long long*)take(24);  // code bits, pruned bits, superblock span
   w.bytes = pos;
   if (ws) *ws = w;
   return pos;
@@ -386,16 +405,23 @@ int cass_encode_plan(const uint16_t* w, int64_t rows, int64_t cols, int64_t ld,
     return hip_fail(e, "code lengths");
   if ((e = launch_row_scan(sh, W, stream)) != hipSuccess) return hip_fail(e, "row scan");
   if ((e = launch_rows_scan(sh, W, stream)) != hipSuccess) return hip_fail(e, "rows scan");
-  unsigned long long totals[2];
+  if (p->format == CASS_FMT_C1_SUPERBLOCK &&
+      (e = launch_superblock_span(sh, W, CASS_SUPERBLOCK_BLOCKS, stream)) != hipSuccess)
+    return hip_fail(e, "superblock span");
+  unsigned long long totals[3];
   if ((e = hipMemcpyAsync(totals, W.totals, sizeof totals, hipMemcpyDeviceToHost, stream)) !=
       hipSuccess)
     return hip_fail(e, "totals copy");
   if ((e = hipStreamSynchronize(stream)) != hipSuccess) return hip_fail(e, "synchronize");
-  if (p->format == CASS_FMT_C1_UNARY) {
+  if (is_c1_format(p->format)) {
     plan->spec_code_bits = totals[0];
   } else {
     plan->resid_bits = totals[0];
   }
+  if (p->format == CASS_FMT_C1_SUPERBLOCK && totals[2] > 65535)
+    return fail(CASS_ERR_OVERFLOW,
+                "a block starts %llu code bits after its superblock's base (16-bit offsets); use "
+                "format 1", (unsigned long long)totals[2]);
   plan->verif_code_bits = totals[1];
   std::vector<int64_t> ls, lv;
   stream_lengths(p->format, rows, cols, p->block, p->keep, p->mant_bits, totals[0], totals[1], ls,
@@ -436,7 +462,7 @@ int cass_encode_tensor(const uint16_t* w, int64_t ld, const cass_plan* plan, voi
     rt.rank_pruned[plan->perm_verif[r]] = (uint8_t)r;
   }
   std::vector<int64_t> ls, lv;
-  const uint64_t code_a = p->format == CASS_FMT_C1_UNARY ? plan->spec_code_bits : plan->resid_bits;
+  const uint64_t code_a = is_c1_format(p->format) ? plan->spec_code_bits : plan->resid_bits;
   stream_lengths(p->format, plan->rows, plan->cols, p->block, p->keep, p->mant_bits, code_a,
                  plan->verif_code_bits, ls, lv);
   const Layout Ls = lay_out(ls), Lv = lay_out(lv);
@@ -452,7 +478,7 @@ int cass_encode_tensor(const uint16_t* w, int64_t ld, const cass_plan* plan, voi
   hipError_t e;
   if ((e = launch_fill_zero(spec, Ls.total, stream)) != hipSuccess) return hip_fail(e, "zero fill");
   if ((e = launch_fill_zero(verif, Lv.total, stream)) != hipSuccess) return hip_fail(e, "zero fill");
-  const int64_t srank = p->format == CASS_FMT_C1_UNARY ? Ls.off[S1_RANK] : 0;
+  const int64_t srank = is_c1_format(p->format) ? Ls.off[S1_RANK] : 0;
   const int64_t vrank = p->format == CASS_FMT_C2_MX_TARGET ? 0 : Lv.off[V1_RANK];
   if ((e = launch_write_headers(hb, (uint8_t*)spec, srank, (uint8_t*)verif, vrank,
                                 stream)) != hipSuccess)
@@ -515,6 +541,9 @@ int cass_tensor_describe(const void* spec_header, const void* spec, int64_t spec
   cass_params pp = {out->format, out->mant_bits, out->block, out->keep};
   int st = check_shape(out->rows, out->cols, &pp);
   if (st) return fail(CASS_ERR_CORRUPT, "%s", g_last_error.c_str());
+  const uint32_t want_sb = out->format == CASS_FMT_C1_SUPERBLOCK ? CASS_SUPERBLOCK_BLOCKS : 0u;
+  if (get32(h + 60) != want_sb || (out->verif && get32((const uint8_t*)verif_header + 60) != want_sb))
+    return fail(CASS_ERR_CORRUPT, "superblock size field does not match the format");
   for (int which = 0; which < (out->verif ? 2 : 1); ++which) {
     const uint8_t* hh = which == 0 ? h : (const uint8_t*)verif_header;
     const int64_t total = get64(hh + 48);
@@ -564,13 +593,17 @@ int cass_draft_gemv(const cass_tensor* W, const uint16_t* x, int batch, int64_t 
   if (ldx < W->cols || ldy < W->rows) return fail(CASS_ERR_INVALID, "ldx < cols or ldy < rows");
   const Shape sh = shape_of(W);
   const int64_t code_limit = W->format == CASS_FMT_C1_UNARY ? spec_c1(W).codes_limit : 0;
-  if (!draft_gemv_staged_fits(sh, batch, W->format, code_limit) &&
-      draft_gemv_direct_lds_bytes(sh, batch) > 150 * 1024)
+  const bool staged_ok = W->format != CASS_FMT_C1_SUPERBLOCK &&
+                         draft_gemv_staged_fits(sh, batch, W->format, code_limit);
+  if (!staged_ok && draft_gemv_direct_lds_bytes(sh, batch) > 150 * 1024)
     return fail(CASS_ERR_UNSUPPORTED, "batch %d x cols %lld does not fit in LDS", batch,
                 (long long)W->cols);
-  hipError_t e = W->format == CASS_FMT_C1_UNARY
-                     ? launch_draft_gemv_c1(spec_c1(W), sh, x, batch, ldx, y, ldy, stream)
-                     : launch_draft_gemv_c2(spec_c2(W), sh, x, batch, ldx, y, ldy, stream);
+  hipError_t e =
+      W->format == CASS_FMT_C1_UNARY
+          ? launch_draft_gemv_c1(spec_c1(W), sh, x, batch, ldx, y, ldy, stream)
+      : W->format == CASS_FMT_C1_SUPERBLOCK
+          ? launch_draft_gemv_c1_direct(spec_c1s(W), sh, x, batch, ldx, y, ldy, stream)
+          : launch_draft_gemv_c2(spec_c2(W), sh, x, batch, ldx, y, ldy, stream);
   return e == hipSuccess ? CASS_OK : hip_fail(e, "draft gemv launch");
 }
 
@@ -591,6 +624,8 @@ int cass_verify_gemm(const cass_tensor* W, const uint16_t* X, int ntok, int64_t 
     e = staged_exact_enabled() && exact_staged_fits(sh, sv, vv)
             ? launch_verify_gemm_c1_staged(sv, vv, sh, X, ntok, ldx, Y, ldy, stream)
             : launch_verify_gemm_c1(sv, vv, sh, X, ntok, ldx, Y, ldy, stream);
+  } else if (W->format == CASS_FMT_C1_SUPERBLOCK) {
+    e = launch_verify_gemm_c1(spec_c1s(W), verif_c1(W), sh, X, ntok, ldx, Y, ldy, stream);
   } else if (W->format == CASS_FMT_C2_MX32) {
     e = launch_verify_gemm_c2(spec_c2(W), verif_c2(W), sh, X, ntok, ldx, Y, ldy, stream);
   } else {
@@ -613,6 +648,9 @@ int cass_reconstruct(const cass_tensor* W, uint16_t* out, hipStream_t stream) {
     e = staged_exact_enabled() && exact_staged_fits(sh, sv, vv)
             ? launch_reconstruct_c1_staged(sv, vv, sh, out, stream)
             : launch_decode_c1(sv, &vv, sh, out, stream);
+  } else if (W->format == CASS_FMT_C1_SUPERBLOCK) {
+    const VerifViewC1 vv = verif_c1(W);
+    e = launch_decode_c1(spec_c1s(W), &vv, sh, out, stream);
   } else if (W->format == CASS_FMT_C2_MX32) {
     const VerifViewC2 vv = verif_c2(W);
     e = launch_decode_c2(spec_c2(W), &vv, sh, out, stream);
@@ -636,6 +674,8 @@ int cass_draft_decode(const cass_tensor* W, uint16_t* out, hipStream_t stream) {
     e = staged_exact_enabled() && exact_staged_fits(sh, sv, none)
             ? launch_draft_decode_c1_staged(sv, sh, out, stream)
             : launch_decode_c1(sv, nullptr, sh, out, stream);
+  } else if (W->format == CASS_FMT_C1_SUPERBLOCK) {
+    e = launch_decode_c1(spec_c1s(W), nullptr, sh, out, stream);
   } else {
     e = launch_decode_c2(spec_c2(W), nullptr, sh, out, stream);
   }

@@ -35,7 +35,7 @@ struct ExactC1 {
     const uint32_t kb = sv.keptb[bi];
     const uint64_t kin0 = (uint64_t)row * sh.keep + kb;
     fr.init(sv.fields, kin0 * (uint64_t)(1 + m));
-    er.init(sv.codes, sv.rowbase[row] + sv.blkoff[bi]);
+    er.init(sv.codes, c1_code_start(sv, row, bi, nb));
     lr.init(vv.lowmant, kin0 * (uint64_t)(7 - m));
     vr.init(vv.codes, vv.rowbase[row] + vv.blkoff[bi]);
     const uint64_t pidx = (uint64_t)row * (sh.cols - sh.keep) + (uint64_t)(b * sh.block) - kb;
@@ -72,7 +72,7 @@ struct DraftC1 {
     m = sh.mant;
     const uint32_t kb = sv.keptb[bi];
     fr.init(sv.fields, ((uint64_t)row * sh.keep + kb) * (uint64_t)(1 + m));
-    er.init(sv.codes, sv.rowbase[row] + sv.blkoff[bi]);
+    er.init(sv.codes, c1_code_start(sv, row, bi, nb));
     perm_s = ps;
   }
   __device__ __forceinline__ uint32_t kept(int /*word*/) {

@@ -192,7 +192,7 @@ __global__ void __launch_bounds__(256) k_block_bits(const uint16_t* __restrict__
           ++kept;
           if (format == CASS_FMT_C2_MX_TARGET) {
             // fixed-width verification sections: no code bits
-          } else if (format == CASS_FMT_C1_UNARY) {
+          } else if (is_c1_format(format)) {
             a += rk[e] + 1u;
           } else {
             const int E = shexp[pos0 / 32 + wi];
@@ -276,6 +276,25 @@ __global__ void __launch_bounds__(1024) k_rows_scan(int64_t R, unsigned long lon
   }
 }
 
+// Largest offset of a block's first code bit from its superblock's first
+// block, over the tensor.
+__global__ void __launch_bounds__(256) k_superblock_span(const uint32_t* __restrict__ off_a,
+                                                         int64_t R, int64_t nb, int sblocks,
+                                                         unsigned long long* out) {
+  unsigned long long mx = 0;
+  for (int64_t bi = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; bi < R * nb;
+       bi += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t b = bi % nb;
+    const unsigned long long d = off_a[bi] - off_a[bi - b % sblocks];
+    mx = d > mx ? d : mx;
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    const unsigned long long v = __shfl_xor(mx, o, 64);
+    mx = v > mx ? v : mx;
+  }
+  if ((threadIdx.x & 63) == 0 && mx) atomicMax(out, mx);
+}
+
 __global__ void k_write_headers(HeaderBlob hb, uint8_t* spec, int64_t spec_rank_off,
                                 uint8_t* verif, int64_t verif_rank_off) {
   const int t = threadIdx.x;  // 256 threads
@@ -304,6 +323,8 @@ struct PackPtrs {
   uint8_t* v_gexp;                  // format 3: X per 32 positions
   uint32_t* v_low;                  // format 3: kept low 7-m bits of t
   uint32_t* v_pr9;                  // format 3: pruned (s<<8)|t
+  unsigned long long* s_sbbase;     // format 4: code base per superblock
+  uint16_t* s_blkoff16;             // format 4: block offset from its superblock
 };
 
 // One thread per (row, block): writes every section's share of that block.
@@ -319,8 +340,10 @@ __global__ void __launch_bounds__(256) k_pack(const uint16_t* __restrict__ w, Sh
   const int64_t nb = C / B;
   const int64_t nblk = sh.rows * nb;
   const int m = sh.mant;
-  const bool c1 = format == CASS_FMT_C1_UNARY;
+  const bool c1 = is_c1_format(format);
   const bool c3 = format == CASS_FMT_C2_MX_TARGET;
+  const bool sbm = format == CASS_FMT_C1_SUPERBLOCK;
+  const int64_t nsb = (nb + CASS_SUPERBLOCK_BLOCKS - 1) / CASS_SUPERBLOCK_BLOCKS;
   for (int64_t bi = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; bi < nblk;
        bi += (int64_t)gridDim.x * blockDim.x) {
     const int64_t row = bi / nb, b = bi % nb;
@@ -377,10 +400,19 @@ __global__ void __launch_bounds__(256) k_pack(const uint16_t* __restrict__ w, Sh
     P.s_keptb[bi] = (uint16_t)kb;
     if (c1) {
       if (b == 0) {
-        P.s_rowbase[row] = base_a;
+        if (!sbm) P.s_rowbase[row] = base_a;
         P.v_rowbase[row] = base_v;
       }
-      P.s_blkoff[bi] = ws.off_a[bi];
+      if (sbm) {
+        // superblock metadata: a u64 base at each superblock's first block,
+        // 16-bit offsets from it (the plan checked they fit)
+        const int64_t b0 = b - b % CASS_SUPERBLOCK_BLOCKS;
+        const uint32_t sb_off = ws.off_a[row * nb + b0];
+        if (b == b0) P.s_sbbase[row * nsb + b / CASS_SUPERBLOCK_BLOCKS] = base_a + sb_off;
+        P.s_blkoff16[bi] = (uint16_t)(ws.off_a[bi] - sb_off);
+      } else {
+        P.s_blkoff[bi] = ws.off_a[bi];
+      }
       P.v_blkoff[bi] = ws.off_v[bi];
     } else {
       for (int64_t wi = 0; wi < B / 32; ++wi) P.s_shexp[pos0 / 32 + wi] = ws.shexp[pos0 / 32 + wi];
@@ -472,7 +504,7 @@ hipError_t launch_histograms(const uint16_t* w, const Shape& sh, int format, con
   if (nwords == 0) return hipSuccess;
   k_histograms<<<grid_for(nwords, 256), 256, 0, s>>>(
       w, nwords, sh.cols / 32, sh.ld, ws.bitmap, ws.hist,
-      format != CASS_FMT_C1_UNARY ? ws.shexp : nullptr);
+      is_c1_format(format) ? nullptr : ws.shexp);
   return hipGetLastError();
 }
 
@@ -494,9 +526,17 @@ hipError_t launch_row_scan(const Shape& sh, const Workspace& ws, hipStream_t s) 
 }
 
 hipError_t launch_rows_scan(const Shape& sh, const Workspace& ws, hipStream_t s) {
-  hipError_t e = launch_fill_zero(ws.totals, 2 * sizeof(unsigned long long), s);
+  hipError_t e = launch_fill_zero(ws.totals, 3 * sizeof(unsigned long long), s);
   if (e != hipSuccess || sh.rows == 0) return e;
   k_rows_scan<<<1, 1024, 0, s>>>(sh.rows, ws.row_a, ws.row_v, ws.totals);
+  return hipGetLastError();
+}
+
+hipError_t launch_superblock_span(const Shape& sh, const Workspace& ws, int sblocks, hipStream_t s) {
+  const int64_t nblk = sh.rows * (sh.cols / sh.block);
+  if (nblk == 0) return hipSuccess;
+  k_superblock_span<<<grid_for(nblk, 256), 256, 0, s>>>(ws.off_a, sh.rows, sh.cols / sh.block,
+                                                        sblocks, ws.totals + 2);
   return hipGetLastError();
 }
 
@@ -512,10 +552,15 @@ hipError_t launch_pack(const uint16_t* w, const Shape& sh, int format, const Wor
   const int64_t nblk = sh.rows * (sh.cols / sh.block);
   if (nblk == 0) return hipSuccess;
   PackPtrs P = {};
-  if (format == CASS_FMT_C1_UNARY) {
+  if (is_c1_format(format)) {
     P.s_bitmap = (uint32_t*)(spec + ss[S1_BITMAP]);
-    P.s_rowbase = (unsigned long long*)(spec + ss[S1_ROWBASE]);
-    P.s_blkoff = (uint32_t*)(spec + ss[S1_BLKOFF]);
+    if (format == CASS_FMT_C1_SUPERBLOCK) {
+      P.s_sbbase = (unsigned long long*)(spec + ss[S1_ROWBASE]);
+      P.s_blkoff16 = (uint16_t*)(spec + ss[S1_BLKOFF]);
+    } else {
+      P.s_rowbase = (unsigned long long*)(spec + ss[S1_ROWBASE]);
+      P.s_blkoff = (uint32_t*)(spec + ss[S1_BLKOFF]);
+    }
     P.s_keptb = (uint16_t*)(spec + ss[S1_KEPTB]);
     P.s_fields = (uint32_t*)(spec + ss[S1_FIELDS]);
     P.s_codes = (uint32_t*)(spec + ss[S1_CODES]);

@@ -82,7 +82,7 @@ __global__ void __launch_bounds__(kThreads) k_draft_gemv_c1(SpecViewC1 v, Shape 
       const uint32_t kb = v.keptb[bi];
       BitReader fr, er;
       fr.init(v.fields, ((uint64_t)row * sh.keep + kb) * (uint64_t)(1 + m));
-      er.init(v.codes, v.rowbase[row] + v.blkoff[bi]);
+      er.init(v.codes, c1_code_start(v, row, bi, nb));
       const uint32_t* bmp = v.bitmap + bi * (B / 32);
       const uint16_t* xb = xs + b * B;
       for (int64_t wi = 0; wi < B / 32; ++wi) {

@@ -68,7 +68,24 @@ struct SpecViewC1 {
   int64_t bitmap_limit, fields_limit, codes_limit;
   int64_t blkoff_limit;  // the same for the block offsets (words)
   int64_t keptb_limit;   // and for the kept-before counts (16-bit entries)
+  // format 4 (superblock metadata): code base per superblock of 2^sb_log
+  // blocks and 16-bit block offsets from it; sb_log < 0 for format 1
+  const unsigned long long* sbbase;
+  const uint16_t* blkoff16;
+  int sb_log;
+  int64_t nsb;  // superblocks per row
 };
+
+// First code bit of block bi (of row `row`, nb blocks per row).
+__device__ __forceinline__ uint64_t c1_code_start(const SpecViewC1& v, int64_t row, int64_t bi,
+                                                   int64_t nb) {
+  if (v.sb_log < 0) return v.rowbase[row] + v.blkoff[bi];
+  return v.sbbase[row * v.nsb + ((bi - row * nb) >> v.sb_log)] + v.blkoff16[bi];
+}
+
+__host__ __device__ __forceinline__ bool is_c1_format(int f) {
+  return f == CASS_FMT_C1_UNARY || f == CASS_FMT_C1_SUPERBLOCK;
+}
 struct VerifViewC1 {
   const uint8_t* perm;
   const unsigned long long* rowbase;
@@ -131,6 +148,9 @@ hipError_t launch_histograms(const uint16_t* w, const Shape& sh, int format, con
 hipError_t launch_block_bits(const uint16_t* w, const Shape& sh, int format, const Workspace& ws,
                              const RankTables& rt, hipStream_t s);
 hipError_t launch_row_scan(const Shape& sh, const Workspace& ws, hipStream_t s);
+// Largest code offset of a block from its superblock's first block (into
+// ws.totals[2]; the row scan must have run).
+hipError_t launch_superblock_span(const Shape& sh, const Workspace& ws, int sblocks, hipStream_t s);
 hipError_t launch_rows_scan(const Shape& sh, const Workspace& ws, hipStream_t s);
 hipError_t launch_write_headers(const HeaderBlob& hb, uint8_t* spec, int64_t spec_rank_off,
                                 uint8_t* verif, int64_t verif_rank_off, hipStream_t s);

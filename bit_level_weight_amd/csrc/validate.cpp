@@ -32,14 +32,16 @@ bool parse(const uint8_t* b, int64_t n, uint32_t magic, Hdr* h) {
   h->k = rd64(b + 40);
   h->total = rd64(b + 48);
   h->nsec = rd32(b + 56);
-  if (h->format != 1 && h->format != 2 && h->format != 3) return false;
+  if (h->format < 1 || h->format > 4) return false;
+  if (rd32(b + 60) != (h->format == 4 ? (uint32_t)CASS_SUPERBLOCK_BLOCKS : 0u)) return false;
   if (h->mant > 7 || h->R < 0 || h->C <= 0 || h->C > 65536 || h->B < 32 || (h->B & (h->B - 1)) ||
       h->C % h->B || h->k < 0 || h->k > h->C || h->total > n || h->total < 256 ||
       h->nsec > CASS_MAX_SECTIONS)
     return false;
   if (h->R > ((int64_t)1 << 40) / h->C) return false;
-  const uint32_t want = magic == kMagicSpec ? (h->format == 1 ? 7u : 4u)
-                                            : (h->format == 1 ? 6u : h->format == 2 ? 8u : 3u);
+  const bool c1f = h->format == 1 || h->format == 4;
+  const uint32_t want = magic == kMagicSpec ? (c1f ? 7u : 4u)
+                                            : (c1f ? 6u : h->format == 2 ? 8u : 3u);
   if (h->nsec != want) return false;
   for (int s = 0; s < CASS_MAX_SECTIONS; ++s) {
     h->off[s] = rd64(b + 64 + 16 * s);
@@ -81,7 +83,8 @@ extern "C" int cass_tensor_validate(const void* spec_v, int64_t spec_bytes, cons
   const uint8_t* verif = (const uint8_t*)verif_v;
   Hdr hs, hv;
   if (!parse(spec, spec_bytes, kMagicSpec, &hs)) return CASS_ERR_CORRUPT;
-  const bool c1 = hs.format == 1;
+  const bool c1 = hs.format == 1 || hs.format == 4;
+  const bool sbm = hs.format == 4;  // superblock metadata
   if (verif) {
     if (!parse(verif, verif_bytes, kMagicVerif, &hv)) return CASS_ERR_CORRUPT;
     if (hv.format != hs.format || hv.mant != hs.mant || hv.R != hs.R || hv.C != hs.C ||
@@ -95,7 +98,10 @@ extern "C" int cass_tensor_validate(const void* spec_v, int64_t spec_bytes, cons
   if (hs.len[bm_sec] != R * C / 8 || hs.len[kb_sec] != 2 * R * nb ||
       hs.len[f_sec] != (R * k * (c1 ? 1 + m : 2 + m) + 7) / 8)
     return CASS_ERR_CORRUPT;
-  if (c1 && (hs.len[0] != 256 || hs.len[2] != 8 * R || hs.len[3] != 4 * R * nb))
+  const int64_t SB = CASS_SUPERBLOCK_BLOCKS, nsb = (nb + SB - 1) / SB;
+  if (c1 && !sbm && (hs.len[0] != 256 || hs.len[2] != 8 * R || hs.len[3] != 4 * R * nb))
+    return CASS_ERR_CORRUPT;
+  if (sbm && (hs.len[0] != 256 || hs.len[2] != 8 * R * nsb || hs.len[3] != 2 * R * nb))
     return CASS_ERR_CORRUPT;
   if (!c1 && hs.len[1] != R * C / 32) return CASS_ERR_CORRUPT;
   if (hs.format == 3) {
@@ -144,7 +150,8 @@ extern "C" int cass_tensor_validate(const void* spec_v, int64_t spec_bytes, cons
   uint64_t spos = 0, vpos = 0, kpos = 0;
   for (int64_t r = 0; r < R; ++r) {
     uint64_t sbase = spos, vbase = vpos, kbase = kpos;
-    if (c1 && (uint64_t)rd64(spec + hs.off[2] + 8 * r) != spos) return CASS_ERR_CORRUPT;
+    if (c1 && (uint64_t)rd64(spec + hs.off[2] + 8 * (sbm ? r * nsb : r)) != spos) return CASS_ERR_CORRUPT;
+    uint64_t sb_base = spos;
     if (verif) {
       if (c1 && (uint64_t)rd64(verif + hv.off[1] + 8 * r) != vpos) return CASS_ERR_CORRUPT;
       if (!c1 && ((uint64_t)rd64(verif + hv.off[1] + 8 * r) != kpos ||
@@ -158,7 +165,18 @@ extern "C" int cass_tensor_validate(const void* spec_v, int64_t spec_bytes, cons
         uint16_t kbv;
         memcpy(&kbv, keptb + 2 * blk, 2);
         if (kbv != (uint16_t)kept) return CASS_ERR_CORRUPT;
-        if (c1 && rd32(spec + hs.off[3] + 4 * blk) != (uint32_t)(spos - sbase)) return CASS_ERR_CORRUPT;
+        if (sbm) {
+          if ((j / B) % SB == 0) {
+            sb_base = spos;
+            if ((uint64_t)rd64(spec + hs.off[2] + 8 * (r * nsb + (j / B) / SB)) != spos)
+              return CASS_ERR_CORRUPT;
+          }
+          uint16_t o16;
+          memcpy(&o16, spec + hs.off[3] + 2 * blk, 2);
+          if (spos - sb_base > 65535 || o16 != (uint16_t)(spos - sb_base)) return CASS_ERR_CORRUPT;
+        } else if (c1 && rd32(spec + hs.off[3] + 4 * blk) != (uint32_t)(spos - sbase)) {
+          return CASS_ERR_CORRUPT;
+        }
         if (verif) {
           if (c1 && rd32(verif + hv.off[2] + 4 * blk) != (uint32_t)(vpos - vbase))
             return CASS_ERR_CORRUPT;

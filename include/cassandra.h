@@ -67,6 +67,17 @@
  *   bit (r*keep+i)*(7-m)), 2 pruned values' (s<<8)|t, 9 bits each (pruned
  *   value i of row r at bit (r*(cols-keep)+i)*9).  cass_reconstruct returns
  *   the quantised target and cass_verify_gemm multiplies with it.
+ *  Format 4, Cassandra-1 with superblock metadata (pith.science review,
+ *   Figure 11: superblock-based data management): a superblock is
+ *   CASS_SUPERBLOCK_BLOCKS consecutive blocks of one row (the last of a row
+ *   may be shorter).  Speculation sections as Cassandra-1's but 2 = u64 code
+ *   base per superblock (superblock j of row r at entry r*ceil(nb/16)+j) and
+ *   3 = u16 code offset per block from its superblock's base; the
+ *   verification stream is Cassandra-1's.  Both headers hold 16 in the u32 at
+ *   byte 60 (0 in the other formats).  Encoding returns CASS_ERR_OVERFLOW when
+ *   a block starts 2^16 or more code bits after its superblock's base.  The
+ *   draft GEMV, verification GEMM and decoders of format 4 are the per-thread
+ *   stream readers (the balanced and staged kernels take format 1).
  */
 #ifndef CASSANDRA_H
 #define CASSANDRA_H
@@ -92,7 +103,9 @@ enum cass_status {
   CASS_ERR_HIP = 6          /* a HIP runtime call or launch failed */
 };
 
-enum cass_format { CASS_FMT_C1_UNARY = 1, CASS_FMT_C2_MX32 = 2, CASS_FMT_C2_MX_TARGET = 3 };
+enum cass_format { CASS_FMT_C1_UNARY = 1, CASS_FMT_C2_MX32 = 2, CASS_FMT_C2_MX_TARGET = 3,
+                   CASS_FMT_C1_SUPERBLOCK = 4 };
+#define CASS_SUPERBLOCK_BLOCKS 16
 
 #define CASS_MAX_SECTIONS 12
 

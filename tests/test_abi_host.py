@@ -54,7 +54,7 @@ def test_ws_bytes_and_argument_errors(cass):
     n = ctypes.c_int64(0)
     assert L.cass_encode_ws_bytes(4096, 4096, ctypes.byref(p), ctypes.byref(n)) == 0
     assert n.value >= 4096 * 4096 // 8
-    for bad in [cass.CassParams(4, 3, 256, 10), cass.CassParams(1, 8, 256, 10),
+    for bad in [cass.CassParams(5, 3, 256, 10), cass.CassParams(1, 8, 256, 10),
                 cass.CassParams(1, 3, 100, 10), cass.CassParams(1, 3, 256, 5000),
                 cass.CassParams(1, 3, 16, 10)]:
         assert L.cass_encode_ws_bytes(16, 4096, ctypes.byref(bad), ctypes.byref(n)) == \
@@ -292,3 +292,26 @@ def test_prefix_argument_errors(cass):
     hist2[200] = 1
     with pytest.raises(cass.CassError):
         cass.cass_prefix_stream_bits(huff, hist2)
+
+
+def test_format4_validate_and_describe(cass, orc):
+    """Format 4 (superblock metadata): oracle streams validate and describe;
+    a moved superblock base, a wrong 16-bit offset or a wrong superblock-size
+    field is corrupt."""
+    w = synth.weight(12, 8192, 9, outlier_frac=0.01)
+    spec, verif = orc.encode(w, 2458, 3, fmt=4)
+    assert cass.cass_tensor_validate(spec, verif) == cass.CASS_OK
+    t = cass.cass_tensor_describe(spec.tobytes(), FakeDev(spec.size), verif.tobytes(),
+                                  FakeDev(verif.size))
+    assert (t.format, t.rows, t.cols) == (4, 12, 8192)
+    h = orc.header(spec)
+    sb_off, bo_off = h["sections"][2][0], h["sections"][3][0]
+    for pos in (sb_off + 8, bo_off + 2, 60):
+        bad = spec.copy()
+        bad[pos] ^= 1
+        assert cass.cass_tensor_validate(bad, verif) == cass.CASS_ERR_CORRUPT, pos
+    bad = spec.copy()
+    bad[60] = 8
+    with pytest.raises(cass.CassError):
+        cass.cass_tensor_describe(bad.tobytes(), FakeDev(spec.size), verif.tobytes(),
+                                  FakeDev(verif.size))
