@@ -257,9 +257,12 @@ def main():
     n_launch = args.steps * len(MATS)
     layer_ms = [sum(kern_ms[n][i] for n in MATS) for i in range(args.steps)]
     step_pct = {f"p{q}": round(float(np.percentile(layer_ms, q)) * 1e3, 2) for q in (10, 50, 90)}
-    ceiling = read_ceiling(torch, stream)
-    avg_launch_ms = sum_ms / n_launch
+    ceiling = read_ceiling(torch, cass, stream)
+    # the kernel's mean launch time over the timed region (HIP events on the
+    # launch stream around all steps; launches are back to back)
+    avg_launch_ms = total_ms / (args.steps * len(MATS))
     achieved = alg_bytes / n_launch / (avg_launch_ms * 1e-3) / 1e9
+    trace = trace_summary()
     per_matrix = {n: {"spec_MB": round(spec_bytes[n] / 1e6, 3),
                       "avg_us": round(1e3 * float(np.mean(kern_ms[n])), 2),
                       "GB_s": round(spec_bytes[n] / (float(np.mean(kern_ms[n])) * 1e-3) / 1e9, 1)}
@@ -310,8 +313,11 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic_from_profile(),
-            "kernel": "k_gemv_c1_bal<1, 8>",
+            "kernel": trace["kernel"],
             "avg_launch_us": round(avg_launch_ms * 1e3, 3),
+            "avg_launch_us_per_launch_events": round(sum_ms / n_launch * 1e3, 3),
+            "profile_avg_launch_us": trace["avg_us"],
+            "profile_on_current_sources": trace["sources_match"],
             "algorithmic_bytes_per_launch": round(alg_bytes / n_launch),
         },
         "valu_ceiling": valu_from_profile(step_pct["p50"]),
@@ -319,6 +325,10 @@ def main():
         "cpu_baseline": cpu,
         "cpu_baseline_1core": cpu1,
     }
+    result["inputs_sha256"] = input_digest([layers[0][n] for n in MATS] + [xs[n] for n in MATS])
+    if not args.no_extras:
+        result["worked_config_1024_cache_resident"] = cache_resident_row(torch, cass, synth, dev16,
+                                                                         timer, stream)
     result.update(extras)
     print(json.dumps(result))
 
@@ -826,21 +836,23 @@ def run_dense_stack(torch, synth, nl=32):
     return res
 
 
-def read_ceiling(torch, stream):
-    """Achievable HBM read rate of a plain streaming read on this GPU: torch's
-    sum over a 2 GiB fp32 tensor (one read of every byte), best of 5."""
+def read_ceiling(torch, cass, stream):
+    """Achievable HBM read rate on this GPU: the library's streaming-read kernel
+    (cass_stream_read: 16-byte nontemporal loads, four in flight per lane, one
+    word per workgroup written) over 2 GiB, best of 6; a 1 GiB device copy as
+    context (bytes read plus bytes written)."""
     t = torch.ones(1 << 29, dtype=torch.float32, device="cuda")
+    fold = torch.empty((cass.CASS_STREAM_READ_BLOCKS,), dtype=torch.int32, device="cuda")
     best = None
     for _ in range(6):
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record(stream)
-        t.sum()
+        cass.cass_stream_read(t, fold, stream)
         b.record(stream)
         torch.cuda.synchronize()
         ms = a.elapsed_time(b)
         best = ms if best is None else min(best, ms)
     gbs = t.numel() * 4 / (best * 1e-3) / 1e9
-    # a device copy of 1 GiB: bytes read plus bytes written per second
     src = t.view(torch.uint8)[: 1 << 30]
     dst = torch.empty_like(src)
     cbest = None
@@ -856,12 +868,78 @@ def read_ceiling(torch, stream):
     del t, src, dst
     torch.cuda.empty_cache()
     return {"GB_s": round(gbs, 1), "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
-            "kernel": "torch sum over 2 GiB fp32 (best of 6)",
+            "kernel": "k_stream_read (cass_stream_read) over 2 GiB, best of 6",
             "copy_read_plus_write_GB_s": round(copy_gbs, 1),
             "copy_pct_hbm_peak": round(100 * copy_gbs / HBM_PEAK_GBS, 2)}
 
 
+def host_facts():
+    """nproc and the CPU model of the host the benchmark runs on."""
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"nproc": os.cpu_count(), "cpu_model": model}
+
+
+def input_digest(tensors):
+    """SHA-256 over the bytes of the generated inputs, in order."""
+    import hashlib
+    h = hashlib.sha256()
+    for t in tensors:
+        h.update(t.cpu().numpy().tobytes())
+    return h.hexdigest()
+
+
+def trace_summary():
+    """Kernel name and mean launch time of the GEMV from the committed
+    rocprofv3 kernel-trace summary, and whether it was taken on the current
+    kernel sources."""
+    path = os.path.join(ROOT, "profiles", "draft_gemv_llama8b_layer_kernel_trace.txt")
+    out = {"kernel": None, "avg_us": None, "sources_match": False}
+    if not os.path.exists(path):
+        return out
+    f = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            f[k.strip()] = v.strip()
+    out["kernel"] = f.get("kernel")
+    try:
+        out["avg_us"] = float(f["gemv_avg_launch_us"])
+    except (KeyError, ValueError):
+        pass
+    out["sources_match"] = profile_fields("draft_gemv_llama8b_layer_kernel_trace.txt") is not None
+    return out
+
+
+def cache_resident_row(torch, cass, synth, dev16, timer, stream):
+    """The 1024 x 1024 worked configuration (keep 0.5, m 3, Cassandra-1): it
+    fits in the last-level cache, so its rate is not an HBM figure."""
+    w = synth.weight(1024, 1024, 1_000_001)
+    enc = cass.encode(dev16(w), 512, 3)
+    x = dev16(synth.activations(1, 1024, 1))
+    y = torch.empty((1, 1024), dtype=torch.float32, device="cuda")
+    X = dev16(synth.activations(5, 1024, 1, t0=1))
+    Y = torch.empty((5, 1024), dtype=torch.float32, device="cuda")
+    out = torch.empty((1024, 1024), dtype=torch.int16, device="cuda")
+    g = timer.ms(lambda: cass.cass_draft_gemv(enc.desc, x, y, stream), 50)
+    v = timer.ms(lambda: cass.cass_verify_gemm(enc.desc, X, Y, stream), 20)
+    r = timer.ms(lambda: cass.cass_reconstruct(enc.desc, out, stream), 20)
+    return {"note": "cache-resident (1024 x 1024 bf16, 0.3 MB of speculation bytes): not an HBM rate",
+            "spec_bytes": enc.spec_bytes, "draft_gemv_us": round(g * 1e3, 2),
+            "draft_gemv_GB_s": round(enc.spec_bytes / (g * 1e-3) / 1e9, 1),
+            "verify_gemm_n5_us": round(v * 1e3, 2), "reconstruct_us": round(r * 1e3, 2)}
+
+
 def cpu_baseline(args, synth, layer0, threads=None, seconds=None):
+    """The oracle's draft product on a row sample, on the host's cores: 16
+    threads (the host share of one GPU of this machine) or fewer if the host
+    has fewer."""
     import oracle
     threads = threads or max(1, min(16, os.cpu_count() or 1))
     seconds = seconds or args.cpu_seconds
@@ -880,6 +958,7 @@ def cpu_baseline(args, synth, layer0, threads=None, seconds=None):
             break
     dt = time.time() - t_start
     return {"value": round(done / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "host": host_facts(),
             "sample": "every 16th row of each fused matrix of layer 0, encoded by the oracle; the "
                       "oracle's draft product (decode + fp64 multiply-accumulate) repeated for "
                       f"{dt:.1f} s"}

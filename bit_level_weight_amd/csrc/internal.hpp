@@ -136,6 +136,7 @@ enum Option {
   OPT_GEMV_SUB,        // lanes per block of the staged kernel's sub-split
   OPT_EXACT_PATH,      // 1: per-thread stream readers for verify/reconstruct
   OPT_EXACT_BLOCKS,    // blocks per stage of the staged exact decoder (1 or 2)
+  OPT_KV_EXACT_PATH,   // 1: per-thread decoders for Cassandra-1 verification attention
   OPT_COUNT
 };
 int option(Option o);

@@ -1045,6 +1045,292 @@ __global__ void __launch_bounds__(128 * kMergeParts) k_kv_merge(AttnArgs a, int 
   }
 }
 
+// ---- verification attention, Cassandra-1: split decode, matrix-core products ----
+// One workgroup of 16 waves per (KV head, chunk of 128 tokens).
+//  1. The chunk's sections of K and V are copied to shared memory with
+//     coalesced loads: fields, low mantissas, pruned bytes, and the
+//     speculation and pruned-exponent code runs (a run longer than its staged
+//     space is read in place).
+//  2. Each of the 1024 threads rebuilds 32 exact values: one keep-bitmap word
+//     of one token of K or V.  Its kept and pruned values start at indices the
+//     popcounts of the token's earlier words give, so its fields, low mantissas
+//     and pruned bytes sit at known bit positions, and its codes start after
+//     that many one bits of the token's code runs (every unary code ends with
+//     its one bit).  Values go to K and V tiles in shared memory.
+//  3. Scores S = Q K^T for up to 32 query rows on the matrix cores
+//     (v_mfma_f32_16x16x16_bf16: bf16 inputs are exact, sums in fp32), scaled
+//     and masked (causal over the appended block).
+//  4. Softmax per row over the chunk; o = p V on the matrix cores with p split
+//     into two bf16 terms (p = hi + lo to about 2^-17 relative), fp32 sums;
+//     written as a chunk partial (row maximum, sum, numerator) for k_kv_merge.
+constexpr int kXThreads = 1024;
+constexpr int kXRows = 32;
+constexpr int kXStride = 132;  // bf16 per tile row (8-byte aligned rows, banks shifted by 2 words)
+
+typedef short xv4s __attribute__((ext_vector_type(4)));
+typedef float xv4f __attribute__((ext_vector_type(4)));
+
+// Staged words per stream of the split-decode attention.
+struct XCaps {
+  int scode, pcode;     // speculation / pruned-exponent code runs
+  int field, low, pbyte;  // fields, low mantissas, pruned bytes
+  __host__ __device__ int per_stream() const { return scode + pcode + field + low + pbyte; }
+};
+
+__host__ __device__ __forceinline__ int64_t x1_lds_bytes(const XCaps& cp) {
+  return (int64_t)2 * kChunk * kXStride * 2 + (int64_t)kXRows * kChunk * 4 +
+         (int64_t)2 * cp.per_stream() * 4;
+}
+
+// bf16 bits of x rounded to nearest even (x finite).
+__device__ __forceinline__ uint32_t x1_bf16_rne(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+__global__ void __launch_bounds__(kXThreads) k_kv_attn_x1(KvDev kv, AttnArgs a, XCaps cp) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  uint16_t* kt = reinterpret_cast<uint16_t*>(smem);          // [128][kXStride] keys
+  uint16_t* vt = kt + kChunk * kXStride;                       // [128][kXStride] values
+  float* sc = reinterpret_cast<float*>(vt + kChunk * kXStride);  // [32][128] scores, then p
+  uint32_t* stg = reinterpret_cast<uint32_t*>(sc + kXRows * kChunk);  // staged sections
+  __shared__ uint8_t tabs[4][256];  // rank tables: K spec, K verif, V spec, V verif
+  __shared__ long long cfirst[2][2];  // first staged code word [stream][spec | pruned], -1: in place
+  __shared__ float rmax[kXRows], rsum[kXRows];
+  const int h = blockIdx.x, c = blockIdx.y;
+  const int rows = a.nq * a.G;
+  const int tid = threadIdx.x;
+  const int k = kv.k, m = kv.m, np = kDim - kv.k;
+  const int64_t t0 = (int64_t)c * kChunk;
+  const int64_t t1 = t0 + kChunk < a.T ? t0 + kChunk : a.T;  // tokens of the chunk: [t0, t1)
+  const int psw = cp.per_stream();
+  // staged words of stream j: codes (spec, pruned), fields, low mantissas, pruned bytes
+  auto sbase = [&](int j) { return stg + j * psw; };
+  const int64_t fw0 = (t0 * k * (1 + m)) >> 5, lw0 = (t0 * k * (7 - m)) >> 5, bw0 = (t0 * np) >> 2;
+  for (int i = tid; i < 4 * 256; i += kXThreads) {
+    const int s = 2 * h + (i >> 9), which = (i >> 8) & 1;
+    const uint8_t* src = which ? kv.verif + s * kv.vstride + kv.vo[0] : kv.spec + s * kv.sstride + kv.so[0];
+    tabs[i >> 8][i & 255] = src[i & 255];
+  }
+  // 1. code runs of the chunk: [offset of t0, offset of t1 or the stream tail)
+  if (tid < 4) {
+    const int j = tid >> 1, which = tid & 1;
+    const int s = 2 * h + j;
+    const uint32_t* offs = reinterpret_cast<const uint32_t*>(
+        which ? kv.verif + s * kv.vstride + kv.vo[3] : kv.spec + s * kv.sstride + kv.so[2]);
+    const uint32_t b0 = offs[t0];
+    const unsigned long long b1 = t1 < kv.T_max && t1 < a.T ? (unsigned long long)offs[t1]
+                                                            : kv.state[2 + 2 * s + which];
+    const int cap = which ? cp.pcode : cp.scode;
+    long long first = -1;
+    if (b0 != 0xFFFFFFFFu && b1 != 0xFFFFFFFFull && b1 >= b0 &&
+        (long long)((b1 + 31) >> 5) + 4 - (long long)(b0 >> 5) <= cap)
+      first = (long long)(b0 >> 5);
+    cfirst[j][which] = first;
+  }
+  __syncthreads();
+  for (int j = 0; j < 2; ++j) {
+    const int s = 2 * h + j;
+    const uint8_t* sr = kv.spec + s * kv.sstride;
+    const uint8_t* vr = kv.verif + s * kv.vstride;
+    uint32_t* b = sbase(j);
+    for (int which = 0; which < 2; ++which) {
+      const long long first = cfirst[j][which];
+      if (first < 0) continue;
+      const uint32_t* src = reinterpret_cast<const uint32_t*>(which ? vr + kv.vo[4] : sr + kv.so[4]);
+      const int64_t lim = ((which ? kv.vcap : kv.ccap) + 31) / 32 + 4;  // plus the zero pad
+      copy_words(b + (which ? cp.scode : 0), src, first, which ? cp.pcode : cp.scode, lim, tid,
+                 kXThreads);
+    }
+    b += cp.scode + cp.pcode;
+    copy_words(b, reinterpret_cast<const uint32_t*>(sr + kv.so[3]), fw0, cp.field,
+               (kv.T_max * k * (1 + m) + 31) / 32 + 4, tid, kXThreads);
+    b += cp.field;
+    copy_words(b, reinterpret_cast<const uint32_t*>(vr + kv.vo[1]), lw0, cp.low,
+               (kv.T_max * k * (7 - m) + 31) / 32 + 4, tid, kXThreads);
+    b += cp.low;
+    copy_words(b, reinterpret_cast<const uint32_t*>(vr + kv.vo[2]), bw0, cp.pbyte,
+               (kv.T_max * np + 3) / 4 + 4, tid, kXThreads);
+  }
+  __syncthreads();
+
+  // 2. exact values: thread = (stream j, token, keep word w)
+  {
+    const int j = tid >> 9, tl = (tid >> 2) & (kChunk - 1), w = tid & 3;
+    const int64_t tok = t0 + tl;
+    uint16_t* row = (j ? vt : kt) + tl * kXStride + w * 32;
+    if (tok >= t1) {
+      for (int i = 0; i < 32; ++i) row[i] = 0;
+    } else {
+      const int s = 2 * h + j;
+      const uint8_t* sr = kv.spec + s * kv.sstride;
+      const uint8_t* vr = kv.verif + s * kv.vstride;
+      const uint32_t* bmp = reinterpret_cast<const uint32_t*>(sr + kv.so[1]) + tok * (kDim / 32);
+      const uint32_t wd0 = bmp[0], wd1 = bmp[1], wd2 = bmp[2], wd3 = bmp[3];
+      const uint32_t word = w == 0 ? wd0 : w == 1 ? wd1 : w == 2 ? wd2 : wd3;
+      const int kb = (w > 0 ? __builtin_popcount(wd0) : 0) + (w > 1 ? __builtin_popcount(wd1) : 0) +
+                     (w > 2 ? __builtin_popcount(wd2) : 0);
+      const int pb = 32 * w - kb;
+      const uint32_t* base = sbase(j);
+      const uint32_t* fl = base + cp.scode + cp.pcode;
+      const uint32_t* ll = fl + cp.field;
+      const uint8_t* bl = reinterpret_cast<const uint8_t*>(ll + cp.low);
+      const int64_t kin = (int64_t)tok * k + kb;
+      uint32_t fpos = (uint32_t)(kin * (1 + m) - fw0 * 32);
+      uint32_t lpos = (uint32_t)(kin * (7 - m) - lw0 * 32);
+      uint32_t bpos = (uint32_t)((int64_t)tok * np + pb - bw0 * 4);
+      // code runs: from the staged copy, or in place (a token whose codes did
+      // not fit the stream reads from bit 0: meaningless values, reads inside)
+      const uint32_t* cw[2];
+      uint32_t cpos[2];
+      for (int which = 0; which < 2; ++which) {
+        const uint32_t* offs = reinterpret_cast<const uint32_t*>(
+            which ? vr + kv.vo[3] : sr + kv.so[2]);
+        uint32_t off = offs[tok];
+        off = off == 0xFFFFFFFFu ? 0u : off;
+        const long long first = cfirst[j][which];
+        if (first >= 0) {
+          cw[which] = base + (which ? cp.scode : 0);
+          cpos[which] = off - (uint32_t)first * 32u;
+        } else {
+          cw[which] = reinterpret_cast<const uint32_t*>(which ? vr + kv.vo[4] : sr + kv.so[4]);
+          cpos[which] = off;
+        }
+      }
+      cpos[0] = skip_codes(cw[0], cpos[0], kb);
+      cpos[1] = skip_codes(cw[1], cpos[1], pb);
+      const uint8_t* ps = tabs[2 * j];
+      const uint8_t* pv = tabs[2 * j + 1];
+      const uint32_t fmask = (2u << m) - 1u, lmask = (1u << (7 - m)) - 1u;
+      for (uint32_t km = word; km; km &= km - 1u) {
+        const uint32_t f = window32(fl, fpos) & fmask;
+        const uint32_t lo = window32(ll, lpos) & lmask;
+        fpos += 1 + m;
+        lpos += 7 - m;
+        const int r = unary_at(cw[0], cpos[0]);
+        const uint32_t e = ps[r & 255];
+        row[__builtin_ctz(km)] = (uint16_t)(((f >> m) << 15) | (e << 7) |
+                                            ((f & ((1u << m) - 1u)) << (7 - m)) | lo);
+      }
+      for (uint32_t pm = ~word; pm; pm &= pm - 1u) {
+        const uint32_t byte = bl[bpos++];
+        const int r = unary_at(cw[1], cpos[1]);
+        const uint32_t e = pv[r & 255];
+        row[__builtin_ctz(pm)] = (uint16_t)(((byte >> 7) << 15) | (e << 7) | (byte & 0x7F));
+      }
+    }
+  }
+  __syncthreads();
+
+  const int lane = tid & 63, wv = tid >> 6;
+  const int rg = wv >> 3, cg = wv & 7;  // 16-row group, 16-column group (tokens, then dims)
+  const int i16 = lane & 15, kq = lane >> 4;
+  // 3. scores: lane (i16, kq) feeds query row / token i16 of its group and
+  // dimensions 4kq..4kq+3 of each 16-dimension step
+  {
+    const int r = rg * 16 + i16;
+    const uint16_t* qrow = nullptr;
+    if (r < rows) {
+      const int qi = r / a.G, g = r % a.G;
+      qrow = a.q + ((int64_t)qi * a.Hq + h * a.G + g) * kDim;
+    }
+    const uint32_t* krow = reinterpret_cast<const uint32_t*>(kt + (cg * 16 + i16) * kXStride);
+    xv4f acc = xv4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < kDim / 16; ++ks) {
+      xv4s aop = xv4s{0, 0, 0, 0};
+      if (qrow) {
+        const uint16_t* qp = qrow + ks * 16 + 4 * kq;
+        aop = xv4s{(short)qp[0], (short)qp[1], (short)qp[2], (short)qp[3]};
+      }
+      const uint32_t b0 = krow[ks * 8 + 2 * kq], b1 = krow[ks * 8 + 2 * kq + 1];
+      const xv4s bop = xv4s{(short)(b0 & 0xFFFF), (short)(b0 >> 16), (short)(b1 & 0xFFFF),
+                            (short)(b1 >> 16)};
+      acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(aop, bop, acc, 0, 0, 0);
+    }
+    // D: this lane holds rows rg*16 + 4kq + e, token cg*16 + i16
+    const int64_t tok = t0 + cg * 16 + i16;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int rr = rg * 16 + 4 * kq + e;
+      if (rr < rows) {
+        const int qi = rr / a.G;
+        const bool vis = tok < t1 && tok < a.T - a.nq + qi + 1;
+        sc[rr * kChunk + cg * 16 + i16] = vis ? acc[e] * a.scale : -INFINITY;
+      }
+    }
+  }
+  __syncthreads();
+
+  // 4a. softmax per row: 32 threads per row, 4 tokens each
+  {
+    const int r = tid >> 5, q = tid & 31;
+    if (r < rows) {
+      float* srow = sc + r * kChunk;
+      float v0 = srow[q], v1 = srow[q + 32], v2 = srow[q + 64], v3 = srow[q + 96];
+      float mx = fmaxf(fmaxf(v0, v1), fmaxf(v2, v3));
+#pragma unroll
+      for (int o = 16; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+      const bool none = mx == -INFINITY;
+      v0 = none || v0 == -INFINITY ? 0.f : __expf(v0 - mx);
+      v1 = none || v1 == -INFINITY ? 0.f : __expf(v1 - mx);
+      v2 = none || v2 == -INFINITY ? 0.f : __expf(v2 - mx);
+      v3 = none || v3 == -INFINITY ? 0.f : __expf(v3 - mx);
+      srow[q] = v0;
+      srow[q + 32] = v1;
+      srow[q + 64] = v2;
+      srow[q + 96] = v3;
+      float l = (v0 + v1) + (v2 + v3);
+#pragma unroll
+      for (int o = 16; o >= 1; o >>= 1) l += __shfl_xor(l, o, 64);
+      if (q == 0) {
+        rmax[r] = mx;
+        rsum[r] = l;
+      }
+    }
+  }
+  __syncthreads();
+  // 4b. o = p V: lane (i16, kq) feeds row i16 of p and column i16 of V (dims of
+  // its group), tokens 4kq..4kq+3 of each 16-token step; p = hi + lo in bf16
+  {
+    const int r = rg * 16 + i16;
+    const float* prow = sc + r * kChunk;
+    const int dcol = cg * 16 + i16;
+    xv4f acc = xv4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 2
+    for (int ks = 0; ks < kChunk / 16; ++ks) {
+      const int tb = ks * 16 + 4 * kq;
+      uint32_t hi[4], lo[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float p = r < rows ? prow[tb + u] : 0.f;
+        hi[u] = x1_bf16_rne(p);
+        lo[u] = x1_bf16_rne(p - __uint_as_float(hi[u] << 16));
+      }
+      const xv4s ahi = xv4s{(short)hi[0], (short)hi[1], (short)hi[2], (short)hi[3]};
+      const xv4s alo = xv4s{(short)lo[0], (short)lo[1], (short)lo[2], (short)lo[3]};
+      const xv4s bop = xv4s{(short)vt[(tb + 0) * kXStride + dcol], (short)vt[(tb + 1) * kXStride + dcol],
+                            (short)vt[(tb + 2) * kXStride + dcol], (short)vt[(tb + 3) * kXStride + dcol]};
+      acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ahi, bop, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(alo, bop, acc, 0, 0, 0);
+    }
+    // D: this lane holds rows rg*16 + 4kq + e, dimension cg*16 + i16
+    float* part = a.part + (((int64_t)h * a.nchunks + c) * rows) * (2 + kDim);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int rr = rg * 16 + 4 * kq + e;
+      if (rr < rows) {
+        float* pr = part + (int64_t)rr * (2 + kDim);
+        pr[2 + dcol] = acc[e];
+        if (dcol == 0) {
+          pr[0] = rmax[rr];
+          pr[1] = rsum[rr];
+        }
+      }
+    }
+  }
+}
+
 int64_t aln256(int64_t v) { return (v + 255) / 256 * 256; }
 int64_t part_at(int64_t* pos, int64_t bytes) {
   const int64_t o = *pos;
@@ -1202,6 +1488,28 @@ int run_attention(const cass_kv* kv, const uint16_t* q, int nq, int n_q_heads, f
   const KvDev d = dev_of(kv);
   const size_t lds = 0;  // per launch, from the row bound (attn_launch_f)
   const int rows = nq * G;
+  if (exact && d.fmt == CASS_FMT_C1_UNARY && option(OPT_KV_EXACT_PATH) != 1) {
+    // split decode and matrix-core scores; staged code space averaging up to
+    // 4 bits per value (longer runs are read in place)
+    const int64_t kk = kv->p.keep, mm = kv->p.mant_bits;
+    XCaps cp;
+    cp.scode = (int)((kChunk * kk * 4 + 31) / 32) + 64;
+    cp.pcode = (int)((kChunk * (kDim - kk) * 4 + 31) / 32) + 64;
+    cp.field = (int)((kChunk * kk * (1 + mm) + 31) / 32) + 8;  // (a run may start mid-word)
+    cp.low = (int)((kChunk * kk * (7 - mm) + 31) / 32) + 8;
+    cp.pbyte = (int)((kChunk * (kDim - kk) + 3) / 4) + 8;
+    const int64_t xl = x1_lds_bytes(cp);
+    hipError_t e = hipFuncSetAttribute((const void*)&k_kv_attn_x1,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)xl);
+    if (e == hipSuccess) {
+      k_kv_attn_x1<<<dim3(H, a.nchunks), kXThreads, (size_t)xl, stream>>>(d, a, cp);
+      e = hipGetLastError();
+    }
+    if (e != hipSuccess) return report(CASS_ERR_HIP, "attention: %s", hipGetErrorString(e));
+    k_kv_merge<<<H * nq * G, kDim * kMergeParts, 0, stream>>>(a, H, out);
+    if ((e = hipGetLastError()) != hipSuccess) return report(CASS_ERR_HIP, "merge: %s", hipGetErrorString(e));
+    return CASS_OK;
+  }
   // row bounds: one query of 4 heads (draft), 5 queries of 4 heads (verify), ...
   // (the 20-row instance of the exact Cassandra-2 kernel gave results that
   // changed from run to run in workgroups sharing a CU with another one, and

@@ -418,6 +418,8 @@ int cass_version(void);
  *   "gemv_sub"     lanes per block of the staged kernel
  *   "exact_path"   1: per-thread stream readers for verification/reconstruction
  *   "exact_blocks" blocks per stage of the staged exact decoder, 1 or 2
+ *   "kv_exact_path" 1: per-thread decoders for Cassandra-1 verification
+ *                  attention (default: split decode, matrix-core scores)
  * Unknown names or values out of range give CASS_ERR_INVALID.  Not
  * synchronised with launches in flight on other threads. */
 int cass_set_option(const char* name, int64_t value);
