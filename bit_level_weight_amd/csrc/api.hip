@@ -569,7 +569,8 @@ int cass_set_option(const char* name, int64_t value) {
   static const struct { const char* name; Option o; int64_t lo, hi; } table[] = {
       {"gemv_parts", OPT_GEMV_PARTS, 0, 64}, {"gemv_path", OPT_GEMV_PATH, 0, 2},
       {"gemv_sub", OPT_GEMV_SUB, 0, 64},     {"exact_path", OPT_EXACT_PATH, 0, 1},
-      {"exact_blocks", OPT_EXACT_BLOCKS, 0, 2}, {"kv_exact_path", OPT_KV_EXACT_PATH, 0, 1}};
+      {"exact_blocks", OPT_EXACT_BLOCKS, 0, 2}, {"kv_exact_path", OPT_KV_EXACT_PATH, 0, 1},
+      {"kv_append_path", OPT_KV_APPEND_PATH, 0, 1}};
   if (!name) return fail(CASS_ERR_INVALID, "option name is NULL");
   for (const auto& t : table)
     if (strcmp(name, t.name) == 0) {

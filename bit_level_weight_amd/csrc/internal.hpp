@@ -137,6 +137,7 @@ enum Option {
   OPT_EXACT_PATH,      // 1: per-thread stream readers for verify/reconstruct
   OPT_EXACT_BLOCKS,    // blocks per stage of the staged exact decoder (1 or 2)
   OPT_KV_EXACT_PATH,   // 1: per-thread decoders for Cassandra-1 verification attention
+  OPT_KV_APPEND_PATH,  // 1: the five-launch append for any token count
   OPT_COUNT
 };
 int option(Option o);

@@ -53,6 +53,40 @@ __device__ __forceinline__ const uint16_t* vec_ptr(const uint16_t* kk, const uin
 }
 
 // ---- append, step 1: top-k of each vector (one wave per vector) ----
+// Keep bits of vector x of stream s into bm[0 .. D/32) (lane 0 writes), and on
+// the first append its exponents into the stream's histograms.  keys: the
+// wave's shared-memory scratch of D entries.
+__device__ __forceinline__ void vec_select(const KvDev& kv, const uint16_t* x, int s, int first,
+                                           const AppendWs& ws, uint16_t* keys, uint32_t* bm,
+                                           int lane) {
+  for (int j = lane; j < kv.D; j += 64) keys[j] = x[j];
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  for (int c = 0; c < kv.D / 64 + ((kv.D % 64) ? 1 : 0); ++c) {
+    const int j = c * 64 + lane;
+    bool keep = false;
+    if (j < kv.D) {
+      const int kj = key_of(keys[j]);
+      int rank = 0;  // values ordered before j: larger |x|, or equal and lower index
+      for (int i = 0; i < kv.D; ++i) {
+        const int ki = key_of(keys[i]);
+        rank += (ki > kj) || (ki == kj && i < j);
+      }
+      keep = rank < kv.k;
+      if (first) {
+        const int e = (keys[j] >> 7) & 0xFF;
+        atomicAdd(ws.hist + s * 512 + (keep ? 0 : 256) + e, 1u);
+      }
+    }
+    const unsigned long long mask = __ballot(keep);
+    if (lane == 0) {
+      const int w0 = c * 2;
+      if (w0 < kv.D / 32) bm[w0] = (uint32_t)mask;
+      if (w0 + 1 < kv.D / 32) bm[w0 + 1] = (uint32_t)(mask >> 32);
+    }
+  }
+}
+
 __global__ void __launch_bounds__(64 * kWaves) k_kv_select(KvDev kv, const uint16_t* kk,
                                                            const uint16_t* vv, int ntok, int first,
                                                            AppendWs ws) {
@@ -65,34 +99,8 @@ __global__ void __launch_bounds__(64 * kWaves) k_kv_select(KvDev kv, const uint1
   const int64_t th = vi >> 1;
   const int h = (int)(th % kv.H);
   const int64_t t = th / kv.H;
-  const int s = 2 * h + kind;
-  const uint16_t* x = vec_ptr(kk, vv, t, h, kind, kv.H, kv.D);
-  for (int j = lane; j < kv.D; j += 64) keys[wv][j] = x[j];
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  for (int c = 0; c < kv.D / 64 + ((kv.D % 64) ? 1 : 0); ++c) {
-    const int j = c * 64 + lane;
-    bool keep = false;
-    if (j < kv.D) {
-      const int kj = key_of(keys[wv][j]);
-      int rank = 0;  // values ordered before j: larger |x|, or equal and lower index
-      for (int i = 0; i < kv.D; ++i) {
-        const int ki = key_of(keys[wv][i]);
-        rank += (ki > kj) || (ki == kj && i < j);
-      }
-      keep = rank < kv.k;
-      if (first) {
-        const int e = (keys[wv][j] >> 7) & 0xFF;
-        atomicAdd(ws.hist + s * 512 + (keep ? 0 : 256) + e, 1u);
-      }
-    }
-    const unsigned long long mask = __ballot(keep);
-    if (lane == 0) {
-      const int w0 = c * 2;
-      if (w0 < kv.D / 32) ws.bm[vi * (kv.D / 32) + w0] = (uint32_t)mask;
-      if (w0 + 1 < kv.D / 32) ws.bm[vi * (kv.D / 32) + w0 + 1] = (uint32_t)(mask >> 32);
-    }
-  }
+  vec_select(kv, vec_ptr(kk, vv, t, h, kind, kv.H, kv.D), 2 * h + kind, first, ws, keys[wv],
+             ws.bm + vi * (kv.D / 32), lane);
 }
 
 // ---- append, step 2 (first append only): rank tables from the histograms ----
@@ -127,8 +135,8 @@ __device__ __forceinline__ void load_ranks(const KvDev& kv, int s, uint8_t* rs, 
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-__device__ __forceinline__ bool kept_bit(const AppendWs& ws, int64_t vi, int D, int j) {
-  return (ws.bm[vi * (D / 32) + (j >> 5)] >> (j & 31)) & 1u;
+__device__ __forceinline__ bool kept_bit(const uint32_t* bm, int j) {
+  return (bm[j >> 5] >> (j & 31)) & 1u;
 }
 
 __device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
@@ -160,6 +168,36 @@ __device__ __forceinline__ int group_shexp(bool kept, int e) {
 }
 
 // ---- append, step 3: code bits of each vector ----
+// Speculation (C-1) or residue (C-2) code bits, and pruned-code bits, of
+// vector x with keep bits bm (rs / rv: the stream's inverse rank tables);
+// the same in every lane.
+__device__ __forceinline__ void vec_lengths(const KvDev& kv, const uint16_t* x, const uint32_t* bm,
+                                            const uint8_t* rs, const uint8_t* rv, int lane,
+                                            uint32_t& a_out, uint32_t& b_out) {
+  uint32_t a = 0, b = 0;
+  if (kv.fmt == CASS_FMT_C1_UNARY) {
+    for (int j = lane; j < kv.D; j += 64) {
+      const int e = (x[j] >> 7) & 0xFF;
+      if (kept_bit(bm, j)) a += rs[e] + 1u;
+      else b += rv[e] + 1u;
+    }
+  } else {
+    // Cassandra-2: a kept value's residue is unary(d) and min(8, 7-m+d) bits
+    for (int c0 = 0; c0 < kv.D; c0 += 64) {
+      const int j = c0 + lane;
+      const bool in = j < kv.D;
+      const int e = in ? (x[j] >> 7) & 0xFF : 0;
+      const bool kept = in && kept_bit(bm, j);
+      const int d = group_shexp(kept, e) - (e > 0 ? e : 1);
+      const int w = 7 - kv.m + d < 8 ? 7 - kv.m + d : 8;
+      if (kept) a += (uint32_t)(d + 1 + w);
+      else if (in) b += rv[e] + 1u;
+    }
+  }
+  a_out = wave_sum(a);
+  b_out = wave_sum(b);
+}
+
 __global__ void __launch_bounds__(64 * kWaves) k_kv_lengths(KvDev kv, const uint16_t* kk,
                                                             const uint16_t* vv, int ntok,
                                                             AppendWs ws) {
@@ -173,29 +211,9 @@ __global__ void __launch_bounds__(64 * kWaves) k_kv_lengths(KvDev kv, const uint
   const int64_t t = (vi >> 1) / kv.H;
   const int s = 2 * h + kind;
   load_ranks(kv, s, rs[wv], rv[wv], lane);
-  const uint16_t* x = vec_ptr(kk, vv, t, h, kind, kv.H, kv.D);
-  uint32_t a = 0, b = 0;
-  if (kv.fmt == CASS_FMT_C1_UNARY) {
-    for (int j = lane; j < kv.D; j += 64) {
-      const int e = (x[j] >> 7) & 0xFF;
-      if (kept_bit(ws, vi, kv.D, j)) a += rs[wv][e] + 1u;
-      else b += rv[wv][e] + 1u;
-    }
-  } else {
-    // Cassandra-2: a kept value's residue is unary(d) and min(8, 7-m+d) bits
-    for (int c0 = 0; c0 < kv.D; c0 += 64) {
-      const int j = c0 + lane;
-      const bool in = j < kv.D;
-      const int e = in ? (x[j] >> 7) & 0xFF : 0;
-      const bool kept = in && kept_bit(ws, vi, kv.D, j);
-      const int d = group_shexp(kept, e) - (e > 0 ? e : 1);
-      const int w = 7 - kv.m + d < 8 ? 7 - kv.m + d : 8;
-      if (kept) a += (uint32_t)(d + 1 + w);
-      else if (in) b += rv[wv][e] + 1u;
-    }
-  }
-  a = wave_sum(a);
-  b = wave_sum(b);
+  uint32_t a, b;
+  vec_lengths(kv, vec_ptr(kk, vv, t, h, kind, kv.H, kv.D), ws.bm + vi * (kv.D / 32), rs[wv], rv[wv],
+              lane, a, b);
   if (lane == 0) {
     ws.lens[2 * vi] = a;
     ws.lens[2 * vi + 1] = b;
@@ -265,29 +283,15 @@ __device__ __forceinline__ void or_bits(uint8_t* sec, uint64_t pos, uint32_t v, 
 }
 
 // ---- append, step 5: pack (one wave per vector) ----
-__global__ void __launch_bounds__(64 * kWaves) k_kv_pack(KvDev kv, const uint16_t* kk,
-                                                         const uint16_t* vv, int ntok, int64_t t0,
-                                                         AppendWs ws) {
-  __shared__ uint8_t rs[kWaves][256], rv[kWaves][256];
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int64_t nvec = (int64_t)ntok * 2 * kv.H;
-  const int64_t vi = (int64_t)blockIdx.x * kWaves + wv;
-  if (vi >= nvec) return;
-  const int kind = (int)(vi & 1);
-  const int h = (int)((vi >> 1) % kv.H);
-  const int64_t i = (vi >> 1) / kv.H;
-  const int s = 2 * h + kind;
-  const int64_t tok = t0 + i;
-  load_ranks(kv, s, rs[wv], rv[wv], lane);
-  const uint16_t* x = vec_ptr(kk, vv, i, h, kind, kv.H, kv.D);
+// Vector x (keep bits bm) as token tok of stream s; its codes start at bits
+// sstart / vstart of the code sections (0xFFFFFFFF: not written).
+__device__ __forceinline__ void vec_pack(const KvDev& kv, const uint16_t* x, const uint32_t* bm,
+                                         const uint8_t* rsw, const uint8_t* rvw, int s,
+                                         int64_t tok, uint32_t sstart, uint32_t vstart, int lane) {
   uint8_t* sr = kv.spec + s * kv.sstride;
   uint8_t* vr = kv.verif + s * kv.vstride;
   const int D = kv.D, k = kv.k, m = kv.m;
-  if (lane < D / 32) {
-    reinterpret_cast<uint32_t*>(sr + kv.so[1])[tok * (D / 32) + lane] =
-        ws.bm[vi * (D / 32) + lane];
-  }
-  const uint32_t sstart = ws.start[2 * vi], vstart = ws.start[2 * vi + 1];
+  if (lane < D / 32) reinterpret_cast<uint32_t*>(sr + kv.so[1])[tok * (D / 32) + lane] = bm[lane];
   uint32_t kept_carry = 0, scode_carry = 0, vcode_carry = 0;
   if (kv.fmt != CASS_FMT_C1_UNARY) {
     // Cassandra-2: shared exponents, aligned significands, residues
@@ -295,7 +299,7 @@ __global__ void __launch_bounds__(64 * kWaves) k_kv_pack(KvDev kv, const uint16_
       const int j = c0 + lane;
       const bool in = j < D;
       const uint16_t b = in ? x[j] : 0;
-      const bool kept = in && kept_bit(ws, vi, D, j);
+      const bool kept = in && kept_bit(bm, j);
       const int sgn = b >> 15, e = (b >> 7) & 0xFF, f = b & 0x7F;
       const int eff = e > 0 ? e : 1, M = ((e > 0) << 7) | f;
       const int E = group_shexp(kept, e);
@@ -307,7 +311,7 @@ __global__ void __launch_bounds__(64 * kWaves) k_kv_pack(KvDev kv, const uint16_
       const uint32_t pidx = (uint32_t)(c0 - kept_carry) +
                             (uint32_t)__builtin_popcountll(pm & ((1ull << lane) - 1ull));
       const uint32_t rlen = kept ? (uint32_t)(d + 1 + w) : 0u;
-      const uint32_t vlen = (in && !kept) ? rv[wv][e] + 1u : 0u;
+      const uint32_t vlen = (in && !kept) ? rvw[e] + 1u : 0u;
       const uint32_t rin = wave_incl_scan(rlen, lane), vin = wave_incl_scan(vlen, lane);
       if (in && (j & 31) == 0) (sr + kv.so[2])[tok * (D / 32) + j / 32] = (uint8_t)E;
       if (kept) {
@@ -335,15 +339,15 @@ __global__ void __launch_bounds__(64 * kWaves) k_kv_pack(KvDev kv, const uint16_
     const int j = c0 + lane;
     const bool in = j < D;
     const uint16_t b = in ? x[j] : 0;
-    const bool kept = in && kept_bit(ws, vi, D, j);
+    const bool kept = in && kept_bit(bm, j);
     const int sgn = b >> 15, e = (b >> 7) & 0xFF, f = b & 0x7F;
     const unsigned long long km = __ballot(kept);
     const unsigned long long pm = __ballot(in && !kept);
     const uint32_t kidx = kept_carry + (uint32_t)__builtin_popcountll(km & ((1ull << lane) - 1ull));
     const uint32_t pidx = (uint32_t)(c0 - kept_carry) +
                           (uint32_t)__builtin_popcountll(pm & ((1ull << lane) - 1ull));
-    const uint32_t slen = kept ? rs[wv][e] + 1u : 0u;
-    const uint32_t vlen = (in && !kept) ? rv[wv][e] + 1u : 0u;
+    const uint32_t slen = kept ? rsw[e] + 1u : 0u;
+    const uint32_t vlen = (in && !kept) ? rvw[e] + 1u : 0u;
     const uint32_t sin = wave_incl_scan(slen, lane), vin = wave_incl_scan(vlen, lane);
     if (kept) {
       const uint64_t kin = (uint64_t)tok * k + kidx;
@@ -363,6 +367,72 @@ __global__ void __launch_bounds__(64 * kWaves) k_kv_pack(KvDev kv, const uint16_
     kept_carry += (uint32_t)__builtin_popcountll(km);
     scode_carry += __shfl(sin, 63, 64);
     vcode_carry += __shfl(vin, 63, 64);
+  }
+}
+
+__global__ void __launch_bounds__(64 * kWaves) k_kv_pack(KvDev kv, const uint16_t* kk,
+                                                         const uint16_t* vv, int ntok, int64_t t0,
+                                                         AppendWs ws) {
+  __shared__ uint8_t rs[kWaves][256], rv[kWaves][256];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int64_t nvec = (int64_t)ntok * 2 * kv.H;
+  const int64_t vi = (int64_t)blockIdx.x * kWaves + wv;
+  if (vi >= nvec) return;
+  const int kind = (int)(vi & 1);
+  const int h = (int)((vi >> 1) % kv.H);
+  const int64_t i = (vi >> 1) / kv.H;
+  const int s = 2 * h + kind;
+  load_ranks(kv, s, rs[wv], rv[wv], lane);
+  vec_pack(kv, vec_ptr(kk, vv, i, h, kind, kv.H, kv.D), ws.bm + vi * (kv.D / 32), rs[wv], rv[wv], s,
+           t0 + i, ws.start[2 * vi], ws.start[2 * vi + 1], lane);
+}
+
+// ---- a few tokens in one launch: one wave per stream runs select, lengths,
+// code positions and packing for the stream's tokens in order (the rank tables
+// are frozen).  The same bytes, tails and flags as the five-launch path.
+constexpr int kFusedMaxTokens = 16;
+
+__global__ void __launch_bounds__(64) k_kv_append_few(KvDev kv, const uint16_t* kk,
+                                                      const uint16_t* vv, int ntok, int64_t t0,
+                                                      AppendWs ws) {
+  __shared__ uint16_t keys[256];
+  __shared__ uint32_t bm[8];
+  __shared__ uint8_t rs[256], rv[256];
+  const int s = blockIdx.x, h = s >> 1, kind = s & 1;
+  const int lane = threadIdx.x;
+  load_ranks(kv, s, rs, rv, lane);
+  const bool c1 = kv.fmt == CASS_FMT_C1_UNARY;
+  unsigned long long tail[2] = {kv.state[2 + 2 * s], kv.state[3 + 2 * s]};
+  const unsigned long long cap[2] = {(unsigned long long)kv.ccap, (unsigned long long)kv.vcap};
+  uint32_t* vofs = reinterpret_cast<uint32_t*>(kv.verif + s * kv.vstride + kv.vo[3]);
+  uint32_t* offs[2] = {c1 ? reinterpret_cast<uint32_t*>(kv.spec + s * kv.sstride + kv.so[2]) : vofs,
+                       c1 ? vofs : vofs + 1};
+  const int ostride = c1 ? 1 : 2;
+  bool over[2] = {false, false};
+  for (int i = 0; i < ntok; ++i) {
+    const uint16_t* x = vec_ptr(kk, vv, i, h, kind, kv.H, kv.D);
+    vec_select(kv, x, s, 0, ws, keys, bm, lane);
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    uint32_t len[2];
+    vec_lengths(kv, x, bm, rs, rv, lane, len[0], len[1]);
+    uint32_t start[2];
+    for (int which = 0; which < 2; ++which) {
+      const bool fits = tail[which] + len[which] <= cap[which];
+      start[which] = fits ? (uint32_t)tail[which] : 0xFFFFFFFFu;
+      if (!fits) over[which] = true;
+      tail[which] += len[which];
+      if (lane == 0) offs[which][(t0 + i) * ostride] = start[which];
+    }
+    vec_pack(kv, x, bm, rs, rv, s, t0 + i, start[0], start[1], lane);
+    __builtin_amdgcn_wave_barrier();  // the next token's select rewrites keys and bm
+  }
+  if (lane == 0) {
+    // on overflow the stream is closed, as in the five-launch path
+    if (over[0] || over[1]) atomicOr(kv.state + 1, (unsigned long long)CASS_KV_FLAG_OVERFLOW);
+    kv.state[2 + 2 * s] = over[0] ? cap[0] : tail[0];
+    kv.state[3 + 2 * s] = over[1] ? cap[1] : tail[1];
+    if (s == 0) kv.state[0] += (unsigned long long)ntok;
   }
 }
 
@@ -1632,6 +1702,13 @@ int cass_kv_append_encode(cass_kv* kv, const uint16_t* k, const uint16_t* v, int
   const int first = kv->tokens == 0;
   const int64_t nvec = (int64_t)ntok * 2 * kv->p.n_kv_heads;
   hipError_t e;
+  if (!first && ntok <= kFusedMaxTokens && option(OPT_KV_APPEND_PATH) != 1) {
+    // a decoding step's few tokens: one launch, one wave per stream
+    k_kv_append_few<<<2 * kv->p.n_kv_heads, 64, 0, stream>>>(d, k, v, ntok, kv->tokens, w);
+    if ((e = hipGetLastError()) != hipSuccess) return report(CASS_ERR_HIP, "append: %s", hipGetErrorString(e));
+    kv->tokens += ntok;
+    return CASS_OK;
+  }
   if (first && (e = launch_fill_zero(w.hist, (int64_t)2 * kv->p.n_kv_heads * 512 * 4, stream)) != hipSuccess)
     return report(CASS_ERR_HIP, "append: %s", hipGetErrorString(e));
   k_kv_select<<<grid_of(nvec, kWaves), 64 * kWaves, 0, stream>>>(d, k, v, ntok, first, w);

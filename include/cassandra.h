@@ -420,6 +420,8 @@ int cass_version(void);
  *   "exact_blocks" blocks per stage of the staged exact decoder, 1 or 2
  *   "kv_exact_path" 1: per-thread decoders for Cassandra-1 verification
  *                  attention (default: split decode, matrix-core scores)
+ *   "kv_append_path" 1: the five-launch append also for appends of up to 16
+ *                  tokens (default there: one launch, one wave per stream)
  * Unknown names or values out of range give CASS_ERR_INVALID.  Not
  * synchronised with launches in flight on other threads. */
 int cass_set_option(const char* name, int64_t value);

@@ -258,3 +258,38 @@ def test_attention_long_context(gpu, orc, fmt, T):
         ref, bound = oracle_attention(orc, rows, Kt[:Ttot, h, :], Vt[:Ttot, h, :], scale, vis)
         gv = np.concatenate([gotv[:, h * G + g, :] for g in range(G)])
         attn_check(gv, ref, bound)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("caps", [None, (2600, 2600)])
+def test_kv_append_few_tokens_one_launch(gpu, orc, fmt, caps):
+    """Appends of up to 16 tokens run as one launch (one wave per stream); the
+    regions, tails, flags and token counts equal those of the five-launch path
+    step by step, with and without code capacities that overflow; and the
+    result equals the oracle's encoding."""
+    torch, cass = gpu
+    H, k, m, T0 = 4, 38, 3, 40
+    sizes = [1, 5, 3, 16, 17, 2]
+    T = T0 + sum(sizes)
+    Kt, Vt = make_kv(T, H, 321 + fmt)
+    kw = {} if caps is None else dict(code_cap_bits=caps[0], vcode_cap_bits=caps[1])
+    a = cass.KvCache(H, D, k, m, max_tokens=T + 8, fmt=fmt, **kw)
+    b = cass.KvCache(H, D, k, m, max_tokens=T + 8, fmt=fmt, **kw)
+    a.append(dev(torch, Kt[:T0]), dev(torch, Vt[:T0]))
+    b.append(dev(torch, Kt[:T0]), dev(torch, Vt[:T0]))
+    t = T0
+    for n in sizes:
+        a.append(dev(torch, Kt[t:t + n]), dev(torch, Vt[t:t + n]))
+        cass.cass_set_option("kv_append_path", 1)
+        try:
+            b.append(dev(torch, Kt[t:t + n]), dev(torch, Vt[t:t + n]))
+        finally:
+            cass.cass_set_option("kv_append_path", 0)
+        t += n
+        torch.cuda.synchronize()
+        assert torch.equal(a.spec, b.spec) and torch.equal(a.verif, b.verif), n
+        assert torch.equal(a.state, b.state), n
+    if caps is None:
+        check_regions(torch, a, orc, Kt, Vt, T0, k, m, fmt)
+    else:
+        assert cass.cass_kv_status(a.kv)[1] & cass.CASS_KV_FLAG_OVERFLOW
