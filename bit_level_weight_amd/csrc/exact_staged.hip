@@ -24,7 +24,7 @@
 // table read of the group plus the next group's window words (LDS only);
 // the values, written to their columns of a 16 x (Wb*B) bf16 tile.  The
 // verification GEMM multiplies the tile with the matching columns of X on the
-// matrix cores (v_mfma_f32_16x16x16_bf16, tokens padded to 16); the
+// matrix cores (v_mfma_f32_16x16x32_bf16, tokens padded to 16); the
 // reconstruction copies the tile rows to the output.
 #include <stdlib.h>
 
@@ -39,6 +39,8 @@ namespace {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef short v4s __attribute__((ext_vector_type(4)));
+typedef short v8s __attribute__((ext_vector_type(8)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) const uint8_t lds_u8c;
@@ -721,17 +723,22 @@ __global__ void __launch_bounds__(64 * kWaves) k_exact_staged(SpecViewC1 sv, Ver
     if (MODE == 0) {
       const int n = lane & 15, kq = lane >> 4;
       const int64_t col0 = bf * B;
-      for (int ks = 0; ks < nbs * (int)B / 16; ++ks) {
-        v4s bop = v4s{0, 0, 0, 0};
+      // v_mfma_f32_16x16x32_bf16: lane (n, kq) feeds tile row n and token n,
+      // columns 8kq..8kq+7 of each 32-column step
+      for (int ks = 0; ks < nbs * (int)B / 32; ++ks) {
+        v8s bop = v8s{0, 0, 0, 0, 0, 0, 0, 0};
         if (n < ntok) {
-          const uint16_t* xp = X + (int64_t)n * ldx + col0 + ks * 16 + 4 * kq;
-          bop = v4s{(short)xp[0], (short)xp[1], (short)xp[2], (short)xp[3]};
+          const uint16_t* xp = X + (int64_t)n * ldx + col0 + ks * 32 + 8 * kq;
+          bop = v8s{(short)xp[0], (short)xp[1], (short)xp[2], (short)xp[3],
+                    (short)xp[4], (short)xp[5], (short)xp[6], (short)xp[7]};
         }
-        const uint32_t ta = tileb + 2u * (uint32_t)(n * g.TS + ks * 16 + 4 * kq);
-        const uint32_t a0 = ldw(ta), a1 = ldw(ta + 4);
-        const v4s aop = v4s{(short)(a0 & 0xFFFF), (short)(a0 >> 16), (short)(a1 & 0xFFFF),
-                            (short)(a1 >> 16)};
-        acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(aop, bop, acc, 0, 0, 0);
+        const uint32_t ta = tileb + 2u * (uint32_t)(n * g.TS + ks * 32 + 8 * kq);
+        const uint32_t a0 = ldw(ta), a1 = ldw(ta + 4), a2 = ldw(ta + 8), a3 = ldw(ta + 12);
+        const v8s aop = v8s{(short)(a0 & 0xFFFF), (short)(a0 >> 16), (short)(a1 & 0xFFFF),
+                            (short)(a1 >> 16), (short)(a2 & 0xFFFF), (short)(a2 >> 16),
+                            (short)(a3 & 0xFFFF), (short)(a3 >> 16)};
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, aop),
+                                                      __builtin_bit_cast(v8bf, bop), acc, 0, 0, 0);
       }
     } else {
       const int cpr = nbs * (int)B / 8;  // 16-byte chunks per tile row

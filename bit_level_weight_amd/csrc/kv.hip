@@ -1128,7 +1128,7 @@ __global__ void __launch_bounds__(128 * kMergeParts) k_kv_merge(AttnArgs a, int 
 //     that many one bits of the token's code runs (every unary code ends with
 //     its one bit).  Values go to K and V tiles in shared memory.
 //  3. Scores S = Q K^T for up to 32 query rows on the matrix cores
-//     (v_mfma_f32_16x16x16_bf16: bf16 inputs are exact, sums in fp32), scaled
+//     (v_mfma_f32_16x16x32_bf16: bf16 inputs are exact, sums in fp32), scaled
 //     and masked (causal over the appended block).
 //  4. Softmax per row over the chunk; o = p V on the matrix cores with p split
 //     into two bf16 terms (p = hi + lo to about 2^-17 relative), fp32 sums;
@@ -1138,6 +1138,8 @@ constexpr int kXRows = 32;
 constexpr int kXStride = 132;  // bf16 per tile row (8-byte aligned rows, banks shifted by 2 words)
 
 typedef short xv4s __attribute__((ext_vector_type(4)));
+typedef short xv8s __attribute__((ext_vector_type(8)));
+typedef __bf16 xv8bf __attribute__((ext_vector_type(8)));
 typedef float xv4f __attribute__((ext_vector_type(4)));
 
 // Staged words per stream of the split-decode attention.
@@ -1296,7 +1298,7 @@ __global__ void __launch_bounds__(kXThreads) k_kv_attn_x1(KvDev kv, AttnArgs a, 
   const int rg = wv >> 3, cg = wv & 7;  // 16-row group, 16-column group (tokens, then dims)
   const int i16 = lane & 15, kq = lane >> 4;
   // 3. scores: lane (i16, kq) feeds query row / token i16 of its group and
-  // dimensions 4kq..4kq+3 of each 16-dimension step
+  // dimensions 8kq..8kq+7 of each 32-dimension step
   {
     const int r = rg * 16 + i16;
     const uint16_t* qrow = nullptr;
@@ -1307,16 +1309,20 @@ __global__ void __launch_bounds__(kXThreads) k_kv_attn_x1(KvDev kv, AttnArgs a, 
     const uint32_t* krow = reinterpret_cast<const uint32_t*>(kt + (cg * 16 + i16) * kXStride);
     xv4f acc = xv4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < kDim / 16; ++ks) {
-      xv4s aop = xv4s{0, 0, 0, 0};
+    for (int ks = 0; ks < kDim / 32; ++ks) {
+      xv8s aop = xv8s{0, 0, 0, 0, 0, 0, 0, 0};
       if (qrow) {
-        const uint16_t* qp = qrow + ks * 16 + 4 * kq;
-        aop = xv4s{(short)qp[0], (short)qp[1], (short)qp[2], (short)qp[3]};
+        const uint16_t* qp = qrow + ks * 32 + 8 * kq;
+        aop = xv8s{(short)qp[0], (short)qp[1], (short)qp[2], (short)qp[3],
+                   (short)qp[4], (short)qp[5], (short)qp[6], (short)qp[7]};
       }
-      const uint32_t b0 = krow[ks * 8 + 2 * kq], b1 = krow[ks * 8 + 2 * kq + 1];
-      const xv4s bop = xv4s{(short)(b0 & 0xFFFF), (short)(b0 >> 16), (short)(b1 & 0xFFFF),
-                            (short)(b1 >> 16)};
-      acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(aop, bop, acc, 0, 0, 0);
+      const uint32_t* kp = krow + ks * 16 + 4 * kq;
+      const uint32_t b0 = kp[0], b1 = kp[1], b2 = kp[2], b3 = kp[3];
+      const xv8s bop = xv8s{(short)(b0 & 0xFFFF), (short)(b0 >> 16), (short)(b1 & 0xFFFF),
+                            (short)(b1 >> 16), (short)(b2 & 0xFFFF), (short)(b2 >> 16),
+                            (short)(b3 & 0xFFFF), (short)(b3 >> 16)};
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(xv8bf, aop),
+                                                    __builtin_bit_cast(xv8bf, bop), acc, 0, 0, 0);
     }
     // D: this lane holds rows rg*16 + 4kq + e, token cg*16 + i16
     const int64_t tok = t0 + cg * 16 + i16;
@@ -1361,28 +1367,28 @@ __global__ void __launch_bounds__(kXThreads) k_kv_attn_x1(KvDev kv, AttnArgs a, 
   }
   __syncthreads();
   // 4b. o = p V: lane (i16, kq) feeds row i16 of p and column i16 of V (dims of
-  // its group), tokens 4kq..4kq+3 of each 16-token step; p = hi + lo in bf16
+  // its group), tokens 8kq..8kq+7 of each 32-token step; p = hi + lo in bf16
   {
     const int r = rg * 16 + i16;
     const float* prow = sc + r * kChunk;
     const int dcol = cg * 16 + i16;
     xv4f acc = xv4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll 2
-    for (int ks = 0; ks < kChunk / 16; ++ks) {
-      const int tb = ks * 16 + 4 * kq;
-      uint32_t hi[4], lo[4];
+    for (int ks = 0; ks < kChunk / 32; ++ks) {
+      const int tb = ks * 32 + 8 * kq;
+      xv8s ahi, alo, bop;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < 8; ++u) {
         const float p = r < rows ? prow[tb + u] : 0.f;
-        hi[u] = x1_bf16_rne(p);
-        lo[u] = x1_bf16_rne(p - __uint_as_float(hi[u] << 16));
+        const uint32_t hb = x1_bf16_rne(p);
+        ahi[u] = (short)hb;
+        alo[u] = (short)x1_bf16_rne(p - __uint_as_float(hb << 16));
+        bop[u] = (short)vt[(tb + u) * kXStride + dcol];
       }
-      const xv4s ahi = xv4s{(short)hi[0], (short)hi[1], (short)hi[2], (short)hi[3]};
-      const xv4s alo = xv4s{(short)lo[0], (short)lo[1], (short)lo[2], (short)lo[3]};
-      const xv4s bop = xv4s{(short)vt[(tb + 0) * kXStride + dcol], (short)vt[(tb + 1) * kXStride + dcol],
-                            (short)vt[(tb + 2) * kXStride + dcol], (short)vt[(tb + 3) * kXStride + dcol]};
-      acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ahi, bop, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(alo, bop, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(xv8bf, ahi),
+                                                    __builtin_bit_cast(xv8bf, bop), acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(xv8bf, alo),
+                                                    __builtin_bit_cast(xv8bf, bop), acc, 0, 0, 0);
     }
     // D: this lane holds rows rg*16 + 4kq + e, dimension cg*16 + i16
     float* part = a.part + (((int64_t)h * a.nchunks + c) * rows) * (2 + kDim);

@@ -9,7 +9,7 @@
 // Work split: one wave per (64 rows, range of blocks).  Each lane decodes one
 // row, 32 positions at a time, into an LDS tile of 64 x 32 bf16; the wave then
 // multiplies the tile with the matching 32 columns of X on the matrix cores
-// (v_mfma_f32_16x16x16_bf16, tokens padded to 16).  Partial sums over block
+// (v_mfma_f32_16x16x32_bf16, tokens padded to 16).  Partial sums over block
 // ranges are combined with fp32 atomics on Y, which the launcher zeroes first.
 #include "decoders.hpp"
 
@@ -18,6 +18,8 @@ namespace cass {
 namespace {
 
 typedef short v4s __attribute__((ext_vector_type(4)));
+typedef short v8s __attribute__((ext_vector_type(8)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ const uint8_t* spec_perm_of(const SpecViewC1& s) { return s.perm; }
@@ -79,20 +81,25 @@ __global__ void __launch_bounds__(64) k_verify(SV sv, VV vv, Shape sh,
       }
       __syncthreads();
       const int64_t col0 = b * sh.block + wi * 32;
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        v4s bop = v4s{0, 0, 0, 0};
+      // v_mfma_f32_16x16x32_bf16: lane (n, kq) feeds tile row n of each 16-row
+      // group and token n, columns 8kq..8kq+7 of the word's 32
+      {
+        v8s bop = v8s{0, 0, 0, 0, 0, 0, 0, 0};
         if (n < ntok) {
-          const uint16_t* xp = X + (int64_t)n * ldx + col0 + ks * 16 + 4 * kq;
-          bop = v4s{(short)xp[0], (short)xp[1], (short)xp[2], (short)xp[3]};
+          const uint16_t* xp = X + (int64_t)n * ldx + col0 + 8 * kq;
+          bop = v8s{(short)xp[0], (short)xp[1], (short)xp[2], (short)xp[3],
+                    (short)xp[4], (short)xp[5], (short)xp[6], (short)xp[7]};
         }
 #pragma unroll
         for (int rg = 0; rg < 4; ++rg) {
-          const uint32_t* tp = tile + (rg * 16 + n) * kTileStride + ks * 8 + 2 * kq;
-          const uint32_t a0 = tp[0], a1 = tp[1];
-          const v4s aop = v4s{(short)(a0 & 0xFFFF), (short)(a0 >> 16), (short)(a1 & 0xFFFF),
-                              (short)(a1 >> 16)};
-          acc[rg] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(aop, bop, acc[rg], 0, 0, 0);
+          const uint32_t* tp = tile + (rg * 16 + n) * kTileStride + 4 * kq;
+          const uint32_t a0 = tp[0], a1 = tp[1], a2 = tp[2], a3 = tp[3];
+          const v8s aop = v8s{(short)(a0 & 0xFFFF), (short)(a0 >> 16), (short)(a1 & 0xFFFF),
+                              (short)(a1 >> 16), (short)(a2 & 0xFFFF), (short)(a2 >> 16),
+                              (short)(a3 & 0xFFFF), (short)(a3 >> 16)};
+          acc[rg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, aop),
+                                                            __builtin_bit_cast(v8bf, bop), acc[rg],
+                                                            0, 0, 0);
         }
       }
       __syncthreads();
