@@ -514,6 +514,7 @@ def run_extras(args, torch, cass, synth, timer, stream, layers, encs, layer0, en
         b.record(stream)
         torch.cuda.synchronize()
         app_us = a.elapsed_time(b) * 1e3 / 64
+        app_gpu_us = append_graph_us(torch, cache, tokK, tokV)
         q1 = dev16(synth.activations(Hq, 128, 4, t0=T))
         wsa = torch.empty(cass.cass_kv_attn_ws_bytes(cache.kv, nq, Hq), dtype=torch.uint8, device="cuda")
         o1 = torch.empty((Hq, 128), dtype=torch.float32, device="cuda")
@@ -529,7 +530,9 @@ def run_extras(args, torch, cass, synth, timer, stream, layers, encs, layer0, en
         st = cache.state.cpu().numpy().view(np.int64)
         code_bytes = sum(int(st[2 + 2 * s]) for s in range(2 * H)) / 8
         attn_bytes = 2 * H * T * (128 / 8 + 4 + keep * (1 + mant) / 8) + code_bytes * T / tokens
-        kvres[f"T{T}"] = {"append_1tok_us": round(app_us, 2), "draft_attn_us": round(d_ms * 1e3, 1),
+        kvres[f"T{T}"] = {"append_1tok_us": round(app_gpu_us, 2),
+                          "append_1tok_us_eager": round(app_us, 2),
+                          "draft_attn_us": round(d_ms * 1e3, 1),
                           "draft_attn_spec_MB": round(attn_bytes / 1e6, 2),
                           "draft_attn_GB_s": round(attn_bytes / (d_ms * 1e-3) / 1e9, 1),
                           "verify_attn_n5_us": round(v_ms * 1e3, 1), "tokens": tokens,
@@ -554,6 +557,8 @@ def run_extras(args, torch, cass, synth, timer, stream, layers, encs, layer0, en
         cache.append(tokK[i], tokV[i])
     b.record(stream)
     torch.cuda.synchronize()
+    app_eager_us = a.elapsed_time(b) * 1e3 / 64
+    app_gpu_us = append_graph_us(torch, cache, tokK, tokV)
     q1 = dev16(synth.activations(Hq, 128, 5, t0=T))
     wsa = torch.empty(cass.cass_kv_attn_ws_bytes(cache.kv, 1, Hq), dtype=torch.uint8, device="cuda")
     o1 = torch.empty((Hq, 128), dtype=torch.float32, device="cuda")
@@ -562,7 +567,7 @@ def run_extras(args, torch, cass, synth, timer, stream, layers, encs, layer0, en
     # draft attention reads, per K|V stream and token: bitmap, shared exponents, fields
     attn_bytes = 2 * H * T * (128 / 8 + 128 / 32 + keep * (2 + mant) / 8)
     out["kv_cache_qwen3_4b_c2_128k"] = {
-        "append_1tok_us": round(a.elapsed_time(b) * 1e3 / 64, 2),
+        "append_1tok_us": round(app_gpu_us, 2), "append_1tok_us_eager": round(app_eager_us, 2),
         "draft_attn_us": round(d_ms * 1e3, 1), "draft_attn_spec_MB": round(attn_bytes / 1e6, 2),
         "draft_attn_GB_s": round(attn_bytes / (d_ms * 1e-3) / 1e9, 1), "tokens": tokens,
         "overflow": bool(flags & cass.CASS_KV_FLAG_OVERFLOW),
@@ -573,6 +578,44 @@ def run_extras(args, torch, cass, synth, timer, stream, layers, encs, layer0, en
     torch.cuda.empty_cache()
     log("qwen kv done")
     return out
+
+
+def append_graph_us(torch, cache, tokK, tokV, n=16, reps=7):
+    """GPU time of one single-token append: HIP graphs of n and of n/2
+    single-token appends, each followed by a truncation back to the starting
+    length; the difference of their replay times over n/2.  Graph replays run
+    back to back on the GPU, so host time (the binding's per-call cost, which
+    bounds the eager figure) does not enter."""
+    base = cache.tokens
+
+    def body(k):
+        s = torch.cuda.current_stream()
+        for i in range(k):
+            cache.append(tokK[i], tokV[i], s)
+        cache.truncate(base, s)
+
+    def replay_ms(g):
+        ms = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            g.replay()
+            b.record()
+            torch.cuda.synchronize()
+            ms.append(a.elapsed_time(b))
+        return float(np.median(ms))
+
+    t = []
+    for k in (n, n // 2):
+        body(k)  # warm: workspace sized, kernels loaded
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            body(k)
+        torch.cuda.synchronize()
+        t.append(replay_ms(g))
+        del g
+    return (t[0] - t[1]) * 1e3 / (n - n // 2)
 
 
 def run_mx_target(torch, cass, synth, timer, stream, dev16):

@@ -55,34 +55,62 @@ __device__ __forceinline__ const uint16_t* vec_ptr(const uint16_t* kk, const uin
 // ---- append, step 1: top-k of each vector (one wave per vector) ----
 // Keep bits of vector x of stream s into bm[0 .. D/32) (lane 0 writes), and on
 // the first append its exponents into the stream's histograms.  keys: the
-// wave's shared-memory scratch of D entries.
+// wave's shared-memory copy of the vector (D entries), which the later steps
+// of the fused append read instead of x.
+//
+// The kept values are the k largest keys |x| (15 bits), ties to the lower
+// index.  T, the k-th largest key, is found bit by bit from the top: a bit
+// stays set when at least k keys are >= the prefix with it (one ballot per
+// 64 keys per bit).  Then every key > T is kept, and of the keys equal to T
+// the first k - #(keys > T) in index order.
+constexpr int kSelChunks = 4;  // head_dim <= 256
+
 __device__ __forceinline__ void vec_select(const KvDev& kv, const uint16_t* x, int s, int first,
                                            const AppendWs& ws, uint16_t* keys, uint32_t* bm,
                                            int lane) {
-  for (int j = lane; j < kv.D; j += 64) keys[j] = x[j];
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  for (int c = 0; c < kv.D / 64 + ((kv.D % 64) ? 1 : 0); ++c) {
+  const int D = kv.D, nc = (D + 63) / 64;
+  int key[kSelChunks];
+#pragma unroll
+  for (int c = 0; c < kSelChunks; ++c) {
     const int j = c * 64 + lane;
-    bool keep = false;
-    if (j < kv.D) {
-      const int kj = key_of(keys[j]);
-      int rank = 0;  // values ordered before j: larger |x|, or equal and lower index
-      for (int i = 0; i < kv.D; ++i) {
-        const int ki = key_of(keys[i]);
-        rank += (ki > kj) || (ki == kj && i < j);
-      }
-      keep = rank < kv.k;
-      if (first) {
-        const int e = (keys[j] >> 7) & 0xFF;
-        atomicAdd(ws.hist + s * 512 + (keep ? 0 : 256) + e, 1u);
-      }
+    const bool in = c < nc && j < D;
+    const uint16_t b = in ? x[j] : (uint16_t)0;
+    if (in) keys[j] = b;
+    key[c] = in ? key_of(b) : -1;  // -1: no value, below every candidate
+  }
+  int T = 0;
+  for (int bit = 14; bit >= 0; --bit) {
+    const int cand = T | (1 << bit);
+    int cnt = 0;
+#pragma unroll
+    for (int c = 0; c < kSelChunks; ++c)
+      if (c < nc) cnt += __builtin_popcountll(__ballot(key[c] >= cand));
+    T = cnt >= kv.k ? cand : T;
+  }
+  int gt = 0;
+#pragma unroll
+  for (int c = 0; c < kSelChunks; ++c)
+    if (c < nc) gt += __builtin_popcountll(__ballot(key[c] > T));
+  const int need = kv.k - gt;  // keys equal to T that are kept
+  const unsigned long long below = (1ull << lane) - 1ull;
+  int ties = 0;
+#pragma unroll
+  for (int c = 0; c < kSelChunks; ++c) {
+    if (c >= nc) break;
+    const unsigned long long tm = __ballot(key[c] == T);
+    const int trank = ties + __builtin_popcountll(tm & below);
+    const bool keep = key[c] > T || (key[c] == T && trank < need);
+    ties += __builtin_popcountll(tm);
+    const int j = c * 64 + lane;
+    if (first && j < D) {
+      const int e = (keys[j] >> 7) & 0xFF;
+      atomicAdd(ws.hist + s * 512 + (keep ? 0 : 256) + e, 1u);
     }
     const unsigned long long mask = __ballot(keep);
     if (lane == 0) {
       const int w0 = c * 2;
-      if (w0 < kv.D / 32) bm[w0] = (uint32_t)mask;
-      if (w0 + 1 < kv.D / 32) bm[w0 + 1] = (uint32_t)(mask >> 32);
+      if (w0 < D / 32) bm[w0] = (uint32_t)mask;
+      if (w0 + 1 < D / 32) bm[w0 + 1] = (uint32_t)(mask >> 32);
     }
   }
 }
@@ -414,8 +442,11 @@ __global__ void __launch_bounds__(64) k_kv_append_few(KvDev kv, const uint16_t* 
     vec_select(kv, x, s, 0, ws, keys, bm, lane);
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // the vector is read from global memory once: the later steps take the
+    // shared-memory copy
+    const uint16_t* xs = keys;
     uint32_t len[2];
-    vec_lengths(kv, x, bm, rs, rv, lane, len[0], len[1]);
+    vec_lengths(kv, xs, bm, rs, rv, lane, len[0], len[1]);
     uint32_t start[2];
     for (int which = 0; which < 2; ++which) {
       const bool fits = tail[which] + len[which] <= cap[which];
@@ -424,7 +455,7 @@ __global__ void __launch_bounds__(64) k_kv_append_few(KvDev kv, const uint16_t* 
       tail[which] += len[which];
       if (lane == 0) offs[which][(t0 + i) * ostride] = start[which];
     }
-    vec_pack(kv, x, bm, rs, rv, s, t0 + i, start[0], start[1], lane);
+    vec_pack(kv, xs, bm, rs, rv, s, t0 + i, start[0], start[1], lane);
     __builtin_amdgcn_wave_barrier();  // the next token's select rewrites keys and bm
   }
   if (lane == 0) {

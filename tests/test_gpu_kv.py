@@ -75,6 +75,36 @@ def test_kv_append_one_call(gpu, orc, T, H, k, m, fmt):
 
 
 @pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("k", [1, 38, 127])
+def test_kv_select_ties(gpu, orc, fmt, k):
+    """Vectors whose magnitudes repeat (four distinct keys, mixed signs) and a
+    token whose keys are all equal: the top-k keeps ties by lower index, in the
+    first append and in single-token appends (the one-launch path), and the
+    regions equal the oracle's encoding."""
+    torch, cass = gpu
+    H, m, T0, T = 2, 3, 6, 10
+    rng = np.random.default_rng(900 + k + fmt)
+    mags = np.array([0x3F80, 0x3F00, 0x3E80, 0x3C00], dtype=np.uint16)  # 1, 1/2, 1/4, 2^-7
+
+    def tensor():
+        X = mags[rng.integers(0, 4, size=(T, H, D))]
+        X = X | (rng.integers(0, 2, size=(T, H, D)).astype(np.uint16) << 15)
+        X[3, 0, :] = 0x3F80
+        X[8, 1, :] = 0xBF00
+        return X.astype(np.uint16)
+
+    Kt, Vt = tensor(), tensor()
+    # (exponents first kept after the tables froze take long codes: room for them)
+    cache = cass.KvCache(H, D, k, m, max_tokens=T + 4, fmt=fmt, code_cap_bits=(T + 4) * D * 260,
+                         vcode_cap_bits=(T + 4) * D * 260)
+    cache.append(dev(torch, Kt[:T0]), dev(torch, Vt[:T0]))
+    for t in range(T0, T):
+        cache.append(dev(torch, Kt[t:t + 1]), dev(torch, Vt[t:t + 1]))
+    torch.cuda.synchronize()
+    check_regions(torch, cache, orc, Kt, Vt, T0, k, m, fmt)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
 def test_kv_token_at_a_time_equals_one_call(gpu, orc, fmt):
     """A first chunk of T0 tokens then single-token appends gives the bytes of
     one encoding with the tables of the first chunk."""
