@@ -229,15 +229,18 @@ __device__ __forceinline__ void kept_group(KRaw& w, uint32_t& bp, uint32_t& fp, 
 }
 
 // U <= kPU pruned values (positions: zero bits of the bitmap); MASKED as for
-// the kept groups.
-template <int U, bool MASKED>
+// the kept groups.  W32: the 32 positions at bp hold U pruned values for every
+// lane (pruned values are the dense ones), so the window never moves on to
+// its second word.
+template <int U, bool MASKED, bool W32 = false>
 __device__ __forceinline__ void pruned_group(PRaw& w, uint32_t& bp, uint32_t& yp, uint32_t& cp,
                                              uint32_t sb, uint32_t torg, uint32_t plutb,
                                              uint32_t dummy, int t) {
   static_assert(U <= 8, "pruned bytes come from two 32-bit windows");
+  static_assert(!(W32 && MASKED), "the 32-bit window serves full groups");
   const uint32_t sbit = bp & 31u;
   const uint32_t lo0 = ~__builtin_amdgcn_alignbit(w.q1, w.q0, sbit);
-  const uint32_t hi0 = ~__builtin_amdgcn_alignbit(w.q2, w.q1, sbit) | (MASKED ? 0x80000000u : 0u);
+  const uint32_t hi0 = W32 ? 0u : ~__builtin_amdgcn_alignbit(w.q2, w.q1, sbit) | (MASKED ? 0x80000000u : 0u);
   const uint32_t ysh = yp & 31u;
   const uint32_t ylo = __builtin_amdgcn_alignbit(w.y1, w.y0, ysh);
   const uint32_t yhi = __builtin_amdgcn_alignbit(w.y2, w.y1, ysh);
@@ -246,9 +249,11 @@ __device__ __forceinline__ void pruned_group(PRaw& w, uint32_t& bp, uint32_t& yp
   uint32_t lo = lo0, wc = wc0, p = 0, base = bp;
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    const bool z = lo == 0u;
-    lo = z ? hi0 : lo;
-    base = z ? bp + 32u : base;
+    if (!W32) {
+      const bool z = lo == 0u;
+      lo = z ? hi0 : lo;
+      base = z ? bp + 32u : base;
+    }
     p = (uint32_t)__builtin_ctz(lo);
     lo &= lo - 1u;
     const uint32_t r = (uint32_t)__builtin_ctz(MASKED ? wc | 0x80000000u : wc);
@@ -508,7 +513,8 @@ __global__ void __launch_bounds__(64 * kWaves) k_exact_staged(SpecViewC1 sv, Ver
     int64_t bias[kSec];
     int nsec[kSec];
     int inc_l[kSec];      // this lane's row: inclusive packed chunk count
-    int64_t d_l[kSec];    // and first source chunk - first packed chunk
+    int d_l[kSec];        // and first source chunk - first packed chunk (sections hold
+                          // fewer than 2^30 chunks, so the difference fits 32 bits)
     int foff = 0, coff = 0;
     bool overflow = false;
 #pragma unroll
@@ -534,7 +540,7 @@ __global__ void __launch_bounds__(64 * kWaves) k_exact_staged(SpecViewC1 sv, Ver
       nsec[sec] = (sec < 4 || !overflow) ? N : 0;
       bias[sec] = (int64_t)(off + 16 * pre) * 8 - c0 * 128;
       inc_l[sec] = incl;
-      d_l[sec] = c0 - pre;
+      d_l[sec] = (int)(c0 - pre);
     }
     {
       int off_f = wbase + g.fix_off, off_c = wbase + g.cod_off;
@@ -544,24 +550,22 @@ __global__ void __launch_bounds__(64 * kWaves) k_exact_staged(SpecViewC1 sv, Ver
         const int off = sec < 4 ? off_f : off_c;
         if (N > 0) {
           // the section's row table in scalars (lanes 0..15 hold rows 0..15)
-          int inc[16];
-          int64_t dd[16];
+          int inc[16], dd[16];
 #pragma unroll
           for (int q = 0; q < 16; ++q) {
             inc[q] = __builtin_amdgcn_readlane(inc_l[sec], q);
-            const uint32_t dlo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)d_l[sec], q);
-            const uint32_t dhi = (uint32_t)__builtin_amdgcn_readlane((int)(d_l[sec] >> 32), q);
-            dd[q] = (int64_t)(((uint64_t)dhi << 32) | dlo);
+            dd[q] = __builtin_amdgcn_readlane(d_l[sec], q);
           }
           for (int base = 0; base < N; base += 64) {
             const int c = base + lane;
             if (c < N) {
               // row of packed chunk c: past every row whose run ends at or before it
-              int64_t d = dd[0];
+              int d = dd[0];
 #pragma unroll
               for (int q = 0; q < 15; ++q) d = inc[q] <= c ? dd[q + 1] : d;
-              __builtin_amdgcn_global_load_lds((const void*)(sec_base[sec] + 16 * (c + d)),
-                                               (lds_void*)(smem + off + 16 * base), 16, 0, 2);
+              __builtin_amdgcn_global_load_lds(
+                  (const void*)(sec_base[sec] + 16 * (int64_t)(c + d)),
+                  (lds_void*)(smem + off + 16 * base), 16, 0, 2);
             }
           }
         }
@@ -689,7 +693,10 @@ __global__ void __launch_bounds__(64 * kWaves) k_exact_staged(SpecViewC1 sv, Ver
                            __builtin_popcount(~__builtin_amdgcn_alignbit(w.q2, w.q1, sbit));
           const int ncode = __builtin_popcount(__builtin_amdgcn_alignbit(w.c1, w.c0, cp & 31u));
           const bool ok = min(have, ncode) >= t;
-          if (__all(t == kPU && ok)) {
+          const int have32 = __builtin_popcount(~__builtin_amdgcn_alignbit(w.q1, w.q0, sbit));
+          if (__all(t == kPU && ncode >= kPU && have32 >= kPU)) {
+            pruned_group<kPU, false, true>(w, bp, yp, cp, sb, torg, plutb, dummy, kPU);
+          } else if (__all(t == kPU && ok)) {
             pruned_group<kPU, false>(w, bp, yp, cp, sb, torg, plutb, dummy, kPU);
           } else if (__all(ok)) {
             pruned_group<kPU, true>(w, bp, yp, cp, sb, torg, plutb, dummy, t);
@@ -879,6 +886,11 @@ hipError_t launch_staged(const SpecViewC1& sv, const VerifViewC1& vv, const Shap
 
 bool exact_staged_fits(const Shape& sh, const SpecViewC1& sv, const VerifViewC1& vv) {
   if (sh.block < 32 || sh.block % 32) return false;
+  // staged chunk indices are 32-bit: every section under 2^30 chunks of 16 bytes
+  const int64_t lim = (int64_t)1 << 32;  // in 32-bit words
+  if (sv.bitmap_limit >= lim || sv.fields_limit >= lim || sv.codes_limit >= lim ||
+      vv.lowmant_limit >= lim || vv.pruned_limit >= lim || vv.codes_limit >= lim)
+    return false;
   return make_xgeom(sh, sv, vv).lds_bytes <= kMaxLds;
 }
 
