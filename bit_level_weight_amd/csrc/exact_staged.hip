@@ -7,8 +7,10 @@
 // section 3.2 -- a unary exponent code is decoded by counting the zeros up to
 // its one; section 3.3 -- the keep bitmap is de-sparsified.
 //
-// Work split.  A workgroup is one wave and takes 16 rows; it walks their
-// columns in stages of Wb blocks.  A stage copies, for every row, the row's
+// Work split.  A workgroup takes 16 rows; each of its waves walks one range of
+// their columns in stages of Wb blocks, and the verification GEMM adds the
+// waves' products in wave order (no atomics: the result is the same on every
+// run).  A stage copies, for every row, the row's
 // range of each section -- bitmap, fields, low mantissas, pruned bytes and
 // both code sections -- into LDS by LDS DMA: per section the 16 runs are
 // packed back to back and every instruction moves 64 chunks of 16 bytes, so
@@ -49,7 +51,7 @@ typedef __attribute__((address_space(3))) uint16_t lds_u16;
 typedef __attribute__((address_space(3))) const uint32_t lds_u32c;
 
 constexpr int kRows = 16;   // rows per wave
-constexpr int kWaves = 4;   // waves per workgroup (sharing the rank tables)
+constexpr int kMaxWaves = 8;  // waves per workgroup: the same 16 rows, column ranges side by side
 constexpr int kSec = 6;     // bitmap, fields, low mantissas, pruned bytes, spec codes, verif codes
 constexpr int kPU = 6;      // pruned values per group (6 codes nearly always fit 32 bits)
 
@@ -57,7 +59,7 @@ struct XGeom {
   int Wb;                    // blocks per stage
   int TS;                    // u16 per tile row (Wb*B + 2)
   int64_t nstage, stages_per_split;
-  int nsplit;
+  int nsplit;                // waves per workgroup, one stage range each
   int perm_off, klut_off, plut_off, wave_off, wave_bytes;  // shared tables, wave regions
   int meta_off, dummy_off, tile_off;                       // inside a wave region
   int fix_off, fix_cap, cod_off, cod_cap, lds_bytes;
@@ -363,7 +365,7 @@ __device__ __forceinline__ uint32_t find_in_block(uint32_t wa, int nwb, int skip
 // MODE 0: verification GEMM into Y; 1: reconstruction; 2: zero-filled draft
 // (speculation stream only: vv is not read)
 template <int MODE, int KU, bool KLUT>
-__global__ void __launch_bounds__(64 * kWaves) k_exact_staged(SpecViewC1 sv, VerifViewC1 vv, Shape sh,
+__global__ void __launch_bounds__(64 * kMaxWaves) k_exact_staged(SpecViewC1 sv, VerifViewC1 vv, Shape sh,
                                                      XGeom g, const uint16_t* __restrict__ X,
                                                      int ntok, int64_t ldx,
                                                      float* __restrict__ Y, int64_t ldy,
@@ -383,12 +385,12 @@ __global__ void __launch_bounds__(64 * kWaves) k_exact_staged(SpecViewC1 sv, Ver
   uint16_t* klut = reinterpret_cast<uint16_t*>(smem + g.klut_off);
   uint16_t* plut = reinterpret_cast<uint16_t*>(smem + g.plut_off);
   // (tables shared by the workgroup's waves)
-  for (int i = threadIdx.x; i < 256; i += 64 * kWaves) {
+  for (int i = threadIdx.x; i < 256; i += blockDim.x) {
     ps[i] = sv.perm[i];
     pv[i] = MODE == 2 ? 0 : vv.perm[i];
   }
   if (KLUT) {
-    for (int i = threadIdx.x; i < (32 << fw); i += 64 * kWaves) {
+    for (int i = threadIdx.x; i < (32 << fw); i += blockDim.x) {
       const uint32_t f = (uint32_t)i & ((1u << fw) - 1u);
       klut[i] = (uint16_t)(((f >> m) << 15) | ((uint32_t)sv.perm[i >> fw] << 7) |
                            ((f & ((1u << m) - 1u)) << lw));
@@ -407,12 +409,14 @@ __global__ void __launch_bounds__(64 * kWaves) k_exact_staged(SpecViewC1 sv, Ver
   const uint32_t tileb = sb + wbase + g.tile_off;
 
   const int r = lane & 15, j = lane >> 4;
-  const int64_t row0 = ((int64_t)blockIdx.x * kWaves + wave) * kRows;
+  // the workgroup's waves share its 16 rows; wave w takes the w-th range of
+  // stages, and the verification GEMM sums the waves' products in wave order
+  const int64_t row0 = (int64_t)blockIdx.x * kRows;
   if (row0 >= R) return;
   const int64_t row = row0 + r;
   const bool row_ok = row < R;
   const int64_t rowc = row_ok ? row : R - 1;  // clamped for loads
-  const int64_t st0 = (int64_t)blockIdx.y * g.stages_per_split;
+  const int64_t st0 = (int64_t)wave * g.stages_per_split;
   const int64_t st1 = std::min<int64_t>(st0 + g.stages_per_split, g.nstage);
   const int64_t rbs = (int64_t)sv.rowbase[rowc];
   const int64_t rbv = MODE == 2 ? 0 : (int64_t)vv.rowbase[rowc];
@@ -764,26 +768,30 @@ __global__ void __launch_bounds__(64 * kWaves) k_exact_staged(SpecViewC1 sv, Ver
   }
 
   if (MODE == 0) {
-    // D[i][j]: this lane holds rows 4 kq + e of the 16, token n
-    const int n = lane & 15, kq = lane >> 4;
-    if (n < ntok) {
+    // the waves' partial products through shared memory (each wave's tile
+    // region), summed in wave order: the result does not depend on timing
+    float* part = reinterpret_cast<float*>(smem + g.wave_off + g.tile_off);
+    const int pstride = g.wave_bytes / 4;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int64_t rr = row0 + 4 * kq + e;
-        if (rr < R) {
-          if (g.nsplit == 1) Y[(int64_t)n * ldy + rr] = acc[e];
-          else atomicAdd(Y + (int64_t)n * ldy + rr, acc[e]);
+    for (int e = 0; e < 4; ++e) part[wave * pstride + 64 * e + lane] = acc[e];
+    __syncthreads();
+    if (wave == 0) {
+      float sum[4] = {0.f, 0.f, 0.f, 0.f};
+      for (int w = 0; w < g.nsplit; ++w) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sum[e] += part[w * pstride + 64 * e + lane];
+      }
+      // D[i][j]: this lane holds rows 4 kq + e of the 16, token n
+      const int n = lane & 15, kq = lane >> 4;
+      if (n < ntok) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int64_t rr = row0 + 4 * kq + e;
+          if (rr < R) Y[(int64_t)n * ldy + rr] = sum[e];
         }
       }
     }
   }
-}
-
-__global__ void __launch_bounds__(256) k_zero_y(float* Y, int ntok, int64_t rows, int64_t ldy) {
-  const int64_t n = (int64_t)ntok * rows;
-  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
-       i += (int64_t)gridDim.x * blockDim.x)
-    Y[(i / rows) * ldy + (i % rows)] = 0.f;
 }
 
 int a16(int64_t v) { return (int)((v + 15) / 16 * 16); }
@@ -828,7 +836,15 @@ XGeom make_xgeom(const Shape& sh, const SpecViewC1& sv, const VerifViewC1& vv) {
   g.cod_cap = (int)std::min<int64_t>(kRows * cod_row, 24 * 1024);
   w += g.cod_cap + 64;
   g.wave_bytes = (int)a16(w);
-  g.lds_bytes = (int)(o + kWaves * g.wave_bytes);
+  // waves per workgroup: as many stage ranges as shared memory holds, at most
+  // kMaxWaves; each takes an equal share of the row's stages
+  int64_t W = std::min<int64_t>(kMaxWaves, g.nstage);
+  while (W > 1 && o + W * g.wave_bytes > kMaxLds) --W;
+  if (W < 1) W = 1;
+  g.stages_per_split = (g.nstage + W - 1) / W;
+  g.nsplit = (int)((g.nstage + g.stages_per_split - 1) / g.stages_per_split);
+  if (g.nsplit < 1) g.nsplit = 1;
+  g.lds_bytes = (int)(o + (int64_t)g.nsplit * g.wave_bytes);
   return g;
 }
 
@@ -838,35 +854,16 @@ hipError_t launch_staged_t(const SpecViewC1& sv, const VerifViewC1& vv, const Sh
                            int64_t ldy, uint16_t* out, hipStream_t s) {
   auto kern = k_exact_staged<MODE, KU, KLUT>;
   if (g.lds_bytes > kMaxLds) return hipErrorInvalidValue;
-  int occ = 0;
   if (g.lds_bytes > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute((const void*)kern,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, g.lds_bytes);
     if (e != hipSuccess) return e;
   }
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, (const void*)kern, 64 * kWaves,
-                                                   (size_t)g.lds_bytes) != hipSuccess || occ < 1)
-    occ = 1;
-  const int64_t gx = (sh.rows + kRows * kWaves - 1) / (kRows * kWaves);
-  // about four workgroups per resident slot: the dispatcher hands them out as
-  // slots free up, which evens out the finish across CUs
-  const int64_t want = (int64_t)device_cu_count() * occ * 4;
-  int64_t nsplit = (want + gx - 1) / gx;
-  if (nsplit > g.nstage) nsplit = g.nstage;
-  if (nsplit < 1) nsplit = 1;
-  g.stages_per_split = (g.nstage + nsplit - 1) / nsplit;
-  nsplit = (g.nstage + g.stages_per_split - 1) / g.stages_per_split;
-  g.nsplit = (int)nsplit;
-  if (MODE == 0 && nsplit > 1) {
-    int64_t gz = ((int64_t)ntok * sh.rows + 255) / 256;
-    if (gz > 4096) gz = 4096;
-    k_zero_y<<<(unsigned)gz, 256, 0, s>>>(Y, ntok, sh.rows, ldy);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  kern<<<dim3((unsigned)gx, (unsigned)nsplit), 64 * kWaves, (size_t)g.lds_bytes, s>>>(sv, vv, sh, g, X,
-                                                                            ntok, ldx, Y, ldy,
-                                                                            out);
+  // one workgroup per 16 rows; its g.nsplit waves take the stage ranges, so
+  // every output element is written once, by one wave
+  const int64_t gx = (sh.rows + kRows - 1) / kRows;
+  kern<<<dim3((unsigned)gx), 64 * g.nsplit, (size_t)g.lds_bytes, s>>>(sv, vv, sh, g, X, ntok, ldx,
+                                                                    Y, ldy, out);
   return hipGetLastError();
 }
 

@@ -218,6 +218,29 @@ def test_exact_paths(gpu, orc, opt, path):
         check_product(Y.cpu().numpy(), Y_ref, absY)
 
 
+def test_verify_gemm_repeatable(gpu, orc):
+    """The staged verification GEMM (Cassandra-1) splits a row's columns over
+    the waves of one workgroup and adds their partial sums in wave order, so
+    repeated calls give bit-identical outputs, within the product tolerance of
+    the oracle."""
+    torch, cass = gpu
+    fmt = 1
+    R, C, k, m, B = 200, 4096, 1229, 3, 256
+    w = make_w(R, C, 77 + fmt)
+    spec_o, verif_o = orc.encode(w, k, m, block=B, fmt=fmt)
+    enc = cass.encode(dev(torch, w), k, m, block=B, fmt=fmt)
+    X = dev(torch, synth.activations(5, C, 3, t0=fmt))
+    outs = []
+    for _ in range(3):
+        Y = torch.full((5, R), float("nan"), dtype=torch.float32, device="cuda")
+        cass.cass_verify_gemm(enc.desc, X, Y)
+        torch.cuda.synchronize()
+        outs.append(Y.cpu().numpy())
+    assert all(np.array_equal(outs[0].view(np.uint32), o.view(np.uint32)) for o in outs[1:])
+    Y_ref, absY = orc.product(spec_o, synth.activations(5, C, 3, t0=fmt), verif=verif_o, threads=4)
+    check_product(outs[0], Y_ref, absY)
+
+
 @pytest.mark.parametrize("fmt", [1, 2])
 def test_direct_gemv_path(gpu, orc, opt, fmt):
     """The direct (non-staged) GEMV kernels, selected with the gemv_path option."""
