@@ -732,9 +732,9 @@ def codec_compare(torch, cass, timer, stream, sym):
 def run_superblock(torch, cass, timer, stream, layer, xs):
     """Cassandra-1 with superblock metadata (format 4) against the flat
     metadata (format 1) on one Llama-3-8B-shaped layer (keep 0.3, m 3):
-    speculation bits per value, metadata bits per value, and the draft GEMV of
-    the per-thread stream-reader kernel (the one format 4 runs on) for both,
-    with format 1's default kernel as context."""
+    speculation bits per value, metadata bits per value, and the draft GEMV
+    time per layer of both formats on the default (balanced) kernel and on the
+    per-thread stream-reader kernel."""
     import synth
     res = {}
     n_values = sum(layer[n].numel() for n in MATS)
@@ -757,10 +757,13 @@ def run_superblock(torch, cass, timer, stream, layer, xs):
             res[name]["draft_gemv_direct_kernel_ms_per_layer"] = round(ms, 4)
     finally:
         cass.cass_set_option("gemv_path", 0)
-    e = enc["flat"]
-    res["flat"]["draft_gemv_default_kernel_ms_per_layer"] = round(
-        sum(timer.ms(lambda n=n: cass.cass_draft_gemv(e[n].desc, xs[n], ys_of(torch, e[n]), stream), 10)
-            for n in MATS), 4)
+    for name in ("flat", "superblock"):
+        e = enc[name]
+        ms = sum(timer.ms(lambda n=n: cass.cass_draft_gemv(e[n].desc, xs[n], ys_of(torch, e[n]),
+                                                           stream), 20) for n in MATS)
+        res[name]["draft_gemv_default_kernel_ms_per_layer"] = round(ms, 4)
+        res[name]["draft_gemv_default_GB_s"] = round(
+            sum(e[n].spec_bytes for n in MATS) / (ms * 1e-3) / 1e9, 1)
     res["spec_bytes_saved_pct"] = round(
         100 * (1 - res["superblock"]["spec_bits_per_value"] / res["flat"]["spec_bits_per_value"]), 3)
     del enc

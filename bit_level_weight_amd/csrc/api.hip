@@ -206,7 +206,7 @@ SpecViewC1 spec_c1(const cass_tensor* W) {
                     (const uint32_t*)(b + o[S1_FIELDS]), (const uint32_t*)(b + o[S1_CODES]),
                     word_limit(W->spec_bytes, o[S1_BITMAP]), word_limit(W->spec_bytes, o[S1_FIELDS]),
                     word_limit(W->spec_bytes, o[S1_CODES]), word_limit(W->spec_bytes, o[S1_BLKOFF]),
-                    2 * word_limit(W->spec_bytes, o[S1_KEPTB]), nullptr, nullptr, -1, 0};
+                    2 * word_limit(W->spec_bytes, o[S1_KEPTB]), nullptr, nullptr, -1, 0, 0};
 }
 // Format 4: the row-base / block-offset sections hold superblock bases and
 // 16-bit block offsets.
@@ -220,6 +220,7 @@ SpecViewC1 spec_c1s(const cass_tensor* W) {
   v.blkoff = nullptr;
   v.sb_log = 4;
   v.nsb = (nb + CASS_SUPERBLOCK_BLOCKS - 1) / CASS_SUPERBLOCK_BLOCKS;
+  v.sbbase_limit = word_limit(W->spec_bytes, W->spec_sec[S1_ROWBASE]) / 2;
   return v;
 }
 VerifViewC1 verif_c1(const cass_tensor* W) {
@@ -593,9 +594,11 @@ int cass_draft_gemv(const cass_tensor* W, const uint16_t* x, int batch, int64_t 
   if (!x || !y) return fail(CASS_ERR_INVALID, "x or y is NULL");
   if (ldx < W->cols || ldy < W->rows) return fail(CASS_ERR_INVALID, "ldx < cols or ldy < rows");
   const Shape sh = shape_of(W);
-  const int64_t code_limit = W->format == CASS_FMT_C1_UNARY ? spec_c1(W).codes_limit : 0;
-  const bool staged_ok = W->format != CASS_FMT_C1_SUPERBLOCK &&
-                         draft_gemv_staged_fits(sh, batch, W->format, code_limit);
+  const int64_t code_limit = is_c1_format(W->format) ? spec_c1(W).codes_limit : 0;
+  const bool staged_ok =
+      W->format == CASS_FMT_C1_SUPERBLOCK
+          ? draft_gemv_bal_fits(sh, batch, code_limit, spec_c1s(W).nsb)
+          : draft_gemv_staged_fits(sh, batch, W->format, code_limit);
   if (!staged_ok && draft_gemv_direct_lds_bytes(sh, batch) > 150 * 1024)
     return fail(CASS_ERR_UNSUPPORTED, "batch %d x cols %lld does not fit in LDS", batch,
                 (long long)W->cols);
@@ -603,7 +606,7 @@ int cass_draft_gemv(const cass_tensor* W, const uint16_t* x, int batch, int64_t 
       W->format == CASS_FMT_C1_UNARY
           ? launch_draft_gemv_c1(spec_c1(W), sh, x, batch, ldx, y, ldy, stream)
       : W->format == CASS_FMT_C1_SUPERBLOCK
-          ? launch_draft_gemv_c1_direct(spec_c1s(W), sh, x, batch, ldx, y, ldy, stream)
+          ? launch_draft_gemv_c1(spec_c1s(W), sh, x, batch, ldx, y, ldy, stream)
           : launch_draft_gemv_c2(spec_c2(W), sh, x, batch, ldx, y, ldy, stream);
   return e == hipSuccess ? CASS_OK : hip_fail(e, "draft gemv launch");
 }

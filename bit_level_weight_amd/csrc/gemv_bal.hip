@@ -58,6 +58,7 @@ struct BalGeom {
   int lut_off;          // LDS byte offsets (x at 0)
   int wave_off, wave_bytes;
   int kb_off, bo_off, bm_off, f_off, c_off;  // inside a wave region
+  int sb_off;           // inside a wave region: superblock code bases (format 4)
   int perm_off;         // inside a wave region: the wave's copy of the rank table (C-1)
   int c_cap;            // code words a wave region holds
   int lds_bytes;
@@ -269,7 +270,9 @@ struct Part {
   int64_t cabs;  // absolute code bit of the part's first value
 };
 
-template <int BATCH, int U>
+// SB: format 4 -- a u64 code base per superblock of 16 blocks and u16 block
+// offsets from it, in place of the u64 row base and u32 block offsets.
+template <int BATCH, int U, bool SB>
 __global__ void __launch_bounds__(kBalThreads) k_gemv_c1_bal(SpecViewC1 v, Shape sh, BalGeom g,
                                                              const uint16_t* __restrict__ x,
                                                              int64_t ldx, float* __restrict__ y,
@@ -286,6 +289,9 @@ __global__ void __launch_bounds__(kBalThreads) k_gemv_c1_bal(SpecViewC1 v, Shape
   uint8_t* reg = smem + g.wave_off + wave * g.wave_bytes;
   uint16_t* kb_l = reinterpret_cast<uint16_t*>(reg + g.kb_off);
   uint32_t* bo_l = reinterpret_cast<uint32_t*>(reg + g.bo_off);
+  uint16_t* bo16_l = reinterpret_cast<uint16_t*>(reg + g.bo_off);
+  unsigned long long* sb_l = reinterpret_cast<unsigned long long*>(reg + g.sb_off);
+  const int64_t nsb = SB ? v.nsb : 0;
   uint32_t* bm_l = reinterpret_cast<uint32_t*>(reg + g.bm_off);
   uint32_t* f_l = reinterpret_cast<uint32_t*>(reg + g.f_off);
   uint32_t* c_l = reinterpret_cast<uint32_t*>(reg + g.c_off);
@@ -305,7 +311,7 @@ __global__ void __launch_bounds__(kBalThreads) k_gemv_c1_bal(SpecViewC1 v, Shape
   struct Plan {
     int64_t row0;
     int rows_here;
-    int kb_sh, bo_sh;             // entries before the round's first one in the staged kb / bo
+    int kb_sh, bo_sh, sb_sh;      // entries before the round's first one in the staged kb / bo / sb
     int64_t bm_a0, f_a0, c_a0;    // first staged word of bitmap, fields and codes
     bool c_in_lds;
   };
@@ -314,7 +320,8 @@ __global__ void __launch_bounds__(kBalThreads) k_gemv_c1_bal(SpecViewC1 v, Shape
     pl.row0 = round * g.rpw;
     pl.rows_here = (int)((R - pl.row0 < g.rpw) ? R - pl.row0 : g.rpw);
     pl.kb_sh = (int)((pl.row0 * nb) & 7);
-    pl.bo_sh = (int)((pl.row0 * nb) & 3);
+    pl.bo_sh = (int)((pl.row0 * nb) & (SB ? 7 : 3));
+    pl.sb_sh = SB ? (int)((pl.row0 * nsb) & 1) : 0;
     pl.bm_a0 = (pl.row0 * wpr) & ~(int64_t)3;
     pl.f_a0 = ((pl.row0 * k * fw) >> 5) & ~(int64_t)3;
     pl.c_a0 = 0;
@@ -327,9 +334,20 @@ __global__ void __launch_bounds__(kBalThreads) k_gemv_c1_bal(SpecViewC1 v, Shape
     const int64_t kb1 = std::min<int64_t>((e1 + 7) & ~(int64_t)7, v.keptb_limit);
     dma_run(reinterpret_cast<const u32x4*>(v.keptb + (e0 - pl.kb_sh)),
             reinterpret_cast<u32x4*>(kb_l), (int)((kb1 - (e0 - pl.kb_sh)) >> 3), lane);
-    const int64_t bo1 = std::min<int64_t>((e1 + 3) & ~(int64_t)3, v.blkoff_limit);
-    dma_run(reinterpret_cast<const u32x4*>(v.blkoff + (e0 - pl.bo_sh)),
-            reinterpret_cast<u32x4*>(bo_l), (int)((bo1 - (e0 - pl.bo_sh)) >> 2), lane);
+    if (SB) {
+      // u16 block offsets (eight per chunk) and u64 superblock bases (two per chunk)
+      const int64_t o1 = std::min<int64_t>((e1 + 7) & ~(int64_t)7, 2 * v.blkoff_limit);
+      dma_run(reinterpret_cast<const u32x4*>(v.blkoff16 + (e0 - pl.bo_sh)),
+              reinterpret_cast<u32x4*>(bo16_l), (int)((o1 - (e0 - pl.bo_sh)) >> 3), lane);
+      const int64_t s0 = pl.row0 * nsb, s1 = (pl.row0 + pl.rows_here) * nsb;
+      const int64_t q1 = std::min<int64_t>((s1 + 1) & ~(int64_t)1, v.sbbase_limit);
+      dma_run(reinterpret_cast<const u32x4*>(v.sbbase + (s0 - pl.sb_sh)),
+              reinterpret_cast<u32x4*>(sb_l), (int)((q1 - (s0 - pl.sb_sh)) >> 1), lane);
+    } else {
+      const int64_t bo1 = std::min<int64_t>((e1 + 3) & ~(int64_t)3, v.blkoff_limit);
+      dma_run(reinterpret_cast<const u32x4*>(v.blkoff + (e0 - pl.bo_sh)),
+              reinterpret_cast<u32x4*>(bo_l), (int)((bo1 - (e0 - pl.bo_sh)) >> 2), lane);
+    }
     const int64_t bm1 = std::min<int64_t>(((pl.row0 + pl.rows_here) * wpr + 3) & ~(int64_t)3,
                                           v.bitmap_limit);
     dma_run(reinterpret_cast<const u32x4*>(v.bitmap + pl.bm_a0), reinterpret_cast<u32x4*>(bm_l),
@@ -353,10 +371,12 @@ __global__ void __launch_bounds__(kBalThreads) k_gemv_c1_bal(SpecViewC1 v, Shape
     const int64_t r0 = round * g.rpw, r1 = r0 + g.rpw;
     // the round's two bounds through the scalar cache (the table is read-only
     // here), so that the codes' copy waits for nothing else
-    const const_u64* rb = (const const_u64*)v.rowbase;
-    cb0 = (int64_t)rb[r0];
-    cb1 = r1 < R ? (int64_t)rb[r1] : v.codes_limit * 32;
-    rowcb = r0 + rl < R ? (int64_t)v.rowbase[r0 + rl] : 0;
+    // (format 4: a row's first code bit is its first superblock's base)
+    const const_u64* rb = (const const_u64*)(SB ? v.sbbase : v.rowbase);
+    const int64_t rs = SB ? nsb : 1;
+    cb0 = (int64_t)rb[r0 * rs];
+    cb1 = r1 < R ? (int64_t)rb[r1 * rs] : v.codes_limit * 32;
+    rowcb = r0 + rl < R ? (int64_t)(SB ? v.sbbase : v.rowbase)[(r0 + rl) * rs] : 0;
   };
 
   // Where this lane's part of the round starts.  The block holding its first
@@ -421,7 +441,11 @@ __global__ void __launch_bounds__(kBalThreads) k_gemv_c1_bal(SpecViewC1 v, Shape
     pt.bp = pt.rowbit + (uint32_t)(b * B) + inblk;
     pt.fp = (uint32_t)(pl.row0 * k * fw - pl.f_a0 * 32) + ((uint32_t)rl * uk + i0) * (uint32_t)fw;
     // the codes: the block's code offset, then `skip` codes on
-    const uint32_t bo = bo_l[pl.bo_sh + rl * nb + b];
+    // the block's first code bit, from the row's first
+    const uint32_t bo =
+        SB ? (uint32_t)(sb_l[pl.sb_sh + rl * nsb + (b >> v.sb_log)] - (unsigned long long)rowcb) +
+                 bo16_l[pl.bo_sh + rl * nb + b]
+           : bo_l[pl.bo_sh + rl * nb + b];
     pt.cabs = rowcb + bo;
     if (pl.c_in_lds) {
       const uint32_t cpos = (uint32_t)(rowcb - pl.c_a0 * 32) + bo;
@@ -1010,7 +1034,7 @@ int pick_u(const Shape& sh) {
 }
 
 // LDS plan; lds_bytes > kBalMaxLds means "does not fit".
-BalGeom make_bal_geom(const Shape& sh, int batch, int64_t code_limit_words) {
+BalGeom make_bal_geom(const Shape& sh, int batch, int64_t code_limit_words, int64_t nsb) {
   BalGeom g = {};
   const int64_t R = sh.rows, C = sh.cols, k = sh.keep, nb = C / sh.block;
   const int fw = 1 + sh.mant;
@@ -1038,7 +1062,10 @@ BalGeom make_bal_geom(const Shape& sh, int batch, int64_t code_limit_words) {
   g.kb_off = (int)w;
   w += a16((int64_t)g.rpw * nb * 2 + 32);
   g.bo_off = (int)w;
-  w += a16(((int64_t)g.rpw * nb + 8) * 4);
+  // (format 4, nsb > 0: u16 offsets in this region, then the superblock bases)
+  w += nsb > 0 ? a16((int64_t)g.rpw * nb * 2 + 32) : a16(((int64_t)g.rpw * nb + 8) * 4);
+  g.sb_off = (int)w;
+  if (nsb > 0) w += a16(((int64_t)g.rpw * nsb + 4) * 8);
   g.bm_off = (int)w;
   w += a16((g.rpw * C / 32 + 4 + kSlack) * 4);
   g.f_off = (int)w;
@@ -1060,7 +1087,7 @@ BalGeom make_bal_geom(const Shape& sh, int batch, int64_t code_limit_words) {
 template <int BATCH, int U>
 hipError_t launch_bal(const SpecViewC1& v, const Shape& sh, const BalGeom& g, const uint16_t* x,
                       int64_t ldx, float* y, int64_t ldy, hipStream_t s) {
-  auto kern = k_gemv_c1_bal<BATCH, U>;
+  auto kern = v.sb_log >= 0 ? k_gemv_c1_bal<BATCH, U, true> : k_gemv_c1_bal<BATCH, U, false>;
   if (g.lds_bytes > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute((const void*)kern,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, g.lds_bytes);
@@ -1161,15 +1188,15 @@ hipError_t launch_bal_c2_u(const SpecViewC2& v, const Shape& sh, const BalGeom& 
 }
 }  // namespace
 
-bool draft_gemv_bal_fits(const Shape& sh, int batch, int64_t code_limit_words) {
-  return make_bal_geom(sh, batch, code_limit_words).lds_bytes <= kBalMaxLds;
+bool draft_gemv_bal_fits(const Shape& sh, int batch, int64_t code_limit_words, int64_t nsb) {
+  return make_bal_geom(sh, batch, code_limit_words, nsb).lds_bytes <= kBalMaxLds;
 }
 
 hipError_t launch_draft_gemv_c1_bal(const SpecViewC1& v, const Shape& sh, const uint16_t* x,
                                     int batch, int64_t ldx, float* y, int64_t ldy,
                                     hipStream_t s) {
   if (sh.rows == 0) return hipSuccess;
-  const BalGeom g = make_bal_geom(sh, batch, v.codes_limit);
+  const BalGeom g = make_bal_geom(sh, batch, v.codes_limit, v.sb_log >= 0 ? v.nsb : 0);
   if (g.lds_bytes > kBalMaxLds) return hipErrorInvalidValue;
   const int U = pick_u(sh);
   switch (batch) {

@@ -355,10 +355,12 @@ hipError_t launch_draft_gemv_c1(const SpecViewC1& v, const Shape& sh, const uint
                                 int batch, int64_t ldx, float* y, int64_t ldy, hipStream_t s) {
   if (sh.rows == 0) return hipSuccess;
   const bool want_staged = option(OPT_GEMV_PATH) == 1;
-  if (!force_direct() && !want_staged && draft_gemv_bal_fits(sh, batch, v.codes_limit))
+  const bool sb = v.sb_log >= 0;  // format 4: the balanced kernel or the direct one
+  if (!force_direct() && !want_staged &&
+      draft_gemv_bal_fits(sh, batch, v.codes_limit, sb ? v.nsb : 0))
     return launch_draft_gemv_c1_bal(v, sh, x, batch, ldx, y, ldy, s);
   const StagedGeom g = make_geom(sh, batch, CASS_FMT_C1_UNARY, v.codes_limit);
-  if (g.lds_bytes > kMaxLds || force_direct())
+  if (sb || g.lds_bytes > kMaxLds || force_direct())
     return launch_draft_gemv_c1_direct(v, sh, x, batch, ldx, y, ldy, s);
   CASS_BATCH_CASES(k_gemv_c1_staged, v)
 }

@@ -73,7 +73,8 @@ struct SpecViewC1 {
   const unsigned long long* sbbase;
   const uint16_t* blkoff16;
   int sb_log;
-  int64_t nsb;  // superblocks per row
+  int64_t nsb;           // superblocks per row
+  int64_t sbbase_limit;  // u64 entries from the bases to the end of the stream buffer
 };
 
 // First code bit of block bi (of row `row`, nb blocks per row).
@@ -175,7 +176,7 @@ hipError_t launch_draft_gemv_c2_direct(const SpecViewC2& v, const Shape& sh, con
                                        hipStream_t s);
 int64_t draft_gemv_direct_lds_bytes(const Shape& sh, int batch);
 // Balanced kernel (Cassandra-1): equal kept-value parts per lane.
-bool draft_gemv_bal_fits(const Shape& sh, int batch, int64_t code_limit_words);
+bool draft_gemv_bal_fits(const Shape& sh, int batch, int64_t code_limit_words, int64_t nsb);
 bool draft_gemv_bal_c2_fits(const Shape& sh, int batch);
 hipError_t launch_draft_gemv_c2_bal(const SpecViewC2& v, const Shape& sh, const uint16_t* x,
                                     int batch, int64_t ldx, float* y, int64_t ldy,

@@ -62,12 +62,18 @@ def test_format4_against_oracle(gpu, orc, case):
     cass.cass_draft_decode(enc.desc, out)
     torch.cuda.synchronize()
     assert np.array_equal(out.cpu().numpy().view(np.uint16), orc.draft_decode(spec_o)), "draft"
-    for batch in (1, 2):
-        x = synth.activations(batch, C, 2, t0=batch)
-        y = torch.full((batch, R), float("nan"), dtype=torch.float32, device="cuda")
-        cass.cass_draft_gemv(enc.desc, dev(torch, x), y)
-        torch.cuda.synchronize()
-        within(y.cpu().numpy(), *orc.product(spec_o, x, threads=8))
+    # the balanced kernel (default) and the per-thread one (option gemv_path 2)
+    for path in (0, 2):
+        cass.cass_set_option("gemv_path", path)
+        try:
+            for batch in (1, 2):
+                x = synth.activations(batch, C, 2, t0=batch)
+                y = torch.full((batch, R), float("nan"), dtype=torch.float32, device="cuda")
+                cass.cass_draft_gemv(enc.desc, dev(torch, x), y)
+                torch.cuda.synchronize()
+                within(y.cpu().numpy(), *orc.product(spec_o, x, threads=8))
+        finally:
+            cass.cass_set_option("gemv_path", 0)
     X = synth.activations(5, C, 2, t0=9)
     Y = torch.full((5, R), float("nan"), dtype=torch.float32, device="cuda")
     cass.cass_verify_gemm(enc.desc, dev(torch, X), Y)
