@@ -629,7 +629,11 @@ int cass_verify_gemm(const cass_tensor* W, const uint16_t* X, int ntok, int64_t 
             ? launch_verify_gemm_c1_staged(sv, vv, sh, X, ntok, ldx, Y, ldy, stream)
             : launch_verify_gemm_c1(sv, vv, sh, X, ntok, ldx, Y, ldy, stream);
   } else if (W->format == CASS_FMT_C1_SUPERBLOCK) {
-    e = launch_verify_gemm_c1(spec_c1s(W), verif_c1(W), sh, X, ntok, ldx, Y, ldy, stream);
+    const SpecViewC1 sv = spec_c1s(W);
+    const VerifViewC1 vv = verif_c1(W);
+    e = staged_exact_enabled() && exact_staged_fits(sh, sv, vv)
+            ? launch_verify_gemm_c1_staged(sv, vv, sh, X, ntok, ldx, Y, ldy, stream)
+            : launch_verify_gemm_c1(sv, vv, sh, X, ntok, ldx, Y, ldy, stream);
   } else if (W->format == CASS_FMT_C2_MX32) {
     e = launch_verify_gemm_c2(spec_c2(W), verif_c2(W), sh, X, ntok, ldx, Y, ldy, stream);
   } else {
@@ -653,8 +657,11 @@ int cass_reconstruct(const cass_tensor* W, uint16_t* out, hipStream_t stream) {
             ? launch_reconstruct_c1_staged(sv, vv, sh, out, stream)
             : launch_decode_c1(sv, &vv, sh, out, stream);
   } else if (W->format == CASS_FMT_C1_SUPERBLOCK) {
+    const SpecViewC1 sv = spec_c1s(W);
     const VerifViewC1 vv = verif_c1(W);
-    e = launch_decode_c1(spec_c1s(W), &vv, sh, out, stream);
+    e = staged_exact_enabled() && exact_staged_fits(sh, sv, vv)
+            ? launch_reconstruct_c1_staged(sv, vv, sh, out, stream)
+            : launch_decode_c1(sv, &vv, sh, out, stream);
   } else if (W->format == CASS_FMT_C2_MX32) {
     const VerifViewC2 vv = verif_c2(W);
     e = launch_decode_c2(spec_c2(W), &vv, sh, out, stream);
@@ -679,7 +686,11 @@ int cass_draft_decode(const cass_tensor* W, uint16_t* out, hipStream_t stream) {
             ? launch_draft_decode_c1_staged(sv, sh, out, stream)
             : launch_decode_c1(sv, nullptr, sh, out, stream);
   } else if (W->format == CASS_FMT_C1_SUPERBLOCK) {
-    e = launch_decode_c1(spec_c1s(W), nullptr, sh, out, stream);
+    const SpecViewC1 sv = spec_c1s(W);
+    const VerifViewC1 none = {};
+    e = staged_exact_enabled() && exact_staged_fits(sh, sv, none)
+            ? launch_draft_decode_c1_staged(sv, sh, out, stream)
+            : launch_decode_c1(sv, nullptr, sh, out, stream);
   } else {
     e = launch_decode_c2(spec_c2(W), nullptr, sh, out, stream);
   }

@@ -418,9 +418,16 @@ __global__ void __launch_bounds__(64 * kMaxWaves) k_exact_staged(SpecViewC1 sv, 
   const int64_t rowc = row_ok ? row : R - 1;  // clamped for loads
   const int64_t st0 = (int64_t)wave * g.stages_per_split;
   const int64_t st1 = std::min<int64_t>(st0 + g.stages_per_split, g.nstage);
-  const int64_t rbs = (int64_t)sv.rowbase[rowc];
+  // format 4 (sv.sb_log >= 0): a row's first code bit is its first superblock's
+  // base, and a block's code offset from it is (superblock base - that) + the
+  // block's 16-bit offset
+  const bool sbm = sv.sb_log >= 0;
+  const unsigned long long* rb0 = sbm ? sv.sbbase : sv.rowbase;
+  const int64_t rstride = sbm ? sv.nsb : 1;
+  const int64_t rbs = (int64_t)rb0[rowc * rstride];
   const int64_t rbv = MODE == 2 ? 0 : (int64_t)vv.rowbase[rowc];
-  const int64_t rbs_next = rowc + 1 < R ? (int64_t)sv.rowbase[rowc + 1] : sv.codes_limit * 32;
+  const int64_t rbs_next =
+      rowc + 1 < R ? (int64_t)rb0[(rowc + 1) * rstride] : sv.codes_limit * 32;
   const int64_t rbv_next =
       MODE == 2 ? 0 : (rowc + 1 < R ? (int64_t)vv.rowbase[rowc + 1] : vv.codes_limit * 32);
   const uint8_t* sec_base[kSec] = {
@@ -445,7 +452,9 @@ __global__ void __launch_bounds__(64 * kMaxWaves) k_exact_staged(SpecViewC1 sv, 
     for (int i = 0; i < 3; ++i) {
       const int64_t bb = std::min<int64_t>(bf + i, nb - 1);
       mr.kb[i] = sv.keptb[rowc * nb + bb];
-      mr.bs[i] = sv.blkoff[rowc * nb + bb];
+      mr.bs[i] = sbm ? (uint32_t)(sv.sbbase[rowc * sv.nsb + (bb >> sv.sb_log)] - (uint64_t)rbs) +
+                           sv.blkoff16[rowc * nb + bb]
+                     : sv.blkoff[rowc * nb + bb];
       mr.bv[i] = MODE == 2 ? 0u : vv.blkoff[rowc * nb + bb];
     }
     return mr;

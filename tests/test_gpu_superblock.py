@@ -53,15 +53,29 @@ def test_format4_against_oracle(gpu, orc, case):
     w = synth.weight(R, C, 8000 + R + C + k, outlier_frac=0.01)
     spec_o, verif_o = orc.encode(w, k, m, block=B, fmt=FMT)
     enc = cass.encode(dev(torch, w), k, m, block=B, fmt=FMT)
-    out = torch.empty((R, C), dtype=torch.int16, device="cuda")
-    cass.cass_reconstruct(enc.desc, out)
     torch.cuda.synchronize()
     assert np.array_equal(enc.spec.cpu().numpy(), spec_o), "speculation stream"
     assert np.array_equal(enc.verif.cpu().numpy(), verif_o), "verification stream"
-    assert np.array_equal(out.cpu().numpy().view(np.uint16), w), "reconstruction"
-    cass.cass_draft_decode(enc.desc, out)
-    torch.cuda.synchronize()
-    assert np.array_equal(out.cpu().numpy().view(np.uint16), orc.draft_decode(spec_o)), "draft"
+    X = synth.activations(5, C, 2, t0=9)
+    Yr = orc.product(spec_o, X, verif=verif_o, threads=8)
+    # the staged exact kernel (default) and the per-thread readers (option exact_path 1)
+    for ep in (0, 1):
+        cass.cass_set_option("exact_path", ep)
+        try:
+            out = torch.empty((R, C), dtype=torch.int16, device="cuda")
+            cass.cass_reconstruct(enc.desc, out)
+            torch.cuda.synchronize()
+            assert np.array_equal(out.cpu().numpy().view(np.uint16), w), ("reconstruction", ep)
+            cass.cass_draft_decode(enc.desc, out)
+            torch.cuda.synchronize()
+            assert np.array_equal(out.cpu().numpy().view(np.uint16), orc.draft_decode(spec_o)), \
+                ("draft", ep)
+            Y = torch.full((5, R), float("nan"), dtype=torch.float32, device="cuda")
+            cass.cass_verify_gemm(enc.desc, dev(torch, X), Y)
+            torch.cuda.synchronize()
+            within(Y.cpu().numpy(), *Yr)
+        finally:
+            cass.cass_set_option("exact_path", 0)
     # the balanced kernel (default) and the per-thread one (option gemv_path 2)
     for path in (0, 2):
         cass.cass_set_option("gemv_path", path)
@@ -74,22 +88,27 @@ def test_format4_against_oracle(gpu, orc, case):
                 within(y.cpu().numpy(), *orc.product(spec_o, x, threads=8))
         finally:
             cass.cass_set_option("gemv_path", 0)
-    X = synth.activations(5, C, 2, t0=9)
-    Y = torch.full((5, R), float("nan"), dtype=torch.float32, device="cuda")
-    cass.cass_verify_gemm(enc.desc, dev(torch, X), Y)
-    torch.cuda.synchronize()
-    within(Y.cpu().numpy(), *orc.product(spec_o, X, verif=verif_o, threads=8))
 
 
 def test_format4_llama8b_gate_up_full_size(gpu, orc):
     """The Llama-3-8B-shaped gate|up matrix (28672 x 4096) at keep 0.3, m = 3:
-    every byte of both streams, and sampled rows of the draft GEMV."""
+    every byte of both streams, the exact reconstruction, and sampled rows of
+    the draft GEMV and of the verification GEMM."""
     torch, cass = gpu
     w = np.concatenate([synth.weight(14336, 4096, 91_001, outlier_frac=0.01),
                         synth.weight(14336, 4096, 91_002, outlier_frac=0.01)])
     R, C = w.shape
     k = synth.keep_count(0.3, C)
-    enc = cass.encode(dev(torch, w), k, 3, fmt=FMT)
+    wd = dev(torch, w)
+    enc = cass.encode(wd, k, 3, fmt=FMT)
+    out = torch.empty_like(wd)
+    cass.cass_reconstruct(enc.desc, out)
+    X = synth.activations(5, C, 2, t0=6)
+    Y = torch.full((5, R), float("nan"), dtype=torch.float32, device="cuda")
+    cass.cass_verify_gemm(enc.desc, dev(torch, X), Y)
+    torch.cuda.synchronize()
+    assert torch.equal(out, wd)
+    del out
     x = synth.activations(1, C, 2, t0=4)
     y = torch.full((1, R), float("nan"), dtype=torch.float32, device="cuda")
     cass.cass_draft_gemv(enc.desc, dev(torch, x), y)
@@ -100,6 +119,8 @@ def test_format4_llama8b_gate_up_full_size(gpu, orc):
     rows = np.random.default_rng(0).choice(R, size=512, replace=False)
     yr, ar = orc.product_rows(spec_o, x, rows)
     within(y.cpu().numpy()[:, rows], yr, ar)
+    Yr, Ar = orc.product_rows(spec_o, X, rows, verif=verif_o)
+    within(Y.cpu().numpy()[:, rows], Yr, Ar)
 
 
 def test_format4_offsets_past_16_bits_refused(gpu):
