@@ -1304,22 +1304,75 @@ __global__ void __launch_bounds__(kXThreads) k_kv_attn_x1(KvDev kv, AttnArgs a, 
       cpos[1] = skip_codes(cw[1], cpos[1], pb);
       const uint8_t* ps = tabs[2 * j];
       const uint8_t* pv = tabs[2 * j + 1];
-      const uint32_t fmask = (2u << m) - 1u, lmask = (1u << (7 - m)) - 1u;
-      for (uint32_t km = word; km; km &= km - 1u) {
-        const uint32_t f = window32(fl, fpos) & fmask;
-        const uint32_t lo = window32(ll, lpos) & lmask;
-        fpos += 1 + m;
-        lpos += 7 - m;
-        const int r = unary_at(cw[0], cpos[0]);
-        const uint32_t e = ps[r & 255];
-        row[__builtin_ctz(km)] = (uint16_t)(((f >> m) << 15) | (e << 7) |
-                                            ((f & ((1u << m) - 1u)) << (7 - m)) | lo);
+      const int fwd = 1 + m, lwd = 7 - m;
+      const uint32_t fmask = (2u << m) - 1u, lmask = (1u << lwd) - 1u;
+      // Windows held in registers: fields and low mantissas of the next
+      // 32 / width values, pruned bytes four at a time, codes until the window
+      // runs out of one bits (a code of 32 bits or more: the general reader).
+      // Every lane refills its field, low and byte windows at the same value
+      // index, so those refills do not diverge.
+      {
+        const int uf = 32 / fwd, ul = lwd > 0 ? 32 / lwd : 32;
+        uint32_t fwin = 0, lwin = 0, cwin = window32(cw[0], cpos[0]);
+        int fleft = 0, lleft = 0;
+        for (uint32_t km = word; km; km &= km - 1u) {
+          if (fleft == 0) {
+            fwin = window32(fl, fpos);
+            fleft = uf;
+          }
+          if (lleft == 0) {
+            lwin = window32(ll, lpos);
+            lleft = ul;
+          }
+          const uint32_t f = fwin & fmask;
+          const uint32_t lo = lwin & lmask;
+          fwin >>= fwd;
+          lwin >>= lwd;
+          --fleft;
+          --lleft;
+          fpos += fwd;
+          lpos += lwd;
+          if (cwin == 0u) cwin = window32(cw[0], cpos[0]);
+          int r;
+          if (cwin != 0u) {
+            r = __builtin_ctz(cwin);
+            cwin = (cwin >> r) >> 1;
+            cpos[0] += (uint32_t)r + 1u;
+          } else {
+            r = unary_at(cw[0], cpos[0]);
+            cwin = window32(cw[0], cpos[0]);
+          }
+          const uint32_t e = ps[r & 255];
+          row[__builtin_ctz(km)] = (uint16_t)(((f >> m) << 15) | (e << 7) |
+                                              ((f & ((1u << m) - 1u)) << lwd) | lo);
+        }
       }
-      for (uint32_t pm = ~word; pm; pm &= pm - 1u) {
-        const uint32_t byte = bl[bpos++];
-        const int r = unary_at(cw[1], cpos[1]);
-        const uint32_t e = pv[r & 255];
-        row[__builtin_ctz(pm)] = (uint16_t)(((byte >> 7) << 15) | (e << 7) | (byte & 0x7F));
+      {
+        const uint32_t* bw = reinterpret_cast<const uint32_t*>(bl);
+        uint32_t bwin = 0, cwin = window32(cw[1], cpos[1]);
+        int bleft = 0;
+        for (uint32_t pm = ~word; pm; pm &= pm - 1u) {
+          if (bleft == 0) {
+            bwin = window32(bw, bpos * 8u);
+            bleft = 4;
+          }
+          const uint32_t byte = bwin & 0xFFu;
+          bwin >>= 8;
+          --bleft;
+          ++bpos;
+          if (cwin == 0u) cwin = window32(cw[1], cpos[1]);
+          int r;
+          if (cwin != 0u) {
+            r = __builtin_ctz(cwin);
+            cwin = (cwin >> r) >> 1;
+            cpos[1] += (uint32_t)r + 1u;
+          } else {
+            r = unary_at(cw[1], cpos[1]);
+            cwin = window32(cw[1], cpos[1]);
+          }
+          const uint32_t e = pv[r & 255];
+          row[__builtin_ctz(pm)] = (uint16_t)(((byte >> 7) << 15) | (e << 7) | (byte & 0x7F));
+        }
       }
     }
   }
