@@ -1166,7 +1166,8 @@ __global__ void __launch_bounds__(128 * kMergeParts) k_kv_merge(AttnArgs a, int 
 //     written as a chunk partial (row maximum, sum, numerator) for k_kv_merge.
 constexpr int kXThreads = 1024;
 constexpr int kXRows = 32;
-constexpr int kXStride = 132;  // bf16 per tile row (8-byte aligned rows, banks shifted by 2 words)
+constexpr int kXStride = 132;  // bf16 per key tile row (8-byte aligned rows, banks shifted by 2 words)
+constexpr int kXVStride = 136;  // bf16 per row of the transposed value tile (16-byte aligned rows)
 
 typedef short xv4s __attribute__((ext_vector_type(4)));
 typedef short xv8s __attribute__((ext_vector_type(8)));
@@ -1181,8 +1182,8 @@ struct XCaps {
 };
 
 __host__ __device__ __forceinline__ int64_t x1_lds_bytes(const XCaps& cp) {
-  return (int64_t)2 * kChunk * kXStride * 2 + (int64_t)kXRows * kChunk * 4 +
-         (int64_t)2 * cp.per_stream() * 4;
+  return (int64_t)kChunk * kXStride * 2 + (int64_t)kDim * kXVStride * 2 +
+         (int64_t)kXRows * kChunk * 4 + (int64_t)2 * cp.per_stream() * 4;
 }
 
 // bf16 bits of x rounded to nearest even (x finite).
@@ -1193,9 +1194,10 @@ __device__ __forceinline__ uint32_t x1_bf16_rne(float x) {
 
 __global__ void __launch_bounds__(kXThreads) k_kv_attn_x1(KvDev kv, AttnArgs a, XCaps cp) {
   extern __shared__ __align__(16) uint8_t smem[];
-  uint16_t* kt = reinterpret_cast<uint16_t*>(smem);          // [128][kXStride] keys
-  uint16_t* vt = kt + kChunk * kXStride;                       // [128][kXStride] values
-  float* sc = reinterpret_cast<float*>(vt + kChunk * kXStride);  // [32][128] scores, then p
+  uint16_t* kt = reinterpret_cast<uint16_t*>(smem);          // [token][kXStride] keys
+  uint16_t* vt = kt + kChunk * kXStride;                       // [dim][kXVStride] values, transposed
+  // [32][128] scores; then per row p in bf16, hi terms then lo terms
+  float* sc = reinterpret_cast<float*>(vt + kDim * kXVStride);
   uint32_t* stg = reinterpret_cast<uint32_t*>(sc + kXRows * kChunk);  // staged sections
   __shared__ uint8_t tabs[4][256];  // rank tables: K spec, K verif, V spec, V verif
   __shared__ long long cfirst[2][2];  // first staged code word [stream][spec | pruned], -1: in place
@@ -1261,9 +1263,11 @@ __global__ void __launch_bounds__(kXThreads) k_kv_attn_x1(KvDev kv, AttnArgs a, 
   {
     const int j = tid >> 9, tl = (tid >> 2) & (kChunk - 1), w = tid & 3;
     const int64_t tok = t0 + tl;
-    uint16_t* row = (j ? vt : kt) + tl * kXStride + w * 32;
+    // value d of the word goes to row[d * dstride]: keys by token, values by dimension
+    uint16_t* row = j ? vt + w * 32 * kXVStride + tl : kt + tl * kXStride + w * 32;
+    const int dstride = j ? kXVStride : 1;
     if (tok >= t1) {
-      for (int i = 0; i < 32; ++i) row[i] = 0;
+      for (int i = 0; i < 32; ++i) row[i * dstride] = 0;
     } else {
       const int s = 2 * h + j;
       const uint8_t* sr = kv.spec + s * kv.sstride;
@@ -1343,8 +1347,8 @@ __global__ void __launch_bounds__(kXThreads) k_kv_attn_x1(KvDev kv, AttnArgs a, 
             cwin = window32(cw[0], cpos[0]);
           }
           const uint32_t e = ps[r & 255];
-          row[__builtin_ctz(km)] = (uint16_t)(((f >> m) << 15) | (e << 7) |
-                                              ((f & ((1u << m) - 1u)) << lwd) | lo);
+          row[__builtin_ctz(km) * dstride] = (uint16_t)(((f >> m) << 15) | (e << 7) |
+                                                        ((f & ((1u << m) - 1u)) << lwd) | lo);
         }
       }
       {
@@ -1371,7 +1375,8 @@ __global__ void __launch_bounds__(kXThreads) k_kv_attn_x1(KvDev kv, AttnArgs a, 
             cwin = window32(cw[1], cpos[1]);
           }
           const uint32_t e = pv[r & 255];
-          row[__builtin_ctz(pm)] = (uint16_t)(((byte >> 7) << 15) | (e << 7) | (byte & 0x7F));
+          row[__builtin_ctz(pm) * dstride] =
+              (uint16_t)(((byte >> 7) << 15) | (e << 7) | (byte & 0x7F));
         }
       }
     }
@@ -1436,10 +1441,16 @@ __global__ void __launch_bounds__(kXThreads) k_kv_attn_x1(KvDev kv, AttnArgs a, 
       v1 = none || v1 == -INFINITY ? 0.f : __expf(v1 - mx);
       v2 = none || v2 == -INFINITY ? 0.f : __expf(v2 - mx);
       v3 = none || v3 == -INFINITY ? 0.f : __expf(v3 - mx);
-      srow[q] = v0;
-      srow[q + 32] = v1;
-      srow[q + 64] = v2;
-      srow[q + 96] = v3;
+      // p as two bf16 terms (hi, then lo = p - hi), over the row's scores: a
+      // row's 32 threads are in one wave, so every read above comes first
+      uint16_t* ph = reinterpret_cast<uint16_t*>(srow);
+      const float pv4[4] = {v0, v1, v2, v3};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t hb = x1_bf16_rne(pv4[i]);
+        ph[q + 32 * i] = (uint16_t)hb;
+        ph[kChunk + q + 32 * i] = (uint16_t)x1_bf16_rne(pv4[i] - __uint_as_float(hb << 16));
+      }
       float l = (v0 + v1) + (v2 + v3);
 #pragma unroll
       for (int o = 16; o >= 1; o >>= 1) l += __shfl_xor(l, o, 64);
@@ -1454,21 +1465,17 @@ __global__ void __launch_bounds__(kXThreads) k_kv_attn_x1(KvDev kv, AttnArgs a, 
   // its group), tokens 8kq..8kq+7 of each 32-token step; p = hi + lo in bf16
   {
     const int r = rg * 16 + i16;
-    const float* prow = sc + r * kChunk;
+    const uint16_t* ph = reinterpret_cast<const uint16_t*>(sc + r * kChunk);
     const int dcol = cg * 16 + i16;
+    const uint16_t* vcol = vt + dcol * kXVStride;
     xv4f acc = xv4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll 2
     for (int ks = 0; ks < kChunk / 32; ++ks) {
       const int tb = ks * 32 + 8 * kq;
-      xv8s ahi, alo, bop;
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const float p = r < rows ? prow[tb + u] : 0.f;
-        const uint32_t hb = x1_bf16_rne(p);
-        ahi[u] = (short)hb;
-        alo[u] = (short)x1_bf16_rne(p - __uint_as_float(hb << 16));
-        bop[u] = (short)vt[(tb + u) * kXStride + dcol];
-      }
+      const xv8s zero = xv8s{0, 0, 0, 0, 0, 0, 0, 0};
+      const xv8s ahi = r < rows ? *reinterpret_cast<const xv8s*>(ph + tb) : zero;
+      const xv8s alo = r < rows ? *reinterpret_cast<const xv8s*>(ph + kChunk + tb) : zero;
+      const xv8s bop = *reinterpret_cast<const xv8s*>(vcol + tb);
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(xv8bf, ahi),
                                                     __builtin_bit_cast(xv8bf, bop), acc, 0, 0, 0);
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(xv8bf, alo),
