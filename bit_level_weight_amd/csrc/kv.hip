@@ -825,7 +825,7 @@ constexpr int kChunk = 128;  // tokens per workgroup, one per thread
 constexpr int kDim = 128;
 constexpr int kVStride = kDim + 2;  // bf16 per LDS row of the value tile (bank spread)
 constexpr int kMaxRows = 32;
-constexpr int kMaxChunksMerge = 4096;  // tokens up to 4096 * kChunk = 512K per merge
+constexpr int kMaxChunksMerge = 8192;  // chunk partials one merge takes (512K tokens in 64-token chunks)
 
 struct AttnArgs {
   const uint16_t* q;  // [nq][Hq][D]
@@ -1147,12 +1147,14 @@ __global__ void __launch_bounds__(128 * kMergeParts) k_kv_merge(AttnArgs a, int 
 }
 
 // ---- verification attention, Cassandra-1: split decode, matrix-core products ----
-// One workgroup of 16 waves per (KV head, chunk of 128 tokens).
+// One workgroup of 8 waves per (KV head, chunk of 64 tokens): about 60 KB of
+// shared memory, so two workgroups share a CU and one's copies overlap the
+// other's arithmetic.
 //  1. The chunk's sections of K and V are copied to shared memory with
 //     coalesced loads: fields, low mantissas, pruned bytes, and the
 //     speculation and pruned-exponent code runs (a run longer than its staged
 //     space is read in place).
-//  2. Each of the 1024 threads rebuilds 32 exact values: one keep-bitmap word
+//  2. Each of the 512 threads rebuilds 32 exact values: one keep-bitmap word
 //     of one token of K or V.  Its kept and pruned values start at indices the
 //     popcounts of the token's earlier words give, so its fields, low mantissas
 //     and pruned bytes sit at known bit positions, and its codes start after
@@ -1164,10 +1166,11 @@ __global__ void __launch_bounds__(128 * kMergeParts) k_kv_merge(AttnArgs a, int 
 //  4. Softmax per row over the chunk; o = p V on the matrix cores with p split
 //     into two bf16 terms (p = hi + lo to about 2^-17 relative), fp32 sums;
 //     written as a chunk partial (row maximum, sum, numerator) for k_kv_merge.
-constexpr int kXThreads = 1024;
+constexpr int kXChunk = 64;  // tokens per workgroup
+constexpr int kXThreads = 2 * kXChunk * 4;  // (K | V, token, keep word)
 constexpr int kXRows = 32;
 constexpr int kXStride = 132;  // bf16 per key tile row (8-byte aligned rows, banks shifted by 2 words)
-constexpr int kXVStride = 136;  // bf16 per row of the transposed value tile (16-byte aligned rows)
+constexpr int kXVStride = kXChunk + 8;  // bf16 per row of the transposed value tile (16-byte rows)
 
 typedef short xv4s __attribute__((ext_vector_type(4)));
 typedef short xv8s __attribute__((ext_vector_type(8)));
@@ -1182,8 +1185,8 @@ struct XCaps {
 };
 
 __host__ __device__ __forceinline__ int64_t x1_lds_bytes(const XCaps& cp) {
-  return (int64_t)kChunk * kXStride * 2 + (int64_t)kDim * kXVStride * 2 +
-         (int64_t)kXRows * kChunk * 4 + (int64_t)2 * cp.per_stream() * 4;
+  return (int64_t)kXChunk * kXStride * 2 + (int64_t)kDim * kXVStride * 2 +
+         (int64_t)kXRows * kXChunk * 4 + (int64_t)2 * cp.per_stream() * 4;
 }
 
 // bf16 bits of x rounded to nearest even (x finite).
@@ -1195,10 +1198,10 @@ __device__ __forceinline__ uint32_t x1_bf16_rne(float x) {
 __global__ void __launch_bounds__(kXThreads) k_kv_attn_x1(KvDev kv, AttnArgs a, XCaps cp) {
   extern __shared__ __align__(16) uint8_t smem[];
   uint16_t* kt = reinterpret_cast<uint16_t*>(smem);          // [token][kXStride] keys
-  uint16_t* vt = kt + kChunk * kXStride;                       // [dim][kXVStride] values, transposed
+  uint16_t* vt = kt + kXChunk * kXStride;                       // [dim][kXVStride] values, transposed
   // [32][128] scores; then per row p in bf16, hi terms then lo terms
   float* sc = reinterpret_cast<float*>(vt + kDim * kXVStride);
-  uint32_t* stg = reinterpret_cast<uint32_t*>(sc + kXRows * kChunk);  // staged sections
+  uint32_t* stg = reinterpret_cast<uint32_t*>(sc + kXRows * kXChunk);  // staged sections
   __shared__ uint8_t tabs[4][256];  // rank tables: K spec, K verif, V spec, V verif
   __shared__ long long cfirst[2][2];  // first staged code word [stream][spec | pruned], -1: in place
   __shared__ float rmax[kXRows], rsum[kXRows];
@@ -1206,8 +1209,8 @@ __global__ void __launch_bounds__(kXThreads) k_kv_attn_x1(KvDev kv, AttnArgs a, 
   const int rows = a.nq * a.G;
   const int tid = threadIdx.x;
   const int k = kv.k, m = kv.m, np = kDim - kv.k;
-  const int64_t t0 = (int64_t)c * kChunk;
-  const int64_t t1 = t0 + kChunk < a.T ? t0 + kChunk : a.T;  // tokens of the chunk: [t0, t1)
+  const int64_t t0 = (int64_t)c * kXChunk;
+  const int64_t t1 = t0 + kXChunk < a.T ? t0 + kXChunk : a.T;  // tokens of the chunk: [t0, t1)
   const int psw = cp.per_stream();
   // staged words of stream j: codes (spec, pruned), fields, low mantissas, pruned bytes
   auto sbase = [&](int j) { return stg + j * psw; };
@@ -1261,7 +1264,7 @@ __global__ void __launch_bounds__(kXThreads) k_kv_attn_x1(KvDev kv, AttnArgs a, 
 
   // 2. exact values: thread = (stream j, token, keep word w)
   {
-    const int j = tid >> 9, tl = (tid >> 2) & (kChunk - 1), w = tid & 3;
+    const int j = tid / (4 * kXChunk), tl = (tid >> 2) & (kXChunk - 1), w = tid & 3;
     const int64_t tok = t0 + tl;
     // value d of the word goes to row[d * dstride]: keys by token, values by dimension
     uint16_t* row = j ? vt + w * 32 * kXVStride + tl : kt + tl * kXStride + w * 32;
@@ -1384,7 +1387,7 @@ __global__ void __launch_bounds__(kXThreads) k_kv_attn_x1(KvDev kv, AttnArgs a, 
   __syncthreads();
 
   const int lane = tid & 63, wv = tid >> 6;
-  const int rg = wv >> 3, cg = wv & 7;  // 16-row group, 16-column group (tokens, then dims)
+  const int rg = wv >> 2, cg = wv & 3;  // 16-row group, 16-column group (tokens, then dims)
   const int i16 = lane & 15, kq = lane >> 4;
   // 3. scores: lane (i16, kq) feeds query row / token i16 of its group and
   // dimensions 8kq..8kq+7 of each 32-dimension step
@@ -1421,7 +1424,7 @@ __global__ void __launch_bounds__(kXThreads) k_kv_attn_x1(KvDev kv, AttnArgs a, 
       if (rr < rows) {
         const int qi = rr / a.G;
         const bool vis = tok < t1 && tok < a.T - a.nq + qi + 1;
-        sc[rr * kChunk + cg * 16 + i16] = vis ? acc[e] * a.scale : -INFINITY;
+        sc[rr * kXChunk + cg * 16 + i16] = vis ? acc[e] * a.scale : -INFINITY;
       }
     }
   }
@@ -1429,13 +1432,14 @@ __global__ void __launch_bounds__(kXThreads) k_kv_attn_x1(KvDev kv, AttnArgs a, 
 
   // 4a. softmax per row: 32 threads per row, 4 tokens each
   {
-    const int r = tid >> 5, q = tid & 31;
+    constexpr int TPR = kXChunk / 4;  // threads per row, 4 tokens each (a row in one wave)
+    const int r = tid / TPR, q = tid % TPR;
     if (r < rows) {
-      float* srow = sc + r * kChunk;
-      float v0 = srow[q], v1 = srow[q + 32], v2 = srow[q + 64], v3 = srow[q + 96];
+      float* srow = sc + r * kXChunk;
+      float v0 = srow[q], v1 = srow[q + TPR], v2 = srow[q + 2 * TPR], v3 = srow[q + 3 * TPR];
       float mx = fmaxf(fmaxf(v0, v1), fmaxf(v2, v3));
 #pragma unroll
-      for (int o = 16; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+      for (int o = TPR / 2; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
       const bool none = mx == -INFINITY;
       v0 = none || v0 == -INFINITY ? 0.f : __expf(v0 - mx);
       v1 = none || v1 == -INFINITY ? 0.f : __expf(v1 - mx);
@@ -1448,12 +1452,12 @@ __global__ void __launch_bounds__(kXThreads) k_kv_attn_x1(KvDev kv, AttnArgs a, 
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const uint32_t hb = x1_bf16_rne(pv4[i]);
-        ph[q + 32 * i] = (uint16_t)hb;
-        ph[kChunk + q + 32 * i] = (uint16_t)x1_bf16_rne(pv4[i] - __uint_as_float(hb << 16));
+        ph[q + TPR * i] = (uint16_t)hb;
+        ph[kXChunk + q + TPR * i] = (uint16_t)x1_bf16_rne(pv4[i] - __uint_as_float(hb << 16));
       }
       float l = (v0 + v1) + (v2 + v3);
 #pragma unroll
-      for (int o = 16; o >= 1; o >>= 1) l += __shfl_xor(l, o, 64);
+      for (int o = TPR / 2; o >= 1; o >>= 1) l += __shfl_xor(l, o, 64);
       if (q == 0) {
         rmax[r] = mx;
         rsum[r] = l;
@@ -1462,36 +1466,44 @@ __global__ void __launch_bounds__(kXThreads) k_kv_attn_x1(KvDev kv, AttnArgs a, 
   }
   __syncthreads();
   // 4b. o = p V: lane (i16, kq) feeds row i16 of p and column i16 of V (dims of
-  // its group), tokens 8kq..8kq+7 of each 32-token step; p = hi + lo in bf16
+  // its group), tokens 8kq..8kq+7 of each 32-token step; p = hi + lo in bf16.
+  // A wave takes its row group and two of the eight 16-dimension groups.
   {
     const int r = rg * 16 + i16;
-    const uint16_t* ph = reinterpret_cast<const uint16_t*>(sc + r * kChunk);
-    const int dcol = cg * 16 + i16;
-    const uint16_t* vcol = vt + dcol * kXVStride;
-    xv4f acc = xv4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 2
-    for (int ks = 0; ks < kChunk / 32; ++ks) {
+    const uint16_t* ph = reinterpret_cast<const uint16_t*>(sc + r * kXChunk);
+    const xv8s zero = xv8s{0, 0, 0, 0, 0, 0, 0, 0};
+    xv8s ahi[kXChunk / 32], alo[kXChunk / 32];
+#pragma unroll
+    for (int ks = 0; ks < kXChunk / 32; ++ks) {
       const int tb = ks * 32 + 8 * kq;
-      const xv8s zero = xv8s{0, 0, 0, 0, 0, 0, 0, 0};
-      const xv8s ahi = r < rows ? *reinterpret_cast<const xv8s*>(ph + tb) : zero;
-      const xv8s alo = r < rows ? *reinterpret_cast<const xv8s*>(ph + kChunk + tb) : zero;
-      const xv8s bop = *reinterpret_cast<const xv8s*>(vcol + tb);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(xv8bf, ahi),
-                                                    __builtin_bit_cast(xv8bf, bop), acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(xv8bf, alo),
-                                                    __builtin_bit_cast(xv8bf, bop), acc, 0, 0, 0);
+      ahi[ks] = r < rows ? *reinterpret_cast<const xv8s*>(ph + tb) : zero;
+      alo[ks] = r < rows ? *reinterpret_cast<const xv8s*>(ph + kXChunk + tb) : zero;
     }
-    // D: this lane holds rows rg*16 + 4kq + e, dimension cg*16 + i16
     float* part = a.part + (((int64_t)h * a.nchunks + c) * rows) * (2 + kDim);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int rr = rg * 16 + 4 * kq + e;
-      if (rr < rows) {
-        float* pr = part + (int64_t)rr * (2 + kDim);
-        pr[2 + dcol] = acc[e];
-        if (dcol == 0) {
-          pr[0] = rmax[rr];
-          pr[1] = rsum[rr];
+    for (int half = 0; half < 2; ++half) {
+      const int dcol = (cg + 4 * half) * 16 + i16;
+      const uint16_t* vcol = vt + dcol * kXVStride;
+      xv4f acc = xv4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < kXChunk / 32; ++ks) {
+        const xv8s bop = *reinterpret_cast<const xv8s*>(vcol + ks * 32 + 8 * kq);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(xv8bf, ahi[ks]),
+                                                      __builtin_bit_cast(xv8bf, bop), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(xv8bf, alo[ks]),
+                                                      __builtin_bit_cast(xv8bf, bop), acc, 0, 0, 0);
+      }
+      // D: this lane holds rows rg*16 + 4kq + e, dimension dcol
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int rr = rg * 16 + 4 * kq + e;
+        if (rr < rows) {
+          float* pr = part + (int64_t)rr * (2 + kDim);
+          pr[2 + dcol] = acc[e];
+          if (dcol == 0) {
+            pr[0] = rmax[rr];
+            pr[1] = rsum[rr];
+          }
         }
       }
     }
@@ -1594,8 +1606,10 @@ int64_t append_ws_layout(const cass_kv* kv, int ntok, AppendWs* ws, uint8_t* bas
   return pos;
 }
 
-int64_t attn_ws(const cass_kv* kv, int nq, int G) {
-  const int64_t nchunks = (kv->tokens + kChunk - 1) / kChunk;
+// Chunk partials of one attention call in chunks of `chunk` tokens; the
+// public size is that of the smaller chunks (the verification kernel's 64).
+int64_t attn_ws(const cass_kv* kv, int nq, int G, int chunk = kXChunk) {
+  const int64_t nchunks = (kv->tokens + chunk - 1) / chunk;
   return (int64_t)kv->p.n_kv_heads * nchunks * nq * G * (2 + kDim) * 4;
 }
 
@@ -1633,7 +1647,8 @@ int run_attention(const cass_kv* kv, const uint16_t* q, int nq, int n_q_heads, f
   if (nq < 1 || nq * G > kMaxRows) return report(CASS_ERR_UNSUPPORTED, "nq * heads per group > 32");
   if (kv->tokens < nq) return report(CASS_ERR_INVALID, "cache holds fewer tokens than queries");
   if (!q || !out) return report(CASS_ERR_INVALID, "q or out is NULL");
-  const int64_t need = attn_ws(kv, nq, G);
+  const bool x1 = exact && fmt_of(&kv->p) == CASS_FMT_C1_UNARY && option(OPT_KV_EXACT_PATH) != 1;
+  const int64_t need = attn_ws(kv, nq, G, x1 ? kXChunk : kChunk);
   if (!ws || ws_bytes < need) return report(CASS_ERR_CAPACITY, "attention workspace too small");
   AttnArgs a;
   a.q = q;
@@ -1643,7 +1658,8 @@ int run_attention(const cass_kv* kv, const uint16_t* q, int nq, int n_q_heads, f
   a.scale = scale;
   a.T = kv->tokens;
   a.nchunks = (int)((kv->tokens + kChunk - 1) / kChunk);
-  if (a.nchunks > kMaxChunksMerge) return report(CASS_ERR_UNSUPPORTED, "attention over more than 512K tokens");
+  if ((kv->tokens + kXChunk - 1) / kXChunk > kMaxChunksMerge)
+    return report(CASS_ERR_UNSUPPORTED, "attention over more than 512K tokens");
   a.part = (float*)ws;
   {
     // draft staging: every field of the chunk, and codes averaging up to 4
@@ -1655,25 +1671,27 @@ int run_attention(const cass_kv* kv, const uint16_t* q, int nq, int n_q_heads, f
   const KvDev d = dev_of(kv);
   const size_t lds = 0;  // per launch, from the row bound (attn_launch_f)
   const int rows = nq * G;
-  if (exact && d.fmt == CASS_FMT_C1_UNARY && option(OPT_KV_EXACT_PATH) != 1) {
+  if (x1) {
     // split decode and matrix-core scores; staged code space averaging up to
     // 4 bits per value (longer runs are read in place)
     const int64_t kk = kv->p.keep, mm = kv->p.mant_bits;
+    AttnArgs ax = a;
+    ax.nchunks = (int)((kv->tokens + kXChunk - 1) / kXChunk);
     XCaps cp;
-    cp.scode = (int)((kChunk * kk * 4 + 31) / 32) + 64;
-    cp.pcode = (int)((kChunk * (kDim - kk) * 4 + 31) / 32) + 64;
-    cp.field = (int)((kChunk * kk * (1 + mm) + 31) / 32) + 8;  // (a run may start mid-word)
-    cp.low = (int)((kChunk * kk * (7 - mm) + 31) / 32) + 8;
-    cp.pbyte = (int)((kChunk * (kDim - kk) + 3) / 4) + 8;
+    cp.scode = (int)((kXChunk * kk * 4 + 31) / 32) + 64;
+    cp.pcode = (int)((kXChunk * (kDim - kk) * 4 + 31) / 32) + 64;
+    cp.field = (int)((kXChunk * kk * (1 + mm) + 31) / 32) + 8;  // (a run may start mid-word)
+    cp.low = (int)((kXChunk * kk * (7 - mm) + 31) / 32) + 8;
+    cp.pbyte = (int)((kXChunk * (kDim - kk) + 3) / 4) + 8;
     const int64_t xl = x1_lds_bytes(cp);
     hipError_t e = hipFuncSetAttribute((const void*)&k_kv_attn_x1,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)xl);
     if (e == hipSuccess) {
-      k_kv_attn_x1<<<dim3(H, a.nchunks), kXThreads, (size_t)xl, stream>>>(d, a, cp);
+      k_kv_attn_x1<<<dim3(H, ax.nchunks), kXThreads, (size_t)xl, stream>>>(d, ax, cp);
       e = hipGetLastError();
     }
     if (e != hipSuccess) return report(CASS_ERR_HIP, "attention: %s", hipGetErrorString(e));
-    k_kv_merge<<<H * nq * G, kDim * kMergeParts, 0, stream>>>(a, H, out);
+    k_kv_merge<<<H * nq * G, kDim * kMergeParts, 0, stream>>>(ax, H, out);
     if ((e = hipGetLastError()) != hipSuccess) return report(CASS_ERR_HIP, "merge: %s", hipGetErrorString(e));
     return CASS_OK;
   }
@@ -1889,7 +1907,7 @@ int cass_kv_draft_attn_static(const cass_kv* kv, const uint16_t* q, int n_q_head
   if (st) return st;
   if (n_q_heads < kv->p.n_kv_heads || n_q_heads % kv->p.n_kv_heads)
     return report(CASS_ERR_INVALID, "n_q_heads must be a multiple of n_kv_heads");
-  const int64_t need = attn_ws(kv, 1, n_q_heads / kv->p.n_kv_heads);
+  const int64_t need = attn_ws(kv, 1, n_q_heads / kv->p.n_kv_heads, kChunk);
   if (need > kStaticScratchBytes)
     return report(CASS_ERR_CAPACITY, "draft attention needs %lld scratch bytes, the fixed scratch holds %lld",
                   (long long)need, (long long)kStaticScratchBytes);

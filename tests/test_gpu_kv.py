@@ -237,13 +237,15 @@ def test_draft_attention_uneven_tokens(gpu, orc, fmt):
         attn_check(got[h * G:(h + 1) * G], ref, bound)
 
 
-@pytest.mark.parametrize("fmt,T", [(1, 16640), (2, 16640), (2, 66000)])
+@pytest.mark.parametrize("fmt,T", [(1, 16640), (2, 16640), (1, 33000), (2, 66000)])
 def test_attention_long_context(gpu, orc, fmt, T):
     """Draft and verification attention at contexts where the chunk merge uses
     its whole structure: 16640 tokens are 130 chunks of 128 (past 64 chunks,
-    every merge wave carries chunk maxima and sums); 66000 + 5 tokens are more
-    than 512 chunks, so the merge's strided loop runs a second pass.  All 32
-    query heads are checked against the oracle's decode plus fp64 attention."""
+    every merge wave carries chunk maxima and sums); past 512 chunks the
+    merge's strided loop runs a second pass: 66000 + 5 tokens in chunks of 128,
+    33000 + 5 in the 64-token chunks of the Cassandra-1 verification kernel.
+    All 32 query heads are checked against the oracle's decode plus fp64
+    attention."""
     torch, cass = gpu
     H, Hq, k, m, nq = 8, 32, 38, 3, 5
     G = Hq // H
