@@ -1307,8 +1307,9 @@ __global__ void __launch_bounds__(kXThreads) k_kv_attn_x1(KvDev kv, AttnArgs a, 
           cpos[which] = off;
         }
       }
-      cpos[0] = skip_codes(cw[0], cpos[0], kb);
-      cpos[1] = skip_codes(cw[1], cpos[1], pb);
+      // (staged runs have 64 words of slack: the first 256 bits in one round trip)
+      cpos[0] = cfirst[j][0] >= 0 ? skip_codes8(cw[0], cpos[0], kb) : skip_codes(cw[0], cpos[0], kb);
+      cpos[1] = cfirst[j][1] >= 0 ? skip_codes8(cw[1], cpos[1], pb) : skip_codes(cw[1], cpos[1], pb);
       const uint8_t* ps = tabs[2 * j];
       const uint8_t* pv = tabs[2 * j + 1];
       const int fwd = 1 + m, lwd = 7 - m;
