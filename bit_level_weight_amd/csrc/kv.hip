@@ -880,7 +880,7 @@ __global__ void __launch_bounds__(2 * kChunk) k_kv_attn(KvDev kv, AttnArgs a) {
   float* sc = qf + MAXR * kDim;                              // [MAXR][kChunk]
   uint16_t* vt = reinterpret_cast<uint16_t*>(sc + MAXR * kChunk);  // [kChunk][130]
   __shared__ float red[MAXR][kChunk / 64];
-  __shared__ uint8_t tabs[4][256];  // rank tables: K spec, K verif, V spec, V verif
+  __shared__ __align__(16) uint8_t tabs[4][256];  // rank tables: K spec, K verif, V spec, V verif
   const int h = blockIdx.x, c = blockIdx.y;
   const int rows = a.nq * a.G;
   const int tid = threadIdx.x;
@@ -1189,6 +1189,8 @@ __host__ __device__ __forceinline__ int64_t x1_lds_bytes(const XCaps& cp) {
          (int64_t)kXRows * kXChunk * 4 + (int64_t)2 * cp.per_stream() * 4;
 }
 
+typedef __attribute__((address_space(3))) void lds_void;
+
 // bf16 bits of x rounded to nearest even (x finite).
 __device__ __forceinline__ uint32_t x1_bf16_rne(float x) {
   const uint32_t u = __float_as_uint(x);
@@ -1214,13 +1216,26 @@ __global__ void __launch_bounds__(kXThreads) k_kv_attn_x1(KvDev kv, AttnArgs a, 
   const int psw = cp.per_stream();
   // staged words of stream j: codes (spec, pruned), fields, low mantissas, pruned bytes
   auto sbase = [&](int j) { return stg + j * psw; };
-  const int64_t fw0 = (t0 * k * (1 + m)) >> 5, lw0 = (t0 * k * (7 - m)) >> 5, bw0 = (t0 * np) >> 2;
-  for (int i = tid; i < 4 * 256; i += kXThreads) {
-    const int s = 2 * h + (i >> 9), which = (i >> 8) & 1;
-    const uint8_t* src = which ? kv.verif + s * kv.vstride + kv.vo[0] : kv.spec + s * kv.sstride + kv.so[0];
-    tabs[i >> 8][i & 255] = src[i & 255];
-  }
-  // 1. code runs of the chunk: [offset of t0, offset of t1 or the stream tail)
+  // staged copies start at the 16-byte boundary at or before the chunk's first word
+  const int64_t fw0 = ((t0 * k * (1 + m)) >> 5) & ~(int64_t)3,
+                lw0 = ((t0 * k * (7 - m)) >> 5) & ~(int64_t)3, bw0 = ((t0 * np) >> 2) & ~(int64_t)3;
+  const int l64 = tid & 63, w64 = tid >> 6;
+  // LDS DMA of up to n words from word a0 (a multiple of 4) of src, never past
+  // word lim: 64 chunks of 16 bytes per instruction, the waves' runs
+  // interleaved; the last 0-3 words of a run that ends inside a chunk by plain
+  // loads.  Completion: vmcnt(0) in every wave, then a barrier.
+  auto dma = [&](uint32_t* dst, const uint32_t* src, int64_t a0, int n, int64_t lim) {
+    int64_t a1 = a0 + n < lim ? a0 + n : lim;
+    if (a1 < a0) a1 = a0;
+    const int nw = (int)(a1 - a0), nch = nw >> 2;
+    for (int base = w64 * 64; base < nch; base += kXThreads)
+      if (base + l64 < nch)
+        __builtin_amdgcn_global_load_lds((const void*)(src + a0 + 4 * (base + l64)),
+                                         (lds_void*)(dst + 4 * base), 16, 0, 0);
+    if (tid < (nw & 3)) dst[4 * nch + tid] = src[a0 + 4 * nch + tid];
+  };
+  // 1. code runs of the chunk: [offset of t0, offset of t1 or the stream tail);
+  // wave 0 finds them while the other waves start the fixed-width copies
   if (tid < 4) {
     const int j = tid >> 1, which = tid & 1;
     const int s = 2 * h + j;
@@ -1229,37 +1244,48 @@ __global__ void __launch_bounds__(kXThreads) k_kv_attn_x1(KvDev kv, AttnArgs a, 
     const uint32_t b0 = offs[t0];
     const unsigned long long b1 = t1 < kv.T_max && t1 < a.T ? (unsigned long long)offs[t1]
                                                             : kv.state[2 + 2 * s + which];
-    const int cap = which ? cp.pcode : cp.scode;
+    const int room = (which ? cp.pcode : cp.scode) - 8;  // words a staged run may take
     long long first = -1;
     if (b0 != 0xFFFFFFFFu && b1 != 0xFFFFFFFFull && b1 >= b0 &&
-        (long long)((b1 + 31) >> 5) + 4 - (long long)(b0 >> 5) <= cap)
-      first = (long long)(b0 >> 5);
+        (long long)((b1 + 31) >> 5) + 4 - (long long)((b0 >> 5) & ~3u) <= room)
+      first = (long long)((b0 >> 5) & ~3u);
     cfirst[j][which] = first;
   }
-  __syncthreads();
+  if (w64 == 1) {
+    // the four rank tables: 16 chunks each
+    const int s = 2 * h + (l64 >> 5), which = (l64 >> 4) & 1;
+    const uint8_t* src = which ? kv.verif + s * kv.vstride + kv.vo[0] : kv.spec + s * kv.sstride + kv.so[0];
+    __builtin_amdgcn_global_load_lds((const void*)(src + 16 * (l64 & 15)), (lds_void*)&tabs[0][0], 16,
+                                     0, 0);
+  }
   for (int j = 0; j < 2; ++j) {
     const int s = 2 * h + j;
     const uint8_t* sr = kv.spec + s * kv.sstride;
     const uint8_t* vr = kv.verif + s * kv.vstride;
-    uint32_t* b = sbase(j);
+    uint32_t* b = sbase(j) + cp.scode + cp.pcode;
+    dma(b, reinterpret_cast<const uint32_t*>(sr + kv.so[3]), fw0, cp.field - 8,
+        (kv.T_max * k * (1 + m) + 31) / 32 + 4);
+    b += cp.field;
+    dma(b, reinterpret_cast<const uint32_t*>(vr + kv.vo[1]), lw0, cp.low - 8,
+        (kv.T_max * k * (7 - m) + 31) / 32 + 4);
+    b += cp.low;
+    dma(b, reinterpret_cast<const uint32_t*>(vr + kv.vo[2]), bw0, cp.pbyte - 8,
+        (kv.T_max * np + 3) / 4 + 4);
+  }
+  __syncthreads();  // the code runs' starts
+  for (int j = 0; j < 2; ++j) {
+    const int s = 2 * h + j;
+    const uint8_t* sr = kv.spec + s * kv.sstride;
+    const uint8_t* vr = kv.verif + s * kv.vstride;
     for (int which = 0; which < 2; ++which) {
       const long long first = cfirst[j][which];
       if (first < 0) continue;
       const uint32_t* src = reinterpret_cast<const uint32_t*>(which ? vr + kv.vo[4] : sr + kv.so[4]);
       const int64_t lim = ((which ? kv.vcap : kv.ccap) + 31) / 32 + 4;  // plus the zero pad
-      copy_words(b + (which ? cp.scode : 0), src, first, which ? cp.pcode : cp.scode, lim, tid,
-                 kXThreads);
+      dma(sbase(j) + (which ? cp.scode : 0), src, first, (which ? cp.pcode : cp.scode) - 8, lim);
     }
-    b += cp.scode + cp.pcode;
-    copy_words(b, reinterpret_cast<const uint32_t*>(sr + kv.so[3]), fw0, cp.field,
-               (kv.T_max * k * (1 + m) + 31) / 32 + 4, tid, kXThreads);
-    b += cp.field;
-    copy_words(b, reinterpret_cast<const uint32_t*>(vr + kv.vo[1]), lw0, cp.low,
-               (kv.T_max * k * (7 - m) + 31) / 32 + 4, tid, kXThreads);
-    b += cp.low;
-    copy_words(b, reinterpret_cast<const uint32_t*>(vr + kv.vo[2]), bw0, cp.pbyte,
-               (kv.T_max * np + 3) / 4 + 4, tid, kXThreads);
   }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies
   __syncthreads();
 
   // 2. exact values: thread = (stream j, token, keep word w)
@@ -1679,11 +1705,14 @@ int run_attention(const cass_kv* kv, const uint16_t* q, int nq, int n_q_heads, f
     AttnArgs ax = a;
     ax.nchunks = (int)((kv->tokens + kXChunk - 1) / kXChunk);
     XCaps cp;
-    cp.scode = (int)((kXChunk * kk * 4 + 31) / 32) + 64;
-    cp.pcode = (int)((kXChunk * (kDim - kk) * 4 + 31) / 32) + 64;
-    cp.field = (int)((kXChunk * kk * (1 + mm) + 31) / 32) + 8;  // (a run may start mid-word)
-    cp.low = (int)((kXChunk * kk * (7 - mm) + 31) / 32) + 8;
-    cp.pbyte = (int)((kXChunk * (kDim - kk) + 3) / 4) + 8;
+    // (regions in whole 16-byte chunks; 8 words beyond what a run may take,
+    // which covers a copy that starts up to 3 words early and a chunk's tail)
+    auto r4 = [](int64_t w) { return (int)((w + 3) / 4 * 4); };
+    cp.scode = r4((kXChunk * kk * 4 + 31) / 32 + 64 + 8);
+    cp.pcode = r4((kXChunk * (kDim - kk) * 4 + 31) / 32 + 64 + 8);
+    cp.field = r4((kXChunk * kk * (1 + mm) + 31) / 32 + 8 + 8);  // (a run may start mid-word)
+    cp.low = r4((kXChunk * kk * (7 - mm) + 31) / 32 + 8 + 8);
+    cp.pbyte = r4((kXChunk * (kDim - kk) + 3) / 4 + 8 + 8);
     const int64_t xl = x1_lds_bytes(cp);
     hipError_t e = hipFuncSetAttribute((const void*)&k_kv_attn_x1,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)xl);
