@@ -838,33 +838,33 @@ struct AttnArgs {
 };
 
 // Draft attention: the chunk's speculation sections of K and V, copied to
-// shared memory before the decode (words past a section's end read as 0).
-// Per stream: keep words [kChunk][D/32], fields (fcap words from the word
-// holding the chunk's first field bit), codes (C-1: ccap words from the word
-// holding the first token's first code bit) or shared exponents (C-2:
-// [kChunk][D/32] bytes).
-// n words src[g0 + i] (0 past word `lim`) to dst[i], by nthr threads: eight
-// loads per thread issued before their stores, so a batch waits on memory once.
-__device__ __forceinline__ void copy_words(uint32_t* dst, const uint32_t* src, int64_t g0, int n,
-                                           int64_t lim, int tid, int nthr) {
-  for (int b = 0; b < n; b += 8 * nthr) {
-    uint32_t v[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int i = b + j * nthr + tid;
-      const int64_t g = g0 + i;
-      v[j] = (i < n && g < lim) ? src[g] : 0u;
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int i = b + j * nthr + tid;
-      if (i < n) dst[i] = v[j];
-    }
-  }
-}
+// shared memory before the decode.  Per stream: keep words [kChunk][D/32],
+// fields (fcap words from the 16-byte boundary at or before the chunk's first
+// field bit), codes (C-1: ccap words from the 16-byte boundary at or before
+// the first token's first code bit) or shared exponents (C-2: [kChunk][D/32]
+// bytes).
 
 __host__ __device__ __forceinline__ int staged_words(int fcap, int ccap, int fmt) {
   return kChunk * (kDim / 32) + fcap + (fmt == CASS_FMT_C1_UNARY ? ccap : kChunk);
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// LDS DMA of up to n words from word a0 (a multiple of 4) of src, never past
+// word lim, to dst (16-byte aligned): 64 chunks of 16 bytes per instruction,
+// the waves' runs interleaved; the last 0-3 words of a run that ends inside a
+// chunk by plain loads.  Completion: vmcnt(0) in every wave, then a barrier.
+__device__ __forceinline__ void dma_words(uint32_t* dst, const uint32_t* src, int64_t a0, int n,
+                                          int64_t lim, int tid, int nthr) {
+  const int l64 = tid & 63, w64 = tid >> 6;
+  int64_t a1 = a0 + n < lim ? a0 + n : lim;
+  if (a1 < a0) a1 = a0;
+  const int nw = (int)(a1 - a0), nch = nw >> 2;
+  for (int base = w64 * 64; base < nch; base += nthr)
+    if (base + l64 < nch)
+      __builtin_amdgcn_global_load_lds((const void*)(src + a0 + 4 * (base + l64)),
+                                       (lds_void*)(dst + 4 * base), 16, 0, 0);
+  if (tid < (nw & 3)) dst[4 * nch + tid] = src[a0 + 4 * nch + tid];
 }
 
 // MAXR: a bound on the query rows (nq * G) the launch serves.  Shared
@@ -884,10 +884,19 @@ __global__ void __launch_bounds__(2 * kChunk) k_kv_attn(KvDev kv, AttnArgs a) {
   const int h = blockIdx.x, c = blockIdx.y;
   const int rows = a.nq * a.G;
   const int tid = threadIdx.x;
-  for (int i = tid; i < 4 * 256; i += 2 * kChunk) {
-    const int s = 2 * h + (i >> 9), which = (i >> 8) & 1;
+  if (EXACT) {
+    for (int i = tid; i < 4 * 256; i += 2 * kChunk) {
+      const int s = 2 * h + (i >> 9), which = (i >> 8) & 1;
+      const uint8_t* src = which ? kv.verif + s * kv.vstride + kv.vo[0] : kv.spec + s * kv.sstride + kv.so[0];
+      tabs[i >> 8][i & 255] = src[i & 255];
+    }
+  } else if ((tid >> 6) == 1) {
+    // the four rank tables by LDS DMA: 16 chunks each
+    const int l = tid & 63;
+    const int s = 2 * h + (l >> 5), which = (l >> 4) & 1;
     const uint8_t* src = which ? kv.verif + s * kv.vstride + kv.vo[0] : kv.spec + s * kv.sstride + kv.so[0];
-    tabs[i >> 8][i & 255] = src[i & 255];
+    __builtin_amdgcn_global_load_lds((const void*)(src + 16 * (l & 15)), (lds_void*)&tabs[0][0], 16, 0,
+                                     0);
   }
   // query rows of this KV head: row r = qi * G + g  (query qi, head h*G + g)
   for (int idx = tid; idx < MAXR * kDim; idx += 2 * kChunk) {  // rows past `rows` stay zero
@@ -901,26 +910,28 @@ __global__ void __launch_bounds__(2 * kChunk) k_kv_attn(KvDev kv, AttnArgs a) {
   const int fwid = FMT == CASS_FMT_C1_UNARY ? 1 + kv.m : 2 + kv.m;
   const int sw = staged_words(a.fcap, a.ccap, FMT);
   uint32_t* stg = reinterpret_cast<uint32_t*>(vt + kChunk * kVStride);
-  const int64_t fw0 = (t0 * kv.k * fwid) >> 5;  // first staged field word
-  int64_t cw0[2] = {0, 0};                        // first staged code word per stream
+  // (staged runs start at the 16-byte boundary at or before their first word)
+  const int64_t fw0 = ((t0 * kv.k * fwid) >> 5) & ~(int64_t)3;  // first staged field word
+  int64_t cw0[2] = {0, 0};                                      // first staged code word per stream
   if (!EXACT) {
+    // every copy by LDS DMA, all in flight at once
     for (int j = 0; j < 2; ++j) {
       const uint8_t* sr = kv.spec + (2 * h + j) * kv.sstride;
       uint32_t* base = stg + j * sw;
-      copy_words(base, reinterpret_cast<const uint32_t*>(sr + kv.so[1]), t0 * (kDim / 32),
-                 kChunk * (kDim / 32), kv.T_max * (kDim / 32), tid, 2 * kChunk);
-      copy_words(base + kChunk * (kDim / 32), reinterpret_cast<const uint32_t*>(sr + kv.so[3]), fw0,
-                 a.fcap, (kv.T_max * kv.k * fwid + 31) / 32, tid, 2 * kChunk);
+      dma_words(base, reinterpret_cast<const uint32_t*>(sr + kv.so[1]), t0 * (kDim / 32),
+                kChunk * (kDim / 32), kv.T_max * (kDim / 32), tid, 2 * kChunk);
+      dma_words(base + kChunk * (kDim / 32), reinterpret_cast<const uint32_t*>(sr + kv.so[3]), fw0,
+                a.fcap, (kv.T_max * kv.k * fwid + 31) / 32, tid, 2 * kChunk);
       uint32_t* rest = base + kChunk * (kDim / 32) + a.fcap;
       if (FMT == CASS_FMT_C1_UNARY) {
         const uint32_t o0 = reinterpret_cast<const uint32_t*>(sr + kv.so[2])[t0];
-        cw0[j] = o0 == 0xFFFFFFFFu ? 0 : (int64_t)(o0 >> 5);
-        copy_words(rest, reinterpret_cast<const uint32_t*>(sr + kv.so[4]), cw0[j], a.ccap,
-                   (kv.ccap + 31) / 32, tid, 2 * kChunk);
+        cw0[j] = o0 == 0xFFFFFFFFu ? 0 : (int64_t)((o0 >> 5) & ~3u);
+        dma_words(rest, reinterpret_cast<const uint32_t*>(sr + kv.so[4]), cw0[j], a.ccap,
+                  (kv.ccap + 31) / 32, tid, 2 * kChunk);
       } else {
         // shared exponents: D/32 = 4 bytes, one word, per token
-        copy_words(rest, reinterpret_cast<const uint32_t*>(sr + kv.so[2]), t0, kChunk, kv.T_max,
-                   tid, 2 * kChunk);
+        dma_words(rest, reinterpret_cast<const uint32_t*>(sr + kv.so[2]), t0, kChunk, kv.T_max,
+                  tid, 2 * kChunk);
       }
     }
   }
@@ -930,6 +941,7 @@ __global__ void __launch_bounds__(2 * kChunk) k_kv_attn(KvDev kv, AttnArgs a) {
     typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
     u32x4v* vt4 = reinterpret_cast<u32x4v*>(vt);
     for (int i = tid; i < kChunk * kVStride * 2 / 16; i += 2 * kChunk) vt4[i] = u32x4v{0, 0, 0, 0};
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies
   }
   __syncthreads();
   const int ti = tid & (kChunk - 1);
@@ -1189,8 +1201,6 @@ __host__ __device__ __forceinline__ int64_t x1_lds_bytes(const XCaps& cp) {
          (int64_t)kXRows * kXChunk * 4 + (int64_t)2 * cp.per_stream() * 4;
 }
 
-typedef __attribute__((address_space(3))) void lds_void;
-
 // bf16 bits of x rounded to nearest even (x finite).
 __device__ __forceinline__ uint32_t x1_bf16_rne(float x) {
   const uint32_t u = __float_as_uint(x);
@@ -1220,19 +1230,8 @@ __global__ void __launch_bounds__(kXThreads) k_kv_attn_x1(KvDev kv, AttnArgs a, 
   const int64_t fw0 = ((t0 * k * (1 + m)) >> 5) & ~(int64_t)3,
                 lw0 = ((t0 * k * (7 - m)) >> 5) & ~(int64_t)3, bw0 = ((t0 * np) >> 2) & ~(int64_t)3;
   const int l64 = tid & 63, w64 = tid >> 6;
-  // LDS DMA of up to n words from word a0 (a multiple of 4) of src, never past
-  // word lim: 64 chunks of 16 bytes per instruction, the waves' runs
-  // interleaved; the last 0-3 words of a run that ends inside a chunk by plain
-  // loads.  Completion: vmcnt(0) in every wave, then a barrier.
   auto dma = [&](uint32_t* dst, const uint32_t* src, int64_t a0, int n, int64_t lim) {
-    int64_t a1 = a0 + n < lim ? a0 + n : lim;
-    if (a1 < a0) a1 = a0;
-    const int nw = (int)(a1 - a0), nch = nw >> 2;
-    for (int base = w64 * 64; base < nch; base += kXThreads)
-      if (base + l64 < nch)
-        __builtin_amdgcn_global_load_lds((const void*)(src + a0 + 4 * (base + l64)),
-                                         (lds_void*)(dst + 4 * base), 16, 0, 0);
-    if (tid < (nw & 3)) dst[4 * nch + tid] = src[a0 + 4 * nch + tid];
+    dma_words(dst, src, a0, n, lim, tid, kXThreads);
   };
   // 1. code runs of the chunk: [offset of t0, offset of t1 or the stream tail);
   // wave 0 finds them while the other waves start the fixed-width copies
@@ -1692,8 +1691,9 @@ int run_attention(const cass_kv* kv, const uint16_t* q, int nq, int n_q_heads, f
     // draft staging: every field of the chunk, and codes averaging up to 4
     // bits per kept value (longer runs read their codes from global memory)
     const int fwid = fmt_of(&kv->p) == CASS_FMT_C1_UNARY ? 1 + kv->p.mant_bits : 2 + kv->p.mant_bits;
-    a.fcap = (int)(((int64_t)kChunk * kv->p.keep * fwid + 31) / 32) + 8;
-    a.ccap = (int)((int64_t)kChunk * kv->p.keep * 4 / 32) + 64;
+    // (multiples of 4 words: the staged regions stay 16-byte aligned)
+    a.fcap = (int)(((int64_t)kChunk * kv->p.keep * fwid + 31) / 32 + 8 + 3) / 4 * 4;
+    a.ccap = (int)(((int64_t)kChunk * kv->p.keep * 4 / 32 + 64 + 3) / 4 * 4);
   }
   const KvDev d = dev_of(kv);
   const size_t lds = 0;  // per launch, from the row bound (attn_launch_f)
