@@ -880,6 +880,7 @@ __global__ void __launch_bounds__(2 * kChunk) k_kv_attn(KvDev kv, AttnArgs a) {
   float* sc = qf + MAXR * kDim;                              // [MAXR][kChunk]
   uint16_t* vt = reinterpret_cast<uint16_t*>(sc + MAXR * kChunk);  // [kChunk][130]
   __shared__ float red[MAXR][kChunk / 64];
+  __shared__ float lsum[MAXR][kChunk / 64];  // (up to 4 rows) per-wave sums of p
   __shared__ __align__(16) uint8_t tabs[4][256];  // rank tables: K spec, K verif, V spec, V verif
   const int h = blockIdx.x, c = blockIdx.y;
   const int rows = a.nq * a.G;
@@ -1075,6 +1076,60 @@ __global__ void __launch_bounds__(2 * kChunk) k_kv_attn(KvDev kv, AttnArgs a) {
     }
   }
   __syncthreads();
+  if (MAXR == 4) {
+    // up to 4 rows: p also as [token][4] over the queries (no longer read), the
+    // row sums by wave reductions; then o[r][d] = sum_t p[r][t] V[t][d] with
+    // thread (d, half of the tokens) reading each value once for every row
+    float* pt = qf;  // [kChunk][4]
+    if (tid < kChunk) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float p = 0.f;
+        if (r < rows) {
+          const float mx = fmaxf(red[r][0], red[r][1]);
+          const float sv = sc[r * kChunk + ti];
+          p = (mx == -INFINITY || sv == -INFINITY) ? 0.f : __expf(sv - mx);
+        }
+        pt[ti * 4 + r] = p;
+        float l = p;
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) l += __shfl_xor(l, o, 64);
+        if (lane == 0) lsum[r][wv] = l;
+      }
+    }
+    __syncthreads();
+    const int d = tid & (kDim - 1), half = tid >> 7;
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    typedef float f4v __attribute__((ext_vector_type(4)));
+#pragma unroll 8
+    for (int t = half * (kChunk / 2); t < (half + 1) * (kChunk / 2); ++t) {
+      const float v = bf16_bits_to_float(vt[t * kVStride + d]);
+      const f4v p4 = *reinterpret_cast<const f4v*>(pt + 4 * t);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[r] = __builtin_fmaf(p4[r], v, acc[r]);
+    }
+    float* other = sc;  // [kDim][4]: the second half's sums (the scores are dead)
+    if (half == 1) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) other[d * 4 + r] = acc[r];
+    }
+    __syncthreads();
+    if (half == 0) {
+      float* part = a.part + (((int64_t)h * a.nchunks + c) * rows) * (2 + kDim);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if (r < rows) {
+          float* pr = part + (int64_t)r * (2 + kDim);
+          pr[2 + d] = acc[r] + other[d * 4 + r];
+          if (d == 0) {
+            pr[0] = fmaxf(red[r][0], red[r][1]);
+            pr[1] = lsum[r][0] + lsum[r][1];
+          }
+        }
+      }
+    }
+    return;
+  }
   if (tid < kChunk) {
     for (int r = 0; r < rows; ++r) {
       const float mx = fmaxf(red[r][0], red[r][1]);
