@@ -18,6 +18,7 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libcassandra.so")
+DEBUG_LIB_PATH = os.path.join(_HERE, "libcassandra_debug.so")
 
 CASS_OK, CASS_ERR_INVALID, CASS_ERR_UNSUPPORTED, CASS_ERR_OVERFLOW, CASS_ERR_CORRUPT, \
     CASS_ERR_CAPACITY, CASS_ERR_HIP = range(7)
@@ -34,8 +35,11 @@ EXPORTED = (
     "cass_kv_verify_attn", "cass_set_option", "cass_stream_read", "cass_kv_draft_attn_static",
     "cass_kv_truncate", "cass_prefix_code_huffman", "cass_prefix_code_unary",
     "cass_prefix_stream_bits", "cass_prefix_encode", "cass_prefix_decode_ws_bytes",
-    "cass_prefix_decode",
+    "cass_prefix_decode", "cass_debug_flags",
 )
+CASS_DBG_STAGE, CASS_DBG_ALIGN, CASS_DBG_TILE, CASS_DBG_WINDOW = 1, 2, 4, 8
+# the same sources built with CASS_DEBUG (device bounds checks); load it in
+# place of the release library by pointing LIB_PATH here before lib()
 CASS_PREFIX_TABLE, CASS_PREFIX_UNARY_SERIAL, CASS_PREFIX_UNARY_PARALLEL = 1, 2, 3
 CASS_STREAM_READ_BLOCKS = 2048
 CASS_KV_STATE_BYTES = 4096
@@ -127,6 +131,7 @@ def lib():
         L.cass_last_error.argtypes = []
         L.cass_last_error.restype = ctypes.c_char_p
         L.cass_version.argtypes = []
+        L.cass_debug_flags.argtypes = [ctypes.POINTER(ctypes.c_uint32)]
         L.cass_set_option.argtypes = [ctypes.c_char_p, I64]
         L.cass_stream_read.argtypes = [P, I64, P, P]
         KP, KV = ctypes.POINTER(CassKvParams), ctypes.POINTER(CassKv)
@@ -247,6 +252,14 @@ def cass_tensor_validate(spec: np.ndarray, verif: np.ndarray | None = None) -> i
 
 def cass_version() -> int:
     return lib().cass_version()
+
+
+def cass_debug_flags() -> int:
+    """CASS_DBG_* bits the debug library's device bounds checks raised since
+    the previous call (then cleared); raises CassError on the release library."""
+    v = ctypes.c_uint32(0)
+    _check(lib().cass_debug_flags(ctypes.byref(v)))
+    return int(v.value)
 
 
 def cass_set_option(name: str, value: int):

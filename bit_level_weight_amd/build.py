@@ -1,11 +1,15 @@
 """Build libcassandra.so in-tree with hipcc for gfx950.
 
-    python -m bit_level_weight_amd.build
+    python -m bit_level_weight_amd.build          # release library
+    python -m bit_level_weight_amd.build debug    # libcassandra_debug.so
 
 Every .hip / .cpp file under csrc/ is compiled with the same flags and
 linked into bit_level_weight_amd/libcassandra.so.  Device assembly of every
 kernel file is also produced and screened (isa_check) before the library is
 published, so that a kernel that writes through the scalar cache never ships.
+The debug library is the same sources compiled with CASS_DEBUG: device
+bounds checks that record a flag instead of reading or writing out of range
+(cass_debug_flags).
 """
 from __future__ import annotations
 
@@ -21,6 +25,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libcassandra.so")
+LIB_DEBUG = os.path.join(HERE, "libcassandra_debug.so")
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -39,37 +44,40 @@ def _run(cmd):
     return p.stdout
 
 
-def _compile(src):
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *COMMON, "-c", src, "-o", obj]
+def _compile(src, debug=False):
+    out = os.path.join(BUILD, "debug") if debug else BUILD
+    flags = COMMON + (["-DCASS_DEBUG"] if debug else [])
+    obj = os.path.join(out, os.path.basename(src) + ".o")
+    cmd = [HIPCC, *flags, "-c", src, "-o", obj]
     if src.endswith(".cpp"):
-        cmd = [HIPCC, *COMMON, "-x", "hip", "-c", src, "-o", obj]
+        cmd = [HIPCC, *flags, "-x", "hip", "-c", src, "-o", obj]
     _run(cmd)
     asm = None
     if src.endswith(".hip"):
-        asm = os.path.join(BUILD, os.path.basename(src) + ".s")
-        _run([HIPCC, *COMMON, "--cuda-device-only", "-S", src, "-o", asm])
+        asm = os.path.join(out, os.path.basename(src) + ".s")
+        _run([HIPCC, *flags, "--cuda-device-only", "-S", src, "-o", asm])
     return obj, asm
 
 
-def build(verbose: bool = True) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose: bool = True, debug: bool = False) -> str:
+    os.makedirs(os.path.join(BUILD, "debug") if debug else BUILD, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
     with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        results = list(ex.map(_compile, srcs))
+        results = list(ex.map(lambda s: _compile(s, debug), srcs))
     objs = [o for o, _ in results]
     asms = [a for _, a in results if a]
     from . import isa_check  # build-time screen, not needed at run time
     isa_check.check(asms)
-    tmp = LIB + ".tmp"
+    lib = LIB_DEBUG if debug else LIB
+    tmp = lib + ".tmp"
     _run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp])
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     if verbose:
-        print(f"built {LIB} from {len(srcs)} sources")
-    return LIB
+        print(f"built {lib} from {len(srcs)} sources")
+    return lib
 
 
 if __name__ == "__main__":
     if len(sys.argv) > 1 and sys.argv[1] == "clean":
         shutil.rmtree(BUILD, ignore_errors=True)
-    build()
+    build(debug=len(sys.argv) > 1 and sys.argv[1] == "debug")

@@ -332,6 +332,13 @@ int device_cu_count() {
   return cache[dev];
 }
 
+// Readers of the translation units' debug flag words (debug build).
+std::vector<uint32_t (*)()>& debug_registry() {
+  static std::vector<uint32_t (*)()> r;
+  return r;
+}
+void debug_register(uint32_t (*read_and_clear)()) { debug_registry().push_back(read_and_clear); }
+
 }  // namespace cass
 
 using namespace cass;
@@ -339,6 +346,18 @@ using namespace cass;
 extern "C" {
 
 int cass_version(void) { return CASS_VERSION; }
+
+int cass_debug_flags(uint32_t* flags) {
+  g_last_error.clear();
+  if (!flags) return fail(CASS_ERR_INVALID, "flags is NULL");
+  *flags = 0;
+#ifdef CASS_DEBUG
+  for (auto f : debug_registry()) *flags |= f();
+  return CASS_OK;
+#else
+  return fail(CASS_ERR_UNSUPPORTED, "device bounds checks are in the debug build only");
+#endif
+}
 
 const char* cass_last_error(void) { return g_last_error.c_str(); }
 

@@ -300,6 +300,7 @@ __device__ __forceinline__ void kept_step(uint32_t sb, uint32_t& bp, uint32_t bp
     w = lwin(sb, bp);
   }
   const uint32_t pos = bp + (uint32_t)__builtin_ctz(w);
+  CASS_DCHECK(pos < bp_end, CASS_DBG_TILE);
   bp = pos + 1u;
   const uint32_t f = lwin(sb, fp) & ((1u << fw) - 1u);
   fp += (uint32_t)fw;
@@ -319,6 +320,7 @@ __device__ __forceinline__ void pruned_step(uint32_t sb, uint32_t& bp, uint32_t 
     w = ~lwin(sb, bp);
   }
   const uint32_t pos = bp + (uint32_t)__builtin_ctz(w);
+  CASS_DCHECK(pos < bp_end, CASS_DBG_TILE);
   bp = pos + 1u;
   const uint32_t byte = lwin(sb, yp) & 0xFFu;
   yp += 8u;
@@ -545,6 +547,7 @@ __global__ void __launch_bounds__(64 * kMaxWaves) k_exact_staged(SpecViewC1 sv, 
       if (sec < 4) {
         off = wbase + g.fix_off + foff;
         foff += 16 * N;
+        CASS_DCHECK(foff <= g.fix_cap, CASS_DBG_STAGE);
       } else {
         if (coff + 16 * N > g.cod_cap) overflow = true;
         off = wbase + g.cod_off + coff;

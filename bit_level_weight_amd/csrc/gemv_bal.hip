@@ -103,6 +103,7 @@ typedef __attribute__((address_space(4))) const unsigned long long const_u64;
 // LDS address is the wave's, so dst must be uniform).  Nontemporal: each
 // byte is read once.  Completion is awaited by wait_dma.
 __device__ __forceinline__ void dma_run(const u32x4* src, u32x4* dst, int n, int lane) {
+  CASS_DCHECK((((uintptr_t)src | (uintptr_t)dst) & 15) == 0, CASS_DBG_ALIGN);
   for (int base = 0; base < n; base += 64)
     if (base + lane < n)
       __builtin_amdgcn_global_load_lds((const void*)(src + base + lane), (lds_void*)(dst + base),
@@ -332,28 +333,34 @@ __global__ void __launch_bounds__(kBalThreads) k_gemv_c1_bal(SpecViewC1 v, Shape
   auto stage_fixed = [&](const Plan& pl) {
     const int64_t e0 = pl.row0 * nb, e1 = e0 + (int64_t)pl.rows_here * nb;
     const int64_t kb1 = std::min<int64_t>((e1 + 7) & ~(int64_t)7, v.keptb_limit);
+    CASS_DCHECK(((kb1 - (e0 - pl.kb_sh)) >> 3) * 16 <= g.bo_off - g.kb_off, CASS_DBG_STAGE);
     dma_run(reinterpret_cast<const u32x4*>(v.keptb + (e0 - pl.kb_sh)),
             reinterpret_cast<u32x4*>(kb_l), (int)((kb1 - (e0 - pl.kb_sh)) >> 3), lane);
     if (SB) {
       // u16 block offsets (eight per chunk) and u64 superblock bases (two per chunk)
       const int64_t o1 = std::min<int64_t>((e1 + 7) & ~(int64_t)7, 2 * v.blkoff_limit);
+      CASS_DCHECK(((o1 - (e0 - pl.bo_sh)) >> 3) * 16 <= g.sb_off - g.bo_off, CASS_DBG_STAGE);
       dma_run(reinterpret_cast<const u32x4*>(v.blkoff16 + (e0 - pl.bo_sh)),
               reinterpret_cast<u32x4*>(bo16_l), (int)((o1 - (e0 - pl.bo_sh)) >> 3), lane);
       const int64_t s0 = pl.row0 * nsb, s1 = (pl.row0 + pl.rows_here) * nsb;
       const int64_t q1 = std::min<int64_t>((s1 + 1) & ~(int64_t)1, v.sbbase_limit);
+      CASS_DCHECK(((q1 - (s0 - pl.sb_sh)) >> 1) * 16 <= g.bm_off - g.sb_off, CASS_DBG_STAGE);
       dma_run(reinterpret_cast<const u32x4*>(v.sbbase + (s0 - pl.sb_sh)),
               reinterpret_cast<u32x4*>(sb_l), (int)((q1 - (s0 - pl.sb_sh)) >> 1), lane);
     } else {
       const int64_t bo1 = std::min<int64_t>((e1 + 3) & ~(int64_t)3, v.blkoff_limit);
+      CASS_DCHECK(((bo1 - (e0 - pl.bo_sh)) >> 2) * 16 <= g.sb_off - g.bo_off, CASS_DBG_STAGE);
       dma_run(reinterpret_cast<const u32x4*>(v.blkoff + (e0 - pl.bo_sh)),
               reinterpret_cast<u32x4*>(bo_l), (int)((bo1 - (e0 - pl.bo_sh)) >> 2), lane);
     }
     const int64_t bm1 = std::min<int64_t>(((pl.row0 + pl.rows_here) * wpr + 3) & ~(int64_t)3,
                                           v.bitmap_limit);
+    CASS_DCHECK(((bm1 - pl.bm_a0) >> 2) * 16 <= g.f_off - g.bm_off, CASS_DBG_STAGE);
     dma_run(reinterpret_cast<const u32x4*>(v.bitmap + pl.bm_a0), reinterpret_cast<u32x4*>(bm_l),
             (int)((bm1 - pl.bm_a0) >> 2), lane);
     const int64_t fb1 = (pl.row0 + pl.rows_here) * k * fw;
     const int64_t f1 = std::min<int64_t>((((fb1 + 31) >> 5) + 3) & ~(int64_t)3, v.fields_limit);
+    CASS_DCHECK(((f1 - pl.f_a0) >> 2) * 16 <= g.c_off - g.f_off, CASS_DBG_STAGE);
     dma_run(reinterpret_cast<const u32x4*>(v.fields + pl.f_a0), reinterpret_cast<u32x4*>(f_l),
             (int)((f1 - pl.f_a0) >> 2), lane);
   };
@@ -363,6 +370,7 @@ __global__ void __launch_bounds__(kBalThreads) k_gemv_c1_bal(SpecViewC1 v, Shape
     const int64_t c1 = std::min<int64_t>((((cb1 + 31) >> 5) + 3) & ~(int64_t)3, v.codes_limit);
     const int n = (int)((c1 - pl.c_a0) >> 2);
     pl.c_in_lds = n * 4 <= g.c_cap;
+    CASS_DCHECK(!pl.c_in_lds || n * 16 <= g.perm_off - g.c_off, CASS_DBG_STAGE);
     if (pl.c_in_lds)
       dma_run(reinterpret_cast<const u32x4*>(v.codes + pl.c_a0), reinterpret_cast<u32x4*>(c_l), n,
               lane);

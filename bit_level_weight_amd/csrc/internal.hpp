@@ -212,6 +212,37 @@ hipError_t launch_verify_gemm_c3(const SpecViewC2& sv, const VerifViewC3& vv, co
 
 int device_cu_count();
 
+// Debug build (CASS_DEBUG): device bounds checks.  Each translation unit has
+// its own flag words (one per lane, so the atomic is a vector one) and
+// registers a reader that returns and clears them; CASS_DCHECK compiles to
+// nothing in release builds.
+void debug_register(uint32_t (*read_and_clear)());
+#ifdef CASS_DEBUG
+namespace {
+__device__ uint32_t g_debug_bits[64];
+uint32_t debug_read_and_clear() {
+  uint32_t h[64] = {}, z[64] = {};
+  if (hipMemcpyFromSymbol(h, HIP_SYMBOL(g_debug_bits), sizeof h) != hipSuccess) return 0x80000000u;
+  if (hipMemcpyToSymbol(HIP_SYMBOL(g_debug_bits), z, sizeof z) != hipSuccess) return 0x80000000u;
+  uint32_t v = 0;
+  for (int i = 0; i < 64; ++i) v |= h[i];
+  return v;
+}
+struct DebugRegistrar {
+  DebugRegistrar() { debug_register(&debug_read_and_clear); }
+};
+DebugRegistrar g_debug_registrar;
+}  // namespace
+#define CASS_DCHECK(cond, bit)                                                 \
+  do {                                                                         \
+    if (!(cond)) atomicOr(&g_debug_bits[threadIdx.x & 63], (uint32_t)(bit));   \
+  } while (0)
+#else
+#define CASS_DCHECK(cond, bit) \
+  do {                         \
+  } while (0)
+#endif
+
 // Sets the calling thread's error text (cass_last_error) and returns status.
 int report(int status, const char* fmt, ...);
 void clear_error();

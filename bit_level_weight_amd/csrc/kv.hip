@@ -857,6 +857,7 @@ typedef __attribute__((address_space(3))) void lds_void;
 __device__ __forceinline__ void dma_words(uint32_t* dst, const uint32_t* src, int64_t a0, int n,
                                           int64_t lim, int tid, int nthr) {
   const int l64 = tid & 63, w64 = tid >> 6;
+  CASS_DCHECK((((uintptr_t)(src + a0) | (uintptr_t)dst) & 15) == 0, CASS_DBG_ALIGN);
   int64_t a1 = a0 + n < lim ? a0 + n : lim;
   if (a1 < a0) a1 = a0;
   const int nw = (int)(a1 - a0), nch = nw >> 2;
@@ -1463,6 +1464,12 @@ __global__ void __launch_bounds__(kXThreads) k_kv_attn_x1(KvDev kv, AttnArgs a, 
               (uint16_t)(((byte >> 7) << 15) | (e << 7) | (byte & 0x7F));
         }
       }
+      // every window this thread read lay inside its staged section
+      CASS_DCHECK((fpos >> 5) + 1 < (uint32_t)cp.field && (lpos >> 5) + 1 < (uint32_t)cp.low &&
+                      ((bpos * 8u) >> 5) + 1 < (uint32_t)cp.pbyte,
+                  CASS_DBG_WINDOW);
+      CASS_DCHECK(cfirst[j][0] < 0 || (cpos[0] >> 5) + 1 < (uint32_t)cp.scode, CASS_DBG_WINDOW);
+      CASS_DCHECK(cfirst[j][1] < 0 || (cpos[1] >> 5) + 1 < (uint32_t)cp.pcode, CASS_DBG_WINDOW);
     }
   }
   __syncthreads();

@@ -411,6 +411,20 @@ const char* cass_last_error(void);
 /* CASS_VERSION of the loaded library. */
 int cass_version(void);
 
+/* Device bounds checks of the debug build (libcassandra_debug.so, compiled
+ * with CASS_DEBUG; plumbing, not part of the method).  A failed check sets a
+ * CASS_DBG_* bit and the kernel carries on; *flags receives the OR of the
+ * bits raised since the previous call, which clears them.  Call after the
+ * work has completed (host only).  Release builds set *flags to 0 and return
+ * CASS_ERR_UNSUPPORTED. */
+enum {
+  CASS_DBG_STAGE = 1 << 0,  /* a staged copy would pass the end of its shared-memory region */
+  CASS_DBG_ALIGN = 1 << 1,  /* a shared-memory DMA source or target off its 16-byte boundary */
+  CASS_DBG_TILE = 1 << 2,   /* a decoded value written outside its tile row */
+  CASS_DBG_WINDOW = 1 << 3  /* a bit position outside its staged section */
+};
+int cass_debug_flags(uint32_t* flags);
+
 /* Code-path switches for tests and benchmarks, process-wide, 0 = default
  * (not part of the method; every path computes the same result):
  *   "gemv_parts"   parts per row of the balanced draft GEMV, power of two 1..64

@@ -41,6 +41,21 @@ def test_exports_every_declared_symbol(cass):
     assert set(cass.EXPORTED) == names
 
 
+def test_debug_flags_release_and_debug_builds(cass):
+    """The release library reports that its bounds checks are compiled out;
+    the debug library (same sources with CASS_DEBUG) exports the same
+    symbols."""
+    L = cass.lib()
+    v = ctypes.c_uint32(7)
+    assert L.cass_debug_flags(ctypes.byref(v)) == 2 and v.value == 0  # CASS_ERR_UNSUPPORTED
+    assert L.cass_debug_flags(None) == 1
+    if not os.path.exists(cass.DEBUG_LIB_PATH):
+        pytest.fail("libcassandra_debug.so is not built (python -m bit_level_weight_amd.build debug)")
+    D = ctypes.CDLL(cass.DEBUG_LIB_PATH)
+    for n in declared_symbols():
+        assert hasattr(D, n), n
+
+
 def test_version_and_status_strings(cass):
     L = cass.lib()
     assert L.cass_version() == 1
