@@ -2,6 +2,7 @@
 
     python -m bit_level_weight_amd.build          # release library
     python -m bit_level_weight_amd.build debug    # libcassandra_debug.so
+    python -m bit_level_weight_amd.build all      # both
 
 Every .hip / .cpp file under csrc/ is compiled with the same flags and
 linked into bit_level_weight_amd/libcassandra.so.  Device assembly of every
@@ -59,11 +60,11 @@ def _compile(src, debug=False):
     return obj, asm
 
 
-def build(verbose: bool = True, debug: bool = False) -> str:
-    os.makedirs(os.path.join(BUILD, "debug") if debug else BUILD, exist_ok=True)
-    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        results = list(ex.map(lambda s: _compile(s, debug), srcs))
+def _sources():
+    return sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
+
+
+def _link(results, debug, verbose, nsrc):
     objs = [o for o, _ in results]
     asms = [a for _, a in results if a]
     from . import isa_check  # build-time screen, not needed at run time
@@ -73,11 +74,36 @@ def build(verbose: bool = True, debug: bool = False) -> str:
     _run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp])
     os.replace(tmp, lib)
     if verbose:
-        print(f"built {lib} from {len(srcs)} sources")
+        print(f"built {lib} from {nsrc} sources")
     return lib
 
 
+def build(verbose: bool = True, debug: bool = False) -> str:
+    """One library: the release build, or with debug=True the CASS_DEBUG one."""
+    os.makedirs(os.path.join(BUILD, "debug") if debug else BUILD, exist_ok=True)
+    srcs = _sources()
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        results = list(ex.map(lambda s: _compile(s, debug), srcs))
+    return _link(results, debug, verbose, len(srcs))
+
+
+def build_all(verbose: bool = True):
+    """Both libraries, every compilation in one pool (the slowest files of the
+    two builds overlap)."""
+    os.makedirs(os.path.join(BUILD, "debug"), exist_ok=True)
+    srcs = _sources()
+    jobs = [(s, d) for d in (True, False) for s in srcs]
+    with cf.ThreadPoolExecutor(max_workers=8) as ex:
+        results = list(ex.map(lambda j: _compile(*j), jobs))
+    n = len(srcs)
+    return (_link(results[n:], False, verbose, n), _link(results[:n], True, verbose, n))
+
+
 if __name__ == "__main__":
-    if len(sys.argv) > 1 and sys.argv[1] == "clean":
+    arg = sys.argv[1] if len(sys.argv) > 1 else ""
+    if arg == "clean":
         shutil.rmtree(BUILD, ignore_errors=True)
-    build(debug=len(sys.argv) > 1 and sys.argv[1] == "debug")
+    if arg == "all":
+        build_all()
+    else:
+        build(debug=arg == "debug")
