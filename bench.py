@@ -53,7 +53,7 @@ def parse():
     ap.add_argument("--block", type=int, default=256)
     ap.add_argument("--copies", type=int, default=8)
     ap.add_argument("--mode", choices=("full", "gemv", "exact", "copy", "spec", "mxt", "codecs",
-                                       "superblock"), default="full")
+                                       "superblock", "kv"), default="full")
     ap.add_argument("--no-extras", action="store_true", help="headline and CPU baseline only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -147,6 +147,15 @@ def main():
                           run_mx_target(torch, cass, synth, timer, stream, dev16)}))
         return
 
+    if args.mode == "kv":
+        # one layer's Cassandra-1 KV cache at 32K tokens (8 KV heads x 128, 32
+        # query heads): single-token appends, draft attention, a 5-token append
+        # and verification attention, each repeated (for kernel traces and
+        # counters)
+        print(json.dumps({"mode": "kv", "kv_llama8b_32k": run_kv_profile(torch, cass, synth, dev16,
+                                                                           args.steps)}))
+        return
+
     if args.mode == "spec":
         # the speculative step over 32 layers and the dense context, nothing else
         gen = torch.Generator(device="cuda")
@@ -205,7 +214,14 @@ def main():
             for n in MATS:
                 cass.cass_reconstruct(e[n].desc, outb[n], stream)
         torch.cuda.synchronize()
-        print(json.dumps({"mode": "exact", "steps": args.steps}))
+        # algorithmic bytes per call: both streams read; X read and Y written (verification),
+        # the bf16 tensor written (reconstruction)
+        e0 = encs[0]
+        print(json.dumps({"mode": "exact", "steps": args.steps, "bytes": {
+            n: {"spec": e0[n].spec_bytes, "verif": e0[n].verif_bytes,
+                "verify_gemm": e0[n].spec_bytes + e0[n].verif_bytes + 5 * 2 * e0[n].cols + 5 * 4 * e0[n].rows,
+                "reconstruct": e0[n].spec_bytes + e0[n].verif_bytes + 2 * e0[n].rows * e0[n].cols}
+            for n in MATS}}))
         return
 
     xs = {n: dev16(synth.activations(1, layer0[n].shape[1], 2, t0=i)) for i, n in enumerate(MATS)}
@@ -578,6 +594,44 @@ def run_extras(args, torch, cass, synth, timer, stream, layers, encs, layer0, en
     torch.cuda.empty_cache()
     log("qwen kv done")
     return out
+
+
+def run_kv_profile(torch, cass, synth, dev16, steps, T=32768):
+    """The KV calls of one Cassandra-1 layer at T tokens, `steps` times each,
+    with their algorithmic bytes per call (what each kernel must read)."""
+    H, Hq, keep, mant, nq = 8, 32, 38, 3, 5
+    Kt = synth.kv_tensor(T + nq + steps, H, 128, 1_000_000 * 4 + 7)
+    Vt = synth.kv_tensor(T + nq + steps, H, 128, 1_000_000 * 4 + 8)
+    cache = cass.KvCache(H, 128, keep, mant, max_tokens=T + nq + steps + 8)
+    cache.append(dev16(Kt[:T]), dev16(Vt[:T]))
+    q1 = dev16(synth.activations(Hq, 128, 4, t0=T))
+    qv = dev16(np.stack([synth.activations(Hq, 128, 5, t0=T + i) for i in range(nq)]))
+    o1 = torch.empty((Hq, 128), dtype=torch.float32, device="cuda")
+    ov = torch.empty((nq, Hq, 128), dtype=torch.float32, device="cuda")
+    ws = torch.empty(cass.cass_kv_attn_ws_bytes(cache.kv, nq, Hq) * 2, dtype=torch.uint8,
+                     device="cuda")
+    torch.cuda.synchronize()
+    st = cache.state.cpu().numpy().view(np.int64)
+    code_bits = [int(st[2 + 2 * s]) for s in range(2 * H)], [int(st[3 + 2 * s]) for s in range(2 * H)]
+    tk = [dev16(Kt[t:t + 1]) for t in range(T, T + steps)]
+    tv = [dev16(Vt[t:t + 1]) for t in range(T, T + steps)]
+    for i in range(steps):  # single-token appends (the one-launch path)
+        cache.append(tk[i], tv[i])
+    for _ in range(steps):
+        cass.cass_kv_draft_attn(cache.kv, q1, 1 / np.sqrt(128), o1, ws)
+    cache.append(dev16(Kt[T + steps:T + steps + nq]), dev16(Vt[T + steps:T + steps + nq]))
+    for _ in range(steps):
+        cass.cass_kv_verify_attn(cache.kv, qv, 1 / np.sqrt(128), ov, ws)
+    torch.cuda.synchronize()
+    tokens = cache.tokens
+    # per K|V stream and token: keep words 16 B, code offset 4 B, fields k(1+m)/8 B; the used
+    # code bits; the verification side adds low mantissas k(7-m)/8 B, pruned bytes D-k, its
+    # offset 4 B and its code bits
+    spec_b = 2 * H * tokens * (16 + 4 + keep * (1 + mant) / 8) + sum(code_bits[0]) / 8
+    verif_b = 2 * H * tokens * (keep * (7 - mant) / 8 + (128 - keep) + 4) + sum(code_bits[1]) / 8
+    return {"tokens": tokens, "steps": steps,
+            "draft_attn_bytes_per_call": round(spec_b),
+            "verify_attn_bytes_per_call": round(spec_b + verif_b)}
 
 
 def append_graph_us(torch, cache, tokK, tokV, n=16, reps=7):
