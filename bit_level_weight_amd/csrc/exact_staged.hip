@@ -14,8 +14,7 @@
 // range of each section -- bitmap, fields, low mantissas, pruned bytes and
 // both code sections -- into LDS by LDS DMA: per section the 16 runs are
 // packed back to back and every instruction moves 64 chunks of 16 bytes, so
-// a stage takes a handful of instructions, all in flight at once, and every
-// stream byte is read from HBM once.
+// a stage takes a handful of instructions, all in flight at once.
 //
 // Decode.  Four lanes serve each row.  The row's kept values of the stage are
 // cut into four equal parts, one per lane, and so are its pruned values, so
@@ -579,9 +578,11 @@ __global__ void __launch_bounds__(64 * kMaxWaves) k_exact_staged(SpecViewC1 sv, 
               int d = dd[0];
 #pragma unroll
               for (int q = 0; q < 15; ++q) d = inc[q] <= c ? dd[q + 1] : d;
+              // (cached, not streaming: a row's run for one block covers part of a
+              // 128-byte line whose rest the next stage reads)
               __builtin_amdgcn_global_load_lds(
                   (const void*)(sec_base[sec] + 16 * (int64_t)(c + d)),
-                  (lds_void*)(smem + off + 16 * base), 16, 0, 2);
+                  (lds_void*)(smem + off + 16 * base), 16, 0, 0);
             }
           }
         }
