@@ -833,7 +833,8 @@ struct AttnArgs {
   float scale;
   int64_t T;          // tokens in the cache
   int nchunks;
-  float* part;        // [H][nchunks][rows][2 + D]
+  float* part;        // chunk numerators [H][nchunks][rows][D]
+  float* ml;          // chunk (row maximum, sum of p) [H][rows][nchunks][2]
   int fcap, ccap;     // draft: shared-memory words per stream for fields and codes
 };
 
@@ -1116,15 +1117,14 @@ __global__ void __launch_bounds__(2 * kChunk) k_kv_attn(KvDev kv, AttnArgs a) {
     }
     __syncthreads();
     if (half == 0) {
-      float* part = a.part + (((int64_t)h * a.nchunks + c) * rows) * (2 + kDim);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         if (r < rows) {
-          float* pr = part + (int64_t)r * (2 + kDim);
-          pr[2 + d] = acc[r] + other[d * 4 + r];
+          a.part[(((int64_t)h * a.nchunks + c) * rows + r) * kDim + d] = acc[r] + other[d * 4 + r];
           if (d == 0) {
-            pr[0] = fmaxf(red[r][0], red[r][1]);
-            pr[1] = lsum[r][0] + lsum[r][1];
+            float* ml = a.ml + (((int64_t)h * rows + r) * a.nchunks + c) * 2;
+            ml[0] = fmaxf(red[r][0], red[r][1]);
+            ml[1] = lsum[r][0] + lsum[r][1];
           }
         }
       }
@@ -1141,7 +1141,6 @@ __global__ void __launch_bounds__(2 * kChunk) k_kv_attn(KvDev kv, AttnArgs a) {
   __syncthreads();
   // o[r][d] = sum_t p[r][t] V[t][d]; thread = (d, half of the rows)
   const int d = tid & (kDim - 1), half = tid >> 7;
-  float* part = a.part + (((int64_t)h * a.nchunks + c) * rows) * (2 + kDim);
   for (int r = half; r < rows; r += 2) {
     float acc = 0.f, l = 0.f;
 #pragma unroll 8
@@ -1150,32 +1149,38 @@ __global__ void __launch_bounds__(2 * kChunk) k_kv_attn(KvDev kv, AttnArgs a) {
       acc = __builtin_fmaf(p, bf16_bits_to_float(vt[t * kVStride + d]), acc);
       l += p;
     }
-    float* pr = part + (int64_t)r * (2 + kDim);
-    pr[2 + d] = acc;
+    a.part[(((int64_t)h * a.nchunks + c) * rows + r) * kDim + d] = acc;
     if (d == 0) {
-      pr[0] = fmaxf(red[r][0], red[r][1]);
-      pr[1] = l;
+      float* ml = a.ml + (((int64_t)h * rows + r) * a.nchunks + c) * 2;
+      ml[0] = fmaxf(red[r][0], red[r][1]);
+      ml[1] = l;
     }
   }
 }
 
-// combine the chunk partials: o = sum_c e^{m_c - M} o_c / sum_c e^{m_c - M} l_c
-constexpr int kMergeParts = 4;  // chunk ranges summed side by side per output
+// combine the chunk partials: o = sum_c e^{m_c - M} o_c / sum_c e^{m_c - M} l_c.
+// A workgroup per (KV head, query row, range of kMergeDims dimensions); every
+// workgroup of a row computes the same weights and denominator.
+constexpr int kMergeDims = 32;                       // dimensions per workgroup
+constexpr int kMergeSplit = kDim / kMergeDims;       // workgroups per (head, row)
+constexpr int kMergeParts = 16;                      // chunk ranges summed side by side
+constexpr int kMergeThreads = kMergeDims * kMergeParts;
 
-__global__ void __launch_bounds__(128 * kMergeParts) k_kv_merge(AttnArgs a, int H, float* out) {
+__global__ void __launch_bounds__(kMergeThreads) k_kv_merge(AttnArgs a, int H, float* out) {
   __shared__ float wgt[kMaxChunksMerge];
-  __shared__ float red[2][8];
-  __shared__ float nums[kMergeParts][kDim];
+  __shared__ float red[2][kMergeThreads / 64];
+  __shared__ float nums[kMergeParts][kMergeDims];
   const int rows = a.nq * a.G;
-  const int hr = blockIdx.x;  // h * rows + r
+  const int hr = blockIdx.x / kMergeSplit, ds = blockIdx.x % kMergeSplit;  // (h * rows + r, dims)
   const int h = hr / rows, r = hr % rows;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, nw = blockDim.x / 64;
-  const float* base = a.part + ((int64_t)h * a.nchunks * rows + r) * (2 + kDim);
-  const int64_t cstride = (int64_t)rows * (2 + kDim);
+  const float* base = a.part + ((int64_t)h * a.nchunks * rows + r) * kDim;  // chunk 0's numerator
+  const int64_t cstride = (int64_t)rows * kDim;
+  const float* ml = a.ml + ((int64_t)h * rows + r) * a.nchunks * 2;       // contiguous per row
   // chunk maxima and their overall maximum (the loads of every chunk in flight at once)
   float M = -INFINITY;
   for (int c = tid; c < a.nchunks; c += blockDim.x) {
-    const float mc = base[c * cstride];
+    const float mc = ml[2 * c];
     wgt[c] = mc;
     M = fmaxf(M, mc);
   }
@@ -1191,7 +1196,7 @@ __global__ void __launch_bounds__(128 * kMergeParts) k_kv_merge(AttnArgs a, int 
     const float mc = wgt[c];
     const float w = mc == -INFINITY ? 0.f : __expf(mc - M);
     wgt[c] = w;
-    den += w * base[c * cstride + 1];
+    den += w * ml[2 * c + 1];
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) den += __shfl_xor(den, o, 64);
@@ -1200,15 +1205,15 @@ __global__ void __launch_bounds__(128 * kMergeParts) k_kv_merge(AttnArgs a, int 
   den = 0.f;
   for (int i = 0; i < nw; ++i) den += red[1][i];
   // numerator: thread (d, part) sums chunks part, part + kMergeParts, ...
-  const int d = tid & (kDim - 1), q = tid >> 7;
+  const int dl = tid & (kMergeDims - 1), q = tid / kMergeDims, d = ds * kMergeDims + dl;
   float num = 0.f;
 #pragma unroll 8
-  for (int c = q; c < a.nchunks; c += kMergeParts) num += wgt[c] * base[c * cstride + 2 + d];
-  nums[q][d] = num;
+  for (int c = q; c < a.nchunks; c += kMergeParts) num += wgt[c] * base[c * cstride + d];
+  nums[q][dl] = num;
   __syncthreads();
   if (q == 0) {
     float tot = 0.f;
-    for (int i = 0; i < kMergeParts; ++i) tot += nums[i][d];
+    for (int i = 0; i < kMergeParts; ++i) tot += nums[i][dl];
     const int qi = r / a.G, g = r % a.G;
     out[((int64_t)qi * a.Hq + h * a.G + g) * kDim + d] = tot / den;
   }
@@ -1567,7 +1572,6 @@ __global__ void __launch_bounds__(kXThreads) k_kv_attn_x1(KvDev kv, AttnArgs a, 
       ahi[ks] = r < rows ? *reinterpret_cast<const xv8s*>(ph + tb) : zero;
       alo[ks] = r < rows ? *reinterpret_cast<const xv8s*>(ph + kXChunk + tb) : zero;
     }
-    float* part = a.part + (((int64_t)h * a.nchunks + c) * rows) * (2 + kDim);
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       const int dcol = (cg + 4 * half) * 16 + i16;
@@ -1586,11 +1590,11 @@ __global__ void __launch_bounds__(kXThreads) k_kv_attn_x1(KvDev kv, AttnArgs a, 
       for (int e = 0; e < 4; ++e) {
         const int rr = rg * 16 + 4 * kq + e;
         if (rr < rows) {
-          float* pr = part + (int64_t)rr * (2 + kDim);
-          pr[2 + dcol] = acc[e];
+          a.part[(((int64_t)h * a.nchunks + c) * rows + rr) * kDim + dcol] = acc[e];
           if (dcol == 0) {
-            pr[0] = rmax[rr];
-            pr[1] = rsum[rr];
+            float* ml = a.ml + (((int64_t)h * rows + rr) * a.nchunks + c) * 2;
+            ml[0] = rmax[rr];
+            ml[1] = rsum[rr];
           }
         }
       }
@@ -1749,6 +1753,7 @@ int run_attention(const cass_kv* kv, const uint16_t* q, int nq, int n_q_heads, f
   if ((kv->tokens + kXChunk - 1) / kXChunk > kMaxChunksMerge)
     return report(CASS_ERR_UNSUPPORTED, "attention over more than 512K tokens");
   a.part = (float*)ws;
+  a.ml = a.part + (int64_t)H * a.nchunks * (nq * G) * kDim;
   {
     // draft staging: every field of the chunk, and codes averaging up to 4
     // bits per kept value (longer runs read their codes from global memory)
@@ -1766,6 +1771,7 @@ int run_attention(const cass_kv* kv, const uint16_t* q, int nq, int n_q_heads, f
     const int64_t kk = kv->p.keep, mm = kv->p.mant_bits;
     AttnArgs ax = a;
     ax.nchunks = (int)((kv->tokens + kXChunk - 1) / kXChunk);
+    ax.ml = ax.part + (int64_t)H * ax.nchunks * (nq * G) * kDim;
     XCaps cp;
     // (regions in whole 16-byte chunks; 8 words beyond what a run may take,
     // which covers a copy that starts up to 3 words early and a chunk's tail)
@@ -1783,7 +1789,7 @@ int run_attention(const cass_kv* kv, const uint16_t* q, int nq, int n_q_heads, f
       e = hipGetLastError();
     }
     if (e != hipSuccess) return report(CASS_ERR_HIP, "attention: %s", hipGetErrorString(e));
-    k_kv_merge<<<H * nq * G, kDim * kMergeParts, 0, stream>>>(ax, H, out);
+    k_kv_merge<<<H * nq * G * kMergeSplit, kMergeThreads, 0, stream>>>(ax, H, out);
     if ((e = hipGetLastError()) != hipSuccess) return report(CASS_ERR_HIP, "merge: %s", hipGetErrorString(e));
     return CASS_OK;
   }
@@ -1804,7 +1810,7 @@ int run_attention(const cass_kv* kv, const uint16_t* q, int nq, int n_q_heads, f
                           : rows <= 20 ? attn_launch<false, 20>(d, a, H, lds, stream)
                                        : attn_launch<false, 32>(d, a, H, lds, stream));
   if (e != hipSuccess) return report(CASS_ERR_HIP, "attention: %s", hipGetErrorString(e));
-  k_kv_merge<<<H * nq * G, kDim * kMergeParts, 0, stream>>>(a, H, out);
+  k_kv_merge<<<H * nq * G * kMergeSplit, kMergeThreads, 0, stream>>>(a, H, out);
   if ((e = hipGetLastError()) != hipSuccess) return report(CASS_ERR_HIP, "merge: %s", hipGetErrorString(e));
   return CASS_OK;
 }
