@@ -12,9 +12,11 @@
 // waves' products in wave order (no atomics: the result is the same on every
 // run).  A stage copies, for every row, the row's
 // range of each section -- bitmap, fields, low mantissas, pruned bytes and
-// both code sections -- into LDS by LDS DMA: per section the 16 runs are
-// packed back to back and every instruction moves 64 chunks of 16 bytes, so
-// a stage takes a handful of instructions, all in flight at once.
+// both code sections -- into LDS by LDS DMA: per section every row gets a slot
+// as long as the longest of the 16 runs (packed back to back instead when the
+// slots do not fit), and every instruction moves 64 chunks of 16 bytes, so a
+// stage takes a handful of instructions, all in flight at once.  The next
+// stage's block words and this stage's X columns load while it decodes.
 //
 // Decode.  Four lanes serve each row.  The row's kept values of the stage are
 // cut into four equal parts, one per lane, and so are its pruned values, so
@@ -53,6 +55,7 @@ constexpr int kRows = 16;   // rows per wave
 constexpr int kMaxWaves = 8;  // waves per workgroup: the same 16 rows, column ranges side by side
 constexpr int kSec = 6;     // bitmap, fields, low mantissas, pruned bytes, spec codes, verif codes
 constexpr int kPU = 6;      // pruned values per group (6 codes nearly always fit 32 bits)
+constexpr int kXPre = 8;    // X column steps of a stage loaded before its decode
 
 struct XGeom {
   int Wb;                    // blocks per stage
@@ -69,6 +72,8 @@ __device__ __forceinline__ void wsync() {
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
+
+__device__ __forceinline__ uint32_t u32(int64_t v) { return (uint32_t)v; }
 
 __device__ __forceinline__ uint32_t lds_addr_of(const uint8_t* p) {
   return (uint32_t)(uintptr_t)(lds_u8c*)p;
@@ -112,6 +117,16 @@ __device__ __forceinline__ int scan16(int v) {
   v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);  // row_shr:2
   v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);  // row_shr:4
   v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);  // row_shr:8
+  return v;
+}
+
+// Maximum over each row of 16 lanes (every row of the wave holds the same 16
+// values here, so this is also the wave's maximum).
+__device__ __forceinline__ int max16(int v) {
+  v = max(v, __shfl_xor(v, 1, 64));
+  v = max(v, __shfl_xor(v, 2, 64));
+  v = max(v, __shfl_xor(v, 4, 64));
+  v = max(v, __shfl_xor(v, 8, 64));
   return v;
 }
 
@@ -380,28 +395,6 @@ __global__ void __launch_bounds__(64 * kMaxWaves) k_exact_staged(SpecViewC1 sv, 
   const uint32_t sb = lds_addr_of(smem);
   const uint32_t* sm32 = reinterpret_cast<const uint32_t*>(smem);
 
-  // rank tables: bytes for the one-value steps, bf16 templates for the groups
-  uint8_t* ps = smem + g.perm_off;
-  uint8_t* pv = ps + 256;
-  uint16_t* klut = reinterpret_cast<uint16_t*>(smem + g.klut_off);
-  uint16_t* plut = reinterpret_cast<uint16_t*>(smem + g.plut_off);
-  // (tables shared by the workgroup's waves)
-  for (int i = threadIdx.x; i < 256; i += blockDim.x) {
-    ps[i] = sv.perm[i];
-    pv[i] = MODE == 2 ? 0 : vv.perm[i];
-  }
-  if (KLUT) {
-    for (int i = threadIdx.x; i < (32 << fw); i += blockDim.x) {
-      const uint32_t f = (uint32_t)i & ((1u << fw) - 1u);
-      klut[i] = (uint16_t)(((f >> m) << 15) | ((uint32_t)sv.perm[i >> fw] << 7) |
-                           ((f & ((1u << m) - 1u)) << lw));
-    }
-  } else if (threadIdx.x < 32) {
-    klut[threadIdx.x] = (uint16_t)((uint32_t)sv.perm[threadIdx.x] << 7);
-  }
-  if (MODE != 2 && threadIdx.x < 64)
-    plut[lane] = (uint16_t)(((uint32_t)(lane & 1) << 15) | ((uint32_t)vv.perm[lane >> 1] << 7));
-  __syncthreads();  // the tables
   // this wave's region: 16 rows of its own
   const int wbase = g.wave_off + wave * g.wave_bytes;
   uint8_t* wsm = smem + wbase;
@@ -410,6 +403,7 @@ __global__ void __launch_bounds__(64 * kMaxWaves) k_exact_staged(SpecViewC1 sv, 
   const uint32_t tileb = sb + wbase + g.tile_off;
 
   const int r = lane & 15, j = lane >> 4;
+  const int xn = lane & 15, xkq = lane >> 4;  // MFMA operand lane: token / row n, k slice
   // the workgroup's waves share its 16 rows; wave w takes the w-th range of
   // stages, and the verification GEMM sums the waves' products in wave order
   const int64_t row0 = (int64_t)blockIdx.x * kRows;
@@ -417,6 +411,7 @@ __global__ void __launch_bounds__(64 * kMaxWaves) k_exact_staged(SpecViewC1 sv, 
   const int64_t row = row0 + r;
   const bool row_ok = row < R;
   const int64_t rowc = row_ok ? row : R - 1;  // clamped for loads
+  const uint32_t rowk = u32(rowc) * u32(k), rowpk = u32(rowc) * u32(C - k);  // mod 2^32
   const int64_t st0 = (int64_t)wave * g.stages_per_split;
   const int64_t st1 = std::min<int64_t>(st0 + g.stages_per_split, g.nstage);
   // format 4 (sv.sb_log >= 0): a row's first code bit is its first superblock's
@@ -444,19 +439,34 @@ __global__ void __launch_bounds__(64 * kMaxWaves) k_exact_staged(SpecViewC1 sv, 
   // loaded one stage ahead as plain words (indices clamped, so the loads are
   // unconditional and nothing waits for them until the next stage)
   struct MetaRaw {
-    uint32_t kb[3], bs[3], bv[3];
+    uint32_t kb[3], bs[3], bv[3], o16[3];  // (format 4: bs the superblock base's low word)
   };
+  // (one branch on the format around all the loads, and no arithmetic on the
+  // loaded words until they are stored: a branch or a use after a load makes
+  // the compiler wait for the loads in flight)
   auto load_meta = [&](int64_t stg) {
     MetaRaw mr;
     const int64_t bf = stg * g.Wb;
+    int64_t bb[3];
 #pragma unroll
-    for (int i = 0; i < 3; ++i) {
-      const int64_t bb = std::min<int64_t>(bf + i, nb - 1);
-      mr.kb[i] = sv.keptb[rowc * nb + bb];
-      mr.bs[i] = sbm ? (uint32_t)(sv.sbbase[rowc * sv.nsb + (bb >> sv.sb_log)] - (uint64_t)rbs) +
-                           sv.blkoff16[rowc * nb + bb]
-                     : sv.blkoff[rowc * nb + bb];
-      mr.bv[i] = MODE == 2 ? 0u : vv.blkoff[rowc * nb + bb];
+    for (int i = 0; i < 3; ++i) bb[i] = rowc * nb + std::min<int64_t>(bf + i, nb - 1);
+    if (sbm) {
+      const uint32_t* sb32 = reinterpret_cast<const uint32_t*>(sv.sbbase);
+#pragma unroll
+      for (int i = 0; i < 3; ++i) {
+        mr.kb[i] = sv.keptb[bb[i]];
+        mr.bs[i] = sb32[2 * (rowc * sv.nsb + ((bb[i] - rowc * nb) >> sv.sb_log))];
+        mr.o16[i] = sv.blkoff16[bb[i]];
+        mr.bv[i] = MODE == 2 ? 0u : vv.blkoff[bb[i]];
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 3; ++i) {
+        mr.kb[i] = sv.keptb[bb[i]];
+        mr.bs[i] = sv.blkoff[bb[i]];
+        mr.o16[i] = 0u;
+        mr.bv[i] = MODE == 2 ? 0u : vv.blkoff[bb[i]];
+      }
     }
     return mr;
   };
@@ -468,12 +478,41 @@ __global__ void __launch_bounds__(64 * kMaxWaves) k_exact_staged(SpecViewC1 sv, 
 #pragma unroll
       for (int i = 0; i < 3; ++i) {
         meta_s[r * 9 + i] = mr.kb[i];
-        meta_s[r * 9 + 3 + i] = mr.bs[i];
+        // format 4: a block's code offset from the row's first code bit is
+        // (superblock base - row base) + its 16-bit offset, taken mod 2^32
+        meta_s[r * 9 + 3 + i] = sbm ? mr.bs[i] - u32(rbs) + mr.o16[i] : mr.bs[i];
         meta_s[r * 9 + 6 + i] = mr.bv[i];
       }
     }
   };
-  if (st0 < st1) put_meta(load_meta(st0));
+  // (the row bases and the first stage's words are loaded before the tables
+  // are built, so the three global round trips overlap)
+  MetaRaw mr0{};
+  if (st0 < st1) mr0 = load_meta(st0);
+
+  // rank tables: bytes for the one-value steps, bf16 templates for the groups
+  uint8_t* ps = smem + g.perm_off;
+  uint8_t* pv = ps + 256;
+  uint16_t* klut = reinterpret_cast<uint16_t*>(smem + g.klut_off);
+  uint16_t* plut = reinterpret_cast<uint16_t*>(smem + g.plut_off);
+  // (tables shared by the workgroup's waves)
+  for (int i = threadIdx.x; i < 256; i += blockDim.x) {
+    ps[i] = sv.perm[i];
+    pv[i] = MODE == 2 ? 0 : vv.perm[i];
+  }
+  if (KLUT) {
+    for (int i = threadIdx.x; i < (32 << fw); i += blockDim.x) {
+      const uint32_t f = (uint32_t)i & ((1u << fw) - 1u);
+      klut[i] = (uint16_t)(((f >> m) << 15) | ((uint32_t)sv.perm[i >> fw] << 7) |
+                           ((f & ((1u << m) - 1u)) << lw));
+    }
+  } else if (threadIdx.x < 32) {
+    klut[threadIdx.x] = (uint16_t)((uint32_t)sv.perm[threadIdx.x] << 7);
+  }
+  if (MODE != 2 && threadIdx.x < 64)
+    plut[lane] = (uint16_t)(((uint32_t)(lane & 1) << 15) | ((uint32_t)vv.perm[lane >> 1] << 7));
+  __syncthreads();  // the tables
+  if (st0 < st1) put_meta(mr0);
   wsync();
 
   for (int64_t st = st0; st < st1; ++st) {
@@ -523,14 +562,17 @@ __global__ void __launch_bounds__(64 * kMaxWaves) k_exact_staged(SpecViewC1 sv, 
     lo[5] = bov[0];
     hi[5] = bove;
 
-    // ---- staging: per section, the 16 row runs packed back to back
+    // ---- staging.  Per section, each row's run of 16-byte chunks.  Usually
+    // every row gets a slot of S chunks, S the longest run of the 16 (row r's
+    // run at slot offset r*S): a DMA lane then finds its row by one division
+    // and takes the row's first chunk and run length from the row's lane.  When
+    // the slots do not fit the region (rows with very different runs), the 16
+    // runs are packed back to back instead, and a lane finds its row through
+    // the runs' prefix sums.
     int64_t bias[kSec];
-    int nsec[kSec];
-    int inc_l[kSec];      // this lane's row: inclusive packed chunk count
-    int d_l[kSec];        // and first source chunk - first packed chunk (sections hold
-                          // fewer than 2^30 chunks, so the difference fits 32 bits)
-    int foff = 0, coff = 0;
-    bool overflow = false;
+    int n_l[kSec];        // this lane's row: run length in chunks
+    int c0_l[kSec];       // and first source chunk (sections hold fewer than 2^30 chunks)
+    int S[kSec];          // longest run of the 16 rows (uniform)
 #pragma unroll
     for (int sec = 0; sec < kSec; ++sec) {
       const int64_t c0 = lo[sec] >> 7;
@@ -538,38 +580,75 @@ __global__ void __launch_bounds__(64 * kMaxWaves) k_exact_staged(SpecViewC1 sv, 
       if (c1 > sec_lim[sec]) c1 = sec_lim[sec];
       // (the draft stages the speculation sections only)
       const bool used = MODE != 2 || sec == 0 || sec == 1 || sec == 4;
-      const int n = (used && row_ok && hi[sec] > lo[sec] && c1 > c0) ? (int)(c1 - c0) : 0;
-      const int incl = scan16(n);
-      const int pre = incl - n;
-      const int N = __builtin_amdgcn_readlane(incl, 15);
-      int off;
-      if (sec < 4) {
-        off = wbase + g.fix_off + foff;
-        foff += 16 * N;
-        CASS_DCHECK(foff <= g.fix_cap, CASS_DBG_STAGE);
-      } else {
-        if (coff + 16 * N > g.cod_cap) overflow = true;
-        off = wbase + g.cod_off + coff;
-        coff += 16 * N;
-      }
-      nsec[sec] = (sec < 4 || !overflow) ? N : 0;
-      bias[sec] = (int64_t)(off + 16 * pre) * 8 - c0 * 128;
-      inc_l[sec] = incl;
-      d_l[sec] = (int)(c0 - pre);
+      n_l[sec] = (used && row_ok && hi[sec] > lo[sec] && c1 > c0) ? (int)(c1 - c0) : 0;
+      c0_l[sec] = (int)c0;
+      S[sec] = __builtin_amdgcn_readfirstlane(max16(n_l[sec]));
     }
+    // (all six sections share the fixed and code regions, which are adjacent)
+    int smax = 0, stot = 0;
+#pragma unroll
+    for (int sec = 0; sec < kSec; ++sec) {
+      smax = max(smax, S[sec]);
+      stot += S[sec];
+    }
+    const int ucap = g.fix_cap + 64 + g.cod_cap;  // (cod_off = fix_off + fix_cap + 64)
+    const bool uni = smax <= 64 && kRows * 16 * stot <= ucap;
+    bool overflow = false;  // codes over the region: read from global memory
     {
-      int off_f = wbase + g.fix_off, off_c = wbase + g.cod_off;
+      int foff = 0, coff = 0, uoff = 0;
 #pragma unroll
       for (int sec = 0; sec < kSec; ++sec) {
-        const int N = nsec[sec];
-        const int off = sec < 4 ? off_f : off_c;
-        if (N > 0) {
+        const bool fixed = sec < 4;
+        if (uni) {
+          const int Ss = S[sec], tot = kRows * Ss;
+          const int off = wbase + g.fix_off + uoff;
+          uoff += 16 * tot;
+          CASS_DCHECK(uoff <= ucap, CASS_DBG_STAGE);
+          bias[sec] = (int64_t)(off + 16 * Ss * r) * 8 - (int64_t)c0_l[sec] * 128;
+          if (Ss > 0) {
+            // row of slot s = floor((s + 1/2) / S), exact in fp32 for s < 1024
+            // and S <= 64 even with a reciprocal one ulp off
+            const float rs = __builtin_amdgcn_rcpf((float)Ss), hs = 0.5f * rs;
+            for (int base = 0; base < tot; base += 64) {
+              const int s = base + lane;
+              const int d = (int)__builtin_fmaf((float)s, rs, hs);
+              const int q = s - d * Ss;
+              // lanes 0..15 hold rows 0..15
+              const int cd = __builtin_amdgcn_ds_bpermute(d << 2, c0_l[sec]);
+              const int nd = __builtin_amdgcn_ds_bpermute(d << 2, n_l[sec]);
+              if (s < tot && q < nd) {
+                CASS_DCHECK(d < kRows, CASS_DBG_STAGE);
+                __builtin_amdgcn_global_load_lds(
+                    (const void*)(sec_base[sec] + 16 * (int64_t)(cd + q)),
+                    (lds_void*)(smem + off + 16 * base), 16, 0, 0);
+              }
+            }
+          }
+          continue;
+        }
+        // packed runs
+        const int off = wbase + (fixed ? g.fix_off + foff : g.cod_off + coff);
+        const int n = n_l[sec];
+        const int incl = scan16(n);
+        const int pre = incl - n;
+        const int N = __builtin_amdgcn_readlane(incl, 15);
+        if (fixed) {
+          foff += 16 * N;
+          CASS_DCHECK(foff <= g.fix_cap, CASS_DBG_STAGE);
+        } else {
+          if (coff + 16 * N > g.cod_cap) overflow = true;
+          coff += 16 * N;
+        }
+        bias[sec] = (int64_t)(off + 16 * pre) * 8 - (int64_t)c0_l[sec] * 128;
+        if (N > 0 && (fixed || !overflow)) {
+          const int dl = c0_l[sec] - pre;  // first source chunk - first packed chunk
+          // the section's row table in scalars (lanes 0..15 hold rows 0..15)
           // the section's row table in scalars (lanes 0..15 hold rows 0..15)
           int inc[16], dd[16];
 #pragma unroll
           for (int q = 0; q < 16; ++q) {
-            inc[q] = __builtin_amdgcn_readlane(inc_l[sec], q);
-            dd[q] = __builtin_amdgcn_readlane(d_l[sec], q);
+            inc[q] = __builtin_amdgcn_readlane(incl, q);
+            dd[q] = __builtin_amdgcn_readlane(dl, q);
           }
           for (int base = 0; base < N; base += 64) {
             const int c = base + lane;
@@ -578,25 +657,39 @@ __global__ void __launch_bounds__(64 * kMaxWaves) k_exact_staged(SpecViewC1 sv, 
               int d = dd[0];
 #pragma unroll
               for (int q = 0; q < 15; ++q) d = inc[q] <= c ? dd[q + 1] : d;
-              // (cached, not streaming: a row's run for one block covers part of a
-              // 128-byte line whose rest the next stage reads)
               __builtin_amdgcn_global_load_lds(
                   (const void*)(sec_base[sec] + 16 * (int64_t)(c + d)),
                   (lds_void*)(smem + off + 16 * base), 16, 0, 0);
             }
           }
         }
-        if (sec < 4) off_f += 16 * N;
-        else off_c += 16 * N;
       }
     }
+    // (both layouts copy with the default, allocating cache policy: a row's
+    // run for one block covers part of a 128-byte line whose rest the next
+    // stage reads)
     wait_all();
     const bool more = st + 1 < st1;
-    MetaRaw mr_next{};
-    if (more) mr_next = load_meta(st + 1);  // lands while this stage decodes
 
+    MetaRaw mr_next{};
+    // X for the stage's first kXPre column steps
+    const int nks = nbs * (int)B / 32;
+    const int64_t xcol0 = bf * B;
+    auto x_frag = [&](int ks) {
+      v8s v = v8s{0, 0, 0, 0, 0, 0, 0, 0};
+      if (xn < ntok && ks < nks) {
+        const uint16_t* xp = X + (int64_t)xn * ldx + xcol0 + ks * 32 + 8 * xkq;
+        v = v8s{(short)xp[0], (short)xp[1], (short)xp[2], (short)xp[3],
+                (short)xp[4], (short)xp[5], (short)xp[6], (short)xp[7]};
+      }
+      return v;
+    };
+    v8s xq[kXPre];
     // ---- decode: kept values, then pruned values, into the tile
-    const uint32_t bm_row = (uint32_t)(bias[0] + (rowc * nb + bf) * B);  // bitmap bit of column 0
+    // (LDS bit positions are taken mod 2^32 in 32-bit arithmetic: a 64-bit
+    // product truncated afterwards leaves a don't-care high half that the
+    // compiler may place in a register with a load still in flight)
+    const uint32_t bm_row = u32(bias[0]) + (u32(rowc) * u32(nb) + u32(bf)) * u32(B);  // bitmap bit of column 0
     const uint32_t torg = tileb + 2u * (uint32_t)(r * g.TS) - 2u * bm_row;
     const uint32_t bm_end = bm_row + (uint32_t)(nbs * B);
     if (MODE == 2) {
@@ -619,15 +712,24 @@ __global__ void __launch_bounds__(64 * kMaxWaves) k_exact_staged(SpecViewC1 sv, 
         const int skip = (int)(kidx - kbv[bi]);
         const uint32_t blk = bm_row + (uint32_t)(bi * B);
         bp = blk + find_in_block<false>(sb + (blk >> 3), nwb, skip);
-        fp = (uint32_t)(bias[1] + (rowc * k + kidx) * fw);
-        lp = (uint32_t)(bias[2] + (rowc * k + kidx) * lw);
+        const uint32_t kabs = rowk + u32(kidx);
+        fp = u32(bias[1]) + kabs * (uint32_t)fw;
+        lp = u32(bias[2]) + kabs * (uint32_t)lw;
         if (!overflow) {
-          cp = skip_codes8(sm32, (uint32_t)(bias[4] + bos[bi]), skip);
+          cp = skip_codes8(sm32, u32(bias[4]) + u32(bos[bi]), skip);
         } else {
           cg = sv.codes + (bos[bi] >> 5);
           cp = skip_codes(cg, (uint32_t)(bos[bi] & 31), skip);
         }
       }
+      // the next stage's words and this stage's X: issued here, after the
+      // part start, so they land while the groups decode (a 32-bit multiply-
+      // add in the part start is selected as a 64-bit one whose don't-care
+      // high half may share a register with a load in flight, which would
+      // make it wait for the load)
+      if (more) mr_next = load_meta(st + 1);
+#pragma unroll
+      for (int q = 0; q < kXPre; ++q) xq[q] = MODE == 0 ? x_frag(q) : v8s{0, 0, 0, 0, 0, 0, 0, 0};
       int nmax = n;
 #pragma unroll
       for (int o = 32; o >= 1; o >>= 1) nmax = max(nmax, __shfl_xor(nmax, o, 64));
@@ -690,9 +792,9 @@ __global__ void __launch_bounds__(64 * kMaxWaves) k_exact_staged(SpecViewC1 sv, 
         const int skip = (int)(pidx - (bi ? pb1 : bf * B - kbv[0]));
         const uint32_t blk = bm_row + (uint32_t)(bi * B);
         bp = blk + find_in_block<true>(sb + (blk >> 3), nwb, skip);
-        yp = (uint32_t)(bias[3] + (rowc * (C - k) + pidx) * 8);
+        yp = u32(bias[3]) + (rowpk + u32(pidx)) * 8u;
         if (!overflow) {
-          cp = skip_codes8(sm32, (uint32_t)(bias[5] + bov[bi]), skip);
+          cp = skip_codes8(sm32, u32(bias[5]) + u32(bov[bi]), skip);
         } else {
           cg = vv.codes + (bov[bi] >> 5);
           cp = skip_codes(cg, (uint32_t)(bov[bi] & 31), skip);
@@ -702,8 +804,9 @@ __global__ void __launch_bounds__(64 * kMaxWaves) k_exact_staged(SpecViewC1 sv, 
 #pragma unroll
       for (int o = 32; o >= 1; o >>= 1) nmax = max(nmax, __shfl_xor(nmax, o, 64));
       if (!overflow) {
+        int done = 0;
         PRaw w = praw(sb, bp, yp, cp);
-        for (int done = 0; done < nmax; done += kPU) {
+        for (; done < nmax; done += kPU) {
           const int t = min(max(n - done, 0), kPU);
           const uint32_t sbit = bp & 31u;
           const int have = __builtin_popcount(~__builtin_amdgcn_alignbit(w.q1, w.q0, sbit)) +
@@ -745,25 +848,21 @@ __global__ void __launch_bounds__(64 * kMaxWaves) k_exact_staged(SpecViewC1 sv, 
     wsync();  // the tile is complete
 
     if (MODE == 0) {
-      const int n = lane & 15, kq = lane >> 4;
-      const int64_t col0 = bf * B;
       // v_mfma_f32_16x16x32_bf16: lane (n, kq) feeds tile row n and token n,
       // columns 8kq..8kq+7 of each 32-column step
-      for (int ks = 0; ks < nbs * (int)B / 32; ++ks) {
-        v8s bop = v8s{0, 0, 0, 0, 0, 0, 0, 0};
-        if (n < ntok) {
-          const uint16_t* xp = X + (int64_t)n * ldx + col0 + ks * 32 + 8 * kq;
-          bop = v8s{(short)xp[0], (short)xp[1], (short)xp[2], (short)xp[3],
-                    (short)xp[4], (short)xp[5], (short)xp[6], (short)xp[7]};
-        }
-        const uint32_t ta = tileb + 2u * (uint32_t)(n * g.TS + ks * 32 + 8 * kq);
+      auto step = [&](int ks, const v8s& bop) {
+        const uint32_t ta = tileb + 2u * (uint32_t)(xn * g.TS + ks * 32 + 8 * xkq);
         const uint32_t a0 = ldw(ta), a1 = ldw(ta + 4), a2 = ldw(ta + 8), a3 = ldw(ta + 12);
         const v8s aop = v8s{(short)(a0 & 0xFFFF), (short)(a0 >> 16), (short)(a1 & 0xFFFF),
                             (short)(a1 >> 16), (short)(a2 & 0xFFFF), (short)(a2 >> 16),
                             (short)(a3 & 0xFFFF), (short)(a3 >> 16)};
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, aop),
                                                       __builtin_bit_cast(v8bf, bop), acc, 0, 0, 0);
-      }
+      };
+#pragma unroll
+      for (int q = 0; q < kXPre; ++q)
+        if (q < nks) step(q, xq[q]);
+      for (int ks = kXPre; ks < nks; ++ks) step(ks, x_frag(ks));
     } else {
       const int cpr = nbs * (int)B / 8;  // 16-byte chunks per tile row
       for (int c = lane; c < kRows * cpr; c += 64) {
