@@ -7,10 +7,10 @@
 // section 3.2 -- a unary exponent code is decoded by counting the zeros up to
 // its one; section 3.3 -- the keep bitmap is de-sparsified.
 //
-// Work split.  A workgroup takes 16 rows; each of its waves walks one range of
-// their columns in stages of Wb blocks, and the verification GEMM adds the
-// waves' products in wave order (no atomics: the result is the same on every
-// run).  A stage copies, for every row, the row's
+// Work split.  A workgroup takes 16 rows; its waves take their columns in
+// stages of Wb blocks, in turn (neighbouring stages run side by side), and the
+// verification GEMM adds the waves' products in wave order (no atomics: the
+// result is the same on every run).  A stage copies, for every row, the row's
 // range of each section -- bitmap, fields, low mantissas, pruned bytes and
 // both code sections -- into LDS by LDS DMA: per section every row gets a slot
 // as long as the longest of the 16 runs (packed back to back instead when the
@@ -60,8 +60,8 @@ constexpr int kXPre = 8;    // X column steps of a stage loaded before its decod
 struct XGeom {
   int Wb;                    // blocks per stage
   int TS;                    // u16 per tile row (Wb*B + 2)
-  int64_t nstage, stages_per_split;
-  int nsplit;                // waves per workgroup, one stage range each
+  int64_t nstage;
+  int nsplit;                // waves per workgroup; wave w takes stages w, w + nsplit, ...
   int perm_off, klut_off, plut_off, wave_off, wave_bytes;  // shared tables, wave regions
   int meta_off, dummy_off, tile_off;                       // inside a wave region
   int fix_off, fix_cap, cod_off, cod_cap, lds_bytes;
@@ -404,16 +404,18 @@ __global__ void __launch_bounds__(64 * kMaxWaves) k_exact_staged(SpecViewC1 sv, 
 
   const int r = lane & 15, j = lane >> 4;
   const int xn = lane & 15, xkq = lane >> 4;  // MFMA operand lane: token / row n, k slice
-  // the workgroup's waves share its 16 rows; wave w takes the w-th range of
-  // stages, and the verification GEMM sums the waves' products in wave order
+  // the workgroup's waves share its 16 rows and take their stages in turn; the
+  // verification GEMM sums the waves' products in wave order
   const int64_t row0 = (int64_t)blockIdx.x * kRows;
   if (row0 >= R) return;
   const int64_t row = row0 + r;
   const bool row_ok = row < R;
   const int64_t rowc = row_ok ? row : R - 1;  // clamped for loads
   const uint32_t rowk = u32(rowc) * u32(k), rowpk = u32(rowc) * u32(C - k);  // mod 2^32
-  const int64_t st0 = (int64_t)wave * g.stages_per_split;
-  const int64_t st1 = std::min<int64_t>(st0 + g.stages_per_split, g.nstage);
+  // stages interleaved over the waves (wave w takes w, w + nsplit, ...), so
+  // neighbouring blocks of a row, which share the 128-byte lines at their
+  // boundary, are read at about the same time and the second read hits in L2
+  const int64_t st0 = wave, sstep = g.nsplit;
   // format 4 (sv.sb_log >= 0): a row's first code bit is its first superblock's
   // base, and a block's code offset from it is (superblock base - that) + the
   // block's 16-bit offset
@@ -488,7 +490,7 @@ __global__ void __launch_bounds__(64 * kMaxWaves) k_exact_staged(SpecViewC1 sv, 
   // (the row bases and the first stage's words are loaded before the tables
   // are built, so the three global round trips overlap)
   MetaRaw mr0{};
-  if (st0 < st1) mr0 = load_meta(st0);
+  if (st0 < g.nstage) mr0 = load_meta(st0);
 
   // rank tables: bytes for the one-value steps, bf16 templates for the groups
   uint8_t* ps = smem + g.perm_off;
@@ -512,10 +514,10 @@ __global__ void __launch_bounds__(64 * kMaxWaves) k_exact_staged(SpecViewC1 sv, 
   if (MODE != 2 && threadIdx.x < 64)
     plut[lane] = (uint16_t)(((uint32_t)(lane & 1) << 15) | ((uint32_t)vv.perm[lane >> 1] << 7));
   __syncthreads();  // the tables
-  if (st0 < st1) put_meta(mr0);
+  if (st0 < g.nstage) put_meta(mr0);
   wsync();
 
-  for (int64_t st = st0; st < st1; ++st) {
+  for (int64_t st = st0; st < g.nstage; st += sstep) {
     const int64_t bf = st * g.Wb;
     const int64_t be = std::min<int64_t>(bf + g.Wb, nb);
     const int nbs = (int)(be - bf);  // 1 or 2
@@ -669,7 +671,7 @@ __global__ void __launch_bounds__(64 * kMaxWaves) k_exact_staged(SpecViewC1 sv, 
     // run for one block covers part of a 128-byte line whose rest the next
     // stage reads)
     wait_all();
-    const bool more = st + 1 < st1;
+    const bool more = st + sstep < g.nstage;
 
     MetaRaw mr_next{};
     // X for the stage's first kXPre column steps
@@ -727,7 +729,7 @@ __global__ void __launch_bounds__(64 * kMaxWaves) k_exact_staged(SpecViewC1 sv, 
       // add in the part start is selected as a 64-bit one whose don't-care
       // high half may share a register with a load in flight, which would
       // make it wait for the load)
-      if (more) mr_next = load_meta(st + 1);
+      if (more) mr_next = load_meta(st + sstep);
 #pragma unroll
       for (int q = 0; q < kXPre; ++q) xq[q] = MODE == 0 ? x_frag(q) : v8s{0, 0, 0, 0, 0, 0, 0, 0};
       int nmax = n;
@@ -948,14 +950,12 @@ XGeom make_xgeom(const Shape& sh, const SpecViewC1& sv, const VerifViewC1& vv) {
   g.cod_cap = (int)std::min<int64_t>(kRows * cod_row, 24 * 1024);
   w += g.cod_cap + 64;
   g.wave_bytes = (int)a16(w);
-  // waves per workgroup: as many stage ranges as shared memory holds, at most
-  // kMaxWaves; each takes an equal share of the row's stages
+  // waves per workgroup: as many as shared memory holds, at most kMaxWaves and
+  // at most one per stage; they take the row's stages in turn
   int64_t W = std::min<int64_t>(kMaxWaves, g.nstage);
   while (W > 1 && o + W * g.wave_bytes > kMaxLds) --W;
   if (W < 1) W = 1;
-  g.stages_per_split = (g.nstage + W - 1) / W;
-  g.nsplit = (int)((g.nstage + g.stages_per_split - 1) / g.stages_per_split);
-  if (g.nsplit < 1) g.nsplit = 1;
+  g.nsplit = (int)W;
   g.lds_bytes = (int)(o + (int64_t)g.nsplit * g.wave_bytes);
   return g;
 }
@@ -971,7 +971,7 @@ hipError_t launch_staged_t(const SpecViewC1& sv, const VerifViewC1& vv, const Sh
                                        hipFuncAttributeMaxDynamicSharedMemorySize, g.lds_bytes);
     if (e != hipSuccess) return e;
   }
-  // one workgroup per 16 rows; its g.nsplit waves take the stage ranges, so
+  // one workgroup per 16 rows; its g.nsplit waves take the stages in turn, so
   // every output element is written once, by one wave
   const int64_t gx = (sh.rows + kRows - 1) / kRows;
   kern<<<dim3((unsigned)gx), 64 * g.nsplit, (size_t)g.lds_bytes, s>>>(sv, vv, sh, g, X, ntok, ldx,
