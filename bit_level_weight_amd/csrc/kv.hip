@@ -901,14 +901,10 @@ __global__ void __launch_bounds__(2 * kChunk) k_kv_attn(KvDev kv, AttnArgs a) {
     __builtin_amdgcn_global_load_lds((const void*)(src + 16 * (l & 15)), (lds_void*)&tabs[0][0], 16, 0,
                                      0);
   }
-  // query rows of this KV head: row r = qi * G + g  (query qi, head h*G + g)
-  for (int idx = tid; idx < MAXR * kDim; idx += 2 * kChunk) {  // rows past `rows` stay zero
-    const int r = idx / kDim, d = idx % kDim;
-    const int qi = r / a.G, g = r % a.G;
-    qf[d * MAXR + r] = r < rows ? bf16_bits_to_float(a.q[((int64_t)qi * a.Hq + h * a.G + g) * kDim + d])
-                                : 0.f;
-  }
-  // draft: stage the chunk's speculation sections of K and V
+  // draft: stage the chunk's speculation sections of K and V.  Order of the
+  // loads: the query, every fixed-width copy, the two code offsets, then the
+  // code copies (which need the offsets); the query is stored last.  The
+  // chain is an offset then its codes, with everything else in flight.
   const int64_t t0 = (int64_t)c * kChunk;
   const int fwid = FMT == CASS_FMT_C1_UNARY ? 1 + kv.m : 2 + kv.m;
   const int sw = staged_words(a.fcap, a.ccap, FMT);
@@ -916,6 +912,22 @@ __global__ void __launch_bounds__(2 * kChunk) k_kv_attn(KvDev kv, AttnArgs a) {
   // (staged runs start at the 16-byte boundary at or before their first word)
   const int64_t fw0 = ((t0 * kv.k * fwid) >> 5) & ~(int64_t)3;  // first staged field word
   int64_t cw0[2] = {0, 0};                                      // first staged code word per stream
+  // (through the scalar cache: the offsets are read-only here, and a scalar
+  // wait does not wait for the vector loads and copies in flight)
+  typedef __attribute__((address_space(4))) const uint32_t const_u32;
+  // query rows of this KV head: row r = qi * G + g  (query qi, head h*G + g);
+  // rows past `rows` stay zero
+  constexpr int kQPer = MAXR * kDim / (2 * kChunk);
+  static_assert(MAXR * kDim % (2 * kChunk) == 0, "query elements split evenly over the threads");
+  uint16_t qv[kQPer];
+#pragma unroll
+  for (int i = 0; i < kQPer; ++i) {
+    const int idx = tid + i * 2 * kChunk;
+    const int r = idx / kDim, d = idx % kDim;
+    const int rc = r < rows ? r : 0;  // (unconditional loads: no branch to wait at)
+    const int qi = rc / a.G, g = rc % a.G;
+    qv[i] = a.q[((int64_t)qi * a.Hq + h * a.G + g) * kDim + d];
+  }
   if (!EXACT) {
     // every copy by LDS DMA, all in flight at once
     for (int j = 0; j < 2; ++j) {
@@ -925,18 +937,33 @@ __global__ void __launch_bounds__(2 * kChunk) k_kv_attn(KvDev kv, AttnArgs a) {
                 kChunk * (kDim / 32), kv.T_max * (kDim / 32), tid, 2 * kChunk);
       dma_words(base + kChunk * (kDim / 32), reinterpret_cast<const uint32_t*>(sr + kv.so[3]), fw0,
                 a.fcap, (kv.T_max * kv.k * fwid + 31) / 32, tid, 2 * kChunk);
-      uint32_t* rest = base + kChunk * (kDim / 32) + a.fcap;
-      if (FMT == CASS_FMT_C1_UNARY) {
-        const uint32_t o0 = reinterpret_cast<const uint32_t*>(sr + kv.so[2])[t0];
-        cw0[j] = o0 == 0xFFFFFFFFu ? 0 : (int64_t)((o0 >> 5) & ~3u);
-        dma_words(rest, reinterpret_cast<const uint32_t*>(sr + kv.so[4]), cw0[j], a.ccap,
-                  (kv.ccap + 31) / 32, tid, 2 * kChunk);
-      } else {
+      if (FMT != CASS_FMT_C1_UNARY) {
         // shared exponents: D/32 = 4 bytes, one word, per token
-        dma_words(rest, reinterpret_cast<const uint32_t*>(sr + kv.so[2]), t0, kChunk, kv.T_max,
-                  tid, 2 * kChunk);
+        dma_words(base + kChunk * (kDim / 32) + a.fcap,
+                  reinterpret_cast<const uint32_t*>(sr + kv.so[2]), t0, kChunk, kv.T_max, tid,
+                  2 * kChunk);
       }
     }
+    if (FMT == CASS_FMT_C1_UNARY) {
+      // (the offsets after the fixed-width copies: a scalar wait covers every
+      // scalar load in flight, kernel arguments included)
+      uint32_t o0[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        o0[j] = ((const_u32*)(kv.spec + (2 * h + j) * kv.sstride + kv.so[2]))[t0];
+      for (int j = 0; j < 2; ++j) {
+        const uint8_t* sr = kv.spec + (2 * h + j) * kv.sstride;
+        uint32_t* rest = stg + j * sw + kChunk * (kDim / 32) + a.fcap;
+        cw0[j] = o0[j] == 0xFFFFFFFFu ? 0 : (int64_t)((o0[j] >> 5) & ~3u);
+        dma_words(rest, reinterpret_cast<const uint32_t*>(sr + kv.so[4]), cw0[j], a.ccap,
+                  (kv.ccap + 31) / 32, tid, 2 * kChunk);
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < kQPer; ++i) {
+    const int idx = tid + i * 2 * kChunk;
+    qf[(idx % kDim) * MAXR + idx / kDim] = idx / kDim < rows ? bf16_bits_to_float(qv[i]) : 0.f;
   }
   if (!EXACT) {
     // the draft value tile starts zero-filled (pruned positions and tokens past
