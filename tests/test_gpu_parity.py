@@ -181,7 +181,28 @@ EXACT_CASES = [
     (33, 2048, 614, 3, 256, "wide"),   # long codes: past the LDS code share
     (19, 1280, 384, 5, 256, "normal"),  # odd block count, mantissa without the value table
     (40, 1024, 307, 1, 64, "normal"),
+    # even rows keep their first positions, odd rows their last: in the first
+    # and last blocks the rows' runs differ so much (full fields and low
+    # mantissas against full pruned bytes) that the staged kernel packs them
+    # back to back instead of giving every row an equal slot
+    (32, 4096, 1229, 3, 256, "split"),
 ]
+
+
+def exact_weights(R, C, kind, seed, keep=0):
+    if kind == "wide":
+        return synth.weight_wide(R, C, seed)
+    w = make_w(R, C, seed)
+    if kind == "split":
+        # magnitudes at least 1 in each row's chosen range, below 1 elsewhere
+        a = synth.f32_from_bf16(w)
+        k = keep
+        big = np.zeros_like(a, dtype=bool)
+        big[0::2, :k] = True
+        big[1::2, C - k:] = True
+        a = np.where(big, np.sign(a) * (1.0 + np.abs(a)), a * np.float32(1e-3)).astype(np.float32)
+        w = synth.bf16_from_f32(a)
+    return w
 
 
 @pytest.mark.parametrize("path", ["default", "blocks1", "blocks2", "direct"])
@@ -200,7 +221,7 @@ def test_exact_paths(gpu, orc, opt, path):
     for case in EXACT_CASES:
         R, C, k, m, B, kind = case
         print("case", path, case, flush=True)
-        w = (synth.weight_wide(R, C, 31 + R) if kind == "wide" else make_w(R, C, 41 + R + C))
+        w = exact_weights(R, C, kind, 31 + R if kind == "wide" else 41 + R + C, keep=k)
         spec_o, verif_o = orc.encode(w, k, m, block=B)
         enc = cass.encode(dev(torch, w), k, m, block=B)
         out = torch.empty((R, C), dtype=torch.int16, device="cuda")
