@@ -677,6 +677,77 @@ struct KvVec {
       }
     }
   }
+  // One group of ng <= 8 values of kept_windows.  FULL: ng is 8, and the
+  // group is straight-line code (a per-value test of u < ng, though uniform,
+  // becomes a branch per value and splits the group into small blocks).
+  template <bool FULL, typename F>
+  __device__ __forceinline__ void windows_group(int ng, uint32_t& w0, uint32_t& w1, uint32_t& w2,
+                                                uint32_t& w3, uint32_t& base, F&& use) {
+    const uint32_t fw = 1u + (uint32_t)m, fmask = (1u << fw) - 1u;
+    const uint32_t wf = window32(fw_l, fpos);
+    const uint32_t wc0 = window32(cw_l, cpos);
+    uint32_t dd[8], ff[8], rr[8], ee[8];
+    if (__all(__builtin_popcount(wc0) >= (FULL ? 8 : ng))) {
+      uint32_t wc = wc0;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (FULL || u < ng) {
+          const bool adv = w0 == 0u;
+          w0 = adv ? w1 : w0;
+          w1 = adv ? w2 : w1;
+          w2 = adv ? w3 : w2;
+          w3 = adv ? 0u : w3;
+          base += adv ? 32u : 0u;
+          dd[u] = (base + (uint32_t)__builtin_ctz(w0)) & 127u;
+          w0 &= w0 - 1u;
+          ff[u] = __builtin_amdgcn_ubfe(wf, (uint32_t)u * fw, fw);
+          const uint32_t r = (uint32_t)__builtin_ctz(wc);
+          rr[u] = r;
+          wc = (wc >> r) >> 1;
+        }
+      }
+      // bits the codes took: the window was shifted right by that many
+      cpos += (wc ? (uint32_t)__builtin_clz(wc) : 32u) - (uint32_t)__builtin_clz(wc0);
+    } else {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (FULL || u < ng) {
+          const bool adv = w0 == 0u;
+          w0 = adv ? w1 : w0;
+          w1 = adv ? w2 : w1;
+          w2 = adv ? w3 : w2;
+          w3 = adv ? 0u : w3;
+          base += adv ? 32u : 0u;
+          dd[u] = (base + (uint32_t)__builtin_ctz(w0)) & 127u;
+          w0 &= w0 - 1u;
+          ff[u] = window32(fw_l, fpos + (uint32_t)u * fw) & fmask;
+          // a code of any length (at most 256 bits; the bound keeps a
+          // corrupt stream from running on)
+          uint32_t r = 0, wv = window32(cw_l, cpos);
+          for (int it = 0; it < 8 && wv == 0u; ++it) {
+            r += 32u;
+            cpos += 32u;
+            wv = window32(cw_l, cpos);
+          }
+          const uint32_t t = (uint32_t)__builtin_ctz(wv | (wv ? 0u : 0x80000000u));
+          r += t;
+          cpos += t + 1u;
+          rr[u] = r < 256u ? r : 255u;
+        }
+      }
+    }
+    fpos += (uint32_t)(FULL ? 8 : ng) * fw;
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (FULL || u < ng) ee[u] = perm_s[rr[u]];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (FULL || u < ng) {
+        const uint32_t f = ff[u];
+        use(dd[u], ((f >> m) << 15) | (ee[u] << 7) | ((f & ((1u << m) - 1u)) << (7 - m)));
+      }
+    }
+  }
   // The same, Cassandra-1 with the token's fields and codes staged (fw_l,
   // cw_l): 32-bit field and code windows read from shared memory (two words
   // and a funnel shift each), a rank as the zeros before the window's next
@@ -687,105 +758,47 @@ struct KvVec {
   __device__ __forceinline__ void kept_windows(int k, F&& use) {
     uint32_t w0 = bm[0], w1 = bm[1], w2 = bm[2], w3 = bm[3];
     uint32_t base = 0;
-    const uint32_t fw = 1u + (uint32_t)m, fmask = (1u << fw) - 1u;
-    for (int i0 = 0; i0 < k; i0 += 8) {
-      const int ng = k - i0 < 8 ? k - i0 : 8;  // values in this group (the same for every lane)
-      const uint32_t wf = window32(fw_l, fpos);
-      const uint32_t wc0 = window32(cw_l, cpos);
-      uint32_t dd[8], ff[8], rr[8], ee[8];
-      if (__all(__builtin_popcount(wc0) >= ng)) {
-        uint32_t wc = wc0;
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          if (u < ng) {
-            const bool adv = w0 == 0u;
-            w0 = adv ? w1 : w0;
-            w1 = adv ? w2 : w1;
-            w2 = adv ? w3 : w2;
-            w3 = adv ? 0u : w3;
-            base += adv ? 32u : 0u;
-            dd[u] = (base + (uint32_t)__builtin_ctz(w0)) & 127u;
-            w0 &= w0 - 1u;
-            ff[u] = __builtin_amdgcn_ubfe(wf, (uint32_t)u * fw, fw);
-            const uint32_t r = (uint32_t)__builtin_ctz(wc);
-            rr[u] = r;
-            wc = (wc >> r) >> 1;
-          }
-        }
-        // bits the codes took: the window was shifted right by that many
-        cpos += (wc ? (uint32_t)__builtin_clz(wc) : 32u) - (uint32_t)__builtin_clz(wc0);
-      } else {
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          if (u < ng) {
-            const bool adv = w0 == 0u;
-            w0 = adv ? w1 : w0;
-            w1 = adv ? w2 : w1;
-            w2 = adv ? w3 : w2;
-            w3 = adv ? 0u : w3;
-            base += adv ? 32u : 0u;
-            dd[u] = (base + (uint32_t)__builtin_ctz(w0)) & 127u;
-            w0 &= w0 - 1u;
-            ff[u] = window32(fw_l, fpos + (uint32_t)u * fw) & fmask;
-            // a code of any length (at most 256 bits; the bound keeps a
-            // corrupt stream from running on)
-            uint32_t r = 0, wv = window32(cw_l, cpos);
-            for (int it = 0; it < 8 && wv == 0u; ++it) {
-              r += 32u;
-              cpos += 32u;
-              wv = window32(cw_l, cpos);
-            }
-            const uint32_t t = (uint32_t)__builtin_ctz(wv | (wv ? 0u : 0x80000000u));
-            r += t;
-            cpos += t + 1u;
-            rr[u] = r < 256u ? r : 255u;
-          }
-        }
-      }
-      fpos += (uint32_t)ng * fw;
-#pragma unroll
-      for (int u = 0; u < 8; ++u)
-        if (u < ng) ee[u] = perm_s[rr[u]];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        if (u < ng) {
-          const uint32_t f = ff[u];
-          use(dd[u], ((f >> m) << 15) | (ee[u] << 7) | ((f & ((1u << m) - 1u)) << (7 - m)));
-        }
-      }
-    }
+    int i0 = 0;
+    for (; i0 + 8 <= k; i0 += 8) windows_group<true>(8, w0, w1, w2, w3, base, use);
+    if (i0 < k) windows_group<false>(k - i0, w0, w1, w2, w3, base, use);
   }
   // Cassandra-2 draft decode of the k kept values from the staged fields: four
   // (sign, significand) fields per 32-bit window (fields of up to 8 bits), the
   // shared exponent of a value's 32-position group from the token's four
   // exponent bytes (one word).  Needs every keep word non-empty.
+  template <bool FULL, typename F>
+  __device__ __forceinline__ void windows_group_c2(int ng, uint32_t& w0, uint32_t& w1,
+                                                   uint32_t& w2, uint32_t& w3, uint32_t& base,
+                                                   uint32_t e4, F&& use) {
+    const uint32_t fw = 2u + (uint32_t)m;
+    const uint32_t wf = window32(fw_l, fpos);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (FULL || u < ng) {
+        const bool adv = w0 == 0u;
+        w0 = adv ? w1 : w0;
+        w1 = adv ? w2 : w1;
+        w2 = adv ? w3 : w2;
+        w3 = adv ? 0u : w3;
+        base += adv ? 32u : 0u;
+        const uint32_t d = (base + (uint32_t)__builtin_ctz(w0)) & 127u;
+        w0 &= w0 - 1u;
+        const uint32_t f = __builtin_amdgcn_ubfe(wf, (uint32_t)u * fw, fw);
+        const int E = (int)((e4 >> (8u * ((base >> 5) & 3u))) & 0xFFu);
+        use(d, mx_value_bits(f >> (m + 1), f & ((2u << m) - 1u), E, m));
+      }
+    }
+    fpos += (uint32_t)(FULL ? 4 : ng) * fw;
+  }
   template <typename F>
   __device__ __forceinline__ void kept_windows_c2(int k, F&& use) {
     uint32_t w0 = bm[0], w1 = bm[1], w2 = bm[2], w3 = bm[3];
     const uint32_t e4 = *reinterpret_cast<const uint32_t*>(shexp);
     uint32_t base = 0;
-    const uint32_t fw = 2u + (uint32_t)m;
-    for (int i0 = 0; i0 < k; i0 += 4) {
-      const int ng = k - i0 < 4 ? k - i0 : 4;  // values in this group (the same for every lane)
-      const uint32_t wf = window32(fw_l, fpos);
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        if (u < ng) {
-          const bool adv = w0 == 0u;
-          w0 = adv ? w1 : w0;
-          w1 = adv ? w2 : w1;
-          w2 = adv ? w3 : w2;
-          w3 = adv ? 0u : w3;
-          base += adv ? 32u : 0u;
-          const uint32_t d = (base + (uint32_t)__builtin_ctz(w0)) & 127u;
-          w0 &= w0 - 1u;
-          const uint32_t f = __builtin_amdgcn_ubfe(wf, (uint32_t)u * fw, fw);
-          const int E = (int)((e4 >> (8u * ((base >> 5) & 3u))) & 0xFFu);
-          use(d, mx_value_bits(f >> (m + 1), f & ((2u << m) - 1u), E, m));
-        }
-      }
-      fpos += (uint32_t)ng * fw;
-    }
+    int i0 = 0;
+    // (full groups as straight-line code, the last partial group by value)
+    for (; i0 + 4 <= k; i0 += 4) windows_group_c2<true>(4, w0, w1, w2, w3, base, e4, use);
+    if (i0 < k) windows_group_c2<false>(k - i0, w0, w1, w2, w3, base, e4, use);
   }
   // the kept values into their positions of o[0..D) (the rest left as they are)
   __device__ __forceinline__ void kept_into(int D, uint16_t* o) {
