@@ -801,9 +801,10 @@ struct KvVec {
     if (i0 < k) windows_group_c2<false>(k - i0, w0, w1, w2, w3, base, e4, use);
   }
   // the kept values into their positions of o[0..D) (the rest left as they are)
-  __device__ __forceinline__ void kept_into(int D, uint16_t* o) {
+  __device__ __forceinline__ void kept_into(int D, uint16_t* o, int stride = 1) {
     for (int w = 0; w < D / 32; ++w)
-      for (uint32_t km = bm[w]; km; km &= km - 1u) o[w * 32 + __builtin_ctz(km)] = (uint16_t)kept(w);
+      for (uint32_t km = bm[w]; km; km &= km - 1u)
+        o[(w * 32 + __builtin_ctz(km)) * stride] = (uint16_t)kept(w);
   }
   // all D positions into o[0..D)
   __device__ __forceinline__ void all(int D, uint16_t* o) {
@@ -837,6 +838,24 @@ __global__ void __launch_bounds__(256) k_kv_decode(KvDev kv, int64_t T, uint16_t
 constexpr int kChunk = 128;  // tokens per workgroup, one per thread
 constexpr int kDim = 128;
 constexpr int kVStride = kDim + 2;  // bf16 per LDS row of the value tile (bank spread)
+// draft attention with at most 4 query rows: the value tile transposed,
+// [dim][token] with 16-byte rows (P·V on the matrix cores reads 8 tokens of a
+// dimension at once; rows 68 words apart spread a 16-lane read over the banks)
+constexpr int kVTStride = kChunk + 8;
+__host__ __device__ constexpr int vt_elems(bool transposed) {
+  return transposed ? kDim * kVTStride : kChunk * kVStride;
+}
+
+typedef short xv4s __attribute__((ext_vector_type(4)));
+typedef short xv8s __attribute__((ext_vector_type(8)));
+typedef __bf16 xv8bf __attribute__((ext_vector_type(8)));
+typedef float xv4f __attribute__((ext_vector_type(4)));
+
+// bf16 bits of x rounded to nearest even (x finite).
+__device__ __forceinline__ uint32_t x1_bf16_rne(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
 constexpr int kMaxRows = 32;
 constexpr int kMaxChunksMerge = 8192;  // chunk partials one merge takes (512K tokens in 64-token chunks)
 
@@ -921,7 +940,8 @@ __global__ void __launch_bounds__(2 * kChunk) k_kv_attn(KvDev kv, AttnArgs a) {
   const int64_t t0 = (int64_t)c * kChunk;
   const int fwid = FMT == CASS_FMT_C1_UNARY ? 1 + kv.m : 2 + kv.m;
   const int sw = staged_words(a.fcap, a.ccap, FMT);
-  uint32_t* stg = reinterpret_cast<uint32_t*>(vt + kChunk * kVStride);
+  constexpr bool VTR = !EXACT && MAXR == 4;  // transposed value tile, P·V on the matrix cores
+  uint32_t* stg = reinterpret_cast<uint32_t*>(vt + vt_elems(VTR));
   // (staged runs start at the 16-byte boundary at or before their first word)
   const int64_t fw0 = ((t0 * kv.k * fwid) >> 5) & ~(int64_t)3;  // first staged field word
   int64_t cw0[2] = {0, 0};                                      // first staged code word per stream
@@ -983,7 +1003,7 @@ __global__ void __launch_bounds__(2 * kChunk) k_kv_attn(KvDev kv, AttnArgs a) {
     // the end); the decoders write the kept values only
     typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
     u32x4v* vt4 = reinterpret_cast<u32x4v*>(vt);
-    for (int i = tid; i < kChunk * kVStride * 2 / 16; i += 2 * kChunk) vt4[i] = u32x4v{0, 0, 0, 0};
+    for (int i = tid; i < vt_elems(VTR) * 2 / 16; i += 2 * kChunk) vt4[i] = u32x4v{0, 0, 0, 0};
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies
   }
   __syncthreads();
@@ -1078,8 +1098,10 @@ __global__ void __launch_bounds__(2 * kChunk) k_kv_attn(KvDev kv, AttnArgs a) {
       }
     }
   } else {
-    // value tile (zero for tokens past the end)
-    uint16_t* row = vt + ti * kVStride;
+    // value tile (zero for tokens past the end): value d of the token at
+    // row[d * vs] (a column of the transposed tile, or a row of the other)
+    uint16_t* row = VTR ? vt + ti : vt + ti * kVStride;
+    const int vs = VTR ? kVTStride : 1;
     if (live) {
       KvVec<EXACT, FMT> dec;
       if (EXACT) {
@@ -1091,16 +1113,16 @@ __global__ void __launch_bounds__(2 * kChunk) k_kv_attn(KvDev kv, AttnArgs a) {
         dec.use_tables(tabs[2], tabs[3]);
         if (FMT == CASS_FMT_C2_MX32 && kv.m <= 6 &&
             __all(dec.bm[0] != 0u && dec.bm[1] != 0u && dec.bm[2] != 0u && dec.bm[3] != 0u))
-          dec.kept_windows_c2(kv.k, [&](uint32_t d, uint32_t bits) { row[d] = (uint16_t)bits; });
+          dec.kept_windows_c2(kv.k, [&](uint32_t d, uint32_t bits) { row[d * vs] = (uint16_t)bits; });
         else if (FMT == CASS_FMT_C1_UNARY && kv.m <= 3 &&
             __all(dec.bm[0] != 0u && dec.bm[1] != 0u && dec.bm[2] != 0u && dec.bm[3] != 0u &&
                   dec.cw_l != nullptr))
-          dec.kept_windows(kv.k, [&](uint32_t d, uint32_t bits) { row[d] = (uint16_t)bits; });
+          dec.kept_windows(kv.k, [&](uint32_t d, uint32_t bits) { row[d * vs] = (uint16_t)bits; });
         else if (FMT == CASS_FMT_C1_UNARY &&
             __all(dec.bm[0] != 0u && dec.bm[1] != 0u && dec.bm[2] != 0u && dec.bm[3] != 0u))
-          dec.kept_grouped(kv.k, [&](uint32_t d, uint32_t bits) { row[d] = (uint16_t)bits; });
+          dec.kept_grouped(kv.k, [&](uint32_t d, uint32_t bits) { row[d * vs] = (uint16_t)bits; });
         else
-          dec.kept_into(kDim, row);
+          dec.kept_into(kDim, row, vs);
       }
     } else if (EXACT) {
       for (int d = 0; d < kDim; ++d) row[d] = 0;
@@ -1118,6 +1140,69 @@ __global__ void __launch_bounds__(2 * kChunk) k_kv_attn(KvDev kv, AttnArgs a) {
     }
   }
   __syncthreads();
+  if constexpr (VTR) {
+    // p as two bf16 terms (hi, then lo = p - hi: about 2^-17 relative), rows
+    // [4][kChunk] each, over the query region (no longer read); the row sums
+    // by wave reductions; then o = p V on the matrix cores
+    uint16_t* ph = reinterpret_cast<uint16_t*>(qf);
+    if (tid < kChunk) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float p = 0.f;
+        if (r < rows) {
+          const float mx = fmaxf(red[r][0], red[r][1]);
+          const float sv = sc[r * kChunk + ti];
+          p = (mx == -INFINITY || sv == -INFINITY) ? 0.f : __expf(sv - mx);
+        }
+        const uint32_t hb = x1_bf16_rne(p);
+        ph[r * kChunk + ti] = (uint16_t)hb;
+        ph[4 * kChunk + r * kChunk + ti] = (uint16_t)x1_bf16_rne(p - __uint_as_float(hb << 16));
+        float l = p;
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) l += __shfl_xor(l, o, 64);
+        if (lane == 0) lsum[r][wv] = l;
+      }
+    }
+    __syncthreads();
+    // v_mfma_f32_16x16x32_bf16: lane (i16, kq) feeds row i16 of p (rows 4..15
+    // zero) and dimension i16 of its group, tokens 8kq..8kq+7 of each 32-token
+    // step; a wave takes dimension groups wv and wv + 4
+    const int i16 = lane & 15, kq = lane >> 4;
+    const xv8s zero = xv8s{0, 0, 0, 0, 0, 0, 0, 0};
+    xv8s ahi[kChunk / 32], alo[kChunk / 32];
+#pragma unroll
+    for (int ks = 0; ks < kChunk / 32; ++ks) {
+      const int tb = ks * 32 + 8 * kq;
+      ahi[ks] = i16 < 4 ? *reinterpret_cast<const xv8s*>(ph + i16 * kChunk + tb) : zero;
+      alo[ks] = i16 < 4 ? *reinterpret_cast<const xv8s*>(ph + 4 * kChunk + i16 * kChunk + tb) : zero;
+    }
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int dcol = (wv + 4 * half) * 16 + i16;
+      const uint16_t* vcol = vt + dcol * kVTStride;
+      xv4f acc = xv4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < kChunk / 32; ++ks) {
+        const xv8s bop = *reinterpret_cast<const xv8s*>(vcol + ks * 32 + 8 * kq);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(xv8bf, ahi[ks]),
+                                                      __builtin_bit_cast(xv8bf, bop), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(xv8bf, alo[ks]),
+                                                      __builtin_bit_cast(xv8bf, bop), acc, 0, 0, 0);
+      }
+      // D: lanes kq = 0 hold rows 0..3 of dimension dcol
+      if (kq == 0) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (e < rows) a.part[(((int64_t)h * a.nchunks + c) * rows + e) * kDim + dcol] = acc[e];
+      }
+    }
+    if (tid < rows) {
+      float* ml = a.ml + (((int64_t)h * rows + tid) * a.nchunks + c) * 2;
+      ml[0] = fmaxf(red[tid][0], red[tid][1]);
+      ml[1] = lsum[tid][0] + lsum[tid][1];
+    }
+    return;
+  }
   if (MAXR == 4) {
     // up to 4 rows: p also as [token][4] over the queries (no longer read), the
     // row sums by wave reductions; then o[r][d] = sum_t p[r][t] V[t][d] with
@@ -1285,11 +1370,6 @@ constexpr int kXRows = 32;
 constexpr int kXStride = 132;  // bf16 per key tile row (8-byte aligned rows, banks shifted by 2 words)
 constexpr int kXVStride = kXChunk + 8;  // bf16 per row of the transposed value tile (16-byte rows)
 
-typedef short xv4s __attribute__((ext_vector_type(4)));
-typedef short xv8s __attribute__((ext_vector_type(8)));
-typedef __bf16 xv8bf __attribute__((ext_vector_type(8)));
-typedef float xv4f __attribute__((ext_vector_type(4)));
-
 // Staged words per stream of the split-decode attention.
 struct XCaps {
   int scode, pcode;     // speculation / pruned-exponent code runs
@@ -1300,12 +1380,6 @@ struct XCaps {
 __host__ __device__ __forceinline__ int64_t x1_lds_bytes(const XCaps& cp) {
   return (int64_t)kXChunk * kXStride * 2 + (int64_t)kDim * kXVStride * 2 +
          (int64_t)kXRows * kXChunk * 4 + (int64_t)2 * cp.per_stream() * 4;
-}
-
-// bf16 bits of x rounded to nearest even (x finite).
-__device__ __forceinline__ uint32_t x1_bf16_rne(float x) {
-  const uint32_t u = __float_as_uint(x);
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
 __global__ void __launch_bounds__(kXThreads) k_kv_attn_x1(KvDev kv, AttnArgs a, XCaps cp) {
@@ -1753,7 +1827,7 @@ unsigned grid_of(int64_t n, int per) {
 template <bool EXACT, int MAXR, int FMT>
 hipError_t attn_launch_f(const KvDev& d, const AttnArgs& a, int H, size_t, hipStream_t stream) {
   const size_t lds = (size_t)MAXR * kDim * 4 + (size_t)MAXR * kChunk * 4 +
-                     (size_t)kChunk * kVStride * 2 +
+                     (size_t)vt_elems(!EXACT && MAXR == 4) * 2 +
                      (EXACT ? 0 : (size_t)2 * staged_words(a.fcap, a.ccap, FMT) * 4);
   hipError_t e = hipFuncSetAttribute((const void*)&k_kv_attn<EXACT, MAXR, FMT>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -1800,7 +1874,9 @@ int run_attention(const cass_kv* kv, const uint16_t* q, int nq, int n_q_heads, f
     const int fwid = fmt_of(&kv->p) == CASS_FMT_C1_UNARY ? 1 + kv->p.mant_bits : 2 + kv->p.mant_bits;
     // (multiples of 4 words: the staged regions stay 16-byte aligned)
     a.fcap = (int)(((int64_t)kChunk * kv->p.keep * fwid + 31) / 32 + 8 + 3) / 4 * 4;
-    a.ccap = (int)(((int64_t)kChunk * kv->p.keep * 4 / 32 + 64 + 3) / 4 * 4);
+    // (3 bits per kept value: the staged code run; a token whose codes run
+    // past it reads them in place)
+    a.ccap = (int)(((int64_t)kChunk * kv->p.keep * 3 / 32 + 64 + 3) / 4 * 4);
   }
   const KvDev d = dev_of(kv);
   const size_t lds = 0;  // per launch, from the row bound (attn_launch_f)
