@@ -24,11 +24,12 @@
 // (two LDS words and a funnel shift each): 64 keep bits, 32 code bits and 32
 // field bits.  Per value: position = find-first-set of the keep window, rank
 // = count-trailing-zeros of the code window, field = bit-field extract, weight
-// = one LDS table entry indexed by (rank, field).  A group whose windows do
-// not hold U values for every lane of the wave runs as two half groups; only a
-// half that still falls short (codes of 32 bits or more, long runs of pruned
-// positions) is decoded one value at a time by the general step.  The part's
-// last group is masked.
+// = one LDS table entry indexed by (rank, field), a bf16 pattern (exact for
+// m <= 7) multiplied with x's bf16 by one dot-product instruction.  A group
+// whose windows do not hold U values for every lane of the wave runs as two
+// half groups; only a half that still falls short (codes of 32 bits or more,
+// long runs of pruned positions) is decoded one value at a time by the
+// general step.  The part's last group is masked.
 #include <stdlib.h>
 #include <string.h>
 
@@ -43,7 +44,7 @@ namespace {
 
 constexpr int kBalThreads = 256;
 constexpr int kBalWaves = kBalThreads / 64;
-constexpr int kRanks = 32;     // ranks of the (rank, field) -> fp32 table
+constexpr int kRanks = 32;     // ranks of the (rank, field) -> weight table
 constexpr int kSlack = 8;      // LDS words after each staged section (window look-ahead)
 constexpr int kMaxFw = 6;      // field widths the table path serves (table <= 8 KB)
 constexpr int64_t kBalMaxLds = 150 * 1024;
@@ -136,7 +137,7 @@ __device__ __forceinline__ float x_at_addr(uint32_t a) {
 template <int BATCH>
 __device__ __forceinline__ void c1_step(const uint32_t* bm_l, uint32_t& bp, const uint32_t* f_l,
                                         uint32_t& fp, const uint32_t* cw, uint32_t& cp,
-                                        uint32_t rowbit, int64_t row_len, const float* lut,
+                                        uint32_t rowbit, int64_t row_len, const uint32_t* lut,
                                         const uint8_t* perm, int m, const uint8_t* xs,
                                         uint32_t xstride, float* acc) {
   const int fw = 1 + m;
@@ -154,7 +155,7 @@ __device__ __forceinline__ void c1_step(const uint32_t* bm_l, uint32_t& bp, cons
   const int r = unary_at(cw, cp);
   uint32_t bits;
   if (r < kRanks)
-    bits = __float_as_uint(lut[((uint32_t)r << fw) | f]);
+    bits = lut[((uint32_t)r << fw) | f] << 16;
   else
     bits = ((f >> m) << 31) | ((uint32_t)perm[r] << 23) | ((f & ((1u << m) - 1u)) << (23 - m));
   const float wv = __uint_as_float(bits);
@@ -191,6 +192,16 @@ __device__ __forceinline__ Raw load_raw(uint32_t bm_b, uint32_t f_b, uint32_t c_
 }
 
 typedef __attribute__((address_space(3))) const float lds_f32;
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// acc + w * x for a bf16 weight and a bf16 x, each zero-extended to 32 bits
+// (the high halves multiply to zero): one dot-product instruction in place of
+// a conversion and a fused multiply-add.  A product of two bf16 values is
+// exact in fp32.
+__device__ __forceinline__ float fma_bf16(uint32_t w, uint32_t x, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w),
+                                         __builtin_bit_cast(bf16x2_t, x), acc, false);
+}
 
 // U values from the windows in `w` (read at bp, fp, cp), each window holding
 // at least U values: 64 keep bits, 32 field bits, 32 code bits.  Three phases:
@@ -200,7 +211,7 @@ typedef __attribute__((address_space(3))) const float lds_f32;
 // With ADVANCE (the default when not MASKED) the positions advance past the U
 // slots and `w` receives the next group's words; a masked group advances
 // correctly only for lanes whose t is U (the others have no values left).
-//   lutb  LDS byte address of the (rank, field) -> fp32 table
+//   lutb  LDS byte address of the (rank, field) -> bf16 table (u32 entries)
 //   xorg  LDS byte address of x for staged bitmap bit 0
 template <int BATCH, int U, bool MASKED, bool ADVANCE = !MASKED>
 __device__ __forceinline__ void c1_group(Raw& w, uint32_t& bp, uint32_t& fp, uint32_t& cp,
@@ -244,12 +255,12 @@ __device__ __forceinline__ void c1_group(Raw& w, uint32_t& bp, uint32_t& fp, uin
   }
   __builtin_amdgcn_sched_barrier(0);
   // phase 2: every LDS read of the group
-  float wv[U], xv[BATCH][U];
+  uint32_t wv[U], xv[BATCH][U];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    wv[u] = *(lds_f32*)(uintptr_t)la[u];
+    wv[u] = *(lds_u32*)(uintptr_t)la[u];
 #pragma unroll
-    for (int bb = 0; bb < BATCH; ++bb) xv[bb][u] = x_at_addr(xa[u] + bb * xstride);
+    for (int bb = 0; bb < BATCH; ++bb) xv[bb][u] = *(lds_u16*)(uintptr_t)(xa[u] + bb * xstride);
   }
   if (ADVANCE) w = load_raw(bm_b, f_b, c_b, bp, fp, cp, wb);
   __builtin_amdgcn_sched_barrier(0);
@@ -258,7 +269,7 @@ __device__ __forceinline__ void c1_group(Raw& w, uint32_t& bp, uint32_t& fp, uin
   for (int u = 0; u < U; ++u) {
 #pragma unroll
     for (int bb = 0; bb < BATCH; ++bb) {
-      const float a = __builtin_fmaf(wv[u], xv[bb][u], acc[bb]);
+      const float a = fma_bf16(wv[u], xv[bb][u], acc[bb]);
       acc[bb] = (MASKED && u >= t) ? acc[bb] : a;
     }
   }
@@ -286,7 +297,7 @@ __global__ void __launch_bounds__(kBalThreads) k_gemv_c1_bal(SpecViewC1 v, Shape
   // (wave index made visibly uniform so that per-round values and the row
   // bases of the first round come through scalar registers and loads)
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  float* lut = reinterpret_cast<float*>(smem + g.lut_off);
+  uint32_t* lut = reinterpret_cast<uint32_t*>(smem + g.lut_off);  // bf16 patterns
   uint8_t* reg = smem + g.wave_off + wave * g.wave_bytes;
   uint16_t* kb_l = reinterpret_cast<uint16_t*>(reg + g.kb_off);
   uint32_t* bo_l = reinterpret_cast<uint32_t*>(reg + g.bo_off);
@@ -474,7 +485,7 @@ __global__ void __launch_bounds__(kBalThreads) k_gemv_c1_bal(SpecViewC1 v, Shape
     return pt;
   };
 
-  // ---- first round, x and the (rank, field) -> fp32 table.  Every copy of
+  // ---- first round, x and the (rank, field) -> bf16 table.  Every copy of
   // the first round is in flight at once: the rank table, the sections, the
   // codes (whose range needs only the two row bases, scalar loads) and x.
   int64_t round = (int64_t)blockIdx.x * kBalWaves + wave;
@@ -516,8 +527,9 @@ __global__ void __launch_bounds__(kBalThreads) k_gemv_c1_bal(SpecViewC1 v, Shape
     const int i = threadIdx.x + kBalThreads * j;
     if (i < nlut) {
       const uint32_t f = (uint32_t)i & fmask;
-      lut[i] = __uint_as_float(((f >> m) << 31) | ((uint32_t)perm_l[i >> fw] << 23) |
-                               ((f & ((1u << m) - 1u)) << (23 - m)));
+      // (m <= 7: the fp32 pattern's low 16 bits are zero, so the value is a bf16)
+      lut[i] = (((f >> m) << 31) | ((uint32_t)perm_l[i >> fw] << 23) |
+                ((f & ((1u << m) - 1u)) << (23 - m))) >> 16;
     }
   }
   Part pt{};
