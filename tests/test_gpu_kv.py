@@ -198,6 +198,36 @@ def test_draft_and_verify_attention(gpu, orc, T, fmt):
 
 
 @pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("G", [1, 2, 3])
+def test_draft_attention_fewer_query_rows(gpu, orc, G, fmt):
+    """Draft attention with fewer than four query heads per KV head (one, two
+    or three rows per chunk workgroup): the rows past the last are zero in the
+    matrix-core product and write no partials."""
+    torch, cass = gpu
+    H, k, m, T = 4, 38, 3, 300
+    Hq = H * G
+    Kt, Vt = make_kv(T, H, 77 + G)
+    cache = cass.KvCache(H, D, k, m, max_tokens=T + 8, fmt=fmt)
+    cache.append(dev(torch, Kt), dev(torch, Vt))
+    scale = 1.0 / np.sqrt(D)
+    q1 = synth.activations(Hq, D, 4, t0=T + G)
+    ws = torch.empty(cass.cass_kv_attn_ws_bytes(cache.kv, 1, Hq) + 256, dtype=torch.uint8, device="cuda")
+    out = torch.empty((Hq, D), dtype=torch.float32, device="cuda")
+    cass.cass_kv_draft_attn(cache.kv, dev(torch, q1), scale, out, ws)
+    torch.cuda.synchronize()
+    p = cache.params
+    got = out.cpu().numpy()
+    caps = (p.max_tokens, p.code_cap_bits, p.vcode_cap_bits)
+    for h in range(H):
+        sk, _, _ = orc.kv_encode(Kt[:, h, :], T, k, m, *caps, fmt=fmt)
+        sv, _, _ = orc.kv_encode(Vt[:, h, :], T, k, m, *caps, fmt=fmt)
+        Kd = orc.kv_decode(sk, T, D, k, m, *caps, fmt=fmt)
+        Vd = orc.kv_decode(sv, T, D, k, m, *caps, fmt=fmt)
+        ref, bound = oracle_attention(orc, q1[h * G:(h + 1) * G], Kd, Vd, scale)
+        attn_check(got[h * G:(h + 1) * G], ref, bound)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
 def test_draft_attention_uneven_tokens(gpu, orc, fmt):
     """Draft attention on tokens the grouped decoders cannot take whole: a first
     chunk whose keep bitmaps leave the first 32 positions empty (channels 0-31
