@@ -566,15 +566,28 @@ __global__ void __launch_bounds__(kBalThreads) k_gemv_c1_bal(SpecViewC1 v, Shape
       // full groups: runs of fast groups; a group whose windows fall short
       // for some lane goes value by value
       int gi = 0;
+      auto fits = [&](int need) {
+        const uint32_t sb = bp & 31u;
+        const int have = __builtin_popcount(__builtin_amdgcn_alignbit(w.q1, w.q0, sb)) +
+                         __builtin_popcount(__builtin_amdgcn_alignbit(w.q2, w.q1, sb));
+        const int ncode = __builtin_popcount(__builtin_amdgcn_alignbit(w.c1, w.c0, cp & 31u));
+        return __all(min(have, ncode) >= need);
+      };
       while (gi < G) {
-        for (; gi < G; ++gi) {
-          const uint32_t sb = bp & 31u;
-          const int have = __builtin_popcount(__builtin_amdgcn_alignbit(w.q1, w.q0, sb)) +
-                           __builtin_popcount(__builtin_amdgcn_alignbit(w.q2, w.q1, sb));
-          const int ncode = __builtin_popcount(__builtin_amdgcn_alignbit(w.c1, w.c0, cp & 31u));
-          if (!__all(min(have, ncode) >= U)) break;
+        // two groups per iteration, so the window words of the next group
+        // alternate between two register sets instead of being copied back
+        for (; gi + 1 < G; gi += 2) {
+          if (!fits(U)) break;
           c1_group<BATCH, U, false>(w, bp, fp, cp, bm_b, f_b, c_b, xorg, lutb, fw, g.xstride, g.word_bits, U,
                                     acc);
+          if (!fits(U)) { ++gi; break; }
+          c1_group<BATCH, U, false>(w, bp, fp, cp, bm_b, f_b, c_b, xorg, lutb, fw, g.xstride, g.word_bits, U,
+                                    acc);
+        }
+        if (gi + 1 == G && fits(U)) {
+          c1_group<BATCH, U, false>(w, bp, fp, cp, bm_b, f_b, c_b, xorg, lutb, fw, g.xstride, g.word_bits, U,
+                                    acc);
+          ++gi;
         }
         if (gi < G) {
           // some lane's windows hold fewer than U values: the group as two halves
