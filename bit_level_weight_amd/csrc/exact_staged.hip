@@ -65,6 +65,7 @@ struct XGeom {
   int perm_off, klut_off, plut_off, wave_off, wave_bytes;  // shared tables, wave regions
   int meta_off, dummy_off, tile_off;                       // inside a wave region
   int fix_off, fix_cap, cod_off, cod_cap, lds_bytes;
+  uint32_t wbits;            // 27, the width of a bit position's word index (see word_ptr)
 };
 
 __device__ __forceinline__ void wsync() {
@@ -78,7 +79,6 @@ __device__ __forceinline__ uint32_t u32(int64_t v) { return (uint32_t)v; }
 __device__ __forceinline__ uint32_t lds_addr_of(const uint8_t* p) {
   return (uint32_t)(uintptr_t)(lds_u8c*)p;
 }
-__device__ __forceinline__ uint32_t ldw(uint32_t a) { return *(lds_u32c*)(uintptr_t)a; }
 __device__ __forceinline__ uint32_t ldh(uint32_t a) { return *(lds_u16c*)(uintptr_t)a; }
 __device__ __forceinline__ void sth(uint32_t a, uint32_t v) { *(lds_u16*)(uintptr_t)a = (uint16_t)v; }
 
@@ -89,8 +89,8 @@ __device__ __forceinline__ void wait_all() {
 
 // 32 bits of the LDS bit stream at byte address base, bit offset pos.
 __device__ __forceinline__ uint32_t lwin(uint32_t base, uint32_t pos) {
-  const uint32_t a = base + ((pos >> 5) << 2);
-  return __builtin_amdgcn_alignbit(ldw(a + 4), ldw(a), pos & 31u);
+  const lds_u32c* q = (const lds_u32c*)(uintptr_t)(base + ((pos >> 5) << 2));
+  return __builtin_amdgcn_alignbit(q[1], q[0], pos & 31u);
 }
 
 // Unary code at LDS bit pos (up to 256 bits); advances pos.
@@ -137,12 +137,20 @@ __device__ __forceinline__ int max16(int v) {
 struct KRaw {
   uint32_t q0, q1, q2, f0, f1, l0, l1, c0, c1;
 };
+// The LDS word holding bit `pos` of the staged words at byte address sb: the
+// word index by bit-field extract, then one shift-and-add.  `wb` = 27 comes
+// from a kernel argument (with a literal width the extract becomes a shift
+// and a mask).  Reads index the returned pointer, so the offsets of the next
+// words go into the reads' offset fields instead of separate adds.
+__device__ __forceinline__ const lds_u32c* word_ptr(uint32_t sb, uint32_t pos, uint32_t wb) {
+  return (const lds_u32c*)(uintptr_t)(sb + (__builtin_amdgcn_ubfe(pos, 5u, wb) << 2));
+}
+
 __device__ __forceinline__ KRaw kraw(uint32_t sb, uint32_t bp, uint32_t fp, uint32_t lp,
-                                     uint32_t cp) {
-  const uint32_t qa = sb + ((bp >> 5) << 2), fa = sb + ((fp >> 5) << 2);
-  const uint32_t la = sb + ((lp >> 5) << 2), ca = sb + ((cp >> 5) << 2);
-  return KRaw{ldw(qa), ldw(qa + 4), ldw(qa + 8), ldw(fa), ldw(fa + 4),
-              ldw(la), ldw(la + 4), ldw(ca), ldw(ca + 4)};
+                                     uint32_t cp, uint32_t wb) {
+  const lds_u32c *q = word_ptr(sb, bp, wb), *f = word_ptr(sb, fp, wb);
+  const lds_u32c *l = word_ptr(sb, lp, wb), *c = word_ptr(sb, cp, wb);
+  return KRaw{q[0], q[1], q[2], f[0], f[1], l[0], l[1], c[0], c[1]};
 }
 
 // Pruned group: bitmap (3 words at bp, inverted on use), pruned bytes (3 at
@@ -150,11 +158,11 @@ __device__ __forceinline__ KRaw kraw(uint32_t sb, uint32_t bp, uint32_t fp, uint
 struct PRaw {
   uint32_t q0, q1, q2, y0, y1, y2, c0, c1;
 };
-__device__ __forceinline__ PRaw praw(uint32_t sb, uint32_t bp, uint32_t yp, uint32_t cp) {
-  const uint32_t qa = sb + ((bp >> 5) << 2), ya = sb + ((yp >> 5) << 2);
-  const uint32_t ca = sb + ((cp >> 5) << 2);
-  return PRaw{ldw(qa), ldw(qa + 4), ldw(qa + 8), ldw(ya), ldw(ya + 4), ldw(ya + 8),
-              ldw(ca), ldw(ca + 4)};
+__device__ __forceinline__ PRaw praw(uint32_t sb, uint32_t bp, uint32_t yp, uint32_t cp,
+                                     uint32_t wb) {
+  const lds_u32c *q = word_ptr(sb, bp, wb), *y = word_ptr(sb, yp, wb);
+  const lds_u32c* c = word_ptr(sb, cp, wb);
+  return PRaw{q[0], q[1], q[2], y[0], y[1], y[2], c[0], c[1]};
 }
 
 // Whether the windows in w hold t values: t keep (or pruned) positions in the
@@ -186,7 +194,7 @@ template <int U, bool KLUT, bool MASKED>
 __device__ __forceinline__ void kept_group(KRaw& w, uint32_t& bp, uint32_t& fp, uint32_t& lp,
                                            uint32_t& cp, uint32_t sb, uint32_t torg,
                                            uint32_t klutb, uint32_t dummy, int fw, int lw,
-                                           int lwid, int m, int t) {
+                                           int lwid, int m, int t, uint32_t wb) {
   const uint32_t sbit = bp & 31u;
   const uint32_t lo0 = __builtin_amdgcn_alignbit(w.q1, w.q0, sbit);
   const uint32_t hi0 = __builtin_amdgcn_alignbit(w.q2, w.q1, sbit) | (MASKED ? 0x80000000u : 0u);
@@ -228,7 +236,7 @@ __device__ __forceinline__ void kept_group(KRaw& w, uint32_t& bp, uint32_t& fp, 
   uint32_t hv[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) hv[u] = ldh(la[u]);
-  w = kraw(sb, bp, fp, lp, cp);
+  w = kraw(sb, bp, fp, lp, cp, wb);
   __builtin_amdgcn_sched_barrier(0);
   // phase 3: the values
 #pragma unroll
@@ -251,7 +259,7 @@ __device__ __forceinline__ void kept_group(KRaw& w, uint32_t& bp, uint32_t& fp, 
 template <int U, bool MASKED, bool W32 = false>
 __device__ __forceinline__ void pruned_group(PRaw& w, uint32_t& bp, uint32_t& yp, uint32_t& cp,
                                              uint32_t sb, uint32_t torg, uint32_t plutb,
-                                             uint32_t dummy, int t) {
+                                             uint32_t dummy, int t, uint32_t wb) {
   static_assert(U <= 8, "pruned bytes come from two 32-bit windows");
   static_assert(!(W32 && MASKED), "the 32-bit window serves full groups");
   const uint32_t sbit = bp & 31u;
@@ -294,7 +302,7 @@ __device__ __forceinline__ void pruned_group(PRaw& w, uint32_t& bp, uint32_t& yp
   uint32_t hv[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) hv[u] = ldh(la[u]);
-  w = praw(sb, bp, yp, cp);
+  w = praw(sb, bp, yp, cp, wb);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int u = 0; u < U; ++u) sth(ta[u], hv[u] | mt[u]);
@@ -349,10 +357,11 @@ template <bool INV>
 __device__ __forceinline__ uint32_t find_in_block(uint32_t wa, int nwb, int skip) {
   int rem = skip, wsel = nwb - 1;
   uint32_t wd = 0;
+  const lds_u32c* q = (const lds_u32c*)(uintptr_t)wa;
   if (nwb <= 8) {
     uint32_t wv[8];
 #pragma unroll
-    for (int w = 0; w < 8; ++w) wv[w] = w < nwb ? (INV ? ~ldw(wa + 4 * w) : ldw(wa + 4 * w)) : 0u;
+    for (int w = 0; w < 8; ++w) wv[w] = w < nwb ? (INV ? ~q[w] : q[w]) : 0u;
     bool found = false;
 #pragma unroll
     for (int w = 0; w < 8; ++w) {
@@ -365,13 +374,13 @@ __device__ __forceinline__ uint32_t find_in_block(uint32_t wa, int nwb, int skip
     }
   } else {
     int wi = 0;
-    wd = INV ? ~ldw(wa) : ldw(wa);
+    wd = INV ? ~q[0] : q[0];
     for (;;) {
       const int c = __builtin_popcount(wd);
       if (rem < c || wi == nwb - 1) break;  // (the second test: corrupt streams only)
       rem -= c;
       ++wi;
-      wd = INV ? ~ldw(wa + 4 * wi) : ldw(wa + 4 * wi);
+      wd = INV ? ~q[wi] : q[wi];
     }
     wsel = wi;
   }
@@ -736,7 +745,7 @@ __global__ void __launch_bounds__(64 * kMaxWaves) k_exact_staged(SpecViewC1 sv, 
 #pragma unroll
       for (int o = 32; o >= 1; o >>= 1) nmax = max(nmax, __shfl_xor(nmax, o, 64));
       if (!overflow) {
-        KRaw w = kraw(sb, bp, fp, lp, cp);
+        KRaw w = kraw(sb, bp, fp, lp, cp, g.wbits);
         for (int done = 0; done < nmax; done += KU) {
           const int t = min(max(n - done, 0), KU);
           const uint32_t sbit = bp & 31u;
@@ -746,11 +755,11 @@ __global__ void __launch_bounds__(64 * kMaxWaves) k_exact_staged(SpecViewC1 sv, 
           const bool ok = min(have, ncode) >= t;
           if (__all(t == KU && ok)) {
             kept_group<KU, KLUT, false>(w, bp, fp, lp, cp, sb, torg, klutb, dummy, fw, lw, lwid, m,
-                                        KU);
+                                        KU, g.wbits);
           } else if (__all(ok)) {
             // some part ends inside this group
             kept_group<KU, KLUT, true>(w, bp, fp, lp, cp, sb, torg, klutb, dummy, fw, lw, lwid, m,
-                                       t);
+                                       t, g.wbits);
           } else {
             // some lane's windows hold fewer than its t values: the group in two
             // halves on the fast path (a lane whose first half is short of its
@@ -759,20 +768,20 @@ __global__ void __launch_bounds__(64 * kMaxWaves) k_exact_staged(SpecViewC1 sv, 
             const int t1 = t < H1 ? t : H1, t2 = t - t1;
             if (__all(ok1_kept(w, bp, cp, t1))) {
               kept_group<H1, KLUT, true>(w, bp, fp, lp, cp, sb, torg, klutb, dummy, fw, lw, lwid,
-                                         m, t1);
+                                         m, t1, g.wbits);
               if (__all(ok1_kept(w, bp, cp, t2))) {
                 kept_group<H2, KLUT, true>(w, bp, fp, lp, cp, sb, torg, klutb, dummy, fw, lw,
-                                           lwid, m, t2);
+                                           lwid, m, t2, g.wbits);
               } else {
                 for (int u = 0; u < H2; ++u)
                   if (u < t2)
                     kept_step(sb, bp, bm_end, fp, lp, cp, nullptr, torg, ps, fw, lw, lwid, m);
-                w = kraw(sb, bp, fp, lp, cp);
+                w = kraw(sb, bp, fp, lp, cp, g.wbits);
               }
             } else {
               for (int u = 0; u < KU; ++u)
                 if (u < t) kept_step(sb, bp, bm_end, fp, lp, cp, nullptr, torg, ps, fw, lw, lwid, m);
-              w = kraw(sb, bp, fp, lp, cp);
+              w = kraw(sb, bp, fp, lp, cp, g.wbits);
             }
           }
         }
@@ -807,7 +816,7 @@ __global__ void __launch_bounds__(64 * kMaxWaves) k_exact_staged(SpecViewC1 sv, 
       for (int o = 32; o >= 1; o >>= 1) nmax = max(nmax, __shfl_xor(nmax, o, 64));
       if (!overflow) {
         int done = 0;
-        PRaw w = praw(sb, bp, yp, cp);
+        PRaw w = praw(sb, bp, yp, cp, g.wbits);
         for (; done < nmax; done += kPU) {
           const int t = min(max(n - done, 0), kPU);
           const uint32_t sbit = bp & 31u;
@@ -817,28 +826,28 @@ __global__ void __launch_bounds__(64 * kMaxWaves) k_exact_staged(SpecViewC1 sv, 
           const bool ok = min(have, ncode) >= t;
           const int have32 = __builtin_popcount(~__builtin_amdgcn_alignbit(w.q1, w.q0, sbit));
           if (__all(t == kPU && ncode >= kPU && have32 >= kPU)) {
-            pruned_group<kPU, false, true>(w, bp, yp, cp, sb, torg, plutb, dummy, kPU);
+            pruned_group<kPU, false, true>(w, bp, yp, cp, sb, torg, plutb, dummy, kPU, g.wbits);
           } else if (__all(t == kPU && ok)) {
-            pruned_group<kPU, false>(w, bp, yp, cp, sb, torg, plutb, dummy, kPU);
+            pruned_group<kPU, false>(w, bp, yp, cp, sb, torg, plutb, dummy, kPU, g.wbits);
           } else if (__all(ok)) {
-            pruned_group<kPU, true>(w, bp, yp, cp, sb, torg, plutb, dummy, t);
+            pruned_group<kPU, true>(w, bp, yp, cp, sb, torg, plutb, dummy, t, g.wbits);
           } else {
             // in two halves, as for the kept values
             constexpr int H1 = kPU / 2, H2 = kPU - kPU / 2;
             const int t1 = t < H1 ? t : H1, t2 = t - t1;
             if (__all(ok1_pruned(w, bp, cp, t1))) {
-              pruned_group<H1, true>(w, bp, yp, cp, sb, torg, plutb, dummy, t1);
+              pruned_group<H1, true>(w, bp, yp, cp, sb, torg, plutb, dummy, t1, g.wbits);
               if (__all(ok1_pruned(w, bp, cp, t2))) {
-                pruned_group<H2, true>(w, bp, yp, cp, sb, torg, plutb, dummy, t2);
+                pruned_group<H2, true>(w, bp, yp, cp, sb, torg, plutb, dummy, t2, g.wbits);
               } else {
                 for (int u = 0; u < H2; ++u)
                   if (u < t2) pruned_step(sb, bp, bm_end, yp, cp, nullptr, torg, pv);
-                w = praw(sb, bp, yp, cp);
+                w = praw(sb, bp, yp, cp, g.wbits);
               }
             } else {
               for (int u = 0; u < kPU; ++u)
                 if (u < t) pruned_step(sb, bp, bm_end, yp, cp, nullptr, torg, pv);
-              w = praw(sb, bp, yp, cp);
+              w = praw(sb, bp, yp, cp, g.wbits);
             }
           }
         }
@@ -854,7 +863,8 @@ __global__ void __launch_bounds__(64 * kMaxWaves) k_exact_staged(SpecViewC1 sv, 
       // columns 8kq..8kq+7 of each 32-column step
       auto step = [&](int ks, const v8s& bop) {
         const uint32_t ta = tileb + 2u * (uint32_t)(xn * g.TS + ks * 32 + 8 * xkq);
-        const uint32_t a0 = ldw(ta), a1 = ldw(ta + 4), a2 = ldw(ta + 8), a3 = ldw(ta + 12);
+        const lds_u32c* tp = (const lds_u32c*)(uintptr_t)ta;
+        const uint32_t a0 = tp[0], a1 = tp[1], a2 = tp[2], a3 = tp[3];
         const v8s aop = v8s{(short)(a0 & 0xFFFF), (short)(a0 >> 16), (short)(a1 & 0xFFFF),
                             (short)(a1 >> 16), (short)(a2 & 0xFFFF), (short)(a2 >> 16),
                             (short)(a3 & 0xFFFF), (short)(a3 >> 16)};
@@ -871,7 +881,8 @@ __global__ void __launch_bounds__(64 * kMaxWaves) k_exact_staged(SpecViewC1 sv, 
         const int rr = c / cpr, cc = c - rr * cpr;
         if (row0 + rr < R) {
           const uint32_t ta = tileb + 2u * (uint32_t)(rr * g.TS + cc * 8);
-          const u32x4 v = u32x4{ldw(ta), ldw(ta + 4), ldw(ta + 8), ldw(ta + 12)};
+          const lds_u32c* tp = (const lds_u32c*)(uintptr_t)ta;
+          const u32x4 v = u32x4{tp[0], tp[1], tp[2], tp[3]};
           *reinterpret_cast<u32x4*>(out + (row0 + rr) * C + bf * B + cc * 8) = v;
         }
       }
@@ -920,6 +931,7 @@ XGeom make_xgeom(const Shape& sh, const SpecViewC1& sv, const VerifViewC1& vv) {
   if (const int w = option(OPT_EXACT_BLOCKS); w >= 1 && w <= 2) g.Wb = w;
   g.TS = (int)(g.Wb * B + 2);
   g.nstage = (nb + g.Wb - 1) / g.Wb;
+  g.wbits = 27;
   const int64_t pos = (int64_t)g.Wb * B;  // positions per row per stage
   // fixed-width sections: 1 + 8 bits per position, plus chunk rounding
   const int64_t fix_row = (9 * pos + 127) / 128 * 16 + 7 * 16;
