@@ -962,13 +962,19 @@ __global__ void __launch_bounds__(kBalThreads) k_gemv_c2_bal(SpecViewC2 v, Shape
       C2Raw w = c2raw(bm_l, f_l, bp, fp);
       int gi = 0;
       while (gi < G) {
-        for (; gi < G; ++gi) {
-          const uint32_t sb = bp & 31u;
-          const int have = __builtin_popcount(__builtin_amdgcn_alignbit(w.q1, w.q0, sb)) +
-                           __builtin_popcount(__builtin_amdgcn_alignbit(w.q2, w.q1, sb));
-          if (!__all(have >= U)) break;
+        // two groups per iteration, as in the Cassandra-1 kernel
+        for (; gi + 1 < G; gi += 2) {
+          if (!__all(c2_have(w, bp) >= U)) break;
           c2_group<BATCH, U, false>(w, bp, fp, bm_l, f_l, xorg, eorg, lutb, fw, ebias,
                                     g.xstride, U, acc);
+          if (!__all(c2_have(w, bp) >= U)) { ++gi; break; }
+          c2_group<BATCH, U, false>(w, bp, fp, bm_l, f_l, xorg, eorg, lutb, fw, ebias,
+                                    g.xstride, U, acc);
+        }
+        if (gi + 1 == G && __all(c2_have(w, bp) >= U)) {
+          c2_group<BATCH, U, false>(w, bp, fp, bm_l, f_l, xorg, eorg, lutb, fw, ebias,
+                                    g.xstride, U, acc);
+          ++gi;
         }
         if (gi < G) {
           // some lane's keep window holds fewer than U positions: the group as
