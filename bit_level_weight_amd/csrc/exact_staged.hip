@@ -827,6 +827,16 @@ __global__ void __launch_bounds__(64 * kMaxWaves) k_exact_staged(SpecViewC1 sv, 
           const int have32 = __builtin_popcount(~__builtin_amdgcn_alignbit(w.q1, w.q0, sbit));
           if (__all(t == kPU && ncode >= kPU && have32 >= kPU)) {
             pruned_group<kPU, false, true>(w, bp, yp, cp, sb, torg, plutb, dummy, kPU, g.wbits);
+            // a second full group at once when it also fits the 32-bit windows
+            // (fewer trips through the loop's tests and branches)
+            const int t2 = min(max(n - done - kPU, 0), kPU);
+            const uint32_t sb2 = bp & 31u;
+            const int nc2 = __builtin_popcount(__builtin_amdgcn_alignbit(w.c1, w.c0, cp & 31u));
+            const int h2 = __builtin_popcount(~__builtin_amdgcn_alignbit(w.q1, w.q0, sb2));
+            if (__all(t2 == kPU && nc2 >= kPU && h2 >= kPU)) {
+              pruned_group<kPU, false, true>(w, bp, yp, cp, sb, torg, plutb, dummy, kPU, g.wbits);
+              done += kPU;
+            }
           } else if (__all(t == kPU && ok)) {
             pruned_group<kPU, false>(w, bp, yp, cp, sb, torg, plutb, dummy, kPU, g.wbits);
           } else if (__all(ok)) {
