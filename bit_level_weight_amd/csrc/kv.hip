@@ -415,54 +415,78 @@ __global__ void __launch_bounds__(64 * kWaves) k_kv_pack(KvDev kv, const uint16_
            t0 + i, ws.start[2 * vi], ws.start[2 * vi + 1], lane);
 }
 
-// ---- a few tokens in one launch: one wave per stream runs select, lengths,
-// code positions and packing for the stream's tokens in order (the rank tables
-// are frozen).  The same bytes, tails and flags as the five-launch path.
+// ---- a few tokens in one launch: a workgroup per stream and a wave per token
+// (the rank tables are frozen).  The waves select and measure their tokens side
+// by side, take their code starts from the tokens' lengths in order through
+// shared memory, and pack side by side (every multi-bit write is an atomic or
+// into zeroed words, so neighbouring tokens may share a word).  The same bytes,
+// tails and flags as the five-launch path.
 constexpr int kFusedMaxTokens = 16;
 
-__global__ void __launch_bounds__(64) k_kv_append_few(KvDev kv, const uint16_t* kk,
-                                                      const uint16_t* vv, int ntok, int64_t t0,
-                                                      AppendWs ws) {
-  __shared__ uint16_t keys[256];
-  __shared__ uint32_t bm[8];
+__global__ void __launch_bounds__(64 * kFusedMaxTokens) k_kv_append_few(KvDev kv, const uint16_t* kk,
+                                                                     const uint16_t* vv, int ntok,
+                                                                     int64_t t0, AppendWs ws) {
+  __shared__ uint16_t keys[kFusedMaxTokens][256];
+  __shared__ uint32_t bm[kFusedMaxTokens][8];
   __shared__ uint8_t rs[256], rv[256];
+  __shared__ uint32_t lens[kFusedMaxTokens][2];
   const int s = blockIdx.x, h = s >> 1, kind = s & 1;
-  const int lane = threadIdx.x;
-  load_ranks(kv, s, rs, rv, lane);
+  const int lane = threadIdx.x & 63, i = threadIdx.x >> 6;  // wave i takes token t0 + i
+  {
+    const uint8_t* ps = kv.spec + s * kv.sstride + kv.so[0];
+    const uint8_t* pv = kv.verif + s * kv.vstride + kv.vo[0];
+    for (int r = threadIdx.x; r < 256; r += blockDim.x) {
+      rs[ps[r]] = (uint8_t)r;
+      rv[pv[r]] = (uint8_t)r;
+    }
+  }
+  __syncthreads();  // the rank tables
   const bool c1 = kv.fmt == CASS_FMT_C1_UNARY;
-  unsigned long long tail[2] = {kv.state[2 + 2 * s], kv.state[3 + 2 * s]};
+  const unsigned long long tail0[2] = {kv.state[2 + 2 * s], kv.state[3 + 2 * s]};
   const unsigned long long cap[2] = {(unsigned long long)kv.ccap, (unsigned long long)kv.vcap};
   uint32_t* vofs = reinterpret_cast<uint32_t*>(kv.verif + s * kv.vstride + kv.vo[3]);
   uint32_t* offs[2] = {c1 ? reinterpret_cast<uint32_t*>(kv.spec + s * kv.sstride + kv.so[2]) : vofs,
                        c1 ? vofs : vofs + 1};
   const int ostride = c1 ? 1 : 2;
-  bool over[2] = {false, false};
-  for (int i = 0; i < ntok; ++i) {
-    const uint16_t* x = vec_ptr(kk, vv, i, h, kind, kv.H, kv.D);
-    vec_select(kv, x, s, 0, ws, keys, bm, lane);
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    // the vector is read from global memory once: the later steps take the
-    // shared-memory copy
-    const uint16_t* xs = keys;
-    uint32_t len[2];
-    vec_lengths(kv, xs, bm, rs, rv, lane, len[0], len[1]);
-    uint32_t start[2];
-    for (int which = 0; which < 2; ++which) {
-      const bool fits = tail[which] + len[which] <= cap[which];
-      start[which] = fits ? (uint32_t)tail[which] : 0xFFFFFFFFu;
-      if (!fits) over[which] = true;
-      tail[which] += len[which];
-      if (lane == 0) offs[which][(t0 + i) * ostride] = start[which];
-    }
-    vec_pack(kv, xs, bm, rs, rv, s, t0 + i, start[0], start[1], lane);
-    __builtin_amdgcn_wave_barrier();  // the next token's select rewrites keys and bm
-  }
+  // each wave selects its token's kept values and measures its two code runs
+  const uint16_t* x = vec_ptr(kk, vv, i, h, kind, kv.H, kv.D);
+  vec_select(kv, x, s, 0, ws, keys[i], bm[i], lane);
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  // (the vector is read from global memory once: the later steps take the
+  // shared-memory copy)
+  uint32_t len[2];
+  vec_lengths(kv, keys[i], bm[i], rs, rv, lane, len[0], len[1]);
   if (lane == 0) {
+    lens[i][0] = len[0];
+    lens[i][1] = len[1];
+  }
+  __syncthreads();  // every token's lengths
+  // a token's codes start after the stream's tail and the earlier tokens'
+  // codes; a token that does not fit gets no code start, and then no later
+  // one fits either (the tail only grows), so the stream overflows exactly
+  // when its last token ends past the cap
+  unsigned long long before[2] = {tail0[0], tail0[1]}, end[2] = {tail0[0], tail0[1]};
+  for (int t = 0; t < ntok; ++t) {
+#pragma unroll
+    for (int which = 0; which < 2; ++which) {
+      before[which] += t < i ? lens[t][which] : 0u;
+      end[which] += lens[t][which];
+    }
+  }
+  uint32_t start[2];
+#pragma unroll
+  for (int which = 0; which < 2; ++which) {
+    start[which] = before[which] + len[which] <= cap[which] ? (uint32_t)before[which] : 0xFFFFFFFFu;
+    if (lane == 0) offs[which][(t0 + i) * ostride] = start[which];
+  }
+  vec_pack(kv, keys[i], bm[i], rs, rv, s, t0 + i, start[0], start[1], lane);
+  if (threadIdx.x == 0) {
     // on overflow the stream is closed, as in the five-launch path
-    if (over[0] || over[1]) atomicOr(kv.state + 1, (unsigned long long)CASS_KV_FLAG_OVERFLOW);
-    kv.state[2 + 2 * s] = over[0] ? cap[0] : tail[0];
-    kv.state[3 + 2 * s] = over[1] ? cap[1] : tail[1];
+    const bool over0 = end[0] > cap[0], over1 = end[1] > cap[1];
+    if (over0 || over1) atomicOr(kv.state + 1, (unsigned long long)CASS_KV_FLAG_OVERFLOW);
+    kv.state[2 + 2 * s] = over0 ? cap[0] : end[0];
+    kv.state[3 + 2 * s] = over1 ? cap[1] : end[1];
     if (s == 0) kv.state[0] += (unsigned long long)ntok;
   }
 }
@@ -2033,7 +2057,8 @@ int cass_kv_append_encode(cass_kv* kv, const uint16_t* k, const uint16_t* v, int
   hipError_t e;
   if (!first && ntok <= kFusedMaxTokens && option(OPT_KV_APPEND_PATH) != 1) {
     // a decoding step's few tokens: one launch, one wave per stream
-    k_kv_append_few<<<2 * kv->p.n_kv_heads, 64, 0, stream>>>(d, k, v, ntok, kv->tokens, w);
+    // one wave per token: selections, lengths and packing side by side
+    k_kv_append_few<<<2 * kv->p.n_kv_heads, 64 * ntok, 0, stream>>>(d, k, v, ntok, kv->tokens, w);
     if ((e = hipGetLastError()) != hipSuccess) return report(CASS_ERR_HIP, "append: %s", hipGetErrorString(e));
     kv->tokens += ntok;
     return CASS_OK;
