@@ -65,16 +65,27 @@ __device__ __forceinline__ const uint16_t* vec_ptr(const uint16_t* kk, const uin
 // the first k - #(keys > T) in index order.
 constexpr int kSelChunks = 4;  // head_dim <= 256
 
-__device__ __forceinline__ void vec_select(const KvDev& kv, const uint16_t* x, int s, int first,
-                                           const AppendWs& ws, uint16_t* keys, uint32_t* bm,
-                                           int lane) {
+// A vector's values for vec_select_loaded: lane l holds elements l, l + 64, ...
+__device__ __forceinline__ void vec_load(const KvDev& kv, const uint16_t* x,
+                                         uint16_t (&xin)[kSelChunks], int lane) {
+  const int D = kv.D, nc = (D + 63) / 64;
+#pragma unroll
+  for (int c = 0; c < kSelChunks; ++c) {
+    const int j = c * 64 + lane;
+    xin[c] = (c < nc && j < D) ? x[j] : (uint16_t)0;
+  }
+}
+
+__device__ __forceinline__ void vec_select_loaded(const KvDev& kv, const uint16_t (&xin)[kSelChunks],
+                                                  int s, int first, const AppendWs& ws,
+                                                  uint16_t* keys, uint32_t* bm, int lane) {
   const int D = kv.D, nc = (D + 63) / 64;
   int key[kSelChunks];
 #pragma unroll
   for (int c = 0; c < kSelChunks; ++c) {
     const int j = c * 64 + lane;
     const bool in = c < nc && j < D;
-    const uint16_t b = in ? x[j] : (uint16_t)0;
+    const uint16_t b = xin[c];
     if (in) keys[j] = b;
     key[c] = in ? key_of(b) : -1;  // -1: no value, below every candidate
   }
@@ -113,6 +124,14 @@ __device__ __forceinline__ void vec_select(const KvDev& kv, const uint16_t* x, i
       if (w0 + 1 < D / 32) bm[w0 + 1] = (uint32_t)(mask >> 32);
     }
   }
+}
+
+__device__ __forceinline__ void vec_select(const KvDev& kv, const uint16_t* x, int s, int first,
+                                           const AppendWs& ws, uint16_t* keys, uint32_t* bm,
+                                           int lane) {
+  uint16_t xin[kSelChunks];
+  vec_load(kv, x, xin, lane);
+  vec_select_loaded(kv, xin, s, first, ws, keys, bm, lane);
 }
 
 __global__ void __launch_bounds__(64 * kWaves) k_kv_select(KvDev kv, const uint16_t* kk,
@@ -432,6 +451,10 @@ __global__ void __launch_bounds__(64 * kFusedMaxTokens) k_kv_append_few(KvDev kv
   __shared__ uint32_t lens[kFusedMaxTokens][2];
   const int s = blockIdx.x, h = s >> 1, kind = s & 1;
   const int lane = threadIdx.x & 63, i = threadIdx.x >> 6;  // wave i takes token t0 + i
+  // the token's vector is loaded before the rank tables, so the two loads
+  // overlap
+  uint16_t xin[kSelChunks];
+  vec_load(kv, vec_ptr(kk, vv, i, h, kind, kv.H, kv.D), xin, lane);
   {
     const uint8_t* ps = kv.spec + s * kv.sstride + kv.so[0];
     const uint8_t* pv = kv.verif + s * kv.vstride + kv.vo[0];
@@ -449,8 +472,7 @@ __global__ void __launch_bounds__(64 * kFusedMaxTokens) k_kv_append_few(KvDev kv
                        c1 ? vofs : vofs + 1};
   const int ostride = c1 ? 1 : 2;
   // each wave selects its token's kept values and measures its two code runs
-  const uint16_t* x = vec_ptr(kk, vv, i, h, kind, kv.H, kv.D);
-  vec_select(kv, x, s, 0, ws, keys[i], bm[i], lane);
+  vec_select_loaded(kv, xin, s, 0, ws, keys[i], bm[i], lane);
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   // (the vector is read from global memory once: the later steps take the
